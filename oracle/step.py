@@ -1,0 +1,175 @@
+"""Plain CPU fp64 oracle for the EMA-Gram quarter-power preconditioner step.
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU-baseline
+leg of the benchmark may import or run this module. The product path (the HIP
+library and its Python binding) never calls it and must fail loudly when the
+HIP library is missing.
+
+What it computes, and where the pages define it:
+
+* marin.community, "Sharding EMA-Gram eigensolves", section "Background":
+  for every linear weight the optimizer keeps an exponential moving average of
+  G·Gᵀ (the left Gram) and of Gᵀ·G (the right Gram, "the reverse order"). At
+  each update it rescales both Grams, decomposes each into eigenvectors and
+  eigenvalues, adds a small regulariser to the eigenvalues, raises them to
+  -1/4, rebuilds the matrices, and uses these inverse quarter powers to shape
+  the direction of the update.
+* The two-sided shape U = L^-1/4 · G · R^-1/4 is the Shampoo form described
+  in tilderesearch, "Online KL Shampoo", section 1 (its formulas did not
+  survive extraction; the shape used here is the one the build's problem
+  statement fixes).
+
+Readings taken where the pages are silent (each is listed with its reason in
+the design notes):
+
+* rescale = divide by the trace, so the rescaled Gram has unit trace;
+* EMA = beta*S + (1-beta)*Gram, starting from zero, no bias correction;
+* the regulariser eps is added to the eigenvalues of the rescaled Gram;
+* the rescale is not undone after the root;
+* no clamping of eigenvalues: a Gram whose shifted spectrum is not positive is
+  reported as not positive definite;
+* the input of the root is taken as the symmetric part (A + Aᵀ)/2;
+* the output root is symmetrised, (X + Xᵀ)/2 (the OKLS page, appendix D, does
+  the same to its root).
+
+Everything is float64. numpy's ``@`` (BLAS dgemm) and ``numpy.linalg.eigh``
+(LAPACK dsyevd) are the only library steps; nothing is blocked, fused or
+reordered beyond the definitions above.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# Per-matrix outcome flags (same meaning as the library's info flags).
+FLAG_NONFINITE = 1
+FLAG_ZERO_TRACE = 2
+FLAG_NOT_PD = 4
+
+NORM_NONE = "none"
+NORM_TRACE = "trace"
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def left_gram(G) -> np.ndarray:
+    """G·Gᵀ (m×m): the product the left Gram averages (EMA-Gram page, Background)."""
+    G = _f64(G)
+    return G @ G.T
+
+
+def right_gram(G) -> np.ndarray:
+    """Gᵀ·G (n×n): the product "in the reverse order" (EMA-Gram page, Background)."""
+    G = _f64(G)
+    return G.T @ G
+
+
+def gram_ema_update(L, R, G, beta: float):
+    """One EMA step of both Grams: S <- beta*S + (1-beta)*Gram(G).
+
+    EMA-Gram page, Background: each Gram is an exponential moving average of
+    gradient products. The weighting convention is not printed; this is the
+    plain one. Returns new (L, R) in float64; the inputs are not modified.
+    """
+    beta = float(beta)
+    L_new = beta * _f64(L) + (1.0 - beta) * left_gram(G)
+    R_new = beta * _f64(R) + (1.0 - beta) * right_gram(G)
+    return L_new, R_new
+
+
+def rescale(A, normalize: str = NORM_TRACE):
+    """Rescale a Gram before its root (EMA-Gram page, Background and Approach).
+
+    TRACE: s = tr(A), returns (A/s, s). NONE: s = 1, returns (A, 1).
+    A zero trace returns (A, 0.0); the caller reports ZERO_TRACE.
+    """
+    A = _f64(A)
+    if normalize == NORM_NONE:
+        return A.copy(), 1.0
+    if normalize != NORM_TRACE:
+        raise ValueError(f"unknown normalize mode {normalize!r}")
+    s = float(np.trace(A))
+    if s == 0.0:
+        return A.copy(), 0.0
+    return A / s, s
+
+
+def inv_quarter_root(A, eps: float, normalize: str = NORM_TRACE):
+    """X = (Â + eps·I)^(-1/4) by a dense symmetric eigensolver.
+
+    EMA-Gram page, Background: decompose into eigenvectors and eigenvalues,
+    add a small regulariser to the eigenvalues, raise them to -1/4 and
+    rebuild the matrix.  Â = sym(A)/s with s from :func:`rescale`.
+
+    Returns (X, info) with info = {"scale": s, "flags": bits,
+    "eigenvalues": eigenvalues of Â (ascending)}.  Special cases:
+    non-finite input -> X all NaN, NONFINITE; zero trace -> X = eps^(-1/4)·I,
+    ZERO_TRACE; some eigenvalue + eps <= 0 -> X all NaN, NOT_PD.
+    """
+    A = _f64(A)
+    d = A.shape[0]
+    if A.shape != (d, d):
+        raise ValueError("A must be square")
+    eps = float(eps)
+    if not np.all(np.isfinite(A)):
+        return np.full((d, d), np.nan), {"scale": float("nan"), "flags": FLAG_NONFINITE,
+                                         "eigenvalues": None}
+    A = 0.5 * (A + A.T)
+    Ahat, s = rescale(A, normalize)
+    if s == 0.0:
+        return eps ** -0.25 * np.eye(d), {"scale": 0.0, "flags": FLAG_ZERO_TRACE,
+                                          "eigenvalues": np.zeros(d)}
+    w, V = np.linalg.eigh(Ahat)
+    shifted = w + eps
+    if np.min(shifted) <= 0.0:
+        return np.full((d, d), np.nan), {"scale": s, "flags": FLAG_NOT_PD, "eigenvalues": w}
+    f = shifted ** -0.25
+    X = (V * f) @ V.T
+    X = 0.5 * (X + X.T)
+    return X, {"scale": s, "flags": 0, "eigenvalues": w}
+
+
+def precondition_apply(XL, G, XR, alpha: float = 1.0) -> np.ndarray:
+    """U = alpha · X_L · G · X_R (the two-sided quarter-power direction)."""
+    return float(alpha) * ((_f64(XL) @ _f64(G)) @ _f64(XR))
+
+
+def preconditioner_step(L, R, G, beta: float, eps: float, normalize: str = NORM_TRACE):
+    """The whole per-weight step: EMA both Grams, root both, apply to G.
+
+    Returns (L, R, XL, XR, U, flags) where flags ORs both roots' flags.
+    """
+    L, R = gram_ema_update(L, R, G, beta)
+    XL, il = inv_quarter_root(L, eps, normalize)
+    XR, ir = inv_quarter_root(R, eps, normalize)
+    U = precondition_apply(XL, G, XR)
+    return L, R, XL, XR, U, il["flags"] | ir["flags"]
+
+
+def run_sequence(grads, beta: float, eps: float, normalize: str = NORM_TRACE, L0=None, R0=None):
+    """Run the step over a sequence of gradients of one weight from zero state.
+
+    Yields (t, L, R, XL, XR, U, flags) for t = 1, 2, ...
+    """
+    L = R = None
+    for t, G in enumerate(grads, start=1):
+        G = _f64(G)
+        m, n = G.shape
+        if L is None:
+            L = np.zeros((m, m)) if L0 is None else _f64(L0)
+            R = np.zeros((n, n)) if R0 is None else _f64(R0)
+        L, R, XL, XR, U, flags = preconditioner_step(L, R, G, beta, eps, normalize)
+        yield t, L, R, XL, XR, U, flags
+
+
+def relative_frobenius(x, ref) -> float:
+    """‖x − ref‖_F / ‖ref‖_F: the comparison the EMA-Gram page uses for update
+    directions (section "Results")."""
+    x = _f64(x)
+    ref = _f64(ref)
+    den = np.linalg.norm(ref)
+    if den == 0.0:
+        return float(np.linalg.norm(x))
+    return float(np.linalg.norm(x - ref) / den)

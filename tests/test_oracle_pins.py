@@ -1,0 +1,325 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a closed
+form, an independent library routine (SVD, mpmath's arbitrary-precision
+symmetric eigensolver), brute force on tiny inputs, or an invariant of the
+matrix function.  A dropped term, a wrong sign or index, a transposed operand
+or swapped EMA weights in the oracle fails at least one of them.
+"""
+
+import itertools
+
+import mpmath
+import numpy as np
+import pytest
+
+import oracle
+from matrix_roots_amd import workloads
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+# ---------------------------------------------------------------- Gram EMA
+def test_gram_products_by_loops():
+    """L_ij = sum_k G_ik G_jk and R_ij = sum_k G_ki G_kj, by explicit loops."""
+    rng = np.random.default_rng(1)
+    G = rng.standard_normal((3, 5))
+    L = oracle.left_gram(G)
+    R = oracle.right_gram(G)
+    assert L.shape == (3, 3) and R.shape == (5, 5)
+    for i, j in itertools.product(range(3), range(3)):
+        assert L[i, j] == pytest.approx(sum(G[i, k] * G[j, k] for k in range(5)), rel=1e-14)
+    for i, j in itertools.product(range(5), range(5)):
+        assert R[i, j] == pytest.approx(sum(G[k, i] * G[k, j] for k in range(3)), rel=1e-14)
+
+
+def test_ema_weights_by_loops():
+    """Two EMA steps from zero with beta=0.9: S2 = 0.9*0.1*P1 + 0.1*P2."""
+    rng = np.random.default_rng(2)
+    G1, G2 = rng.standard_normal((2, 4, 3))
+    L = np.zeros((4, 4))
+    R = np.zeros((3, 3))
+    L, R = oracle.gram_ema_update(L, R, G1, 0.9)
+    L, R = oracle.gram_ema_update(L, R, G2, 0.9)
+    for i, j in itertools.product(range(4), range(4)):
+        p1 = sum(G1[i, k] * G1[j, k] for k in range(3))
+        p2 = sum(G2[i, k] * G2[j, k] for k in range(3))
+        assert L[i, j] == pytest.approx(0.9 * 0.1 * p1 + 0.1 * p2, rel=1e-13, abs=1e-15)
+
+
+# ------------------------------------------------------- diagonal closed form
+@pytest.mark.parametrize("m,n", [(4, 6), (5, 5), (7, 3)])
+def test_diagonal_closed_form_multistep(m, n):
+    """Diagonal gradients keep both Grams diagonal: every quantity is scalar.
+
+    l_i = sum_t beta^(T-t) (1-beta) g_ti^2 ; x_i = (l_i / sum l + eps)^(-1/4);
+    U_ii = g_Ti x_i y_i, off-diagonal U zero.
+    """
+    rng = np.random.default_rng(3)
+    beta, eps, T = 0.8, 1e-3, 4
+    k = min(m, n)
+    diags = rng.uniform(0.5, 2.0, size=(T, k)) * rng.choice([-1, 1], size=(T, k))
+    grads = []
+    for t in range(T):
+        G = np.zeros((m, n))
+        G[np.arange(k), np.arange(k)] = diags[t]
+        grads.append(G)
+    res = list(oracle.run_sequence(grads, beta, eps))
+    for t in range(1, T + 1):
+        _, L, R, XL, XR, U, flags = res[t - 1]
+        assert flags == 0
+        lvals = np.zeros(m)
+        rvals = np.zeros(n)
+        for s in range(1, t + 1):
+            w = beta ** (t - s) * (1.0 - beta)
+            lvals[:k] += w * diags[s - 1] ** 2
+            rvals[:k] += w * diags[s - 1] ** 2
+        x = (lvals / lvals.sum() + eps) ** -0.25
+        y = (rvals / rvals.sum() + eps) ** -0.25
+        np.testing.assert_allclose(np.diag(L), lvals, rtol=1e-14)
+        np.testing.assert_allclose(XL, np.diag(x), rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(XR, np.diag(y), rtol=1e-13, atol=1e-13)
+        Uexp = np.zeros((m, n))
+        Uexp[np.arange(k), np.arange(k)] = diags[t - 1] * x[:k] * y[:k]
+        np.testing.assert_allclose(U, Uexp, rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------- 2x2 closed form
+@pytest.mark.parametrize("a,b,c,eps", [(3.0, 1.0, 2.0, 1e-6), (0.1, -0.4, 2.5, 1e-2),
+                                       (1.0, 0.0, 4.0, 0.0), (2.0, 1.9, 2.0, 1e-8)])
+def test_2x2_closed_form(a, b, c, eps):
+    """Eigenpairs of [[a,b],[b,c]] in closed form; X = sum_k f(l_k) P_k with the
+    spectral projectors P_k = (A - l_other I)/(l_k - l_other)."""
+    A = np.array([[a, b], [b, c]])
+    mid, rad = (a + c) / 2.0, np.hypot((a - c) / 2.0, b)
+    lp, lm = mid + rad, mid - rad
+    I = np.eye(2)
+    if rad == 0.0:
+        Xexp = (lp + eps) ** -0.25 * I
+    else:
+        Pp = (A - lm * I) / (lp - lm)
+        Pm = (A - lp * I) / (lm - lp)
+        Xexp = (lp + eps) ** -0.25 * Pp + (lm + eps) ** -0.25 * Pm
+    X, info = oracle.inv_quarter_root(A, eps, normalize="none")
+    assert info["flags"] == 0
+    np.testing.assert_allclose(X, Xexp, rtol=1e-13, atol=1e-14)
+    # trace mode: same with A/tr(A)
+    X2, info2 = oracle.inv_quarter_root(A, eps, normalize="trace")
+    s = a + c
+    lp2, lm2 = lp / s, lm / s
+    if rad == 0.0:
+        Xexp2 = (lp2 + eps) ** -0.25 * I
+    else:
+        Xexp2 = (lp2 + eps) ** -0.25 * Pp + (lm2 + eps) ** -0.25 * Pm
+    assert info2["scale"] == pytest.approx(s, rel=1e-15)
+    np.testing.assert_allclose(X2, Xexp2, rtol=1e-13, atol=1e-14)
+
+
+# ------------------------------------------------- brute force, 50 digits
+def _mp_root(A, eps, normalize):
+    mpmath.mp.dps = 50
+    d = A.shape[0]
+    M = mpmath.matrix([[mpmath.mpf(float(A[i, j])) for j in range(d)] for i in range(d)])
+    if normalize == "trace":
+        s = sum(M[i, i] for i in range(d))
+        M = M / s
+    E, Q = mpmath.mp.eigsy(M)
+    f = [(E[k] + mpmath.mpf(eps)) ** mpmath.mpf(-0.25) for k in range(d)]
+    X = mpmath.matrix(d, d)
+    for i in range(d):
+        for j in range(d):
+            X[i, j] = sum(Q[i, k] * f[k] * Q[j, k] for k in range(d))
+    return X
+
+
+def _to_np(X):
+    return np.array([[float(X[i, j]) for j in range(X.cols)] for i in range(X.rows)])
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_4x4_root_bruteforce_mpmath(seed):
+    rng = np.random.default_rng(10 + seed)
+    B = rng.standard_normal((4, 4))
+    A = B @ B.T + np.diag([0.0, 0.0, 0.0, 1e-3])
+    for normalize, eps in (("trace", 1e-6), ("none", 1e-4)):
+        X, _ = oracle.inv_quarter_root(A, eps, normalize)
+        Xmp = _to_np(_mp_root(A, eps, normalize))
+        assert oracle.relative_frobenius(X, Xmp) < 1e-13
+
+
+def test_full_step_bruteforce_mpmath():
+    """Three whole steps (EMA, trace rescale, root, apply) of a 3×5 weight in
+    50-digit arithmetic, against the oracle."""
+    mpmath.mp.dps = 50
+    rng = np.random.default_rng(20)
+    grads = [rng.standard_normal((3, 5)).astype(np.float32).astype(np.float64) for _ in range(3)]
+    beta, eps = 0.95, 1e-6
+    res = list(oracle.run_sequence(grads, beta, eps))
+    L = mpmath.zeros(3, 3)
+    R = mpmath.zeros(5, 5)
+    b = mpmath.mpf(beta)
+    for t, G in enumerate(grads):
+        Gm = mpmath.matrix(G.tolist())
+        L = b * L + (1 - b) * (Gm * Gm.T)
+        R = b * R + (1 - b) * (Gm.T * Gm)
+        XL = _mp_root(np.array([[float(L[i, j]) for j in range(3)] for i in range(3)]), eps, "trace")
+        XR = _mp_root(np.array([[float(R[i, j]) for j in range(5)] for i in range(5)]), eps, "trace")
+        U = XL * Gm * XR
+        _, Lo, Ro, XLo, XRo, Uo, flags = res[t]
+        assert flags == 0
+        assert oracle.relative_frobenius(Lo, _to_np(L)) < 1e-14
+        assert oracle.relative_frobenius(XLo, _to_np(XL)) < 1e-12
+        assert oracle.relative_frobenius(XRo, _to_np(XR)) < 1e-10  # R has rank 3 of 5
+        assert oracle.relative_frobenius(Uo, _to_np(U)) < 1e-10
+
+
+# -------------------------------------------------------- step-1 SVD form
+@pytest.mark.parametrize("m,n", [(6, 9), (9, 6), (8, 8)])
+@pytest.mark.parametrize("beta", [0.95, 0.0])
+def test_step1_svd_form(m, n, beta):
+    """From zero state, step 1 gives U = sum_i s_i (s_i^2/t + eps)^(-1/2) u_i v_i^T
+    with t = ||G||_F^2 (G = U S V^T by LAPACK gesdd, independent of eigh).
+    With beta = 0 every step is such a step 1."""
+    rng = np.random.default_rng(30)
+    eps = 1e-4
+    grads = [rng.standard_normal((m, n)) for _ in range(3)]
+    res = list(oracle.run_sequence(grads, beta, eps))
+    steps = range(3) if beta == 0.0 else range(1)
+    for t in steps:
+        G = grads[t]
+        Us, s, Vt = np.linalg.svd(G, full_matrices=False)
+        tt = np.sum(G * G)
+        Uexp = (Us * (s * (s * s / tt + eps) ** -0.5)) @ Vt
+        assert oracle.relative_frobenius(res[t][5], Uexp) < 1e-12
+
+
+def test_step1_polar_limit():
+    """As eps -> 0 the step-1 direction tends to ||G||_F · polar(G)."""
+    rng = np.random.default_rng(31)
+    G = rng.standard_normal((5, 7))
+    _, _, _, _, U, _ = oracle.preconditioner_step(np.zeros((5, 5)), np.zeros((7, 7)), G, 0.9, 1e-14)
+    Us, s, Vt = np.linalg.svd(G, full_matrices=False)
+    polar = Us @ Vt
+    assert oracle.relative_frobenius(U, np.linalg.norm(G) * polar) < 1e-5
+
+
+# ---------------------------------------------------------------- invariants
+def _toy_grams(steps=3):
+    grads = [workloads.gradient("toy", 0, t) for t in range(1, steps + 1)]
+    out = list(oracle.run_sequence(grads, 0.95, 1e-6))
+    return out
+
+
+def test_inverse_root_invariants():
+    """X symmetric, commutes with Â, X^4 (Â + eps I) = I, spectrum inside
+    [(1+eps)^(-1/4), eps^(-1/4)] for a trace-normalised PSD Gram (the explicit
+    residual of the OKLS page, appendix E)."""
+    eps = 1e-6
+    for t, L, R, XL, XR, U, flags in _toy_grams(4):
+        for S, X in ((L, XL), (R, XR)):
+            Ahat = S / np.trace(S)
+            B = Ahat + eps * np.eye(S.shape[0])
+            assert np.array_equal(X, X.T)
+            assert np.linalg.norm(X @ Ahat - Ahat @ X) <= 1e-9 * np.linalg.norm(X)
+            X2 = X @ X
+            res = np.linalg.norm(X2 @ X2 @ B - np.eye(S.shape[0]))
+            assert res < 1e-8, res
+            w = np.linalg.eigvalsh(X)
+            assert w.min() >= (1 + eps) ** -0.25 * (1 - 1e-12)
+            assert w.max() <= eps ** -0.25 * (1 + 1e-9)  # fp64 Gram eigenvalues ~ -1e-17
+
+
+def _coupled_newton_p4(B, iters=60):
+    """Coupled Newton for B^(-1/4) in fp64: X <- X T, M <- T^4 M, T = (5I - M)/4,
+    from M = B/c, X = I, c = ||B||_F >= lambda_max.  Written here, independent
+    of the HIP path's host code and kernels."""
+    d = B.shape[0]
+    c = np.linalg.norm(B)
+    M = B / c
+    X = np.eye(d)
+    I = np.eye(d)
+    for _ in range(iters):
+        T = (5.0 * I - M) / 4.0
+        X = X @ T
+        T2 = T @ T
+        M = T2 @ T2 @ M
+    return X * c ** -0.25
+
+
+def test_second_method_coupled_newton_fp64():
+    eps = 1e-6
+    for t, L, R, XL, XR, U, flags in _toy_grams(2):
+        for S, X in ((L, XL), (R, XR)):
+            B = S / np.trace(S) + eps * np.eye(S.shape[0])
+            Xn = _coupled_newton_p4(B)
+            assert oracle.relative_frobenius(X, Xn) < 1e-9
+    rng = workloads.rng_for(99, 0)
+    A = workloads.spd_loguniform(48, rng, -6.0, 0.0).astype(np.float64)
+    for eps in (1e-6, 1e-4):
+        X, info = oracle.inv_quarter_root(A, eps, normalize="none")
+        Xn = _coupled_newton_p4(A + eps * np.eye(48))
+        assert oracle.relative_frobenius(X, Xn) < 1e-9
+
+
+# --------------------------------------------------------------- equivariance
+def test_power_of_two_scaling_is_exact():
+    rng = np.random.default_rng(40)
+    grads = [rng.standard_normal((6, 10)) for _ in range(3)]
+    a = list(oracle.run_sequence(grads, 0.95, 1e-6))
+    b = list(oracle.run_sequence([8.0 * g for g in grads], 0.95, 1e-6))
+    for ra, rb in zip(a, b):
+        assert np.array_equal(ra[3], rb[3]) and np.array_equal(ra[4], rb[4])
+        assert np.array_equal(8.0 * ra[5], rb[5])
+
+
+def test_permutation_equivariance():
+    rng = np.random.default_rng(41)
+    m, n = 7, 11
+    grads = [rng.standard_normal((m, n)) for _ in range(3)]
+    P = np.eye(m)[rng.permutation(m)]
+    Q = np.eye(n)[rng.permutation(n)]
+    a = list(oracle.run_sequence(grads, 0.9, 1e-5))
+    b = list(oracle.run_sequence([P @ g @ Q.T for g in grads], 0.9, 1e-5))
+    for ra, rb in zip(a, b):
+        # R has rank 7 of 11 (condition ~1/eps): rounding of the eigensolver
+        assert oracle.relative_frobenius(rb[3], P @ ra[3] @ P.T) < 1e-10
+        assert oracle.relative_frobenius(rb[4], Q @ ra[4] @ Q.T) < 1e-10
+        assert oracle.relative_frobenius(rb[5], P @ ra[5] @ Q.T) < 1e-10
+
+
+def test_left_right_orientation():
+    """L is m×m, R is n×n, U has G's shape; swapping them breaks the SVD form."""
+    rng = np.random.default_rng(42)
+    G = rng.standard_normal((3, 8))
+    L, R, XL, XR, U, _ = oracle.preconditioner_step(np.zeros((3, 3)), np.zeros((8, 8)), G, 0.5, 1e-6)
+    assert L.shape == (3, 3) and R.shape == (8, 8) and U.shape == (3, 8)
+
+
+# ------------------------------------------------------------ special cases
+def test_flags():
+    eps = 1e-6
+    d = 5
+    X, info = oracle.inv_quarter_root(np.zeros((d, d)), eps)
+    assert info["flags"] == oracle.FLAG_ZERO_TRACE
+    np.testing.assert_allclose(X, eps ** -0.25 * np.eye(d))
+    A = np.eye(d)
+    A[1, 2] = np.nan
+    X, info = oracle.inv_quarter_root(A, eps)
+    assert info["flags"] == oracle.FLAG_NONFINITE and np.isnan(X).all()
+    A = np.diag([1.0, 0.5, -1e-3, 0.2, 0.1])
+    X, info = oracle.inv_quarter_root(A, eps, normalize="none")
+    assert info["flags"] == oracle.FLAG_NOT_PD
+    X, info = oracle.inv_quarter_root(A, 1e-2, normalize="none")
+    assert info["flags"] == 0
+
+
+def test_input_symmetric_part():
+    """The root reads the symmetric part of its input."""
+    rng = np.random.default_rng(43)
+    B = rng.standard_normal((6, 6))
+    S = B @ B.T
+    K = rng.standard_normal((6, 6))
+    K = K - K.T
+    X1, _ = oracle.inv_quarter_root(S, 1e-4)
+    X2, _ = oracle.inv_quarter_root(S + 0.1 * K, 1e-4)
+    np.testing.assert_allclose(X1, X2, rtol=1e-13, atol=1e-13)
