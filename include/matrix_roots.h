@@ -1,0 +1,213 @@
+/*
+ * matrix_roots.h -- C ABI of the MI355X (gfx950) EMA-Gram quarter-power
+ * preconditioner step.
+ *
+ * The step, per linear weight with gradient G (m x n), is the one described
+ * on marin.community, "Sharding EMA-Gram eigensolves", section "Background":
+ * keep exponential moving averages of G*G^T (left Gram, m x m) and of G^T*G
+ * (right Gram, n x n), rescale them, take the inverse quarter power of each
+ * rescaled Gram with a small regulariser added to its eigenvalues, and use the
+ * two quarter powers to shape the update direction U = L^(-1/4) * G * R^(-1/4)
+ * (the two-sided Shampoo form of tilderesearch, "Online KL Shampoo",
+ * section 1).  Each Gram's root needs only that Gram (same page, section
+ * "Approach"), so all calls are batched over independent problems.
+ *
+ * Conventions for every entry point:
+ *  - Matrix pointers are DEVICE pointers, row-major, element (i, j) at
+ *    ptr[i * ld + j]; ld >= number of columns.  Problem arrays (the structs)
+ *    are HOST memory, read only during the call.
+ *  - The caller owns every device buffer, including the workspace.  The
+ *    library keeps no pointer after returning and allocates nothing on the
+ *    device.  All work is enqueued on `hip_stream` (a hipStream_t passed as
+ *    void*; NULL = the null stream); nothing is waited for, except where an
+ *    entry point says so.
+ *  - Validation is all-or-nothing and happens before anything is enqueued:
+ *    on an error status nothing was enqueued and mr_last_error_message()
+ *    (thread-local) says what was wrong.
+ *  - Numerical outcomes are never return codes: they go to per-matrix
+ *    mr_root_info records in device memory that the caller reads after its
+ *    own synchronisation.
+ *  - Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef MATRIX_ROOTS_H
+#define MATRIX_ROOTS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MR_ABI_VERSION 1
+
+typedef int32_t mr_status;
+#define MR_OK 0
+#define MR_ERR_NULL 1        /* a required pointer is NULL                      */
+#define MR_ERR_SHAPE 2       /* a size is <= 0, too large, or sizes disagree    */
+#define MR_ERR_STRIDE 3      /* a leading dimension is smaller than the columns */
+#define MR_ERR_PARAM 4       /* a scalar parameter or enum is out of range      */
+#define MR_ERR_WORKSPACE 5   /* workspace NULL, too small or misaligned         */
+#define MR_ERR_HIP 6         /* the HIP runtime reported an error               */
+#define MR_ERR_UNSUPPORTED 7 /* valid request the library does not implement    */
+#define MR_ERR_ALIAS 8       /* an output overlaps an input it must not alias   */
+
+typedef int32_t mr_dtype;
+#define MR_F32 0
+#define MR_F64 1
+
+/* gram_ema_update: which Grams to update (bit mask) */
+#define MR_LEFT 1
+#define MR_RIGHT 2
+
+/* inv_quarter_root_batched: rescale mode */
+#define MR_NORM_NONE 0  /* s = 1                                  */
+#define MR_NORM_TRACE 1 /* s = trace(A): the rescaled Gram has trace 1 */
+
+/* inv_quarter_root_batched: method */
+#define MR_AUTO 0   /* Jacobi for d <= 128, coupled Newton above             */
+#define MR_JACOBI 1 /* eigendecomposition in LDS (d <= 128 only)             */
+#define MR_NEWTON 2 /* GEMM-only coupled Newton inverse 4th root             */
+#define MR_NEWTON_F64 3 /* the same iteration with every step in float64       */
+
+/* mr_root_info.flags */
+#define MR_INFO_NONFINITE 1     /* A held NaN or Inf; X is all NaN                          */
+#define MR_INFO_ZERO_TRACE 2    /* trace(A) == 0 under MR_NORM_TRACE; X = eps^(-1/4) * I    */
+#define MR_INFO_NOT_PD 4        /* Jacobi: an eigenvalue + eps <= 0; Newton: no usable bound;
+                                   X is all NaN                                              */
+#define MR_INFO_NOT_CONVERGED 8 /* Jacobi: still rotating after 30 sweeps; Newton: residual
+                                   above 2e-3 * sqrt(d) (e.g. A + eps I not positive definite) */
+
+/* One weight for gram_ema_update.  G: m x n float32 (ldg >= n).
+ * L: m x m, R: n x n, both of the call's state dtype (ldl >= m, ldr >= n),
+ * full symmetric storage, updated in place.  L (R) may be NULL when the
+ * MR_LEFT (MR_RIGHT) bit is not requested. */
+typedef struct {
+  int64_t m, n;
+  const float* G;
+  int64_t ldg;
+  void* L;
+  int64_t ldl;
+  void* R;
+  int64_t ldr;
+} mr_gram_problem;
+
+/* One matrix for inv_quarter_root_batched.  A: d x d of the call's a_dtype
+ * (symmetric; its symmetric part (A + A^T)/2 is what is used), lda >= d.
+ * X: d x d float32 output, ldx >= d; X must not overlap A. */
+typedef struct {
+  int64_t d;
+  const void* A;
+  int64_t lda;
+  float* X;
+  int64_t ldx;
+} mr_root_problem;
+
+/* Per-matrix outcome of inv_quarter_root_batched (device memory, written by
+ * the call).  32 bytes. */
+typedef struct {
+  double scale;       /* s: trace(A) (MR_NORM_TRACE) or 1                        */
+  double bound;       /* c >= lambda_max(A/s + eps I) (Newton); 0 for Jacobi      */
+  int32_t iters;      /* Newton iterations run, or Jacobi sweeps                  */
+  int32_t fp64_iters; /* of those Newton iterations, the ones run in float64      */
+  float residual;     /* Newton: ||M_{K-1} - I||_F, the iterate the last X update
+                         used; Jacobi: off-diagonal Frobenius norm of the
+                         rotated A/s at exit                                      */
+  uint32_t flags;     /* MR_INFO_* bits                                           */
+} mr_root_info;
+
+/* One weight for precondition_apply.  XL: m x m, G: m x n, XR: n x n, U: m x n,
+ * all float32.  U must not overlap XL, G or XR. */
+typedef struct {
+  int64_t m, n;
+  const float* XL;
+  int64_t ldxl;
+  const float* G;
+  int64_t ldg;
+  const float* XR;
+  int64_t ldxr;
+  float* U;
+  int64_t ldu;
+} mr_apply_problem;
+
+/*
+ * gram_ema_update -- for every problem, in place:
+ *     L <- beta * L + (1 - beta) * G * G^T   (if sides & MR_LEFT)
+ *     R <- beta * R + (1 - beta) * G^T * G   (if sides & MR_RIGHT)
+ * The EMA of gradient products of the EMA-Gram page, section "Background";
+ * the weighting convention (beta on the old state, no bias correction) is the
+ * plain reading of that passage.  Products of float32 entries are formed and
+ * summed in float64 on the float64 matrix cores, whatever the state dtype;
+ * a float32 state receives the float64 result rounded once.
+ * state_dtype: MR_F32 or MR_F64.  beta in [0, 1) (double, so that 1 - beta
+ * carries no float32 rounding into a float64 state).  count >= 1 (0 is a no-op).
+ * G must not overlap L or R.
+ * Workspace: none needed (ws may be NULL, ws_bytes 0).
+ */
+mr_status gram_ema_update(const mr_gram_problem* problems, int32_t count, mr_dtype state_dtype,
+                          double beta, uint32_t sides, void* ws, size_t ws_bytes, void* hip_stream);
+size_t gram_ema_update_workspace(const mr_gram_problem* problems, int32_t count,
+                                 mr_dtype state_dtype, uint32_t sides);
+
+/*
+ * inv_quarter_root_batched -- for every problem:
+ *     X = (A/s + eps * I)^(-1/4),  s = trace(A) (MR_NORM_TRACE) or 1 (MR_NORM_NONE)
+ * The regularised inverse quarter power of the rescaled Gram (EMA-Gram page,
+ * section "Background": rescale, add a small regulariser to the eigenvalues,
+ * raise them to -1/4, rebuild).  X is symmetric to the last bit.
+ * Methods:
+ *  - MR_JACOBI (d <= 128): cyclic Jacobi eigendecomposition of A/s in float64,
+ *    one workgroup per matrix with A held in LDS; f = (lambda + eps)^(-1/4);
+ *    X = V f V^T.
+ *  - MR_NEWTON: coupled Newton iteration for the inverse 4th root,
+ *        M0 = (A/s + eps I)/c, X0 = I, T = (5 I - M)/4, X <- X T, M <- T^4 M,
+ *    X = c^(-1/4) X_K, run in float64 while the smallest eigenvalue of M is
+ *    below 1e-2 (by the scalar recurrence), then in float32.  The GEMM-only
+ *    route of tilderesearch, "Online KL Shampoo", sections 2.1-2.2 (there
+ *    for the -1/2 root), taken to the 4th root.  c = 1.01 times the
+ *    Wolkowicz-Styan upper bound on lambda_max(A/s + eps I) (the OKLS page,
+ *    appendix D, normalises by an O(d^2) upper bound in the same way); the
+ *    iteration count follows from eps/c.  The last iteration updates X only.
+ *  - MR_NEWTON_F64: the Newton iteration with every step in float64 (twice
+ *    the cost of the float32 phase; for inputs near the float32 limit).
+ *  - MR_AUTO: Jacobi for d <= 128, Newton otherwise.
+ * a_dtype: MR_F32 or MR_F64.  eps > 0 and finite.  info_dev: device array of
+ * `count` records (may be NULL).  MR_NORM_NONE with any Newton problem
+ * synchronises hip_stream once (the iteration count depends on the bounds
+ * computed on the device); MR_NORM_TRACE never synchronises.
+ * Workspace: at least inv_quarter_root_batched_workspace(...) bytes, 256-byte
+ * aligned; its contents on entry are ignored.
+ */
+mr_status inv_quarter_root_batched(const mr_root_problem* problems, int32_t count,
+                                   mr_dtype a_dtype, double eps, int32_t normalize, int32_t method,
+                                   mr_root_info* info_dev, void* ws, size_t ws_bytes,
+                                   void* hip_stream);
+size_t inv_quarter_root_batched_workspace(const mr_root_problem* problems, int32_t count,
+                                          mr_dtype a_dtype, int32_t method);
+
+/*
+ * precondition_apply -- for every problem:  U = alpha * XL * G * XR
+ * The two-sided application of the quarter powers (EMA-Gram page, section
+ * "Background"; Shampoo form of the OKLS page, section 1).  float32 matrix
+ * cores; the intermediate (G * XR)^T lives in the workspace.
+ * Workspace: at least precondition_apply_workspace(...) bytes, 256-byte aligned.
+ */
+mr_status precondition_apply(const mr_apply_problem* problems, int32_t count, float alpha,
+                             void* ws, size_t ws_bytes, void* hip_stream);
+size_t precondition_apply_workspace(const mr_apply_problem* problems, int32_t count);
+
+/* Iteration count of the coupled Newton p-th root iteration for a smallest
+ * normalised eigenvalue m0 in (0, 1]: the number of steps of the scalar map
+ * m <- m * ((p + 1 - m) / p)^p until 1 - m <= tol (the map every eigenvalue
+ * of M follows).  p in {2, 4}.  Host-only; returns -1 on bad arguments. */
+int32_t mr_newton_iterations(int32_t p, double m0, double tol);
+
+const char* mr_status_string(mr_status status);
+const char* mr_last_error_message(void);
+int32_t mr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MATRIX_ROOTS_H */

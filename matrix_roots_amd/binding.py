@@ -1,0 +1,247 @@
+"""ctypes binding of libmatrix_roots.so (include/matrix_roots.h).
+
+Argument marshalling only: torch tensors provide device memory and the
+current stream; every step of the computation runs in the library's HIP
+kernels.  A missing library raises; there is no other code path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmatrix_roots.so")
+
+MR_OK = 0
+MR_F32, MR_F64 = 0, 1
+MR_LEFT, MR_RIGHT = 1, 2
+MR_NORM_NONE, MR_NORM_TRACE = 0, 1
+MR_AUTO, MR_JACOBI, MR_NEWTON, MR_NEWTON_F64 = 0, 1, 2, 3
+MR_INFO_NONFINITE, MR_INFO_ZERO_TRACE, MR_INFO_NOT_PD, MR_INFO_NOT_CONVERGED = 1, 2, 4, 8
+
+_METHODS = {"auto": MR_AUTO, "jacobi": MR_JACOBI, "newton": MR_NEWTON, "newton_f64": MR_NEWTON_F64}
+_NORMS = {"none": MR_NORM_NONE, "trace": MR_NORM_TRACE}
+
+EXPORTED = (
+    "gram_ema_update",
+    "gram_ema_update_workspace",
+    "inv_quarter_root_batched",
+    "inv_quarter_root_batched_workspace",
+    "precondition_apply",
+    "precondition_apply_workspace",
+    "mr_newton_iterations",
+    "mr_status_string",
+    "mr_last_error_message",
+    "mr_abi_version",
+)
+
+
+class GramProblem(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("G", ctypes.c_void_p), ("ldg", ctypes.c_int64),
+                ("L", ctypes.c_void_p), ("ldl", ctypes.c_int64), ("R", ctypes.c_void_p), ("ldr", ctypes.c_int64)]
+
+
+class RootProblem(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int64), ("A", ctypes.c_void_p), ("lda", ctypes.c_int64), ("X", ctypes.c_void_p),
+                ("ldx", ctypes.c_int64)]
+
+
+class ApplyProblem(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("XL", ctypes.c_void_p), ("ldxl", ctypes.c_int64),
+                ("G", ctypes.c_void_p), ("ldg", ctypes.c_int64), ("XR", ctypes.c_void_p), ("ldxr", ctypes.c_int64),
+                ("U", ctypes.c_void_p), ("ldu", ctypes.c_int64)]
+
+
+ROOT_INFO_DTYPE = np.dtype([("scale", "<f8"), ("bound", "<f8"), ("iters", "<i4"), ("fp64_iters", "<i4"),
+                            ("residual", "<f4"), ("flags", "<u4")])
+assert ROOT_INFO_DTYPE.itemsize == 32
+
+
+class MatrixRootsError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libmatrix_roots.so (built in-tree by matrix_roots_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m matrix_roots_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz, f32, f64, u32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                                      ctypes.c_float, ctypes.c_double, ctypes.c_uint32)
+    lib.gram_ema_update.argtypes = [vp, i32, i32, f64, u32, vp, sz, vp]
+    lib.gram_ema_update.restype = i32
+    lib.gram_ema_update_workspace.argtypes = [vp, i32, i32, u32]
+    lib.gram_ema_update_workspace.restype = sz
+    lib.inv_quarter_root_batched.argtypes = [vp, i32, i32, f64, i32, i32, vp, vp, sz, vp]
+    lib.inv_quarter_root_batched.restype = i32
+    lib.inv_quarter_root_batched_workspace.argtypes = [vp, i32, i32, i32]
+    lib.inv_quarter_root_batched_workspace.restype = sz
+    lib.precondition_apply.argtypes = [vp, i32, f32, vp, sz, vp]
+    lib.precondition_apply.restype = i32
+    lib.precondition_apply_workspace.argtypes = [vp, i32]
+    lib.precondition_apply_workspace.restype = sz
+    lib.mr_newton_iterations.argtypes = [i32, f64, f64]
+    lib.mr_newton_iterations.restype = i32
+    lib.mr_status_string.argtypes = [i32]
+    lib.mr_status_string.restype = ctypes.c_char_p
+    lib.mr_last_error_message.argtypes = []
+    lib.mr_last_error_message.restype = ctypes.c_char_p
+    lib.mr_abi_version.argtypes = []
+    lib.mr_abi_version.restype = i32
+    if lib.mr_abi_version() != 1:
+        raise RuntimeError("libmatrix_roots.so ABI version mismatch")
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != MR_OK:
+        lib = library()
+        raise MatrixRootsError(status, lib.mr_last_error_message().decode())
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _ld(t) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("matrices must be 2-D with unit column stride")
+    return int(t.stride(0))
+
+
+def _stream(stream) -> int:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _workspace(nbytes: int, device):
+    import torch
+
+    if nbytes == 0:
+        return None
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ API
+def gram_ema_update(grads: Sequence, lefts: Optional[Sequence], rights: Optional[Sequence], beta: float,
+                    stream=None):
+    """In place: L <- beta L + (1-beta) G G^T, R <- beta R + (1-beta) G^T G.
+
+    grads: float32 (m, n) device tensors; lefts / rights: (m, m) / (n, n)
+    float32 or float64 tensors of one dtype, or None to skip that side.
+    """
+    lib = library()
+    count = len(grads)
+    sides = (MR_LEFT if lefts is not None else 0) | (MR_RIGHT if rights is not None else 0)
+    states = [s for s in (lefts or []) + (rights or [])]
+    dts = {str(s.dtype) for s in states}
+    if len(dts) != 1:
+        raise ValueError("all Gram states must share one dtype")
+    dt = MR_F64 if dts.pop() == "torch.float64" else MR_F32
+    probs = (GramProblem * max(count, 1))()
+    for i, G in enumerate(grads):
+        L = lefts[i] if lefts is not None else None
+        R = rights[i] if rights is not None else None
+        probs[i] = GramProblem(G.shape[0], G.shape[1], _ptr(G), _ld(G), _ptr(L), _ld(L) if L is not None else 0,
+                               _ptr(R), _ld(R) if R is not None else 0)
+    _check(lib.gram_ema_update(ctypes.addressof(probs), count, dt, float(beta), sides, None, 0, _stream(stream)))
+
+
+class RootWorkspace:
+    """Reusable workspace + info buffer for inv_quarter_root_batched."""
+
+    def __init__(self):
+        self.buf = None
+        self.info = None
+
+    def get(self, nbytes: int, count: int, device):
+        import torch
+
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != torch.device(device):
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        if self.info is None or self.info.numel() < 32 * count or self.info.device != torch.device(device):
+            self.info = torch.empty(32 * max(count, 1), dtype=torch.uint8, device=device)
+        return self.buf, self.info
+
+
+def inv_quarter_root_batched(As: Sequence, eps: float, normalize: str = "trace", method: str = "auto",
+                             Xs: Optional[Sequence] = None, workspace: Optional[RootWorkspace] = None,
+                             stream=None, return_info: bool = True):
+    """X_i = (A_i/s_i + eps I)^(-1/4) for every (d, d) device tensor A_i.
+
+    Returns (Xs, info) where info is a numpy structured array (fields of
+    mr_root_info) read after synchronising the stream, or (Xs, None).
+    """
+    import torch
+
+    lib = library()
+    count = len(As)
+    if count == 0:
+        return [], None
+    dts = {str(a.dtype) for a in As}
+    if len(dts) != 1:
+        raise ValueError("all A must share one dtype")
+    dt = MR_F64 if dts.pop() == "torch.float64" else MR_F32
+    dev = As[0].device
+    if Xs is None:
+        Xs = [torch.empty(a.shape[0], a.shape[0], dtype=torch.float32, device=dev) for a in As]
+    probs = (RootProblem * count)()
+    for i, (A, X) in enumerate(zip(As, Xs)):
+        probs[i] = RootProblem(A.shape[0], _ptr(A), _ld(A), _ptr(X), _ld(X))
+    m = _METHODS[method]
+    need = lib.inv_quarter_root_batched_workspace(ctypes.addressof(probs), count, dt, m)
+    ws = workspace or RootWorkspace()
+    buf, info = ws.get(need, count, dev)
+    _check(lib.inv_quarter_root_batched(ctypes.addressof(probs), count, dt, float(eps), _NORMS[normalize], m,
+                                        _ptr(info), _ptr(buf), buf.numel(), _stream(stream)))
+    if not return_info:
+        return Xs, None
+    torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+    host = info[: 32 * count].cpu().numpy()
+    return Xs, host.view(ROOT_INFO_DTYPE).copy()
+
+
+def precondition_apply(XLs: Sequence, Gs: Sequence, XRs: Sequence, alpha: float = 1.0,
+                       Us: Optional[Sequence] = None, stream=None):
+    """U_i = alpha XL_i G_i XR_i (float32 device tensors).  Returns the Us."""
+    import torch
+
+    lib = library()
+    count = len(Gs)
+    if count == 0:
+        return []
+    dev = Gs[0].device
+    if Us is None:
+        Us = [torch.empty_like(G) for G in Gs]
+    probs = (ApplyProblem * count)()
+    for i in range(count):
+        XL, G, XR, U = XLs[i], Gs[i], XRs[i], Us[i]
+        probs[i] = ApplyProblem(G.shape[0], G.shape[1], _ptr(XL), _ld(XL), _ptr(G), _ld(G), _ptr(XR), _ld(XR),
+                                _ptr(U), _ld(U))
+    need = lib.precondition_apply_workspace(ctypes.addressof(probs), count)
+    ws = _workspace(need, dev)
+    if ws is not None and stream is not None:
+        ws.record_stream(stream)
+    _check(lib.precondition_apply(ctypes.addressof(probs), count, float(alpha), _ptr(ws), need, _stream(stream)))
+    return Us
+
+
+def newton_iterations(p: int, m0: float, tol: float) -> int:
+    return int(library().mr_newton_iterations(p, m0, tol))

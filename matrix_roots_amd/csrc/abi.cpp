@@ -1,0 +1,585 @@
+// Host runtime behind the C ABI of include/matrix_roots.h: argument
+// validation (all-or-nothing, before anything is enqueued), workspace layout,
+// work lists and launch order.  No device allocation, no descriptor copies:
+// per-problem tables travel in kernel arguments.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "launch.hpp"
+#include "schedule.hpp"
+
+using namespace mr;
+
+namespace {
+
+thread_local std::string g_err;
+
+mr_status fail(mr_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+mr_status hip_fail(hipError_t e, const char* where) {
+  return fail(MR_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxDim = 65536;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte range of a rows x cols row-major matrix with leading dimension ld.
+struct Range {
+  uintptr_t lo, hi;
+};
+Range range_of(const void* p, int64_t rows, int64_t cols, int64_t ld, size_t es) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return {lo, lo + (uintptr_t)(((rows - 1) * ld + cols) * (int64_t)es)};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* e = getenv("MR_DEBUG_SYNC");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
+// Check a launch; in debug mode also wait for it and report faults there.
+mr_status check_launch(hipError_t e, hipStream_t s, const char* what) {
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (debug_sync()) {
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, what);
+  }
+  return MR_OK;
+}
+
+int tiles(int64_t d, int t) { return (int)((d + t - 1) / t); }
+
+// ------------------------------------------------------------ root layout
+struct RootPlan {
+  // slot order: Newton matrices grouped by d (ascending), then Jacobi
+  std::vector<int> slot_problem;
+  int n_newton = 0;
+  struct Cls {
+    int64_t d;
+    int first_slot, count;
+    size_t region_off, matrix_bytes;
+  };
+  std::vector<Cls> classes;
+  size_t state_off = 0, partial_off = 0, jac_off = 0;
+  int64_t partial_stride = 0;
+  std::vector<size_t> jac_w_off;  // per Jacobi slot (index slot - n_newton)
+  size_t total = 0;
+};
+
+bool use_jacobi(int64_t d, int32_t method) {
+  return method == MR_JACOBI || (method == MR_AUTO && d <= kJacobiMaxD);
+}
+
+RootPlan plan_root(const mr_root_problem* p, int32_t count, int32_t method) {
+  RootPlan P;
+  std::map<int64_t, std::vector<int>> by_d;
+  std::vector<int> jac;
+  for (int i = 0; i < count; ++i) {
+    if (use_jacobi(p[i].d, method))
+      jac.push_back(i);
+    else
+      by_d[p[i].d].push_back(i);
+  }
+  int64_t dmax_newton = 0;
+  for (auto& kv : by_d) {
+    RootPlan::Cls c;
+    c.d = kv.first;
+    c.first_slot = (int)P.slot_problem.size();
+    c.count = (int)kv.second.size();
+    c.matrix_bytes = align256((size_t)40 * (size_t)c.d * (size_t)c.d);
+    for (int i : kv.second) P.slot_problem.push_back(i);
+    P.classes.push_back(c);
+    dmax_newton = std::max(dmax_newton, c.d);
+  }
+  P.n_newton = (int)P.slot_problem.size();
+  for (int i : jac) P.slot_problem.push_back(i);
+
+  size_t off = 0;
+  P.state_off = off;
+  off = align256(off + sizeof(RootState) * (size_t)std::max(count, 1));
+  P.partial_stride = 3 * ((dmax_newton + kStatsRows - 1) / kStatsRows);
+  P.partial_stride = std::max<int64_t>(P.partial_stride, 1);
+  P.partial_off = off;
+  off = align256(off + sizeof(double) * (size_t)P.partial_stride * (size_t)std::max(P.n_newton, 1));
+  P.jac_off = off;
+  for (size_t k = 0; k < jac.size(); ++k) {
+    P.jac_w_off.push_back(off);
+    const int64_t d = p[jac[k]].d;
+    off = align256(off + sizeof(double) * (size_t)d * (size_t)d);
+  }
+  for (auto& c : P.classes) {
+    c.region_off = off;
+    off += c.matrix_bytes * (size_t)c.count;
+  }
+  P.total = off;
+  return P;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mr_abi_version(void) { return MR_ABI_VERSION; }
+
+const char* mr_last_error_message(void) { return g_err.c_str(); }
+
+const char* mr_status_string(mr_status s) {
+  switch (s) {
+    case MR_OK: return "MR_OK";
+    case MR_ERR_NULL: return "MR_ERR_NULL: a required pointer is NULL";
+    case MR_ERR_SHAPE: return "MR_ERR_SHAPE: invalid or inconsistent size";
+    case MR_ERR_STRIDE: return "MR_ERR_STRIDE: leading dimension smaller than the column count";
+    case MR_ERR_PARAM: return "MR_ERR_PARAM: scalar parameter or enum out of range";
+    case MR_ERR_WORKSPACE: return "MR_ERR_WORKSPACE: workspace missing, too small or misaligned";
+    case MR_ERR_HIP: return "MR_ERR_HIP: HIP runtime error";
+    case MR_ERR_UNSUPPORTED: return "MR_ERR_UNSUPPORTED: request not implemented";
+    case MR_ERR_ALIAS: return "MR_ERR_ALIAS: output overlaps an input";
+    default: return "unknown mr_status";
+  }
+}
+
+int32_t mr_newton_iterations(int32_t p, double m0, double tol) {
+  if (!(p == 2 || p == 4) || !(m0 > 0.0 && m0 <= 1.0) || !(tol > 0.0 && tol < 1.0)) return -1;
+  double m = m0;
+  int k = 0;
+  while (1.0 - m > tol && k < 100000) {
+    m = newton_scalar_step(p, m);
+    ++k;
+  }
+  return k;
+}
+
+// ======================================================== gram_ema_update
+static mr_status validate_gram(const mr_gram_problem* p, int32_t count, mr_dtype dt, double beta, uint32_t sides) {
+  if (count < 0) return fail(MR_ERR_PARAM, "count %d < 0", count);
+  if (count > 0 && !p) return fail(MR_ERR_NULL, "problems is NULL");
+  if (dt != MR_F32 && dt != MR_F64) return fail(MR_ERR_PARAM, "state_dtype %d is not MR_F32 or MR_F64", dt);
+  if (!(beta >= 0.0 && beta < 1.0)) return fail(MR_ERR_PARAM, "beta %g not in [0, 1)", beta);
+  if (sides == 0 || (sides & ~(uint32_t)(MR_LEFT | MR_RIGHT)))
+    return fail(MR_ERR_PARAM, "sides 0x%x must be a non-empty subset of MR_LEFT|MR_RIGHT", sides);
+  const size_t es = dt == MR_F64 ? 8 : 4;
+  for (int i = 0; i < count; ++i) {
+    const mr_gram_problem& q = p[i];
+    if (q.m < 1 || q.n < 1 || q.m > kMaxDim || q.n > kMaxDim)
+      return fail(MR_ERR_SHAPE, "problem %d: m=%lld n=%lld outside [1, %lld]", i, (long long)q.m, (long long)q.n,
+                  (long long)kMaxDim);
+    if (!q.G) return fail(MR_ERR_NULL, "problem %d: G is NULL", i);
+    if (q.ldg < q.n) return fail(MR_ERR_STRIDE, "problem %d: ldg %lld < n %lld", i, (long long)q.ldg, (long long)q.n);
+    if (!aligned(q.G, 4)) return fail(MR_ERR_PARAM, "problem %d: G not 4-byte aligned", i);
+    const Range rg = range_of(q.G, q.m, q.n, q.ldg, 4);
+    Range rl{0, 0}, rr{0, 0};
+    if (sides & MR_LEFT) {
+      if (!q.L) return fail(MR_ERR_NULL, "problem %d: L is NULL", i);
+      if (q.ldl < q.m) return fail(MR_ERR_STRIDE, "problem %d: ldl %lld < m %lld", i, (long long)q.ldl, (long long)q.m);
+      if (!aligned(q.L, es)) return fail(MR_ERR_PARAM, "problem %d: L misaligned for its dtype", i);
+      rl = range_of(q.L, q.m, q.m, q.ldl, es);
+      if (overlap(rl, rg)) return fail(MR_ERR_ALIAS, "problem %d: L overlaps G", i);
+    }
+    if (sides & MR_RIGHT) {
+      if (!q.R) return fail(MR_ERR_NULL, "problem %d: R is NULL", i);
+      if (q.ldr < q.n) return fail(MR_ERR_STRIDE, "problem %d: ldr %lld < n %lld", i, (long long)q.ldr, (long long)q.n);
+      if (!aligned(q.R, es)) return fail(MR_ERR_PARAM, "problem %d: R misaligned for its dtype", i);
+      rr = range_of(q.R, q.n, q.n, q.ldr, es);
+      if (overlap(rr, rg)) return fail(MR_ERR_ALIAS, "problem %d: R overlaps G", i);
+    }
+    if ((sides & MR_LEFT) && (sides & MR_RIGHT) && overlap(rl, rr))
+      return fail(MR_ERR_ALIAS, "problem %d: L overlaps R", i);
+  }
+  return MR_OK;
+}
+
+size_t gram_ema_update_workspace(const mr_gram_problem*, int32_t, mr_dtype, uint32_t) { return 0; }
+
+mr_status gram_ema_update(const mr_gram_problem* p, int32_t count, mr_dtype dt, double beta, uint32_t sides, void* ws,
+                          size_t ws_bytes, void* hip_stream) {
+  (void)ws;
+  (void)ws_bytes;
+  mr_status st = validate_gram(p, count, dt, beta, sides);
+  if (st != MR_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  for (int side = 0; side < 2; ++side) {
+    const bool right = side == 1;
+    if (!(sides & (right ? MR_RIGHT : MR_LEFT))) continue;
+    for (int vecpass = 0; vecpass < 2; ++vecpass) {
+      const int vec = vecpass == 0 ? 4 : 1;
+      SyrkBatch b;
+      memset(&b, 0, sizeof b);
+      b.alpha = 1.0 - beta;
+      b.beta = beta;
+      auto flush = [&]() -> mr_status {
+        if (b.njobs == 0) return MR_OK;
+        mr_status r = check_launch(launch_syrk_ema(b, right, dt == MR_F64, vec, s), s, "gram_ema_update launch");
+        b.njobs = 0;
+        b.total_blocks = 0;
+        return r;
+      };
+      for (int i = 0; i < count; ++i) {
+        const mr_gram_problem& q = p[i];
+        const int64_t d = right ? q.n : q.m;
+        const int64_t K = right ? q.m : q.n;
+        // float4 loads: along columns of G (k for the left Gram, i for the right one)
+        const bool v4 = (q.n % 4 == 0) && (q.ldg % 4 == 0) && aligned(q.G, 16);
+        if ((vec == 4) != v4) continue;
+        SyrkJob& J = b.job[b.njobs];
+        J.G = q.G;
+        J.ldg = q.ldg;
+        J.S = right ? q.R : q.L;
+        J.lds = right ? q.ldr : q.ldl;
+        J.d = (int32_t)d;
+        J.K = (int32_t)K;
+        J.T = tiles(d, 128);
+        J.block_begin = b.total_blocks;
+        b.total_blocks += J.T * (J.T + 1) / 2;
+        ++b.njobs;
+        if (b.njobs == kMaxJobs && (st = flush()) != MR_OK) return st;
+      }
+      if ((st = flush()) != MR_OK) return st;
+    }
+  }
+  return MR_OK;
+}
+
+// ===================================================== precondition_apply
+static mr_status validate_apply(const mr_apply_problem* p, int32_t count, float alpha) {
+  if (count < 0) return fail(MR_ERR_PARAM, "count %d < 0", count);
+  if (count > 0 && !p) return fail(MR_ERR_NULL, "problems is NULL");
+  if (!std::isfinite(alpha)) return fail(MR_ERR_PARAM, "alpha is not finite");
+  for (int i = 0; i < count; ++i) {
+    const mr_apply_problem& q = p[i];
+    if (q.m < 1 || q.n < 1 || q.m > kMaxDim || q.n > kMaxDim)
+      return fail(MR_ERR_SHAPE, "problem %d: m=%lld n=%lld outside [1, %lld]", i, (long long)q.m, (long long)q.n,
+                  (long long)kMaxDim);
+    if (!q.XL || !q.G || !q.XR || !q.U) return fail(MR_ERR_NULL, "problem %d: NULL matrix pointer", i);
+    if (q.ldxl < q.m || q.ldg < q.n || q.ldxr < q.n || q.ldu < q.n)
+      return fail(MR_ERR_STRIDE, "problem %d: a leading dimension is smaller than its column count", i);
+    if (!aligned(q.XL, 4) || !aligned(q.G, 4) || !aligned(q.XR, 4) || !aligned(q.U, 4))
+      return fail(MR_ERR_PARAM, "problem %d: a matrix is not 4-byte aligned", i);
+    const Range ru = range_of(q.U, q.m, q.n, q.ldu, 4);
+    if (overlap(ru, range_of(q.XL, q.m, q.m, q.ldxl, 4)) || overlap(ru, range_of(q.G, q.m, q.n, q.ldg, 4)) ||
+        overlap(ru, range_of(q.XR, q.n, q.n, q.ldxr, 4)))
+      return fail(MR_ERR_ALIAS, "problem %d: U overlaps XL, G or XR", i);
+  }
+  return MR_OK;
+}
+
+size_t precondition_apply_workspace(const mr_apply_problem* p, int32_t count) {
+  if (!p || count <= 0) return 0;
+  size_t tot = 0;
+  for (int i = 0; i < count; ++i)
+    if (p[i].m > 0 && p[i].n > 0) tot += align256((size_t)p[i].m * (size_t)p[i].n * 4);
+  return tot;
+}
+
+mr_status precondition_apply(const mr_apply_problem* p, int32_t count, float alpha, void* ws, size_t ws_bytes,
+                             void* hip_stream) {
+  mr_status st = validate_apply(p, count, alpha);
+  if (st != MR_OK) return st;
+  if (count == 0) return MR_OK;
+  const size_t need = precondition_apply_workspace(p, count);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(MR_ERR_WORKSPACE, "workspace %p of %zu bytes; need %zu bytes, 256-byte aligned", ws, ws_bytes, need);
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  std::vector<float*> wt(count);
+  size_t off = 0;
+  for (int i = 0; i < count; ++i) {
+    wt[i] = reinterpret_cast<float*>(static_cast<char*>(ws) + off);
+    off += align256((size_t)p[i].m * (size_t)p[i].n * 4);
+  }
+  auto v4ok = [](const float* ptr, int64_t ld, int64_t K) { return aligned(ptr, 16) && ld % 4 == 0 && K % 4 == 0; };
+  for (int stage = 0; stage < 2; ++stage) {
+    for (int vecpass = 0; vecpass < 2; ++vecpass) {
+      const int vec = vecpass == 0 ? 4 : 1;
+      F32Batch b;
+      memset(&b, 0, sizeof b);
+      auto flush = [&]() -> mr_status {
+        if (b.njobs == 0) return MR_OK;
+        mr_status r = check_launch(launch_f32_nt(b, vec, s), s, "precondition_apply launch");
+        b.njobs = 0;
+        b.total_blocks = 0;
+        return r;
+      };
+      for (int i = 0; i < count; ++i) {
+        const mr_apply_problem& q = p[i];
+        F32Job J;
+        if (stage == 0) {  // W^T = XR * G^T : (n x m)
+          J.A = q.XR; J.lda = q.ldxr;
+          J.B = q.G; J.ldb = q.ldg;
+          J.C = wt[i]; J.ldc = q.m;
+          J.M = (int32_t)q.n; J.N = (int32_t)q.m; J.K = (int32_t)q.n;
+          J.alpha = 1.f;
+        } else {  // U = alpha * XL * W
+          J.A = q.XL; J.lda = q.ldxl;
+          J.B = wt[i]; J.ldb = q.m;
+          J.C = q.U; J.ldc = q.ldu;
+          J.M = (int32_t)q.m; J.N = (int32_t)q.n; J.K = (int32_t)q.m;
+          J.alpha = alpha;
+        }
+        const bool v4 = v4ok(J.A, J.lda, J.K) && v4ok(J.B, J.ldb, J.K);
+        if ((vec == 4) != v4) continue;
+        const int tm = tiles(J.M, 128), tn = tiles(J.N, 128);
+        J.tiles_n = tn;
+        J.block_begin = b.total_blocks;
+        b.job[b.njobs++] = J;
+        b.total_blocks += tm * tn;
+        if (b.njobs == kMaxJobs && (st = flush()) != MR_OK) return st;
+      }
+      if ((st = flush()) != MR_OK) return st;
+    }
+  }
+  return MR_OK;
+}
+
+// ================================================ inv_quarter_root_batched
+static mr_status validate_root(const mr_root_problem* p, int32_t count, mr_dtype dt, double eps, int32_t normalize,
+                               int32_t method) {
+  if (count < 0) return fail(MR_ERR_PARAM, "count %d < 0", count);
+  if (count > 0 && !p) return fail(MR_ERR_NULL, "problems is NULL");
+  if (dt != MR_F32 && dt != MR_F64) return fail(MR_ERR_PARAM, "a_dtype %d is not MR_F32 or MR_F64", dt);
+  if (!(eps > 0.0) || !std::isfinite(eps)) return fail(MR_ERR_PARAM, "eps %g must be positive and finite", eps);
+  if (normalize != MR_NORM_NONE && normalize != MR_NORM_TRACE)
+    return fail(MR_ERR_PARAM, "normalize %d is not MR_NORM_NONE or MR_NORM_TRACE", normalize);
+  if (method != MR_AUTO && method != MR_JACOBI && method != MR_NEWTON && method != MR_NEWTON_F64)
+    return fail(MR_ERR_PARAM, "method %d unknown", method);
+  const size_t es = dt == MR_F64 ? 8 : 4;
+  for (int i = 0; i < count; ++i) {
+    const mr_root_problem& q = p[i];
+    if (q.d < 1 || q.d > kMaxDim)
+      return fail(MR_ERR_SHAPE, "problem %d: d=%lld outside [1, %lld]", i, (long long)q.d, (long long)kMaxDim);
+    if (!q.A || !q.X) return fail(MR_ERR_NULL, "problem %d: A or X is NULL", i);
+    if (q.lda < q.d || q.ldx < q.d) return fail(MR_ERR_STRIDE, "problem %d: lda or ldx < d", i);
+    if (!aligned(q.A, es) || !aligned(q.X, 4)) return fail(MR_ERR_PARAM, "problem %d: A or X misaligned", i);
+    if (overlap(range_of(q.A, q.d, q.d, q.lda, es), range_of(q.X, q.d, q.d, q.ldx, 4)))
+      return fail(MR_ERR_ALIAS, "problem %d: X overlaps A", i);
+    if (method == MR_JACOBI && q.d > kJacobiMaxD)
+      return fail(MR_ERR_UNSUPPORTED, "problem %d: MR_JACOBI supports d <= %d (d = %lld)", i, kJacobiMaxD,
+                  (long long)q.d);
+  }
+  return MR_OK;
+}
+
+size_t inv_quarter_root_batched_workspace(const mr_root_problem* p, int32_t count, mr_dtype, int32_t method) {
+  if (!p || count <= 0) return 0;
+  for (int i = 0; i < count; ++i)
+    if (p[i].d < 1 || p[i].d > kMaxDim) return 0;
+  return plan_root(p, count, method).total;
+}
+
+mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_dtype dt, double eps, int32_t normalize,
+                                   int32_t method, mr_root_info* info_dev, void* ws, size_t ws_bytes,
+                                   void* hip_stream) {
+  mr_status st = validate_root(p, count, dt, eps, normalize, method);
+  if (st != MR_OK) return st;
+  if (count == 0) return MR_OK;
+  const RootPlan P = plan_root(p, count, method);
+  if (!ws || ws_bytes < P.total || !aligned(ws, 256))
+    return fail(MR_ERR_WORKSPACE, "workspace %p of %zu bytes; need %zu bytes, 256-byte aligned", ws, ws_bytes,
+                P.total);
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  char* base = static_cast<char*>(ws);
+  RootState* state = reinterpret_cast<RootState*>(base + P.state_off);
+  double* partial = reinterpret_cast<double*>(base + P.partial_off);
+  const int a_f64 = dt == MR_F64;
+  const bool all_f64 = method == MR_NEWTON_F64;
+
+  // ---------------- Jacobi matrices: one launch per 16
+  {
+    JacobiBatch jb;
+    memset(&jb, 0, sizeof jb);
+    jb.a_f64 = a_f64;
+    jb.normalize = normalize;
+    jb.max_sweeps = 30;
+    jb.eps = eps;
+    jb.state = state;
+    for (int slot = P.n_newton; slot < count; ++slot) {
+      const mr_root_problem& q = p[P.slot_problem[slot]];
+      JacobiJob& J = jb.job[jb.njobs++];
+      J.A = q.A;
+      J.lda = q.lda;
+      J.X = q.X;
+      J.ldx = q.ldx;
+      J.W = reinterpret_cast<double*>(base + P.jac_w_off[slot - P.n_newton]);
+      J.d = (int32_t)q.d;
+      J.slot = slot;
+      J.problem = P.slot_problem[slot];
+      if (jb.njobs == kMaxJobs || slot == count - 1) {
+        if ((st = check_launch(launch_jacobi(jb, s), s, "jacobi launch")) != MR_OK) return st;
+        jb.njobs = 0;
+      }
+    }
+  }
+
+  if (P.n_newton > 0) {
+    // Build per-matrix batches (stats, init, finalize) over Newton slots.
+    auto run_root_batches = [&](int kind) -> mr_status {
+      RootBatch b;
+      memset(&b, 0, sizeof b);
+      b.a_f64 = a_f64;
+      b.normalize = normalize;
+      b.eps = eps;
+      b.state = state;
+      b.partial = partial;
+      b.partial_stride = P.partial_stride;
+      for (const auto& c : P.classes) {
+        for (int k = 0; k < c.count; ++k) {
+          const int slot = c.first_slot + k;
+          const mr_root_problem& q = p[P.slot_problem[slot]];
+          RootJob& J = b.job[b.njobs];
+          J.A = q.A;
+          J.lda = q.lda;
+          J.X = q.X;
+          J.ldx = q.ldx;
+          J.region = base + c.region_off + c.matrix_bytes * (size_t)k;
+          J.d = (int32_t)q.d;
+          J.slot = slot;
+          J.problem = P.slot_problem[slot];
+          J.block_begin = b.total_blocks;
+          if (kind == 0)
+            J.nblocks = tiles(q.d, kStatsRows);
+          else if (kind == 1)
+            J.nblocks = tiles(q.d, 32) * tiles(q.d, 32);
+          else
+            J.nblocks = tiles(q.d, kFinalRows);
+          b.total_blocks += J.nblocks;
+          ++b.njobs;
+          if (b.njobs == kMaxJobs || slot == P.n_newton - 1) {
+            hipError_t e = kind == 0 ? launch_root_stats(b, s) : kind == 1 ? launch_root_init(b, s)
+                                                                           : launch_root_finalize(b, s);
+            mr_status r = check_launch(e, s, "root launch");
+            if (r != MR_OK) return r;
+            b.njobs = 0;
+            b.total_blocks = 0;
+          }
+        }
+      }
+      return MR_OK;
+    };
+
+    if ((st = run_root_batches(0)) != MR_OK) return st;
+
+    // Iteration cap known on the host.  Trace mode: c <= 1.01 (1 + eps) up to
+    // rounding, so no matrix needs more than K(eps / (1.02 (1 + eps))).
+    int k_cap, j_cap;
+    if (normalize == MR_NORM_TRACE) {
+      newton_schedule(eps / (1.02 * (1.0 + eps)), kNewtonTol, kSwitchM, 1000, &k_cap, &j_cap);
+    } else {
+      k_cap = 100;
+      j_cap = 100;
+    }
+    if ((st = check_launch(launch_root_bound(state, partial, P.partial_stride, 0, P.n_newton, normalize, eps, k_cap,
+                                             all_f64 ? 1 : 0, s),
+                           s, "root bound launch")) != MR_OK)
+      return st;
+    int k_max = k_cap, j_max = all_f64 ? k_cap : j_cap;
+    if (normalize != MR_NORM_TRACE) {
+      // The scale is unknown to the host: read the per-matrix schedules back.
+      std::vector<RootState> hs(P.n_newton);
+      hipError_t e = hipMemcpyAsync(hs.data(), state, sizeof(RootState) * P.n_newton, hipMemcpyDeviceToHost, s);
+      if (e == hipSuccess) e = hipStreamSynchronize(s);
+      if (e != hipSuccess) return hip_fail(e, "reading Newton schedules");
+      k_max = 0;
+      j_max = 0;
+      for (const auto& r : hs) {
+        k_max = std::max(k_max, r.K);
+        j_max = std::max(j_max, std::min(r.j, r.K));
+      }
+    }
+    if ((st = run_root_batches(1)) != MR_OK) return st;
+
+    // Class groups: at most kMaxClasses per launch, split by vector width.
+    struct Group {
+      std::vector<int> cls;
+      int vec64, vec32;
+    };
+    std::vector<Group> groups;
+    for (int aligned4 = 1; aligned4 >= 0; --aligned4) {
+      Group g;
+      g.vec32 = aligned4 ? 4 : 1;
+      g.vec64 = 2;
+      for (int ci = 0; ci < (int)P.classes.size(); ++ci) {
+        const int64_t d = P.classes[ci].d;
+        if ((d % 4 == 0) != (aligned4 == 1)) continue;
+        g.cls.push_back(ci);
+        if (d % 2) g.vec64 = 1;
+        if ((int)g.cls.size() == kMaxClasses) {
+          groups.push_back(g);
+          g.cls.clear();
+          g.vec64 = 2;
+        }
+      }
+      if (!g.cls.empty()) groups.push_back(g);
+    }
+    auto make_launch = [&](const Group& g, int kind, int stage, int t) {
+      NewtonLaunch L;
+      memset(&L, 0, sizeof L);
+      L.stage = stage;
+      L.t = t;
+      L.state = state;
+      for (int ci : g.cls) {
+        const auto& c = P.classes[ci];
+        NewtonClass& C = L.cls[L.ncls++];
+        C.region = base + c.region_off;
+        C.matrix_bytes = (int64_t)c.matrix_bytes;
+        C.d = (int32_t)c.d;
+        C.count = c.count;
+        C.T = tiles(c.d, 128);
+        C.U = C.T * (C.T + 1) / 2;
+        C.slot_begin = c.first_slot;
+        C.block_begin = L.total_blocks;
+        if (kind == 0)
+          C.blocks_per_matrix = (stage == 0 ? 2 : 1) * C.U;
+        else
+          C.blocks_per_matrix = (int32_t)((c.d * c.d + 2047) / 2048);
+        L.total_blocks += C.blocks_per_matrix * C.count;
+      }
+      return L;
+    };
+    for (int t = 0; t < k_max; ++t) {
+      if (t <= j_max && !all_f64) {
+        for (const auto& g : groups)
+          if ((st = check_launch(launch_newton_convert(make_launch(g, 1, 0, t), s), s, "newton convert")) != MR_OK)
+            return st;
+      }
+      for (int stage = 0; stage < 3; ++stage) {
+        for (const auto& g : groups) {
+          const NewtonLaunch L = make_launch(g, 0, stage, t);
+          if (t < j_max) {
+            if ((st = check_launch(launch_newton_stage(L, true, g.vec64, s), s, "newton f64 stage")) != MR_OK)
+              return st;
+          }
+          if (!all_f64) {
+            if ((st = check_launch(launch_newton_stage(L, false, g.vec32, s), s, "newton f32 stage")) != MR_OK)
+              return st;
+          }
+        }
+      }
+    }
+    if ((st = run_root_batches(2)) != MR_OK) return st;
+  }
+
+  return check_launch(launch_root_info(state, partial, P.partial_stride, count, info_dev, s), s, "root info");
+}
+
+}  // extern "C"

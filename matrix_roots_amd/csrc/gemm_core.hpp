@@ -1,0 +1,323 @@
+// MFMA tile cores for gfx950.
+//
+// Both cores compute one 128 x 128 block tile of C = A * B^T where row i of A
+// and row j of B are indexed along the contraction k.  With symmetric operands
+// (every product of the coupled Newton iteration, the Gram of G's rows) this
+// "NT" form reads both operands along contiguous rows.  The float64 core can
+// also read an operand "transposed" (element (i, k) at ptr[k * ld + i]), which
+// the right Gram G^T G needs, and can take float32 inputs that it widens to
+// float64 on the way into LDS (float32 products are exact in float64).
+//
+// Work split: 256 threads = 4 waves in a 2 x 2 grid, each wave owns a 64 x 64
+// sub-tile.  A and B tiles are staged through LDS (one buffer, loads for the
+// next k-chunk prefetched into registers while the current chunk is consumed).
+// Within a k-chunk each lane reads a run of consecutive k for its row with
+// 128-bit LDS reads; consecutive MFMAs consume that run element by element.
+// The k order inside a chunk is therefore permuted, identically for A and B,
+// which leaves the sum unchanged.
+#pragma once
+
+#include "mr_common.hpp"
+
+namespace mr {
+
+// ------------------------------------------------------------------ float32
+struct F32Tile {
+  static constexpr int BM = 128, BN = 128, BK = 32, PAD = 4, LDW = BK + PAD;
+  static constexpr int THREADS = 256;
+  static constexpr int LDS_FLOATS = (BM + BN) * LDW;  // 36 KiB
+};
+
+// Load a BM x BK chunk (rows r0.., k0..) of a K-contiguous float32 operand
+// into registers.  VEC=4 needs ld % 4 == 0, K % 4 == 0 and a 16-byte aligned
+// base; VEC=1 has element guards.
+template <int VEC>
+struct F32Loader {
+  static constexpr int PER = (F32Tile::BM * F32Tile::BK) / (F32Tile::THREADS * VEC);
+  v4f reg[VEC == 4 ? PER : 1];
+  float sreg[VEC == 1 ? PER : 1];
+
+  __device__ __forceinline__ void load(const float* __restrict__ P, int64_t ld, int rows, int K, int r0,
+                                       int k0, int tid) {
+    if constexpr (VEC == 4) {
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int idx = tid + p * F32Tile::THREADS;
+        const int row = idx >> 3;  // BK/4 = 8 float4 per row
+        const int kq = (idx & 7) * 4;
+        const int gr = r0 + row, gk = k0 + kq;
+        v4f v = {0.f, 0.f, 0.f, 0.f};
+        if (gr < rows && gk < K) v = *reinterpret_cast<const v4f*>(P + (int64_t)gr * ld + gk);
+        reg[p] = v;
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int idx = tid + p * F32Tile::THREADS;
+        const int row = idx >> 5;
+        const int kk = idx & 31;
+        const int gr = r0 + row, gk = k0 + kk;
+        sreg[p] = (gr < rows && gk < K) ? P[(int64_t)gr * ld + gk] : 0.f;
+      }
+    }
+  }
+  __device__ __forceinline__ void store(float* __restrict__ s, int tid) const {
+    if constexpr (VEC == 4) {
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int idx = tid + p * F32Tile::THREADS;
+        const int row = idx >> 3;
+        const int kq = (idx & 7) * 4;
+        *reinterpret_cast<v4f*>(s + row * F32Tile::LDW + kq) = reg[p];
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int idx = tid + p * F32Tile::THREADS;
+        s[(idx >> 5) * F32Tile::LDW + (idx & 31)] = sreg[p];
+      }
+    }
+  }
+};
+
+// acc[rb][cb] holds the 32 x 32 MFMA block (rb, cb) of this wave's 64 x 64
+// sub-tile.  sA, sB: LDS, F32Tile::LDS_FLOATS floats in total.
+template <int VEC>
+__device__ __forceinline__ void f32_nt_tile(const float* __restrict__ A, int64_t lda,
+                                            const float* __restrict__ B, int64_t ldb, int M, int N,
+                                            int K, int m0, int n0, float* __restrict__ sA,
+                                            float* __restrict__ sB, v16f (&acc)[2][2]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.f;
+
+  F32Loader<VEC> la, lb;
+  la.load(A, lda, M, K, m0, 0, tid);
+  lb.load(B, ldb, N, K, n0, 0, tid);
+  const int koff = (lane >> 5) * 8;
+  for (int k0 = 0; k0 < K; k0 += F32Tile::BK) {
+    la.store(sA, tid);
+    lb.store(sB, tid);
+    __syncthreads();
+    if (k0 + F32Tile::BK < K) {
+      la.load(A, lda, M, K, m0, k0 + F32Tile::BK, tid);
+      lb.load(B, ldb, N, K, n0, k0 + F32Tile::BK, tid);
+    }
+#pragma unroll
+    for (int g = 0; g < F32Tile::BK / 16; ++g) {
+      v4f a[2][2], b[2][2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const float* pa = sA + (wm * 64 + rb * 32 + (lane & 31)) * F32Tile::LDW + g * 16 + koff;
+        a[rb][0] = *reinterpret_cast<const v4f*>(pa);
+        a[rb][1] = *reinterpret_cast<const v4f*>(pa + 4);
+      }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const float* pb = sB + (wn * 64 + cb * 32 + (lane & 31)) * F32Tile::LDW + g * 16 + koff;
+        b[cb][0] = *reinterpret_cast<const v4f*>(pb);
+        b[cb][1] = *reinterpret_cast<const v4f*>(pb + 4);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb)
+            acc[rb][cb] = mfma_f32_32x32x2(a[rb][i >> 2][i & 3], b[cb][i >> 2][i & 3], acc[rb][cb]);
+    }
+    __syncthreads();
+  }
+}
+
+// Visit every accumulator element of the f32 core as (row, col) local to the
+// block tile.
+template <typename F>
+__device__ __forceinline__ void f32_for_each(const v16f (&acc)[2][2], F&& f) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        f(wm * 64 + rb * 32 + f32_row(lane, v), wn * 64 + cb * 32 + (lane & 31), acc[rb][cb][v]);
+}
+
+// ------------------------------------------------------------------ float64
+struct F64Tile {
+  static constexpr int BM = 128, BN = 128, BK = 16, PAD = 2, LDW = BK + PAD;
+  static constexpr int THREADS = 256;
+  static constexpr int LDS_DOUBLES = (BM + BN) * LDW;  // 36 KiB
+};
+
+// Loader of a BM x BK chunk of operand element (i, k), i in [r0, r0+BM),
+// k in [k0, k0+BK), widened to double.
+//   TRANS = false: element at P[i * ld + k]; TRANS = true: at P[k * ld + i].
+//   VEC: elements per global load (4 for float, 2 for double; 1 = guarded scalar).
+template <typename TIn, bool TRANS, int VEC>
+struct F64Loader {
+  static constexpr int ELEMS = F64Tile::BM * F64Tile::BK;  // 2048
+  static constexpr int PER = ELEMS / (F64Tile::THREADS * VEC);
+  static constexpr int VPR_K = F64Tile::BK / VEC;   // vectors per row when !TRANS
+  static constexpr int VPR_I = F64Tile::BM / VEC;   // vectors per k-row when TRANS
+  double reg[PER * VEC];
+
+  __device__ __forceinline__ void load(const TIn* __restrict__ P, int64_t ld, int rows, int K, int r0,
+                                       int k0, int tid) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int idx = tid + p * F64Tile::THREADS;
+      int i, k;
+      if constexpr (!TRANS) {
+        i = idx / VPR_K;
+        k = (idx % VPR_K) * VEC;
+      } else {
+        k = idx / VPR_I;
+        i = (idx % VPR_I) * VEC;
+      }
+      const int gi = r0 + i, gk = k0 + k;
+      if constexpr (VEC == 1) {
+        reg[p] = (gi < rows && gk < K) ? (double)P[TRANS ? (int64_t)gk * ld + gi : (int64_t)gi * ld + gk]
+                                       : 0.0;
+      } else if constexpr (!TRANS) {
+        // VEC consecutive k of row gi; K % VEC == 0 so the vector is all-in or all-out.
+        const bool ok = gi < rows && gk < K;
+        if constexpr (sizeof(TIn) == 4) {
+          v4f v = {0.f, 0.f, 0.f, 0.f};
+          if (ok) v = *reinterpret_cast<const v4f*>(P + (int64_t)gi * ld + gk);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) reg[p * 4 + e] = (double)v[e];
+        } else {
+          v2d v = {0.0, 0.0};
+          if (ok) v = *reinterpret_cast<const v2d*>(P + (int64_t)gi * ld + gk);
+          reg[p * 2 + 0] = v[0];
+          reg[p * 2 + 1] = v[1];
+        }
+      } else {
+        // VEC consecutive i of k-row gk; rows % VEC == 0.
+        const bool ok = gi < rows && gk < K;
+        if constexpr (sizeof(TIn) == 4) {
+          v4f v = {0.f, 0.f, 0.f, 0.f};
+          if (ok) v = *reinterpret_cast<const v4f*>(P + (int64_t)gk * ld + gi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) reg[p * 4 + e] = (double)v[e];
+        } else {
+          v2d v = {0.0, 0.0};
+          if (ok) v = *reinterpret_cast<const v2d*>(P + (int64_t)gk * ld + gi);
+          reg[p * 2 + 0] = v[0];
+          reg[p * 2 + 1] = v[1];
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void store(double* __restrict__ s, int tid) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int idx = tid + p * F64Tile::THREADS;
+      if constexpr (VEC == 1) {
+        int i, k;
+        if constexpr (!TRANS) {
+          i = idx / F64Tile::BK;
+          k = idx % F64Tile::BK;
+        } else {
+          k = idx / F64Tile::BM;
+          i = idx % F64Tile::BM;
+        }
+        s[i * F64Tile::LDW + k] = reg[p];
+      } else if constexpr (!TRANS) {
+        const int i = idx / VPR_K;
+        const int k = (idx % VPR_K) * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; e += 2) {
+          v2d v = {reg[p * VEC + e], reg[p * VEC + e + 1]};
+          *reinterpret_cast<v2d*>(s + i * F64Tile::LDW + k + e) = v;
+        }
+      } else {
+        const int k = idx / VPR_I;
+        const int i = (idx % VPR_I) * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s[(i + e) * F64Tile::LDW + k] = reg[p * VEC + e];
+      }
+    }
+  }
+};
+
+// acc[rb][cb]: 16 x 16 MFMA block (rb, cb) of this wave's 64 x 64 sub-tile.
+template <typename TA, bool TRANSA, int VECA, typename TB, bool TRANSB, int VECB>
+__device__ __forceinline__ void f64_tile(const TA* __restrict__ A, int64_t lda, const TB* __restrict__ B,
+                                         int64_t ldb, int M, int N, int K, int m0, int n0,
+                                         double* __restrict__ sA, double* __restrict__ sB,
+                                         v4d (&acc)[4][4]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[rb][cb][v] = 0.0;
+
+  F64Loader<TA, TRANSA, VECA> la;
+  F64Loader<TB, TRANSB, VECB> lb;
+  la.load(A, lda, M, K, m0, 0, tid);
+  lb.load(B, ldb, N, K, n0, 0, tid);
+  const int koff = (lane >> 4) * 4;
+  for (int k0 = 0; k0 < K; k0 += F64Tile::BK) {
+    la.store(sA, tid);
+    lb.store(sB, tid);
+    __syncthreads();
+    if (k0 + F64Tile::BK < K) {
+      la.load(A, lda, M, K, m0, k0 + F64Tile::BK, tid);
+      lb.load(B, ldb, N, K, n0, k0 + F64Tile::BK, tid);
+    }
+    v2d a[4][2], b[4][2];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const double* pa = sA + (wm * 64 + rb * 16 + (lane & 15)) * F64Tile::LDW + koff;
+      a[rb][0] = *reinterpret_cast<const v2d*>(pa);
+      a[rb][1] = *reinterpret_cast<const v2d*>(pa + 2);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const double* pb = sB + (wn * 64 + cb * 16 + (lane & 15)) * F64Tile::LDW + koff;
+      b[cb][0] = *reinterpret_cast<const v2d*>(pb);
+      b[cb][1] = *reinterpret_cast<const v2d*>(pb + 2);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+          acc[rb][cb] = mfma_f64_16x16x4(a[rb][i >> 1][i & 1], b[cb][i >> 1][i & 1], acc[rb][cb]);
+    __syncthreads();
+  }
+}
+
+template <typename F>
+__device__ __forceinline__ void f64_for_each(const v4d (&acc)[4][4], F&& f) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        f(wm * 64 + rb * 16 + f64_row(lane, v), wn * 64 + cb * 16 + (lane & 15), acc[rb][cb][v]);
+}
+
+}  // namespace mr

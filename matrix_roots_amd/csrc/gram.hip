@@ -1,0 +1,66 @@
+// Gram EMA on the float64 matrix cores (SYRK with a fused EMA epilogue).
+//
+//   left:  S <- beta * S + (1 - beta) * G * G^T     (S is m x m)
+//   right: S <- beta * S + (1 - beta) * G^T * G     (S is n x n)
+//
+// The exponential moving averages of gradient products that EMA-Gram keeps
+// per linear weight (marin.community, "Sharding EMA-Gram eigensolves",
+// section "Background").  float32 entries of G are widened to float64 on the
+// way into LDS; their products are exact in float64 and are summed in float64
+// by v_mfma_f64_16x16x4_f64.  Only the upper triangle of 128 x 128 tiles is
+// computed; every computed element is written to both (i, j) and (j, i), so
+// the state stays exactly symmetric and only its upper triangle is read.
+#include "gemm_core.hpp"
+#include "launch.hpp"
+
+namespace mr {
+
+template <bool RIGHT, typename TS, int VEC>
+__global__ __launch_bounds__(256) void syrk_ema_kernel(const SyrkBatch batch) {
+  __shared__ double sA[F64Tile::BM * F64Tile::LDW];
+  __shared__ double sB[F64Tile::BN * F64Tile::LDW];
+
+  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
+  int jx = 0;
+  while (jx + 1 < batch.njobs && b >= batch.job[jx + 1].block_begin) ++jx;
+  const SyrkJob& J = batch.job[jx];
+  int ti, tj;
+  upper_tile((int)(b - J.block_begin), J.T, ti, tj);
+  const int m0 = ti * F64Tile::BM, n0 = tj * F64Tile::BN;
+
+  v4d acc[4][4];
+  f64_tile<float, RIGHT, VEC, float, RIGHT, VEC>(J.G, J.ldg, J.G, J.ldg, J.d, J.d, J.K, m0, n0, sA, sB,
+                                                 acc);
+
+  TS* S = reinterpret_cast<TS*>(J.S);
+  const int64_t lds = J.lds;
+  const int d = J.d;
+  const double alpha = batch.alpha, beta = batch.beta;
+  f64_for_each(acc, [&](int r, int c, double v) {
+    const int gr = m0 + r, gc = n0 + c;
+    if (gr < d && gc < d && gr <= gc) {
+      double val = alpha * v;
+      if (beta != 0.0) val += beta * (double)S[(int64_t)gr * lds + gc];
+      const TS out = (TS)val;
+      S[(int64_t)gr * lds + gc] = out;
+      if (gr != gc) S[(int64_t)gc * lds + gr] = out;
+    }
+  });
+}
+
+template <bool RIGHT, typename TS>
+static hipError_t launch_syrk_t(const SyrkBatch& b, int vec, hipStream_t s) {
+  if (vec == 4)
+    hipLaunchKernelGGL((syrk_ema_kernel<RIGHT, TS, 4>), dim3(b.total_blocks), dim3(256), 0, s, b);
+  else
+    hipLaunchKernelGGL((syrk_ema_kernel<RIGHT, TS, 1>), dim3(b.total_blocks), dim3(256), 0, s, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_syrk_ema(const SyrkBatch& b, bool right, bool f64_state, int vec, hipStream_t s) {
+  if (b.total_blocks <= 0) return hipSuccess;
+  if (right) return f64_state ? launch_syrk_t<true, double>(b, vec, s) : launch_syrk_t<true, float>(b, vec, s);
+  return f64_state ? launch_syrk_t<false, double>(b, vec, s) : launch_syrk_t<false, float>(b, vec, s);
+}
+
+}  // namespace mr

@@ -1,0 +1,165 @@
+// Kernel-argument records shared by the host runtime and the kernels, and the
+// launcher functions each kernel file exports to the host runtime.
+//
+// Every per-problem table travels by value in the kernel arguments (at most
+// kMaxJobs records per launch, well under the 4 KiB argument limit), so an
+// entry point never copies descriptors to the device.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/matrix_roots.h"
+
+namespace mr {
+
+constexpr int kMaxJobs = 16;
+constexpr int kMaxClasses = 8;
+constexpr int kJacobiMaxD = 128;
+constexpr int kStatsRows = 8;        // rows of A per statistics workgroup
+constexpr int kFinalRows = 8;        // rows of X per finalize workgroup
+constexpr double kSwitchM = 1e-2;    // float64 -> float32 once the eigenvalue floor reaches this
+constexpr double kNewtonTol = 1e-6;  // stop once 1 - m_K <= this (scalar recurrence)
+constexpr double kBoundSafety = 1.01;
+
+// Per-matrix state of one inv_quarter_root_batched call (device, in the
+// workspace).  Slot order: Newton matrices grouped by size class, then the
+// Jacobi matrices.  64 bytes.
+struct RootState {
+  double s;          // rescale: trace(A) or 1
+  double c;          // bound on lambda_max(A/s + eps I) (Newton)
+  double out_scale;  // c^(-1/4)
+  double eps;
+  int32_t d;
+  int32_t K;  // Newton iterations of this matrix
+  int32_t j;  // first float32 iteration (== K when all float64)
+  uint32_t flags;
+  float residual;
+  int32_t method;  // MR_JACOBI or MR_NEWTON
+  int32_t sweeps;
+  int32_t problem;  // index of the problem in the caller's array
+};
+static_assert(sizeof(RootState) == 64, "RootState layout");
+
+// ---------------------------------------------------------------- Gram EMA
+struct SyrkJob {
+  const float* G;
+  int64_t ldg;
+  void* S;
+  int64_t lds;
+  int32_t d;            // Gram dimension (m left, n right)
+  int32_t K;            // contraction length (n left, m right)
+  int32_t T;            // tiles per side
+  int32_t block_begin;  // first workgroup of this job
+};
+struct SyrkBatch {
+  SyrkJob job[kMaxJobs];
+  int32_t njobs;
+  int32_t total_blocks;
+  double alpha;  // 1 - beta
+  double beta;
+};
+
+// ------------------------------------------------- float32 NT GEMM (apply)
+struct F32Job {
+  const float* A;
+  const float* B;
+  float* C;
+  int64_t lda, ldb, ldc;
+  int32_t M, N, K;
+  int32_t tiles_n;
+  int32_t block_begin;
+  float alpha;
+};
+struct F32Batch {
+  F32Job job[kMaxJobs];
+  int32_t njobs;
+  int32_t total_blocks;
+};
+
+// ------------------------------------------------------ root: per-matrix
+struct RootJob {
+  const void* A;
+  int64_t lda;
+  float* X;
+  int64_t ldx;
+  char* region;  // Newton buffers (5 float64 slots of d*d), NULL for Jacobi
+  int32_t d;
+  int32_t slot;     // index into the RootState array
+  int32_t problem;  // index in the caller's problem array
+  int32_t block_begin;
+  int32_t nblocks;
+  int32_t pad;
+};
+struct RootBatch {
+  RootJob job[kMaxJobs];
+  int32_t njobs;
+  int32_t total_blocks;
+  int32_t a_f64;      // A is float64
+  int32_t normalize;  // MR_NORM_*
+  double eps;
+  RootState* state;
+  double* partial;         // per-workgroup partial sums
+  int64_t partial_stride;  // doubles per matrix slot in `partial`
+};
+
+// ------------------------------------------------ Newton: per size class
+struct NewtonClass {
+  char* region;          // buffers of the class's first matrix
+  int64_t matrix_bytes;  // distance between consecutive matrices' buffers
+  int32_t d, count, T, U;  // size, matrices, tiles per side, upper tiles
+  int32_t block_begin;     // first workgroup of this class in the launch
+  int32_t slot_begin;      // RootState slot of the class's first matrix
+  int32_t blocks_per_matrix;
+  int32_t pad;
+};
+struct NewtonLaunch {
+  NewtonClass cls[kMaxClasses];
+  int32_t ncls;
+  int32_t total_blocks;
+  int32_t stage;  // GEMM stages: 0 -> T2 and X', 1 -> T4, 2 -> M'
+  int32_t t;      // iteration
+  RootState* state;
+};
+
+// ------------------------------------------------------------ Jacobi
+struct JacobiJob {
+  const void* A;
+  int64_t lda;
+  float* X;
+  int64_t ldx;
+  double* W;  // d*d float64 eigenvector scratch in the workspace
+  int32_t d;
+  int32_t slot;
+  int32_t problem;
+  int32_t pad;
+};
+struct JacobiBatch {
+  JacobiJob job[kMaxJobs];
+  int32_t njobs;
+  int32_t a_f64;
+  int32_t normalize;
+  int32_t max_sweeps;
+  double eps;
+  RootState* state;
+};
+
+// ------------------------------------------------------------ launchers
+// Each returns the HIP error of its launch (hipSuccess when launched).
+hipError_t launch_syrk_ema(const SyrkBatch& b, bool right, bool f64_state, int vec, hipStream_t s);
+hipError_t launch_f32_nt(const F32Batch& b, int vec, hipStream_t s);
+
+hipError_t launch_root_stats(const RootBatch& b, hipStream_t s);
+hipError_t launch_root_bound(RootState* state, const double* partial, int64_t partial_stride,
+                             int32_t slot_begin, int32_t nslots, int32_t normalize, double eps,
+                             int32_t k_cap, int32_t all_f64, hipStream_t s);
+hipError_t launch_root_init(const RootBatch& b, hipStream_t s);
+hipError_t launch_newton_stage(const NewtonLaunch& L, bool f64, int vec, hipStream_t s);
+hipError_t launch_newton_convert(const NewtonLaunch& L, hipStream_t s);
+hipError_t launch_root_finalize(const RootBatch& b, hipStream_t s);
+hipError_t launch_root_info(RootState* state, const double* partial, int64_t partial_stride,
+                            int32_t count, mr_root_info* info, hipStream_t s);
+hipError_t launch_jacobi(const JacobiBatch& b, hipStream_t s);
+
+}  // namespace mr

@@ -1,0 +1,62 @@
+// Shared device-side definitions for the gfx950 kernels: vector types, MFMA
+// wrappers with their lane layouts, the XCD-aware block remap and the
+// upper-triangle tile enumeration.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mr {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef double v4d __attribute__((ext_vector_type(4)));
+typedef double v2d __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
+
+// --------------------------------------------------------------------------
+// MFMA lane layouts (verified on gfx950 with an in-bounds probe):
+//
+// v_mfma_f32_32x32x2_f32, D(32x32) += A(32x2) B(2x32):
+//   lane l supplies A[l % 32][l / 32] and B[l / 32][l % 32];
+//   D value v (0..15) of lane l is D[8*(v/4) + 4*(l/32) + v%4][l % 32].
+// v_mfma_f64_16x16x4_f64, D(16x16) += A(16x4) B(4x16):
+//   lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16];
+//   D value v (0..3) of lane l is D[4*v + l/16][l % 16].
+// --------------------------------------------------------------------------
+__device__ __forceinline__ v16f mfma_f32_32x32x2(float a, float b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v4d mfma_f64_16x16x4(double a, double b, v4d c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int f32_row(int lane, int v) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+__device__ __forceinline__ int f64_row(int lane, int v) { return 4 * v + (lane >> 4); }
+
+// Workgroup b of a 1-D grid of n lands on XCD b % 8.  Renumber so that each
+// XCD receives one contiguous range of logical blocks: neighbouring tiles of
+// one matrix (which share operand panels) then share that XCD's L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t n) {
+  const int64_t per = n / kNumXcd;
+  const int64_t full = per * kNumXcd;
+  if (b >= full) return b;  // ragged remainder keeps its order
+  return (b % kNumXcd) * per + b / kNumXcd;
+}
+
+// Upper-triangle tile u (row-major over ti <= tj) of a T x T tile grid.
+__device__ __forceinline__ void upper_tile(int u, int T, int& ti, int& tj) {
+  // rows ti hold T - ti tiles; walk the rows (T <= 128 in practice).
+  int r = 0;
+  int rem = u;
+  while (rem >= T - r) {
+    rem -= T - r;
+    ++r;
+  }
+  ti = r;
+  tj = r + rem;
+}
+
+}  // namespace mr

@@ -1,0 +1,513 @@
+// Regularised inverse quarter root X = (A/s + eps I)^(-1/4) for Grams above
+// the Jacobi size, by the GEMM-only coupled Newton iteration for the inverse
+// p-th root with p = 4:
+//
+//   M0 = (A/s + eps I) / c,  X0 = I,
+//   T_t = (5 I - M_t) / 4,  X_{t+1} = X_t T_t,  M_{t+1} = T_t^4 M_t,
+//   X = c^(-1/4) X_K.
+//
+// The pages' step is "rescale, add a regulariser to the eigenvalues, raise to
+// -1/4, rebuild" (marin.community, "Sharding EMA-Gram eigensolves", section
+// "Background"); tilderesearch, "Online KL Shampoo", sections 2.1-2.2, argue
+// for GEMM-only coupled iterations over eigendecompositions on GPUs and use
+// the p = 2 member (coupled Newton-Schulz for S^(-1/2)) after normalising the
+// largest eigenvalue below 1.  Every eigenvalue of M follows the scalar map
+// m <- m ((5 - m)/4)^4, which is increasing on [0, 1] with fixed point 1, so
+// the smallest one, eps/c, fixes the iteration count K.
+//
+// Per iteration: stage 0 computes T2 = T^2 = (25 I - 10 M + M^2)/16 and
+// X' = (5 X - X M)/4 in one launch, stage 1 T4 = T2 T2, stage 2 M' = T4 M.
+// All matrices are polynomials in M0: symmetric and mutually commuting, so
+// every product is an upper-tile symmetric GEMM.  The last iteration only
+// updates X.  Iterations run in float64 until the scalar map says the
+// smallest eigenvalue of M has reached 1e-2, then in float32.
+//
+// Buffers per matrix (region of 5 float64 slots of d*d, S0..S4): in float64,
+// M alternates S0/S3, X alternates S1/S2, T4 is S4; in float32 (half-slots
+// h0..h9 of 4*d*d bytes) M alternates h8/h0, X h4/h2, T4 is h9.  Roles are a
+// function of the iteration's parity, so every workgroup finds its operands
+// without any table; the conversion at the switch writes float32 M and X into
+// half-slots that the float64 M and X of that parity do not use.
+#include <math.h>
+
+#include "gemm_core.hpp"
+#include "launch.hpp"
+#include "schedule.hpp"
+
+namespace mr {
+
+// ------------------------------------------------------------ roles
+struct Roles64 {
+  double *M, *T2, *X, *Xn, *T4;
+};
+struct Roles32 {
+  float *M, *T2, *X, *Xn, *T4;
+};
+__device__ __forceinline__ Roles64 roles64(char* region, int d, int t) {
+  const int64_t S = (int64_t)d * d * 8;
+  const bool even = (t & 1) == 0;
+  Roles64 r;
+  r.M = reinterpret_cast<double*>(region + (even ? 0 : 3) * S);
+  r.T2 = reinterpret_cast<double*>(region + (even ? 3 : 0) * S);
+  r.X = reinterpret_cast<double*>(region + (even ? 1 : 2) * S);
+  r.Xn = reinterpret_cast<double*>(region + (even ? 2 : 1) * S);
+  r.T4 = reinterpret_cast<double*>(region + 4 * S);
+  return r;
+}
+__device__ __forceinline__ Roles32 roles32(char* region, int d, int t) {
+  const int64_t H = (int64_t)d * d * 4;
+  const bool even = (t & 1) == 0;
+  Roles32 r;
+  r.M = reinterpret_cast<float*>(region + (even ? 8 : 0) * H);
+  r.T2 = reinterpret_cast<float*>(region + (even ? 0 : 8) * H);
+  r.X = reinterpret_cast<float*>(region + (even ? 4 : 2) * H);
+  r.Xn = reinterpret_cast<float*>(region + (even ? 2 : 4) * H);
+  r.T4 = reinterpret_cast<float*>(region + 9 * H);
+  return r;
+}
+
+// ------------------------------------------------------ block reductions
+// Fixed-order tree over 256 threads: the same inputs give the same bits.
+__device__ __forceinline__ double block_sum_256(double v, double* red) {
+  const int tid = threadIdx.x;
+  red[tid] = v;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  const double r = red[0];
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ double block_sum_64(double v, double* red) {
+  const int tid = threadIdx.x;
+  red[tid] = v;
+  __syncthreads();
+  for (int s = 32; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  const double r = red[0];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ int find_job(const RootBatch& B, int64_t b) {
+  int jx = 0;
+  while (jx + 1 < B.njobs && b >= B.job[jx + 1].block_begin) ++jx;
+  return jx;
+}
+
+template <typename TA>
+__device__ __forceinline__ double ld_elem(const void* A, int64_t idx) {
+  return (double)reinterpret_cast<const TA*>(A)[idx];
+}
+
+// ------------------------------------------------------------ statistics
+// Per row block of A: partial trace, sum of squares, count of non-finite.
+template <typename TA>
+__global__ __launch_bounds__(256) void root_stats_kernel(const RootBatch B) {
+  __shared__ double red[256];
+  const int64_t b = blockIdx.x;
+  const RootJob& J = B.job[find_job(B, b)];
+  const int blk = (int)(b - J.block_begin);
+  const int d = J.d;
+  const int r0 = blk * kStatsRows;
+  const int r1 = min(d, r0 + kStatsRows);
+  double tr = 0.0, f2 = 0.0, nf = 0.0;
+  for (int r = r0; r < r1; ++r) {
+    for (int c = threadIdx.x; c < d; c += 256) {
+      const double v = ld_elem<TA>(J.A, (int64_t)r * J.lda + c);
+      if (r == c) tr += v;
+      f2 += v * v;
+      if (!isfinite(v)) nf += 1.0;
+    }
+  }
+  tr = block_sum_256(tr, red);
+  f2 = block_sum_256(f2, red);
+  nf = block_sum_256(nf, red);
+  if (threadIdx.x == 0) {
+    double* p = B.partial + (int64_t)J.slot * B.partial_stride + 3 * blk;
+    p[0] = tr;
+    p[1] = f2;
+    p[2] = nf;
+    if (blk == 0) {
+      RootState& st = B.state[J.slot];
+      st.d = d;
+      st.problem = J.problem;
+      st.method = MR_NEWTON;
+      st.eps = B.eps;
+      st.sweeps = 0;
+      st.residual = 0.f;
+    }
+  }
+}
+
+// One wave per matrix: combine the partials in a fixed order, then derive
+// s, the bound c, the iteration count K and the switch iteration j.
+//
+// c = 1.01 * WS(A/s + eps I), where WS(B) = m + sqrt(max(|B|_F^2/d - m^2, 0)) *
+// sqrt(d - 1), m = tr(B)/d, is the Wolkowicz-Styan upper bound on the largest
+// eigenvalue of a symmetric matrix (the OKLS page, appendix D, bounds the
+// largest eigenvalue by the minimum of this and a second bound before its
+// iteration).  |A|_F is taken over A itself, which bounds that of (A + A^T)/2.
+// For a positive semidefinite A/s of unit trace WS <= 1 + eps.
+__global__ __launch_bounds__(64) void root_bound_kernel(RootState* state, const double* partial,
+                                                        int64_t stride, int32_t slot_begin, int32_t normalize,
+                                                        double eps, int32_t k_cap, int32_t all_f64) {
+  __shared__ double red[64];
+  const int slot = slot_begin + blockIdx.x;
+  RootState& st = state[slot];
+  const int d = st.d;
+  const int nb = (d + kStatsRows - 1) / kStatsRows;
+  const double* p = partial + (int64_t)slot * stride;
+  double tr = 0.0, f2 = 0.0, nf = 0.0;
+  for (int i = threadIdx.x; i < nb; i += 64) {
+    tr += p[3 * i + 0];
+    f2 += p[3 * i + 1];
+    nf += p[3 * i + 2];
+  }
+  tr = block_sum_64(tr, red);
+  f2 = block_sum_64(f2, red);
+  nf = block_sum_64(nf, red);
+  if (threadIdx.x != 0) return;
+  uint32_t flags = 0;
+  double s = 1.0, c = 1.0;
+  int K = 0, j = 0;
+  if (nf > 0.0 || !isfinite(tr) || !isfinite(f2)) {
+    flags |= MR_INFO_NONFINITE;
+  } else {
+    if (normalize == MR_NORM_TRACE) s = tr;
+    if (normalize == MR_NORM_TRACE && s == 0.0) {
+      flags |= MR_INFO_ZERO_TRACE;
+    } else {
+      const double trh = tr / s;
+      const double f2h = f2 / (s * s);
+      const double dd = (double)d;
+      const double trB = trh + dd * eps;
+      const double f2B = f2h + 2.0 * eps * trh + dd * eps * eps;
+      const double m = trB / dd;
+      const double var = fmax(f2B / dd - m * m, 0.0);
+      const double ws = m + sqrt(var) * sqrt(dd - 1.0);
+      c = kBoundSafety * ws;
+      if (!(c > 0.0) || !isfinite(c)) {
+        flags |= MR_INFO_NOT_PD;
+        c = 1.0;
+      } else {
+        newton_schedule(eps / c, kNewtonTol, kSwitchM, k_cap, &K, &j);
+        if (all_f64) j = K;
+      }
+    }
+  }
+  st.s = s;
+  st.c = c;
+  st.out_scale = pow(c, -0.25);
+  st.K = K;
+  st.j = j;
+  st.flags = flags;
+}
+
+// M0 = ((A + A^T)/2 / s + eps I) / c into S0 and X0 = I into S1 (float64),
+// 32 x 32 tiles through LDS so both A reads are coalesced.
+template <typename TA>
+__global__ __launch_bounds__(256) void root_init_kernel(const RootBatch B) {
+  __shared__ double ta[32][33];
+  __shared__ double tb[32][33];
+  const int64_t b = blockIdx.x;
+  const RootJob& J = B.job[find_job(B, b)];
+  const RootState& st = B.state[J.slot];
+  if (st.K == 0) return;
+  const int d = J.d;
+  const int Tt = (d + 31) / 32;
+  const int tile = (int)(b - J.block_begin);
+  const int bi = tile / Tt, bj = tile % Tt;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = ty + 8 * e;
+    const int gi = bi * 32 + r, gj = bj * 32 + tx;
+    ta[r][tx] = (gi < d && gj < d) ? ld_elem<TA>(J.A, (int64_t)gi * J.lda + gj) : 0.0;
+    const int hi = bj * 32 + r, hj = bi * 32 + tx;
+    tb[r][tx] = (hi < d && hj < d) ? ld_elem<TA>(J.A, (int64_t)hi * J.lda + hj) : 0.0;
+  }
+  __syncthreads();
+  const double inv_s = 1.0 / st.s, inv_c = 1.0 / st.c, eps = B.eps;
+  double* M = reinterpret_cast<double*>(J.region);
+  double* X = reinterpret_cast<double*>(J.region + (int64_t)d * d * 8);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = ty + 8 * e;
+    const int gi = bi * 32 + r, gj = bj * 32 + tx;
+    if (gi < d && gj < d) {
+      const double sym = 0.5 * (ta[r][tx] + tb[tx][r]);
+      const double v = (sym * inv_s + (gi == gj ? eps : 0.0)) * inv_c;
+      M[(int64_t)gi * d + gj] = v;
+      X[(int64_t)gi * d + gj] = (gi == gj) ? 1.0 : 0.0;
+    }
+  }
+}
+
+// ------------------------------------------------------------ Newton GEMMs
+__device__ __forceinline__ int find_class(const NewtonLaunch& L, int64_t b) {
+  int ci = 0;
+  while (ci + 1 < L.ncls && b >= L.cls[ci + 1].block_begin) ++ci;
+  return ci;
+}
+
+struct StageJob {
+  bool active;
+  int job;
+  int ti, tj;
+  int d;
+  char* region;
+};
+
+__device__ __forceinline__ StageJob stage_job(const NewtonLaunch& L, bool f64) {
+  StageJob s;
+  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
+  const NewtonClass& C = L.cls[find_class(L, b)];
+  const int local = (int)(b - C.block_begin);
+  const int mat = local / C.blocks_per_matrix;
+  const int rem = local % C.blocks_per_matrix;
+  s.job = rem / C.U;
+  upper_tile(rem % C.U, C.T, s.ti, s.tj);
+  s.d = C.d;
+  s.region = C.region + (int64_t)mat * C.matrix_bytes;
+  const RootState& st = L.state[C.slot_begin + mat];
+  const int t = L.t, K = st.K, j = st.j;
+  bool act = f64 ? (t < K && t < j) : (t >= j && t < K);
+  // The last iteration only updates X (stage 0, job 1).
+  if (t == K - 1 && !(L.stage == 0 && s.job == 1)) act = false;
+  s.active = act;
+  return s;
+}
+
+template <typename T>
+struct StageOps {
+  const T *A, *B, *Cin;
+  T* C;
+  double alpha, beta, gamma;
+};
+
+template <typename T, typename R>
+__device__ __forceinline__ StageOps<T> stage_ops(const R& r, int stage, int job) {
+  StageOps<T> o;
+  o.Cin = nullptr;
+  o.beta = 0.0;
+  o.gamma = 0.0;
+  o.alpha = 1.0;
+  if (stage == 0 && job == 0) {  // T2 = (M M - 10 M + 25 I) / 16
+    o.A = r.M; o.B = r.M; o.C = r.T2; o.Cin = r.M;
+    o.alpha = 1.0 / 16.0; o.beta = -10.0 / 16.0; o.gamma = 25.0 / 16.0;
+  } else if (stage == 0) {  // X' = (5 X - X M) / 4
+    o.A = r.X; o.B = r.M; o.C = r.Xn; o.Cin = r.X;
+    o.alpha = -0.25; o.beta = 1.25;
+  } else if (stage == 1) {  // T4 = T2 T2
+    o.A = r.T2; o.B = r.T2; o.C = r.T4;
+  } else {  // M' = T4 M, written over T2 (dead after stage 1)
+    o.A = r.T4; o.B = r.M; o.C = r.T2;
+  }
+  return o;
+}
+
+template <typename T>
+__device__ __forceinline__ void sym_store(const StageOps<T>& o, int d, int gr, int gc, double v) {
+  if (gr < d && gc < d && gr <= gc) {
+    double val = o.alpha * v;
+    if (o.Cin) val += o.beta * (double)o.Cin[(int64_t)gr * d + gc];
+    if (gr == gc) val += o.gamma;
+    const T out = (T)val;
+    o.C[(int64_t)gr * d + gc] = out;
+    if (gr != gc) o.C[(int64_t)gc * d + gr] = out;
+  }
+}
+
+template <int VEC>
+__global__ __launch_bounds__(256) void newton_f64_kernel(const NewtonLaunch L) {
+  __shared__ double sA[F64Tile::BM * F64Tile::LDW];
+  __shared__ double sB[F64Tile::BN * F64Tile::LDW];
+  const StageJob s = stage_job(L, true);
+  if (!s.active) return;
+  const Roles64 r = roles64(s.region, s.d, L.t);
+  const StageOps<double> o = stage_ops<double>(r, L.stage, s.job);
+  const int m0 = s.ti * F64Tile::BM, n0 = s.tj * F64Tile::BN;
+  v4d acc[4][4];
+  f64_tile<double, false, VEC, double, false, VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, sA, sB, acc);
+  const int d = s.d;
+  f64_for_each(acc, [&](int rr, int cc, double v) { sym_store(o, d, m0 + rr, n0 + cc, v); });
+}
+
+template <int VEC>
+__global__ __launch_bounds__(256, 2) void newton_f32_kernel(const NewtonLaunch L) {
+  __shared__ float sA[F32Tile::BM * F32Tile::LDW];
+  __shared__ float sB[F32Tile::BN * F32Tile::LDW];
+  const StageJob s = stage_job(L, false);
+  if (!s.active) return;
+  const Roles32 r = roles32(s.region, s.d, L.t);
+  const StageOps<float> o = stage_ops<float>(r, L.stage, s.job);
+  const int m0 = s.ti * F32Tile::BM, n0 = s.tj * F32Tile::BN;
+  v16f acc[2][2];
+  f32_nt_tile<VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, sA, sB, acc);
+  const int d = s.d;
+  f32_for_each(acc, [&](int rr, int cc, float v) { sym_store(o, d, m0 + rr, n0 + cc, (double)v); });
+}
+
+// float64 M, X of iteration t -> float32 M, X of iteration t, for the
+// matrices whose switch iteration is t.
+__global__ __launch_bounds__(256) void newton_convert_kernel(const NewtonLaunch L) {
+  const int64_t b = blockIdx.x;
+  const NewtonClass& C = L.cls[find_class(L, b)];
+  const int local = (int)(b - C.block_begin);
+  const int mat = local / C.blocks_per_matrix;
+  const int chunk = local % C.blocks_per_matrix;
+  const RootState& st = L.state[C.slot_begin + mat];
+  const int t = L.t;
+  if (!(st.j == t && t < st.K)) return;
+  char* region = C.region + (int64_t)mat * C.matrix_bytes;
+  const Roles64 r64 = roles64(region, C.d, t);
+  const Roles32 r32 = roles32(region, C.d, t);
+  const int64_t n = (int64_t)C.d * C.d;
+  const int64_t per = 256 * 8;
+  const int64_t e0 = (int64_t)chunk * per;
+  for (int64_t e = e0 + threadIdx.x; e < min(n, e0 + per); e += 256) {
+    r32.M[e] = (float)r64.M[e];
+    r32.X[e] = (float)r64.X[e];
+  }
+}
+
+// ------------------------------------------------------------ finalize
+// X_out = c^(-1/4) X_K (float32), plus per-row-block partial sums of
+// |M_{K-1} - I|^2 for the residual.  Flagged matrices get their special
+// outputs: NaN (non-finite input / no usable bound), eps^(-1/4) I (zero trace).
+__global__ __launch_bounds__(256) void root_finalize_kernel(const RootBatch B) {
+  __shared__ double red[256];
+  const int64_t b = blockIdx.x;
+  const RootJob& J = B.job[find_job(B, b)];
+  const int blk = (int)(b - J.block_begin);
+  const RootState& st = B.state[J.slot];
+  const int d = J.d;
+  const int r0 = blk * kFinalRows, r1 = min(d, r0 + kFinalRows);
+  double res = 0.0;
+  if (st.K == 0) {
+    const bool zero_trace = (st.flags & MR_INFO_ZERO_TRACE) != 0;
+    const float diag = zero_trace ? (float)pow(B.eps, -0.25) : __builtin_nanf("");
+    const float off = zero_trace ? 0.f : __builtin_nanf("");
+    for (int r = r0; r < r1; ++r)
+      for (int c = threadIdx.x; c < d; c += 256) J.X[(int64_t)r * J.ldx + c] = (r == c) ? diag : off;
+  } else {
+    const int K = st.K, j = st.j;
+    const double sc = st.out_scale;
+    const bool x64 = K <= j;
+    const bool m64 = (K - 1) < j;
+    const Roles64 rx64 = roles64(J.region, d, K), rm64 = roles64(J.region, d, K - 1);
+    const Roles32 rx32 = roles32(J.region, d, K), rm32 = roles32(J.region, d, K - 1);
+    for (int r = r0; r < r1; ++r) {
+      for (int c = threadIdx.x; c < d; c += 256) {
+        const int64_t e = (int64_t)r * d + c;
+        const double x = x64 ? rx64.X[e] : (double)rx32.X[e];
+        J.X[(int64_t)r * J.ldx + c] = (float)(sc * x);
+        const double m = (m64 ? rm64.M[e] : (double)rm32.M[e]) - (r == c ? 1.0 : 0.0);
+        res += m * m;
+      }
+    }
+  }
+  res = block_sum_256(res, red);
+  if (threadIdx.x == 0) B.partial[(int64_t)J.slot * B.partial_stride + blk] = res;
+}
+
+// One wave per slot: residual of Newton matrices, convergence flag, info.
+__global__ __launch_bounds__(64) void root_info_kernel(RootState* state, const double* partial, int64_t stride,
+                                                       mr_root_info* info) {
+  __shared__ double red[64];
+  RootState& st = state[blockIdx.x];
+  const bool newton = st.method == MR_NEWTON;
+  double res = 0.0;
+  if (newton) {
+    const int nb = (st.d + kFinalRows - 1) / kFinalRows;
+    const double* p = partial + (int64_t)blockIdx.x * stride;
+    for (int i = threadIdx.x; i < nb; i += 64) res += p[i];
+  }
+  res = block_sum_64(res, red);
+  if (threadIdx.x != 0) return;
+  if (newton && st.K > 0) {
+    const double r = sqrt(res);
+    st.residual = (float)r;
+    if (!(r <= 2e-3 * sqrt((double)st.d))) st.flags |= MR_INFO_NOT_CONVERGED;
+  }
+  if (info) {
+    mr_root_info o;
+    o.scale = st.s;
+    o.bound = newton ? st.c : 0.0;
+    o.iters = newton ? st.K : st.sweeps;
+    o.fp64_iters = newton ? min(st.j, st.K) : 0;
+    o.residual = st.residual;
+    o.flags = st.flags;
+    info[st.problem] = o;
+  }
+}
+
+// ------------------------------------------------------------ launchers
+hipError_t launch_root_stats(const RootBatch& b, hipStream_t s) {
+  if (b.total_blocks <= 0) return hipSuccess;
+  if (b.a_f64)
+    hipLaunchKernelGGL(root_stats_kernel<double>, dim3(b.total_blocks), dim3(256), 0, s, b);
+  else
+    hipLaunchKernelGGL(root_stats_kernel<float>, dim3(b.total_blocks), dim3(256), 0, s, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_root_bound(RootState* state, const double* partial, int64_t partial_stride, int32_t slot_begin,
+                             int32_t nslots, int32_t normalize, double eps, int32_t k_cap, int32_t all_f64,
+                             hipStream_t s) {
+  if (nslots <= 0) return hipSuccess;
+  hipLaunchKernelGGL(root_bound_kernel, dim3(nslots), dim3(64), 0, s, state, partial, partial_stride, slot_begin,
+                     normalize, eps, k_cap, all_f64);
+  return hipGetLastError();
+}
+
+hipError_t launch_root_init(const RootBatch& b, hipStream_t s) {
+  if (b.total_blocks <= 0) return hipSuccess;
+  if (b.a_f64)
+    hipLaunchKernelGGL(root_init_kernel<double>, dim3(b.total_blocks), dim3(256), 0, s, b);
+  else
+    hipLaunchKernelGGL(root_init_kernel<float>, dim3(b.total_blocks), dim3(256), 0, s, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_newton_stage(const NewtonLaunch& L, bool f64, int vec, hipStream_t s) {
+  if (L.total_blocks <= 0) return hipSuccess;
+  if (f64) {
+    if (vec > 1)
+      hipLaunchKernelGGL(newton_f64_kernel<2>, dim3(L.total_blocks), dim3(256), 0, s, L);
+    else
+      hipLaunchKernelGGL(newton_f64_kernel<1>, dim3(L.total_blocks), dim3(256), 0, s, L);
+  } else {
+    if (vec == 4)
+      hipLaunchKernelGGL(newton_f32_kernel<4>, dim3(L.total_blocks), dim3(256), 0, s, L);
+    else
+      hipLaunchKernelGGL(newton_f32_kernel<1>, dim3(L.total_blocks), dim3(256), 0, s, L);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_newton_convert(const NewtonLaunch& L, hipStream_t s) {
+  if (L.total_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(newton_convert_kernel, dim3(L.total_blocks), dim3(256), 0, s, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_root_finalize(const RootBatch& b, hipStream_t s) {
+  if (b.total_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(root_finalize_kernel, dim3(b.total_blocks), dim3(256), 0, s, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_root_info(RootState* state, const double* partial, int64_t partial_stride, int32_t count,
+                            mr_root_info* info, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(root_info_kernel, dim3(count), dim3(64), 0, s, state, partial, partial_stride, info);
+  return hipGetLastError();
+}
+
+}  // namespace mr

@@ -1,0 +1,148 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol of
+include/matrix_roots.h, and rejects invalid arguments before enqueuing
+anything (validation never dereferences the device pointers it is given)."""
+
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import pytest
+
+from matrix_roots_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "matrix_roots.h")
+
+# fake, never-dereferenced "device" addresses, far apart and 256-byte aligned
+P1, P2, P3, P4, P5 = (0x10000000 * k for k in range(1, 6))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    kw = {"if", "while", "sizeof", "defined", "return"}
+    return sorted({n for n in names if n not in kw})
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_abi_version_and_strings(lib):
+    assert lib.mr_abi_version() == 1
+    for s in range(9):
+        assert lib.mr_status_string(s)
+    assert b"unknown" in lib.mr_status_string(99)
+
+
+def test_newton_iteration_count_matches_okls_page(lib):
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "okls_coupled_ns_iterations.json")))
+    k = lib.mr_newton_iterations(g["p"], g["m0"], g["tol"])
+    assert k in g["accept"], k
+    assert lib.mr_newton_iterations(3, 0.5, 1e-3) == -1
+    assert lib.mr_newton_iterations(4, 0.0, 1e-3) == -1
+    assert lib.mr_newton_iterations(4, 1.0, 1e-3) == 0
+    # p = 4 converges from 1e-6 faster than p = 2 per iteration count
+    assert lib.mr_newton_iterations(4, 1e-6, 1e-6) < lib.mr_newton_iterations(2, 1e-6, 1e-6)
+
+
+def gram(m, n, G=P1, ldg=None, L=P2, ldl=None, R=P3, ldr=None):
+    return B.GramProblem(m, n, G, ldg if ldg is not None else n, L, ldl if ldl is not None else m, R,
+                         ldr if ldr is not None else n)
+
+
+def call_gram(lib, probs, count=None, dt=B.MR_F64, beta=0.9, sides=3):
+    arr = (B.GramProblem * max(len(probs), 1))(*probs)
+    c = len(probs) if count is None else count
+    return lib.gram_ema_update(ctypes.addressof(arr) if probs else None, c, dt, beta, sides, None, 0, None)
+
+
+def test_gram_validation(lib):
+    assert call_gram(lib, [], count=0) == B.MR_OK  # empty batch is a no-op
+    assert call_gram(lib, [gram(4, 4)], count=-1) == 4
+    assert lib.gram_ema_update(None, 1, B.MR_F64, 0.9, 3, None, 0, None) == 1
+    assert call_gram(lib, [gram(4, 4)], dt=7) == 4
+    assert call_gram(lib, [gram(4, 4)], beta=1.0) == 4
+    assert call_gram(lib, [gram(4, 4)], beta=-0.1) == 4
+    assert call_gram(lib, [gram(4, 4)], beta=float("nan")) == 4
+    assert call_gram(lib, [gram(4, 4)], sides=0) == 4
+    assert call_gram(lib, [gram(4, 4)], sides=4) == 4
+    assert call_gram(lib, [gram(0, 4)]) == 2
+    assert call_gram(lib, [gram(4, 70000)]) == 2
+    assert call_gram(lib, [gram(4, 4, G=0)]) == 1
+    assert call_gram(lib, [gram(4, 4, L=0)]) == 1
+    assert call_gram(lib, [gram(4, 4, L=0)], sides=B.MR_RIGHT) != 1  # L unused
+    assert call_gram(lib, [gram(4, 8, ldg=7)]) == 3
+    assert call_gram(lib, [gram(4, 8, ldl=3)]) == 3
+    assert call_gram(lib, [gram(4, 8, ldr=7)]) == 3
+    assert call_gram(lib, [gram(4, 8, L=P1 + 16)]) == 8  # L inside G
+    assert call_gram(lib, [gram(4, 8, R=P2 + 8)]) == 8  # R overlaps L
+    assert call_gram(lib, [gram(4, 8, L=P2 + 4)]) == 4  # misaligned float64 state
+    # the second problem is bad: nothing may be enqueued for the first either
+    assert call_gram(lib, [gram(4, 4), gram(4, 4, G=0)]) == 1
+    assert b"problem 1" in lib.mr_last_error_message()
+
+
+def root(d, A=P1, lda=None, X=P2, ldx=None):
+    return B.RootProblem(d, A, lda if lda is not None else d, X, ldx if ldx is not None else d)
+
+
+def call_root(lib, probs, dt=B.MR_F32, eps=1e-6, norm=1, method=0, ws=None, ws_bytes=0):
+    arr = (B.RootProblem * len(probs))(*probs)
+    return lib.inv_quarter_root_batched(ctypes.addressof(arr), len(probs), dt, eps, norm, method, None, ws, ws_bytes,
+                                        None)
+
+
+def test_root_validation(lib):
+    assert call_root(lib, [root(8)], eps=0.0) == 4
+    assert call_root(lib, [root(8)], eps=float("inf")) == 4
+    assert call_root(lib, [root(8)], norm=2) == 4
+    assert call_root(lib, [root(8)], method=9) == 4
+    assert call_root(lib, [root(8)], dt=3) == 4
+    assert call_root(lib, [root(0)]) == 2
+    assert call_root(lib, [root(8, A=0)]) == 1
+    assert call_root(lib, [root(8, lda=7)]) == 3
+    assert call_root(lib, [root(8, ldx=4)]) == 3
+    assert call_root(lib, [root(8, X=P1 + 64)]) == 8
+    assert call_root(lib, [root(200)], method=B.MR_JACOBI) == 7
+    # valid request, no workspace: rejected before any launch
+    assert call_root(lib, [root(200)]) == 5
+    probs = (B.RootProblem * 2)(root(64), root(300, A=P3, X=P4))
+    need = lib.inv_quarter_root_batched_workspace(ctypes.addressof(probs), 2, B.MR_F32, 0)
+    assert need >= 40 * 300 * 300 + 8 * 64 * 64
+    assert call_root(lib, [root(64), root(300, A=P3, X=P4)], ws=P5, ws_bytes=need - 1) == 5
+    assert call_root(lib, [root(64), root(300, A=P3, X=P4)], ws=P5 + 8, ws_bytes=need) == 5
+
+
+def apply_p(m, n, XL=P1, G=P2, XR=P3, U=P4, ldu=None):
+    return B.ApplyProblem(m, n, XL, m, G, n, XR, n, U, ldu if ldu is not None else n)
+
+
+def test_apply_validation(lib):
+    def call(probs, alpha=1.0, ws=None, ws_bytes=0):
+        arr = (B.ApplyProblem * len(probs))(*probs)
+        return lib.precondition_apply(ctypes.addressof(arr), len(probs), alpha, ws, ws_bytes, None)
+
+    assert call([apply_p(4, 8)], alpha=float("nan")) == 4
+    assert call([apply_p(0, 8)]) == 2
+    assert call([apply_p(4, 8, XR=0)]) == 1
+    assert call([apply_p(4, 8, ldu=7)]) == 3
+    assert call([apply_p(4, 8, U=P2 + 4)]) == 8
+    arr = (B.ApplyProblem * 1)(apply_p(4, 8))
+    need = lib.precondition_apply_workspace(ctypes.addressof(arr), 1)
+    assert need == 256
+    assert call([apply_p(4, 8)], ws=None, ws_bytes=0) == 5
