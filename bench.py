@@ -1,0 +1,234 @@
+"""Throughput of the EMA-Gram quarter-power preconditioner step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload w1024]
+
+One step = one pass of the whole hot path over one batch of synthetic
+gradients already resident in HBM: gram_ema_update for every weight (both
+Grams, float64 state), inv_quarter_root_batched over all 2 x weights Grams
+(trace rescale, eps = 1e-6), precondition_apply for every weight.  The
+default workload is the width-1024 transformer weight set (8 layers x
+{q,k,v,o 1024x1024, up 1024x4096, down 4096x1024}, rank-32 + noise
+gradients); the Gram state evolves across steps and the gradients cycle
+through the workload's 5 seeded steps.
+
+Printed: one JSON line with matrix updates/s, the dominant kernel's roofline
+(algorithmic flops / event-measured launch time on the library's stream) and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6}  # MI355X dense MFMA (vendor figures)
+METRIC = "preconditioned matrix updates/sec + TFLOP/s as % fp32 MFMA peak, d=1024–4096"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def sym_gemm_flops(d: int) -> float:
+    """One symmetric-output product of d x d matrices: d(d+1)/2 outputs x d MACs x 2."""
+    return float(d) * d * (d + 1)
+
+
+def newton_flops(d: int, K: int, j: int):
+    """Algorithmic (upper-triangle) flops of one Newton root: iterations t < K-1
+    take 4 symmetric products, the last one 1; t < j run in float64."""
+    f64 = f32 = 0.0
+    for t in range(K):
+        g = (4 if t < K - 1 else 1) * sym_gemm_flops(d)
+        if t < j:
+            f64 += g
+        else:
+            f32 += g
+    return f64, f32
+
+
+def cpu_baseline(workload: str):
+    """The fp64 oracle (as it stands): one step from zero state (Gram EMA, two
+    eigendecomposition roots, apply) on one weight of each distinct shape
+    class of layer 0; the per-layer time is the shape-count-weighted sum."""
+    import oracle
+    from matrix_roots_amd import workloads as W
+
+    try:
+        import threadpoolctl
+
+        cores = max(int(i.get("num_threads", 1)) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    wl = W.WORKLOADS[workload]
+    layer = [i for i, (name, _, _) in enumerate(wl.shapes) if name.startswith("L0.")] or [0, 1]
+    classes = {}
+    for i in layer:
+        _, m, n = wl.shapes[i]
+        key = (min(m, n), max(m, n))  # m x n and n x m cost the same
+        classes.setdefault(key, []).append(i)
+    per_layer = 0.0
+    timed = []
+    for key, members in classes.items():
+        i = members[0]
+        _, m, n = wl.shapes[i]
+        G = W.gradient(workload, i, 1)
+        t0 = time.perf_counter()
+        oracle.preconditioner_step(np.zeros((m, m)), np.zeros((n, n)), G, wl.beta, wl.eps)
+        dt = time.perf_counter() - t0
+        per_layer += dt * len(members)
+        timed.append(f"{wl.shapes[i][0]} {m}x{n}: {dt:.2f}s x{len(members)}")
+    sample = ("one step from zero state of one weight per shape class of layer 0 (" + "; ".join(timed)
+              + f"), scaled to the layer's {len(layer)} weights; fp64 numpy/LAPACK")
+    return {"value": len(layer) / per_layer, "unit": "matrix updates/s", "cores": cores, "kind": "oracle",
+            "sample": sample, "seconds": sum(float(x.split(": ")[1].split("s")[0]) for x in timed)}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="w1024", choices=["toy", "w1024", "w2048", "moe"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--state-dtype", default="f64", choices=["f64", "f32"])
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path has no "
+              f"cross-GPU exchange to time)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from matrix_roots_amd import binding as B
+    from matrix_roots_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    B.library()
+    dev = torch.device("cuda:0")
+    wl = W.WORKLOADS[args.workload]
+    shapes = [(m, n) for _, m, n in wl.shapes]
+    nw = len(shapes)
+    log(f"workload {args.workload}: {nw} weights, generating {wl.steps} steps of gradients")
+    t0 = time.perf_counter()
+    grads = []
+    for t in range(1, wl.steps + 1):
+        grads.append([torch.from_numpy(W.gradient(args.workload, w, t)).to(dev) for w in range(nw)])
+        log(f"  step {t} gradients resident ({time.perf_counter() - t0:.1f}s)")
+    sdt = torch.float64 if args.state_dtype == "f64" else torch.float32
+    Ls = [torch.zeros(m, m, dtype=sdt, device=dev) for m, n in shapes]
+    Rs = [torch.zeros(n, n, dtype=sdt, device=dev) for m, n in shapes]
+    Xs = [torch.empty(m, m, dtype=torch.float32, device=dev) for m, n in shapes] + \
+         [torch.empty(n, n, dtype=torch.float32, device=dev) for m, n in shapes]
+    Us = [torch.empty(m, n, dtype=torch.float32, device=dev) for m, n in shapes]
+    ws = B.RootWorkspace()
+    total = args.warmup + args.steps
+    infos = [torch.empty(32 * 2 * nw, dtype=torch.uint8, device=dev) for _ in range(total)]
+
+    def step(i):
+        G = grads[i % wl.steps]
+        B.gram_ema_update(G, Ls, Rs, wl.beta)
+        B.inv_quarter_root_batched(Ls + Rs, wl.eps, normalize=wl.normalize, Xs=Xs, workspace=ws,
+                                   return_info=False, info_out=infos[i])
+        B.precondition_apply(Xs[:nw], G, Xs[nw:], Us=Us)
+
+    for i in range(args.warmup):
+        step(i)
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+    B.trace_collect()
+    B.trace_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    B.trace_enable(False)
+    trace = B.trace_collect()
+    log(f"timed {args.steps} steps in {t1 - t0:.3f}s")
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = nw / (ms_per_step / 1e3)
+
+    # algorithmic work over the timed steps
+    f64 = f32 = 0.0
+    iters = []
+    for i in range(args.warmup, total):
+        info = B.decode_info(infos[i], 2 * nw)
+        assert (info["flags"] == 0).all(), info[info["flags"] != 0]
+        for k, rec in enumerate(info):
+            d = shapes[k % nw][0] if k < nw else shapes[k % nw][1]
+            if d <= 128:
+                continue
+            a, b = newton_flops(d, int(rec["iters"]), int(rec["fp64_iters"]))
+            f64 += a
+            f32 += b
+            iters.append((int(rec["iters"]), int(rec["fp64_iters"])))
+    syrk = sum(m * (m + 1) * n + n * (n + 1) * m for m, n in shapes) * args.steps
+    apply_f = sum(2.0 * m * n * (m + n) for m, n in shapes) * args.steps
+    step_flops = (f64 + f32 + syrk + apply_f) / args.steps
+
+    kernels = {}
+    for name, (launches, ms) in sorted(trace.items()):
+        flops = {"newton_f64": f64, "newton_f32": f32, "syrk_ema": syrk, "apply_f32": apply_f}.get(name)
+        ent = {"launches": launches, "ms_total": round(ms, 3), "ms_avg": round(ms / launches, 4)}
+        if flops:
+            prec = "f64" if name in ("newton_f64", "syrk_ema") else "f32"
+            tf = flops / (ms / 1e3) / 1e12
+            ent.update({"tflops": round(tf, 2), "peak": PEAK_TFLOPS[prec], "frac": round(tf / PEAK_TFLOPS[prec], 4)})
+        kernels[name] = ent
+    dom = max(kernels.items(), key=lambda kv: kv[1]["ms_total"])
+    dname, dk = dom
+    roofline = {"bound": "mfma", "kernel": dname, "achieved": dk.get("tflops"), "peak": dk.get("peak"),
+                "unit": "TFLOP/s", "frac": dk.get("frac"), "traffic": None,
+                "achieved_per_launch": "algorithmic flops of the class over the timed steps / sum of its "
+                                       "event-measured launch durations"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on its sample")
+        cpu = cpu_baseline(args.workload)
+        log(f"oracle: {cpu['value']:.4f} matrix updates/s on {cpu['cores']} threads ({cpu['seconds']:.1f}s)")
+
+    kmin = min((k for k, _ in iters), default=0)
+    kmax = max((k for k, _ in iters), default=0)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "matrix updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64+f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "weights": nw, "grams_per_step": 2 * nw,
+                   "shapes": sorted({f"{m}x{n}" for m, n in shapes}), "beta": wl.beta, "eps": wl.eps,
+                   "normalize": wl.normalize, "state_dtype": args.state_dtype},
+        "tflops": round(step_flops / (ms_per_step / 1e3) / 1e12, 2),
+        "pct_fp32_mfma_peak": round(100 * step_flops / (ms_per_step / 1e3) / 1e12 / PEAK_TFLOPS["f32"], 2),
+        "newton_iters": {"min": kmin, "max": kmax},
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

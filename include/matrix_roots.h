@@ -202,6 +202,22 @@ size_t precondition_apply_workspace(const mr_apply_problem* problems, int32_t co
  * of M follows).  p in {2, 4}.  Host-only; returns -1 on bad arguments. */
 int32_t mr_newton_iterations(int32_t p, double m0, double tol);
 
+/*
+ * Kernel-class tracing: when enabled, every launch the library makes is
+ * bracketed by a pair of HIP events recorded on the launch's own stream
+ * (host-side bookkeeping only; events come from a pool created once).
+ * mr_trace_collect waits for the traced launches, writes one record per
+ * kernel class that ran (at most `capacity`), clears the log and returns the
+ * number of records.  Not for concurrent use from several threads.
+ */
+typedef struct {
+  char name[32];    /* kernel class, e.g. "newton_f32"             */
+  int64_t launches; /* traced launches of this class               */
+  double total_ms;  /* sum of event-measured launch durations      */
+} mr_trace_record;
+int32_t mr_trace_enable(int32_t on); /* returns the previous setting */
+int32_t mr_trace_collect(mr_trace_record* out, int32_t capacity);
+
 const char* mr_status_string(mr_status status);
 const char* mr_last_error_message(void);
 int32_t mr_abi_version(void);

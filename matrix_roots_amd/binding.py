@@ -34,6 +34,8 @@ EXPORTED = (
     "precondition_apply",
     "precondition_apply_workspace",
     "mr_newton_iterations",
+    "mr_trace_enable",
+    "mr_trace_collect",
     "mr_status_string",
     "mr_last_error_message",
     "mr_abi_version",
@@ -59,6 +61,10 @@ class ApplyProblem(ctypes.Structure):
 ROOT_INFO_DTYPE = np.dtype([("scale", "<f8"), ("bound", "<f8"), ("iters", "<i4"), ("fp64_iters", "<i4"),
                             ("residual", "<f4"), ("flags", "<u4")])
 assert ROOT_INFO_DTYPE.itemsize == 32
+
+
+class TraceRecord(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
 
 
 class MatrixRootsError(RuntimeError):
@@ -94,6 +100,10 @@ def library() -> ctypes.CDLL:
     lib.precondition_apply_workspace.restype = sz
     lib.mr_newton_iterations.argtypes = [i32, f64, f64]
     lib.mr_newton_iterations.restype = i32
+    lib.mr_trace_enable.argtypes = [i32]
+    lib.mr_trace_enable.restype = i32
+    lib.mr_trace_collect.argtypes = [vp, i32]
+    lib.mr_trace_collect.restype = i32
     lib.mr_status_string.argtypes = [i32]
     lib.mr_status_string.restype = ctypes.c_char_p
     lib.mr_last_error_message.argtypes = []
@@ -183,11 +193,14 @@ class RootWorkspace:
 
 def inv_quarter_root_batched(As: Sequence, eps: float, normalize: str = "trace", method: str = "auto",
                              Xs: Optional[Sequence] = None, workspace: Optional[RootWorkspace] = None,
-                             stream=None, return_info: bool = True):
+                             stream=None, return_info: bool = True, info_out=None):
     """X_i = (A_i/s_i + eps I)^(-1/4) for every (d, d) device tensor A_i.
 
     Returns (Xs, info) where info is a numpy structured array (fields of
     mr_root_info) read after synchronising the stream, or (Xs, None).
+    info_out: optional device uint8 tensor of 32*len(As) bytes that receives
+    the info records instead of the workspace's buffer (no synchronisation
+    when return_info is False); decode it later with decode_info().
     """
     import torch
 
@@ -209,13 +222,22 @@ def inv_quarter_root_batched(As: Sequence, eps: float, normalize: str = "trace",
     need = lib.inv_quarter_root_batched_workspace(ctypes.addressof(probs), count, dt, m)
     ws = workspace or RootWorkspace()
     buf, info = ws.get(need, count, dev)
+    if info_out is not None:
+        if info_out.numel() < 32 * count:
+            raise ValueError("info_out too small")
+        info = info_out
     _check(lib.inv_quarter_root_batched(ctypes.addressof(probs), count, dt, float(eps), _NORMS[normalize], m,
                                         _ptr(info), _ptr(buf), buf.numel(), _stream(stream)))
     if not return_info:
         return Xs, None
     torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+    return Xs, decode_info(info, count)
+
+
+def decode_info(info, count: int):
+    """Device or host uint8 buffer of mr_root_info records -> numpy records."""
     host = info[: 32 * count].cpu().numpy()
-    return Xs, host.view(ROOT_INFO_DTYPE).copy()
+    return host.view(ROOT_INFO_DTYPE).copy()
 
 
 def precondition_apply(XLs: Sequence, Gs: Sequence, XRs: Sequence, alpha: float = 1.0,
@@ -245,3 +267,15 @@ def precondition_apply(XLs: Sequence, Gs: Sequence, XRs: Sequence, alpha: float 
 
 def newton_iterations(p: int, m0: float, tol: float) -> int:
     return int(library().mr_newton_iterations(p, m0, tol))
+
+
+def trace_enable(on: bool = True) -> bool:
+    """Bracket every library launch with HIP events on its stream."""
+    return bool(library().mr_trace_enable(1 if on else 0))
+
+
+def trace_collect() -> dict:
+    """{kernel class: (launches, total_ms)} since the last collect (waits for them)."""
+    recs = (TraceRecord * 32)()
+    k = library().mr_trace_collect(ctypes.addressof(recs), 32)
+    return {recs[i].name.decode(): (int(recs[i].launches), float(recs[i].total_ms)) for i in range(k)}

@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -71,6 +72,50 @@ mr_status check_launch(hipError_t e, hipStream_t s, const char* what) {
 }
 
 int tiles(int64_t d, int t) { return (int)((d + t - 1) / t); }
+
+// ------------------------------------------------------------ tracing
+enum TraceClass {
+  kTrSyrk, kTrApply, kTrJacobi, kTrStats, kTrBound, kTrInit, kTrNewton64, kTrNewton32, kTrConvert,
+  kTrFinalize, kTrInfo, kTrCount
+};
+const char* const kTraceNames[kTrCount] = {"syrk_ema", "apply_f32", "jacobi", "root_stats", "root_bound",
+                                           "root_init", "newton_f64", "newton_f32", "newton_convert",
+                                           "root_finalize", "root_info"};
+struct TraceEntry {
+  int cls;
+  hipEvent_t a, b;
+};
+struct Trace {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  std::vector<TraceEntry> log;
+  std::mutex mu;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+Trace g_trace;
+
+// Launch through `fn`; in trace mode bracket it with events on its stream.
+template <class F>
+mr_status traced(int cls, bool nonempty, hipStream_t s, F&& fn, const char* what) {
+  if (!g_trace.on || !nonempty) return check_launch(fn(), s, what);
+  std::lock_guard<std::mutex> lk(g_trace.mu);
+  hipEvent_t a = g_trace.get(), b = g_trace.get();
+  if (!a || !b) return fail(MR_ERR_HIP, "%s: hipEventCreate failed", what);
+  hipError_t e = hipEventRecord(a, s);
+  if (e == hipSuccess) e = fn();
+  if (e == hipSuccess) e = hipEventRecord(b, s);
+  g_trace.log.push_back({cls, a, b});
+  return check_launch(e, s, what);
+}
 
 // ------------------------------------------------------------ root layout
 struct RootPlan {
@@ -161,6 +206,41 @@ const char* mr_status_string(mr_status s) {
   }
 }
 
+int32_t mr_trace_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_trace.mu);
+  const int32_t prev = g_trace.on ? 1 : 0;
+  g_trace.on = on != 0;
+  return prev;
+}
+
+int32_t mr_trace_collect(mr_trace_record* out, int32_t capacity) {
+  std::lock_guard<std::mutex> lk(g_trace.mu);
+  double ms[kTrCount] = {0};
+  int64_t n[kTrCount] = {0};
+  for (const TraceEntry& t : g_trace.log) {
+    float e = 0.f;
+    if (hipEventSynchronize(t.b) == hipSuccess && hipEventElapsedTime(&e, t.a, t.b) == hipSuccess) {
+      ms[t.cls] += e;
+      n[t.cls] += 1;
+    }
+    g_trace.pool.push_back(t.a);
+    g_trace.pool.push_back(t.b);
+  }
+  g_trace.log.clear();
+  int32_t k = 0;
+  for (int c = 0; c < kTrCount; ++c) {
+    if (n[c] == 0) continue;
+    if (out && k < capacity) {
+      memset(out[k].name, 0, sizeof out[k].name);
+      strncpy(out[k].name, kTraceNames[c], sizeof out[k].name - 1);
+      out[k].launches = n[c];
+      out[k].total_ms = ms[c];
+    }
+    ++k;
+  }
+  return std::min(k, capacity);
+}
+
 int32_t mr_newton_iterations(int32_t p, double m0, double tol) {
   if (!(p == 2 || p == 4) || !(m0 > 0.0 && m0 <= 1.0) || !(tol > 0.0 && tol < 1.0)) return -1;
   double m = m0;
@@ -231,7 +311,8 @@ mr_status gram_ema_update(const mr_gram_problem* p, int32_t count, mr_dtype dt, 
       b.beta = beta;
       auto flush = [&]() -> mr_status {
         if (b.njobs == 0) return MR_OK;
-        mr_status r = check_launch(launch_syrk_ema(b, right, dt == MR_F64, vec, s), s, "gram_ema_update launch");
+        mr_status r = traced(kTrSyrk, b.total_blocks > 0, s, [&] { return launch_syrk_ema(b, right, dt == MR_F64, vec, s); },
+                             "gram_ema_update launch");
         b.njobs = 0;
         b.total_blocks = 0;
         return r;
@@ -316,7 +397,8 @@ mr_status precondition_apply(const mr_apply_problem* p, int32_t count, float alp
       memset(&b, 0, sizeof b);
       auto flush = [&]() -> mr_status {
         if (b.njobs == 0) return MR_OK;
-        mr_status r = check_launch(launch_f32_nt(b, vec, s), s, "precondition_apply launch");
+        mr_status r = traced(kTrApply, b.total_blocks > 0, s, [&] { return launch_f32_nt(b, vec, s); },
+                             "precondition_apply launch");
         b.njobs = 0;
         b.total_blocks = 0;
         return r;
@@ -425,7 +507,8 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
       J.slot = slot;
       J.problem = P.slot_problem[slot];
       if (jb.njobs == kMaxJobs || slot == count - 1) {
-        if ((st = check_launch(launch_jacobi(jb, s), s, "jacobi launch")) != MR_OK) return st;
+        if ((st = traced(kTrJacobi, jb.njobs > 0, s, [&] { return launch_jacobi(jb, s); }, "jacobi launch")) != MR_OK)
+          return st;
         jb.njobs = 0;
       }
     }
@@ -465,9 +548,10 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
           b.total_blocks += J.nblocks;
           ++b.njobs;
           if (b.njobs == kMaxJobs || slot == P.n_newton - 1) {
-            hipError_t e = kind == 0 ? launch_root_stats(b, s) : kind == 1 ? launch_root_init(b, s)
-                                                                           : launch_root_finalize(b, s);
-            mr_status r = check_launch(e, s, "root launch");
+            const int cls = kind == 0 ? kTrStats : kind == 1 ? kTrInit : kTrFinalize;
+            mr_status r = traced(cls, b.total_blocks > 0, s, [&] {
+              return kind == 0 ? launch_root_stats(b, s) : kind == 1 ? launch_root_init(b, s) : launch_root_finalize(b, s);
+            }, "root launch");
             if (r != MR_OK) return r;
             b.njobs = 0;
             b.total_blocks = 0;
@@ -488,9 +572,10 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
       k_cap = 100;
       j_cap = 100;
     }
-    if ((st = check_launch(launch_root_bound(state, partial, P.partial_stride, 0, P.n_newton, normalize, eps, k_cap,
-                                             all_f64 ? 1 : 0, s),
-                           s, "root bound launch")) != MR_OK)
+    if ((st = traced(kTrBound, true, s, [&] {
+           return launch_root_bound(state, partial, P.partial_stride, 0, P.n_newton, normalize, eps, k_cap,
+                                    all_f64 ? 1 : 0, s);
+         }, "root bound launch")) != MR_OK)
       return st;
     int k_max = k_cap, j_max = all_f64 ? k_cap : j_cap;
     if (normalize != MR_NORM_TRACE) {
@@ -559,18 +644,21 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
     for (int t = 0; t < k_max; ++t) {
       if (t <= j_max && !all_f64) {
         for (const auto& g : groups)
-          if ((st = check_launch(launch_newton_convert(make_launch(g, 1, 0, t), s), s, "newton convert")) != MR_OK)
+          if ((st = traced(kTrConvert, true, s, [&] { return launch_newton_convert(make_launch(g, 1, 0, t), s); },
+                           "newton convert")) != MR_OK)
             return st;
       }
       for (int stage = 0; stage < 3; ++stage) {
         for (const auto& g : groups) {
           const NewtonLaunch L = make_launch(g, 0, stage, t);
           if (t < j_max) {
-            if ((st = check_launch(launch_newton_stage(L, true, g.vec64, s), s, "newton f64 stage")) != MR_OK)
+            if ((st = traced(kTrNewton64, true, s, [&] { return launch_newton_stage(L, true, g.vec64, s); },
+                             "newton f64 stage")) != MR_OK)
               return st;
           }
           if (!all_f64) {
-            if ((st = check_launch(launch_newton_stage(L, false, g.vec32, s), s, "newton f32 stage")) != MR_OK)
+            if ((st = traced(kTrNewton32, true, s, [&] { return launch_newton_stage(L, false, g.vec32, s); },
+                             "newton f32 stage")) != MR_OK)
               return st;
           }
         }
@@ -579,7 +667,8 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
     if ((st = run_root_batches(2)) != MR_OK) return st;
   }
 
-  return check_launch(launch_root_info(state, partial, P.partial_stride, count, info_dev, s), s, "root info");
+  return traced(kTrInfo, true, s, [&] { return launch_root_info(state, partial, P.partial_stride, count, info_dev, s); },
+                "root info");
 }
 
 }  // extern "C"
