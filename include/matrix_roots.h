@@ -161,8 +161,9 @@ size_t gram_ema_update_workspace(const mr_gram_problem* problems, int32_t count,
  *    X = V f V^T.
  *  - MR_NEWTON: coupled Newton iteration for the inverse 4th root,
  *        M0 = (A/s + eps I)/c, X0 = I, T = (5 I - M)/4, X <- X T, M <- T^4 M,
- *    X = c^(-1/4) X_K, run in float64 while the smallest eigenvalue of M is
- *    below 1e-2 (by the scalar recurrence), then in float32.  The GEMM-only
+ *    X = c^(-1/4) X_K, with M scaled by 1/s_t before each step (per-step
+ *    scales from the spectrum bounds, see mr_newton_schedule), run in float64
+ *    while the smallest eigenvalue of M is below 1e-2, then in float32.  The GEMM-only
  *    route of tilderesearch, "Online KL Shampoo", sections 2.1-2.2 (there
  *    for the -1/2 root), taken to the 4th root.  c = 1.01 times the
  *    Wolkowicz-Styan upper bound on lambda_max(A/s + eps I) (the OKLS page,
@@ -217,6 +218,12 @@ typedef struct {
 } mr_trace_record;
 int32_t mr_trace_enable(int32_t on); /* returns the previous setting */
 int32_t mr_trace_collect(mr_trace_record* out, int32_t capacity);
+
+/* The step scales the library uses for a Newton root whose spectrum bound is
+ * [m0, 1/1.01] (m0 = eps/c): writes min(K, capacity) scales s_t, stores the
+ * count of float64 steps in *fp64_steps (may be NULL) and returns K, the
+ * number of steps (-1 on bad arguments).  Host-only. */
+int32_t mr_newton_schedule(double m0, double* scales, int32_t capacity, int32_t* fp64_steps);
 
 const char* mr_status_string(mr_status status);
 const char* mr_last_error_message(void);

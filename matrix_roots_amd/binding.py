@@ -34,6 +34,7 @@ EXPORTED = (
     "precondition_apply",
     "precondition_apply_workspace",
     "mr_newton_iterations",
+    "mr_newton_schedule",
     "mr_trace_enable",
     "mr_trace_collect",
     "mr_status_string",
@@ -100,6 +101,8 @@ def library() -> ctypes.CDLL:
     lib.precondition_apply_workspace.restype = sz
     lib.mr_newton_iterations.argtypes = [i32, f64, f64]
     lib.mr_newton_iterations.restype = i32
+    lib.mr_newton_schedule.argtypes = [f64, vp, i32, vp]
+    lib.mr_newton_schedule.restype = i32
     lib.mr_trace_enable.argtypes = [i32]
     lib.mr_trace_enable.restype = i32
     lib.mr_trace_collect.argtypes = [vp, i32]
@@ -263,6 +266,16 @@ def precondition_apply(XLs: Sequence, Gs: Sequence, XRs: Sequence, alpha: float 
         ws.record_stream(stream)
     _check(lib.precondition_apply(ctypes.addressof(probs), count, float(alpha), _ptr(ws), need, _stream(stream)))
     return Us
+
+
+def newton_schedule(m0: float):
+    """(scales, fp64_steps) of the library's Newton schedule for floor m0."""
+    buf = (ctypes.c_double * 128)()
+    j = ctypes.c_int32(0)
+    K = library().mr_newton_schedule(float(m0), ctypes.addressof(buf), 128, ctypes.addressof(j))
+    if K < 0:
+        raise ValueError("bad m0")
+    return [buf[i] for i in range(K)], int(j.value)
 
 
 def newton_iterations(p: int, m0: float, tol: float) -> int:

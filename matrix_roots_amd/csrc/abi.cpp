@@ -128,7 +128,7 @@ struct RootPlan {
     size_t region_off, matrix_bytes;
   };
   std::vector<Cls> classes;
-  size_t state_off = 0, partial_off = 0, jac_off = 0;
+  size_t state_off = 0, partial_off = 0, sched_off = 0, jac_off = 0;
   int64_t partial_stride = 0;
   std::vector<size_t> jac_w_off;  // per Jacobi slot (index slot - n_newton)
   size_t total = 0;
@@ -169,6 +169,8 @@ RootPlan plan_root(const mr_root_problem* p, int32_t count, int32_t method) {
   P.partial_stride = std::max<int64_t>(P.partial_stride, 1);
   P.partial_off = off;
   off = align256(off + sizeof(double) * (size_t)P.partial_stride * (size_t)std::max(P.n_newton, 1));
+  P.sched_off = off;
+  off = align256(off + sizeof(double) * kMaxNewtonIters * (size_t)std::max(P.n_newton, 1));
   P.jac_off = off;
   for (size_t k = 0; k < jac.size(); ++k) {
     P.jac_w_off.push_back(off);
@@ -239,6 +241,17 @@ int32_t mr_trace_collect(mr_trace_record* out, int32_t capacity) {
     ++k;
   }
   return std::min(k, capacity);
+}
+
+int32_t mr_newton_schedule(double m0, double* scales, int32_t capacity, int32_t* fp64_steps) {
+  if (!(m0 > 0.0 && m0 <= 1.0 / kBoundSafety) || capacity < 0) return -1;
+  double tmp[kMaxNewtonIters];
+  int K = 0, j = 0;
+  newton_scaled_schedule(m0, 1.0 / kBoundSafety, kNewtonTol, kSwitchM, kMaxNewtonIters, tmp, &K, &j);
+  if (scales)
+    for (int i = 0; i < K && i < capacity; ++i) scales[i] = tmp[i];
+  if (fp64_steps) *fp64_steps = j;
+  return K;
 }
 
 int32_t mr_newton_iterations(int32_t p, double m0, double tol) {
@@ -483,6 +496,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
   char* base = static_cast<char*>(ws);
   RootState* state = reinterpret_cast<RootState*>(base + P.state_off);
   double* partial = reinterpret_cast<double*>(base + P.partial_off);
+  double* sched = reinterpret_cast<double*>(base + P.sched_off);
   const int a_f64 = dt == MR_F64;
   const bool all_f64 = method == MR_NEWTON_F64;
 
@@ -564,16 +578,18 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
     if ((st = run_root_batches(0)) != MR_OK) return st;
 
     // Iteration cap known on the host.  Trace mode: c <= 1.01 (1 + eps) up to
-    // rounding, so no matrix needs more than K(eps / (1.02 (1 + eps))).
+    // rounding, so no matrix needs more steps than the schedule from the
+    // floor eps / (1.02 (1 + eps)).
     int k_cap, j_cap;
     if (normalize == MR_NORM_TRACE) {
-      newton_schedule(eps / (1.02 * (1.0 + eps)), kNewtonTol, kSwitchM, 1000, &k_cap, &j_cap);
+      newton_scaled_schedule(eps / (1.02 * (1.0 + eps)), 1.0 / kBoundSafety, kNewtonTol, kSwitchM, kMaxNewtonIters,
+                             nullptr, &k_cap, &j_cap);
     } else {
-      k_cap = 100;
-      j_cap = 100;
+      k_cap = kMaxNewtonIters;
+      j_cap = kMaxNewtonIters;
     }
     if ((st = traced(kTrBound, true, s, [&] {
-           return launch_root_bound(state, partial, P.partial_stride, 0, P.n_newton, normalize, eps, k_cap,
+           return launch_root_bound(state, partial, P.partial_stride, sched, 0, P.n_newton, normalize, eps, k_cap,
                                     all_f64 ? 1 : 0, s);
          }, "root bound launch")) != MR_OK)
       return st;
@@ -622,6 +638,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
       L.stage = stage;
       L.t = t;
       L.state = state;
+      L.sched = sched;
       for (int ci : g.cls) {
         const auto& c = P.classes[ci];
         NewtonClass& C = L.cls[L.ncls++];

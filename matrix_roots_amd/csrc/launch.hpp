@@ -121,6 +121,7 @@ struct NewtonLaunch {
   int32_t stage;  // GEMM stages: 0 -> T2 and X', 1 -> T4, 2 -> M'
   int32_t t;      // iteration
   RootState* state;
+  const double* sched;  // per slot: kMaxNewtonIters step scales
 };
 
 // ------------------------------------------------------------ Jacobi
@@ -151,7 +152,7 @@ hipError_t launch_syrk_ema(const SyrkBatch& b, bool right, bool f64_state, int v
 hipError_t launch_f32_nt(const F32Batch& b, int vec, hipStream_t s);
 
 hipError_t launch_root_stats(const RootBatch& b, hipStream_t s);
-hipError_t launch_root_bound(RootState* state, const double* partial, int64_t partial_stride,
+hipError_t launch_root_bound(RootState* state, const double* partial, int64_t partial_stride, double* sched,
                              int32_t slot_begin, int32_t nslots, int32_t normalize, double eps,
                              int32_t k_cap, int32_t all_f64, hipStream_t s);
 hipError_t launch_root_init(const RootBatch& b, hipStream_t s);

@@ -3,8 +3,11 @@
 // p-th root with p = 4:
 //
 //   M0 = (A/s + eps I) / c,  X0 = I,
-//   T_t = (5 I - M_t) / 4,  X_{t+1} = X_t T_t,  M_{t+1} = T_t^4 M_t,
-//   X = c^(-1/4) X_K.
+//   T_t = (5 I - M_t / s_t) / 4,  X_{t+1} = s_t^(-1/4) X_t T_t,
+//   M_{t+1} = T_t^4 M_t / s_t,  X = c^(-1/4) X_K,
+//
+// with per-step scales s_t from the scalar schedule (schedule.hpp; s_t = 1
+// is the classical iteration).
 //
 // The pages' step is "rescale, add a regulariser to the eigenvalues, raise to
 // -1/4, rebuild" (marin.community, "Sharding EMA-Gram eigensolves", section
@@ -13,10 +16,11 @@
 // the p = 2 member (coupled Newton-Schulz for S^(-1/2)) after normalising the
 // largest eigenvalue below 1.  Every eigenvalue of M follows the scalar map
 // m <- m ((5 - m)/4)^4, which is increasing on [0, 1] with fixed point 1, so
-// the smallest one, eps/c, fixes the iteration count K.
+// the bounds of the spectrum, [eps/c, 1/1.01], fix the schedule.
 //
-// Per iteration: stage 0 computes T2 = T^2 = (25 I - 10 M + M^2)/16 and
-// X' = (5 X - X M)/4 in one launch, stage 1 T4 = T2 T2, stage 2 M' = T4 M.
+// Per iteration: stage 0 computes T2 = T^2 = (25 I - 10 M/s + (M/s)^2)/16 and
+// X' = s^(-1/4) (5 X - X M/s)/4 in one launch, stage 1 T4 = T2 T2, stage 2
+// M' = T4 M / s.
 // All matrices are polynomials in M0: symmetric and mutually commuting, so
 // every product is an upper-tile symmetric GEMM.  The last iteration only
 // updates X.  Iterations run in float64 until the scalar map says the
@@ -154,8 +158,9 @@ __global__ __launch_bounds__(256) void root_stats_kernel(const RootBatch B) {
 // iteration).  |A|_F is taken over A itself, which bounds that of (A + A^T)/2.
 // For a positive semidefinite A/s of unit trace WS <= 1 + eps.
 __global__ __launch_bounds__(64) void root_bound_kernel(RootState* state, const double* partial,
-                                                        int64_t stride, int32_t slot_begin, int32_t normalize,
-                                                        double eps, int32_t k_cap, int32_t all_f64) {
+                                                        int64_t stride, double* sched, int32_t slot_begin,
+                                                        int32_t normalize, double eps, int32_t k_cap,
+                                                        int32_t all_f64) {
   __shared__ double red[64];
   const int slot = slot_begin + blockIdx.x;
   RootState& st = state[slot];
@@ -195,7 +200,8 @@ __global__ __launch_bounds__(64) void root_bound_kernel(RootState* state, const 
         flags |= MR_INFO_NOT_PD;
         c = 1.0;
       } else {
-        newton_schedule(eps / c, kNewtonTol, kSwitchM, k_cap, &K, &j);
+        newton_scaled_schedule(fmin(eps / c, 1.0 / kBoundSafety), 1.0 / kBoundSafety, kNewtonTol, kSwitchM,
+                               k_cap, sched + (int64_t)slot * kMaxNewtonIters, &K, &j);
         if (all_f64) j = K;
       }
     }
@@ -261,6 +267,7 @@ struct StageJob {
   int ti, tj;
   int d;
   char* region;
+  double s;  // step scale
 };
 
 __device__ __forceinline__ StageJob stage_job(const NewtonLaunch& L, bool f64) {
@@ -274,12 +281,14 @@ __device__ __forceinline__ StageJob stage_job(const NewtonLaunch& L, bool f64) {
   upper_tile(rem % C.U, C.T, s.ti, s.tj);
   s.d = C.d;
   s.region = C.region + (int64_t)mat * C.matrix_bytes;
-  const RootState& st = L.state[C.slot_begin + mat];
+  const int slot = C.slot_begin + mat;
+  const RootState& st = L.state[slot];
   const int t = L.t, K = st.K, j = st.j;
   bool act = f64 ? (t < K && t < j) : (t >= j && t < K);
   // The last iteration only updates X (stage 0, job 1).
   if (t == K - 1 && !(L.stage == 0 && s.job == 1)) act = false;
   s.active = act;
+  s.s = act ? L.sched[(int64_t)slot * kMaxNewtonIters + t] : 1.0;
   return s;
 }
 
@@ -291,22 +300,25 @@ struct StageOps {
 };
 
 template <typename T, typename R>
-__device__ __forceinline__ StageOps<T> stage_ops(const R& r, int stage, int job) {
+__device__ __forceinline__ StageOps<T> stage_ops(const R& r, int stage, int job, double s) {
   StageOps<T> o;
   o.Cin = nullptr;
   o.beta = 0.0;
   o.gamma = 0.0;
   o.alpha = 1.0;
-  if (stage == 0 && job == 0) {  // T2 = (M M - 10 M + 25 I) / 16
+  const double is = 1.0 / s;
+  if (stage == 0 && job == 0) {  // T2 = ((M/s)^2 - 10 M/s + 25 I) / 16
     o.A = r.M; o.B = r.M; o.C = r.T2; o.Cin = r.M;
-    o.alpha = 1.0 / 16.0; o.beta = -10.0 / 16.0; o.gamma = 25.0 / 16.0;
-  } else if (stage == 0) {  // X' = (5 X - X M) / 4
+    o.alpha = is * is / 16.0; o.beta = -10.0 * is / 16.0; o.gamma = 25.0 / 16.0;
+  } else if (stage == 0) {  // X' = s^(-1/4) (5 X - X M/s) / 4
+    const double q = pow(s, -0.25);
     o.A = r.X; o.B = r.M; o.C = r.Xn; o.Cin = r.X;
-    o.alpha = -0.25; o.beta = 1.25;
+    o.alpha = -0.25 * q * is; o.beta = 1.25 * q;
   } else if (stage == 1) {  // T4 = T2 T2
     o.A = r.T2; o.B = r.T2; o.C = r.T4;
-  } else {  // M' = T4 M, written over T2 (dead after stage 1)
+  } else {  // M' = T4 M / s, written over T2 (dead after stage 1)
     o.A = r.T4; o.B = r.M; o.C = r.T2;
+    o.alpha = is;
   }
   return o;
 }
@@ -330,7 +342,7 @@ __global__ __launch_bounds__(256) void newton_f64_kernel(const NewtonLaunch L) {
   const StageJob s = stage_job(L, true);
   if (!s.active) return;
   const Roles64 r = roles64(s.region, s.d, L.t);
-  const StageOps<double> o = stage_ops<double>(r, L.stage, s.job);
+  const StageOps<double> o = stage_ops<double>(r, L.stage, s.job, s.s);
   const int m0 = s.ti * F64Tile::BM, n0 = s.tj * F64Tile::BN;
   v4d acc[4][4];
   f64_tile<double, false, VEC, double, false, VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, sA, sB, acc);
@@ -345,7 +357,7 @@ __global__ __launch_bounds__(256, 2) void newton_f32_kernel(const NewtonLaunch L
   const StageJob s = stage_job(L, false);
   if (!s.active) return;
   const Roles32 r = roles32(s.region, s.d, L.t);
-  const StageOps<float> o = stage_ops<float>(r, L.stage, s.job);
+  const StageOps<float> o = stage_ops<float>(r, L.stage, s.job, s.s);
   const int m0 = s.ti * F32Tile::BM, n0 = s.tj * F32Tile::BN;
   v16f acc[2][2];
   f32_nt_tile<VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, sA, sB, acc);
@@ -457,12 +469,12 @@ hipError_t launch_root_stats(const RootBatch& b, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_root_bound(RootState* state, const double* partial, int64_t partial_stride, int32_t slot_begin,
-                             int32_t nslots, int32_t normalize, double eps, int32_t k_cap, int32_t all_f64,
-                             hipStream_t s) {
+hipError_t launch_root_bound(RootState* state, const double* partial, int64_t partial_stride, double* sched,
+                             int32_t slot_begin, int32_t nslots, int32_t normalize, double eps, int32_t k_cap,
+                             int32_t all_f64, hipStream_t s) {
   if (nslots <= 0) return hipSuccess;
-  hipLaunchKernelGGL(root_bound_kernel, dim3(nslots), dim3(64), 0, s, state, partial, partial_stride, slot_begin,
-                     normalize, eps, k_cap, all_f64);
+  hipLaunchKernelGGL(root_bound_kernel, dim3(nslots), dim3(64), 0, s, state, partial, partial_stride, sched,
+                     slot_begin, normalize, eps, k_cap, all_f64);
   return hipGetLastError();
 }
 

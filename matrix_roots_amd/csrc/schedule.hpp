@@ -1,16 +1,31 @@
-// Iteration schedule of the coupled Newton inverse p-th root (host and device).
+// Iteration schedules of the coupled Newton inverse p-th root (host and device).
 //
-// Every eigenvalue m of the iterate M follows m <- m * ((p + 1 - m) / p)^p.
-// On [0, 1] the map is increasing with fixed point 1 and zero derivative
-// there, so starting from the smallest normalised eigenvalue m0 (a lower bound
-// eps / c) the count of steps until 1 - m <= tol serves every eigenvalue.
-// For p = 2 this is the scalar recurrence behind the coupled Newton-Schulz
-// iteration of tilderesearch, "Online KL Shampoo", section 2.2.
+// Coupled iteration: T = ((p+1) I - M/s)/p, X <- s^(-1/p) X T, M <- T^p M / s.
+// For any scale s the invariant X^p M0 = M holds (all iterates are
+// polynomials in M0 and commute), so X -> M0^(-1/p) once M -> I.  Every
+// eigenvalue m of M follows the scalar map m <- g(m/s) with
+// g(x) = x ((p+1-x)/p)^p, which rises on [0, 1] to its fixed point g(1) = 1
+// and falls beyond 1.
+//
+// * s = 1 is the classical iteration: the smallest eigenvalue eps/c fixes the
+//   count of steps until 1 - m <= tol.  For p = 2 this is the scalar recurrence
+//   behind coupled Newton-Schulz (tilderesearch, "Online KL Shampoo",
+//   section 2.2, roughly 21 iterations from a floor of 1e-6).
+// * Per-step scales shorten the slow start.  The OKLS page (section 2.3) tunes
+//   per-step polynomial coefficients of the coupled iteration for a fixed
+//   step budget (CANS); it prints them for p = 2 only.  Here, for p = 4, the
+//   scale of each step is chosen from the interval [l, u] that holds the
+//   spectrum of M: s balances g(l/s) = g(u/s) (the best new floor for this
+//   polynomial family), with u/s capped at kScaleCap, and the interval becomes
+//   [min(g(l/s), g(u/s)), 1].  This needs bounds only, never the matrix.
 #pragma once
 
 #include <hip/hip_runtime.h>
 
 namespace mr {
+
+constexpr int kMaxNewtonIters = 100;
+constexpr double kScaleCap = 3.0;
 
 __host__ __device__ inline double newton_scalar_step(int p, double m) {
   const double t = ((double)(p + 1) - m) / (double)p;
@@ -19,18 +34,47 @@ __host__ __device__ inline double newton_scalar_step(int p, double m) {
   return m * tp;
 }
 
-// K: iterations until 1 - m_K <= tol (at most cap, at least 1).
-// j: first iteration index whose input eigenvalue floor m_j >= switch_m
-//    (iterations t < j run in float64); j <= K.
-__host__ __device__ inline void newton_schedule(double m0, double tol, double switch_m, int cap, int* K,
-                                                int* j) {
-  double m = m0;
+__host__ __device__ inline double g4(double x) {
+  const double t = (5.0 - x) * 0.25;
+  const double t2 = t * t;
+  return x * t2 * t2;
+}
+
+// Scaled schedule for p = 4 from the spectrum bound [l, u] of M0, 0 < l <= u.
+// Writes the step scales to s_out[0..K) (s_out may be null), returns K >= 1
+// (steps until 1 - l <= tol, at most cap) and j <= K, the first step whose
+// input floor l >= switch_m (steps t < j run in float64).
+__host__ __device__ inline void newton_scaled_schedule(double l, double u, double tol, double switch_m, int cap,
+                                                       double* s_out, int* K, int* j) {
   int k = 0;
-  int jj = (m >= switch_m) ? 0 : -1;
-  while (1.0 - m > tol && k < cap) {
-    m = newton_scalar_step(4, m);
+  int jj = -1;
+  while (true) {
+    if (jj < 0 && l >= switch_m) jj = k;
+    if ((k > 0 && 1.0 - l <= tol) || k >= cap) break;
+    // y = u/s in [1, min(cap, u/l)] with g(y) = g(y l/u), by bisection
+    const double r = l / u;
+    double hi = fmin(kScaleCap, 1.0 / r);
+    double y;
+    if (hi <= 1.0 || g4(hi) >= g4(hi * r)) {
+      y = fmax(hi, 1.0);
+    } else {
+      double lo = 1.0;
+      for (int it = 0; it < 80; ++it) {
+        const double mid = 0.5 * (lo + hi);
+        if (g4(mid) - g4(mid * r) > 0.0)
+          lo = mid;
+        else
+          hi = mid;
+      }
+      y = lo;
+    }
+    const double s = u / y;
+    if (s_out) s_out[k] = s;
+    const double a = g4(l / s), b = g4(u / s);
+    const bool peak_inside = l / s <= 1.0 && u / s >= 1.0;
+    l = fmin(a, b);
+    u = peak_inside ? 1.0 : fmax(a, b);
     ++k;
-    if (jj < 0 && m >= switch_m) jj = k;
   }
   if (k == 0) k = 1;
   *K = k;

@@ -8,6 +8,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 from matrix_roots_amd import binding as B
@@ -146,3 +147,40 @@ def test_apply_validation(lib):
     need = lib.precondition_apply_workspace(ctypes.addressof(arr), 1)
     assert need == 256
     assert call([apply_p(4, 8)], ws=None, ws_bytes=0) == 5
+
+
+def test_newton_schedule_converges_every_eigenvalue(lib):
+    """For the library's step scales, every eigenvalue m0 <= m <= 1/1.01 of
+    M0 ends with x_K^4 m = m_K within 1e-6 of 1, i.e. x_K = m^(-1/4) to 2.5e-7:
+    each step maps m -> g(m/s), x -> x s^(-1/4) (5 - m/s)/4, g(y) = y((5-y)/4)^4.
+    Written here from the iteration's definition, independent of the library."""
+    import numpy as np
+
+    for m0 in (0.9, 0.5, 1e-2, 1e-4, 1e-6, 3e-7, 1e-8, 1e-10, 1e-14):
+        scales, j = B.newton_schedule(m0)
+        K = len(scales)
+        assert 1 <= K <= 40 and 0 <= j <= K
+        m = np.concatenate([np.geomspace(m0, 1 / 1.01, 4000), [m0, 1 / 1.01]])
+        m_init = m.copy()
+        x = np.ones_like(m)
+        for t, s in enumerate(scales):
+            y = m / s
+            x = x * s ** -0.25 * (5.0 - y) / 4.0
+            m = y * ((5.0 - y) / 4.0) ** 4
+            if t + 1 == j:
+                assert m.min() >= 1e-2 * (1 - 1e-12)  # float32 steps start at a floor >= 1e-2
+        assert np.max(np.abs(1.0 - m)) <= 1.01e-6, (m0, np.max(np.abs(1 - m)))
+        assert np.max(np.abs(x * m_init ** 0.25 - 1.0)) <= 1e-6
+
+
+def test_newton_schedule_monotone_in_floor(lib):
+    """A larger eigenvalue floor never needs more steps: the host caps the
+    launch count with the schedule of the smallest floor it can see."""
+    prev = None
+    for m0 in np.geomspace(1e-14, 0.99, 400):
+        K = len(B.newton_schedule(float(m0))[0])
+        if prev is not None:
+            assert K <= prev, m0
+        prev = K
+    # the scaled schedule beats the classical count (same tolerance)
+    assert len(B.newton_schedule(1e-6)[0]) < lib.mr_newton_iterations(4, 1e-6, 1e-6)
