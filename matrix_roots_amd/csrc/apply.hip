@@ -17,8 +17,7 @@ namespace mr {
 
 template <int VEC>
 __global__ __launch_bounds__(256, 2) void f32_nt_kernel(const F32Batch batch) {
-  __shared__ float sA[F32Tile::BM * F32Tile::LDW];
-  __shared__ float sB[F32Tile::BN * F32Tile::LDW];
+  __shared__ float smem[F32Tile::LDS_FLOATS];
 
   const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
   int jx = 0;
@@ -29,7 +28,7 @@ __global__ __launch_bounds__(256, 2) void f32_nt_kernel(const F32Batch batch) {
   const int n0 = (tile % J.tiles_n) * F32Tile::BN;
 
   v16f acc[2][2];
-  f32_nt_tile<VEC>(J.A, J.lda, J.B, J.ldb, J.M, J.N, J.K, m0, n0, sA, sB, acc);
+  f32_nt_tile<VEC>(J.A, J.lda, J.B, J.ldb, J.M, J.N, J.K, m0, n0, smem, acc);
 
   const float alpha = J.alpha;
   float* C = J.C;

@@ -22,10 +22,19 @@
 namespace mr {
 
 // ------------------------------------------------------------------ float32
+#ifndef MR_F32_BK
+#define MR_F32_BK 32
+#endif
+#ifndef MR_F32_DBUF
+#define MR_F32_DBUF 1
+#endif
+
 struct F32Tile {
-  static constexpr int BM = 128, BN = 128, BK = 32, PAD = 4, LDW = BK + PAD;
+  static constexpr int BM = 128, BN = 128, BK = MR_F32_BK, PAD = 4, LDW = BK + PAD;
   static constexpr int THREADS = 256;
-  static constexpr int LDS_FLOATS = (BM + BN) * LDW;  // 36 KiB
+  static constexpr bool DBUF = MR_F32_DBUF != 0;
+  static constexpr int STAGE = (BM + BN) * LDW;         // floats per LDS stage (A then B)
+  static constexpr int LDS_FLOATS = STAGE * (DBUF ? 2 : 1);
 };
 
 // Load a BM x BK chunk (rows r0.., k0..) of a K-contiguous float32 operand
@@ -33,7 +42,9 @@ struct F32Tile {
 // base; VEC=1 has element guards.
 template <int VEC>
 struct F32Loader {
-  static constexpr int PER = (F32Tile::BM * F32Tile::BK) / (F32Tile::THREADS * VEC);
+  static constexpr int BK = F32Tile::BK;
+  static constexpr int PER = (F32Tile::BM * BK) / (F32Tile::THREADS * VEC);
+  static constexpr int VPR = BK / 4;  // float4 per row
   v4f reg[VEC == 4 ? PER : 1];
   float sreg[VEC == 1 ? PER : 1];
 
@@ -43,8 +54,8 @@ struct F32Loader {
 #pragma unroll
       for (int p = 0; p < PER; ++p) {
         const int idx = tid + p * F32Tile::THREADS;
-        const int row = idx >> 3;  // BK/4 = 8 float4 per row
-        const int kq = (idx & 7) * 4;
+        const int row = idx / VPR;
+        const int kq = (idx % VPR) * 4;
         const int gr = r0 + row, gk = k0 + kq;
         v4f v = {0.f, 0.f, 0.f, 0.f};
         if (gr < rows && gk < K) v = *reinterpret_cast<const v4f*>(P + (int64_t)gr * ld + gk);
@@ -54,8 +65,8 @@ struct F32Loader {
 #pragma unroll
       for (int p = 0; p < PER; ++p) {
         const int idx = tid + p * F32Tile::THREADS;
-        const int row = idx >> 5;
-        const int kk = idx & 31;
+        const int row = idx / BK;
+        const int kk = idx % BK;
         const int gr = r0 + row, gk = k0 + kk;
         sreg[p] = (gr < rows && gk < K) ? P[(int64_t)gr * ld + gk] : 0.f;
       }
@@ -66,31 +77,61 @@ struct F32Loader {
 #pragma unroll
       for (int p = 0; p < PER; ++p) {
         const int idx = tid + p * F32Tile::THREADS;
-        const int row = idx >> 3;
-        const int kq = (idx & 7) * 4;
-        *reinterpret_cast<v4f*>(s + row * F32Tile::LDW + kq) = reg[p];
+        *reinterpret_cast<v4f*>(s + (idx / VPR) * F32Tile::LDW + (idx % VPR) * 4) = reg[p];
       }
     } else {
 #pragma unroll
       for (int p = 0; p < PER; ++p) {
         const int idx = tid + p * F32Tile::THREADS;
-        s[(idx >> 5) * F32Tile::LDW + (idx & 31)] = sreg[p];
+        s[(idx / BK) * F32Tile::LDW + (idx % BK)] = sreg[p];
       }
     }
   }
 };
 
+__device__ __forceinline__ void f32_chunk(const float* __restrict__ sA, const float* __restrict__ sB,
+                                          v16f (&acc)[2][2], int lane, int wm, int wn) {
+  const int koff = (lane >> 5) * 8;
+#pragma unroll
+  for (int g = 0; g < F32Tile::BK / 16; ++g) {
+    v4f a[2][2], b[2][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float* pa = sA + (wm * 64 + rb * 32 + (lane & 31)) * F32Tile::LDW + g * 16 + koff;
+      a[rb][0] = *reinterpret_cast<const v4f*>(pa);
+      a[rb][1] = *reinterpret_cast<const v4f*>(pa + 4);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const float* pb = sB + (wn * 64 + cb * 32 + (lane & 31)) * F32Tile::LDW + g * 16 + koff;
+      b[cb][0] = *reinterpret_cast<const v4f*>(pb);
+      b[cb][1] = *reinterpret_cast<const v4f*>(pb + 4);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+          acc[rb][cb] = mfma_f32_32x32x2(a[rb][i >> 2][i & 3], b[cb][i >> 2][i & 3], acc[rb][cb]);
+  }
+}
+
 // acc[rb][cb] holds the 32 x 32 MFMA block (rb, cb) of this wave's 64 x 64
-// sub-tile.  sA, sB: LDS, F32Tile::LDS_FLOATS floats in total.
+// sub-tile.  lds: F32Tile::LDS_FLOATS floats.  With DBUF the next k-chunk is
+// written to the other LDS stage while the current one is consumed, so each
+// chunk costs one barrier.
 template <int VEC>
 __device__ __forceinline__ void f32_nt_tile(const float* __restrict__ A, int64_t lda,
                                             const float* __restrict__ B, int64_t ldb, int M, int N,
-                                            int K, int m0, int n0, float* __restrict__ sA,
-                                            float* __restrict__ sB, v16f (&acc)[2][2]) {
+                                            int K, int m0, int n0, float* __restrict__ lds,
+                                            v16f (&acc)[2][2]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  constexpr int BK = F32Tile::BK;
+  constexpr int AOFF = 0, BOFF = F32Tile::BM * F32Tile::LDW;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -101,39 +142,39 @@ __device__ __forceinline__ void f32_nt_tile(const float* __restrict__ A, int64_t
   F32Loader<VEC> la, lb;
   la.load(A, lda, M, K, m0, 0, tid);
   lb.load(B, ldb, N, K, n0, 0, tid);
-  const int koff = (lane >> 5) * 8;
-  for (int k0 = 0; k0 < K; k0 += F32Tile::BK) {
-    la.store(sA, tid);
-    lb.store(sB, tid);
+  if constexpr (F32Tile::DBUF) {
+    la.store(lds + AOFF, tid);
+    lb.store(lds + BOFF, tid);
     __syncthreads();
-    if (k0 + F32Tile::BK < K) {
-      la.load(A, lda, M, K, m0, k0 + F32Tile::BK, tid);
-      lb.load(B, ldb, N, K, n0, k0 + F32Tile::BK, tid);
-    }
-#pragma unroll
-    for (int g = 0; g < F32Tile::BK / 16; ++g) {
-      v4f a[2][2], b[2][2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const float* pa = sA + (wm * 64 + rb * 32 + (lane & 31)) * F32Tile::LDW + g * 16 + koff;
-        a[rb][0] = *reinterpret_cast<const v4f*>(pa);
-        a[rb][1] = *reinterpret_cast<const v4f*>(pa + 4);
+    int stage = 0;
+    for (int k0 = 0; k0 < K; k0 += BK) {
+      const bool more = k0 + BK < K;
+      if (more) {
+        la.load(A, lda, M, K, m0, k0 + BK, tid);
+        lb.load(B, ldb, N, K, n0, k0 + BK, tid);
       }
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const float* pb = sB + (wn * 64 + cb * 32 + (lane & 31)) * F32Tile::LDW + g * 16 + koff;
-        b[cb][0] = *reinterpret_cast<const v4f*>(pb);
-        b[cb][1] = *reinterpret_cast<const v4f*>(pb + 4);
+      const float* cur = lds + stage * F32Tile::STAGE;
+      f32_chunk(cur + AOFF, cur + BOFF, acc, lane, wm, wn);
+      if (more) {
+        float* nxt = lds + (stage ^ 1) * F32Tile::STAGE;
+        la.store(nxt + AOFF, tid);
+        lb.store(nxt + BOFF, tid);
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb)
-            acc[rb][cb] = mfma_f32_32x32x2(a[rb][i >> 2][i & 3], b[cb][i >> 2][i & 3], acc[rb][cb]);
+      __syncthreads();
+      stage ^= 1;
     }
-    __syncthreads();
+  } else {
+    for (int k0 = 0; k0 < K; k0 += BK) {
+      la.store(lds + AOFF, tid);
+      lb.store(lds + BOFF, tid);
+      __syncthreads();
+      if (k0 + BK < K) {
+        la.load(A, lda, M, K, m0, k0 + BK, tid);
+        lb.load(B, ldb, N, K, n0, k0 + BK, tid);
+      }
+      f32_chunk(lds + AOFF, lds + BOFF, acc, lane, wm, wn);
+      __syncthreads();
+    }
   }
 }
 
@@ -154,10 +195,19 @@ __device__ __forceinline__ void f32_for_each(const v16f (&acc)[2][2], F&& f) {
 }
 
 // ------------------------------------------------------------------ float64
+#ifndef MR_F64_BK
+#define MR_F64_BK 16
+#endif
+#ifndef MR_F64_DBUF
+#define MR_F64_DBUF 1
+#endif
+
 struct F64Tile {
-  static constexpr int BM = 128, BN = 128, BK = 16, PAD = 2, LDW = BK + PAD;
+  static constexpr int BM = 128, BN = 128, BK = MR_F64_BK, PAD = 2, LDW = BK + PAD;
   static constexpr int THREADS = 256;
-  static constexpr int LDS_DOUBLES = (BM + BN) * LDW;  // 36 KiB
+  static constexpr bool DBUF = MR_F64_DBUF != 0;
+  static constexpr int STAGE = (BM + BN) * LDW;  // doubles per LDS stage (A then B)
+  static constexpr int LDS_DOUBLES = STAGE * (DBUF ? 2 : 1);
 };
 
 // Loader of a BM x BK chunk of operand element (i, k), i in [r0, r0+BM),
@@ -166,9 +216,10 @@ struct F64Tile {
 //   VEC: elements per global load (4 for float, 2 for double; 1 = guarded scalar).
 template <typename TIn, bool TRANS, int VEC>
 struct F64Loader {
-  static constexpr int ELEMS = F64Tile::BM * F64Tile::BK;  // 2048
+  static constexpr int BK = F64Tile::BK;
+  static constexpr int ELEMS = F64Tile::BM * BK;
   static constexpr int PER = ELEMS / (F64Tile::THREADS * VEC);
-  static constexpr int VPR_K = F64Tile::BK / VEC;   // vectors per row when !TRANS
+  static constexpr int VPR_K = BK / VEC;            // vectors per row when !TRANS
   static constexpr int VPR_I = F64Tile::BM / VEC;   // vectors per k-row when TRANS
   double reg[PER * VEC];
 
@@ -189,31 +240,20 @@ struct F64Loader {
       if constexpr (VEC == 1) {
         reg[p] = (gi < rows && gk < K) ? (double)P[TRANS ? (int64_t)gk * ld + gi : (int64_t)gi * ld + gk]
                                        : 0.0;
-      } else if constexpr (!TRANS) {
-        // VEC consecutive k of row gi; K % VEC == 0 so the vector is all-in or all-out.
-        const bool ok = gi < rows && gk < K;
-        if constexpr (sizeof(TIn) == 4) {
-          v4f v = {0.f, 0.f, 0.f, 0.f};
-          if (ok) v = *reinterpret_cast<const v4f*>(P + (int64_t)gi * ld + gk);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) reg[p * 4 + e] = (double)v[e];
-        } else {
-          v2d v = {0.0, 0.0};
-          if (ok) v = *reinterpret_cast<const v2d*>(P + (int64_t)gi * ld + gk);
-          reg[p * 2 + 0] = v[0];
-          reg[p * 2 + 1] = v[1];
-        }
       } else {
-        // VEC consecutive i of k-row gk; rows % VEC == 0.
+        // VEC consecutive elements along the contiguous index; the host only
+        // picks VEC > 1 when that index's extent is a multiple of VEC, so the
+        // vector is all-in or all-out.
         const bool ok = gi < rows && gk < K;
+        const int64_t off = TRANS ? (int64_t)gk * ld + gi : (int64_t)gi * ld + gk;
         if constexpr (sizeof(TIn) == 4) {
           v4f v = {0.f, 0.f, 0.f, 0.f};
-          if (ok) v = *reinterpret_cast<const v4f*>(P + (int64_t)gk * ld + gi);
+          if (ok) v = *reinterpret_cast<const v4f*>(P + off);
 #pragma unroll
           for (int e = 0; e < 4; ++e) reg[p * 4 + e] = (double)v[e];
         } else {
           v2d v = {0.0, 0.0};
-          if (ok) v = *reinterpret_cast<const v2d*>(P + (int64_t)gk * ld + gi);
+          if (ok) v = *reinterpret_cast<const v2d*>(P + off);
           reg[p * 2 + 0] = v[0];
           reg[p * 2 + 1] = v[1];
         }
@@ -227,8 +267,8 @@ struct F64Loader {
       if constexpr (VEC == 1) {
         int i, k;
         if constexpr (!TRANS) {
-          i = idx / F64Tile::BK;
-          k = idx % F64Tile::BK;
+          i = idx / BK;
+          k = idx % BK;
         } else {
           k = idx / F64Tile::BM;
           i = idx % F64Tile::BM;
@@ -252,16 +292,46 @@ struct F64Loader {
   }
 };
 
+// Fragments are read two k-steps at a time (one 128-bit LDS read per operand
+// block) to keep register pressure low enough for two waves per SIMD.
+__device__ __forceinline__ void f64_chunk(const double* __restrict__ sA, const double* __restrict__ sB,
+                                          v4d (&acc)[4][4], int lane, int wm, int wn) {
+  const int koff = (lane >> 4) * 4;
+  const double* pa0 = sA + (wm * 64 + (lane & 15)) * F64Tile::LDW + koff;
+  const double* pb0 = sB + (wn * 64 + (lane & 15)) * F64Tile::LDW + koff;
+#pragma unroll
+  for (int g = 0; g < F64Tile::BK / 16; ++g) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      v2d a[4], b[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        a[rb] = *reinterpret_cast<const v2d*>(pa0 + rb * 16 * F64Tile::LDW + g * 16 + 2 * h);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+        b[cb] = *reinterpret_cast<const v2d*>(pb0 + cb * 16 * F64Tile::LDW + g * 16 + 2 * h);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma_f64_16x16x4(a[rb][i], b[cb][i], acc[rb][cb]);
+    }
+  }
+}
+
 // acc[rb][cb]: 16 x 16 MFMA block (rb, cb) of this wave's 64 x 64 sub-tile.
+// lds: F64Tile::LDS_DOUBLES doubles.
 template <typename TA, bool TRANSA, int VECA, typename TB, bool TRANSB, int VECB>
 __device__ __forceinline__ void f64_tile(const TA* __restrict__ A, int64_t lda, const TB* __restrict__ B,
                                          int64_t ldb, int M, int N, int K, int m0, int n0,
-                                         double* __restrict__ sA, double* __restrict__ sB,
-                                         v4d (&acc)[4][4]) {
+                                         double* __restrict__ lds, v4d (&acc)[4][4]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  constexpr int BK = F64Tile::BK;
+  constexpr int AOFF = 0, BOFF = F64Tile::BM * F64Tile::LDW;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
@@ -273,36 +343,39 @@ __device__ __forceinline__ void f64_tile(const TA* __restrict__ A, int64_t lda, 
   F64Loader<TB, TRANSB, VECB> lb;
   la.load(A, lda, M, K, m0, 0, tid);
   lb.load(B, ldb, N, K, n0, 0, tid);
-  const int koff = (lane >> 4) * 4;
-  for (int k0 = 0; k0 < K; k0 += F64Tile::BK) {
-    la.store(sA, tid);
-    lb.store(sB, tid);
+  if constexpr (F64Tile::DBUF) {
+    la.store(lds + AOFF, tid);
+    lb.store(lds + BOFF, tid);
     __syncthreads();
-    if (k0 + F64Tile::BK < K) {
-      la.load(A, lda, M, K, m0, k0 + F64Tile::BK, tid);
-      lb.load(B, ldb, N, K, n0, k0 + F64Tile::BK, tid);
+    int stage = 0;
+    for (int k0 = 0; k0 < K; k0 += BK) {
+      const bool more = k0 + BK < K;
+      if (more) {
+        la.load(A, lda, M, K, m0, k0 + BK, tid);
+        lb.load(B, ldb, N, K, n0, k0 + BK, tid);
+      }
+      const double* cur = lds + stage * F64Tile::STAGE;
+      f64_chunk(cur + AOFF, cur + BOFF, acc, lane, wm, wn);
+      if (more) {
+        double* nxt = lds + (stage ^ 1) * F64Tile::STAGE;
+        la.store(nxt + AOFF, tid);
+        lb.store(nxt + BOFF, tid);
+      }
+      __syncthreads();
+      stage ^= 1;
     }
-    v2d a[4][2], b[4][2];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const double* pa = sA + (wm * 64 + rb * 16 + (lane & 15)) * F64Tile::LDW + koff;
-      a[rb][0] = *reinterpret_cast<const v2d*>(pa);
-      a[rb][1] = *reinterpret_cast<const v2d*>(pa + 2);
+  } else {
+    for (int k0 = 0; k0 < K; k0 += BK) {
+      la.store(lds + AOFF, tid);
+      lb.store(lds + BOFF, tid);
+      __syncthreads();
+      if (k0 + BK < K) {
+        la.load(A, lda, M, K, m0, k0 + BK, tid);
+        lb.load(B, ldb, N, K, n0, k0 + BK, tid);
+      }
+      f64_chunk(lds + AOFF, lds + BOFF, acc, lane, wm, wn);
+      __syncthreads();
     }
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const double* pb = sB + (wn * 64 + cb * 16 + (lane & 15)) * F64Tile::LDW + koff;
-      b[cb][0] = *reinterpret_cast<const v2d*>(pb);
-      b[cb][1] = *reinterpret_cast<const v2d*>(pb + 2);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-          acc[rb][cb] = mfma_f64_16x16x4(a[rb][i >> 1][i & 1], b[cb][i >> 1][i & 1], acc[rb][cb]);
-    __syncthreads();
   }
 }
 

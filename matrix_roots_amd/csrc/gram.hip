@@ -16,9 +16,8 @@
 namespace mr {
 
 template <bool RIGHT, typename TS, int VEC>
-__global__ __launch_bounds__(256) void syrk_ema_kernel(const SyrkBatch batch) {
-  __shared__ double sA[F64Tile::BM * F64Tile::LDW];
-  __shared__ double sB[F64Tile::BN * F64Tile::LDW];
+__global__ __launch_bounds__(256, 2) void syrk_ema_kernel(const SyrkBatch batch) {
+  __shared__ double smem[F64Tile::LDS_DOUBLES];
 
   const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
   int jx = 0;
@@ -29,8 +28,7 @@ __global__ __launch_bounds__(256) void syrk_ema_kernel(const SyrkBatch batch) {
   const int m0 = ti * F64Tile::BM, n0 = tj * F64Tile::BN;
 
   v4d acc[4][4];
-  f64_tile<float, RIGHT, VEC, float, RIGHT, VEC>(J.G, J.ldg, J.G, J.ldg, J.d, J.d, J.K, m0, n0, sA, sB,
-                                                 acc);
+  f64_tile<float, RIGHT, VEC, float, RIGHT, VEC>(J.G, J.ldg, J.G, J.ldg, J.d, J.d, J.K, m0, n0, smem, acc);
 
   TS* S = reinterpret_cast<TS*>(J.S);
   const int64_t lds = J.lds;

@@ -38,6 +38,13 @@
 #include "launch.hpp"
 #include "schedule.hpp"
 
+#ifndef MR_F64_OCC
+#define MR_F64_OCC 2
+#endif
+#ifndef MR_F32_OCC
+#define MR_F32_OCC 2
+#endif
+
 namespace mr {
 
 // ------------------------------------------------------------ roles
@@ -336,31 +343,29 @@ __device__ __forceinline__ void sym_store(const StageOps<T>& o, int d, int gr, i
 }
 
 template <int VEC>
-__global__ __launch_bounds__(256) void newton_f64_kernel(const NewtonLaunch L) {
-  __shared__ double sA[F64Tile::BM * F64Tile::LDW];
-  __shared__ double sB[F64Tile::BN * F64Tile::LDW];
+__global__ __launch_bounds__(256, MR_F64_OCC) void newton_f64_kernel(const NewtonLaunch L) {
+  __shared__ double smem[F64Tile::LDS_DOUBLES];
   const StageJob s = stage_job(L, true);
   if (!s.active) return;
   const Roles64 r = roles64(s.region, s.d, L.t);
   const StageOps<double> o = stage_ops<double>(r, L.stage, s.job, s.s);
   const int m0 = s.ti * F64Tile::BM, n0 = s.tj * F64Tile::BN;
   v4d acc[4][4];
-  f64_tile<double, false, VEC, double, false, VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, sA, sB, acc);
+  f64_tile<double, false, VEC, double, false, VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, smem, acc);
   const int d = s.d;
   f64_for_each(acc, [&](int rr, int cc, double v) { sym_store(o, d, m0 + rr, n0 + cc, v); });
 }
 
 template <int VEC>
-__global__ __launch_bounds__(256, 2) void newton_f32_kernel(const NewtonLaunch L) {
-  __shared__ float sA[F32Tile::BM * F32Tile::LDW];
-  __shared__ float sB[F32Tile::BN * F32Tile::LDW];
+__global__ __launch_bounds__(256, MR_F32_OCC) void newton_f32_kernel(const NewtonLaunch L) {
+  __shared__ float smem[F32Tile::LDS_FLOATS];
   const StageJob s = stage_job(L, false);
   if (!s.active) return;
   const Roles32 r = roles32(s.region, s.d, L.t);
   const StageOps<float> o = stage_ops<float>(r, L.stage, s.job, s.s);
   const int m0 = s.ti * F32Tile::BM, n0 = s.tj * F32Tile::BN;
   v16f acc[2][2];
-  f32_nt_tile<VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, sA, sB, acc);
+  f32_nt_tile<VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, smem, acc);
   const int d = s.d;
   f32_for_each(acc, [&](int rr, int cc, float v) { sym_store(o, d, m0 + rr, n0 + cc, (double)v); });
 }
