@@ -19,7 +19,7 @@ constexpr int kMaxClasses = 8;
 constexpr int kJacobiMaxD = 128;
 constexpr int kStatsRows = 8;        // rows of A per statistics workgroup
 constexpr int kFinalRows = 8;        // rows of X per finalize workgroup
-constexpr double kSwitchM = 1e-2;    // float64 -> float32 once the eigenvalue floor reaches this
+constexpr double kSwitchM = 2e-3;    // float64 -> float32 once the eigenvalue floor reaches this
 constexpr double kNewtonTol = 1e-6;  // stop once 1 - m_K <= this (scalar recurrence)
 constexpr double kBoundSafety = 1.01;
 

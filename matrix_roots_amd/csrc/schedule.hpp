@@ -16,7 +16,8 @@
 //   step budget (CANS); it prints them for p = 2 only.  Here, for p = 4, the
 //   scale of each step is chosen from the interval [l, u] that holds the
 //   spectrum of M: s balances g(l/s) = g(u/s) (the best new floor for this
-//   polynomial family), with u/s capped at kScaleCap, and the interval becomes
+//   polynomial family), with u/s capped (kScaleCap64 while the steps run in
+//   float64, kScaleCap32 after the switch), and the interval becomes
 //   [min(g(l/s), g(u/s)), 1].  This needs bounds only, never the matrix.
 #pragma once
 
@@ -25,7 +26,9 @@
 namespace mr {
 
 constexpr int kMaxNewtonIters = 100;
-constexpr double kScaleCap = 3.0;
+constexpr double kScaleCap64 = 4.0;  // cap on u/s while steps run in float64
+constexpr double kScaleCap32 = 3.0;  // ... and in float32 (errors in the top
+                                     // eigenvalues grow ~|1 - 4x/(5-x)| per step)
 
 __host__ __device__ inline double newton_scalar_step(int p, double m) {
   const double t = ((double)(p + 1) - m) / (double)p;
@@ -53,7 +56,7 @@ __host__ __device__ inline void newton_scaled_schedule(double l, double u, doubl
     if ((k > 0 && 1.0 - l <= tol) || k >= cap) break;
     // y = u/s in [1, min(cap, u/l)] with g(y) = g(y l/u), by bisection
     const double r = l / u;
-    double hi = fmin(kScaleCap, 1.0 / r);
+    double hi = fmin(jj < 0 ? kScaleCap64 : kScaleCap32, 1.0 / r);
     double y;
     if (hi <= 1.0 || g4(hi) >= g4(hi * r)) {
       y = fmax(hi, 1.0);
