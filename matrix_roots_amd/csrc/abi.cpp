@@ -346,7 +346,7 @@ mr_status gram_ema_update(const mr_gram_problem* p, int32_t count, mr_dtype dt, 
         J.K = (int32_t)K;
         J.T = tiles(d, 128);
         J.block_begin = b.total_blocks;
-        b.total_blocks += J.T * (J.T + 1) / 2;
+        b.total_blocks += round8(J.T * (J.T + 1) / 2);
         ++b.njobs;
         if (b.njobs == kMaxJobs && (st = flush()) != MR_OK) return st;
       }
@@ -436,9 +436,11 @@ mr_status precondition_apply(const mr_apply_problem* p, int32_t count, float alp
         if ((vec == 4) != v4) continue;
         const int tm = tiles(J.M, 128), tn = tiles(J.N, 128);
         J.tiles_n = tn;
+        J.nblocks = tm * tn;
+        J.pad = 0;
         J.block_begin = b.total_blocks;
         b.job[b.njobs++] = J;
-        b.total_blocks += tm * tn;
+        b.total_blocks += round8(J.nblocks);
         if (b.njobs == kMaxJobs && (st = flush()) != MR_OK) return st;
       }
       if ((st = flush()) != MR_OK) return st;
@@ -654,7 +656,8 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
           C.blocks_per_matrix = (stage == 0 ? 2 : 1) * C.U;
         else
           C.blocks_per_matrix = (int32_t)((c.d * c.d + 2047) / 2048);
-        L.total_blocks += C.blocks_per_matrix * C.count;
+        C.nblocks = C.blocks_per_matrix * C.count;
+        L.total_blocks += round8(C.nblocks);
       }
       return L;
     };

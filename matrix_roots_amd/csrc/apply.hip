@@ -19,11 +19,12 @@ template <int VEC>
 __global__ __launch_bounds__(256, 2) void f32_nt_kernel(const F32Batch batch) {
   __shared__ float smem[F32Tile::LDS_FLOATS];
 
-  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t b = blockIdx.x;
   int jx = 0;
   while (jx + 1 < batch.njobs && b >= batch.job[jx + 1].block_begin) ++jx;
   const F32Job& J = batch.job[jx];
-  const int tile = (int)(b - J.block_begin);
+  const int tile = (int)xcd_remap(b - J.block_begin, round8(J.nblocks));
+  if (tile >= J.nblocks) return;
   const int m0 = (tile / J.tiles_n) * F32Tile::BM;
   const int n0 = (tile % J.tiles_n) * F32Tile::BN;
 

@@ -19,12 +19,15 @@ template <bool RIGHT, typename TS, int VEC>
 __global__ __launch_bounds__(256, 2) void syrk_ema_kernel(const SyrkBatch batch) {
   __shared__ double smem[F64Tile::LDS_DOUBLES];
 
-  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t b = blockIdx.x;
   int jx = 0;
   while (jx + 1 < batch.njobs && b >= batch.job[jx + 1].block_begin) ++jx;
   const SyrkJob& J = batch.job[jx];
+  const int ntiles = J.T * (J.T + 1) / 2;
+  const int local = (int)xcd_remap(b - J.block_begin, round8(ntiles));
+  if (local >= ntiles) return;
   int ti, tj;
-  upper_tile((int)(b - J.block_begin), J.T, ti, tj);
+  upper_tile(local, J.T, ti, tj);
   const int m0 = ti * F64Tile::BM, n0 = tj * F64Tile::BN;
 
   v4d acc[4][4];

@@ -23,6 +23,10 @@ constexpr double kSwitchM = 2e-3;    // float64 -> float32 once the eigenvalue f
 constexpr double kNewtonTol = 1e-6;  // stop once 1 - m_K <= this (scalar recurrence)
 constexpr double kBoundSafety = 1.01;
 
+// Workgroup ranges of jobs and size classes start on multiples of 8 (one per
+// XCD) and are padded to a multiple of 8.
+__host__ __device__ inline int32_t round8(int32_t n) { return (n + 7) & ~7; }
+
 // Per-matrix state of one inv_quarter_root_batched call (device, in the
 // workspace).  Slot order: Newton matrices grouped by size class, then the
 // Jacobi matrices.  64 bytes.
@@ -51,7 +55,7 @@ struct SyrkJob {
   int32_t d;            // Gram dimension (m left, n right)
   int32_t K;            // contraction length (n left, m right)
   int32_t T;            // tiles per side
-  int32_t block_begin;  // first workgroup of this job
+  int32_t block_begin;  // first workgroup of this job (multiple of 8; range round8(T(T+1)/2))
 };
 struct SyrkBatch {
   SyrkJob job[kMaxJobs];
@@ -69,8 +73,10 @@ struct F32Job {
   int64_t lda, ldb, ldc;
   int32_t M, N, K;
   int32_t tiles_n;
-  int32_t block_begin;
+  int32_t block_begin;  // multiple of 8
+  int32_t nblocks;      // tiles of this job (its range is round8(nblocks) long)
   float alpha;
+  int32_t pad;
 };
 struct F32Batch {
   F32Job job[kMaxJobs];
@@ -109,10 +115,10 @@ struct NewtonClass {
   char* region;          // buffers of the class's first matrix
   int64_t matrix_bytes;  // distance between consecutive matrices' buffers
   int32_t d, count, T, U;  // size, matrices, tiles per side, upper tiles
-  int32_t block_begin;     // first workgroup of this class in the launch
+  int32_t block_begin;     // first workgroup of this class in the launch (multiple of 8)
   int32_t slot_begin;      // RootState slot of the class's first matrix
   int32_t blocks_per_matrix;
-  int32_t pad;
+  int32_t nblocks;         // count * blocks_per_matrix (range is round8(nblocks) long)
 };
 struct NewtonLaunch {
   NewtonClass cls[kMaxClasses];

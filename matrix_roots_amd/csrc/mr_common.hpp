@@ -36,9 +36,12 @@ __device__ __forceinline__ v4d mfma_f64_16x16x4(double a, double b, v4d c) {
 __device__ __forceinline__ int f32_row(int lane, int v) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 __device__ __forceinline__ int f64_row(int lane, int v) { return 4 * v + (lane >> 4); }
 
-// Workgroup b of a 1-D grid of n lands on XCD b % 8.  Renumber so that each
-// XCD receives one contiguous range of logical blocks: neighbouring tiles of
-// one matrix (which share operand panels) then share that XCD's L2.
+// Workgroup b of a 1-D grid lands on XCD b % 8.  Within a range of n blocks
+// that starts on a multiple of 8, renumber so that each XCD receives one
+// contiguous run of logical blocks: neighbouring tiles of one matrix (which
+// share operand panels) then share that XCD's L2.  Launches remap each job or
+// size class separately (8-aligned, padded), so every XCD gets the same mix of
+// cheap and expensive tiles.
 __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t n) {
   const int64_t per = n / kNumXcd;
   const int64_t full = per * kNumXcd;

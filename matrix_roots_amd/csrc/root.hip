@@ -279,9 +279,13 @@ struct StageJob {
 
 __device__ __forceinline__ StageJob stage_job(const NewtonLaunch& L, bool f64) {
   StageJob s;
-  const int64_t b = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t b = blockIdx.x;
   const NewtonClass& C = L.cls[find_class(L, b)];
-  const int local = (int)(b - C.block_begin);
+  const int local = (int)xcd_remap(b - C.block_begin, round8(C.nblocks));
+  if (local >= C.nblocks) {
+    s.active = false;
+    return s;
+  }
   const int mat = local / C.blocks_per_matrix;
   const int rem = local % C.blocks_per_matrix;
   s.job = rem / C.U;
@@ -376,6 +380,7 @@ __global__ __launch_bounds__(256) void newton_convert_kernel(const NewtonLaunch 
   const int64_t b = blockIdx.x;
   const NewtonClass& C = L.cls[find_class(L, b)];
   const int local = (int)(b - C.block_begin);
+  if (local >= C.nblocks) return;
   const int mat = local / C.blocks_per_matrix;
   const int chunk = local % C.blocks_per_matrix;
   const RootState& st = L.state[C.slot_begin + mat];
