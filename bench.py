@@ -92,6 +92,27 @@ def cpu_baseline(workload: str):
             "sample": sample, "seconds": sum(float(x.split(": ")[1].split("s")[0]) for x in timed)}
 
 
+def recorded_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    if the kernel sources are unchanged since the counters were taken."""
+    from matrix_roots_amd import profile_summary
+
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if ":" in line and line.split(":", 1)[0].strip() in ("traffic_bytes_per_launch", "source_sha256"):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip().strip("`")
+    if rec.get("source_sha256") != profile_summary.sources_sha256():
+        return None
+    try:
+        return float(rec["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,6 +121,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="w1024", choices=["toy", "w1024", "w2048", "moe"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--state-dtype", default="f64", choices=["f64", "f32"])
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="run a plain device copy of this many MiB 3 times first (counter calibration)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path has no "
@@ -116,6 +139,14 @@ def main(argv=None) -> int:
         return 2
     B.library()
     dev = torch.device("cuda:0")
+    if args.calibration_copy_mib > 0:
+        src = torch.ones(args.calibration_copy_mib * 2 ** 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"calibration copies of {args.calibration_copy_mib} MiB done")
     wl = W.WORKLOADS[args.workload]
     shapes = [(m, n) for _, m, n in wl.shapes]
     nw = len(shapes)
@@ -191,7 +222,7 @@ def main(argv=None) -> int:
     dom = max(kernels.items(), key=lambda kv: kv[1]["ms_total"])
     dname, dk = dom
     roofline = {"bound": "mfma", "kernel": dname, "achieved": dk.get("tflops"), "peak": dk.get("peak"),
-                "unit": "TFLOP/s", "frac": dk.get("frac"), "traffic": None,
+                "unit": "TFLOP/s", "frac": dk.get("frac"), "traffic": recorded_traffic(dname, args.workload),
                 "achieved_per_launch": "algorithmic flops of the class over the timed steps / sum of its "
                                        "event-measured launch durations"}
 

@@ -1,0 +1,100 @@
+"""Summarise rocprofv3 output for one kernel of this library.
+
+    python -m matrix_roots_amd.profile_summary \
+        --fetch gpurun_out/pmc_fetch --write gpurun_out/pmc_write \
+        --kernel newton_f64_kernel --copy-mib 1024 [--out profiles/x.md]
+
+Reads the `*counter_collection.csv` files of two `rocprofv3 --pmc` runs
+(FETCH_SIZE, then WRITE_SIZE; both in KiB per dispatch) of the same program.
+The program must also run a plain device copy of `--copy-mib` MiB (bench.py
+--calibration-copy-mib does), whose dispatches calibrate each counter: the
+copy moves exactly copy-mib MiB each way, so
+    scale = copy bytes / counter reading of the copy
+and the kernel's HBM bytes per dispatch = its mean reading x scale.
+Also prints the sha256 of the kernel sources, which bench.py compares before
+it reports the traffic.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ("csrc/gemm_core.hpp", "csrc/mr_common.hpp", "csrc/launch.hpp", "csrc/schedule.hpp",
+                  "csrc/root.hip", "csrc/gram.hip", "csrc/apply.hip")
+
+
+def sources_sha256() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def read_counter(run_dir: str, counter: str):
+    """{kernel name: [value per dispatch]} for one counter."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    out = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def pick(values: dict, needle: str):
+    hits = {k: v for k, v in values.items() if needle in k}
+    if not hits:
+        raise KeyError(f"no kernel matching {needle!r}")
+    vals = [x for v in hits.values() for x in v]
+    return sorted(hits), vals
+
+
+def summarise(fetch_dir, write_dir, kernel, copy_mib):
+    copy_bytes = copy_mib * 2 ** 20
+    res = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = read_counter(d, name)
+        _, copy_vals = pick(vals, "copyBuffer" if any("copyBuffer" in k for k in vals) else "copy")
+        # the calibration copies are the largest copy dispatches
+        top = sorted(copy_vals)[-3:]
+        copy_kib = sum(top) / len(top)
+        scale = copy_bytes / (copy_kib * 1024.0)
+        names, kvals = pick(vals, kernel)
+        mean_kib = sum(kvals) / len(kvals)
+        res[name] = {"kernels": names, "dispatches": len(kvals), "mean_kib": mean_kib, "copy_kib": copy_kib,
+                     "scale": scale, "bytes_per_dispatch": mean_kib * 1024.0 * scale}
+    return res
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--kernel", required=True)
+    ap.add_argument("--copy-mib", type=float, required=True)
+    args = ap.parse_args(argv)
+    res = summarise(args.fetch, args.write, args.kernel, args.copy_mib)
+    f, w = res["FETCH_SIZE"], res["WRITE_SIZE"]
+    print(f"kernel: {', '.join(f['kernels'])}")
+    print(f"dispatches: {f['dispatches']}")
+    for name, r in res.items():
+        print(f"{name}: mean {r['mean_kib']:.1f} KiB/dispatch; calibration copy of {args.copy_mib:g} MiB "
+              f"read {r['copy_kib']:.1f} KiB -> scale {r['scale']:.4f}; {r['bytes_per_dispatch']:.4e} B/dispatch")
+    print(f"traffic_bytes_per_launch: {f['bytes_per_dispatch'] + w['bytes_per_dispatch']:.6e}")
+    print(f"source_sha256: {sources_sha256()}")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
