@@ -29,7 +29,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6}  # MI355X dense MFMA (vendor figures)
+PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6, "f16": 2500.0}  # MI355X dense MFMA (vendor figures)
+# kernel class -> arithmetic whose peak bounds it
+CLASS_PREC = {"newton_f64": "f64", "syrk_ema": "f64", "newton_f32": "f32", "apply_f32": "f32", "newton_x3": "f16"}
 METRIC = "preconditioned matrix updates/sec + TFLOP/s as % fp32 MFMA peak, d=1024–4096"
 
 
@@ -212,12 +214,15 @@ def main(argv=None) -> int:
 
     kernels = {}
     for name, (launches, ms) in sorted(trace.items()):
-        flops = {"newton_f64": f64, "newton_f32": f32, "syrk_ema": syrk, "apply_f32": apply_f}.get(name)
+        flops = {"newton_f64": f64, "newton_f32": f32, "newton_x3": f32, "syrk_ema": syrk,
+                 "apply_f32": apply_f}.get(name)
         ent = {"launches": launches, "ms_total": round(ms, 3), "ms_avg": round(ms / launches, 4)}
         if flops:
-            prec = "f64" if name in ("newton_f64", "syrk_ema") else "f32"
+            prec = CLASS_PREC[name]
             tf = flops / (ms / 1e3) / 1e12
             ent.update({"tflops": round(tf, 2), "peak": PEAK_TFLOPS[prec], "frac": round(tf / PEAK_TFLOPS[prec], 4)})
+            if name == "newton_x3":  # three fp16 MFMA products per float32-accurate product
+                ent["mfma_tflops"] = round(3 * tf, 2)
         kernels[name] = ent
     dom = max(kernels.items(), key=lambda kv: kv[1]["ms_total"])
     dname, dk = dom
@@ -245,7 +250,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f64+f32",
+        "dtype": "f64+f32(split-f16 products)",
         "data": "synthetic",
         "config": {"workload": args.workload, "weights": nw, "grams_per_step": 2 * nw,
                    "shapes": sorted({f"{m}x{n}" for m, n in shapes}), "beta": wl.beta, "eps": wl.eps,

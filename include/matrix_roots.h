@@ -69,6 +69,7 @@ typedef int32_t mr_dtype;
 #define MR_JACOBI 1 /* eigendecomposition in LDS (d <= 128 only)             */
 #define MR_NEWTON 2 /* GEMM-only coupled Newton inverse 4th root             */
 #define MR_NEWTON_F64 3 /* the same iteration with every step in float64       */
+#define MR_NEWTON_F32 4 /* float64 steps, then float32 matrix cores            */
 
 /* mr_root_info.flags */
 #define MR_INFO_NONFINITE 1     /* A held NaN or Inf; X is all NaN                          */
@@ -163,12 +164,17 @@ size_t gram_ema_update_workspace(const mr_gram_problem* problems, int32_t count,
  *        M0 = (A/s + eps I)/c, X0 = I, T = (5 I - M)/4, X <- X T, M <- T^4 M,
  *    X = c^(-1/4) X_K, with M scaled by 1/s_t before each step (per-step
  *    scales from the spectrum bounds, see mr_newton_schedule), run in float64
- *    while the smallest eigenvalue of M is below 1e-2, then in float32.  The GEMM-only
+ *    while the smallest eigenvalue of M is below 2e-3, then with float32
+ *    storage on the fp16 matrix cores with split operands (x = hi + 2^-11 lo,
+ *    three products per product, float32 accumulation: about 2^-22 relative
+ *    error per product).  The GEMM-only
  *    route of tilderesearch, "Online KL Shampoo", sections 2.1-2.2 (there
  *    for the -1/2 root), taken to the 4th root.  c = 1.01 times the
  *    Wolkowicz-Styan upper bound on lambda_max(A/s + eps I) (the OKLS page,
  *    appendix D, normalises by an O(d^2) upper bound in the same way); the
  *    iteration count follows from eps/c.  The last iteration updates X only.
+ *  - MR_NEWTON_F32: as MR_NEWTON with the float32 steps on the float32
+ *    matrix cores.
  *  - MR_NEWTON_F64: the Newton iteration with every step in float64 (twice
  *    the cost of the float32 phase; for inputs near the float32 limit).
  *  - MR_AUTO: Jacobi for d <= 128, Newton otherwise.

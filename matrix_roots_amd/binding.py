@@ -20,10 +20,11 @@ MR_OK = 0
 MR_F32, MR_F64 = 0, 1
 MR_LEFT, MR_RIGHT = 1, 2
 MR_NORM_NONE, MR_NORM_TRACE = 0, 1
-MR_AUTO, MR_JACOBI, MR_NEWTON, MR_NEWTON_F64 = 0, 1, 2, 3
+MR_AUTO, MR_JACOBI, MR_NEWTON, MR_NEWTON_F64, MR_NEWTON_F32 = 0, 1, 2, 3, 4
 MR_INFO_NONFINITE, MR_INFO_ZERO_TRACE, MR_INFO_NOT_PD, MR_INFO_NOT_CONVERGED = 1, 2, 4, 8
 
-_METHODS = {"auto": MR_AUTO, "jacobi": MR_JACOBI, "newton": MR_NEWTON, "newton_f64": MR_NEWTON_F64}
+_METHODS = {"auto": MR_AUTO, "jacobi": MR_JACOBI, "newton": MR_NEWTON, "newton_f64": MR_NEWTON_F64,
+            "newton_f32": MR_NEWTON_F32}
 _NORMS = {"none": MR_NORM_NONE, "trace": MR_NORM_TRACE}
 
 EXPORTED = (

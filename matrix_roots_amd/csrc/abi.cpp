@@ -76,11 +76,11 @@ int tiles(int64_t d, int t) { return (int)((d + t - 1) / t); }
 // ------------------------------------------------------------ tracing
 enum TraceClass {
   kTrSyrk, kTrApply, kTrJacobi, kTrStats, kTrBound, kTrInit, kTrNewton64, kTrNewton32, kTrConvert,
-  kTrFinalize, kTrInfo, kTrCount
+  kTrFinalize, kTrInfo, kTrNewtonX3, kTrCount
 };
 const char* const kTraceNames[kTrCount] = {"syrk_ema", "apply_f32", "jacobi", "root_stats", "root_bound",
                                            "root_init", "newton_f64", "newton_f32", "newton_convert",
-                                           "root_finalize", "root_info"};
+                                           "root_finalize", "root_info", "newton_x3"};
 struct TraceEntry {
   int cls;
   hipEvent_t a, b;
@@ -458,7 +458,8 @@ static mr_status validate_root(const mr_root_problem* p, int32_t count, mr_dtype
   if (!(eps > 0.0) || !std::isfinite(eps)) return fail(MR_ERR_PARAM, "eps %g must be positive and finite", eps);
   if (normalize != MR_NORM_NONE && normalize != MR_NORM_TRACE)
     return fail(MR_ERR_PARAM, "normalize %d is not MR_NORM_NONE or MR_NORM_TRACE", normalize);
-  if (method != MR_AUTO && method != MR_JACOBI && method != MR_NEWTON && method != MR_NEWTON_F64)
+  if (method != MR_AUTO && method != MR_JACOBI && method != MR_NEWTON && method != MR_NEWTON_F64 &&
+      method != MR_NEWTON_F32)
     return fail(MR_ERR_PARAM, "method %d unknown", method);
   const size_t es = dt == MR_F64 ? 8 : 4;
   for (int i = 0; i < count; ++i) {
@@ -501,6 +502,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
   double* sched = reinterpret_cast<double*>(base + P.sched_off);
   const int a_f64 = dt == MR_F64;
   const bool all_f64 = method == MR_NEWTON_F64;
+  const bool f32_mfma = method == MR_NEWTON_F32;
 
   // ---------------- Jacobi matrices: one launch per 16
   {
@@ -672,13 +674,14 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
         for (const auto& g : groups) {
           const NewtonLaunch L = make_launch(g, 0, stage, t);
           if (t < j_max) {
-            if ((st = traced(kTrNewton64, true, s, [&] { return launch_newton_stage(L, true, g.vec64, s); },
+            if ((st = traced(kTrNewton64, true, s, [&] { return launch_newton_stage(L, kStageF64, g.vec64, s); },
                              "newton f64 stage")) != MR_OK)
               return st;
           }
           if (!all_f64) {
-            if ((st = traced(kTrNewton32, true, s, [&] { return launch_newton_stage(L, false, g.vec32, s); },
-                             "newton f32 stage")) != MR_OK)
+            const int kind = f32_mfma ? kStageF32 : kStageX3;
+            if ((st = traced(f32_mfma ? kTrNewton32 : kTrNewtonX3, true, s,
+                             [&] { return launch_newton_stage(L, kind, g.vec32, s); }, "newton f32 stage")) != MR_OK)
               return st;
           }
         }

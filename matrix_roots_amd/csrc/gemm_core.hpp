@@ -178,6 +178,173 @@ __device__ __forceinline__ void f32_nt_tile(const float* __restrict__ A, int64_t
   }
 }
 
+// ------------------------------------------------------------- split fp16
+// C = A * B^T for float32 operands on the fp16 matrix cores: each operand
+// value x is split on its way into LDS into hi = fp16(x) and
+// lo = fp16((x - hi) * 2^11) (x - hi is exact in float32), and
+//   C = sum hi_a hi_b + 2^-11 * sum (hi_a lo_b + lo_a hi_b),
+// the two sums in separate float32 accumulators.  Products of 11-bit
+// significands are exact in float32; the dropped lo*lo term and the rounding
+// of lo leave about 2^-22 relative error per product (float32: 2^-24), and
+// the float32 accumulation is the same as on the float32 matrix cores.  The
+// caller passes a power-of-two pre-scale for A that keeps hi below the fp16
+// range (|x * ascale| < 2^15); B is used unscaled.
+struct X3Tile {
+  static constexpr int BM = 128, BN = 128, BK = 32, PAD = 8, LDW = BK + PAD;  // halves per LDS row
+  static constexpr int THREADS = 256;
+  static constexpr int ARR = BM * LDW;         // halves per array (A_hi, A_lo, B_hi, B_lo)
+  static constexpr int STAGE = 4 * ARR;
+  static constexpr int LDS_HALVES = 2 * STAGE;  // two stages: 80 KiB
+};
+
+template <int VEC>
+struct X3Loader {
+  static constexpr int BK = X3Tile::BK;
+  static constexpr int PER = (X3Tile::BM * BK) / (X3Tile::THREADS * VEC);
+  static constexpr int VPR = BK / 4;
+  v4f reg[VEC == 4 ? PER : 1];
+  float sreg[VEC == 1 ? PER : 1];
+
+  __device__ __forceinline__ void load(const float* __restrict__ P, int64_t ld, int rows, int K, int r0,
+                                       int k0, int tid) {
+    if constexpr (VEC == 4) {
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int idx = tid + p * X3Tile::THREADS;
+        const int gr = r0 + idx / VPR, gk = k0 + (idx % VPR) * 4;
+        v4f v = {0.f, 0.f, 0.f, 0.f};
+        if (gr < rows && gk < K) v = *reinterpret_cast<const v4f*>(P + (int64_t)gr * ld + gk);
+        reg[p] = v;
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int idx = tid + p * X3Tile::THREADS;
+        const int gr = r0 + idx / BK, gk = k0 + idx % BK;
+        sreg[p] = (gr < rows && gk < K) ? P[(int64_t)gr * ld + gk] : 0.f;
+      }
+    }
+  }
+  __device__ __forceinline__ static void split(float x, _Float16& h, _Float16& l) {
+    h = (_Float16)x;
+    l = (_Float16)((x - (float)h) * 2048.0f);
+  }
+  __device__ __forceinline__ void store(_Float16* __restrict__ hi, _Float16* __restrict__ lo, float scale,
+                                        int tid) const {
+    if constexpr (VEC == 4) {
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int idx = tid + p * X3Tile::THREADS;
+        const int off = (idx / VPR) * X3Tile::LDW + (idx % VPR) * 4;
+        v4h h, l;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          _Float16 a, b;
+          split(reg[p][e] * scale, a, b);
+          h[e] = a;
+          l[e] = b;
+        }
+        *reinterpret_cast<v4h*>(hi + off) = h;
+        *reinterpret_cast<v4h*>(lo + off) = l;
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int idx = tid + p * X3Tile::THREADS;
+        const int off = (idx / BK) * X3Tile::LDW + idx % BK;
+        _Float16 a, b;
+        split(sreg[p] * scale, a, b);
+        hi[off] = a;
+        lo[off] = b;
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ void x3_chunk(const _Float16* __restrict__ st, v16f (&acc)[2][2], v16f (&acc2)[2][2],
+                                         int lane, int wm, int wn) {
+  const _Float16* Ahi = st;
+  const _Float16* Alo = st + X3Tile::ARR;
+  const _Float16* Bhi = st + 2 * X3Tile::ARR;
+  const _Float16* Blo = st + 3 * X3Tile::ARR;
+  const int koff = (lane >> 5) * 8;
+#pragma unroll
+  for (int ks = 0; ks < X3Tile::BK / 16; ++ks) {
+    v8h ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int o = (wm * 64 + rb * 32 + (lane & 31)) * X3Tile::LDW + ks * 16 + koff;
+      ah[rb] = *reinterpret_cast<const v8h*>(Ahi + o);
+      al[rb] = *reinterpret_cast<const v8h*>(Alo + o);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int o = (wn * 64 + cb * 32 + (lane & 31)) * X3Tile::LDW + ks * 16 + koff;
+      bh[cb] = *reinterpret_cast<const v8h*>(Bhi + o);
+      bl[cb] = *reinterpret_cast<const v8h*>(Blo + o);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        acc[rb][cb] = mfma_f16_32x32x16(ah[rb], bh[cb], acc[rb][cb]);
+        acc2[rb][cb] = mfma_f16_32x32x16(ah[rb], bl[cb], acc2[rb][cb]);
+        acc2[rb][cb] = mfma_f16_32x32x16(al[rb], bh[cb], acc2[rb][cb]);
+      }
+  }
+}
+
+// Result in acc (already combined: acc + 2^-11 acc2, divided by ascale).
+template <int VEC>
+__device__ __forceinline__ void x3_nt_tile(const float* __restrict__ A, int64_t lda, const float* __restrict__ B,
+                                           int64_t ldb, int M, int N, int K, int m0, int n0, float ascale,
+                                           _Float16* __restrict__ lds, v16f (&acc)[2][2]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  constexpr int BK = X3Tile::BK;
+  v16f acc2[2][2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        acc[rb][cb][v] = 0.f;
+        acc2[rb][cb][v] = 0.f;
+      }
+  X3Loader<VEC> la, lb;
+  la.load(A, lda, M, K, m0, 0, tid);
+  lb.load(B, ldb, N, K, n0, 0, tid);
+  la.store(lds, lds + X3Tile::ARR, ascale, tid);
+  lb.store(lds + 2 * X3Tile::ARR, lds + 3 * X3Tile::ARR, 1.0f, tid);
+  __syncthreads();
+  int stage = 0;
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    const bool more = k0 + BK < K;
+    if (more) {
+      la.load(A, lda, M, K, m0, k0 + BK, tid);
+      lb.load(B, ldb, N, K, n0, k0 + BK, tid);
+    }
+    x3_chunk(lds + stage * X3Tile::STAGE, acc, acc2, lane, wm, wn);
+    if (more) {
+      _Float16* nxt = lds + (stage ^ 1) * X3Tile::STAGE;
+      la.store(nxt, nxt + X3Tile::ARR, ascale, tid);
+      lb.store(nxt + 2 * X3Tile::ARR, nxt + 3 * X3Tile::ARR, 1.0f, tid);
+    }
+    __syncthreads();
+    stage ^= 1;
+  }
+  const float inv = 1.0f / ascale;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = (acc[rb][cb][v] + acc2[rb][cb][v] * (1.0f / 2048.0f)) * inv;
+}
+
 // Visit every accumulator element of the f32 core as (row, col) local to the
 // block tile.
 template <typename F>

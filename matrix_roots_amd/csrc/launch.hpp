@@ -162,7 +162,8 @@ hipError_t launch_root_bound(RootState* state, const double* partial, int64_t pa
                              int32_t slot_begin, int32_t nslots, int32_t normalize, double eps,
                              int32_t k_cap, int32_t all_f64, hipStream_t s);
 hipError_t launch_root_init(const RootBatch& b, hipStream_t s);
-hipError_t launch_newton_stage(const NewtonLaunch& L, bool f64, int vec, hipStream_t s);
+enum StageKind { kStageF64 = 0, kStageF32 = 1, kStageX3 = 2 };
+hipError_t launch_newton_stage(const NewtonLaunch& L, int kind, int vec, hipStream_t s);
 hipError_t launch_newton_convert(const NewtonLaunch& L, hipStream_t s);
 hipError_t launch_root_finalize(const RootBatch& b, hipStream_t s);
 hipError_t launch_root_info(RootState* state, const double* partial, int64_t partial_stride,

@@ -12,6 +12,8 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef double v4d __attribute__((ext_vector_type(4)));
 typedef double v2d __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kNumXcd = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
@@ -22,12 +24,18 @@ constexpr int kNumXcd = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
 // v_mfma_f32_32x32x2_f32, D(32x32) += A(32x2) B(2x32):
 //   lane l supplies A[l % 32][l / 32] and B[l / 32][l % 32];
 //   D value v (0..15) of lane l is D[8*(v/4) + 4*(l/32) + v%4][l % 32].
+// v_mfma_f32_32x32x16_f16, D(32x32) += A(32x16) B(16x32):
+//   lane l supplies A[l % 32][8*(l/32) + e] and B[8*(l/32) + e][l % 32],
+//   e = 0..7; D is laid out as for v_mfma_f32_32x32x2_f32.
 // v_mfma_f64_16x16x4_f64, D(16x16) += A(16x4) B(4x16):
 //   lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16];
 //   D value v (0..3) of lane l is D[4*v + l/16][l % 16].
 // --------------------------------------------------------------------------
 __device__ __forceinline__ v16f mfma_f32_32x32x2(float a, float b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v16f mfma_f16_32x32x16(v8h a, v8h b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ v4d mfma_f64_16x16x4(double a, double b, v4d c) {
   return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);

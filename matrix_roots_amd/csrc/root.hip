@@ -274,7 +274,8 @@ struct StageJob {
   int ti, tj;
   int d;
   char* region;
-  double s;  // step scale
+  double s;   // step scale
+  double m0;  // floor of the initial spectrum, eps / c
 };
 
 __device__ __forceinline__ StageJob stage_job(const NewtonLaunch& L, bool f64) {
@@ -300,6 +301,7 @@ __device__ __forceinline__ StageJob stage_job(const NewtonLaunch& L, bool f64) {
   if (t == K - 1 && !(L.stage == 0 && s.job == 1)) act = false;
   s.active = act;
   s.s = act ? L.sched[(int64_t)slot * kMaxNewtonIters + t] : 1.0;
+  s.m0 = st.eps / st.c;
   return s;
 }
 
@@ -370,6 +372,29 @@ __global__ __launch_bounds__(256, MR_F32_OCC) void newton_f32_kernel(const Newto
   const int m0 = s.ti * F32Tile::BM, n0 = s.tj * F32Tile::BN;
   v16f acc[2][2];
   f32_nt_tile<VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, smem, acc);
+  const int d = s.d;
+  f32_for_each(acc, [&](int rr, int cc, float v) { sym_store(o, d, m0 + rr, n0 + cc, (double)v); });
+}
+
+// Float32 phase on the fp16 matrix cores with split operands (see x3_nt_tile).
+// X can grow to (eps/c)^(-1/4); the A operand is pre-scaled by a power of two
+// that keeps it below 2^13.
+template <int VEC>
+__global__ __launch_bounds__(256, VEC == 4 ? 2 : 1) void newton_x3_kernel(const NewtonLaunch L) {
+  __shared__ _Float16 smem[X3Tile::LDS_HALVES];
+  const StageJob s = stage_job(L, false);
+  if (!s.active) return;
+  const Roles32 r = roles32(s.region, s.d, L.t);
+  const StageOps<float> o = stage_ops<float>(r, L.stage, s.job, s.s);
+  float ascale = 1.0f;
+  if (L.stage == 0 && s.job == 1) {
+    const double xmax = pow(s.m0, -0.25);  // |X| <= m0^(-1/4) throughout
+    const int e = (int)ceil(log2(xmax)) - 13;
+    if (e > 0) ascale = ldexpf(1.0f, -e);
+  }
+  const int m0 = s.ti * X3Tile::BM, n0 = s.tj * X3Tile::BN;
+  v16f acc[2][2];
+  x3_nt_tile<VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, ascale, smem, acc);
   const int d = s.d;
   f32_for_each(acc, [&](int rr, int cc, float v) { sym_store(o, d, m0 + rr, n0 + cc, (double)v); });
 }
@@ -497,9 +522,16 @@ hipError_t launch_root_init(const RootBatch& b, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_newton_stage(const NewtonLaunch& L, bool f64, int vec, hipStream_t s) {
+hipError_t launch_newton_stage(const NewtonLaunch& L, int kind, int vec, hipStream_t s) {
   if (L.total_blocks <= 0) return hipSuccess;
-  if (f64) {
+  if (kind == kStageX3) {
+    if (vec == 4)
+      hipLaunchKernelGGL(newton_x3_kernel<4>, dim3(L.total_blocks), dim3(256), 0, s, L);
+    else
+      hipLaunchKernelGGL(newton_x3_kernel<1>, dim3(L.total_blocks), dim3(256), 0, s, L);
+    return hipGetLastError();
+  }
+  if (kind == kStageF64) {
     if (vec > 1)
       hipLaunchKernelGGL(newton_f64_kernel<2>, dim3(L.total_blocks), dim3(256), 0, s, L);
     else

@@ -103,7 +103,7 @@ def test_jacobi_root_matches_oracle(torch_dev, a_dtype, normalize):
     assert (info["iters"] <= 30).all()
 
 
-@pytest.mark.parametrize("method", ["newton", "newton_f64"])
+@pytest.mark.parametrize("method", ["newton", "newton_f32", "newton_f64"])
 @pytest.mark.parametrize("a_dtype", ["f32", "f64"])
 def test_newton_root_matches_oracle(torch_dev, method, a_dtype):
     torch, dev = torch_dev
@@ -111,7 +111,7 @@ def test_newton_root_matches_oracle(torch_dev, method, a_dtype):
     sizes = [129, 200, 256, 301, 384]
     mats = [spd(d, rng) for d in sizes]
     dt = torch.float64 if a_dtype == "f64" else torch.float32
-    tol = ROOT_TOL if method == "newton" else 1e-6
+    tol = 1e-6 if method == "newton_f64" else ROOT_TOL
     for normalize in ("trace", "none"):
         _check_roots(torch, dev, mats, 1e-6, normalize, method, dt, tol)
 
@@ -207,7 +207,7 @@ def test_toy_end_to_end(torch_dev):
     print(f"toy worst root err {worst[0]:.3e} update err {worst[1]:.3e}")
 
 
-@pytest.mark.parametrize("method", ["auto", "newton"])
+@pytest.mark.parametrize("method", ["auto", "newton", "newton_f32"])
 def test_small_transformer_like_end_to_end(torch_dev, method):
     """Low-rank gradients on ragged shapes above the Jacobi size, 3 steps."""
     torch, dev = torch_dev
