@@ -44,17 +44,25 @@ def sym_gemm_flops(d: int) -> float:
     return float(d) * d * (d + 1)
 
 
-def newton_flops(d: int, K: int, j: int):
-    """Algorithmic (upper-triangle) flops of one Newton root: iterations t < K-1
-    take 4 symmetric products, the last one 1; t < j run in float64."""
-    f64 = f32 = 0.0
+def newton_flops(d: int, K: int, j: int, x_low: bool = True):
+    """Algorithmic (upper-triangle) flops of one Newton root, split by the
+    kernel class that runs them: iterations t < K-1 take 4 symmetric products
+    (M^2, T2^2, T4 M, X M), the last one only X M; t < j run M's products in
+    float64, and the X product too unless x_low (then it runs on the
+    split-fp16 kernel, like every product of the float32 steps)."""
+    f64 = low = 0.0
+    g = sym_gemm_flops(d)
     for t in range(K):
-        g = (4 if t < K - 1 else 1) * sym_gemm_flops(d)
+        m_products = 3 * g if t < K - 1 else 0.0
         if t < j:
-            f64 += g
+            f64 += m_products
+            if x_low:
+                low += g
+            else:
+                f64 += g
         else:
-            f32 += g
-    return f64, f32
+            low += m_products + g
+    return f64, low
 
 
 def cpu_baseline(workload: str):

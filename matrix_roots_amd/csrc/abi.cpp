@@ -503,6 +503,9 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
   const int a_f64 = dt == MR_F64;
   const bool all_f64 = method == MR_NEWTON_F64;
   const bool f32_mfma = method == MR_NEWTON_F32;
+  // Default Newton path: X in float32 storage with split-fp16 products from
+  // the first step; only M and its powers run in float64 while the floor is low.
+  const bool x_low = !all_f64 && !f32_mfma;
 
   // ---------------- Jacobi matrices: one launch per 16
   {
@@ -543,6 +546,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
       b.state = state;
       b.partial = partial;
       b.partial_stride = P.partial_stride;
+      b.x_low = x_low ? 1 : 0;
       for (const auto& c : P.classes) {
         for (int k = 0; k < c.count; ++k) {
           const int slot = c.first_slot + k;
@@ -636,13 +640,15 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
       }
       if (!g.cls.empty()) groups.push_back(g);
     }
-    auto make_launch = [&](const Group& g, int kind, int stage, int t) {
+    auto make_launch = [&](const Group& g, int kind, int stage, int t, int job_only) {
       NewtonLaunch L;
       memset(&L, 0, sizeof L);
       L.stage = stage;
       L.t = t;
       L.state = state;
       L.sched = sched;
+      L.x_low = x_low ? 1 : 0;
+      L.job_only = job_only;
       for (int ci : g.cls) {
         const auto& c = P.classes[ci];
         NewtonClass& C = L.cls[L.ncls++];
@@ -655,7 +661,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
         C.slot_begin = c.first_slot;
         C.block_begin = L.total_blocks;
         if (kind == 0)
-          C.blocks_per_matrix = (stage == 0 ? 2 : 1) * C.U;
+          C.blocks_per_matrix = (stage == 0 && job_only < 0 ? 2 : 1) * C.U;
         else
           C.blocks_per_matrix = (int32_t)((c.d * c.d + 2047) / 2048);
         C.nblocks = C.blocks_per_matrix * C.count;
@@ -666,19 +672,28 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
     for (int t = 0; t < k_max; ++t) {
       if (t <= j_max && !all_f64) {
         for (const auto& g : groups)
-          if ((st = traced(kTrConvert, true, s, [&] { return launch_newton_convert(make_launch(g, 1, 0, t), s); },
+          if ((st = traced(kTrConvert, true, s, [&] { return launch_newton_convert(make_launch(g, 1, 0, t, -1), s); },
                            "newton convert")) != MR_OK)
             return st;
       }
       for (int stage = 0; stage < 3; ++stage) {
         for (const auto& g : groups) {
-          const NewtonLaunch L = make_launch(g, 0, stage, t);
           if (t < j_max) {
-            if ((st = traced(kTrNewton64, true, s, [&] { return launch_newton_stage(L, kStageF64, g.vec64, s); },
+            // float64 steps; with x_low the X update goes to the split-fp16 kernel
+            const bool split = x_low && stage == 0;
+            const NewtonLaunch L64 = make_launch(g, 0, stage, t, split ? 0 : -1);
+            if ((st = traced(kTrNewton64, true, s, [&] { return launch_newton_stage(L64, kStageF64, g.vec64, s); },
                              "newton f64 stage")) != MR_OK)
               return st;
+            if (split) {
+              const NewtonLaunch LX = make_launch(g, 0, stage, t, 1);
+              if ((st = traced(kTrNewtonX3, true, s, [&] { return launch_newton_stage(LX, kStageX3B64, g.vec32, s); },
+                               "newton x3 X update")) != MR_OK)
+                return st;
+            }
           }
           if (!all_f64) {
+            const NewtonLaunch L = make_launch(g, 0, stage, t, -1);
             const int kind = f32_mfma ? kStageF32 : kStageX3;
             if ((st = traced(f32_mfma ? kTrNewton32 : kTrNewtonX3, true, s,
                              [&] { return launch_newton_stage(L, kind, g.vec32, s); }, "newton f32 stage")) != MR_OK)

@@ -197,32 +197,42 @@ struct X3Tile {
   static constexpr int LDS_HALVES = 2 * STAGE;  // two stages: 80 KiB
 };
 
-template <int VEC>
+// Loads a BM x BK chunk of a K-contiguous float32 or float64 operand as
+// groups of 4 consecutive k per thread (float64 is rounded to float32 first).
+// VEC: elements per global load (4 for float, 2 for double, 1 = guarded
+// scalar); VEC > 1 needs ld and K multiples of VEC and an aligned base.
+template <typename TIn, int VEC>
 struct X3Loader {
   static constexpr int BK = X3Tile::BK;
-  static constexpr int PER = (X3Tile::BM * BK) / (X3Tile::THREADS * VEC);
-  static constexpr int VPR = BK / 4;
-  v4f reg[VEC == 4 ? PER : 1];
-  float sreg[VEC == 1 ? PER : 1];
+  static constexpr int GROUPS = (X3Tile::BM * BK) / (X3Tile::THREADS * 4);
+  static constexpr int GPR = BK / 4;  // groups per row
+  v4f reg[GROUPS];
 
-  __device__ __forceinline__ void load(const float* __restrict__ P, int64_t ld, int rows, int K, int r0,
-                                       int k0, int tid) {
-    if constexpr (VEC == 4) {
+  __device__ __forceinline__ void load(const TIn* __restrict__ P, int64_t ld, int rows, int K, int r0, int k0,
+                                       int tid) {
 #pragma unroll
-      for (int p = 0; p < PER; ++p) {
-        const int idx = tid + p * X3Tile::THREADS;
-        const int gr = r0 + idx / VPR, gk = k0 + (idx % VPR) * 4;
-        v4f v = {0.f, 0.f, 0.f, 0.f};
-        if (gr < rows && gk < K) v = *reinterpret_cast<const v4f*>(P + (int64_t)gr * ld + gk);
-        reg[p] = v;
-      }
-    } else {
+    for (int p = 0; p < GROUPS; ++p) {
+      const int idx = tid + p * X3Tile::THREADS;
+      const int gr = r0 + idx / GPR, gk = k0 + (idx % GPR) * 4;
+      const bool row_ok = gr < rows;
+      const TIn* src = P + (int64_t)gr * ld + gk;
+      v4f v = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (VEC == 4) {
+        if (row_ok && gk < K) v = *reinterpret_cast<const v4f*>(src);
+      } else if constexpr (VEC == 2) {
 #pragma unroll
-      for (int p = 0; p < PER; ++p) {
-        const int idx = tid + p * X3Tile::THREADS;
-        const int gr = r0 + idx / BK, gk = k0 + idx % BK;
-        sreg[p] = (gr < rows && gk < K) ? P[(int64_t)gr * ld + gk] : 0.f;
+        for (int h = 0; h < 2; ++h)
+          if (row_ok && gk + 2 * h < K) {
+            const v2d w = *reinterpret_cast<const v2d*>(src + 2 * h);
+            v[2 * h] = (float)w[0];
+            v[2 * h + 1] = (float)w[1];
+          }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (row_ok && gk + e < K) v[e] = (float)src[e];
       }
+      reg[p] = v;
     }
   }
   __device__ __forceinline__ static void split(float x, _Float16& h, _Float16& l) {
@@ -231,32 +241,20 @@ struct X3Loader {
   }
   __device__ __forceinline__ void store(_Float16* __restrict__ hi, _Float16* __restrict__ lo, float scale,
                                         int tid) const {
-    if constexpr (VEC == 4) {
 #pragma unroll
-      for (int p = 0; p < PER; ++p) {
-        const int idx = tid + p * X3Tile::THREADS;
-        const int off = (idx / VPR) * X3Tile::LDW + (idx % VPR) * 4;
-        v4h h, l;
+    for (int p = 0; p < GROUPS; ++p) {
+      const int idx = tid + p * X3Tile::THREADS;
+      const int off = (idx / GPR) * X3Tile::LDW + (idx % GPR) * 4;
+      v4h h, l;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          _Float16 a, b;
-          split(reg[p][e] * scale, a, b);
-          h[e] = a;
-          l[e] = b;
-        }
-        *reinterpret_cast<v4h*>(hi + off) = h;
-        *reinterpret_cast<v4h*>(lo + off) = l;
-      }
-    } else {
-#pragma unroll
-      for (int p = 0; p < PER; ++p) {
-        const int idx = tid + p * X3Tile::THREADS;
-        const int off = (idx / BK) * X3Tile::LDW + idx % BK;
+      for (int e = 0; e < 4; ++e) {
         _Float16 a, b;
-        split(sreg[p] * scale, a, b);
-        hi[off] = a;
-        lo[off] = b;
+        split(reg[p][e] * scale, a, b);
+        h[e] = a;
+        l[e] = b;
       }
+      *reinterpret_cast<v4h*>(hi + off) = h;
+      *reinterpret_cast<v4h*>(lo + off) = l;
     }
   }
 };
@@ -295,8 +293,8 @@ __device__ __forceinline__ void x3_chunk(const _Float16* __restrict__ st, v16f (
 }
 
 // Result in acc (already combined: acc + 2^-11 acc2, divided by ascale).
-template <int VEC>
-__device__ __forceinline__ void x3_nt_tile(const float* __restrict__ A, int64_t lda, const float* __restrict__ B,
+template <int VECA, typename TB, int VECB>
+__device__ __forceinline__ void x3_nt_tile(const float* __restrict__ A, int64_t lda, const TB* __restrict__ B,
                                            int64_t ldb, int M, int N, int K, int m0, int n0, float ascale,
                                            _Float16* __restrict__ lds, v16f (&acc)[2][2]) {
   const int tid = threadIdx.x;
@@ -314,7 +312,8 @@ __device__ __forceinline__ void x3_nt_tile(const float* __restrict__ A, int64_t 
         acc[rb][cb][v] = 0.f;
         acc2[rb][cb][v] = 0.f;
       }
-  X3Loader<VEC> la, lb;
+  X3Loader<float, VECA> la;
+  X3Loader<TB, VECB> lb;
   la.load(A, lda, M, K, m0, 0, tid);
   lb.load(B, ldb, N, K, n0, 0, tid);
   la.store(lds, lds + X3Tile::ARR, ascale, tid);

@@ -108,6 +108,8 @@ struct RootBatch {
   RootState* state;
   double* partial;         // per-workgroup partial sums
   int64_t partial_stride;  // doubles per matrix slot in `partial`
+  int32_t x_low;           // X kept in float32 from the first step
+  int32_t pad;
 };
 
 // ------------------------------------------------ Newton: per size class
@@ -128,6 +130,8 @@ struct NewtonLaunch {
   int32_t t;      // iteration
   RootState* state;
   const double* sched;  // per slot: kMaxNewtonIters step scales
+  int32_t x_low;        // X kept in float32 from the first step
+  int32_t job_only;     // -1: every job of the stage; else only that job
 };
 
 // ------------------------------------------------------------ Jacobi
@@ -162,7 +166,7 @@ hipError_t launch_root_bound(RootState* state, const double* partial, int64_t pa
                              int32_t slot_begin, int32_t nslots, int32_t normalize, double eps,
                              int32_t k_cap, int32_t all_f64, hipStream_t s);
 hipError_t launch_root_init(const RootBatch& b, hipStream_t s);
-enum StageKind { kStageF64 = 0, kStageF32 = 1, kStageX3 = 2 };
+enum StageKind { kStageF64 = 0, kStageF32 = 1, kStageX3 = 2, kStageX3B64 = 3 };
 hipError_t launch_newton_stage(const NewtonLaunch& L, int kind, int vec, hipStream_t s);
 hipError_t launch_newton_convert(const NewtonLaunch& L, hipStream_t s);
 hipError_t launch_root_finalize(const RootBatch& b, hipStream_t s);

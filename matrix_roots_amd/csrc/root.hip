@@ -248,6 +248,7 @@ __global__ __launch_bounds__(256) void root_init_kernel(const RootBatch B) {
   const double inv_s = 1.0 / st.s, inv_c = 1.0 / st.c, eps = B.eps;
   double* M = reinterpret_cast<double*>(J.region);
   double* X = reinterpret_cast<double*>(J.region + (int64_t)d * d * 8);
+  float* X32 = roles32(J.region, d, 0).X;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int r = ty + 8 * e;
@@ -256,7 +257,10 @@ __global__ __launch_bounds__(256) void root_init_kernel(const RootBatch B) {
       const double sym = 0.5 * (ta[r][tx] + tb[tx][r]);
       const double v = (sym * inv_s + (gi == gj ? eps : 0.0)) * inv_c;
       M[(int64_t)gi * d + gj] = v;
-      X[(int64_t)gi * d + gj] = (gi == gj) ? 1.0 : 0.0;
+      if (B.x_low)
+        X32[(int64_t)gi * d + gj] = (gi == gj) ? 1.f : 0.f;
+      else
+        X[(int64_t)gi * d + gj] = (gi == gj) ? 1.0 : 0.0;
     }
   }
 }
@@ -278,7 +282,12 @@ struct StageJob {
   double m0;  // floor of the initial spectrum, eps / c
 };
 
-__device__ __forceinline__ StageJob stage_job(const NewtonLaunch& L, bool f64) {
+// Which kernel runs a (matrix, stage, job) at iteration t:
+//   kStageF64  : t < j (float64 steps); with x_low not the X update
+//   kStageX3B64: t < j, X update only (x_low: float32 X, float64 M)
+//   kStageF32 / kStageX3: t >= j (float32 steps)
+// and the last iteration (t = K-1) only updates X (stage 0, job 1).
+__device__ __forceinline__ StageJob stage_job(const NewtonLaunch& L, int kind) {
   StageJob s;
   const int64_t b = blockIdx.x;
   const NewtonClass& C = L.cls[find_class(L, b)];
@@ -289,16 +298,22 @@ __device__ __forceinline__ StageJob stage_job(const NewtonLaunch& L, bool f64) {
   }
   const int mat = local / C.blocks_per_matrix;
   const int rem = local % C.blocks_per_matrix;
-  s.job = rem / C.U;
+  s.job = L.job_only >= 0 ? L.job_only : rem / C.U;
   upper_tile(rem % C.U, C.T, s.ti, s.tj);
   s.d = C.d;
   s.region = C.region + (int64_t)mat * C.matrix_bytes;
   const int slot = C.slot_begin + mat;
   const RootState& st = L.state[slot];
   const int t = L.t, K = st.K, j = st.j;
-  bool act = f64 ? (t < K && t < j) : (t >= j && t < K);
-  // The last iteration only updates X (stage 0, job 1).
-  if (t == K - 1 && !(L.stage == 0 && s.job == 1)) act = false;
+  const bool xupdate = L.stage == 0 && s.job == 1;
+  bool act;
+  if (kind == kStageF64)
+    act = t < K && t < j && !(L.x_low && xupdate);
+  else if (kind == kStageX3B64)
+    act = t < K && t < j && L.x_low && xupdate;
+  else
+    act = t >= j && t < K;
+  if (t == K - 1 && !xupdate) act = false;
   s.active = act;
   s.s = act ? L.sched[(int64_t)slot * kMaxNewtonIters + t] : 1.0;
   s.m0 = st.eps / st.c;
@@ -351,7 +366,7 @@ __device__ __forceinline__ void sym_store(const StageOps<T>& o, int d, int gr, i
 template <int VEC>
 __global__ __launch_bounds__(256, MR_F64_OCC) void newton_f64_kernel(const NewtonLaunch L) {
   __shared__ double smem[F64Tile::LDS_DOUBLES];
-  const StageJob s = stage_job(L, true);
+  const StageJob s = stage_job(L, kStageF64);
   if (!s.active) return;
   const Roles64 r = roles64(s.region, s.d, L.t);
   const StageOps<double> o = stage_ops<double>(r, L.stage, s.job, s.s);
@@ -365,7 +380,7 @@ __global__ __launch_bounds__(256, MR_F64_OCC) void newton_f64_kernel(const Newto
 template <int VEC>
 __global__ __launch_bounds__(256, MR_F32_OCC) void newton_f32_kernel(const NewtonLaunch L) {
   __shared__ float smem[F32Tile::LDS_FLOATS];
-  const StageJob s = stage_job(L, false);
+  const StageJob s = stage_job(L, kStageF32);
   if (!s.active) return;
   const Roles32 r = roles32(s.region, s.d, L.t);
   const StageOps<float> o = stage_ops<float>(r, L.stage, s.job, s.s);
@@ -376,16 +391,22 @@ __global__ __launch_bounds__(256, MR_F32_OCC) void newton_f32_kernel(const Newto
   f32_for_each(acc, [&](int rr, int cc, float v) { sym_store(o, d, m0 + rr, n0 + cc, (double)v); });
 }
 
-// Float32 phase on the fp16 matrix cores with split operands (see x3_nt_tile).
+// Float32 steps on the fp16 matrix cores with split operands (see
+// x3_nt_tile).  TB = double: the X update of a float64 step, X (float32) times
+// the float64 M rounded to float32 on load -- M enters X' = (5X - XM/s)/4
+// only as a perturbation of 5, so its float32 rounding is harmless there.
 // X can grow to (eps/c)^(-1/4); the A operand is pre-scaled by a power of two
 // that keeps it below 2^13.
-template <int VEC>
+template <int VEC, typename TB, int VECB>
 __global__ __launch_bounds__(256, VEC == 4 ? 2 : 1) void newton_x3_kernel(const NewtonLaunch L) {
   __shared__ _Float16 smem[X3Tile::LDS_HALVES];
-  const StageJob s = stage_job(L, false);
+  constexpr bool B64 = sizeof(TB) == 8;
+  const StageJob s = stage_job(L, B64 ? kStageX3B64 : kStageX3);
   if (!s.active) return;
   const Roles32 r = roles32(s.region, s.d, L.t);
-  const StageOps<float> o = stage_ops<float>(r, L.stage, s.job, s.s);
+  StageOps<float> o = stage_ops<float>(r, L.stage, s.job, s.s);
+  const TB* Bop = reinterpret_cast<const TB*>(o.B);
+  if constexpr (B64) Bop = roles64(s.region, s.d, L.t).M;
   float ascale = 1.0f;
   if (L.stage == 0 && s.job == 1) {
     const double xmax = pow(s.m0, -0.25);  // |X| <= m0^(-1/4) throughout
@@ -394,7 +415,7 @@ __global__ __launch_bounds__(256, VEC == 4 ? 2 : 1) void newton_x3_kernel(const 
   }
   const int m0 = s.ti * X3Tile::BM, n0 = s.tj * X3Tile::BN;
   v16f acc[2][2];
-  x3_nt_tile<VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, ascale, smem, acc);
+  x3_nt_tile<VEC, TB, VECB>(o.A, s.d, Bop, s.d, s.d, s.d, s.d, m0, n0, ascale, smem, acc);
   const int d = s.d;
   f32_for_each(acc, [&](int rr, int cc, float v) { sym_store(o, d, m0 + rr, n0 + cc, (double)v); });
 }
@@ -419,7 +440,7 @@ __global__ __launch_bounds__(256) void newton_convert_kernel(const NewtonLaunch 
   const int64_t e0 = (int64_t)chunk * per;
   for (int64_t e = e0 + threadIdx.x; e < min(n, e0 + per); e += 256) {
     r32.M[e] = (float)r64.M[e];
-    r32.X[e] = (float)r64.X[e];
+    if (!L.x_low) r32.X[e] = (float)r64.X[e];
   }
 }
 
@@ -445,7 +466,7 @@ __global__ __launch_bounds__(256) void root_finalize_kernel(const RootBatch B) {
   } else {
     const int K = st.K, j = st.j;
     const double sc = st.out_scale;
-    const bool x64 = K <= j;
+    const bool x64 = K <= j && !B.x_low;
     const bool m64 = (K - 1) < j;
     const Roles64 rx64 = roles64(J.region, d, K), rm64 = roles64(J.region, d, K - 1);
     const Roles32 rx32 = roles32(J.region, d, K), rm32 = roles32(J.region, d, K - 1);
@@ -526,9 +547,16 @@ hipError_t launch_newton_stage(const NewtonLaunch& L, int kind, int vec, hipStre
   if (L.total_blocks <= 0) return hipSuccess;
   if (kind == kStageX3) {
     if (vec == 4)
-      hipLaunchKernelGGL(newton_x3_kernel<4>, dim3(L.total_blocks), dim3(256), 0, s, L);
+      hipLaunchKernelGGL((newton_x3_kernel<4, float, 4>), dim3(L.total_blocks), dim3(256), 0, s, L);
     else
-      hipLaunchKernelGGL(newton_x3_kernel<1>, dim3(L.total_blocks), dim3(256), 0, s, L);
+      hipLaunchKernelGGL((newton_x3_kernel<1, float, 1>), dim3(L.total_blocks), dim3(256), 0, s, L);
+    return hipGetLastError();
+  }
+  if (kind == kStageX3B64) {
+    if (vec == 4)
+      hipLaunchKernelGGL((newton_x3_kernel<4, double, 2>), dim3(L.total_blocks), dim3(256), 0, s, L);
+    else
+      hipLaunchKernelGGL((newton_x3_kernel<1, double, 1>), dim3(L.total_blocks), dim3(256), 0, s, L);
     return hipGetLastError();
   }
   if (kind == kStageF64) {
