@@ -618,24 +618,26 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
     if ((st = run_root_batches(1)) != MR_OK) return st;
 
     // Class groups: at most kMaxClasses per launch, split by vector width.
+    // vec64: float64 loads of 2 (d even); vec32: float32 loads of 4 (d % 4 == 0);
+    // vecx3: fp16 loads of 8 (d % 8 == 0).
     struct Group {
       std::vector<int> cls;
-      int vec64, vec32;
+      int vec64, vec32, vecx3;
     };
     std::vector<Group> groups;
-    for (int aligned4 = 1; aligned4 >= 0; --aligned4) {
+    for (const int align : {8, 4, 2, 1}) {
       Group g;
-      g.vec32 = aligned4 ? 4 : 1;
-      g.vec64 = 2;
+      g.vec64 = align >= 2 ? 2 : 1;
+      g.vec32 = align >= 4 ? 4 : 1;
+      g.vecx3 = align >= 8 ? 8 : 1;
       for (int ci = 0; ci < (int)P.classes.size(); ++ci) {
         const int64_t d = P.classes[ci].d;
-        if ((d % 4 == 0) != (aligned4 == 1)) continue;
+        const int a = d % 8 == 0 ? 8 : d % 4 == 0 ? 4 : d % 2 == 0 ? 2 : 1;
+        if (a != align) continue;
         g.cls.push_back(ci);
-        if (d % 2) g.vec64 = 1;
         if ((int)g.cls.size() == kMaxClasses) {
           groups.push_back(g);
           g.cls.clear();
-          g.vec64 = 2;
         }
       }
       if (!g.cls.empty()) groups.push_back(g);
@@ -687,7 +689,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
               return st;
             if (split) {
               const NewtonLaunch LX = make_launch(g, 0, stage, t, 1);
-              if ((st = traced(kTrNewtonX3, true, s, [&] { return launch_newton_stage(LX, kStageX3B64, g.vec32, s); },
+              if ((st = traced(kTrNewtonX3, true, s, [&] { return launch_newton_stage(LX, kStageX3B64, g.vecx3, s); },
                                "newton x3 X update")) != MR_OK)
                 return st;
             }
@@ -696,7 +698,8 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
             const NewtonLaunch L = make_launch(g, 0, stage, t, -1);
             const int kind = f32_mfma ? kStageF32 : kStageX3;
             if ((st = traced(f32_mfma ? kTrNewton32 : kTrNewtonX3, true, s,
-                             [&] { return launch_newton_stage(L, kind, g.vec32, s); }, "newton f32 stage")) != MR_OK)
+                             [&] { return launch_newton_stage(L, kind, f32_mfma ? g.vec32 : g.vecx3, s); },
+                             "newton f32 stage")) != MR_OK)
               return st;
           }
         }

@@ -179,82 +179,82 @@ __device__ __forceinline__ void f32_nt_tile(const float* __restrict__ A, int64_t
 }
 
 // ------------------------------------------------------------- split fp16
-// C = A * B^T for float32 operands on the fp16 matrix cores: each operand
-// value x is split on its way into LDS into hi = fp16(x) and
-// lo = fp16((x - hi) * 2^11) (x - hi is exact in float32), and
+// C = A * B^T for float32-accurate operands on the fp16 matrix cores.  Every
+// operand is stored split: x = hi + 2^-11 lo with hi = fp16(x) and
+// lo = fp16((x - hi) * 2^11) (x - hi is exact in float32), as two fp16 arrays
+// of the operand's shape (the producers write this form, so the GEMM loop only
+// copies fp16 tiles).  Then
 //   C = sum hi_a hi_b + 2^-11 * sum (hi_a lo_b + lo_a hi_b),
 // the two sums in separate float32 accumulators.  Products of 11-bit
 // significands are exact in float32; the dropped lo*lo term and the rounding
 // of lo leave about 2^-22 relative error per product (float32: 2^-24), and
-// the float32 accumulation is the same as on the float32 matrix cores.  The
-// caller passes a power-of-two pre-scale for A that keeps hi below the fp16
-// range (|x * ascale| < 2^15); B is used unscaled.
+// the float32 accumulation is the same as on the float32 matrix cores.
+#ifndef MR_X3_BK
+#define MR_X3_BK 32
+#endif
+#ifndef MR_X3_DBUF
+#define MR_X3_DBUF 1
+#endif
 struct X3Tile {
-  static constexpr int BM = 128, BN = 128, BK = 32, PAD = 8, LDW = BK + PAD;  // halves per LDS row
+  static constexpr int BM = 128, BN = 128, BK = MR_X3_BK, PAD = 8, LDW = BK + PAD;  // halves per LDS row
   static constexpr int THREADS = 256;
-  static constexpr int ARR = BM * LDW;         // halves per array (A_hi, A_lo, B_hi, B_lo)
+  static constexpr bool DBUF = MR_X3_DBUF != 0;
+  static constexpr int ARR = BM * LDW;  // halves per array (A_hi, A_lo, B_hi, B_lo)
   static constexpr int STAGE = 4 * ARR;
-  static constexpr int LDS_HALVES = 2 * STAGE;  // two stages: 80 KiB
+  static constexpr int LDS_HALVES = (DBUF ? 2 : 1) * STAGE;
 };
 
-// Loads a BM x BK chunk of a K-contiguous float32 or float64 operand as
-// groups of 4 consecutive k per thread (float64 is rounded to float32 first).
-// VEC: elements per global load (4 for float, 2 for double, 1 = guarded
-// scalar); VEC > 1 needs ld and K multiples of VEC and an aligned base.
-template <typename TIn, int VEC>
-struct X3Loader {
-  static constexpr int BK = X3Tile::BK;
-  static constexpr int GROUPS = (X3Tile::BM * BK) / (X3Tile::THREADS * 4);
-  static constexpr int GPR = BK / 4;  // groups per row
-  v4f reg[GROUPS];
+struct SplitRef {
+  const _Float16* hi;
+  const _Float16* lo;
+};
 
-  __device__ __forceinline__ void load(const TIn* __restrict__ P, int64_t ld, int rows, int K, int r0, int k0,
-                                       int tid) {
+__device__ __forceinline__ void split_f32(float x, _Float16& h, _Float16& l) {
+  h = (_Float16)x;
+  l = (_Float16)((x - (float)h) * 2048.0f);
+}
+__device__ __forceinline__ float join_f32(_Float16 h, _Float16 l) { return (float)h + (float)l * (1.0f / 2048.0f); }
+
+// Loads a BM x BK chunk of a K-contiguous split operand.  VEC = 8 (16-byte
+// loads; needs ld and K multiples of 8 and 16-byte aligned arrays) or 1.
+template <int VEC>
+struct SplitLoader {
+  static constexpr int BK = X3Tile::BK;
+  static constexpr int PER = (X3Tile::BM * BK) / (X3Tile::THREADS * 8);  // groups of 8 halves
+  static constexpr int GPR = BK / 8;
+  v8h rh[PER], rl[PER];
+
+  __device__ __forceinline__ void load(SplitRef P, int64_t ld, int rows, int K, int r0, int k0, int tid) {
 #pragma unroll
-    for (int p = 0; p < GROUPS; ++p) {
+    for (int p = 0; p < PER; ++p) {
       const int idx = tid + p * X3Tile::THREADS;
-      const int gr = r0 + idx / GPR, gk = k0 + (idx % GPR) * 4;
-      const bool row_ok = gr < rows;
-      const TIn* src = P + (int64_t)gr * ld + gk;
-      v4f v = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (VEC == 4) {
-        if (row_ok && gk < K) v = *reinterpret_cast<const v4f*>(src);
-      } else if constexpr (VEC == 2) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          if (row_ok && gk + 2 * h < K) {
-            const v2d w = *reinterpret_cast<const v2d*>(src + 2 * h);
-            v[2 * h] = (float)w[0];
-            v[2 * h + 1] = (float)w[1];
-          }
+      const int gr = r0 + idx / GPR, gk = k0 + (idx % GPR) * 8;
+      const int64_t off = (int64_t)gr * ld + gk;
+      if constexpr (VEC == 8) {
+        v8h h = {}, l = {};
+        if (gr < rows && gk < K) {
+          h = *reinterpret_cast<const v8h*>(P.hi + off);
+          l = *reinterpret_cast<const v8h*>(P.lo + off);
+        }
+        rh[p] = h;
+        rl[p] = l;
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (row_ok && gk + e < K) v[e] = (float)src[e];
+        for (int e = 0; e < 8; ++e) {
+          const bool ok = gr < rows && gk + e < K;
+          rh[p][e] = ok ? P.hi[off + e] : (_Float16)0.0f;
+          rl[p][e] = ok ? P.lo[off + e] : (_Float16)0.0f;
+        }
       }
-      reg[p] = v;
     }
   }
-  __device__ __forceinline__ static void split(float x, _Float16& h, _Float16& l) {
-    h = (_Float16)x;
-    l = (_Float16)((x - (float)h) * 2048.0f);
-  }
-  __device__ __forceinline__ void store(_Float16* __restrict__ hi, _Float16* __restrict__ lo, float scale,
-                                        int tid) const {
+  __device__ __forceinline__ void store(_Float16* __restrict__ hi, _Float16* __restrict__ lo, int tid) const {
 #pragma unroll
-    for (int p = 0; p < GROUPS; ++p) {
+    for (int p = 0; p < PER; ++p) {
       const int idx = tid + p * X3Tile::THREADS;
-      const int off = (idx / GPR) * X3Tile::LDW + (idx % GPR) * 4;
-      v4h h, l;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        _Float16 a, b;
-        split(reg[p][e] * scale, a, b);
-        h[e] = a;
-        l[e] = b;
-      }
-      *reinterpret_cast<v4h*>(hi + off) = h;
-      *reinterpret_cast<v4h*>(lo + off) = l;
+      const int off = (idx / GPR) * X3Tile::LDW + (idx % GPR) * 8;
+      *reinterpret_cast<v8h*>(hi + off) = rh[p];
+      *reinterpret_cast<v8h*>(lo + off) = rl[p];
     }
   }
 };
@@ -292,11 +292,10 @@ __device__ __forceinline__ void x3_chunk(const _Float16* __restrict__ st, v16f (
   }
 }
 
-// Result in acc (already combined: acc + 2^-11 acc2, divided by ascale).
-template <int VECA, typename TB, int VECB>
-__device__ __forceinline__ void x3_nt_tile(const float* __restrict__ A, int64_t lda, const TB* __restrict__ B,
-                                           int64_t ldb, int M, int N, int K, int m0, int n0, float ascale,
-                                           _Float16* __restrict__ lds, v16f (&acc)[2][2]) {
+// Result in acc (combined: acc + 2^-11 acc2).
+template <int VEC>
+__device__ __forceinline__ void x3_nt_tile(SplitRef A, int64_t lda, SplitRef B, int64_t ldb, int M, int N, int K,
+                                           int m0, int n0, _Float16* __restrict__ lds, v16f (&acc)[2][2]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -312,36 +311,48 @@ __device__ __forceinline__ void x3_nt_tile(const float* __restrict__ A, int64_t 
         acc[rb][cb][v] = 0.f;
         acc2[rb][cb][v] = 0.f;
       }
-  X3Loader<float, VECA> la;
-  X3Loader<TB, VECB> lb;
+  SplitLoader<VEC> la, lb;
   la.load(A, lda, M, K, m0, 0, tid);
   lb.load(B, ldb, N, K, n0, 0, tid);
-  la.store(lds, lds + X3Tile::ARR, ascale, tid);
-  lb.store(lds + 2 * X3Tile::ARR, lds + 3 * X3Tile::ARR, 1.0f, tid);
-  __syncthreads();
-  int stage = 0;
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    const bool more = k0 + BK < K;
-    if (more) {
-      la.load(A, lda, M, K, m0, k0 + BK, tid);
-      lb.load(B, ldb, N, K, n0, k0 + BK, tid);
-    }
-    x3_chunk(lds + stage * X3Tile::STAGE, acc, acc2, lane, wm, wn);
-    if (more) {
-      _Float16* nxt = lds + (stage ^ 1) * X3Tile::STAGE;
-      la.store(nxt, nxt + X3Tile::ARR, ascale, tid);
-      lb.store(nxt + 2 * X3Tile::ARR, nxt + 3 * X3Tile::ARR, 1.0f, tid);
-    }
+  if constexpr (X3Tile::DBUF) {
+    la.store(lds, lds + X3Tile::ARR, tid);
+    lb.store(lds + 2 * X3Tile::ARR, lds + 3 * X3Tile::ARR, tid);
     __syncthreads();
-    stage ^= 1;
+    int stage = 0;
+    for (int k0 = 0; k0 < K; k0 += BK) {
+      const bool more = k0 + BK < K;
+      if (more) {
+        la.load(A, lda, M, K, m0, k0 + BK, tid);
+        lb.load(B, ldb, N, K, n0, k0 + BK, tid);
+      }
+      x3_chunk(lds + stage * X3Tile::STAGE, acc, acc2, lane, wm, wn);
+      if (more) {
+        _Float16* nxt = lds + (stage ^ 1) * X3Tile::STAGE;
+        la.store(nxt, nxt + X3Tile::ARR, tid);
+        lb.store(nxt + 2 * X3Tile::ARR, nxt + 3 * X3Tile::ARR, tid);
+      }
+      __syncthreads();
+      stage ^= 1;
+    }
+  } else {
+    for (int k0 = 0; k0 < K; k0 += BK) {
+      la.store(lds, lds + X3Tile::ARR, tid);
+      lb.store(lds + 2 * X3Tile::ARR, lds + 3 * X3Tile::ARR, tid);
+      __syncthreads();
+      if (k0 + BK < K) {
+        la.load(A, lda, M, K, m0, k0 + BK, tid);
+        lb.load(B, ldb, N, K, n0, k0 + BK, tid);
+      }
+      x3_chunk(lds, acc, acc2, lane, wm, wn);
+      __syncthreads();
+    }
   }
-  const float inv = 1.0f / ascale;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = (acc[rb][cb][v] + acc2[rb][cb][v] * (1.0f / 2048.0f)) * inv;
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = acc[rb][cb][v] + acc2[rb][cb][v] * (1.0f / 2048.0f);
 }
 
 // Visit every accumulator element of the f32 core as (row, col) local to the

@@ -77,6 +77,47 @@ __device__ __forceinline__ Roles32 roles32(char* region, int d, int t) {
   return r;
 }
 
+// Split storage (default Newton path): a half-slot h holds hi[d*d] then
+// lo[d*d] (fp16 each), value = hi + 2^-11 lo.  Float32 steps use the Roles32
+// positions; during float64 steps X sits at its Roles32 position too and the
+// split copy of the float64 M for the X update (Mx) at half-slot 5.
+struct SplitBuf {
+  _Float16* hi;
+  _Float16* lo;
+  __device__ SplitRef ref() const { return SplitRef{hi, lo}; }
+};
+__device__ __forceinline__ SplitBuf split_at(char* region, int d, int h) {
+  _Float16* hi = reinterpret_cast<_Float16*>(region + (int64_t)h * d * d * 4);
+  return SplitBuf{hi, hi + (int64_t)d * d};
+}
+struct RolesS {
+  SplitBuf M, T2, X, Xn, T4, Mx;
+};
+__device__ __forceinline__ RolesS roless(char* region, int d, int t) {
+  const bool even = (t & 1) == 0;
+  RolesS r;
+  r.M = split_at(region, d, even ? 8 : 0);
+  r.T2 = split_at(region, d, even ? 0 : 8);
+  r.X = split_at(region, d, even ? 4 : 2);
+  r.Xn = split_at(region, d, even ? 2 : 4);
+  r.T4 = split_at(region, d, 9);
+  r.Mx = split_at(region, d, 5);
+  return r;
+}
+// X is stored times 2^-e so that |X| <= (eps/c)^(-1/4) stays below 2^13 in
+// fp16 (X updates are linear in X; the finalize undoes the scale).
+__device__ __forceinline__ float x_store_scale(const RootState& st) {
+  const double xmax = pow(st.eps / st.c, -0.25);
+  const int e = (int)ceil(log2(xmax)) - 13;
+  return e > 0 ? ldexpf(1.0f, -e) : 1.0f;
+}
+__device__ __forceinline__ void split_put(const SplitBuf& b, int64_t i, float v) {
+  _Float16 h, l;
+  split_f32(v, h, l);
+  b.hi[i] = h;
+  b.lo[i] = l;
+}
+
 // ------------------------------------------------------ block reductions
 // Fixed-order tree over 256 threads: the same inputs give the same bits.
 __device__ __forceinline__ double block_sum_256(double v, double* red) {
@@ -248,7 +289,8 @@ __global__ __launch_bounds__(256) void root_init_kernel(const RootBatch B) {
   const double inv_s = 1.0 / st.s, inv_c = 1.0 / st.c, eps = B.eps;
   double* M = reinterpret_cast<double*>(J.region);
   double* X = reinterpret_cast<double*>(J.region + (int64_t)d * d * 8);
-  float* X32 = roles32(J.region, d, 0).X;
+  const RolesS rs = roless(J.region, d, 0);
+  const float xs = B.x_low ? x_store_scale(st) : 1.0f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int r = ty + 8 * e;
@@ -256,11 +298,14 @@ __global__ __launch_bounds__(256) void root_init_kernel(const RootBatch B) {
     if (gi < d && gj < d) {
       const double sym = 0.5 * (ta[r][tx] + tb[tx][r]);
       const double v = (sym * inv_s + (gi == gj ? eps : 0.0)) * inv_c;
-      M[(int64_t)gi * d + gj] = v;
-      if (B.x_low)
-        X32[(int64_t)gi * d + gj] = (gi == gj) ? 1.f : 0.f;
-      else
-        X[(int64_t)gi * d + gj] = (gi == gj) ? 1.0 : 0.0;
+      const int64_t e = (int64_t)gi * d + gj;
+      M[e] = v;
+      if (B.x_low) {
+        split_put(rs.Mx, e, (float)v);
+        split_put(rs.X, e, gi == gj ? xs : 0.f);
+      } else {
+        X[e] = (gi == gj) ? 1.0 : 0.0;
+      }
     }
   }
 }
@@ -364,7 +409,8 @@ __device__ __forceinline__ void sym_store(const StageOps<T>& o, int d, int gr, i
 }
 
 template <int VEC>
-__global__ __launch_bounds__(256, MR_F64_OCC) void newton_f64_kernel(const NewtonLaunch L) {
+__global__ __launch_bounds__(256, VEC == 2 ? MR_F64_OCC : 1) void newton_f64_kernel(const NewtonLaunch L) {
+  // (with x_low, stage 2 also writes the split copy Mx of the new M)
   __shared__ double smem[F64Tile::LDS_DOUBLES];
   const StageJob s = stage_job(L, kStageF64);
   if (!s.active) return;
@@ -374,7 +420,23 @@ __global__ __launch_bounds__(256, MR_F64_OCC) void newton_f64_kernel(const Newto
   v4d acc[4][4];
   f64_tile<double, false, VEC, double, false, VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, smem, acc);
   const int d = s.d;
-  f64_for_each(acc, [&](int rr, int cc, double v) { sym_store(o, d, m0 + rr, n0 + cc, v); });
+  if (L.x_low && L.stage == 2) {
+    const SplitBuf mx = roless(s.region, d, L.t).Mx;
+    f64_for_each(acc, [&](int rr, int cc, double v) {
+      const int gr = m0 + rr, gc = n0 + cc;
+      if (gr < d && gc < d && gr <= gc) {
+        const double val = o.alpha * v;
+        o.C[(int64_t)gr * d + gc] = val;
+        split_put(mx, (int64_t)gr * d + gc, (float)val);
+        if (gr != gc) {
+          o.C[(int64_t)gc * d + gr] = val;
+          split_put(mx, (int64_t)gc * d + gr, (float)val);
+        }
+      }
+    });
+  } else {
+    f64_for_each(acc, [&](int rr, int cc, double v) { sym_store(o, d, m0 + rr, n0 + cc, v); });
+  }
 }
 
 template <int VEC>
@@ -391,33 +453,95 @@ __global__ __launch_bounds__(256, MR_F32_OCC) void newton_f32_kernel(const Newto
   f32_for_each(acc, [&](int rr, int cc, float v) { sym_store(o, d, m0 + rr, n0 + cc, (double)v); });
 }
 
-// Float32 steps on the fp16 matrix cores with split operands (see
-// x3_nt_tile).  TB = double: the X update of a float64 step, X (float32) times
-// the float64 M rounded to float32 on load -- M enters X' = (5X - XM/s)/4
-// only as a perturbation of 5, so its float32 rounding is harmless there.
-// X can grow to (eps/c)^(-1/4); the A operand is pre-scaled by a power of two
-// that keeps it below 2^13.
-template <int VEC, typename TB, int VECB>
-__global__ __launch_bounds__(256, VEC == 4 ? 2 : 1) void newton_x3_kernel(const NewtonLaunch L) {
-  __shared__ _Float16 smem[X3Tile::LDS_HALVES];
-  constexpr bool B64 = sizeof(TB) == 8;
-  const StageJob s = stage_job(L, B64 ? kStageX3B64 : kStageX3);
-  if (!s.active) return;
-  const Roles32 r = roles32(s.region, s.d, L.t);
-  StageOps<float> o = stage_ops<float>(r, L.stage, s.job, s.s);
-  const TB* Bop = reinterpret_cast<const TB*>(o.B);
-  if constexpr (B64) Bop = roles64(s.region, s.d, L.t).M;
-  float ascale = 1.0f;
-  if (L.stage == 0 && s.job == 1) {
-    const double xmax = pow(s.m0, -0.25);  // |X| <= m0^(-1/4) throughout
-    const int e = (int)ceil(log2(xmax)) - 13;
-    if (e > 0) ascale = ldexpf(1.0f, -e);
+// Float32 steps on the fp16 matrix cores with split storage (see
+// x3_nt_tile).  kStageX3B64: the X update of a float64 step, X times the
+// split copy Mx of the float64 M -- M enters X' = s^(-1/4)(5X - XM/s)/4 only
+// as a perturbation of 5, so its float32 rounding is harmless there.
+struct SplitOps {
+  SplitRef A, B, Cin;
+  SplitBuf C;
+  bool has_cin;
+  double alpha, beta, gamma;
+};
+
+__device__ __forceinline__ SplitOps split_ops(const RolesS& r, int stage, int job, double s, bool xm) {
+  SplitOps o;
+  o.has_cin = false;
+  o.alpha = 1.0;
+  o.beta = 0.0;
+  o.gamma = 0.0;
+  const double is = 1.0 / s;
+  if (stage == 0 && job == 0) {  // T2 = ((M/s)^2 - 10 M/s + 25 I) / 16
+    o.A = r.M.ref(); o.B = r.M.ref(); o.C = r.T2; o.Cin = r.M.ref(); o.has_cin = true;
+    o.alpha = is * is / 16.0; o.beta = -10.0 * is / 16.0; o.gamma = 25.0 / 16.0;
+  } else if (stage == 0) {  // X' = s^(-1/4) (5 X - X M/s) / 4
+    const double q = pow(s, -0.25);
+    o.A = r.X.ref(); o.B = xm ? r.Mx.ref() : r.M.ref(); o.C = r.Xn; o.Cin = r.X.ref(); o.has_cin = true;
+    o.alpha = -0.25 * q * is; o.beta = 1.25 * q;
+  } else if (stage == 1) {  // T4 = T2 T2
+    o.A = r.T2.ref(); o.B = r.T2.ref(); o.C = r.T4;
+  } else {  // M' = T4 M / s, written over T2
+    o.A = r.T4.ref(); o.B = r.M.ref(); o.C = r.T2;
+    o.alpha = is;
   }
+  return o;
+}
+
+template <int VEC>
+__global__ __launch_bounds__(256, 2) void newton_x3_kernel(const NewtonLaunch L, int kind) {
+  __shared__ _Float16 smem[X3Tile::LDS_HALVES];
+  const StageJob s = stage_job(L, kind);
+  if (!s.active) return;
+  const RolesS r = roless(s.region, s.d, L.t);
+  const SplitOps o = split_ops(r, L.stage, s.job, s.s, kind == kStageX3B64);
   const int m0 = s.ti * X3Tile::BM, n0 = s.tj * X3Tile::BN;
   v16f acc[2][2];
-  x3_nt_tile<VEC, TB, VECB>(o.A, s.d, Bop, s.d, s.d, s.d, s.d, m0, n0, ascale, smem, acc);
+  x3_nt_tile<VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, smem, acc);
   const int d = s.d;
-  f32_for_each(acc, [&](int rr, int cc, float v) { sym_store(o, d, m0 + rr, n0 + cc, (double)v); });
+  if (VEC == 8 && s.ti < s.tj && m0 + X3Tile::BM <= d && n0 + X3Tile::BN <= d) {
+    // Full off-diagonal tile: every element is above the diagonal.  A lane
+    // holds 4 consecutive rows of one column per MFMA value group, i.e. 4
+    // consecutive columns of the mirrored row: one 8-byte store per array.
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int gc = n0 + wn * 64 + cb * 32 + (lane & 31);
+          const int gr0 = m0 + wm * 64 + rb * 32 + 8 * g + 4 * (lane >> 5);
+          v4h hh, ll;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t idx = (int64_t)(gr0 + e) * d + gc;
+            double val = o.alpha * (double)acc[rb][cb][4 * g + e];
+            if (o.has_cin) val += o.beta * (double)join_f32(o.Cin.hi[idx], o.Cin.lo[idx]);
+            _Float16 h, l;
+            split_f32((float)val, h, l);
+            o.C.hi[idx] = h;
+            o.C.lo[idx] = l;
+            hh[e] = h;
+            ll[e] = l;
+          }
+          const int64_t midx = (int64_t)gc * d + gr0;
+          *reinterpret_cast<v4h*>(o.C.hi + midx) = hh;
+          *reinterpret_cast<v4h*>(o.C.lo + midx) = ll;
+        }
+    return;
+  }
+  f32_for_each(acc, [&](int rr, int cc, float v) {
+    const int gr = m0 + rr, gc = n0 + cc;
+    if (gr < d && gc < d && gr <= gc) {
+      const int64_t e = (int64_t)gr * d + gc;
+      double val = o.alpha * (double)v;
+      if (o.has_cin) val += o.beta * (double)join_f32(o.Cin.hi[e], o.Cin.lo[e]);
+      if (gr == gc) val += o.gamma;
+      split_put(o.C, e, (float)val);
+      if (gr != gc) split_put(o.C, (int64_t)gc * d + gr, (float)val);
+    }
+  });
 }
 
 // float64 M, X of iteration t -> float32 M, X of iteration t, for the
@@ -438,9 +562,14 @@ __global__ __launch_bounds__(256) void newton_convert_kernel(const NewtonLaunch 
   const int64_t n = (int64_t)C.d * C.d;
   const int64_t per = 256 * 8;
   const int64_t e0 = (int64_t)chunk * per;
-  for (int64_t e = e0 + threadIdx.x; e < min(n, e0 + per); e += 256) {
-    r32.M[e] = (float)r64.M[e];
-    if (!L.x_low) r32.X[e] = (float)r64.X[e];
+  if (L.x_low) {
+    const SplitBuf ms = roless(region, C.d, t).M;
+    for (int64_t e = e0 + threadIdx.x; e < min(n, e0 + per); e += 256) split_put(ms, e, (float)r64.M[e]);
+  } else {
+    for (int64_t e = e0 + threadIdx.x; e < min(n, e0 + per); e += 256) {
+      r32.M[e] = (float)r64.M[e];
+      r32.X[e] = (float)r64.X[e];
+    }
   }
 }
 
@@ -466,16 +595,25 @@ __global__ __launch_bounds__(256) void root_finalize_kernel(const RootBatch B) {
   } else {
     const int K = st.K, j = st.j;
     const double sc = st.out_scale;
-    const bool x64 = K <= j && !B.x_low;
+    const bool x64 = K <= j;
     const bool m64 = (K - 1) < j;
     const Roles64 rx64 = roles64(J.region, d, K), rm64 = roles64(J.region, d, K - 1);
     const Roles32 rx32 = roles32(J.region, d, K), rm32 = roles32(J.region, d, K - 1);
+    const RolesS rxs = roless(J.region, d, K), rms = roless(J.region, d, K - 1);
+    const double xsc = B.x_low ? sc / (double)x_store_scale(st) : sc;
     for (int r = r0; r < r1; ++r) {
       for (int c = threadIdx.x; c < d; c += 256) {
         const int64_t e = (int64_t)r * d + c;
-        const double x = x64 ? rx64.X[e] : (double)rx32.X[e];
-        J.X[(int64_t)r * J.ldx + c] = (float)(sc * x);
-        const double m = (m64 ? rm64.M[e] : (double)rm32.M[e]) - (r == c ? 1.0 : 0.0);
+        double x, m;
+        if (B.x_low) {
+          x = (double)join_f32(rxs.X.hi[e], rxs.X.lo[e]);
+          m = m64 ? rm64.M[e] : (double)join_f32(rms.M.hi[e], rms.M.lo[e]);
+        } else {
+          x = x64 ? rx64.X[e] : (double)rx32.X[e];
+          m = m64 ? rm64.M[e] : (double)rm32.M[e];
+        }
+        J.X[(int64_t)r * J.ldx + c] = (float)(xsc * x);
+        m -= (r == c ? 1.0 : 0.0);
         res += m * m;
       }
     }
@@ -545,18 +683,11 @@ hipError_t launch_root_init(const RootBatch& b, hipStream_t s) {
 
 hipError_t launch_newton_stage(const NewtonLaunch& L, int kind, int vec, hipStream_t s) {
   if (L.total_blocks <= 0) return hipSuccess;
-  if (kind == kStageX3) {
-    if (vec == 4)
-      hipLaunchKernelGGL((newton_x3_kernel<4, float, 4>), dim3(L.total_blocks), dim3(256), 0, s, L);
+  if (kind == kStageX3 || kind == kStageX3B64) {
+    if (vec >= 8)
+      hipLaunchKernelGGL(newton_x3_kernel<8>, dim3(L.total_blocks), dim3(256), 0, s, L, kind);
     else
-      hipLaunchKernelGGL((newton_x3_kernel<1, float, 1>), dim3(L.total_blocks), dim3(256), 0, s, L);
-    return hipGetLastError();
-  }
-  if (kind == kStageX3B64) {
-    if (vec == 4)
-      hipLaunchKernelGGL((newton_x3_kernel<4, double, 2>), dim3(L.total_blocks), dim3(256), 0, s, L);
-    else
-      hipLaunchKernelGGL((newton_x3_kernel<1, double, 1>), dim3(L.total_blocks), dim3(256), 0, s, L);
+      hipLaunchKernelGGL(newton_x3_kernel<1>, dim3(L.total_blocks), dim3(256), 0, s, L, kind);
     return hipGetLastError();
   }
   if (kind == kStageF64) {
