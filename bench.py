@@ -102,6 +102,38 @@ def cpu_baseline(workload: str):
             "sample": sample, "seconds": sum(float(x.split(": ")[1].split("s")[0]) for x in timed)}
 
 
+def per_size_class(B, torch, grams, wl):
+    """One inv_quarter_root_batched call per Gram size d > 128 on the given
+    (final) state, timed with events on the current stream after one untimed
+    call: ms, algorithmic TFLOP/s and its fraction of the fp32 MFMA peak."""
+    out = {}
+    for d in sorted({int(A.shape[0]) for A in grams}):
+        if d <= 128:
+            continue
+        As = [A for A in grams if A.shape[0] == d]
+        Xs = [torch.empty(d, d, dtype=torch.float32, device=A.device) for A in As]
+        ws = B.RootWorkspace()
+        B.inv_quarter_root_batched(As, wl.eps, normalize=wl.normalize, Xs=Xs, workspace=ws, return_info=False)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        raw = torch.empty(32 * len(As), dtype=torch.uint8, device=As[0].device)
+        e0.record()
+        B.inv_quarter_root_batched(As, wl.eps, normalize=wl.normalize, Xs=Xs, workspace=ws, return_info=False,
+                                   info_out=raw)
+        e1.record()
+        torch.cuda.synchronize()
+        info = B.decode_info(raw, len(As))
+        ms = e0.elapsed_time(e1)
+        flops = sum(sum(newton_flops(d, int(r["iters"]), int(r["fp64_iters"]))) for r in info)
+        tf = flops / (ms / 1e3) / 1e12
+        out[str(d)] = {"count": len(As), "ms": round(ms, 3), "tflops": round(tf, 2),
+                       "pct_fp32_mfma_peak": round(100 * tf / PEAK_TFLOPS["f32"], 2),
+                       "iters": [int(info["iters"].min()), int(info["iters"].max())],
+                       "fp64_iters": [int(info["fp64_iters"].min()), int(info["fp64_iters"].max())]}
+        log(f"size class {d}: {out[str(d)]}")
+        del Xs, ws
+    return out
+
+
 def recorded_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` from the committed counter summary,
     if the kernel sources are unchanged since the counters were taken."""
@@ -131,6 +163,12 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="w1024", choices=["toy", "w1024", "w2048", "moe"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--state-dtype", default="f64", choices=["f64", "f32"])
+    ap.add_argument("--gradients", default="auto", choices=["auto", "host", "device"],
+                    help="where the synthetic gradients are drawn: host = the seeded numpy draws the "
+                         "parity tests use; device = same distribution drawn with torch on the GPU "
+                         "(auto: device for w2048, whose Haar factors take seconds each on the host)")
+    ap.add_argument("--per-size-class", action="store_true",
+                    help="after the timed steps, time one root call per Gram size class on the final state")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run a plain device copy of this many MiB 3 times first (counter calibration)")
     args = ap.parse_args(argv)
@@ -160,11 +198,16 @@ def main(argv=None) -> int:
     wl = W.WORKLOADS[args.workload]
     shapes = [(m, n) for _, m, n in wl.shapes]
     nw = len(shapes)
-    log(f"workload {args.workload}: {nw} weights, generating {wl.steps} steps of gradients")
+    gen = args.gradients if args.gradients != "auto" else ("device" if args.workload == "w2048" else "host")
+    log(f"workload {args.workload}: {nw} weights, generating {wl.steps} steps of gradients on the {gen}")
     t0 = time.perf_counter()
     grads = []
     for t in range(1, wl.steps + 1):
-        grads.append([torch.from_numpy(W.gradient(args.workload, w, t)).to(dev) for w in range(nw)])
+        if gen == "host":
+            grads.append([torch.from_numpy(W.gradient(args.workload, w, t)).to(dev) for w in range(nw)])
+        else:
+            grads.append([W.gradient_device(args.workload, w, t, dev) for w in range(nw)])
+        torch.cuda.synchronize()
         log(f"  step {t} gradients resident ({time.perf_counter() - t0:.1f}s)")
     sdt = torch.float64 if args.state_dtype == "f64" else torch.float32
     Ls = [torch.zeros(m, m, dtype=sdt, device=dev) for m, n in shapes]
@@ -239,6 +282,12 @@ def main(argv=None) -> int:
                 "achieved_per_launch": "algorithmic flops of the class over the timed steps / sum of its "
                                        "event-measured launch durations"}
 
+    size_classes = None
+    if args.per_size_class:
+        del ws, Xs, Us, grads  # the per-class calls take their own workspaces
+        torch.cuda.empty_cache()
+        size_classes = per_size_class(B, torch, Ls + Rs, wl)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on its sample")
@@ -262,7 +311,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": args.workload, "weights": nw, "grams_per_step": 2 * nw,
                    "shapes": sorted({f"{m}x{n}" for m, n in shapes}), "beta": wl.beta, "eps": wl.eps,
-                   "normalize": wl.normalize, "state_dtype": args.state_dtype},
+                   "normalize": wl.normalize, "state_dtype": args.state_dtype, "gradients": gen},
         "tflops": round(step_flops / (ms_per_step / 1e3) / 1e12, 2),
         "pct_fp32_mfma_peak": round(100 * step_flops / (ms_per_step / 1e3) / 1e12 / PEAK_TFLOPS["f32"], 2),
         "newton_iters": {"min": kmin, "max": kmax},
@@ -270,6 +319,8 @@ def main(argv=None) -> int:
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
+    if size_classes is not None:
+        out["size_classes"] = size_classes
     print(json.dumps(out), flush=True)
     return 0
 

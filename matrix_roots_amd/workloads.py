@@ -141,3 +141,55 @@ def illcond_batch(count: int = 256, d: int = 512) -> np.ndarray:
     for i in range(count):
         out[i] = spd_loguniform(d, rng_for(WORKLOAD_IDS["illcond"], 0, i, 0))
     return out
+
+
+def _device_seed(workload_id: int, *key: int) -> int:
+    ss = np.random.SeedSequence(0, spawn_key=(int(workload_id), 1) + tuple(int(k) for k in key))
+    return int(ss.generate_state(1, dtype=np.uint64)[0] & np.uint64(2 ** 63 - 1))
+
+
+def gradient_device(workload: str, weight: int, step: int, device, shape=None):
+    """A gradient with the same distribution, shape and structure as
+    `gradient`, drawn on a torch device with torch's own generator.
+
+    The values differ from the host draws (another random stream, seeded
+    from the same (workload, weight, step) key); throughput runs use these
+    where host generation would take minutes (the width-2048 set's Haar
+    factors), parity tests never do.
+    """
+    import torch
+
+    w = WORKLOADS[workload]
+    if shape is None:
+        _, m, n = w.shapes[weight]
+    else:
+        m, n = shape
+    g = torch.Generator(device=device)
+    g.manual_seed(_device_seed(WORKLOAD_IDS[workload], weight, step))
+
+    def normal(*size, dtype=torch.float32):
+        return torch.randn(*size, generator=g, device=device, dtype=dtype)
+
+    if w.kind == "gaussian":
+        return normal(m, n)
+    if w.kind == "lowrank32":
+        A, B, N = normal(m, 32), normal(n, 32), normal(m, n)
+        return A @ B.T.contiguous() + 0.1 * N
+    if w.kind == "powerlaw":
+        r = min(m, n)
+
+        def haar(rows):
+            Q, Rm = torch.linalg.qr(normal(rows, r, dtype=torch.float64))
+            sgn = torch.sign(torch.diagonal(Rm))
+            sgn[sgn == 0] = 1.0
+            return Q * sgn
+
+        U, V = haar(m), haar(n)
+        sigma = torch.arange(1, r + 1, device=device, dtype=torch.float64) ** -0.7
+        return ((U * sigma) @ V.T.contiguous()).to(torch.float32)
+    if w.kind == "sparserows":
+        G = normal(m, n)
+        zero = torch.randperm(m, generator=g, device=device)[: int(np.floor(0.3 * m))]
+        G[zero, :] = 0.0
+        return G
+    raise ValueError(f"unknown gradient kind {w.kind!r}")
