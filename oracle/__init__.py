@@ -12,6 +12,7 @@ from .step import (  # noqa: F401
     NORM_TRACE,
     gram_ema_update,
     inv_quarter_root,
+    inv_sqrt_root,
     left_gram,
     precondition_apply,
     preconditioner_step,

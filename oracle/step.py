@@ -9,15 +9,18 @@ What it computes, and where the pages define it:
 
 * marin.community, "Sharding EMA-Gram eigensolves", section "Background":
   for every linear weight the optimizer keeps an exponential moving average of
-  G·Gᵀ (the left Gram) and of Gᵀ·G (the right Gram, "the reverse order"). At
+  G·Gᵀ (the left Gram) and of Gᵀ·G (the right Gram, factors in reverse order). At
   each update it rescales both Grams, decomposes each into eigenvectors and
   eigenvalues, adds a small regulariser to the eigenvalues, raises them to
   -1/4, rebuilds the matrices, and uses these inverse quarter powers to shape
   the direction of the update.
 * The two-sided shape U = L^-1/4 · G · R^-1/4 is the Shampoo form described
   in tilderesearch, "Online KL Shampoo", section 1 (its formulas did not
-  survive extraction; the shape used here is the one the build's problem
-  statement fixes).
+  survive extraction; the quarter powers on both sides are the EMA-Gram
+  page's).
+* The inverse square root of a symmetric positive definite matrix, the root
+  tilderesearch, "Online KL Shampoo", computes for its preconditioner
+  (sections 2.2-2.4, appendix D), as the same eigenvalue map with power -1/2.
 
 Readings taken where the pages are silent (each is listed with its reason in
 the design notes):
@@ -61,7 +64,7 @@ def left_gram(G) -> np.ndarray:
 
 
 def right_gram(G) -> np.ndarray:
-    """Gᵀ·G (n×n): the product "in the reverse order" (EMA-Gram page, Background)."""
+    """Gᵀ·G (n×n): the product with the factors in reverse order (EMA-Gram page, Background)."""
     G = _f64(G)
     return G.T @ G
 
@@ -129,6 +132,44 @@ def inv_quarter_root(A, eps: float, normalize: str = NORM_TRACE):
     X = (V * f) @ V.T
     X = 0.5 * (X + X.T)
     return X, {"scale": s, "flags": 0, "eigenvalues": w}
+
+
+def inv_sqrt_root(A, eps: float, normalize: str = NORM_NONE):
+    """W = (Â + eps·I)^(-1/2) by a dense symmetric eigensolver.
+
+    tilderesearch, "Online KL Shampoo", appendix D: the batched root returns
+    the inverse square root of a symmetric positive definite matrix S (its
+    section 2.2 computes it by a coupled Newton-Schulz iteration; what that
+    iteration converges to is this matrix function).  Here S = Â + eps·I with
+    Â = sym(A)/s from :func:`rescale`; normalize="none" and eps=0 give the
+    page's S^(-1/2) of sym(A) itself.
+
+    Returns (W, info) like :func:`inv_quarter_root`: NaN for non-finite
+    input (NONFINITE) or some eigenvalue + eps <= 0 (NOT_PD);
+    eps^(-1/2)·I for a zero trace (ZERO_TRACE).
+    """
+    A = _f64(A)
+    d = A.shape[0]
+    if A.shape != (d, d):
+        raise ValueError("A must be square")
+    eps = float(eps)
+    if not np.all(np.isfinite(A)):
+        return np.full((d, d), np.nan), {"scale": float("nan"), "flags": FLAG_NONFINITE,
+                                         "eigenvalues": None}
+    A = 0.5 * (A + A.T)
+    Ahat, s = rescale(A, normalize)
+    if s == 0.0:
+        W = eps ** -0.5 * np.eye(d) if eps > 0.0 else np.full((d, d), np.nan)
+        return W, {"scale": 0.0, "flags": FLAG_ZERO_TRACE | (0 if eps > 0.0 else FLAG_NOT_PD),
+                   "eigenvalues": np.zeros(d)}
+    w, V = np.linalg.eigh(Ahat)
+    shifted = w + eps
+    if np.min(shifted) <= 0.0:
+        return np.full((d, d), np.nan), {"scale": s, "flags": FLAG_NOT_PD, "eigenvalues": w}
+    f = shifted ** -0.5
+    W = (V * f) @ V.T
+    W = 0.5 * (W + W.T)
+    return W, {"scale": s, "flags": 0, "eigenvalues": w}
 
 
 def precondition_apply(XL, G, XR, alpha: float = 1.0) -> np.ndarray:
