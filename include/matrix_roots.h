@@ -192,6 +192,59 @@ mr_status inv_quarter_root_batched(const mr_root_problem* problems, int32_t coun
 size_t inv_quarter_root_batched_workspace(const mr_root_problem* problems, int32_t count,
                                           mr_dtype a_dtype, int32_t method);
 
+/* inv_sqrt_root_batched: precision of the products */
+#define MR_CANS_F16 0   /* fp16 products with float32 accumulation (the OKLS page's) */
+#define MR_CANS_SPLIT 1 /* split-fp16 products: float32-accurate, three times the
+                           matrix-core work                                        */
+
+/*
+ * inv_sqrt_root_batched -- for every problem:
+ *     W = S^(-1/2),  S = (A + A^T)/2 / s + eps * I,
+ *     s = trace(A) (MR_NORM_TRACE) or 1 (MR_NORM_NONE)
+ * The inverse square root of a symmetric positive definite matrix by the
+ * scaled CANS coupled Newton-Schulz iteration of tilderesearch, "Online KL
+ * Shampoo", sections 2.3-2.4 and appendix D: L = 1.01 times the
+ * Wolkowicz-Styan bound on lambda_max(S); from Y0 = S/L, Z0 = I, ten steps
+ *     P = Z Y,  Q = a_k I + b_k P,  Y <- Y Q,  Z <- Q Z
+ * with the page's ten CANS coefficient pairs; W = Z_10 / sqrt(L).  Every
+ * intermediate is stored in fp16 (plus a second fp16 half holding its
+ * float32 rounding remainder) times a power of two fixed per step by the
+ * scalar recurrence, so that no entry exceeds 2^14 (the page's per-step
+ * range scaling).  P is a full product; Y Q = Y Z Y and Q Z = Z Y Z are
+ * computed as symmetric (upper-triangle) products.  27 products in 19
+ * launches for the whole batch; no host synchronisation.
+ * Accuracy: the composed CANS map reaches (lambda/L)^(-1/2) to 3e-5 for
+ * lambda/L in [1e-6, 1] and fails far below; with MR_CANS_F16 the fp16
+ * rounding of S itself limits the relative error to a few 1e-3 for
+ * condition numbers up to 1e3, and to about 1e-2 on eigenvalues near L,
+ * where the first step cancels (fp16-grade, as on the page); MR_CANS_SPLIT
+ * reaches about 1e-4 up to 1e4.  W is symmetric to the last bit.
+ * a_dtype: MR_F32 or MR_F64.  eps >= 0 and finite.  precision: MR_CANS_F16
+ * or MR_CANS_SPLIT.  info_dev: device array of `count` records (may be
+ * NULL): scale = s, bound = L, iters = 10, fp64_iters = 0, residual =
+ * ||P_9 - I||_F (the last coupled product, which the final step maps to I);
+ * flags: NONFINITE (W all NaN), ZERO_TRACE (W = eps^(-1/2) I; with eps = 0
+ * also NOT_PD and W all NaN), NOT_PD (no positive bound: W all NaN),
+ * NOT_CONVERGED (residual above 0.1 * sqrt(d): S not positive definite, or
+ * eigenvalues below the map's reach).
+ * Workspace: at least inv_sqrt_root_batched_workspace(...) bytes (24 d^2
+ * bytes per matrix plus per-matrix state), 256-byte aligned; contents on
+ * entry ignored.  Errors as for inv_quarter_root_batched; nothing is
+ * enqueued on a validation failure.
+ */
+mr_status inv_sqrt_root_batched(const mr_root_problem* problems, int32_t count, mr_dtype a_dtype,
+                                double eps, int32_t normalize, int32_t precision,
+                                mr_root_info* info_dev, void* ws, size_t ws_bytes, void* hip_stream);
+size_t inv_sqrt_root_batched_workspace(const mr_root_problem* problems, int32_t count,
+                                       mr_dtype a_dtype, int32_t precision);
+
+/* Suprema over y0 in (0, 1] of the CANS scalar recurrence y <- y q, z <- z q,
+ * q = a_k + b_k z y (y, z from y0, 1), at steps k = 0..10: the per-step
+ * bounds inv_sqrt_root_batched scales its intermediates by (y: Y_k, z: Z_k,
+ * p: P_k = Z_k Y_k).  Writes min(11, capacity) values to each non-NULL
+ * array and returns 11.  Host-only. */
+int32_t mr_cans_ceilings(double* y, double* z, double* p, int32_t capacity);
+
 /*
  * precondition_apply -- for every problem:  U = alpha * XL * G * XR
  * The two-sided application of the quarter powers (EMA-Gram page, section

@@ -22,16 +22,21 @@ MR_LEFT, MR_RIGHT = 1, 2
 MR_NORM_NONE, MR_NORM_TRACE = 0, 1
 MR_AUTO, MR_JACOBI, MR_NEWTON, MR_NEWTON_F64, MR_NEWTON_F32 = 0, 1, 2, 3, 4
 MR_INFO_NONFINITE, MR_INFO_ZERO_TRACE, MR_INFO_NOT_PD, MR_INFO_NOT_CONVERGED = 1, 2, 4, 8
+MR_CANS_F16, MR_CANS_SPLIT = 0, 1
 
 _METHODS = {"auto": MR_AUTO, "jacobi": MR_JACOBI, "newton": MR_NEWTON, "newton_f64": MR_NEWTON_F64,
             "newton_f32": MR_NEWTON_F32}
 _NORMS = {"none": MR_NORM_NONE, "trace": MR_NORM_TRACE}
+_PRECISIONS = {"f16": MR_CANS_F16, "split": MR_CANS_SPLIT}
 
 EXPORTED = (
     "gram_ema_update",
     "gram_ema_update_workspace",
     "inv_quarter_root_batched",
     "inv_quarter_root_batched_workspace",
+    "inv_sqrt_root_batched",
+    "inv_sqrt_root_batched_workspace",
+    "mr_cans_ceilings",
     "precondition_apply",
     "precondition_apply_workspace",
     "mr_newton_iterations",
@@ -96,6 +101,12 @@ def library() -> ctypes.CDLL:
     lib.inv_quarter_root_batched.restype = i32
     lib.inv_quarter_root_batched_workspace.argtypes = [vp, i32, i32, i32]
     lib.inv_quarter_root_batched_workspace.restype = sz
+    lib.inv_sqrt_root_batched.argtypes = [vp, i32, i32, f64, i32, i32, vp, vp, sz, vp]
+    lib.inv_sqrt_root_batched.restype = i32
+    lib.inv_sqrt_root_batched_workspace.argtypes = [vp, i32, i32, i32]
+    lib.inv_sqrt_root_batched_workspace.restype = sz
+    lib.mr_cans_ceilings.argtypes = [vp, vp, vp, i32]
+    lib.mr_cans_ceilings.restype = i32
     lib.precondition_apply.argtypes = [vp, i32, f32, vp, sz, vp]
     lib.precondition_apply.restype = i32
     lib.precondition_apply_workspace.argtypes = [vp, i32]
@@ -236,6 +247,57 @@ def inv_quarter_root_batched(As: Sequence, eps: float, normalize: str = "trace",
         return Xs, None
     torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
     return Xs, decode_info(info, count)
+
+
+def _root_call(entry, size_entry, code, As, eps, normalize, Xs, workspace, stream, return_info, info_out):
+    import torch
+
+    lib = library()
+    count = len(As)
+    if count == 0:
+        return [], None
+    dts = {str(a.dtype) for a in As}
+    if len(dts) != 1:
+        raise ValueError("all A must share one dtype")
+    dt = MR_F64 if dts.pop() == "torch.float64" else MR_F32
+    dev = As[0].device
+    if Xs is None:
+        Xs = [torch.empty(a.shape[0], a.shape[0], dtype=torch.float32, device=dev) for a in As]
+    probs = (RootProblem * count)()
+    for i, (A, X) in enumerate(zip(As, Xs)):
+        probs[i] = RootProblem(A.shape[0], _ptr(A), _ld(A), _ptr(X), _ld(X))
+    need = size_entry(ctypes.addressof(probs), count, dt, code)
+    ws = workspace or RootWorkspace()
+    buf, info = ws.get(need, count, dev)
+    if info_out is not None:
+        if info_out.numel() < 32 * count:
+            raise ValueError("info_out too small")
+        info = info_out
+    _check(entry(ctypes.addressof(probs), count, dt, float(eps), _NORMS[normalize], code, _ptr(info), _ptr(buf),
+                 buf.numel(), _stream(stream)))
+    if not return_info:
+        return Xs, None
+    torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+    return Xs, decode_info(info, count)
+
+
+def inv_sqrt_root_batched(As: Sequence, eps: float = 0.0, normalize: str = "none", precision: str = "f16",
+                          Xs: Optional[Sequence] = None, workspace: Optional[RootWorkspace] = None,
+                          stream=None, return_info: bool = True, info_out=None):
+    """W_i = (sym(A_i)/s_i + eps I)^(-1/2) by the scaled CANS coupled
+    Newton-Schulz iteration; precision "f16" (fp16 products) or "split"
+    (float32-accurate split-fp16 products).  Returns (Ws, info) like
+    inv_quarter_root_batched."""
+    lib = library()
+    return _root_call(lib.inv_sqrt_root_batched, lib.inv_sqrt_root_batched_workspace, _PRECISIONS[precision], As,
+                      eps, normalize, Xs, workspace, stream, return_info, info_out)
+
+
+def cans_ceilings():
+    """(y, z, p) suprema of the CANS scalar recurrence at steps 0..10."""
+    arrs = [(ctypes.c_double * 11)() for _ in range(3)]
+    n = library().mr_cans_ceilings(*[ctypes.addressof(a) for a in arrs], 11)
+    return tuple([a[i] for i in range(n)] for a in arrs)
 
 
 def decode_info(info, count: int):

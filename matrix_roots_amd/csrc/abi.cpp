@@ -15,6 +15,7 @@
 #include <string>
 #include <vector>
 
+#include "cans.hpp"
 #include "launch.hpp"
 #include "schedule.hpp"
 
@@ -76,11 +77,13 @@ int tiles(int64_t d, int t) { return (int)((d + t - 1) / t); }
 // ------------------------------------------------------------ tracing
 enum TraceClass {
   kTrSyrk, kTrApply, kTrJacobi, kTrStats, kTrBound, kTrInit, kTrNewton64, kTrNewton32, kTrConvert,
-  kTrFinalize, kTrInfo, kTrNewtonX3, kTrCount
+  kTrFinalize, kTrInfo, kTrNewtonX3, kTrCansBound, kTrCansInit, kTrCansP, kTrCansYZ, kTrCansFinal, kTrCansInfo,
+  kTrCount
 };
 const char* const kTraceNames[kTrCount] = {"syrk_ema", "apply_f32", "jacobi", "root_stats", "root_bound",
                                            "root_init", "newton_f64", "newton_f32", "newton_convert",
-                                           "root_finalize", "root_info", "newton_x3"};
+                                           "root_finalize", "root_info", "newton_x3", "cans_bound",
+                                           "cans_init", "cans_p", "cans_yz", "cans_finalize", "cans_info"};
 struct TraceEntry {
   int cls;
   hipEvent_t a, b;
@@ -450,6 +453,21 @@ mr_status precondition_apply(const mr_apply_problem* p, int32_t count, float alp
 }
 
 // ================================================ inv_quarter_root_batched
+static mr_status validate_root_problems(const mr_root_problem* p, int32_t count, mr_dtype dt) {
+  const size_t es = dt == MR_F64 ? 8 : 4;
+  for (int i = 0; i < count; ++i) {
+    const mr_root_problem& q = p[i];
+    if (q.d < 1 || q.d > kMaxDim)
+      return fail(MR_ERR_SHAPE, "problem %d: d=%lld outside [1, %lld]", i, (long long)q.d, (long long)kMaxDim);
+    if (!q.A || !q.X) return fail(MR_ERR_NULL, "problem %d: A or X is NULL", i);
+    if (q.lda < q.d || q.ldx < q.d) return fail(MR_ERR_STRIDE, "problem %d: lda or ldx < d", i);
+    if (!aligned(q.A, es) || !aligned(q.X, 4)) return fail(MR_ERR_PARAM, "problem %d: A or X misaligned", i);
+    if (overlap(range_of(q.A, q.d, q.d, q.lda, es), range_of(q.X, q.d, q.d, q.ldx, 4)))
+      return fail(MR_ERR_ALIAS, "problem %d: X overlaps A", i);
+  }
+  return MR_OK;
+}
+
 static mr_status validate_root(const mr_root_problem* p, int32_t count, mr_dtype dt, double eps, int32_t normalize,
                                int32_t method) {
   if (count < 0) return fail(MR_ERR_PARAM, "count %d < 0", count);
@@ -461,20 +479,12 @@ static mr_status validate_root(const mr_root_problem* p, int32_t count, mr_dtype
   if (method != MR_AUTO && method != MR_JACOBI && method != MR_NEWTON && method != MR_NEWTON_F64 &&
       method != MR_NEWTON_F32)
     return fail(MR_ERR_PARAM, "method %d unknown", method);
-  const size_t es = dt == MR_F64 ? 8 : 4;
-  for (int i = 0; i < count; ++i) {
-    const mr_root_problem& q = p[i];
-    if (q.d < 1 || q.d > kMaxDim)
-      return fail(MR_ERR_SHAPE, "problem %d: d=%lld outside [1, %lld]", i, (long long)q.d, (long long)kMaxDim);
-    if (!q.A || !q.X) return fail(MR_ERR_NULL, "problem %d: A or X is NULL", i);
-    if (q.lda < q.d || q.ldx < q.d) return fail(MR_ERR_STRIDE, "problem %d: lda or ldx < d", i);
-    if (!aligned(q.A, es) || !aligned(q.X, 4)) return fail(MR_ERR_PARAM, "problem %d: A or X misaligned", i);
-    if (overlap(range_of(q.A, q.d, q.d, q.lda, es), range_of(q.X, q.d, q.d, q.ldx, 4)))
-      return fail(MR_ERR_ALIAS, "problem %d: X overlaps A", i);
-    if (method == MR_JACOBI && q.d > kJacobiMaxD)
+  mr_status st = validate_root_problems(p, count, dt);
+  if (st != MR_OK) return st;
+  for (int i = 0; i < count; ++i)
+    if (method == MR_JACOBI && p[i].d > kJacobiMaxD)
       return fail(MR_ERR_UNSUPPORTED, "problem %d: MR_JACOBI supports d <= %d (d = %lld)", i, kJacobiMaxD,
-                  (long long)q.d);
-  }
+                  (long long)p[i].d);
   return MR_OK;
 }
 
@@ -710,6 +720,226 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
 
   return traced(kTrInfo, true, s, [&] { return launch_root_info(state, partial, P.partial_stride, count, info_dev, s); },
                 "root info");
+}
+
+}  // extern "C"
+
+// ================================================ inv_sqrt_root_batched
+namespace {
+
+const CansCeilings& cans_ceilings() {
+  static const CansCeilings c = cans_ceilings_compute();
+  return c;
+}
+const CansScales& cans_scales() {
+  static const CansScales s = cans_scales_from(cans_ceilings());
+  return s;
+}
+
+struct CansPlan {
+  std::vector<int> slot_problem;  // slots grouped by d, ascending
+  std::vector<RootPlan::Cls> classes;
+  size_t state_off = 0, partial_off = 0, total = 0;
+  int64_t partial_stride = 0;
+};
+
+CansPlan plan_cans(const mr_root_problem* p, int32_t count) {
+  CansPlan P;
+  std::map<int64_t, std::vector<int>> by_d;
+  for (int i = 0; i < count; ++i) by_d[p[i].d].push_back(i);
+  int64_t dmax = 1;
+  for (auto& kv : by_d) {
+    RootPlan::Cls c;
+    c.d = kv.first;
+    c.first_slot = (int)P.slot_problem.size();
+    c.count = (int)kv.second.size();
+    c.matrix_bytes = align256((size_t)cans_matrix_bytes(c.d));
+    for (int i : kv.second) P.slot_problem.push_back(i);
+    P.classes.push_back(c);
+    dmax = std::max(dmax, c.d);
+  }
+  size_t off = 0;
+  P.state_off = off;
+  off = align256(off + sizeof(RootState) * (size_t)std::max(count, 1));
+  P.partial_stride = 3 * ((dmax + kStatsRows - 1) / kStatsRows);
+  P.partial_off = off;
+  off = align256(off + sizeof(double) * (size_t)P.partial_stride * (size_t)std::max(count, 1));
+  for (auto& c : P.classes) {
+    c.region_off = off;
+    off += c.matrix_bytes * (size_t)c.count;
+  }
+  P.total = off;
+  return P;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mr_cans_ceilings(double* y, double* z, double* p, int32_t capacity) {
+  const CansCeilings& c = cans_ceilings();
+  const int n = std::min(std::max(capacity, 0), kCansSteps + 1);
+  for (int k = 0; k < n; ++k) {
+    if (y) y[k] = c.y[k];
+    if (z) z[k] = c.z[k];
+    if (p) p[k] = c.p[k];
+  }
+  return kCansSteps + 1;
+}
+
+size_t inv_sqrt_root_batched_workspace(const mr_root_problem* p, int32_t count, mr_dtype, int32_t) {
+  if (!p || count <= 0) return 0;
+  for (int i = 0; i < count; ++i)
+    if (p[i].d < 1 || p[i].d > kMaxDim) return 0;
+  return plan_cans(p, count).total;
+}
+
+mr_status inv_sqrt_root_batched(const mr_root_problem* p, int32_t count, mr_dtype dt, double eps, int32_t normalize,
+                                int32_t precision, mr_root_info* info_dev, void* ws, size_t ws_bytes,
+                                void* hip_stream) {
+  if (count < 0) return fail(MR_ERR_PARAM, "count %d < 0", count);
+  if (count > 0 && !p) return fail(MR_ERR_NULL, "problems is NULL");
+  if (dt != MR_F32 && dt != MR_F64) return fail(MR_ERR_PARAM, "a_dtype %d is not MR_F32 or MR_F64", dt);
+  if (!(eps >= 0.0) || !std::isfinite(eps)) return fail(MR_ERR_PARAM, "eps %g must be >= 0 and finite", eps);
+  if (normalize != MR_NORM_NONE && normalize != MR_NORM_TRACE)
+    return fail(MR_ERR_PARAM, "normalize %d is not MR_NORM_NONE or MR_NORM_TRACE", normalize);
+  if (precision != MR_CANS_F16 && precision != MR_CANS_SPLIT)
+    return fail(MR_ERR_PARAM, "precision %d is not MR_CANS_F16 or MR_CANS_SPLIT", precision);
+  mr_status st = validate_root_problems(p, count, dt);
+  if (st != MR_OK) return st;
+  if (count == 0) return MR_OK;
+  const CansPlan P = plan_cans(p, count);
+  if (!ws || ws_bytes < P.total || !aligned(ws, 256))
+    return fail(MR_ERR_WORKSPACE, "workspace %p of %zu bytes; need %zu bytes, 256-byte aligned", ws, ws_bytes,
+                P.total);
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  char* base = static_cast<char*>(ws);
+  RootState* state = reinterpret_cast<RootState*>(base + P.state_off);
+  double* partial = reinterpret_cast<double*>(base + P.partial_off);
+  const CansScales& sc = cans_scales();
+  const int prec = precision == MR_CANS_SPLIT ? 3 : 1;
+
+  // per-matrix batches: 0 statistics, 1 init, 2 finalize
+  auto run_batches = [&](int kind) -> mr_status {
+    RootBatch b;
+    memset(&b, 0, sizeof b);
+    b.a_f64 = dt == MR_F64;
+    b.normalize = normalize;
+    b.eps = eps;
+    b.state = state;
+    b.partial = partial;
+    b.partial_stride = P.partial_stride;
+    for (const auto& c : P.classes) {
+      for (int k = 0; k < c.count; ++k) {
+        const int slot = c.first_slot + k;
+        const mr_root_problem& q = p[P.slot_problem[slot]];
+        RootJob& J = b.job[b.njobs];
+        J.A = q.A;
+        J.lda = q.lda;
+        J.X = q.X;
+        J.ldx = q.ldx;
+        J.region = base + c.region_off + c.matrix_bytes * (size_t)k;
+        J.d = (int32_t)q.d;
+        J.slot = slot;
+        J.problem = P.slot_problem[slot];
+        J.block_begin = b.total_blocks;
+        J.nblocks = kind == 0 ? tiles(q.d, kStatsRows) : kind == 1 ? tiles(q.d, 32) * tiles(q.d, 32)
+                                                                   : tiles(q.d, kFinalRows);
+        b.total_blocks += J.nblocks;
+        ++b.njobs;
+        if (b.njobs == kMaxJobs || slot == count - 1) {
+          const int cls = kind == 0 ? kTrStats : kind == 1 ? kTrCansInit : kTrCansFinal;
+          mr_status r = traced(cls, b.total_blocks > 0, s, [&] {
+            if (kind == 0) return launch_root_stats(b, s);
+            if (kind == 1)
+              return launch_cans_init(b, sc.sy[0], sc.sz[1] * kCansCoeff[0][0], sc.sz[1] * kCansCoeff[0][1], s);
+            return launch_cans_finalize(b, 1.0 / sc.sp[kCansSteps - 1], s);
+          }, "cans batch launch");
+          if (r != MR_OK) return r;
+          b.njobs = 0;
+          b.total_blocks = 0;
+        }
+      }
+    }
+    return MR_OK;
+  };
+
+  if ((st = run_batches(0)) != MR_OK) return st;
+  if ((st = traced(kTrCansBound, true, s, [&] {
+         return launch_cans_bound(state, partial, P.partial_stride, count, normalize, eps, sc.sz[kCansSteps], s);
+       }, "cans bound launch")) != MR_OK)
+    return st;
+  if ((st = run_batches(1)) != MR_OK) return st;
+
+  // size-class groups: at most kMaxClasses per launch, split by fp16 vector width
+  struct Group {
+    std::vector<int> cls;
+    int vec;
+  };
+  std::vector<Group> groups;
+  for (const int vec : {8, 1}) {
+    Group g;
+    g.vec = vec;
+    for (int ci = 0; ci < (int)P.classes.size(); ++ci) {
+      if ((P.classes[ci].d % 8 == 0 ? 8 : 1) != vec) continue;
+      g.cls.push_back(ci);
+      if ((int)g.cls.size() == kMaxClasses) {
+        groups.push_back(g);
+        g.cls.clear();
+      }
+    }
+    if (!g.cls.empty()) groups.push_back(g);
+  }
+  auto launch_stage = [&](int stage, int k, double a0, double b0, double a1, double b1) -> mr_status {
+    for (const auto& g : groups) {
+      CansLaunch L;
+      memset(&L, 0, sizeof L);
+      L.state = state;
+      L.stage = stage;
+      L.k = k;
+      L.alpha[0] = a0;
+      L.beta[0] = b0;
+      L.alpha[1] = a1;
+      L.beta[1] = b1;
+      for (int ci : g.cls) {
+        const auto& c = P.classes[ci];
+        CansClass& C = L.cls[L.ncls++];
+        C.region = base + c.region_off;
+        C.matrix_bytes = (int64_t)c.matrix_bytes;
+        C.d = (int32_t)c.d;
+        C.count = c.count;
+        C.T = tiles(c.d, 128);
+        C.U = C.T * (C.T + 1) / 2;
+        C.slot_begin = c.first_slot;
+        C.block_begin = L.total_blocks;
+        C.blocks_per_matrix = stage == kCansP ? C.T * C.T : stage == kCansYZ ? 2 * C.U : C.U;
+        C.nblocks = C.blocks_per_matrix * C.count;
+        L.total_blocks += round8(C.nblocks);
+      }
+      const int cls = stage == kCansP ? kTrCansP : kTrCansYZ;
+      mr_status r = traced(cls, true, s, [&] { return launch_cans_gemm(L, g.vec, prec, s); }, "cans gemm launch");
+      if (r != MR_OK) return r;
+    }
+    return MR_OK;
+  };
+  // k = 0: P_0 = Y_0, so Z_1 = Q_0 (written by the init) and Y_1 = a0 Y0 + b0 Y0^2
+  {
+    const double a = kCansCoeff[0][0], b = kCansCoeff[0][1];
+    if ((st = launch_stage(kCansY1, 0, b * sc.sy[1] / (sc.sy[0] * sc.sy[0]), a * sc.sy[1] / sc.sy[0], 0.0, 0.0)) !=
+        MR_OK)
+      return st;
+  }
+  for (int k = 1; k < kCansSteps; ++k) {
+    const double a = kCansCoeff[k][0], b = kCansCoeff[k][1];
+    if ((st = launch_stage(kCansP, k, sc.sp[k] / (sc.sz[k] * sc.sy[k]), 0.0, 0.0, 0.0)) != MR_OK) return st;
+    const double ay = b * sc.sy[k + 1] / (sc.sy[k] * sc.sp[k]), by = a * sc.sy[k + 1] / sc.sy[k];
+    const double az = b * sc.sz[k + 1] / (sc.sz[k] * sc.sp[k]), bz = a * sc.sz[k + 1] / sc.sz[k];
+    if ((st = launch_stage(k + 1 < kCansSteps ? kCansYZ : kCansZ, k, ay, by, az, bz)) != MR_OK) return st;
+  }
+  if ((st = run_batches(2)) != MR_OK) return st;
+  return traced(kTrCansInfo, true, s, [&] {
+    return launch_cans_info(state, partial, P.partial_stride, count, info_dev, kCansResidualRms, s);
+  }, "cans info");
 }
 
 }  // extern "C"

@@ -184,3 +184,42 @@ def test_newton_schedule_monotone_in_floor(lib):
         prev = K
     # the scaled schedule beats the classical count (same tolerance)
     assert len(B.newton_schedule(1e-6)[0]) < lib.mr_newton_iterations(4, 1e-6, 1e-6)
+
+
+def call_sqrt(lib, probs, dt=B.MR_F32, eps=0.0, norm=0, prec=0, ws=None, ws_bytes=0):
+    arr = (B.RootProblem * len(probs))(*probs)
+    return lib.inv_sqrt_root_batched(ctypes.addressof(arr), len(probs), dt, eps, norm, prec, None, ws, ws_bytes,
+                                     None)
+
+
+def test_sqrt_root_validation(lib):
+    assert call_sqrt(lib, [root(8)], eps=-1e-3) == 4
+    assert call_sqrt(lib, [root(8)], eps=float("nan")) == 4
+    assert call_sqrt(lib, [root(8)], norm=2) == 4
+    assert call_sqrt(lib, [root(8)], prec=2) == 4
+    assert call_sqrt(lib, [root(8)], dt=3) == 4
+    assert call_sqrt(lib, [root(0)]) == 2
+    assert call_sqrt(lib, [root(8, X=0)]) == 1
+    assert call_sqrt(lib, [root(8, lda=7)]) == 3
+    assert call_sqrt(lib, [root(8, X=P1 + 64)]) == 8
+    arr = (B.RootProblem * 0)()
+    assert lib.inv_sqrt_root_batched(ctypes.addressof(arr), 0, 0, 0.0, 0, 0, None, None, 0, None) == 0
+    # eps = 0 is valid here (the page's S^(-1/2)); no workspace: rejected before any launch
+    assert call_sqrt(lib, [root(200)]) == 5
+    probs = (B.RootProblem * 2)(root(64), root(300, A=P3, X=P4))
+    need = lib.inv_sqrt_root_batched_workspace(ctypes.addressof(probs), 2, B.MR_F32, 0)
+    assert need >= 24 * (300 * 300 + 64 * 64)
+    assert call_sqrt(lib, [root(64), root(300, A=P3, X=P4)], ws=P5, ws_bytes=need - 1) == 5
+    assert call_sqrt(lib, [root(64), root(300, A=P3, X=P4)], ws=P5 + 8, ws_bytes=need) == 5
+
+
+def test_cans_ceilings_match_okls_page():
+    """The library's step bounds (from which its fp16 scales follow) against
+    the ceilings the OKLS page prints for its coefficient table."""
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "okls_cans_table.json")))
+    y, z, p = B.cans_ceilings()
+    assert len(y) == len(z) == len(p) == g["steps"] + 1
+    for k in range(g["steps"] + 1):
+        assert z[k] == pytest.approx(g["z_ceilings"][k], rel=2e-4), k
+        assert p[k] == pytest.approx(g["p_ceilings"][k], rel=1e-2), k
+        assert y[k] <= g["y_ceilings"][k] * 1.005, k
