@@ -134,7 +134,112 @@ def per_size_class(B, torch, grams, wl):
     return out
 
 
-def recorded_traffic(kernel: str, workload: str):
+CANS_METRIC = "inverse square roots/s (scaled CANS coupled Newton-Schulz, S^-1/2 of SPD 8192x8192, batch 4)"
+
+
+def bench_cans(args, torch, B):
+    """The OKLS page's root benchmark shape (section 2.4, figure 4): one
+    inv_sqrt_root_batched call on 4 SPD matrices of 8192 x 8192 (float32,
+    S = G G^T / 8192 + eps I with G Gaussian: condition number about 1e3),
+    timed per call with the library's HIP events around each launch."""
+    d, batch, eps = 8192, 4, 4e-3
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(8192)
+    As = []
+    for _ in range(batch):
+        G = torch.randn(d, d, generator=gen, device=dev, dtype=torch.float32)
+        As.append(G @ G.T.contiguous() / d)
+    del G
+    Ws = [torch.empty(d, d, dtype=torch.float32, device=dev) for _ in As]
+    ws = B.RootWorkspace()
+    infos = torch.empty(32 * batch, dtype=torch.uint8, device=dev)
+
+    def step():
+        B.inv_sqrt_root_batched(As, eps, normalize="none", precision=args.precision, Xs=Ws, workspace=ws,
+                                return_info=False, info_out=infos)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup call {i + 1}/{args.warmup} done")
+    B.trace_collect()
+    B.trace_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    B.trace_enable(False)
+    trace = B.trace_collect()
+    info = B.decode_info(infos, batch)
+    assert (info["flags"] == 0).all(), info
+    ms = (t1 - t0) * 1e3 / args.steps
+    g = sym_gemm_flops(d)
+    # 27 products, all symmetric in exact arithmetic: 9 P products (cans_p), 18 Y/Z products (cans_yz)
+    flops = {"cans_p": 9 * g * batch * args.steps, "cans_yz": 18 * g * batch * args.steps}
+    prec = "f16"
+    kernels = {}
+    for name, (launches, kms) in sorted(trace.items()):
+        ent = {"launches": launches, "ms_total": round(kms, 3), "ms_avg": round(kms / launches, 4)}
+        if name in flops:
+            tf = flops[name] / (kms / 1e3) / 1e12
+            mult = 3 if args.precision == "split" else 1
+            ent.update({"tflops": round(tf, 2), "mfma_tflops": round(mult * tf, 2), "peak": PEAK_TFLOPS[prec],
+                        "frac": round(mult * tf / PEAK_TFLOPS[prec], 4)})
+        kernels[name] = ent
+    dname, dk = max(((k, v) for k, v in kernels.items() if k in flops), key=lambda kv: kv[1]["ms_total"])
+    roofline = {"bound": "mfma", "kernel": dname, "achieved": dk["mfma_tflops"], "peak": dk["peak"],
+                "unit": "TFLOP/s", "frac": dk["frac"],
+                "traffic": recorded_traffic(dname, f"cans8192_{args.precision}", "cans"),
+                "achieved_per_launch": "algorithmic fp16 MFMA flops of the class (symmetric-product count; "
+                                       "x3 for split products) / sum of its event-measured launch durations"}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        import numpy as np
+
+        log("timing the fp64 oracle on one 8192 x 8192 root")
+        A0 = As[0].double().cpu().numpy()
+        try:
+            import threadpoolctl
+
+            cores = max(int(i.get("num_threads", 1)) for i in threadpoolctl.threadpool_info()) or 1
+        except Exception:  # pragma: no cover
+            cores = len(os.sched_getaffinity(0))
+        c0 = time.perf_counter()
+        oracle.inv_sqrt_root(A0, eps, "none")
+        sec = time.perf_counter() - c0
+        cpu = {"value": round(1.0 / sec, 5), "unit": "roots/s", "cores": cores, "kind": "oracle",
+               "sample": "one 8192 x 8192 root of the batch (eigh, fp64 numpy/LAPACK)", "seconds": round(sec, 2)}
+        log(f"oracle: {sec:.1f}s per root on {cores} threads")
+    out = {
+        "metric": CANS_METRIC,
+        "value": round(batch / (ms / 1e3), 4),
+        "unit": "roots/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 products, f32 accumulation" if args.precision == "f16" else "split-f16 products (f32-accurate)",
+        "data": "synthetic",
+        "config": {"workload": "cans8192", "d": d, "batch": batch, "eps": eps, "normalize": "none",
+                   "precision": args.precision, "steps_per_root": 10, "products_per_root": 27},
+        "tflops": round((flops["cans_p"] + flops["cans_yz"]) / args.steps / (ms / 1e3) / 1e12, 2),
+        "roofline": roofline,
+        "kernels": kernels,
+        "residual_max": float(info["residual"].max()),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def recorded_traffic(kernel: str, workload: str, family: str = "quarter"):
     """HBM bytes per launch of `kernel` from the committed counter summary,
     if the kernel sources are unchanged since the counters were taken."""
     from matrix_roots_amd import profile_summary
@@ -147,7 +252,7 @@ def recorded_traffic(kernel: str, workload: str):
         if ":" in line and line.split(":", 1)[0].strip() in ("traffic_bytes_per_launch", "source_sha256"):
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip().strip("`")
-    if rec.get("source_sha256") != profile_summary.sources_sha256():
+    if rec.get("source_sha256") != profile_summary.sources_sha256(family):
         return None
     try:
         return float(rec["traffic_bytes_per_launch"])
@@ -155,12 +260,23 @@ def recorded_traffic(kernel: str, workload: str):
         return None
 
 
+def calibration_copies(torch, dev, mib):
+    src = torch.ones(mib * 2 ** 18, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"calibration copies of {mib} MiB done")
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="w1024", choices=["toy", "w1024", "w2048", "moe"])
+    ap.add_argument("--workload", default="w1024", choices=["toy", "w1024", "w2048", "moe", "cans8192"])
+    ap.add_argument("--precision", default="f16", choices=["f16", "split"],
+                    help="products of the cans8192 workload (inv_sqrt_root_batched)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--state-dtype", default="f64", choices=["f64", "f32"])
     ap.add_argument("--gradients", default="auto", choices=["auto", "host", "device"],
@@ -187,14 +303,12 @@ def main(argv=None) -> int:
         return 2
     B.library()
     dev = torch.device("cuda:0")
+    if args.workload == "cans8192":
+        if args.calibration_copy_mib > 0:
+            calibration_copies(torch, dev, args.calibration_copy_mib)
+        return bench_cans(args, torch, B)
     if args.calibration_copy_mib > 0:
-        src = torch.ones(args.calibration_copy_mib * 2 ** 18, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        log(f"calibration copies of {args.calibration_copy_mib} MiB done")
+        calibration_copies(torch, dev, args.calibration_copy_mib)
     wl = W.WORKLOADS[args.workload]
     shapes = [(m, n) for _, m, n in wl.shapes]
     nw = len(shapes)

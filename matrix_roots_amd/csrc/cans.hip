@@ -172,8 +172,9 @@ __global__ __launch_bounds__(256) void cans_init_kernel(const RootBatch B, doubl
 
 // One launch stage of the iteration for every matrix of up to kMaxClasses
 // size classes; workgroup -> (class, matrix, job, tile) through the per-class
-// XCD remap.  PREC 1: fp16 products; PREC 3: split products.
-template <int VEC, int PREC>
+// XCD remap.  PREC 1: fp16 products; PREC 3: split products.  FULL: the P
+// stage (every tile, stored with its transpose); else the symmetric stages.
+template <int VEC, int PREC, bool FULL>
 __global__ __launch_bounds__(256, 2) void cans_gemm_kernel(const CansLaunch L) {
   __shared__ _Float16 smem[PREC == 3 ? X3Tile::LDS_HALVES : H16Tile::LDS_HALVES];
   const int64_t b = blockIdx.x;
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(256, 2) void cans_gemm_kernel(const CansLaunch L) {
   const int d = C.d;
   char* region = C.region + (int64_t)mat * C.matrix_bytes;
   const int k = L.k;
-  const bool full = L.stage == kCansP;
+  constexpr bool full = FULL;
   int job = 0, ti, tj;
   if (full) {
     ti = rem / C.T;
@@ -358,17 +359,26 @@ hipError_t launch_cans_init(const RootBatch& b, double sy0, double za, double zb
 hipError_t launch_cans_gemm(const CansLaunch& L, int vec, int prec, hipStream_t s) {
   if (L.total_blocks <= 0) return hipSuccess;
   const dim3 g(L.total_blocks), t(256);
+  const bool full = L.stage == kCansP;
+#define MR_CANS_LAUNCH(V, P)                                                    \
+  do {                                                                          \
+    if (full)                                                                   \
+      hipLaunchKernelGGL((cans_gemm_kernel<V, P, true>), g, t, 0, s, L);       \
+    else                                                                        \
+      hipLaunchKernelGGL((cans_gemm_kernel<V, P, false>), g, t, 0, s, L);      \
+  } while (0)
   if (prec == 3) {
     if (vec == 8)
-      hipLaunchKernelGGL((cans_gemm_kernel<8, 3>), g, t, 0, s, L);
+      MR_CANS_LAUNCH(8, 3);
     else
-      hipLaunchKernelGGL((cans_gemm_kernel<1, 3>), g, t, 0, s, L);
+      MR_CANS_LAUNCH(1, 3);
   } else {
     if (vec == 8)
-      hipLaunchKernelGGL((cans_gemm_kernel<8, 1>), g, t, 0, s, L);
+      MR_CANS_LAUNCH(8, 1);
     else
-      hipLaunchKernelGGL((cans_gemm_kernel<1, 1>), g, t, 0, s, L);
+      MR_CANS_LAUNCH(1, 1);
   }
+#undef MR_CANS_LAUNCH
   return hipGetLastError();
 }
 

@@ -25,13 +25,18 @@ import os
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("csrc/gemm_core.hpp", "csrc/mr_common.hpp", "csrc/launch.hpp", "csrc/schedule.hpp",
-                  "csrc/root.hip", "csrc/gram.hip", "csrc/apply.hip")
+# Sources whose kernels a counter record covers, per kernel family.
+KERNEL_SOURCES = {
+    "quarter": ("csrc/gemm_core.hpp", "csrc/mr_common.hpp", "csrc/launch.hpp", "csrc/schedule.hpp",
+                "csrc/root.hip", "csrc/gram.hip", "csrc/apply.hip"),
+    "cans": ("csrc/gemm_core.hpp", "csrc/gemm_h16.hpp", "csrc/mr_common.hpp", "csrc/launch.hpp", "csrc/cans.hpp",
+             "csrc/cans.hip"),
+}
 
 
-def sources_sha256() -> str:
+def sources_sha256(family: str = "quarter") -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[family]:
         with open(os.path.join(HERE, rel), "rb") as f:
             h.update(rel.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -83,6 +88,7 @@ def main(argv=None) -> int:
     ap.add_argument("--write", required=True)
     ap.add_argument("--kernel", required=True)
     ap.add_argument("--copy-mib", type=float, required=True)
+    ap.add_argument("--family", default="quarter", choices=sorted(KERNEL_SOURCES))
     args = ap.parse_args(argv)
     res = summarise(args.fetch, args.write, args.kernel, args.copy_mib)
     f, w = res["FETCH_SIZE"], res["WRITE_SIZE"]
@@ -92,7 +98,8 @@ def main(argv=None) -> int:
         print(f"{name}: mean {r['mean_kib']:.1f} KiB/dispatch; calibration copy of {args.copy_mib:g} MiB "
               f"read {r['copy_kib']:.1f} KiB -> scale {r['scale']:.4f}; {r['bytes_per_dispatch']:.4e} B/dispatch")
     print(f"traffic_bytes_per_launch: {f['bytes_per_dispatch'] + w['bytes_per_dispatch']:.6e}")
-    print(f"source_sha256: {sources_sha256()}")
+    print(f"source_family: {args.family}")
+    print(f"source_sha256: {sources_sha256(args.family)}")
     return 0
 
 

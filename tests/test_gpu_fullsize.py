@@ -170,3 +170,40 @@ def test_illcond_full(torch_dev, eps):
         assert err <= ROOT_TOL, (i, eps, err)
     print(f"illcond eps={eps:g}: worst root err {worst:.2e}, iters {info['iters'].max()}, "
           f"fp64 {info['fp64_iters'].max()}")
+
+
+def test_inv_sqrt_8192_batch4(torch_dev):
+    """The inverse square root at the OKLS page's benchmark shape (4 SPD
+    matrices of 8192 x 8192 in one call, as bench.py --workload cans8192
+    times it; S = G G^T / 8192 + 4e-3 I, condition number about 1e3), both
+    precisions: every root symmetric, finite, unflagged, with ||W S W - I||_F
+    / sqrt(d) below the small-size bound; the first against the oracle
+    (relative Frobenius error within the small-size tolerances: 2e-2 fp16,
+    1e-4 split)."""
+    torch, dev = torch_dev
+    d, eps = 8192, 4e-3
+    rng = W.rng_for(91, 0)
+    As = []
+    for _ in range(4):
+        G = rng.standard_normal((d, d), dtype=np.float32)
+        As.append((G @ G.T) / np.float32(d))
+    Ad = [torch.from_numpy(a).to(dev) for a in As]
+    ref, rinfo = oracle.inv_sqrt_root(As[0].astype(np.float64), eps, "none")
+    assert rinfo["flags"] == 0
+    eye = torch.eye(d, dtype=torch.float64, device=dev)
+    for precision, tol, res_tol in (("f16", 2e-2, 5e-2), ("split", 1e-4, 1e-3)):
+        Ws, info = B.inv_sqrt_root_batched(Ad, eps, normalize="none", precision=precision)
+        torch.cuda.synchronize()
+        assert (info["flags"] == 0).all(), info
+        worst = 0.0
+        for A, Wd in zip(Ad, Ws):
+            assert torch.equal(Wd, Wd.T) and bool(torch.isfinite(Wd).all())
+            S = 0.5 * (A.double() + A.double().T) + eps * eye
+            Wt = Wd.double()
+            r = float(torch.linalg.norm(Wt @ S @ Wt - eye)) / d ** 0.5
+            worst = max(worst, r)
+            assert r <= res_tol, (precision, r)
+        err = oracle.relative_frobenius(Ws[0].cpu().numpy(), ref)
+        print(f"8192 x4 {precision}: err {err:.2e}, residual rms {worst:.2e}")
+        assert err <= tol, (precision, err)
+        del Ws
