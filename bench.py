@@ -107,10 +107,11 @@ def per_size_class(B, torch, grams, wl):
     (final) state, timed with events on the current stream after one untimed
     call: ms, algorithmic TFLOP/s and its fraction of the fp32 MFMA peak."""
     out = {}
-    for d in sorted({int(A.shape[0]) for A in grams}):
+    dims = [B.packed_dim(A.numel()) if A.dim() == 1 else int(A.shape[0]) for A in grams]
+    for d in sorted(set(dims)):
         if d <= 128:
             continue
-        As = [A for A in grams if A.shape[0] == d]
+        As = [A for A, dd in zip(grams, dims) if dd == d]
         Xs = [torch.empty(d, d, dtype=torch.float32, device=A.device) for A in As]
         ws = B.RootWorkspace()
         B.inv_quarter_root_batched(As, wl.eps, normalize=wl.normalize, Xs=Xs, workspace=ws, return_info=False)
@@ -279,6 +280,8 @@ def main(argv=None) -> int:
                     help="products of the cans8192 workload (inv_sqrt_root_batched)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--state-dtype", default="f64", choices=["f64", "f32"])
+    ap.add_argument("--packed-state", action="store_true",
+                    help="keep the Gram states packed (upper triangle by rows, d(d+1)/2 elements)")
     ap.add_argument("--gradients", default="auto", choices=["auto", "host", "device"],
                     help="where the synthetic gradients are drawn: host = the seeded numpy draws the "
                          "parity tests use; device = same distribution drawn with torch on the GPU "
@@ -324,8 +327,14 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         log(f"  step {t} gradients resident ({time.perf_counter() - t0:.1f}s)")
     sdt = torch.float64 if args.state_dtype == "f64" else torch.float32
-    Ls = [torch.zeros(m, m, dtype=sdt, device=dev) for m, n in shapes]
-    Rs = [torch.zeros(n, n, dtype=sdt, device=dev) for m, n in shapes]
+    if args.packed_state:
+        Ls = [torch.zeros(m * (m + 1) // 2, dtype=sdt, device=dev) for m, n in shapes]
+        Rs = [torch.zeros(n * (n + 1) // 2, dtype=sdt, device=dev) for m, n in shapes]
+    else:
+        Ls = [torch.zeros(m, m, dtype=sdt, device=dev) for m, n in shapes]
+        Rs = [torch.zeros(n, n, dtype=sdt, device=dev) for m, n in shapes]
+    state_bytes = sum(x.numel() * x.element_size() for x in Ls + Rs)
+    log(f"Gram state: {state_bytes / 1e9:.2f} GB ({'packed' if args.packed_state else 'full'})")
     Xs = [torch.empty(m, m, dtype=torch.float32, device=dev) for m, n in shapes] + \
          [torch.empty(n, n, dtype=torch.float32, device=dev) for m, n in shapes]
     Us = [torch.empty(m, n, dtype=torch.float32, device=dev) for m, n in shapes]
@@ -425,7 +434,8 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": args.workload, "weights": nw, "grams_per_step": 2 * nw,
                    "shapes": sorted({f"{m}x{n}" for m, n in shapes}), "beta": wl.beta, "eps": wl.eps,
-                   "normalize": wl.normalize, "state_dtype": args.state_dtype, "gradients": gen},
+                   "normalize": wl.normalize, "state_dtype": args.state_dtype, "gradients": gen,
+                   "state_layout": "packed" if args.packed_state else "full", "state_gb": round(state_bytes / 1e9, 3)},
         "tflops": round(step_flops / (ms_per_step / 1e3) / 1e12, 2),
         "pct_fp32_mfma_peak": round(100 * step_flops / (ms_per_step / 1e3) / 1e12 / PEAK_TFLOPS["f32"], 2),
         "newton_iters": {"min": kmin, "max": kmax},

@@ -55,6 +55,14 @@ typedef int32_t mr_status;
 typedef int32_t mr_dtype;
 #define MR_F32 0
 #define MR_F64 1
+/* Storage flag OR'ed into a state or input dtype (MR_F64 | MR_PACKED):
+ * a symmetric d x d matrix kept as its upper triangle packed by rows,
+ * element (i, j) with i <= j at offset i*d - i*(i-1)/2 + (j - i), d*(d+1)/2
+ * elements in one contiguous array (the same bytes as LAPACK's lower-packed
+ * column-major layout of the matrix).  Leading dimensions of packed
+ * matrices are ignored.  Half the memory of full storage, and the Gram EMA
+ * then reads and writes each stored element once. */
+#define MR_PACKED 16
 
 /* gram_ema_update: which Grams to update (bit mask) */
 #define MR_LEFT 1
@@ -81,7 +89,7 @@ typedef int32_t mr_dtype;
 
 /* One weight for gram_ema_update.  G: m x n float32 (ldg >= n).
  * L: m x m, R: n x n, both of the call's state dtype (ldl >= m, ldr >= n),
- * full symmetric storage, updated in place.  L (R) may be NULL when the
+ * full symmetric storage (or packed with MR_PACKED), updated in place.  L (R) may be NULL when the
  * MR_LEFT (MR_RIGHT) bit is not requested. */
 typedef struct {
   int64_t m, n;
@@ -93,8 +101,9 @@ typedef struct {
   int64_t ldr;
 } mr_gram_problem;
 
-/* One matrix for inv_quarter_root_batched.  A: d x d of the call's a_dtype
- * (symmetric; its symmetric part (A + A^T)/2 is what is used), lda >= d.
+/* One matrix for inv_quarter_root_batched / inv_sqrt_root_batched.  A: d x d
+ * of the call's a_dtype (symmetric; its symmetric part (A + A^T)/2 is what is
+ * used), lda >= d; or packed (a_dtype | MR_PACKED, lda ignored).
  * X: d x d float32 output, ldx >= d; X must not overlap A. */
 typedef struct {
   int64_t d;

@@ -23,6 +23,7 @@ MR_NORM_NONE, MR_NORM_TRACE = 0, 1
 MR_AUTO, MR_JACOBI, MR_NEWTON, MR_NEWTON_F64, MR_NEWTON_F32 = 0, 1, 2, 3, 4
 MR_INFO_NONFINITE, MR_INFO_ZERO_TRACE, MR_INFO_NOT_PD, MR_INFO_NOT_CONVERGED = 1, 2, 4, 8
 MR_CANS_F16, MR_CANS_SPLIT = 0, 1
+MR_PACKED = 16
 
 _METHODS = {"auto": MR_AUTO, "jacobi": MR_JACOBI, "newton": MR_NEWTON, "newton_f64": MR_NEWTON_F64,
             "newton_f32": MR_NEWTON_F32}
@@ -147,6 +148,49 @@ def _ld(t) -> int:
     return int(t.stride(0))
 
 
+def packed_dim(n: int) -> int:
+    """d with d (d + 1) / 2 == n (the size of a packed symmetric matrix)."""
+    d = int((np.sqrt(8.0 * n + 1.0) - 1.0) / 2.0 + 0.5)
+    if d * (d + 1) // 2 != n:
+        raise ValueError(f"{n} elements is not a packed symmetric matrix")
+    return d
+
+
+def _sym(t):
+    """(d, leading dimension, packed) of a symmetric-matrix argument: a 2-D
+    (d, d) tensor (full storage) or a 1-D tensor of d (d + 1) / 2 elements
+    (upper triangle packed by rows, MR_PACKED)."""
+    if t.dim() == 1:
+        if t.stride(0) != 1:
+            raise ValueError("packed matrices must be contiguous")
+        return packed_dim(t.numel()), 0, True
+    if t.shape[0] != t.shape[1]:
+        raise ValueError("symmetric matrices must be square")
+    return int(t.shape[0]), _ld(t), False
+
+
+def pack_upper(A):
+    """Packed copy (upper triangle by rows) of a full symmetric tensor --
+    host-side indexing with torch, for tests and callers converting state."""
+    import torch
+
+    d = A.shape[0]
+    i, j = torch.triu_indices(d, d, device=A.device)
+    return A[i, j].contiguous()
+
+
+def unpack_upper(P):
+    """Full symmetric tensor from a packed one (torch indexing)."""
+    import torch
+
+    d = packed_dim(P.numel())
+    i, j = torch.triu_indices(d, d, device=P.device)
+    A = torch.empty(d, d, dtype=P.dtype, device=P.device)
+    A[i, j] = P
+    A[j, i] = P
+    return A
+
+
 def _stream(stream) -> int:
     import torch
 
@@ -180,12 +224,21 @@ def gram_ema_update(grads: Sequence, lefts: Optional[Sequence], rights: Optional
     if len(dts) != 1:
         raise ValueError("all Gram states must share one dtype")
     dt = MR_F64 if dts.pop() == "torch.float64" else MR_F32
+    layouts = {s.dim() == 1 for s in states}
+    if len(layouts) != 1:
+        raise ValueError("Gram states must be all full (2-D) or all packed (1-D)")
+    packed = layouts.pop()
+    if packed:
+        dt |= MR_PACKED
     probs = (GramProblem * max(count, 1))()
     for i, G in enumerate(grads):
         L = lefts[i] if lefts is not None else None
         R = rights[i] if rights is not None else None
-        probs[i] = GramProblem(G.shape[0], G.shape[1], _ptr(G), _ld(G), _ptr(L), _ld(L) if L is not None else 0,
-                               _ptr(R), _ld(R) if R is not None else 0)
+        for S, dim in ((L, G.shape[0]), (R, G.shape[1])):
+            if S is not None and _sym(S)[0] != dim:
+                raise ValueError("Gram state size does not match the gradient")
+        probs[i] = GramProblem(G.shape[0], G.shape[1], _ptr(G), _ld(G), _ptr(L), _sym(L)[1] if L is not None else 0,
+                               _ptr(R), _sym(R)[1] if R is not None else 0)
     _check(lib.gram_ema_update(ctypes.addressof(probs), count, dt, float(beta), sides, None, 0, _stream(stream)))
 
 
@@ -209,7 +262,8 @@ class RootWorkspace:
 def inv_quarter_root_batched(As: Sequence, eps: float, normalize: str = "trace", method: str = "auto",
                              Xs: Optional[Sequence] = None, workspace: Optional[RootWorkspace] = None,
                              stream=None, return_info: bool = True, info_out=None):
-    """X_i = (A_i/s_i + eps I)^(-1/4) for every (d, d) device tensor A_i.
+    """X_i = (A_i/s_i + eps I)^(-1/4) for every device tensor A_i: (d, d)
+    full, or 1-D packed (upper triangle by rows, d (d + 1) / 2 elements).
 
     Returns (Xs, info) where info is a numpy structured array (fields of
     mr_root_info) read after synchronising the stream, or (Xs, None).
@@ -217,36 +271,9 @@ def inv_quarter_root_batched(As: Sequence, eps: float, normalize: str = "trace",
     the info records instead of the workspace's buffer (no synchronisation
     when return_info is False); decode it later with decode_info().
     """
-    import torch
-
     lib = library()
-    count = len(As)
-    if count == 0:
-        return [], None
-    dts = {str(a.dtype) for a in As}
-    if len(dts) != 1:
-        raise ValueError("all A must share one dtype")
-    dt = MR_F64 if dts.pop() == "torch.float64" else MR_F32
-    dev = As[0].device
-    if Xs is None:
-        Xs = [torch.empty(a.shape[0], a.shape[0], dtype=torch.float32, device=dev) for a in As]
-    probs = (RootProblem * count)()
-    for i, (A, X) in enumerate(zip(As, Xs)):
-        probs[i] = RootProblem(A.shape[0], _ptr(A), _ld(A), _ptr(X), _ld(X))
-    m = _METHODS[method]
-    need = lib.inv_quarter_root_batched_workspace(ctypes.addressof(probs), count, dt, m)
-    ws = workspace or RootWorkspace()
-    buf, info = ws.get(need, count, dev)
-    if info_out is not None:
-        if info_out.numel() < 32 * count:
-            raise ValueError("info_out too small")
-        info = info_out
-    _check(lib.inv_quarter_root_batched(ctypes.addressof(probs), count, dt, float(eps), _NORMS[normalize], m,
-                                        _ptr(info), _ptr(buf), buf.numel(), _stream(stream)))
-    if not return_info:
-        return Xs, None
-    torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
-    return Xs, decode_info(info, count)
+    return _root_call(lib.inv_quarter_root_batched, lib.inv_quarter_root_batched_workspace, _METHODS[method], As,
+                      eps, normalize, Xs, workspace, stream, return_info, info_out)
 
 
 def _root_call(entry, size_entry, code, As, eps, normalize, Xs, workspace, stream, return_info, info_out):
@@ -260,12 +287,18 @@ def _root_call(entry, size_entry, code, As, eps, normalize, Xs, workspace, strea
     if len(dts) != 1:
         raise ValueError("all A must share one dtype")
     dt = MR_F64 if dts.pop() == "torch.float64" else MR_F32
+    syms = [_sym(a) for a in As]
+    layouts = {p for _, _, p in syms}
+    if len(layouts) != 1:
+        raise ValueError("A must be all full (2-D) or all packed (1-D)")
+    if layouts.pop():
+        dt |= MR_PACKED
     dev = As[0].device
     if Xs is None:
-        Xs = [torch.empty(a.shape[0], a.shape[0], dtype=torch.float32, device=dev) for a in As]
+        Xs = [torch.empty(d, d, dtype=torch.float32, device=dev) for d, _, _ in syms]
     probs = (RootProblem * count)()
     for i, (A, X) in enumerate(zip(As, Xs)):
-        probs[i] = RootProblem(A.shape[0], _ptr(A), _ld(A), _ptr(X), _ld(X))
+        probs[i] = RootProblem(syms[i][0], _ptr(A), syms[i][1], _ptr(X), _ld(X))
     need = size_entry(ctypes.addressof(probs), count, dt, code)
     ws = workspace or RootWorkspace()
     buf, info = ws.get(need, count, dev)

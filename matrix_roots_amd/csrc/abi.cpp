@@ -53,6 +53,14 @@ Range range_of(const void* p, int64_t rows, int64_t cols, int64_t ld, size_t es)
   return {lo, lo + (uintptr_t)(((rows - 1) * ld + cols) * (int64_t)es)};
 }
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+// Byte range of a symmetric d x d matrix, full (leading dimension ld) or packed.
+Range sym_range_of(const void* p, int64_t d, int64_t ld, size_t es, bool packed) {
+  return packed ? range_of(p, 1, d * (d + 1) / 2, 0, es) : range_of(p, d, d, ld, es);
+}
+// Base dtype and storage flag of an mr_dtype argument.
+mr_dtype base_dtype(mr_dtype dt) { return dt & ~MR_PACKED; }
+bool is_packed(mr_dtype dt) { return (dt & MR_PACKED) != 0; }
+bool valid_dtype(mr_dtype dt) { return (dt & ~(MR_PACKED | 1)) == 0; }
 
 bool debug_sync() {
   static const bool on = [] {
@@ -168,7 +176,8 @@ RootPlan plan_root(const mr_root_problem* p, int32_t count, int32_t method) {
   size_t off = 0;
   P.state_off = off;
   off = align256(off + sizeof(RootState) * (size_t)std::max(count, 1));
-  P.partial_stride = 3 * ((dmax_newton + kStatsRows - 1) / kStatsRows);
+  P.partial_stride = std::max<int64_t>(3 * ((dmax_newton + kStatsRows - 1) / kStatsRows),
+                                       (dmax_newton + kFinalRows - 1) / kFinalRows);
   P.partial_stride = std::max<int64_t>(P.partial_stride, 1);
   P.partial_off = off;
   off = align256(off + sizeof(double) * (size_t)P.partial_stride * (size_t)std::max(P.n_newton, 1));
@@ -272,11 +281,13 @@ int32_t mr_newton_iterations(int32_t p, double m0, double tol) {
 static mr_status validate_gram(const mr_gram_problem* p, int32_t count, mr_dtype dt, double beta, uint32_t sides) {
   if (count < 0) return fail(MR_ERR_PARAM, "count %d < 0", count);
   if (count > 0 && !p) return fail(MR_ERR_NULL, "problems is NULL");
-  if (dt != MR_F32 && dt != MR_F64) return fail(MR_ERR_PARAM, "state_dtype %d is not MR_F32 or MR_F64", dt);
+  if (!valid_dtype(dt))
+    return fail(MR_ERR_PARAM, "state_dtype %d is not MR_F32 or MR_F64 (optionally | MR_PACKED)", dt);
+  const bool packed = is_packed(dt);
   if (!(beta >= 0.0 && beta < 1.0)) return fail(MR_ERR_PARAM, "beta %g not in [0, 1)", beta);
   if (sides == 0 || (sides & ~(uint32_t)(MR_LEFT | MR_RIGHT)))
     return fail(MR_ERR_PARAM, "sides 0x%x must be a non-empty subset of MR_LEFT|MR_RIGHT", sides);
-  const size_t es = dt == MR_F64 ? 8 : 4;
+  const size_t es = base_dtype(dt) == MR_F64 ? 8 : 4;
   for (int i = 0; i < count; ++i) {
     const mr_gram_problem& q = p[i];
     if (q.m < 1 || q.n < 1 || q.m > kMaxDim || q.n > kMaxDim)
@@ -289,16 +300,18 @@ static mr_status validate_gram(const mr_gram_problem* p, int32_t count, mr_dtype
     Range rl{0, 0}, rr{0, 0};
     if (sides & MR_LEFT) {
       if (!q.L) return fail(MR_ERR_NULL, "problem %d: L is NULL", i);
-      if (q.ldl < q.m) return fail(MR_ERR_STRIDE, "problem %d: ldl %lld < m %lld", i, (long long)q.ldl, (long long)q.m);
+      if (!packed && q.ldl < q.m)
+        return fail(MR_ERR_STRIDE, "problem %d: ldl %lld < m %lld", i, (long long)q.ldl, (long long)q.m);
       if (!aligned(q.L, es)) return fail(MR_ERR_PARAM, "problem %d: L misaligned for its dtype", i);
-      rl = range_of(q.L, q.m, q.m, q.ldl, es);
+      rl = sym_range_of(q.L, q.m, q.ldl, es, packed);
       if (overlap(rl, rg)) return fail(MR_ERR_ALIAS, "problem %d: L overlaps G", i);
     }
     if (sides & MR_RIGHT) {
       if (!q.R) return fail(MR_ERR_NULL, "problem %d: R is NULL", i);
-      if (q.ldr < q.n) return fail(MR_ERR_STRIDE, "problem %d: ldr %lld < n %lld", i, (long long)q.ldr, (long long)q.n);
+      if (!packed && q.ldr < q.n)
+        return fail(MR_ERR_STRIDE, "problem %d: ldr %lld < n %lld", i, (long long)q.ldr, (long long)q.n);
       if (!aligned(q.R, es)) return fail(MR_ERR_PARAM, "problem %d: R misaligned for its dtype", i);
-      rr = range_of(q.R, q.n, q.n, q.ldr, es);
+      rr = sym_range_of(q.R, q.n, q.ldr, es, packed);
       if (overlap(rr, rg)) return fail(MR_ERR_ALIAS, "problem %d: R overlaps G", i);
     }
     if ((sides & MR_LEFT) && (sides & MR_RIGHT) && overlap(rl, rr))
@@ -325,9 +338,11 @@ mr_status gram_ema_update(const mr_gram_problem* p, int32_t count, mr_dtype dt, 
       memset(&b, 0, sizeof b);
       b.alpha = 1.0 - beta;
       b.beta = beta;
+      b.packed = is_packed(dt) ? 1 : 0;
       auto flush = [&]() -> mr_status {
         if (b.njobs == 0) return MR_OK;
-        mr_status r = traced(kTrSyrk, b.total_blocks > 0, s, [&] { return launch_syrk_ema(b, right, dt == MR_F64, vec, s); },
+        mr_status r = traced(kTrSyrk, b.total_blocks > 0, s,
+                             [&] { return launch_syrk_ema(b, right, base_dtype(dt) == MR_F64, vec, s); },
                              "gram_ema_update launch");
         b.njobs = 0;
         b.total_blocks = 0;
@@ -454,15 +469,16 @@ mr_status precondition_apply(const mr_apply_problem* p, int32_t count, float alp
 
 // ================================================ inv_quarter_root_batched
 static mr_status validate_root_problems(const mr_root_problem* p, int32_t count, mr_dtype dt) {
-  const size_t es = dt == MR_F64 ? 8 : 4;
+  const size_t es = base_dtype(dt) == MR_F64 ? 8 : 4;
+  const bool packed = is_packed(dt);
   for (int i = 0; i < count; ++i) {
     const mr_root_problem& q = p[i];
     if (q.d < 1 || q.d > kMaxDim)
       return fail(MR_ERR_SHAPE, "problem %d: d=%lld outside [1, %lld]", i, (long long)q.d, (long long)kMaxDim);
     if (!q.A || !q.X) return fail(MR_ERR_NULL, "problem %d: A or X is NULL", i);
-    if (q.lda < q.d || q.ldx < q.d) return fail(MR_ERR_STRIDE, "problem %d: lda or ldx < d", i);
+    if ((!packed && q.lda < q.d) || q.ldx < q.d) return fail(MR_ERR_STRIDE, "problem %d: lda or ldx < d", i);
     if (!aligned(q.A, es) || !aligned(q.X, 4)) return fail(MR_ERR_PARAM, "problem %d: A or X misaligned", i);
-    if (overlap(range_of(q.A, q.d, q.d, q.lda, es), range_of(q.X, q.d, q.d, q.ldx, 4)))
+    if (overlap(sym_range_of(q.A, q.d, q.lda, es, packed), range_of(q.X, q.d, q.d, q.ldx, 4)))
       return fail(MR_ERR_ALIAS, "problem %d: X overlaps A", i);
   }
   return MR_OK;
@@ -472,7 +488,8 @@ static mr_status validate_root(const mr_root_problem* p, int32_t count, mr_dtype
                                int32_t method) {
   if (count < 0) return fail(MR_ERR_PARAM, "count %d < 0", count);
   if (count > 0 && !p) return fail(MR_ERR_NULL, "problems is NULL");
-  if (dt != MR_F32 && dt != MR_F64) return fail(MR_ERR_PARAM, "a_dtype %d is not MR_F32 or MR_F64", dt);
+  if (!valid_dtype(dt))
+    return fail(MR_ERR_PARAM, "a_dtype %d is not MR_F32 or MR_F64 (optionally | MR_PACKED)", dt);
   if (!(eps > 0.0) || !std::isfinite(eps)) return fail(MR_ERR_PARAM, "eps %g must be positive and finite", eps);
   if (normalize != MR_NORM_NONE && normalize != MR_NORM_TRACE)
     return fail(MR_ERR_PARAM, "normalize %d is not MR_NORM_NONE or MR_NORM_TRACE", normalize);
@@ -510,7 +527,8 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
   RootState* state = reinterpret_cast<RootState*>(base + P.state_off);
   double* partial = reinterpret_cast<double*>(base + P.partial_off);
   double* sched = reinterpret_cast<double*>(base + P.sched_off);
-  const int a_f64 = dt == MR_F64;
+  const int a_f64 = base_dtype(dt) == MR_F64;
+  const int a_packed = is_packed(dt) ? 1 : 0;
   const bool all_f64 = method == MR_NEWTON_F64;
   const bool f32_mfma = method == MR_NEWTON_F32;
   // Default Newton path: X in float32 storage with split-fp16 products from
@@ -522,6 +540,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
     JacobiBatch jb;
     memset(&jb, 0, sizeof jb);
     jb.a_f64 = a_f64;
+    jb.a_packed = a_packed;
     jb.normalize = normalize;
     jb.max_sweeps = 30;
     jb.eps = eps;
@@ -551,6 +570,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
       RootBatch b;
       memset(&b, 0, sizeof b);
       b.a_f64 = a_f64;
+      b.a_packed = a_packed;
       b.normalize = normalize;
       b.eps = eps;
       b.state = state;
@@ -761,7 +781,7 @@ CansPlan plan_cans(const mr_root_problem* p, int32_t count) {
   size_t off = 0;
   P.state_off = off;
   off = align256(off + sizeof(RootState) * (size_t)std::max(count, 1));
-  P.partial_stride = 3 * ((dmax + kStatsRows - 1) / kStatsRows);
+  P.partial_stride = std::max<int64_t>(3 * ((dmax + kStatsRows - 1) / kStatsRows), (dmax + kFinalRows - 1) / kFinalRows);
   P.partial_off = off;
   off = align256(off + sizeof(double) * (size_t)P.partial_stride * (size_t)std::max(count, 1));
   for (auto& c : P.classes) {
@@ -799,7 +819,8 @@ mr_status inv_sqrt_root_batched(const mr_root_problem* p, int32_t count, mr_dtyp
                                 void* hip_stream) {
   if (count < 0) return fail(MR_ERR_PARAM, "count %d < 0", count);
   if (count > 0 && !p) return fail(MR_ERR_NULL, "problems is NULL");
-  if (dt != MR_F32 && dt != MR_F64) return fail(MR_ERR_PARAM, "a_dtype %d is not MR_F32 or MR_F64", dt);
+  if (!valid_dtype(dt))
+    return fail(MR_ERR_PARAM, "a_dtype %d is not MR_F32 or MR_F64 (optionally | MR_PACKED)", dt);
   if (!(eps >= 0.0) || !std::isfinite(eps)) return fail(MR_ERR_PARAM, "eps %g must be >= 0 and finite", eps);
   if (normalize != MR_NORM_NONE && normalize != MR_NORM_TRACE)
     return fail(MR_ERR_PARAM, "normalize %d is not MR_NORM_NONE or MR_NORM_TRACE", normalize);
@@ -823,7 +844,8 @@ mr_status inv_sqrt_root_batched(const mr_root_problem* p, int32_t count, mr_dtyp
   auto run_batches = [&](int kind) -> mr_status {
     RootBatch b;
     memset(&b, 0, sizeof b);
-    b.a_f64 = dt == MR_F64;
+    b.a_f64 = base_dtype(dt) == MR_F64;
+    b.a_packed = is_packed(dt) ? 1 : 0;
     b.normalize = normalize;
     b.eps = eps;
     b.state = state;

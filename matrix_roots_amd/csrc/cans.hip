@@ -129,8 +129,8 @@ __global__ __launch_bounds__(64) void cans_bound_kernel(RootState* state, const 
 }
 
 // Y0 = sy0 S / L into Y(even) and Z1 = (za + zb y0) -- the scaled
-// a0 I + b0 Y0 -- into Z(odd), 32 x 32 tiles through LDS so both reads of A
-// (for the symmetric part) are coalesced.
+// a0 I + b0 Y0 -- into Z(odd), 32 x 32 tiles of the symmetric part through
+// LDS (load_sym_tile).
 template <typename TA>
 __global__ __launch_bounds__(256) void cans_init_kernel(const RootBatch B, double sy0, double za, double zb) {
   __shared__ double ta[32][33];
@@ -144,16 +144,7 @@ __global__ __launch_bounds__(256) void cans_init_kernel(const RootBatch B, doubl
   const int tile = (int)(b - J.block_begin);
   const int bi = tile / Tt, bj = tile % Tt;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  const TA* A = reinterpret_cast<const TA*>(J.A);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int r = ty + 8 * e;
-    const int gi = bi * 32 + r, gj = bj * 32 + tx;
-    ta[r][tx] = (gi < d && gj < d) ? (double)A[(int64_t)gi * J.lda + gj] : 0.0;
-    const int hi = bj * 32 + r, hj = bi * 32 + tx;
-    tb[r][tx] = (hi < d && hj < d) ? (double)A[(int64_t)hi * J.lda + hj] : 0.0;
-  }
-  __syncthreads();
+  load_sym_tile<TA>(J.A, J.lda, d, B.a_packed != 0, bi, bj, ta, tb);
   const double inv_s = 1.0 / st.s, inv_L = 1.0 / st.c, eps = B.eps;
   const Split Y = cans_buf(J.region, d, buf_y(0));
   const Split Z = cans_buf(J.region, d, buf_z(1));
@@ -162,7 +153,7 @@ __global__ __launch_bounds__(256) void cans_init_kernel(const RootBatch B, doubl
     const int r = ty + 8 * e;
     const int gi = bi * 32 + r, gj = bj * 32 + tx;
     if (gi < d && gj < d) {
-      const double y0 = (0.5 * (ta[r][tx] + tb[tx][r]) * inv_s + (gi == gj ? eps : 0.0)) * inv_L;
+      const double y0 = (sym_tile_value(B.a_packed != 0, bi, bj, r, tx, ta, tb) * inv_s + (gi == gj ? eps : 0.0)) * inv_L;
       const int64_t i = (int64_t)gi * d + gj;
       put(Y, i, (float)(sy0 * y0));
       put(Z, i, (float)(zb * y0 + (gi == gj ? za : 0.0)));

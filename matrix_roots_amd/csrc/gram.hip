@@ -8,8 +8,10 @@
 // section "Background").  float32 entries of G are widened to float64 on the
 // way into LDS; their products are exact in float64 and are summed in float64
 // by v_mfma_f64_16x16x4_f64.  Only the upper triangle of 128 x 128 tiles is
-// computed; every computed element is written to both (i, j) and (j, i), so
-// the state stays exactly symmetric and only its upper triangle is read.
+// computed; in full storage every computed element is written to both (i, j)
+// and (j, i), so the state stays exactly symmetric and only its upper
+// triangle is read; in packed storage (upper triangle by rows) each element
+// is read and written once.
 #include "gemm_core.hpp"
 #include "launch.hpp"
 
@@ -37,14 +39,16 @@ __global__ __launch_bounds__(256, 2) void syrk_ema_kernel(const SyrkBatch batch)
   const int64_t lds = J.lds;
   const int d = J.d;
   const double alpha = batch.alpha, beta = batch.beta;
+  const bool packed = batch.packed != 0;
   f64_for_each(acc, [&](int r, int c, double v) {
     const int gr = m0 + r, gc = n0 + c;
     if (gr < d && gc < d && gr <= gc) {
+      const int64_t i = sym_index(gr, gc, lds, d, packed);
       double val = alpha * v;
-      if (beta != 0.0) val += beta * (double)S[(int64_t)gr * lds + gc];
+      if (beta != 0.0) val += beta * (double)S[i];
       const TS out = (TS)val;
-      S[(int64_t)gr * lds + gc] = out;
-      if (gr != gc) S[(int64_t)gc * lds + gr] = out;
+      S[i] = out;
+      if (!packed && gr != gc) S[(int64_t)gc * lds + gr] = out;
     }
   });
 }

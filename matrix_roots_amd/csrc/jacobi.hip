@@ -17,6 +17,7 @@
 #include <math.h>
 
 #include "launch.hpp"
+#include "mr_common.hpp"
 
 namespace mr {
 
@@ -63,8 +64,9 @@ __global__ __launch_bounds__(256) void jacobi_kernel(const JacobiBatch B) {
     const int i = idx / n, j = idx % n;
     double v = 0.0;
     if (i < d && j < d) {
-      const double a = jac_ld<TA>(J.A, (int64_t)i * J.lda + j);
-      const double at = jac_ld<TA>(J.A, (int64_t)j * J.lda + i);
+      const bool packed = B.a_packed != 0;
+      const double a = jac_ld<TA>(J.A, sym_index(i, j, J.lda, d, packed));
+      const double at = jac_ld<TA>(J.A, sym_index(j, i, J.lda, d, packed));
       v = 0.5 * (a + at);
       if (!isfinite(v)) nf += 1.0;
       if (i == j) tr += v;

@@ -17,7 +17,7 @@ namespace mr {
 constexpr int kMaxJobs = 16;
 constexpr int kMaxClasses = 8;
 constexpr int kJacobiMaxD = 128;
-constexpr int kStatsRows = 8;        // rows of A per statistics workgroup
+constexpr int kStatsRows = 32;       // rows of A per statistics workgroup (one 32-row tile stripe)
 constexpr int kFinalRows = 8;        // rows of X per finalize workgroup
 constexpr double kSwitchM = 2e-3;    // float64 -> float32 once the eigenvalue floor reaches this
 constexpr double kNewtonTol = 1e-6;  // stop once 1 - m_K <= this (scalar recurrence)
@@ -63,6 +63,8 @@ struct SyrkBatch {
   int32_t total_blocks;
   double alpha;  // 1 - beta
   double beta;
+  int32_t packed;  // states stored packed (MR_PACKED)
+  int32_t pad;
 };
 
 // ------------------------------------------------- float32 NT GEMM (apply)
@@ -109,7 +111,7 @@ struct RootBatch {
   double* partial;         // per-workgroup partial sums
   int64_t partial_stride;  // doubles per matrix slot in `partial`
   int32_t x_low;           // X kept in float32 from the first step
-  int32_t pad;
+  int32_t a_packed;        // A stored packed (MR_PACKED)
 };
 
 // ------------------------------------------------ Newton: per size class
@@ -152,6 +154,8 @@ struct JacobiBatch {
   int32_t a_f64;
   int32_t normalize;
   int32_t max_sweeps;
+  int32_t a_packed;  // A stored packed (MR_PACKED)
+  int32_t pad;
   double eps;
   RootState* state;
 };

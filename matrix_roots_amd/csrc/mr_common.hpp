@@ -57,6 +57,57 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t n) {
   return (b % kNumXcd) * per + b / kNumXcd;
 }
 
+// Offset of element (i, j) of a symmetric d x d matrix stored full
+// (row-major, leading dimension ld) or packed (upper triangle by rows:
+// (i, j), i <= j, at i d - i (i - 1) / 2 + j - i); a lower element of a
+// packed matrix reads its mirror.
+__host__ __device__ __forceinline__ int64_t sym_index(int64_t i, int64_t j, int64_t ld, int64_t d, bool packed) {
+  if (!packed) return i * ld + j;
+  if (i > j) {
+    const int64_t t = i;
+    i = j;
+    j = t;
+  }
+  return i * d - (i * (i - 1)) / 2 + (j - i);
+}
+
+// Tile (bi, bj) of 32 x 32 of the symmetric part (A + A^T)/2 through LDS
+// (256 threads, 4 rows each).  Full storage: tiles (bi, bj) into ta and
+// (bj, bi) into tb, both read along rows.  Packed storage: the upper tile of
+// the pair into ta (its rows are contiguous); the matrix is symmetric by
+// construction, so its symmetric part is the stored value itself.
+template <typename TA>
+__device__ __forceinline__ void load_sym_tile(const void* A, int64_t lda, int d, bool packed, int bi, int bj,
+                                              double (*ta)[33], double (*tb)[33]) {
+  const TA* a = reinterpret_cast<const TA*>(A);
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  if (packed) {
+    const int ui = bi < bj ? bi : bj, uj = bi < bj ? bj : bi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = ty + 8 * e;
+      const int gi = ui * 32 + r, gj = uj * 32 + tx;
+      ta[r][tx] = (gi < d && gj < d) ? (double)a[sym_index(gi, gj, 0, d, true)] : 0.0;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = ty + 8 * e;
+      const int gi = bi * 32 + r, gj = bj * 32 + tx;
+      ta[r][tx] = (gi < d && gj < d) ? (double)a[(int64_t)gi * lda + gj] : 0.0;
+      const int hi = bj * 32 + r, hj = bi * 32 + tx;
+      tb[r][tx] = (hi < d && hj < d) ? (double)a[(int64_t)hi * lda + hj] : 0.0;
+    }
+  }
+  __syncthreads();
+}
+// Element (r, c) of the tile loaded by load_sym_tile.
+__device__ __forceinline__ double sym_tile_value(bool packed, int bi, int bj, int r, int c, const double (*ta)[33],
+                                                 const double (*tb)[33]) {
+  if (packed) return bi <= bj ? ta[r][c] : ta[c][r];
+  return 0.5 * (ta[r][c] + tb[c][r]);
+}
+
 // Upper-triangle tile u (row-major over ti <= tj) of a T x T tile grid.
 __device__ __forceinline__ void upper_tile(int u, int T, int& ti, int& tj) {
   // rows ti hold T - ti tiles; walk the rows (T <= 128 in practice).

@@ -157,23 +157,46 @@ __device__ __forceinline__ double ld_elem(const void* A, int64_t idx) {
 }
 
 // ------------------------------------------------------------ statistics
-// Per row block of A: partial trace, sum of squares, count of non-finite.
+// Per 32-row stripe of A: partial trace, sum of squares, count of
+// non-finite, over 32 x 32 tiles left to right, each thread summing its own
+// tile positions in that order.  A packed A's lower tiles are their upper
+// mirrors transposed through LDS, so a packed and a full copy of the same
+// symmetric matrix give bitwise identical partials.
 template <typename TA>
 __global__ __launch_bounds__(256) void root_stats_kernel(const RootBatch B) {
   __shared__ double red[256];
+  __shared__ double tl[32][33];
   const int64_t b = blockIdx.x;
   const RootJob& J = B.job[find_job(B, b)];
   const int blk = (int)(b - J.block_begin);
   const int d = J.d;
-  const int r0 = blk * kStatsRows;
-  const int r1 = min(d, r0 + kStatsRows);
+  const int T = (d + 31) / 32;
+  const bool packed = B.a_packed != 0;
+  const TA* A = reinterpret_cast<const TA*>(J.A);
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   double tr = 0.0, f2 = 0.0, nf = 0.0;
-  for (int r = r0; r < r1; ++r) {
-    for (int c = threadIdx.x; c < d; c += 256) {
-      const double v = ld_elem<TA>(J.A, (int64_t)r * J.lda + c);
-      if (r == c) tr += v;
-      f2 += v * v;
-      if (!isfinite(v)) nf += 1.0;
+  for (int bj = 0; bj < T; ++bj) {
+    const bool mirror = packed && bj < blk;
+    if (mirror) {
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = ty + 8 * e;
+        const int gi = bj * 32 + r, gj = blk * 32 + tx;
+        tl[r][tx] = (gi < d && gj < d) ? (double)A[sym_index(gi, gj, 0, d, true)] : 0.0;
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = ty + 8 * e;
+      const int gi = blk * 32 + r, gj = bj * 32 + tx;
+      if (gi < d && gj < d) {
+        const double v = mirror ? tl[tx][r] : (double)A[sym_index(gi, gj, J.lda, d, packed)];
+        if (gi == gj) tr += v;
+        f2 += v * v;
+        if (!isfinite(v)) nf += 1.0;
+      }
     }
   }
   tr = block_sum_256(tr, red);
@@ -277,15 +300,7 @@ __global__ __launch_bounds__(256) void root_init_kernel(const RootBatch B) {
   const int tile = (int)(b - J.block_begin);
   const int bi = tile / Tt, bj = tile % Tt;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int r = ty + 8 * e;
-    const int gi = bi * 32 + r, gj = bj * 32 + tx;
-    ta[r][tx] = (gi < d && gj < d) ? ld_elem<TA>(J.A, (int64_t)gi * J.lda + gj) : 0.0;
-    const int hi = bj * 32 + r, hj = bi * 32 + tx;
-    tb[r][tx] = (hi < d && hj < d) ? ld_elem<TA>(J.A, (int64_t)hi * J.lda + hj) : 0.0;
-  }
-  __syncthreads();
+  load_sym_tile<TA>(J.A, J.lda, d, B.a_packed != 0, bi, bj, ta, tb);
   const double inv_s = 1.0 / st.s, inv_c = 1.0 / st.c, eps = B.eps;
   double* M = reinterpret_cast<double*>(J.region);
   double* X = reinterpret_cast<double*>(J.region + (int64_t)d * d * 8);
@@ -296,7 +311,7 @@ __global__ __launch_bounds__(256) void root_init_kernel(const RootBatch B) {
     const int r = ty + 8 * e;
     const int gi = bi * 32 + r, gj = bj * 32 + tx;
     if (gi < d && gj < d) {
-      const double sym = 0.5 * (ta[r][tx] + tb[tx][r]);
+      const double sym = sym_tile_value(B.a_packed != 0, bi, bj, r, tx, ta, tb);
       const double v = (sym * inv_s + (gi == gj ? eps : 0.0)) * inv_c;
       const int64_t e = (int64_t)gi * d + gj;
       M[e] = v;

@@ -223,3 +223,34 @@ def test_cans_ceilings_match_okls_page():
         assert z[k] == pytest.approx(g["z_ceilings"][k], rel=2e-4), k
         assert p[k] == pytest.approx(g["p_ceilings"][k], rel=1e-2), k
         assert y[k] <= g["y_ceilings"][k] * 1.005, k
+
+
+def test_packed_validation(lib):
+    """MR_PACKED: leading dimensions ignored, ranges of d(d+1)/2 elements."""
+    F64P = B.MR_F64 | B.MR_PACKED
+    assert call_gram(lib, [gram(4, 8, ldl=0, ldr=0)], dt=F64P) != 3  # ld ignored when packed
+    assert call_gram(lib, [gram(4, 8)], dt=B.MR_F64 | 32) == 4
+    assert call_gram(lib, [gram(4, 8)], dt=2 | B.MR_PACKED) == 4
+    # packed L of m=4 spans 10 doubles = 80 bytes from P2: R at P2 + 72 overlaps, at P2 + 80 does not
+    assert call_gram(lib, [gram(4, 8, R=P2 + 72)], dt=F64P) == 8
+    assert call_gram(lib, [gram(4, 8, R=P2 + 80)], dt=F64P) != 8
+    assert call_root(lib, [root(8, lda=0)], dt=B.MR_F32 | B.MR_PACKED) == 5  # valid; only the workspace is missing
+    assert call_root(lib, [root(8, lda=0)], dt=B.MR_F32) == 3
+    # packed A of d=8 spans 36 floats = 144 bytes from P1
+    assert call_root(lib, [root(8, X=P1 + 140)], dt=B.MR_F32 | B.MR_PACKED) == 8
+    assert call_root(lib, [root(8, X=P1 + 144)], dt=B.MR_F32 | B.MR_PACKED) == 5
+    assert call_sqrt(lib, [root(8, lda=0)], dt=B.MR_F64 | B.MR_PACKED) == 5
+
+
+def test_pack_helpers_roundtrip():
+    import torch
+
+    A = torch.randn(7, 7, dtype=torch.float64)
+    A = A + A.T
+    P = B.pack_upper(A)
+    assert P.numel() == 28 and B.packed_dim(28) == 7
+    # row-packed upper triangle: row i holds columns i..d-1
+    assert P[0].item() == A[0, 0].item() and P[7].item() == A[1, 1].item() and P[27].item() == A[6, 6].item()
+    assert torch.equal(B.unpack_upper(P), A)
+    with pytest.raises(ValueError):
+        B.packed_dim(27)
