@@ -14,6 +14,7 @@ from .step import (  # noqa: F401
     inv_quarter_root,
     inv_sqrt_root,
     left_gram,
+    polar_cans,
     precondition_apply,
     preconditioner_step,
     relative_frobenius,

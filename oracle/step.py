@@ -21,6 +21,9 @@ What it computes, and where the pages define it:
 * The inverse square root of a symmetric positive definite matrix, the root
   tilderesearch, "Online KL Shampoo", computes for its preconditioner
   (sections 2.2-2.4, appendix D), as the same eigenvalue map with power -1/2.
+* The polar orthogonalisation its CANS coefficients were designed for
+  (section 2.3), as the odd polynomial those ten steps apply to the
+  singular values (numpy.linalg.svd, LAPACK gesdd).
 
 Readings taken where the pages are silent (each is listed with its reason in
 the design notes):
@@ -35,8 +38,9 @@ the design notes):
 * the output root is symmetrised, (X + Xᵀ)/2 (the OKLS page, appendix D, does
   the same to its root).
 
-Everything is float64. numpy's ``@`` (BLAS dgemm) and ``numpy.linalg.eigh``
-(LAPACK dsyevd) are the only library steps; nothing is blocked, fused or
+Everything is float64. numpy's ``@`` (BLAS dgemm), ``numpy.linalg.eigh``
+(LAPACK dsyevd) and ``numpy.linalg.svd`` (LAPACK gesdd) are the only library
+steps; nothing is blocked, fused or
 reordered beyond the definitions above.
 """
 
@@ -170,6 +174,48 @@ def inv_sqrt_root(A, eps: float, normalize: str = NORM_NONE):
     W = (V * f) @ V.T
     W = 0.5 * (W + W.T)
     return W, {"scale": s, "flags": 0, "eigenvalues": w}
+
+
+# The ten CANS polynomial coefficient pairs (a_k, b_k) printed in
+# tilderesearch, "Online KL Shampoo", appendix D.
+CANS_COEFFS = (
+    (5.182503604966906, -5.178098480082684), (2.586120737395915, -0.6479542005271643),
+    (2.567364126726186, -0.6454968804392178), (2.520560084348265, -0.6393528082067044),
+    (2.410759275435182, -0.6248683598710716), (2.1883348130094173, -0.5952022073798908),
+    (1.8595760874873613, -0.5504490972723968), (1.589020160467417, -0.5126569802066718),
+    (1.5051653981684994, -0.5007377068751799), (1.5, -0.5),
+)
+
+
+def polar_cans(G):
+    """The orthogonalised update of the ten CANS polar steps.
+
+    tilderesearch, "Online KL Shampoo", section 2.3: the CANS coefficients
+    were built for Muon's polar factor, where each step X <- a_k X +
+    b_k X Xᵀ X moves every singular value by s <- s (a_k + b_k s²) and
+    leaves the singular vectors alone.  So from X0 = G / sqrt(L) the ten
+    steps give exactly U · diag(phi(sigma / sqrt(L))) · Vᵀ with G = U Σ Vᵀ
+    (thin SVD) and phi the composition of the ten odd polynomials; phi is
+    within 3e-5 of 1 for sigma² / L in [1e-6, 0.99], so this is the polar
+    factor U Vᵀ wherever the spectrum lies in that range.  L = 1.01 ||G||_F²
+    (the Frobenius normalisation Muon uses, with the OKLS page's 1.01
+    safety factor), so sigma² / L <= 1/1.01.
+
+    Returns (O, info), info = {"scale": ||G||_F², "bound": L, "flags"}:
+    non-finite G -> O all NaN, NONFINITE; zero G -> O = 0, ZERO_TRACE.
+    """
+    G = _f64(G)
+    if not np.all(np.isfinite(G)):
+        return np.full(G.shape, np.nan), {"scale": float("nan"), "bound": float("nan"), "flags": FLAG_NONFINITE}
+    f2 = float(np.sum(G * G))
+    if f2 == 0.0:
+        return np.zeros(G.shape), {"scale": 0.0, "bound": 0.0, "flags": FLAG_ZERO_TRACE}
+    L = 1.01 * f2
+    U, sigma, Vt = np.linalg.svd(G, full_matrices=False)
+    x = sigma / np.sqrt(L)
+    for a, b in CANS_COEFFS:
+        x = x * (a + b * x * x)
+    return (U * x) @ Vt, {"scale": f2, "bound": L, "flags": 0}
 
 
 def precondition_apply(XL, G, XR, alpha: float = 1.0) -> np.ndarray:
