@@ -247,6 +247,46 @@ mr_status inv_sqrt_root_batched(const mr_root_problem* problems, int32_t count, 
 size_t inv_sqrt_root_batched_workspace(const mr_root_problem* problems, int32_t count,
                                        mr_dtype a_dtype, int32_t precision);
 
+/* One matrix for polar_cans_batched.  G: m x n float32 (ldg >= n); O: m x n
+ * float32 output (ldo >= n), must not overlap G. */
+typedef struct {
+  int64_t m, n;
+  const float* G;
+  int64_t ldg;
+  float* O;
+  int64_t ldo;
+} mr_polar_problem;
+
+/*
+ * polar_cans_batched -- for every problem, the orthogonalised matrix of the
+ * ten CANS polar steps
+ *     X0 = G / sqrt(L),  L = 1.01 ||G||_F^2,  X <- a_k X + b_k X X^T X,  O = X_10
+ * with the OKLS page's ten CANS coefficient pairs (tilderesearch, "Online KL
+ * Shampoo", section 2.3: the coefficients were designed for Muon's polar
+ * factor).  Each step maps every singular value s to s (a_k + b_k s^2) and
+ * keeps the singular vectors, so O = U phi(Sigma / sqrt(L)) V^T for
+ * G = U Sigma V^T; phi is within 3e-5 of 1 for sigma^2 / L in [1e-6, 0.99],
+ * where O is the polar factor U V^T.  The iteration runs on the tall
+ * orientation (G^T for m < n): per step the Gram A = X^T X (symmetric,
+ * upper-triangle product) and X' = a X + b X A (full product), 20 launches
+ * for the whole batch, intermediates stored as fp16 plus an fp16 rounding
+ * remainder, times powers of two from the singular-value recurrence (no
+ * entry above 2^14).  precision: MR_CANS_F16 (fp16 products, float32
+ * accumulation; relative error about 3e-3) or MR_CANS_SPLIT (float32-accurate
+ * products; about 1e-6).
+ * info_dev: device array of `count` records (may be NULL): scale = ||G||_F^2,
+ * bound = L, iters = 10, fp64_iters = 0, residual = ||A_9 - I||_F (the last
+ * Gram; not small for rank-deficient G, so never a flag); flags: NONFINITE
+ * (O all NaN), ZERO_TRACE (G = 0: O = 0).
+ * Workspace: at least polar_cans_batched_workspace(...) bytes (4 (3 M N + N^2)
+ * bytes per matrix, M = max(m, n), N = min(m, n), plus per-matrix state),
+ * 256-byte aligned; contents on entry ignored.  Validation is all-or-nothing
+ * before anything is enqueued; no host synchronisation.
+ */
+mr_status polar_cans_batched(const mr_polar_problem* problems, int32_t count, int32_t precision,
+                             mr_root_info* info_dev, void* ws, size_t ws_bytes, void* hip_stream);
+size_t polar_cans_batched_workspace(const mr_polar_problem* problems, int32_t count, int32_t precision);
+
 /* Suprema over y0 in (0, 1] of the CANS scalar recurrence y <- y q, z <- z q,
  * q = a_k + b_k z y (y, z from y0, 1), at steps k = 0..10: the per-step
  * bounds inv_sqrt_root_batched scales its intermediates by (y: Y_k, z: Z_k,

@@ -38,6 +38,8 @@ EXPORTED = (
     "inv_sqrt_root_batched",
     "inv_sqrt_root_batched_workspace",
     "mr_cans_ceilings",
+    "polar_cans_batched",
+    "polar_cans_batched_workspace",
     "precondition_apply",
     "precondition_apply_workspace",
     "mr_newton_iterations",
@@ -58,6 +60,11 @@ class GramProblem(ctypes.Structure):
 class RootProblem(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int64), ("A", ctypes.c_void_p), ("lda", ctypes.c_int64), ("X", ctypes.c_void_p),
                 ("ldx", ctypes.c_int64)]
+
+
+class PolarProblem(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("G", ctypes.c_void_p), ("ldg", ctypes.c_int64),
+                ("O", ctypes.c_void_p), ("ldo", ctypes.c_int64)]
 
 
 class ApplyProblem(ctypes.Structure):
@@ -108,6 +115,10 @@ def library() -> ctypes.CDLL:
     lib.inv_sqrt_root_batched_workspace.restype = sz
     lib.mr_cans_ceilings.argtypes = [vp, vp, vp, i32]
     lib.mr_cans_ceilings.restype = i32
+    lib.polar_cans_batched.argtypes = [vp, i32, i32, vp, vp, sz, vp]
+    lib.polar_cans_batched.restype = i32
+    lib.polar_cans_batched_workspace.argtypes = [vp, i32, i32]
+    lib.polar_cans_batched_workspace.restype = sz
     lib.precondition_apply.argtypes = [vp, i32, f32, vp, sz, vp]
     lib.precondition_apply.restype = i32
     lib.precondition_apply_workspace.argtypes = [vp, i32]
@@ -324,6 +335,41 @@ def inv_sqrt_root_batched(As: Sequence, eps: float = 0.0, normalize: str = "none
     lib = library()
     return _root_call(lib.inv_sqrt_root_batched, lib.inv_sqrt_root_batched_workspace, _PRECISIONS[precision], As,
                       eps, normalize, Xs, workspace, stream, return_info, info_out)
+
+
+def polar_cans_batched(Gs: Sequence, precision: str = "f16", Os: Optional[Sequence] = None,
+                       workspace: Optional[RootWorkspace] = None, stream=None, return_info: bool = True,
+                       info_out=None):
+    """O_i = the ten CANS polar steps on G_i / sqrt(1.01 ||G_i||_F^2) (float32
+    (m, n) device tensors): U phi(Sigma) V^T, the polar factor for singular
+    values in the polynomials' range.  precision "f16" or "split".  Returns
+    (Os, info) like inv_quarter_root_batched."""
+    import torch
+
+    lib = library()
+    count = len(Gs)
+    if count == 0:
+        return [], None
+    dev = Gs[0].device
+    if Os is None:
+        Os = [torch.empty_like(G) for G in Gs]
+    probs = (PolarProblem * count)()
+    for i, (G, O) in enumerate(zip(Gs, Os)):
+        probs[i] = PolarProblem(G.shape[0], G.shape[1], _ptr(G), _ld(G), _ptr(O), _ld(O))
+    code = _PRECISIONS[precision]
+    need = lib.polar_cans_batched_workspace(ctypes.addressof(probs), count, code)
+    ws = workspace or RootWorkspace()
+    buf, info = ws.get(need, count, dev)
+    if info_out is not None:
+        if info_out.numel() < 32 * count:
+            raise ValueError("info_out too small")
+        info = info_out
+    _check(lib.polar_cans_batched(ctypes.addressof(probs), count, code, _ptr(info), _ptr(buf), buf.numel(),
+                                  _stream(stream)))
+    if not return_info:
+        return Os, None
+    torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+    return Os, decode_info(info, count)
 
 
 def cans_ceilings():

@@ -17,6 +17,7 @@
 
 #include "cans.hpp"
 #include "launch.hpp"
+#include "polar.hpp"
 #include "schedule.hpp"
 
 using namespace mr;
@@ -86,12 +87,14 @@ int tiles(int64_t d, int t) { return (int)((d + t - 1) / t); }
 enum TraceClass {
   kTrSyrk, kTrApply, kTrJacobi, kTrStats, kTrBound, kTrInit, kTrNewton64, kTrNewton32, kTrConvert,
   kTrFinalize, kTrInfo, kTrNewtonX3, kTrCansBound, kTrCansInit, kTrCansP, kTrCansYZ, kTrCansFinal, kTrCansInfo,
-  kTrCount
+  kTrPolarStats, kTrPolarBound, kTrPolarInit, kTrPolarA, kTrPolarX, kTrPolarFinal, kTrPolarInfo, kTrCount
 };
 const char* const kTraceNames[kTrCount] = {"syrk_ema", "apply_f32", "jacobi", "root_stats", "root_bound",
                                            "root_init", "newton_f64", "newton_f32", "newton_convert",
                                            "root_finalize", "root_info", "newton_x3", "cans_bound",
-                                           "cans_init", "cans_p", "cans_yz", "cans_finalize", "cans_info"};
+                                           "cans_init", "cans_p", "cans_yz", "cans_finalize", "cans_info",
+                                           "polar_stats", "polar_bound", "polar_init", "polar_gram",
+                                           "polar_update", "polar_finalize", "polar_info"};
 struct TraceEntry {
   int cls;
   hipEvent_t a, b;
@@ -962,6 +965,218 @@ mr_status inv_sqrt_root_batched(const mr_root_problem* p, int32_t count, mr_dtyp
   return traced(kTrCansInfo, true, s, [&] {
     return launch_cans_info(state, partial, P.partial_stride, count, info_dev, kCansResidualRms, s);
   }, "cans info");
+}
+
+}  // extern "C"
+
+// ================================================ polar_cans_batched
+namespace {
+
+struct PolarPlan {
+  struct Cls {
+    int64_t M, N;
+    int first_slot, count;
+    size_t region_off, matrix_bytes;
+  };
+  std::vector<int> slot_problem;  // slots grouped by (M, N)
+  std::vector<Cls> classes;
+  size_t state_off = 0, partial_off = 0, total = 0;
+  int64_t partial_stride = 0;
+};
+
+PolarPlan plan_polar(const mr_polar_problem* p, int32_t count) {
+  PolarPlan P;
+  std::map<std::pair<int64_t, int64_t>, std::vector<int>> by_shape;
+  int64_t mmax = 1;
+  for (int i = 0; i < count; ++i) {
+    by_shape[{std::max(p[i].m, p[i].n), std::min(p[i].m, p[i].n)}].push_back(i);
+    mmax = std::max(mmax, p[i].m);
+  }
+  for (auto& kv : by_shape) {
+    PolarPlan::Cls c;
+    c.M = kv.first.first;
+    c.N = kv.first.second;
+    c.first_slot = (int)P.slot_problem.size();
+    c.count = (int)kv.second.size();
+    c.matrix_bytes = align256((size_t)polar_matrix_bytes(c.M, c.N));
+    for (int i : kv.second) P.slot_problem.push_back(i);
+    P.classes.push_back(c);
+  }
+  size_t off = 0;
+  P.state_off = off;
+  off = align256(off + sizeof(RootState) * (size_t)std::max(count, 1));
+  P.partial_stride = 3 * ((mmax + kFinalRows - 1) / kFinalRows);
+  P.partial_off = off;
+  off = align256(off + sizeof(double) * (size_t)P.partial_stride * (size_t)std::max(count, 1));
+  for (auto& c : P.classes) {
+    c.region_off = off;
+    off += c.matrix_bytes * (size_t)c.count;
+  }
+  P.total = off;
+  return P;
+}
+
+}  // namespace
+
+extern "C" {
+
+static mr_status validate_polar(const mr_polar_problem* p, int32_t count, int32_t precision) {
+  if (count < 0) return fail(MR_ERR_PARAM, "count %d < 0", count);
+  if (count > 0 && !p) return fail(MR_ERR_NULL, "problems is NULL");
+  if (precision != MR_CANS_F16 && precision != MR_CANS_SPLIT)
+    return fail(MR_ERR_PARAM, "precision %d is not MR_CANS_F16 or MR_CANS_SPLIT", precision);
+  for (int i = 0; i < count; ++i) {
+    const mr_polar_problem& q = p[i];
+    if (q.m < 1 || q.n < 1 || q.m > kMaxDim || q.n > kMaxDim)
+      return fail(MR_ERR_SHAPE, "problem %d: m=%lld n=%lld outside [1, %lld]", i, (long long)q.m, (long long)q.n,
+                  (long long)kMaxDim);
+    if (!q.G || !q.O) return fail(MR_ERR_NULL, "problem %d: G or O is NULL", i);
+    if (q.ldg < q.n || q.ldo < q.n) return fail(MR_ERR_STRIDE, "problem %d: ldg or ldo < n", i);
+    if (!aligned(q.G, 4) || !aligned(q.O, 4)) return fail(MR_ERR_PARAM, "problem %d: G or O misaligned", i);
+    if (overlap(range_of(q.G, q.m, q.n, q.ldg, 4), range_of(q.O, q.m, q.n, q.ldo, 4)))
+      return fail(MR_ERR_ALIAS, "problem %d: O overlaps G", i);
+  }
+  return MR_OK;
+}
+
+size_t polar_cans_batched_workspace(const mr_polar_problem* p, int32_t count, int32_t) {
+  if (!p || count <= 0) return 0;
+  for (int i = 0; i < count; ++i)
+    if (p[i].m < 1 || p[i].n < 1 || p[i].m > kMaxDim || p[i].n > kMaxDim) return 0;
+  return plan_polar(p, count).total;
+}
+
+mr_status polar_cans_batched(const mr_polar_problem* p, int32_t count, int32_t precision, mr_root_info* info_dev,
+                             void* ws, size_t ws_bytes, void* hip_stream) {
+  mr_status st = validate_polar(p, count, precision);
+  if (st != MR_OK) return st;
+  if (count == 0) return MR_OK;
+  const PolarPlan P = plan_polar(p, count);
+  if (!ws || ws_bytes < P.total || !aligned(ws, 256))
+    return fail(MR_ERR_WORKSPACE, "workspace %p of %zu bytes; need %zu bytes, 256-byte aligned", ws, ws_bytes,
+                P.total);
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  char* base = static_cast<char*>(ws);
+  RootState* state = reinterpret_cast<RootState*>(base + P.state_off);
+  double* partial = reinterpret_cast<double*>(base + P.partial_off);
+  const CansCeilings& ce = cans_ceilings();
+  double sx[kCansSteps + 1], sa[kCansSteps + 1];
+  for (int k = 0; k <= kCansSteps; ++k) {
+    sx[k] = cans_pow2_scale(std::sqrt(ce.p[k]));
+    sa[k] = cans_pow2_scale(ce.p[k]);
+  }
+  const int prec = precision == MR_CANS_SPLIT ? 3 : 1;
+
+  // per-matrix batches: 0 statistics, 1 init, 2 finalize
+  auto run_batches = [&](int kind) -> mr_status {
+    PolarBatch b;
+    memset(&b, 0, sizeof b);
+    b.state = state;
+    b.partial = partial;
+    b.partial_stride = P.partial_stride;
+    for (const auto& c : P.classes) {
+      for (int k = 0; k < c.count; ++k) {
+        const int slot = c.first_slot + k;
+        const mr_polar_problem& q = p[P.slot_problem[slot]];
+        PolarJob& J = b.job[b.njobs];
+        J.G = q.G;
+        J.ldg = q.ldg;
+        J.O = q.O;
+        J.ldo = q.ldo;
+        J.region = base + c.region_off + c.matrix_bytes * (size_t)k;
+        J.m = (int32_t)q.m;
+        J.n = (int32_t)q.n;
+        J.slot = slot;
+        J.problem = P.slot_problem[slot];
+        J.block_begin = b.total_blocks;
+        J.nblocks = kind == 1 ? tiles(q.m, 32) * tiles(q.n, 32) : tiles(q.m, kFinalRows);
+        b.total_blocks += J.nblocks;
+        ++b.njobs;
+        if (b.njobs == kMaxJobs || slot == count - 1) {
+          const int cls = kind == 0 ? kTrPolarStats : kind == 1 ? kTrPolarInit : kTrPolarFinal;
+          mr_status r = traced(cls, b.total_blocks > 0, s, [&] {
+            if (kind == 0) return launch_polar_stats(b, s);
+            if (kind == 1) return launch_polar_init(b, sx[0], s);
+            return launch_polar_finalize(b, 1.0 / sa[kCansSteps - 1], s);
+          }, "polar batch launch");
+          if (r != MR_OK) return r;
+          b.njobs = 0;
+          b.total_blocks = 0;
+        }
+      }
+    }
+    return MR_OK;
+  };
+
+  if ((st = run_batches(0)) != MR_OK) return st;
+  if ((st = traced(kTrPolarBound, true, s, [&] {
+         return launch_polar_bound(state, partial, P.partial_stride, count, 1.0 / sx[kCansSteps], s);
+       }, "polar bound launch")) != MR_OK)
+    return st;
+  if ((st = run_batches(1)) != MR_OK) return st;
+
+  struct Group {
+    std::vector<int> cls;
+    int vec;
+  };
+  std::vector<Group> groups;
+  for (const int vec : {8, 1}) {
+    Group g;
+    g.vec = vec;
+    for (int ci = 0; ci < (int)P.classes.size(); ++ci) {
+      const auto& c = P.classes[ci];
+      if (((c.M % 8 == 0 && c.N % 8 == 0) ? 8 : 1) != vec) continue;
+      g.cls.push_back(ci);
+      if ((int)g.cls.size() == kMaxClasses) {
+        groups.push_back(g);
+        g.cls.clear();
+      }
+    }
+    if (!g.cls.empty()) groups.push_back(g);
+  }
+  for (int k = 0; k < kCansSteps; ++k) {
+    const double a = kCansCoeff[k][0], b = kCansCoeff[k][1];
+    for (const int stage : {(int)kPolarA, (int)kPolarX}) {
+      for (const auto& g : groups) {
+        PolarLaunch L;
+        memset(&L, 0, sizeof L);
+        L.state = state;
+        L.stage = stage;
+        L.k = k;
+        if (stage == kPolarA) {
+          L.alpha = sa[k] / (sx[k] * sx[k]);
+        } else {
+          L.alpha = b * sx[k + 1] / (sx[k] * sa[k]);
+          L.beta = a * sx[k + 1] / sx[k];
+        }
+        for (int ci : g.cls) {
+          const auto& c = P.classes[ci];
+          PolarClass& C = L.cls[L.ncls++];
+          C.region = base + c.region_off;
+          C.matrix_bytes = (int64_t)c.matrix_bytes;
+          C.M = (int32_t)c.M;
+          C.N = (int32_t)c.N;
+          C.count = c.count;
+          C.TM = tiles(c.M, 128);
+          C.TN = tiles(c.N, 128);
+          C.U = C.TN * (C.TN + 1) / 2;
+          C.slot_begin = c.first_slot;
+          C.block_begin = L.total_blocks;
+          C.blocks_per_matrix = stage == kPolarA ? C.U : C.TM * C.TN;
+          C.nblocks = C.blocks_per_matrix * C.count;
+          L.total_blocks += round8(C.nblocks);
+        }
+        if ((st = traced(stage == kPolarA ? kTrPolarA : kTrPolarX, true, s,
+                         [&] { return launch_polar_gemm(L, g.vec, prec, s); }, "polar gemm launch")) != MR_OK)
+          return st;
+      }
+    }
+  }
+  if ((st = run_batches(2)) != MR_OK) return st;
+  // the residual of a rank-deficient G is legitimately large: never a flag
+  return traced(kTrPolarInfo, true, s, [&] {
+    return launch_cans_info(state, partial, P.partial_stride, count, info_dev, HUGE_VAL, s);
+  }, "polar info");
 }
 
 }  // extern "C"

@@ -254,3 +254,26 @@ def test_pack_helpers_roundtrip():
     assert torch.equal(B.unpack_upper(P), A)
     with pytest.raises(ValueError):
         B.packed_dim(27)
+
+
+def test_polar_validation(lib):
+    def call(probs, prec=0, ws=None, ws_bytes=0):
+        arr = (B.PolarProblem * len(probs))(*probs)
+        return lib.polar_cans_batched(ctypes.addressof(arr), len(probs), prec, None, ws, ws_bytes, None)
+
+    def pp(m, n, G=P1, ldg=None, O=P2, ldo=None):
+        return B.PolarProblem(m, n, G, ldg if ldg is not None else n, O, ldo if ldo is not None else n)
+
+    assert call([pp(8, 4)], prec=5) == 4
+    assert call([pp(0, 4)]) == 2
+    assert call([pp(8, 70000)]) == 2
+    assert call([pp(8, 4, O=0)]) == 1
+    assert call([pp(8, 4, ldg=3)]) == 3
+    assert call([pp(8, 4, ldo=3)]) == 3
+    assert call([pp(8, 4, O=P1 + 100)]) == 8
+    assert call([pp(8, 4, G=P1 + 2)]) == 4
+    assert call([pp(8, 4)]) == 5  # valid; no workspace
+    arr = (B.PolarProblem * 2)(pp(300, 100), pp(64, 200, G=P3, O=P4))
+    need = lib.polar_cans_batched_workspace(ctypes.addressof(arr), 2, 0)
+    assert need >= 4 * (3 * 300 * 100 + 100 * 100) + 4 * (3 * 200 * 64 + 64 * 64)
+    assert call([pp(300, 100), pp(64, 200, G=P3, O=P4)], ws=P5, ws_bytes=need - 1) == 5
