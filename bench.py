@@ -240,6 +240,107 @@ def bench_cans(args, torch, B):
     return 0
 
 
+POLAR_METRIC = "orthogonalised matrices/s (CANS polar, 10 steps; MoE share 64 x 3072x1536 + 64 x 1536x3072)"
+
+
+def bench_polar(args, torch, B):
+    """One polar_cans_batched call over the 128 expert gradients of the MoE
+    share (step-1 sparse-row gradients, host-drawn), timed per call with the
+    library's HIP events around each launch."""
+    from matrix_roots_amd import workloads as W
+
+    wl = W.WORKLOADS["moe"]
+    dev = torch.device("cuda:0")
+    Gs = [torch.from_numpy(W.gradient("moe", w, 1)).to(dev) for w in range(len(wl.shapes))]
+    Os = [torch.empty_like(G) for G in Gs]
+    ws = B.RootWorkspace()
+    infos = torch.empty(32 * len(Gs), dtype=torch.uint8, device=dev)
+
+    def step():
+        B.polar_cans_batched(Gs, precision=args.precision, Os=Os, workspace=ws, return_info=False, info_out=infos)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup call {i + 1}/{args.warmup} done")
+    B.trace_collect()
+    B.trace_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    B.trace_enable(False)
+    trace = B.trace_collect()
+    info = B.decode_info(infos, len(Gs))
+    assert (info["flags"] == 0).all(), info
+    ms = (t1 - t0) * 1e3 / args.steps
+    gram = update = 0.0
+    for G in Gs:
+        M, N = max(G.shape), min(G.shape)
+        gram += 10 * float(N) * (N + 1) * M  # A = X^T X, symmetric count
+        update += 10 * 2.0 * M * N * N  # X A
+    flops = {"polar_gram": gram * args.steps, "polar_update": update * args.steps}
+    mult = 3 if args.precision == "split" else 1
+    kernels = {}
+    for name, (launches, kms) in sorted(trace.items()):
+        ent = {"launches": launches, "ms_total": round(kms, 3), "ms_avg": round(kms / launches, 4)}
+        if name in flops:
+            tf = flops[name] / (kms / 1e3) / 1e12
+            ent.update({"tflops": round(tf, 2), "mfma_tflops": round(mult * tf, 2), "peak": PEAK_TFLOPS["f16"],
+                        "frac": round(mult * tf / PEAK_TFLOPS["f16"], 4)})
+        kernels[name] = ent
+    dname, dk = max(((k, v) for k, v in kernels.items() if k in flops), key=lambda kv: kv[1]["ms_total"])
+    roofline = {"bound": "mfma", "kernel": dname, "achieved": dk["mfma_tflops"], "peak": dk["peak"],
+                "unit": "TFLOP/s", "frac": dk["frac"],
+                "traffic": recorded_traffic(dname, f"polar_moe_{args.precision}", "polar"),
+                "achieved_per_launch": "algorithmic fp16 MFMA flops of the class (symmetric Gram counted once; "
+                                       "x3 for split products) / sum of its event-measured launch durations"}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        try:
+            import threadpoolctl
+
+            cores = max(int(i.get("num_threads", 1)) for i in threadpoolctl.threadpool_info()) or 1
+        except Exception:  # pragma: no cover
+            cores = len(os.sched_getaffinity(0))
+        sample = [Gs[0].cpu().numpy(), Gs[-1].cpu().numpy()]
+        c0 = time.perf_counter()
+        for _ in range(4):
+            for g in sample:
+                oracle.polar_cans(g)
+        sec = (time.perf_counter() - c0) / 8
+        cpu = {"value": round(1.0 / sec, 4), "unit": "matrices/s", "cores": cores, "kind": "oracle",
+               "sample": "E0.in (3072x1536) and E63.out (1536x3072), 4 times each (thin SVD, fp64 numpy/LAPACK)",
+               "seconds": round(8 * sec, 2)}
+        log(f"oracle: {sec:.2f}s per matrix on {cores} threads")
+    out = {
+        "metric": POLAR_METRIC,
+        "value": round(len(Gs) / (ms / 1e3), 4),
+        "unit": "matrices/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 products, f32 accumulation" if args.precision == "f16" else "split-f16 products (f32-accurate)",
+        "data": "synthetic",
+        "config": {"workload": "polar_moe", "matrices": len(Gs), "shapes": ["3072x1536", "1536x3072"],
+                   "precision": args.precision, "steps_per_matrix": 10},
+        "tflops": round((gram + update) / (ms / 1e3) / 1e12, 2),
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def recorded_traffic(kernel: str, workload: str, family: str = "quarter"):
     """HBM bytes per launch of `kernel` from the committed counter summary,
     if the kernel sources are unchanged since the counters were taken."""
@@ -275,9 +376,10 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="w1024", choices=["toy", "w1024", "w2048", "moe", "cans8192"])
+    ap.add_argument("--workload", default="w1024", choices=["toy", "w1024", "w2048", "moe", "cans8192", "polar_moe"])
     ap.add_argument("--precision", default="f16", choices=["f16", "split"],
-                    help="products of the cans8192 workload (inv_sqrt_root_batched)")
+                    help="products of the cans8192 (inv_sqrt_root_batched) and polar_moe (polar_cans_batched) "
+                         "workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--state-dtype", default="f64", choices=["f64", "f32"])
     ap.add_argument("--packed-state", action="store_true",
@@ -310,6 +412,10 @@ def main(argv=None) -> int:
         if args.calibration_copy_mib > 0:
             calibration_copies(torch, dev, args.calibration_copy_mib)
         return bench_cans(args, torch, B)
+    if args.workload == "polar_moe":
+        if args.calibration_copy_mib > 0:
+            calibration_copies(torch, dev, args.calibration_copy_mib)
+        return bench_polar(args, torch, B)
     if args.calibration_copy_mib > 0:
         calibration_copies(torch, dev, args.calibration_copy_mib)
     wl = W.WORKLOADS[args.workload]

@@ -207,3 +207,27 @@ def test_inv_sqrt_8192_batch4(torch_dev):
         print(f"8192 x4 {precision}: err {err:.2e}, residual rms {worst:.2e}")
         assert err <= tol, (precision, err)
         del Ws
+
+
+def test_polar_moe_share(torch_dev):
+    """All 128 expert gradients of the MoE share in one polar_cans_batched
+    call (as bench.py --workload polar_moe times it), both precisions: every
+    output finite and unflagged, E0.in and E63.out against the oracle within
+    the small-size tolerances (1e-2 fp16, 5e-5 split)."""
+    torch, dev = torch_dev
+    wl = W.WORKLOADS["moe"]
+    names = [s[0] for s in wl.shapes]
+    Gh = [W.gradient("moe", w, 1) for w in range(len(names))]
+    Gd = [torch.from_numpy(g).to(dev) for g in Gh]
+    samples = [names.index("E0.in"), names.index("E63.out")]
+    refs = {k: oracle.polar_cans(Gh[k].astype(np.float64))[0] for k in samples}
+    for precision, tol in (("f16", 1e-2), ("split", 5e-5)):
+        Os, info = B.polar_cans_batched(Gd, precision=precision)
+        torch.cuda.synchronize()
+        assert (info["flags"] == 0).all(), info
+        assert all(bool(torch.isfinite(O).all()) for O in Os)
+        for k in samples:
+            err = oracle.relative_frobenius(Os[k].cpu().numpy(), refs[k])
+            print(f"polar moe {precision} {names[k]}: err {err:.2e}")
+            assert err <= tol, (precision, names[k], err)
+        del Os
