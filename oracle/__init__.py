@@ -11,9 +11,11 @@ from .step import (  # noqa: F401
     NORM_NONE,
     NORM_TRACE,
     gram_ema_update,
+    hyperball_update,
     inv_quarter_root,
     inv_sqrt_root,
     left_gram,
+    momentum_ema,
     polar_cans,
     precondition_apply,
     preconditioner_step,

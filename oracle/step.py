@@ -21,6 +21,9 @@ What it computes, and where the pages define it:
 * The inverse square root of a symmetric positive definite matrix, the root
   tilderesearch, "Online KL Shampoo", computes for its preconditioner
   (sections 2.2-2.4, appendix D), as the same eigenvalue map with power -1/2.
+* The step around the preconditioner: a momentum EMA of the gradient and
+  the MuonH norm-preserving (hyperball) update of the weight
+  (marin.community, "A sphere for every matrix").
 * The polar orthogonalisation its CANS coefficients were designed for
   (section 2.3), as the odd polynomial those ten steps apply to the
   singular values (numpy.linalg.svd, LAPACK gesdd).
@@ -216,6 +219,34 @@ def polar_cans(G):
     for a, b in CANS_COEFFS:
         x = x * (a + b * x * x)
     return (U * x) @ Vt, {"scale": f2, "bound": L, "flags": 0}
+
+
+def momentum_ema(M, G, mu: float) -> np.ndarray:
+    """M <- mu M + (1 - mu) G: the momentum the preconditioned direction is
+    taken of (EMA-Gram page, "Results", compares update directions at equal
+    Grams and momentum; marin.community's MuonH notes take the momentum of
+    each matrix's gradient first).  The EMA form is a reading: its scale
+    cancels in the norm-preserving update below."""
+    return float(mu) * _f64(M) + (1.0 - float(mu)) * _f64(G)
+
+
+def hyperball_update(W, U, lr: float):
+    """The MuonH hyperball step (marin.community, "A sphere for every
+    matrix"): move W against U by lr times W's own norm, then rescale back to
+    W's original norm, with the page's 1e-10 floors on both divisors:
+
+        c = lr ||W|| / max(||U||, 1e-10),  W' = W - c U,
+        W_new = W' ||W|| / max(||W'||, 1e-10).
+
+    Norms are Frobenius norms of the whole matrix.  Returns (W_new,
+    {"w_norm", "u_norm", "new_norm"}) with new_norm = ||W'||.
+    """
+    W, U = _f64(W), _f64(U)
+    wn = float(np.sqrt(np.sum(W * W)))
+    un = float(np.sqrt(np.sum(U * U)))
+    Wp = W - float(lr) * U * (wn / max(un, 1e-10))
+    pn = float(np.sqrt(np.sum(Wp * Wp)))
+    return Wp / max(pn, 1e-10) * wn, {"w_norm": wn, "u_norm": un, "new_norm": pn}
 
 
 def precondition_apply(XL, G, XR, alpha: float = 1.0) -> np.ndarray:
