@@ -287,6 +287,55 @@ mr_status polar_cans_batched(const mr_polar_problem* problems, int32_t count, in
                              mr_root_info* info_dev, void* ws, size_t ws_bytes, void* hip_stream);
 size_t polar_cans_batched_workspace(const mr_polar_problem* problems, int32_t count, int32_t precision);
 
+/* One matrix for momentum_ema_batched: G (read) and M (updated in place),
+ * both m x n float32, ldg, ldm >= n; M must not overlap G. */
+typedef struct {
+  int64_t m, n;
+  const float* G;
+  int64_t ldg;
+  float* M;
+  int64_t ldm;
+} mr_momentum_problem;
+
+/*
+ * momentum_ema_batched -- for every problem, in place:
+ *     M <- mu * M + (1 - mu) * G      (computed in float64, stored float32)
+ * The momentum of each weight's gradient, whose preconditioned direction the
+ * optimizer applies (EMA-Gram page, section "Results", compares update
+ * directions at equal Grams and momentum; the MuonH notes of marin.community,
+ * "A sphere for every matrix", take the momentum first).  0 <= mu < 1.  One
+ * HBM-bound pass (12 bytes per element).  No workspace, no synchronisation.
+ */
+mr_status momentum_ema_batched(const mr_momentum_problem* problems, int32_t count, double mu,
+                               void* hip_stream);
+
+/* One matrix for hyperball_update_batched: W (updated in place) and U (read),
+ * both m x n float32, ldw, ldu >= n; W must not overlap U. */
+typedef struct {
+  int64_t m, n;
+  float* W;
+  int64_t ldw;
+  const float* U;
+  int64_t ldu;
+} mr_hyperball_problem;
+
+/*
+ * hyperball_update_batched -- for every problem, in place, the MuonH
+ * norm-preserving step (marin.community, "A sphere for every matrix"):
+ *     c = lr ||W|| / max(||U||, 1e-10),  W' = W - c U,
+ *     W <- W' ||W|| / max(||W'||, 1e-10)
+ * (Frobenius norms of the whole matrix), so every W keeps its norm.  Two
+ * HBM-bound passes: float64 partial sums of ||W||^2, ||U||^2 and <W, U>, then
+ * ||W'||^2 = ||W||^2 - 2 c <W, U> + c^2 ||U||^2 and the in-place update
+ * (20 bytes per element in all).  lr >= 0 and finite.  norms_dev: optional
+ * device array of 3 doubles per problem, receiving ||W||, ||U||, ||W'||.
+ * Workspace: at least hyperball_update_batched_workspace(...) bytes,
+ * 256-byte aligned.  Deterministic (fixed summation order).
+ */
+mr_status hyperball_update_batched(const mr_hyperball_problem* problems, int32_t count, double lr,
+                                   double* norms_dev, void* ws, size_t ws_bytes, void* hip_stream);
+size_t hyperball_update_batched_workspace(const mr_hyperball_problem* problems, int32_t count);
+
 /* Suprema over y0 in (0, 1] of the CANS scalar recurrence y <- y q, z <- z q,
  * q = a_k + b_k z y (y, z from y0, 1), at steps k = 0..10: the per-step
  * bounds inv_sqrt_root_batched scales its intermediates by (y: Y_k, z: Z_k,

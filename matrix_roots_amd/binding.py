@@ -40,6 +40,9 @@ EXPORTED = (
     "mr_cans_ceilings",
     "polar_cans_batched",
     "polar_cans_batched_workspace",
+    "momentum_ema_batched",
+    "hyperball_update_batched",
+    "hyperball_update_batched_workspace",
     "precondition_apply",
     "precondition_apply_workspace",
     "mr_newton_iterations",
@@ -65,6 +68,16 @@ class RootProblem(ctypes.Structure):
 class PolarProblem(ctypes.Structure):
     _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("G", ctypes.c_void_p), ("ldg", ctypes.c_int64),
                 ("O", ctypes.c_void_p), ("ldo", ctypes.c_int64)]
+
+
+class MomentumProblem(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("G", ctypes.c_void_p), ("ldg", ctypes.c_int64),
+                ("M", ctypes.c_void_p), ("ldm", ctypes.c_int64)]
+
+
+class HyperballProblem(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("W", ctypes.c_void_p), ("ldw", ctypes.c_int64),
+                ("U", ctypes.c_void_p), ("ldu", ctypes.c_int64)]
 
 
 class ApplyProblem(ctypes.Structure):
@@ -119,6 +132,12 @@ def library() -> ctypes.CDLL:
     lib.polar_cans_batched.restype = i32
     lib.polar_cans_batched_workspace.argtypes = [vp, i32, i32]
     lib.polar_cans_batched_workspace.restype = sz
+    lib.momentum_ema_batched.argtypes = [vp, i32, f64, vp]
+    lib.momentum_ema_batched.restype = i32
+    lib.hyperball_update_batched.argtypes = [vp, i32, f64, vp, vp, sz, vp]
+    lib.hyperball_update_batched.restype = i32
+    lib.hyperball_update_batched_workspace.argtypes = [vp, i32]
+    lib.hyperball_update_batched_workspace.restype = sz
     lib.precondition_apply.argtypes = [vp, i32, f32, vp, sz, vp]
     lib.precondition_apply.restype = i32
     lib.precondition_apply_workspace.argtypes = [vp, i32]
@@ -370,6 +389,47 @@ def polar_cans_batched(Gs: Sequence, precision: str = "f16", Os: Optional[Sequen
         return Os, None
     torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
     return Os, decode_info(info, count)
+
+
+def momentum_ema_batched(Gs: Sequence, Ms: Sequence, mu: float, stream=None):
+    """In place: M_i <- mu M_i + (1 - mu) G_i (float32 (m, n) device tensors)."""
+    lib = library()
+    count = len(Gs)
+    if count == 0:
+        return Ms
+    probs = (MomentumProblem * count)()
+    for i, (G, M) in enumerate(zip(Gs, Ms)):
+        if tuple(G.shape) != tuple(M.shape):
+            raise ValueError("G and M shapes differ")
+        probs[i] = MomentumProblem(G.shape[0], G.shape[1], _ptr(G), _ld(G), _ptr(M), _ld(M))
+    _check(lib.momentum_ema_batched(ctypes.addressof(probs), count, float(mu), _stream(stream)))
+    return Ms
+
+
+def hyperball_update_batched(Ws: Sequence, Us: Sequence, lr: float, return_norms: bool = False, stream=None):
+    """In place, the MuonH norm-preserving step: W_i <- (W_i - c U_i) ||W_i|| /
+    ||W_i - c U_i||, c = lr ||W_i|| / ||U_i||.  With return_norms, also a
+    (count, 3) float64 device tensor of ||W||, ||U||, ||W - c U||."""
+    import torch
+
+    lib = library()
+    count = len(Ws)
+    if count == 0:
+        return None
+    dev = Ws[0].device
+    probs = (HyperballProblem * count)()
+    for i, (W, U) in enumerate(zip(Ws, Us)):
+        if tuple(W.shape) != tuple(U.shape):
+            raise ValueError("W and U shapes differ")
+        probs[i] = HyperballProblem(W.shape[0], W.shape[1], _ptr(W), _ld(W), _ptr(U), _ld(U))
+    need = lib.hyperball_update_batched_workspace(ctypes.addressof(probs), count)
+    ws = _workspace(need, dev)
+    if ws is not None and stream is not None:
+        ws.record_stream(stream)
+    norms = torch.empty(count, 3, dtype=torch.float64, device=dev) if return_norms else None
+    _check(lib.hyperball_update_batched(ctypes.addressof(probs), count, float(lr), _ptr(norms), _ptr(ws), need,
+                                        _stream(stream)))
+    return norms
 
 
 def cans_ceilings():

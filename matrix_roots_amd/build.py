@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmatrix_roots.so")
-SOURCES = ["abi.cpp", "gram.hip", "apply.hip", "root.hip", "jacobi.hip", "cans.hip", "polar.hip"]
+SOURCES = ["abi.cpp", "gram.hip", "apply.hip", "root.hip", "jacobi.hip", "cans.hip", "polar.hip", "step.hip"]
 ARCH = "gfx950"
 
 # Packed float32 VALU ops are kept out of every code object.

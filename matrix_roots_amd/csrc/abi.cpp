@@ -18,6 +18,7 @@
 #include "cans.hpp"
 #include "launch.hpp"
 #include "polar.hpp"
+#include "step.hpp"
 #include "schedule.hpp"
 
 using namespace mr;
@@ -87,14 +88,16 @@ int tiles(int64_t d, int t) { return (int)((d + t - 1) / t); }
 enum TraceClass {
   kTrSyrk, kTrApply, kTrJacobi, kTrStats, kTrBound, kTrInit, kTrNewton64, kTrNewton32, kTrConvert,
   kTrFinalize, kTrInfo, kTrNewtonX3, kTrCansBound, kTrCansInit, kTrCansP, kTrCansYZ, kTrCansFinal, kTrCansInfo,
-  kTrPolarStats, kTrPolarBound, kTrPolarInit, kTrPolarA, kTrPolarX, kTrPolarFinal, kTrPolarInfo, kTrCount
+  kTrPolarStats, kTrPolarBound, kTrPolarInit, kTrPolarA, kTrPolarX, kTrPolarFinal, kTrPolarInfo,
+  kTrMomentum, kTrHyperReduce, kTrHyperUpdate, kTrCount
 };
 const char* const kTraceNames[kTrCount] = {"syrk_ema", "apply_f32", "jacobi", "root_stats", "root_bound",
                                            "root_init", "newton_f64", "newton_f32", "newton_convert",
                                            "root_finalize", "root_info", "newton_x3", "cans_bound",
                                            "cans_init", "cans_p", "cans_yz", "cans_finalize", "cans_info",
                                            "polar_stats", "polar_bound", "polar_init", "polar_gram",
-                                           "polar_update", "polar_finalize", "polar_info"};
+                                           "polar_update", "polar_finalize", "polar_info", "momentum",
+                                           "hyperball_reduce", "hyperball_update"};
 struct TraceEntry {
   int cls;
   hipEvent_t a, b;
@@ -1177,6 +1180,148 @@ mr_status polar_cans_batched(const mr_polar_problem* p, int32_t count, int32_t p
   return traced(kTrPolarInfo, true, s, [&] {
     return launch_cans_info(state, partial, P.partial_stride, count, info_dev, HUGE_VAL, s);
   }, "polar info");
+}
+
+}  // extern "C"
+
+// ================================================ momentum / hyperball
+namespace {
+
+// Validation shared by both streaming entry points: `out` is updated in
+// place, `in` is read; m x n float32 each.
+mr_status validate_stream(int i, int64_t m, int64_t n, const void* in, int64_t ld_in, const void* out, int64_t ld_out,
+                          const char* in_name, const char* out_name) {
+  if (m < 1 || n < 1 || m > kMaxDim || n > kMaxDim)
+    return fail(MR_ERR_SHAPE, "problem %d: m=%lld n=%lld outside [1, %lld]", i, (long long)m, (long long)n,
+                (long long)kMaxDim);
+  if (!in || !out) return fail(MR_ERR_NULL, "problem %d: %s or %s is NULL", i, in_name, out_name);
+  if (ld_in < n || ld_out < n) return fail(MR_ERR_STRIDE, "problem %d: a leading dimension < n", i);
+  if (!aligned(in, 4) || !aligned(out, 4)) return fail(MR_ERR_PARAM, "problem %d: %s or %s misaligned", i, in_name, out_name);
+  if (overlap(range_of(in, m, n, ld_in, 4), range_of(out, m, n, ld_out, 4)))
+    return fail(MR_ERR_ALIAS, "problem %d: %s overlaps %s", i, out_name, in_name);
+  return MR_OK;
+}
+
+bool stream_vec4(int64_t n, const void* in, int64_t ld_in, const void* out, int64_t ld_out) {
+  return n % 4 == 0 && ld_in % 4 == 0 && ld_out % 4 == 0 && aligned(in, 16) && aligned(out, 16);
+}
+
+int64_t stream_blocks(int64_t m, int64_t n) {
+  const int64_t r = stream_rows_per_block(m, n);
+  return (m + r - 1) / r;
+}
+
+// Run `launch(batch, vec)` over the problems, one launch per 16 of one width.
+template <class Get, class Launch>
+mr_status run_stream(int32_t count, Get&& get, double* partial, int64_t stride, Launch&& launch) {
+  for (const int vec : {4, 1}) {
+    StreamBatch b;
+    memset(&b, 0, sizeof b);
+    b.partial = partial;
+    b.partial_stride = stride;
+    for (int i = 0; i < count; ++i) {
+      StreamJob J;
+      get(i, J);
+      const bool v4 = stream_vec4(J.n, J.in, J.ld_in, J.inout, J.ld_inout);
+      if ((vec == 4) != v4) continue;
+      J.rows_per_block = stream_rows_per_block(J.m, J.n);
+      J.nblocks = (int32_t)stream_blocks(J.m, J.n);
+      J.block_begin = b.total_blocks;
+      J.slot = i;
+      J.problem = i;
+      b.job[b.njobs++] = J;
+      b.total_blocks += J.nblocks;
+      if (b.njobs == kMaxJobs) {
+        mr_status r = launch(b, vec);
+        if (r != MR_OK) return r;
+        b.njobs = 0;
+        b.total_blocks = 0;
+      }
+    }
+    if (b.njobs > 0) {
+      mr_status r = launch(b, vec);
+      if (r != MR_OK) return r;
+    }
+  }
+  return MR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mr_status momentum_ema_batched(const mr_momentum_problem* p, int32_t count, double mu, void* hip_stream) {
+  if (count < 0) return fail(MR_ERR_PARAM, "count %d < 0", count);
+  if (count > 0 && !p) return fail(MR_ERR_NULL, "problems is NULL");
+  if (!(mu >= 0.0 && mu < 1.0)) return fail(MR_ERR_PARAM, "mu %g not in [0, 1)", mu);
+  for (int i = 0; i < count; ++i) {
+    mr_status st = validate_stream(i, p[i].m, p[i].n, p[i].G, p[i].ldg, p[i].M, p[i].ldm, "G", "M");
+    if (st != MR_OK) return st;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  return run_stream(
+      count,
+      [&](int i, StreamJob& J) {
+        memset(&J, 0, sizeof J);
+        J.in = p[i].G;
+        J.ld_in = p[i].ldg;
+        J.inout = p[i].M;
+        J.ld_inout = p[i].ldm;
+        J.m = (int32_t)p[i].m;
+        J.n = (int32_t)p[i].n;
+      },
+      nullptr, 0,
+      [&](const StreamBatch& b, int vec) {
+        return traced(kTrMomentum, b.total_blocks > 0, s, [&] { return launch_momentum(b, vec, mu, s); },
+                      "momentum launch");
+      });
+}
+
+size_t hyperball_update_batched_workspace(const mr_hyperball_problem* p, int32_t count) {
+  if (!p || count <= 0) return 0;
+  int64_t most = 1;
+  for (int i = 0; i < count; ++i) {
+    if (p[i].m < 1 || p[i].n < 1 || p[i].m > kMaxDim || p[i].n > kMaxDim) return 0;
+    most = std::max(most, stream_blocks(p[i].m, p[i].n));
+  }
+  return align256(sizeof(double) * 3 * (size_t)most * (size_t)count);
+}
+
+mr_status hyperball_update_batched(const mr_hyperball_problem* p, int32_t count, double lr, double* norms_dev,
+                                   void* ws, size_t ws_bytes, void* hip_stream) {
+  if (count < 0) return fail(MR_ERR_PARAM, "count %d < 0", count);
+  if (count > 0 && !p) return fail(MR_ERR_NULL, "problems is NULL");
+  if (!(lr >= 0.0) || !std::isfinite(lr)) return fail(MR_ERR_PARAM, "lr %g must be >= 0 and finite", lr);
+  for (int i = 0; i < count; ++i) {
+    mr_status st = validate_stream(i, p[i].m, p[i].n, p[i].U, p[i].ldu, p[i].W, p[i].ldw, "U", "W");
+    if (st != MR_OK) return st;
+  }
+  if (count == 0) return MR_OK;
+  const size_t need = hyperball_update_batched_workspace(p, count);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(MR_ERR_WORKSPACE, "workspace %p of %zu bytes; need %zu bytes, 256-byte aligned", ws, ws_bytes, need);
+  int64_t most = 1;
+  for (int i = 0; i < count; ++i) most = std::max(most, stream_blocks(p[i].m, p[i].n));
+  double* partial = static_cast<double*>(ws);
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  auto get = [&](int i, StreamJob& J) {
+    memset(&J, 0, sizeof J);
+    J.in = p[i].U;
+    J.ld_in = p[i].ldu;
+    J.inout = p[i].W;
+    J.ld_inout = p[i].ldw;
+    J.m = (int32_t)p[i].m;
+    J.n = (int32_t)p[i].n;
+  };
+  mr_status st = run_stream(count, get, partial, 3 * most, [&](const StreamBatch& b, int vec) {
+    return traced(kTrHyperReduce, b.total_blocks > 0, s, [&] { return launch_hyperball_reduce(b, vec, s); },
+                  "hyperball reduce launch");
+  });
+  if (st != MR_OK) return st;
+  return run_stream(count, get, partial, 3 * most, [&](const StreamBatch& b, int vec) {
+    return traced(kTrHyperUpdate, b.total_blocks > 0, s,
+                  [&] { return launch_hyperball_update(b, vec, lr, norms_dev, s); }, "hyperball update launch");
+  });
 }
 
 }  // extern "C"

@@ -277,3 +277,28 @@ def test_polar_validation(lib):
     need = lib.polar_cans_batched_workspace(ctypes.addressof(arr), 2, 0)
     assert need >= 4 * (3 * 300 * 100 + 100 * 100) + 4 * (3 * 200 * 64 + 64 * 64)
     assert call([pp(300, 100), pp(64, 200, G=P3, O=P4)], ws=P5, ws_bytes=need - 1) == 5
+
+
+def test_momentum_and_hyperball_validation(lib):
+    def mom(probs, mu=0.9):
+        arr = (B.MomentumProblem * len(probs))(*probs)
+        return lib.momentum_ema_batched(ctypes.addressof(arr), len(probs), mu, None)
+
+    def hyp(probs, lr=0.1, ws=None, ws_bytes=0):
+        arr = (B.HyperballProblem * len(probs))(*probs)
+        return lib.hyperball_update_batched(ctypes.addressof(arr), len(probs), lr, None, ws, ws_bytes, None)
+
+    assert mom([B.MomentumProblem(4, 8, P1, 8, P2, 8)], mu=1.0) == 4
+    assert mom([B.MomentumProblem(4, 8, P1, 8, P2, 8)], mu=-0.1) == 4
+    assert mom([B.MomentumProblem(0, 8, P1, 8, P2, 8)]) == 2
+    assert mom([B.MomentumProblem(4, 8, 0, 8, P2, 8)]) == 1
+    assert mom([B.MomentumProblem(4, 8, P1, 7, P2, 8)]) == 3
+    assert mom([B.MomentumProblem(4, 8, P1, 8, P1 + 64, 8)]) == 8
+    assert hyp([B.HyperballProblem(4, 8, P1, 8, P2, 8)], lr=float("inf")) == 4
+    assert hyp([B.HyperballProblem(4, 8, P1, 8, P2, 8)], lr=-1.0) == 4
+    assert hyp([B.HyperballProblem(4, 8, P1, 8, P1 + 4, 8)]) == 8
+    assert hyp([B.HyperballProblem(4, 8, P1, 8, P2, 8)]) == 5  # valid; no workspace
+    arr = (B.HyperballProblem * 2)(B.HyperballProblem(4096, 1024, P1, 1024, P2, 1024),
+                                   B.HyperballProblem(3, 5, P3, 5, P4, 5))
+    need = lib.hyperball_update_batched_workspace(ctypes.addressof(arr), 2)
+    assert need >= 3 * 8 * 512 * 2  # 512 workgroups of 8 rows for the 4096 x 1024 matrix
