@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6, "f16": 2500.0}  # MI355X dense MFMA (vendor figures)
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E (vendor figure)
 # kernel class -> arithmetic whose peak bounds it
 CLASS_PREC = {"newton_f64": "f64", "syrk_ema": "f64", "newton_f32": "f32", "apply_f32": "f32", "newton_x3": "f16"}
 METRIC = "preconditioned matrix updates/sec + TFLOP/s as % fp32 MFMA peak, d=1024–4096"
@@ -382,6 +383,9 @@ def main(argv=None) -> int:
                          "workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--state-dtype", default="f64", choices=["f64", "f32"])
+    ap.add_argument("--optimizer-step", action="store_true",
+                    help="time the whole optimizer step: momentum EMA, Gram EMA, roots, apply to the momentum, "
+                         "hyperball update of the weights")
     ap.add_argument("--packed-state", action="store_true",
                     help="keep the Gram states packed (upper triangle by rows, d(d+1)/2 elements)")
     ap.add_argument("--gradients", default="auto", choices=["auto", "host", "device"],
@@ -448,12 +452,20 @@ def main(argv=None) -> int:
     total = args.warmup + args.steps
     infos = [torch.empty(32 * 2 * nw, dtype=torch.uint8, device=dev) for _ in range(total)]
 
+    if args.optimizer_step:
+        Ms = [torch.zeros(m, n, dtype=torch.float32, device=dev) for m, n in shapes]
+        Wts = [torch.randn(m, n, dtype=torch.float32, device=dev) / (m ** 0.5) for m, n in shapes]
+
     def step(i):
         G = grads[i % wl.steps]
+        if args.optimizer_step:
+            B.momentum_ema_batched(G, Ms, 0.9)
         B.gram_ema_update(G, Ls, Rs, wl.beta)
         B.inv_quarter_root_batched(Ls + Rs, wl.eps, normalize=wl.normalize, Xs=Xs, workspace=ws,
                                    return_info=False, info_out=infos[i])
-        B.precondition_apply(Xs[:nw], G, Xs[nw:], Us=Us)
+        B.precondition_apply(Xs[:nw], Ms if args.optimizer_step else G, Xs[nw:], Us=Us)
+        if args.optimizer_step:
+            B.hyperball_update_batched(Wts, Us, 0.02)
 
     for i in range(args.warmup):
         step(i)
@@ -492,11 +504,16 @@ def main(argv=None) -> int:
     apply_f = sum(2.0 * m * n * (m + n) for m, n in shapes) * args.steps
     step_flops = (f64 + f32 + syrk + apply_f) / args.steps
 
+    elems = sum(m * n for m, n in shapes) * args.steps
+    stream_bytes = {"momentum": 12 * elems, "hyperball_reduce": 8 * elems, "hyperball_update": 12 * elems}
     kernels = {}
     for name, (launches, ms) in sorted(trace.items()):
         flops = {"newton_f64": f64, "newton_f32": f32, "newton_x3": f32, "syrk_ema": syrk,
                  "apply_f32": apply_f}.get(name)
         ent = {"launches": launches, "ms_total": round(ms, 3), "ms_avg": round(ms / launches, 4)}
+        if name in stream_bytes:
+            gbs = stream_bytes[name] / (ms / 1e3) / 1e9
+            ent.update({"gb_per_s": round(gbs, 1), "peak_gb_per_s": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4)})
         if flops:
             prec = CLASS_PREC[name]
             tf = flops / (ms / 1e3) / 1e12
@@ -541,7 +558,8 @@ def main(argv=None) -> int:
         "config": {"workload": args.workload, "weights": nw, "grams_per_step": 2 * nw,
                    "shapes": sorted({f"{m}x{n}" for m, n in shapes}), "beta": wl.beta, "eps": wl.eps,
                    "normalize": wl.normalize, "state_dtype": args.state_dtype, "gradients": gen,
-                   "state_layout": "packed" if args.packed_state else "full", "state_gb": round(state_bytes / 1e9, 3)},
+                   "state_layout": "packed" if args.packed_state else "full", "state_gb": round(state_bytes / 1e9, 3),
+                   "optimizer_step": bool(args.optimizer_step)},
         "tflops": round(step_flops / (ms_per_step / 1e3) / 1e12, 2),
         "pct_fp32_mfma_peak": round(100 * step_flops / (ms_per_step / 1e3) / 1e12 / PEAK_TFLOPS["f32"], 2),
         "newton_iters": {"min": kmin, "max": kmax},

@@ -304,7 +304,8 @@ typedef struct {
  * optimizer applies (EMA-Gram page, section "Results", compares update
  * directions at equal Grams and momentum; the MuonH notes of marin.community,
  * "A sphere for every matrix", take the momentum first).  0 <= mu < 1.  One
- * HBM-bound pass (12 bytes per element).  No workspace, no synchronisation.
+ * HBM-bound pass (12 bytes per element; up to 48 matrices per launch).  No
+ * workspace, no synchronisation.
  */
 mr_status momentum_ema_batched(const mr_momentum_problem* problems, int32_t count, double mu,
                                void* hip_stream);

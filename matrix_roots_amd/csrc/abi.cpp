@@ -1231,7 +1231,7 @@ mr_status run_stream(int32_t count, Get&& get, double* partial, int64_t stride, 
       J.problem = i;
       b.job[b.njobs++] = J;
       b.total_blocks += J.nblocks;
-      if (b.njobs == kMaxJobs) {
+      if (b.njobs == kMaxStreamJobs) {
         mr_status r = launch(b, vec);
         if (r != MR_OK) return r;
         b.njobs = 0;

@@ -20,8 +20,12 @@ struct StreamJob {
   int32_t problem;               // index in the caller's problem array
   int32_t pad;
 };
+// Up to 48 jobs per launch (2.7 KB of kernel arguments): a whole
+// transformer block stack's weights in one HBM-bound pass instead of several
+// short launches that each pay the ramp-up and tail.
+constexpr int kMaxStreamJobs = 48;
 struct StreamBatch {
-  StreamJob job[kMaxJobs];
+  StreamJob job[kMaxStreamJobs];
   double* partial;  // hyperball: 3 doubles per workgroup, partial_stride per slot
   int64_t partial_stride;
   int32_t njobs, total_blocks;

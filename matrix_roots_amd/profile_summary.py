@@ -31,6 +31,7 @@ KERNEL_SOURCES = {
                 "csrc/root.hip", "csrc/gram.hip", "csrc/apply.hip"),
     "cans": ("csrc/gemm_core.hpp", "csrc/gemm_h16.hpp", "csrc/mr_common.hpp", "csrc/launch.hpp", "csrc/cans.hpp",
              "csrc/cans.hip"),
+    "step": ("csrc/mr_common.hpp", "csrc/launch.hpp", "csrc/step.hpp", "csrc/step.hip"),
     "polar": ("csrc/gemm_core.hpp", "csrc/gemm_h16.hpp", "csrc/mr_common.hpp", "csrc/launch.hpp", "csrc/cans.hpp",
               "csrc/polar.hpp", "csrc/polar.hip"),
 }
