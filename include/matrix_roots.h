@@ -173,7 +173,7 @@ size_t gram_ema_update_workspace(const mr_gram_problem* problems, int32_t count,
  *        M0 = (A/s + eps I)/c, X0 = I, T = (5 I - M)/4, X <- X T, M <- T^4 M,
  *    X = c^(-1/4) X_K, with M scaled by 1/s_t before each step (per-step
  *    scales from the spectrum bounds, see mr_newton_schedule), run in float64
- *    while the smallest eigenvalue of M is below 2e-3, then with float32
+ *    while the smallest eigenvalue of M is below 5e-4, then with float32
  *    storage on the fp16 matrix cores with split operands (x = hi + 2^-11 lo,
  *    three products per product, float32 accumulation: about 2^-22 relative
  *    error per product).  The GEMM-only

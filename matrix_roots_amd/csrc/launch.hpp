@@ -19,7 +19,7 @@ constexpr int kMaxClasses = 8;
 constexpr int kJacobiMaxD = 128;
 constexpr int kStatsRows = 32;       // rows of A per statistics workgroup (one 32-row tile stripe)
 constexpr int kFinalRows = 8;        // rows of X per finalize workgroup
-constexpr double kSwitchM = 2e-3;    // float64 -> float32 once the eigenvalue floor reaches this
+constexpr double kSwitchM = 5e-4;    // float64 -> float32 once the eigenvalue floor reaches this
 constexpr double kNewtonTol = 1e-6;  // stop once 1 - m_K <= this (scalar recurrence)
 constexpr double kBoundSafety = 1.01;
 

@@ -26,7 +26,8 @@
 namespace mr {
 
 constexpr int kMaxNewtonIters = 100;
-constexpr double kScaleCap64 = 4.0;  // cap on u/s while steps run in float64
+constexpr double kScaleCap64 = 4.8;  // cap on u/s while steps run in float64 (top-eigenvalue
+                                     // errors grow ~95x per step there: harmless in float64)
 constexpr double kScaleCap32 = 3.0;  // ... and in float32 (errors in the top
                                      // eigenvalues grow ~|1 - 4x/(5-x)| per step)
 
