@@ -25,8 +25,10 @@ __global__ __launch_bounds__(256, 2) void f32_nt_kernel(const F32Batch batch) {
   const F32Job& J = batch.job[jx];
   const int tile = (int)xcd_remap(b - J.block_begin, round8(J.nblocks));
   if (tile >= J.nblocks) return;
-  const int m0 = (tile / J.tiles_n) * F32Tile::BM;
-  const int n0 = (tile % J.tiles_n) * F32Tile::BN;
+  int ti, tj;
+  full_tile_grouped(tile, (J.M + F32Tile::BM - 1) / F32Tile::BM, J.tiles_n, ti, tj);
+  const int m0 = ti * F32Tile::BM;
+  const int n0 = tj * F32Tile::BN;
 
   v16f acc[2][2];
   f32_nt_tile<VEC>(J.A, J.lda, J.B, J.ldb, J.M, J.N, J.K, m0, n0, smem, acc);

@@ -183,11 +183,10 @@ __global__ __launch_bounds__(256, 2) void cans_gemm_kernel(const CansLaunch L) {
   constexpr bool full = FULL;
   int job = 0, ti, tj;
   if (full) {
-    ti = rem / C.T;
-    tj = rem % C.T;
+    full_tile_grouped(rem, C.T, C.T, ti, tj);
   } else {
     job = L.stage == kCansYZ ? rem / C.U : (L.stage == kCansZ ? 1 : 0);
-    upper_tile(rem % C.U, C.T, ti, tj);
+    upper_tile_grouped(rem % C.U, C.T, ti, tj);
   }
   // operands (C = A B^T), output, and the a_k term's input
   Split A, Bm, Out, Cin;

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256, 2) void syrk_ema_kernel(const SyrkBatch batch)
   const int local = (int)xcd_remap(b - J.block_begin, round8(ntiles));
   if (local >= ntiles) return;
   int ti, tj;
-  upper_tile(local, J.T, ti, tj);
+  upper_tile_grouped(local, J.T, ti, tj);
   const int m0 = ti * F64Tile::BM, n0 = tj * F64Tile::BN;
 
   v4d acc[4][4];

@@ -108,6 +108,56 @@ __device__ __forceinline__ double sym_tile_value(bool packed, int bi, int bj, in
   return 0.5 * (ta[r][c] + tb[c][r]);
 }
 
+// L2-friendly tile orders.  A launch keeps ~64 output tiles per XCD in
+// flight (32 CUs x 2 workgroups), and tiles advance through K at the same
+// pace, so what decides the operand traffic is how many distinct operand
+// panels one window of consecutive tiles touches.  Row-major order over a
+// 32-tile-wide grid touches ~2 row panels and ~32 column panels per window
+// (each column panel chunk used about twice before it leaves L2); bands of
+// G tile rows walked column by column touch ~G + G panels per G*G tiles.
+// G = 1 is the row-major order.
+#ifndef MR_TILE_GROUP
+#define MR_TILE_GROUP 8
+#endif
+
+// Tile u of the upper triangle (ti <= tj) of a T x T grid, in bands of
+// MR_TILE_GROUP tile rows, each band column by column.
+__device__ __forceinline__ void upper_tile_grouped(int u, int T, int& ti, int& tj) {
+  constexpr int G = MR_TILE_GROUP;
+  int b0 = 0;
+  while (true) {
+    const int h = T - b0 < G ? T - b0 : G;
+    const int tri = h * (h + 1) / 2;  // columns b0 .. b0+h-1 hold 1 .. h tiles of the band
+    const int total = tri + (T - b0 - h) * h;
+    if (u < total) {
+      if (u < tri) {
+        int c = 0;
+        while ((c + 1) * (c + 2) / 2 <= u) ++c;
+        tj = b0 + c;
+        ti = b0 + (u - c * (c + 1) / 2);
+      } else {
+        const int v = u - tri;
+        tj = b0 + h + v / h;
+        ti = b0 + v % h;
+      }
+      return;
+    }
+    u -= total;
+    b0 += G;
+  }
+}
+
+// Tile u of a full TM x TN grid, in bands of MR_TILE_GROUP tile rows, each
+// band column by column.
+__device__ __forceinline__ void full_tile_grouped(int u, int TM, int TN, int& ti, int& tj) {
+  constexpr int G = MR_TILE_GROUP;
+  const int b0 = (u / (G * TN)) * G;
+  const int h = TM - b0 < G ? TM - b0 : G;
+  const int v = u - b0 * TN;
+  tj = v / h;
+  ti = b0 + v % h;
+}
+
 // Upper-triangle tile u (row-major over ti <= tj) of a T x T tile grid.
 __device__ __forceinline__ void upper_tile(int u, int T, int& ti, int& tj) {
   // rows ti hold T - ti tiles; walk the rows (T <= 128 in practice).

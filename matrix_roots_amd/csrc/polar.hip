@@ -191,8 +191,7 @@ __global__ __launch_bounds__(256, 2) void polar_gemm_kernel(const PolarLaunch L)
   int rows, cols, K;
   int64_t lda, ldb;
   if (FULL) {
-    ti = rem / C.TN;
-    tj = rem % C.TN;
+    full_tile_grouped(rem, C.TM, C.TN, ti, tj);
     Aop = polar_buf(region, M, N, k & 1);
     Bop = polar_buf(region, M, N, 3);
     Out = polar_buf(region, M, N, (k + 1) & 1);
@@ -202,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void polar_gemm_kernel(const PolarLaunch L)
     lda = N;
     ldb = N;
   } else {
-    upper_tile(rem, C.TN, ti, tj);
+    upper_tile_grouped(rem, C.TN, ti, tj);
     Aop = Bop = polar_buf(region, M, N, 2);
     Out = polar_buf(region, M, N, 3);
     rows = cols = N;

@@ -359,7 +359,7 @@ __device__ __forceinline__ StageJob stage_job(const NewtonLaunch& L, int kind) {
   const int mat = local / C.blocks_per_matrix;
   const int rem = local % C.blocks_per_matrix;
   s.job = L.job_only >= 0 ? L.job_only : rem / C.U;
-  upper_tile(rem % C.U, C.T, s.ti, s.tj);
+  upper_tile_grouped(rem % C.U, C.T, s.ti, s.tj);
   s.d = C.d;
   s.region = C.region + (int64_t)mat * C.matrix_bytes;
   const int slot = C.slot_begin + mat;
