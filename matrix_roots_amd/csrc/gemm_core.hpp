@@ -195,8 +195,11 @@ __device__ __forceinline__ void f32_nt_tile(const float* __restrict__ A, int64_t
 #ifndef MR_X3_DBUF
 #define MR_X3_DBUF 1
 #endif
+#ifndef MR_X3_PAD
+#define MR_X3_PAD 8
+#endif
 struct X3Tile {
-  static constexpr int BM = 128, BN = 128, BK = MR_X3_BK, PAD = 8, LDW = BK + PAD;  // halves per LDS row
+  static constexpr int BM = 128, BN = 128, BK = MR_X3_BK, PAD = MR_X3_PAD, LDW = BK + PAD;  // halves per LDS row
   static constexpr int THREADS = 256;
   static constexpr bool DBUF = MR_X3_DBUF != 0;
   static constexpr int ARR = BM * LDW;  // halves per array (A_hi, A_lo, B_hi, B_lo)
@@ -215,6 +218,26 @@ __device__ __forceinline__ void split_f32(float x, _Float16& h, _Float16& l) {
 }
 __device__ __forceinline__ float join_f32(_Float16 h, _Float16 l) { return (float)h + (float)l * (1.0f / 2048.0f); }
 
+// Which (row, 8-half group) of a chunk the thread-slot idx moves.  LDS
+// serves 16-byte accesses 16 lanes per cycle over 64 four-byte banks; a
+// row is LDW halves long (80 bytes for BK = 32: 20 banks), so four lanes per
+// row on four consecutive rows overlap on 12 banks (rows r and r+3) and each
+// store takes two cycles.  With MR_LDS_SWZ the 16 lanes of a cycle take rows
+// r, r+4, r+8, r+12, whose 16-bank spans start 0, 16, 32, 48 banks apart:
+// conflict-free stores, and each row's 64 bytes still come from four
+// consecutive lanes.  The fragment reads (16 consecutive rows, one k group)
+// are conflict-free either way.
+__device__ __forceinline__ void x3_slot(int idx, int& row, int& grp) {
+#if MR_LDS_SWZ
+  const int g = idx >> 4, q = idx & 15;
+  row = 16 * (g >> 2) + (g & 3) + 4 * (q >> 2);
+  grp = q & 3;
+#else
+  row = idx >> 2;
+  grp = idx & 3;
+#endif
+}
+
 // Loads a BM x BK chunk of a K-contiguous split operand.  VEC = 8 (16-byte
 // loads; needs ld and K multiples of 8 and 16-byte aligned arrays) or 1.
 template <int VEC>
@@ -222,13 +245,15 @@ struct SplitLoader {
   static constexpr int BK = X3Tile::BK;
   static constexpr int PER = (X3Tile::BM * BK) / (X3Tile::THREADS * 8);  // groups of 8 halves
   static constexpr int GPR = BK / 8;
+  static_assert(GPR == 4, "x3_slot assumes four 8-half groups per row");
   v8h rh[PER], rl[PER];
 
   __device__ __forceinline__ void load(SplitRef P, int64_t ld, int rows, int K, int r0, int k0, int tid) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int idx = tid + p * X3Tile::THREADS;
-      const int gr = r0 + idx / GPR, gk = k0 + (idx % GPR) * 8;
+      int row, grp;
+      x3_slot(tid + p * X3Tile::THREADS, row, grp);
+      const int gr = r0 + row, gk = k0 + grp * 8;
       const int64_t off = (int64_t)gr * ld + gk;
       if constexpr (VEC == 8) {
         v8h h = {}, l = {};
@@ -251,8 +276,9 @@ struct SplitLoader {
   __device__ __forceinline__ void store(_Float16* __restrict__ hi, _Float16* __restrict__ lo, int tid) const {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int idx = tid + p * X3Tile::THREADS;
-      const int off = (idx / GPR) * X3Tile::LDW + (idx % GPR) * 8;
+      int row, grp;
+      x3_slot(tid + p * X3Tile::THREADS, row, grp);
+      const int off = row * X3Tile::LDW + grp * 8;
       *reinterpret_cast<v8h*>(hi + off) = rh[p];
       *reinterpret_cast<v8h*>(lo + off) = rl[p];
     }
@@ -379,8 +405,11 @@ __device__ __forceinline__ void f32_for_each(const v16f (&acc)[2][2], F&& f) {
 #define MR_F64_DBUF 1
 #endif
 
+#ifndef MR_F64_PAD
+#define MR_F64_PAD 2
+#endif
 struct F64Tile {
-  static constexpr int BM = 128, BN = 128, BK = MR_F64_BK, PAD = 2, LDW = BK + PAD;
+  static constexpr int BM = 128, BN = 128, BK = MR_F64_BK, PAD = MR_F64_PAD, LDW = BK + PAD;
   static constexpr int THREADS = 256;
   static constexpr bool DBUF = MR_F64_DBUF != 0;
   static constexpr int STAGE = (BM + BN) * LDW;  // doubles per LDS stage (A then B)

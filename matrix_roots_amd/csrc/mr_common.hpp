@@ -16,6 +16,12 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+
+// Conflict-free LDS store order of the fp16 tile loaders (gemm_core.hpp,
+// gemm_h16.hpp); 0 keeps the row-major order.
+#ifndef MR_LDS_SWZ
+#define MR_LDS_SWZ 1
+#endif
 constexpr int kNumXcd = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
 
 // --------------------------------------------------------------------------
