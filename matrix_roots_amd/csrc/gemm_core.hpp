@@ -218,26 +218,6 @@ __device__ __forceinline__ void split_f32(float x, _Float16& h, _Float16& l) {
 }
 __device__ __forceinline__ float join_f32(_Float16 h, _Float16 l) { return (float)h + (float)l * (1.0f / 2048.0f); }
 
-// Which (row, 8-half group) of a chunk the thread-slot idx moves.  LDS
-// serves 16-byte accesses 16 lanes per cycle over 64 four-byte banks; a
-// row is LDW halves long (80 bytes for BK = 32: 20 banks), so four lanes per
-// row on four consecutive rows overlap on 12 banks (rows r and r+3) and each
-// store takes two cycles.  With MR_LDS_SWZ the 16 lanes of a cycle take rows
-// r, r+4, r+8, r+12, whose 16-bank spans start 0, 16, 32, 48 banks apart:
-// conflict-free stores, and each row's 64 bytes still come from four
-// consecutive lanes.  The fragment reads (16 consecutive rows, one k group)
-// are conflict-free either way.
-__device__ __forceinline__ void x3_slot(int idx, int& row, int& grp) {
-#if MR_LDS_SWZ
-  const int g = idx >> 4, q = idx & 15;
-  row = 16 * (g >> 2) + (g & 3) + 4 * (q >> 2);
-  grp = q & 3;
-#else
-  row = idx >> 2;
-  grp = idx & 3;
-#endif
-}
-
 // Loads a BM x BK chunk of a K-contiguous split operand.  VEC = 8 (16-byte
 // loads; needs ld and K multiples of 8 and 16-byte aligned arrays) or 1.
 template <int VEC>
@@ -245,14 +225,13 @@ struct SplitLoader {
   static constexpr int BK = X3Tile::BK;
   static constexpr int PER = (X3Tile::BM * BK) / (X3Tile::THREADS * 8);  // groups of 8 halves
   static constexpr int GPR = BK / 8;
-  static_assert(GPR == 4, "x3_slot assumes four 8-half groups per row");
   v8h rh[PER], rl[PER];
 
   __device__ __forceinline__ void load(SplitRef P, int64_t ld, int rows, int K, int r0, int k0, int tid) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       int row, grp;
-      x3_slot(tid + p * X3Tile::THREADS, row, grp);
+      tile_slot<GPR>(tid + p * X3Tile::THREADS, row, grp);
       const int gr = r0 + row, gk = k0 + grp * 8;
       const int64_t off = (int64_t)gr * ld + gk;
       if constexpr (VEC == 8) {
@@ -277,7 +256,7 @@ struct SplitLoader {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       int row, grp;
-      x3_slot(tid + p * X3Tile::THREADS, row, grp);
+      tile_slot<GPR>(tid + p * X3Tile::THREADS, row, grp);
       const int off = row * X3Tile::LDW + grp * 8;
       *reinterpret_cast<v8h*>(hi + off) = rh[p];
       *reinterpret_cast<v8h*>(lo + off) = rl[p];
@@ -435,7 +414,11 @@ struct F64Loader {
     for (int p = 0; p < PER; ++p) {
       const int idx = tid + p * F64Tile::THREADS;
       int i, k;
-      if constexpr (!TRANS) {
+      if constexpr (!TRANS && VEC == 2 && F64Tile::PAD == 2) {
+        // 16-byte groups, 8 per 144-byte row: the conflict-free store order
+        tile_slot<VPR_K>(idx, i, k);
+        k *= VEC;
+      } else if constexpr (!TRANS) {
         i = idx / VPR_K;
         k = (idx % VPR_K) * VEC;
       } else {
@@ -481,8 +464,14 @@ struct F64Loader {
         }
         s[i * F64Tile::LDW + k] = reg[p];
       } else if constexpr (!TRANS) {
-        const int i = idx / VPR_K;
-        const int k = (idx % VPR_K) * VEC;
+        int i, k;
+        if constexpr (VEC == 2 && F64Tile::PAD == 2) {
+          tile_slot<VPR_K>(idx, i, k);
+          k *= VEC;
+        } else {
+          i = idx / VPR_K;
+          k = (idx % VPR_K) * VEC;
+        }
 #pragma unroll
         for (int e = 0; e < VEC; e += 2) {
           v2d v = {reg[p * VEC + e], reg[p * VEC + e + 1]};

@@ -25,29 +25,12 @@ struct H16Tile {
   static constexpr int LDS_HALVES = 2 * STAGE;
 };
 
-// Which (row, 8-half group) of a chunk the thread-slot idx moves.  Rows are
-// 144 bytes (36 banks of the 64); two rows of eight 16-byte groups per
-// 16-lane store cycle overlap on four banks when adjacent, and are disjoint
-// when 8 rows apart (36 * 8 = 288 = 32 mod 64), so with MR_LDS_SWZ a cycle
-// takes rows r and r+8 (gemm_core.hpp explains the bank model).
-__device__ __forceinline__ void h16_slot(int idx, int& row, int& grp) {
-#if MR_LDS_SWZ
-  const int g = idx >> 4, q = idx & 15;
-  row = 16 * (g >> 3) + (g & 7) + 8 * (q >> 3);
-  grp = q & 7;
-#else
-  row = idx >> 3;
-  grp = idx & 7;
-#endif
-}
-
 // A BM x BK chunk of a K-contiguous fp16 operand.  VEC = 8 (16-byte loads:
 // ld and K multiples of 8, 16-byte aligned array) or 1.
 template <int VEC>
 struct H16Loader {
   static constexpr int BK = H16Tile::BK;
   static constexpr int GPR = BK / 8;  // groups of 8 halves per row
-  static_assert(GPR == 8, "h16_slot assumes eight 8-half groups per row");
   static constexpr int PER = (H16Tile::BM * BK) / (H16Tile::THREADS * 8);
   v8h r[PER];
 
@@ -56,7 +39,7 @@ struct H16Loader {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       int row, grp;
-      h16_slot(tid + p * H16Tile::THREADS, row, grp);
+      tile_slot<GPR>(tid + p * H16Tile::THREADS, row, grp);
       const int gr = r0 + row, gk = k0 + grp * 8;
       const int64_t off = (int64_t)gr * ld + gk;
       if constexpr (VEC == 8) {
@@ -73,7 +56,7 @@ struct H16Loader {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       int row, grp;
-      h16_slot(tid + p * H16Tile::THREADS, row, grp);
+      tile_slot<GPR>(tid + p * H16Tile::THREADS, row, grp);
       *reinterpret_cast<v8h*>(dst + row * H16Tile::LDW + grp * 8) = r[p];
     }
   }

@@ -22,6 +22,34 @@ constexpr int kWave = 64;
 #ifndef MR_LDS_SWZ
 #define MR_LDS_SWZ 1
 #endif
+
+// Which (row, 16-byte group) of a loader chunk the thread slot idx moves,
+// for GPR groups per row and rows padded by one group (row stride
+// (GPR + 1) * 16 bytes).  LDS serves 16-byte accesses 16 lanes per cycle
+// over 64 four-byte banks, so a cycle's 16 lanes cover 16 / GPR rows whose
+// GPR * 4-bank spans should be disjoint.  Row-major slots put adjacent rows
+// in one cycle, which overlap (rows r and r+3 for GPR = 4, r and r+1 for
+// GPR = 8); rows 4 apart (GPR = 4: stride 20 banks, spans start 0, 16, 32,
+// 48) or 8 apart (GPR = 8: stride 36 banks, spans start 0 and 32) do not.
+// Each row's GPR groups still come from consecutive lanes.
+template <int GPR>
+__device__ __forceinline__ void tile_slot(int idx, int& row, int& grp) {
+#if MR_LDS_SWZ
+  if constexpr (GPR == 4) {
+    const int g = idx >> 4, q = idx & 15;
+    row = 16 * (g >> 2) + (g & 3) + 4 * (q >> 2);
+    grp = q & 3;
+    return;
+  } else if constexpr (GPR == 8) {
+    const int g = idx >> 4, q = idx & 15;
+    row = 16 * (g >> 3) + (g & 7) + 8 * (q >> 3);
+    grp = q & 7;
+    return;
+  }
+#endif
+  row = idx / GPR;
+  grp = idx % GPR;
+}
 constexpr int kNumXcd = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
 
 // --------------------------------------------------------------------------
