@@ -527,6 +527,13 @@ def main(argv=None) -> int:
                 "unit": "TFLOP/s", "frac": dk.get("frac"), "traffic": recorded_traffic(dname, args.workload),
                 "achieved_per_launch": "algorithmic flops of the class over the timed steps / sum of its "
                                        "event-measured launch durations"}
+    if dname == "newton_x3":
+        # float32-accurate products, each three fp16 MFMA products (hi*hi, hi*lo, lo*hi)
+        roofline.update({"mfma_achieved": dk.get("mfma_tflops"),
+                         "mfma_frac": round(dk["mfma_tflops"] / PEAK_TFLOPS["f16"], 4),
+                         "frac_of_f32_peak": round(dk["tflops"] / PEAK_TFLOPS["f32"], 4),
+                         "note": "achieved/frac count the float32-accurate products against the fp16 MFMA peak "
+                                 "the kernel runs on; mfma_* count the three fp16 products each takes"})
 
     size_classes = None
     if args.per_size_class:
