@@ -936,7 +936,7 @@ mr_status inv_sqrt_root_batched(const mr_root_problem* p, int32_t count, mr_dtyp
         C.matrix_bytes = (int64_t)c.matrix_bytes;
         C.d = (int32_t)c.d;
         C.count = c.count;
-        C.T = tiles(c.d, 128);
+        C.T = tiles(c.d, cans_tile(prec));
         C.U = C.T * (C.T + 1) / 2;
         C.slot_begin = c.first_slot;
         C.block_begin = L.total_blocks;
@@ -1160,8 +1160,8 @@ mr_status polar_cans_batched(const mr_polar_problem* p, int32_t count, int32_t p
           C.M = (int32_t)c.M;
           C.N = (int32_t)c.N;
           C.count = c.count;
-          C.TM = tiles(c.M, 128);
-          C.TN = tiles(c.N, 128);
+          C.TM = tiles(c.M, polar_tile(prec, stage));
+          C.TN = tiles(c.N, polar_tile(prec, stage));
           C.U = C.TN * (C.TN + 1) / 2;
           C.slot_begin = c.first_slot;
           C.block_begin = L.total_blocks;

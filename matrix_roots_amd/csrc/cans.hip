@@ -16,6 +16,8 @@
 // (float32-accurate products, as in the quarter root's float32 phase).
 #include <math.h>
 
+#include <type_traits>
+
 #include "cans.hpp"
 #include "gemm_core.hpp"
 #include "gemm_h16.hpp"
@@ -161,13 +163,34 @@ __global__ __launch_bounds__(256) void cans_init_kernel(const RootBatch B, doubl
   }
 }
 
+// Block shapes: split products use the 128 x 128 split core; fp16 products
+// use MR_CANS_TILE x MR_CANS_TILE tiles (256: 8 waves of 128 x 64, each
+// operand panel read half as often as with 128).
+#ifndef MR_CANS_TILE
+#define MR_CANS_TILE 256
+#endif
+#ifndef MR_CANS_BK
+#define MR_CANS_BK (MR_CANS_TILE == 256 ? 32 : 64)
+#endif
+using CansSplitShape = H16Shape<128, 128, 2, 2>;
+using CansF16Shape = H16Shape<MR_CANS_TILE, MR_CANS_TILE, 2, MR_CANS_TILE / 64, MR_CANS_BK>;
+
 // One launch stage of the iteration for every matrix of up to kMaxClasses
 // size classes; workgroup -> (class, matrix, job, tile) through the per-class
 // XCD remap.  PREC 1: fp16 products; PREC 3: split products.  FULL: the P
 // stage (every tile, stored with its transpose); else the symmetric stages.
-template <int VEC, int PREC, bool FULL>
-__global__ __launch_bounds__(256, 2) void cans_gemm_kernel(const CansLaunch L) {
-  __shared__ _Float16 smem[PREC == 3 ? X3Tile::LDS_HALVES : H16Tile::LDS_HALVES];
+#ifndef MR_CANS_OCC_FULL
+#define MR_CANS_OCC_FULL 2
+#endif
+#ifndef MR_CANS_OCC_SYM
+#define MR_CANS_OCC_SYM 2
+#endif
+template <int VEC, int PREC, bool FULL, class S>
+__global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1
+                                         : PREC == 3      ? 2
+                                         : FULL           ? MR_CANS_OCC_FULL
+                                                          : MR_CANS_OCC_SYM) void cans_gemm_kernel(const CansLaunch L) {
+  __shared__ _Float16 smem[PREC == 3 ? X3Tile::LDS_HALVES : S::LDS_HALVES];
   const int64_t b = blockIdx.x;
   int ci = 0;
   while (ci + 1 < L.ncls && b >= L.cls[ci + 1].block_begin) ++ci;
@@ -206,35 +229,39 @@ __global__ __launch_bounds__(256, 2) void cans_gemm_kernel(const CansLaunch L) {
     Bm = cans_buf(region, d, kBufP);
     Out = cans_buf(region, d, buf_z(k + 1));
   }
-  const double alpha = L.alpha[job], beta = L.beta[job];
-  const int m0 = ti * 128, n0 = tj * 128;
-  v16f acc[2][2];
+  // Epilogue arithmetic: float64 for split products (float32-accurate
+  // results), float32 for fp16 products (its rounding, even under the first
+  // step's 18-fold cancellation, stays far below the fp16 product noise).
+  using E = typename std::conditional<PREC == 3, double, float>::type;
+  const E alpha = (E)L.alpha[job], beta = (E)L.beta[job];
+  const int m0 = ti * S::BM, n0 = tj * S::BN;
+  v16f acc[S::RB][S::CB];
   if constexpr (PREC == 3)
     x3_nt_tile<VEC>(A.ref(), d, Bm.ref(), d, d, d, d, m0, n0, smem, acc);
   else
-    h16_nt_tile<VEC>(A.hi, d, Bm.hi, d, d, d, d, m0, n0, smem, acc);
+    h16g_nt_tile<S, VEC>(A.hi, d, Bm.hi, d, d, d, d, m0, n0, smem, acc);
 
-  const bool whole = m0 + 128 <= d && n0 + 128 <= d;
+  const bool whole = m0 + S::BM <= d && n0 + S::BN <= d;
   if (VEC == 8 && whole && (full || ti < tj)) {
     // A lane holds 4 consecutive rows of one column per MFMA value group:
     // 4 consecutive columns of the transposed row, one 8-byte store per array.
     const Split T = full ? cans_buf(region, d, kBufPt) : Out;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / S::WN, wn = wave % S::WN;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < S::RB; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < S::CB; ++cb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int gc = n0 + wn * 64 + cb * 32 + (lane & 31);
-          const int gr0 = m0 + wm * 64 + rb * 32 + 8 * g + 4 * (lane >> 5);
+          const int gc = n0 + wn * (S::BN / S::WN) + cb * 32 + (lane & 31);
+          const int gr0 = m0 + wm * (S::BM / S::WM) + rb * 32 + 8 * g + 4 * (lane >> 5);
           v4h hh, ll;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int64_t i = (int64_t)(gr0 + e) * d + gc;
-            double v = alpha * (double)acc[rb][cb][4 * g + e];
-            if (!full) v += beta * (double)get(Cin, i);
+            E v = alpha * (E)acc[rb][cb][4 * g + e];
+            if (!full) v += beta * (E)get(Cin, i);
             _Float16 h, l;
             split_f32((float)v, h, l);
             Out.hi[i] = h;
@@ -249,16 +276,16 @@ __global__ __launch_bounds__(256, 2) void cans_gemm_kernel(const CansLaunch L) {
     return;
   }
   const Split Pt = cans_buf(region, d, kBufPt);
-  f32_for_each(acc, [&](int rr, int cc, float a) {
+  h16g_for_each<S>(acc, [&](int rr, int cc, float a) {
     const int gr = m0 + rr, gc = n0 + cc;
     if (gr >= d || gc >= d) return;
     if (full) {
-      const float v = (float)(alpha * (double)a);
+      const float v = (float)(alpha * (E)a);
       put(Out, (int64_t)gr * d + gc, v);
       put(Pt, (int64_t)gc * d + gr, v);
     } else if (gr <= gc) {
       const int64_t i = (int64_t)gr * d + gc;
-      const float v = (float)(alpha * (double)a + beta * (double)get(Cin, i));
+      const float v = (float)(alpha * (E)a + beta * (E)get(Cin, i));
       put(Out, i, v);
       if (gr != gc) put(Out, (int64_t)gc * d + gr, v);
     }
@@ -346,27 +373,29 @@ hipError_t launch_cans_init(const RootBatch& b, double sy0, double za, double zb
   return hipGetLastError();
 }
 
+int cans_tile(int prec) { return prec == 3 ? CansSplitShape::BM : CansF16Shape::BM; }
+
 hipError_t launch_cans_gemm(const CansLaunch& L, int vec, int prec, hipStream_t s) {
   if (L.total_blocks <= 0) return hipSuccess;
-  const dim3 g(L.total_blocks), t(256);
+  const dim3 g(L.total_blocks);
   const bool full = L.stage == kCansP;
-#define MR_CANS_LAUNCH(V, P)                                                    \
-  do {                                                                          \
-    if (full)                                                                   \
-      hipLaunchKernelGGL((cans_gemm_kernel<V, P, true>), g, t, 0, s, L);       \
-    else                                                                        \
-      hipLaunchKernelGGL((cans_gemm_kernel<V, P, false>), g, t, 0, s, L);      \
+#define MR_CANS_LAUNCH(V, P, SH)                                                                        \
+  do {                                                                                                  \
+    if (full)                                                                                           \
+      hipLaunchKernelGGL((cans_gemm_kernel<V, P, true, SH>), g, dim3(SH::THREADS), 0, s, L);           \
+    else                                                                                                \
+      hipLaunchKernelGGL((cans_gemm_kernel<V, P, false, SH>), g, dim3(SH::THREADS), 0, s, L);          \
   } while (0)
   if (prec == 3) {
     if (vec == 8)
-      MR_CANS_LAUNCH(8, 3);
+      MR_CANS_LAUNCH(8, 3, CansSplitShape);
     else
-      MR_CANS_LAUNCH(1, 3);
+      MR_CANS_LAUNCH(1, 3, CansSplitShape);
   } else {
     if (vec == 8)
-      MR_CANS_LAUNCH(8, 1);
+      MR_CANS_LAUNCH(8, 1, CansF16Shape);
     else
-      MR_CANS_LAUNCH(1, 1);
+      MR_CANS_LAUNCH(1, 1, CansF16Shape);
   }
 #undef MR_CANS_LAUNCH
   return hipGetLastError();

@@ -116,6 +116,7 @@ hipError_t launch_cans_bound(RootState* state, const double* partial, int64_t st
                              int32_t normalize, double eps, double z_out_scale, hipStream_t s);
 hipError_t launch_cans_init(const RootBatch& b, double sy0, double za, double zb, hipStream_t s);
 hipError_t launch_cans_gemm(const CansLaunch& L, int vec, int prec, hipStream_t s);
+int cans_tile(int prec);  // output tile side of the GEMM launches of a precision (1: fp16, 3: split)
 hipError_t launch_cans_finalize(const RootBatch& b, double inv_sp9, hipStream_t s);
 hipError_t launch_cans_info(RootState* state, const double* partial, int64_t stride, int32_t count,
                             mr_root_info* info, double rms_limit, hipStream_t s);

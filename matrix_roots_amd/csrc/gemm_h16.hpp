@@ -125,4 +125,137 @@ __device__ __forceinline__ void h16_nt_tile(const _Float16* __restrict__ A, int6
   }
 }
 
+// ------------------------------------------------- block shapes (generic)
+// BM x BN block tile, WM x WN waves, each wave (BM / WM) x (BN / WN) in 32 x 32
+// MFMA blocks (RB x CB of them), K in chunks of BK through two LDS stages.
+// H16Shape<128, 128, 2, 2> is the core above; H16Shape<256, 256, 2, 4> (512
+// threads, 128 accumulator registers per lane, 144 KB of LDS: one block and
+// two waves per SIMD) reads each operand panel half as often.
+template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64>
+struct H16Shape {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int THREADS = 64 * WM * WN;
+  static constexpr int RB = BM / WM / 32, CB = BN / WN / 32;
+  static constexpr int BK = BK_, PAD = 8, LDW = BK + PAD;
+  static constexpr int AARR = BM * LDW, BARR = BN * LDW;
+  static constexpr int STAGE = AARR + BARR;
+  static constexpr int LDS_HALVES = 2 * STAGE;
+};
+
+template <class S, int ROWS, int VEC>
+struct H16GLoader {
+  static constexpr int GPR = S::BK / 8;
+  static constexpr int PER = (ROWS * S::BK) / (S::THREADS * 8);
+  static_assert(PER * S::THREADS * 8 == ROWS * S::BK, "loader covers the chunk");
+  v8h r[PER];
+
+  __device__ __forceinline__ void load(const _Float16* __restrict__ P, int64_t ld, int rows, int K, int r0, int k0,
+                                       int tid) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      int row, grp;
+      tile_slot<GPR>(tid + p * S::THREADS, row, grp);
+      const int gr = r0 + row, gk = k0 + grp * 8;
+      const int64_t off = (int64_t)gr * ld + gk;
+      if constexpr (VEC == 8) {
+        v8h h = {};
+        if (gr < rows && gk < K) h = *reinterpret_cast<const v8h*>(P + off);
+        r[p] = h;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[p][e] = (gr < rows && gk + e < K) ? P[off + e] : (_Float16)0.0f;
+      }
+    }
+  }
+  __device__ __forceinline__ void store(_Float16* __restrict__ dst, int tid) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      int row, grp;
+      tile_slot<GPR>(tid + p * S::THREADS, row, grp);
+      *reinterpret_cast<v8h*>(dst + row * S::LDW + grp * 8) = r[p];
+    }
+  }
+};
+
+template <class S>
+__device__ __forceinline__ void h16g_chunk(const _Float16* __restrict__ st, v16f (&acc)[S::RB][S::CB], int lane,
+                                           int wm, int wn) {
+  const _Float16* As = st;
+  const _Float16* Bs = st + S::AARR;
+  const int koff = (lane >> 5) * 8;
+#pragma unroll
+  for (int ks = 0; ks < S::BK / 16; ++ks) {
+    v8h a[S::RB], b[S::CB];
+#pragma unroll
+    for (int rb = 0; rb < S::RB; ++rb)
+      a[rb] = *reinterpret_cast<const v8h*>(As + (wm * (S::BM / S::WM) + rb * 32 + (lane & 31)) * S::LDW + ks * 16 +
+                                            koff);
+#pragma unroll
+    for (int cb = 0; cb < S::CB; ++cb)
+      b[cb] = *reinterpret_cast<const v8h*>(Bs + (wn * (S::BN / S::WN) + cb * 32 + (lane & 31)) * S::LDW + ks * 16 +
+                                            koff);
+#pragma unroll
+    for (int rb = 0; rb < S::RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < S::CB; ++cb) acc[rb][cb] = mfma_f16_32x32x16(a[rb], b[cb], acc[rb][cb]);
+  }
+}
+
+// acc = A[m0:m0+BM, :K] * B[n0:n0+BN, :K]^T (rows beyond M / N and columns
+// beyond K read as zero), per-wave blocks laid out as in h16g_for_each.
+template <class S, int VEC>
+__device__ __forceinline__ void h16g_nt_tile(const _Float16* __restrict__ A, int64_t lda,
+                                             const _Float16* __restrict__ B, int64_t ldb, int M, int N, int K, int m0,
+                                             int n0, _Float16* __restrict__ lds, v16f (&acc)[S::RB][S::CB]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / S::WN, wn = wave % S::WN;
+#pragma unroll
+  for (int rb = 0; rb < S::RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < S::CB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.f;
+  H16GLoader<S, S::BM, VEC> la;
+  H16GLoader<S, S::BN, VEC> lb;
+  la.load(A, lda, M, K, m0, 0, tid);
+  lb.load(B, ldb, N, K, n0, 0, tid);
+  la.store(lds, tid);
+  lb.store(lds + S::AARR, tid);
+  __syncthreads();
+  int stage = 0;
+  for (int k0 = 0; k0 < K; k0 += S::BK) {
+    const bool more = k0 + S::BK < K;
+    if (more) {
+      la.load(A, lda, M, K, m0, k0 + S::BK, tid);
+      lb.load(B, ldb, N, K, n0, k0 + S::BK, tid);
+    }
+    h16g_chunk<S>(lds + stage * S::STAGE, acc, lane, wm, wn);
+    if (more) {
+      _Float16* nxt = lds + (stage ^ 1) * S::STAGE;
+      la.store(nxt, tid);
+      lb.store(nxt + S::AARR, tid);
+    }
+    __syncthreads();
+    stage ^= 1;
+  }
+}
+
+// Visit every accumulator element as (row, col) local to the block tile.
+template <class S, typename F>
+__device__ __forceinline__ void h16g_for_each(const v16f (&acc)[S::RB][S::CB], F&& f) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / S::WN, wn = wave % S::WN;
+#pragma unroll
+  for (int rb = 0; rb < S::RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < S::CB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        f(wm * (S::BM / S::WM) + rb * 32 + f32_row(lane, v), wn * (S::BN / S::WN) + cb * 32 + (lane & 31),
+          acc[rb][cb][v]);
+}
+
 }  // namespace mr

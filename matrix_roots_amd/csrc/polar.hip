@@ -11,6 +11,8 @@
 // (hi x hi) or split (three-product) MFMA, float32 accumulation.
 #include <math.h>
 
+#include <type_traits>
+
 #include "gemm_core.hpp"
 #include "gemm_h16.hpp"
 #include "polar.hpp"
@@ -171,9 +173,21 @@ __global__ __launch_bounds__(256) void polar_init_kernel(const PolarBatch B, dou
 // Stage A (FULL = false): A = alpha T^T T, upper tiles of N x N, mirrored.
 // Stage X (FULL = true): T' = beta T + alpha T A, every tile of M x N,
 // stored into T(k+1) and, transposed, into T^T.
-template <int VEC, int PREC, bool FULL>
-__global__ __launch_bounds__(256, 2) void polar_gemm_kernel(const PolarLaunch L) {
-  __shared__ _Float16 smem[PREC == 3 ? X3Tile::LDS_HALVES : H16Tile::LDS_HALVES];
+// Block shapes: 128 x 128 for split products and for the fp16 Gram (whose
+// few output tiles would leave the chip half idle with larger ones),
+// MR_POLAR_TILE-square tiles for the fp16 update.
+#ifndef MR_POLAR_TILE
+#define MR_POLAR_TILE 256
+#endif
+#ifndef MR_POLAR_BK
+#define MR_POLAR_BK (MR_POLAR_TILE == 256 ? 32 : 64)
+#endif
+using PolarSplitShape = H16Shape<128, 128, 2, 2>;
+using PolarF16Shape = H16Shape<MR_POLAR_TILE, MR_POLAR_TILE, 2, MR_POLAR_TILE / 64, MR_POLAR_BK>;
+
+template <int VEC, int PREC, bool FULL, class S>
+__global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1 : 2) void polar_gemm_kernel(const PolarLaunch L) {
+  __shared__ _Float16 smem[PREC == 3 ? X3Tile::LDS_HALVES : S::LDS_HALVES];
   const int64_t b = blockIdx.x;
   int ci = 0;
   while (ci + 1 < L.ncls && b >= L.cls[ci + 1].block_begin) ++ci;
@@ -208,37 +222,39 @@ __global__ __launch_bounds__(256, 2) void polar_gemm_kernel(const PolarLaunch L)
     K = M;
     lda = ldb = M;
   }
-  const int m0 = ti * 128, n0 = tj * 128;
-  v16f acc[2][2];
+  const int m0 = ti * S::BM, n0 = tj * S::BN;
+  v16f acc[S::RB][S::CB];
   if constexpr (PREC == 3)
     x3_nt_tile<VEC>(Aop.ref(), lda, Bop.ref(), ldb, rows, cols, K, m0, n0, smem, acc);
   else
-    h16_nt_tile<VEC>(Aop.hi, lda, Bop.hi, ldb, rows, cols, K, m0, n0, smem, acc);
-  const double alpha = L.alpha, beta = L.beta;
+    h16g_nt_tile<S, VEC>(Aop.hi, lda, Bop.hi, ldb, rows, cols, K, m0, n0, smem, acc);
+  // epilogue arithmetic: float64 for split products, float32 for fp16 ones
+  using E = typename std::conditional<PREC == 3, double, float>::type;
+  const E alpha = (E)L.alpha, beta = (E)L.beta;
   const Split Tt = polar_buf(region, M, N, 2);
 
-  const bool whole = m0 + 128 <= rows && n0 + 128 <= cols;
+  const bool whole = m0 + S::BM <= rows && n0 + S::BN <= cols;
   if (VEC == 8 && whole && (FULL || ti < tj)) {
     // A lane holds 4 consecutive rows of one column per MFMA value group:
     // 4 consecutive columns of the transposed row, one 8-byte store per array.
     const Split T = FULL ? Tt : Out;
     const int64_t ldt = FULL ? M : N;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / S::WN, wn = wave % S::WN;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < S::RB; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < S::CB; ++cb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int gc = n0 + wn * 64 + cb * 32 + (lane & 31);
-          const int gr0 = m0 + wm * 64 + rb * 32 + 8 * g + 4 * (lane >> 5);
+          const int gc = n0 + wn * (S::BN / S::WN) + cb * 32 + (lane & 31);
+          const int gr0 = m0 + wm * (S::BM / S::WM) + rb * 32 + 8 * g + 4 * (lane >> 5);
           v4h hh, ll;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int64_t i = (int64_t)(gr0 + e) * cols + gc;
-            double v = alpha * (double)acc[rb][cb][4 * g + e];
-            if (FULL) v += beta * (double)get(Aop, i);
+            E v = alpha * (E)acc[rb][cb][4 * g + e];
+            if (FULL) v += beta * (E)get(Aop, i);
             _Float16 h, l;
             split_f32((float)v, h, l);
             Out.hi[i] = h;
@@ -252,16 +268,16 @@ __global__ __launch_bounds__(256, 2) void polar_gemm_kernel(const PolarLaunch L)
         }
     return;
   }
-  f32_for_each(acc, [&](int rr, int cc, float a) {
+  h16g_for_each<S>(acc, [&](int rr, int cc, float a) {
     const int gr = m0 + rr, gc = n0 + cc;
     if (gr >= rows || gc >= cols) return;
     if (FULL) {
       const int64_t i = (int64_t)gr * cols + gc;
-      const float v = (float)(alpha * (double)a + beta * (double)get(Aop, i));
+      const float v = (float)(alpha * (E)a + beta * (E)get(Aop, i));
       put(Out, i, v);
       put(Tt, (int64_t)gc * M + gr, v);
     } else if (gr <= gc) {
-      const float v = (float)(alpha * (double)a);
+      const float v = (float)(alpha * (E)a);
       put(Out, (int64_t)gr * cols + gc, v);
       if (gr != gc) put(Out, (int64_t)gc * cols + gr, v);
     }
@@ -323,27 +339,38 @@ hipError_t launch_polar_init(const PolarBatch& b, double s0, hipStream_t s) {
   return hipGetLastError();
 }
 
+int polar_tile(int prec, int stage) {
+  return prec == 1 && stage == kPolarX ? PolarF16Shape::BM : PolarSplitShape::BM;
+}
+
 hipError_t launch_polar_gemm(const PolarLaunch& L, int vec, int prec, hipStream_t s) {
   if (L.total_blocks <= 0) return hipSuccess;
-  const dim3 g(L.total_blocks), t(256);
+  const dim3 g(L.total_blocks);
   const bool full = L.stage == kPolarX;
-#define MR_POLAR_LAUNCH(V, P)                                                   \
-  do {                                                                          \
-    if (full)                                                                   \
-      hipLaunchKernelGGL((polar_gemm_kernel<V, P, true>), g, t, 0, s, L);      \
-    else                                                                        \
-      hipLaunchKernelGGL((polar_gemm_kernel<V, P, false>), g, t, 0, s, L);     \
+#define MR_POLAR_LAUNCH(V, P, SH)                                                                       \
+  do {                                                                                                  \
+    if (full)                                                                                           \
+      hipLaunchKernelGGL((polar_gemm_kernel<V, P, true, SH>), g, dim3(SH::THREADS), 0, s, L);          \
+    else                                                                                                \
+      hipLaunchKernelGGL((polar_gemm_kernel<V, P, false, SH>), g, dim3(SH::THREADS), 0, s, L);         \
   } while (0)
   if (prec == 3) {
     if (vec == 8)
-      MR_POLAR_LAUNCH(8, 3);
+      MR_POLAR_LAUNCH(8, 3, PolarSplitShape);
     else
-      MR_POLAR_LAUNCH(1, 3);
+      MR_POLAR_LAUNCH(1, 3, PolarSplitShape);
   } else {
-    if (vec == 8)
-      MR_POLAR_LAUNCH(8, 1);
-    else
-      MR_POLAR_LAUNCH(1, 1);
+    if (full) {
+      if (vec == 8)
+        MR_POLAR_LAUNCH(8, 1, PolarF16Shape);
+      else
+        MR_POLAR_LAUNCH(1, 1, PolarF16Shape);
+    } else {
+      if (vec == 8)
+        MR_POLAR_LAUNCH(8, 1, PolarSplitShape);
+      else
+        MR_POLAR_LAUNCH(1, 1, PolarSplitShape);
+    }
   }
 #undef MR_POLAR_LAUNCH
   return hipGetLastError();

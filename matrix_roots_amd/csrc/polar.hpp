@@ -64,6 +64,7 @@ hipError_t launch_polar_bound(RootState* state, const double* partial, int64_t s
                               double out_scale, hipStream_t s);
 hipError_t launch_polar_init(const PolarBatch& b, double s0, hipStream_t s);
 hipError_t launch_polar_gemm(const PolarLaunch& L, int vec, int prec, hipStream_t s);
+int polar_tile(int prec, int stage);  // output tile side of a GEMM stage (prec 1: fp16, 3: split)
 hipError_t launch_polar_finalize(const PolarBatch& b, double inv_sa9, hipStream_t s);
 
 }  // namespace mr
