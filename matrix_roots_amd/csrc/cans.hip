@@ -190,7 +190,7 @@ __global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1
                                          : PREC == 3      ? 2
                                          : FULL           ? MR_CANS_OCC_FULL
                                                           : MR_CANS_OCC_SYM) void cans_gemm_kernel(const CansLaunch L) {
-  __shared__ _Float16 smem[PREC == 3 ? X3Tile::LDS_HALVES : S::LDS_HALVES];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[PREC == 3 ? 2 * X3Tile::LDS_HALVES : h16_lds_bytes<S>()];
   const int64_t b = blockIdx.x;
   int ci = 0;
   while (ci + 1 < L.ncls && b >= L.cls[ci + 1].block_begin) ++ci;
@@ -237,9 +237,9 @@ __global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1
   const int m0 = ti * S::BM, n0 = tj * S::BN;
   v16f acc[S::RB][S::CB];
   if constexpr (PREC == 3)
-    x3_nt_tile<VEC>(A.ref(), d, Bm.ref(), d, d, d, d, m0, n0, smem, acc);
+    x3_nt_tile<VEC>(A.ref(), d, Bm.ref(), d, d, d, d, m0, n0, reinterpret_cast<_Float16*>(smem), acc);
   else
-    h16g_nt_tile<S, VEC>(A.hi, d, Bm.hi, d, d, d, d, m0, n0, smem, acc);
+    h16_nt_tile_auto<S, VEC>(A.hi, d, Bm.hi, d, d, d, d, m0, n0, smem, acc);
 
   const bool whole = m0 + S::BM <= d && n0 + S::BN <= d;
   if (VEC == 8 && whole && (full || ti < tj)) {

@@ -258,4 +258,149 @@ __device__ __forceinline__ void h16g_for_each(const v16f (&acc)[S::RB][S::CB], F
           acc[rb][cb][v]);
 }
 
+// ------------------------------------------- direct-to-LDS core (fp16 only)
+// The same block tile and wave layout as H16Shape<BM, BN, WM, WN>, with the
+// operand chunks copied from global memory straight into LDS by
+// global_load_lds_dwordx4 (no staging registers, no LDS store instructions):
+// each instruction moves 16 bytes per lane into 1 KB of consecutive LDS.  A
+// chunk row is BK halves (UPR 16-byte units, no padding); the unit of k-group
+// kg of row r sits in slot kg ^ ((r / (16 / UPR)) % UPR), so the 16 lanes of
+// one LDS read cycle (16 consecutive rows, same k-group) hit 16 distinct
+// 16-byte bank groups.  Two stages; a wave waits for its own copies of the
+// next chunk (vmcnt) and a plain s_barrier publishes them, which leaves the
+// copies of the chunk after in flight during the MFMAs.
+//
+// Preconditions (checked by the caller): K a multiple of BK, lda and ldb
+// multiples of 8, A and B 16-byte aligned.  Rows beyond M or N are read from
+// row M - 1 or N - 1: they only feed outputs that are never stored.
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
+
+template <int BM_, int BN_, int WM_, int WN_, int BK_>
+struct H16DLShape {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_;
+  static constexpr int THREADS = 64 * WM * WN, NW = WM * WN;
+  static constexpr int RB = BM / WM / 32, CB = BN / WN / 32;
+  static constexpr int UPR = BK / 8;
+  static constexpr int AU = BM * UPR, BU = BN * UPR;  // 16-byte units per stage
+  static constexpr int STAGE_BYTES = (AU + BU) * 16;
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int NA = AU / (64 * NW), NB = BU / (64 * NW);  // copies per wave per chunk
+  static_assert(NA * 64 * NW == AU && NB * 64 * NW == BU, "copies cover the chunk");
+  static_assert(UPR == 4 || UPR == 8, "swizzle period");
+};
+
+__device__ __forceinline__ int dl_slot(int row, int kg, int upr) { return kg ^ ((row / (16 / upr)) % upr); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <class S>
+__device__ __forceinline__ void h16dl_issue(const _Float16* __restrict__ A, int64_t lda, const _Float16* __restrict__ B,
+                                            int64_t ldb, int M, int N, int m0, int n0, int k0, unsigned char* stage,
+                                            int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < S::NA + S::NB; ++j) {
+    const bool isA = j < S::NA;
+    const int base_u = ((isA ? j : j - S::NA) * S::NW + wave) * 64;
+    const int u = base_u + lane;
+    const int row = u / S::UPR;
+    const int kg = dl_slot(row, u % S::UPR, S::UPR);  // the map is its own inverse
+    const _Float16* src = isA ? A + (int64_t)min(m0 + row, M - 1) * lda + k0 + kg * 8
+                              : B + (int64_t)min(n0 + row, N - 1) * ldb + k0 + kg * 8;
+    __builtin_amdgcn_global_load_lds((global_void_ptr)src,
+                                     (lds_void_ptr)(stage + (isA ? 0 : S::AU * 16) + base_u * 16), 16, 0, 0);
+  }
+}
+
+template <class S>
+__device__ __forceinline__ void h16dl_chunk(const unsigned char* __restrict__ st, v16f (&acc)[S::RB][S::CB], int wm,
+                                            int wn, int lane) {
+  const unsigned char* As = st;
+  const unsigned char* Bs = st + S::AU * 16;
+#pragma unroll
+  for (int ks = 0; ks < S::BK / 16; ++ks) {
+    v8h a[S::RB], b[S::CB];
+    const int kg = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int rb = 0; rb < S::RB; ++rb) {
+      const int r = wm * (S::BM / S::WM) + rb * 32 + (lane & 31);
+      a[rb] = *reinterpret_cast<const v8h*>(As + (r * S::UPR + dl_slot(r, kg, S::UPR)) * 16);
+    }
+#pragma unroll
+    for (int cb = 0; cb < S::CB; ++cb) {
+      const int r = wn * (S::BN / S::WN) + cb * 32 + (lane & 31);
+      b[cb] = *reinterpret_cast<const v8h*>(Bs + (r * S::UPR + dl_slot(r, kg, S::UPR)) * 16);
+    }
+#pragma unroll
+    for (int rb = 0; rb < S::RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < S::CB; ++cb) acc[rb][cb] = mfma_f16_32x32x16(a[rb], b[cb], acc[rb][cb]);
+  }
+}
+
+// acc = A[m0:m0+BM, :K] * B[n0:n0+BN, :K]^T in the accumulator layout of
+// h16g_for_each for the H16Shape of the same BM, BN, WM, WN.
+template <class S>
+__device__ __forceinline__ void h16dl_nt_tile(const _Float16* __restrict__ A, int64_t lda,
+                                              const _Float16* __restrict__ B, int64_t ldb, int M, int N, int K, int m0,
+                                              int n0, unsigned char* __restrict__ lds, v16f (&acc)[S::RB][S::CB]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / S::WN, wn = wave % S::WN;
+#pragma unroll
+  for (int rb = 0; rb < S::RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < S::CB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.f;
+  const int nch = K / S::BK;
+  if (nch > 0) h16dl_issue<S>(A, lda, B, ldb, M, N, m0, n0, 0, lds, wave, lane);
+  for (int c = 0; c < nch; c += 2) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (c + s < nch) {
+        wait_vmcnt<0>();  // this wave's copies of chunk c + s have landed
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // ... and every wave's; stage s ^ 1 is free
+        asm volatile("" ::: "memory");
+        if (c + s + 1 < nch)
+          h16dl_issue<S>(A, lda, B, ldb, M, N, m0, n0, (c + s + 1) * S::BK, lds + (s ^ 1) * S::STAGE_BYTES, wave,
+                         lane);
+        h16dl_chunk<S>(lds + s * S::STAGE_BYTES, acc, wm, wn, lane);
+      }
+    }
+  }
+  __syncthreads();  // no wave leaves while another may still read the last stage
+}
+
+// The direct-to-LDS tile of an H16Shape (K-chunks of 64) and the LDS bytes a
+// kernel needs for either core.
+#ifndef MR_H16_DL
+#define MR_H16_DL 1
+#endif
+template <class S>
+using H16DLOf = H16DLShape<S::BM, S::BN, S::WM, S::WN, 64>;
+template <class S>
+constexpr int h16_lds_bytes() {
+  return (MR_H16_DL && H16DLOf<S>::LDS_BYTES > 2 * S::LDS_HALVES) ? H16DLOf<S>::LDS_BYTES : 2 * S::LDS_HALVES;
+}
+
+// Direct-to-LDS core where its preconditions hold (VEC 8 implies 16-byte
+// aligned operands with leading dimensions multiple of 8), else the
+// register-staged one.
+template <class S, int VEC>
+__device__ __forceinline__ void h16_nt_tile_auto(const _Float16* __restrict__ A, int64_t lda,
+                                                 const _Float16* __restrict__ B, int64_t ldb, int M, int N, int K,
+                                                 int m0, int n0, unsigned char* __restrict__ lds,
+                                                 v16f (&acc)[S::RB][S::CB]) {
+  if (MR_H16_DL && VEC == 8 && K % 64 == 0)
+    h16dl_nt_tile<H16DLOf<S>>(A, lda, B, ldb, M, N, K, m0, n0, lds, acc);
+  else
+    h16g_nt_tile<S, VEC>(A, lda, B, ldb, M, N, K, m0, n0, reinterpret_cast<_Float16*>(lds), acc);
+}
+
 }  // namespace mr

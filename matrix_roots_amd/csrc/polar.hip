@@ -187,7 +187,7 @@ using PolarF16Shape = H16Shape<MR_POLAR_TILE, MR_POLAR_TILE, 2, MR_POLAR_TILE / 
 
 template <int VEC, int PREC, bool FULL, class S>
 __global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1 : 2) void polar_gemm_kernel(const PolarLaunch L) {
-  __shared__ _Float16 smem[PREC == 3 ? X3Tile::LDS_HALVES : S::LDS_HALVES];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[PREC == 3 ? 2 * X3Tile::LDS_HALVES : h16_lds_bytes<S>()];
   const int64_t b = blockIdx.x;
   int ci = 0;
   while (ci + 1 < L.ncls && b >= L.cls[ci + 1].block_begin) ++ci;
@@ -225,9 +225,9 @@ __global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1 : 2) void polar_g
   const int m0 = ti * S::BM, n0 = tj * S::BN;
   v16f acc[S::RB][S::CB];
   if constexpr (PREC == 3)
-    x3_nt_tile<VEC>(Aop.ref(), lda, Bop.ref(), ldb, rows, cols, K, m0, n0, smem, acc);
+    x3_nt_tile<VEC>(Aop.ref(), lda, Bop.ref(), ldb, rows, cols, K, m0, n0, reinterpret_cast<_Float16*>(smem), acc);
   else
-    h16g_nt_tile<S, VEC>(Aop.hi, lda, Bop.hi, ldb, rows, cols, K, m0, n0, smem, acc);
+    h16_nt_tile_auto<S, VEC>(Aop.hi, lda, Bop.hi, ldb, rows, cols, K, m0, n0, smem, acc);
   // epilogue arithmetic: float64 for split products, float32 for fp16 ones
   using E = typename std::conditional<PREC == 3, double, float>::type;
   const E alpha = (E)L.alpha, beta = (E)L.beta;

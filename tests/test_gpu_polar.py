@@ -67,10 +67,12 @@ def check(torch, dev, Gs, precision, orth=True):
 
 @pytest.mark.parametrize("precision", ["f16", "split"])
 @pytest.mark.parametrize("shape", [(1, 1), (1, 7), (7, 1), (64, 48), (48, 64), (130, 130), (257, 129), (300, 100),
-                                   (100, 300), (520, 264), (384, 1152)])
+                                   (100, 300), (520, 264), (384, 1152), (320, 192), (192, 640)])
 def test_shapes(torch_dev, precision, shape):
     """Gaussian gradients over tall, wide, square, ragged and degenerate
-    shapes (16-byte loads when both sides are multiples of 8)."""
+    shapes (16-byte loads when both sides are multiples of 8; fp16 products
+    whose contraction is a multiple of 64 copy straight into LDS, with
+    ragged last tiles at 320 x 192 and 192 x 640)."""
     torch, dev = torch_dev
     worst = check(torch, dev, [grad("gaussian", shape)], precision)
     print(f"{shape} {precision}: err {worst:.2e}")

@@ -69,11 +69,12 @@ def check(torch, dev, As, eps, normalize, precision, dtype=np.float32, tol=None)
 
 
 @pytest.mark.parametrize("precision", ["f16", "split"])
-@pytest.mark.parametrize("d", [1, 7, 64, 130, 257, 300, 520])
+@pytest.mark.parametrize("d", [1, 7, 64, 130, 257, 300, 320, 520, 640])
 def test_sizes_ragged(torch_dev, precision, d):
     """One matrix per call, condition number 1e3, the page's S^(-1/2) (no
     rescale, eps = 0); sizes cover one tile, several tiles and ragged tails,
-    16-byte (d % 8 == 0) and element loads."""
+    16-byte (d % 8 == 0) and element loads, and the direct-to-LDS fp16 core
+    (d % 64 == 0) with ragged last tiles (320, 640)."""
     torch, dev = torch_dev
     A = spd(d, -3.0, 0) if d > 1 else np.array([[0.37]], dtype=np.float32)
     worst, _ = check(torch, dev, [A], 0.0, "none", precision)
