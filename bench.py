@@ -139,7 +139,7 @@ def per_size_class(B, torch, grams, wl):
 CANS_METRIC = "inverse square roots/s (scaled CANS coupled Newton-Schulz, S^-1/2 of SPD 8192x8192, batch 4)"
 
 
-def bench_cans(args, torch, B):
+def bench_cans(args, torch, B, peaks):
     """The OKLS page's root benchmark shape (section 2.4, figure 4): one
     inv_sqrt_root_batched call on 4 SPD matrices of 8192 x 8192 (float32,
     S = G G^T / 8192 + eps I with G Gaussian: condition number about 1e3),
@@ -236,6 +236,7 @@ def bench_cans(args, torch, B):
         "kernels": kernels,
         "residual_max": float(info["residual"].max()),
         "cpu_baseline": cpu,
+        "peaks": peaks,
     }
     print(json.dumps(out), flush=True)
     return 0
@@ -244,7 +245,7 @@ def bench_cans(args, torch, B):
 POLAR_METRIC = "orthogonalised matrices/s (CANS polar, 10 steps; MoE share 64 x 3072x1536 + 64 x 1536x3072)"
 
 
-def bench_polar(args, torch, B):
+def bench_polar(args, torch, B, peaks):
     """One polar_cans_batched call over the 128 expert gradients of the MoE
     share (step-1 sparse-row gradients, host-drawn), timed per call with the
     library's HIP events around each launch."""
@@ -337,6 +338,7 @@ def bench_polar(args, torch, B):
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,
+        "peaks": peaks,
     }
     print(json.dumps(out), flush=True)
     return 0
@@ -412,14 +414,20 @@ def main(argv=None) -> int:
         return 2
     B.library()
     dev = torch.device("cuda:0")
+    # the device's matrix-core peaks: from CU count x clock, and measured by
+    # register-only MFMA loops (reported beside the published figures the
+    # roofline fractions use)
+    peaks = B.measure_peaks()
+    peaks["published_tflops"] = dict(PEAK_TFLOPS)
+    log(f"peaks: {peaks}")
     if args.workload == "cans8192":
         if args.calibration_copy_mib > 0:
             calibration_copies(torch, dev, args.calibration_copy_mib)
-        return bench_cans(args, torch, B)
+        return bench_cans(args, torch, B, peaks)
     if args.workload == "polar_moe":
         if args.calibration_copy_mib > 0:
             calibration_copies(torch, dev, args.calibration_copy_mib)
-        return bench_polar(args, torch, B)
+        return bench_polar(args, torch, B, peaks)
     if args.calibration_copy_mib > 0:
         calibration_copies(torch, dev, args.calibration_copy_mib)
     wl = W.WORKLOADS[args.workload]
@@ -573,6 +581,7 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,
+        "peaks": peaks,
     }
     if size_classes is not None:
         out["size_classes"] = size_classes

@@ -383,6 +383,26 @@ int32_t mr_trace_collect(mr_trace_record* out, int32_t capacity);
  * number of steps (-1 on bad arguments).  Host-only. */
 int32_t mr_newton_schedule(double m0, double* scales, int32_t capacity, int32_t* fp64_steps);
 
+/*
+ * Matrix-core peaks of the current device, for reporting rooflines (the
+ * measurement the hot path's roofline figures are set against).
+ * prop_tflops: multiProcessorCount x clockRate x dense MFMA flops per clock
+ * per compute unit (gfx950: 256 float32, 128 float64, 4096 fp16).
+ * measured_tflops: register-only MFMA loops (v_mfma_f32_32x32x2_f32,
+ * v_mfma_f64_16x16x4_f64, v_mfma_f32_32x32x16_f16), eight workgroups per
+ * CU, about 5 ms each, timed with events on `hip_stream` after one warm-up
+ * launch.  Index 0 float32, 1 float64, 2 fp16.  Synchronises the stream and
+ * touches no device memory; MR_ERR_NULL for a NULL `out`, MR_ERR_HIP on a
+ * runtime error (then `out` holds what was measured before it).
+ */
+typedef struct {
+  int32_t cu_count;          /* hipDeviceProp_t::multiProcessorCount   */
+  int32_t clock_khz;         /* hipDeviceProp_t::clockRate (peak, kHz) */
+  double prop_tflops[3];     /* derived from CU count and clock        */
+  double measured_tflops[3]; /* register-only MFMA loops              */
+} mr_peak_info;
+mr_status mr_measure_peaks(mr_peak_info* out, void* hip_stream);
+
 const char* mr_status_string(mr_status status);
 const char* mr_last_error_message(void);
 int32_t mr_abi_version(void);

@@ -47,6 +47,7 @@ EXPORTED = (
     "precondition_apply_workspace",
     "mr_newton_iterations",
     "mr_newton_schedule",
+    "mr_measure_peaks",
     "mr_trace_enable",
     "mr_trace_collect",
     "mr_status_string",
@@ -132,6 +133,8 @@ def library() -> ctypes.CDLL:
     lib.polar_cans_batched.restype = i32
     lib.polar_cans_batched_workspace.argtypes = [vp, i32, i32]
     lib.polar_cans_batched_workspace.restype = sz
+    lib.mr_measure_peaks.argtypes = [vp, vp]
+    lib.mr_measure_peaks.restype = i32
     lib.momentum_ema_batched.argtypes = [vp, i32, f64, vp]
     lib.momentum_ema_batched.restype = i32
     lib.hyperball_update_batched.argtypes = [vp, i32, f64, vp, vp, sz, vp]
@@ -478,6 +481,24 @@ def newton_schedule(m0: float):
     if K < 0:
         raise ValueError("bad m0")
     return [buf[i] for i in range(K)], int(j.value)
+
+
+class PeakInfo(ctypes.Structure):
+    _fields_ = [("cu_count", ctypes.c_int32), ("clock_khz", ctypes.c_int32),
+                ("prop_tflops", ctypes.c_double * 3), ("measured_tflops", ctypes.c_double * 3)]
+
+
+PEAK_KINDS = ("f32", "f64", "f16")
+
+
+def measure_peaks(stream=None) -> dict:
+    """Matrix-core peaks of the current device: from CU count x clock, and
+    measured by register-only MFMA loops (synchronises the stream)."""
+    out = PeakInfo()
+    _check(library().mr_measure_peaks(ctypes.addressof(out), _stream(stream)))
+    return {"cu_count": int(out.cu_count), "clock_mhz": out.clock_khz / 1e3,
+            "device_prop_tflops": {k: round(out.prop_tflops[i], 1) for i, k in enumerate(PEAK_KINDS)},
+            "measured_tflops": {k: round(out.measured_tflops[i], 1) for i, k in enumerate(PEAK_KINDS)}}
 
 
 def newton_iterations(p: int, m0: float, tol: float) -> int:

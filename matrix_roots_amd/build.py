@@ -19,7 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmatrix_roots.so")
-SOURCES = ["abi.cpp", "gram.hip", "apply.hip", "root.hip", "jacobi.hip", "cans.hip", "polar.hip", "step.hip"]
+SOURCES = ["abi.cpp", "gram.hip", "apply.hip", "root.hip", "jacobi.hip", "cans.hip", "polar.hip", "step.hip",
+           "peaks.hip"]
 ARCH = "gfx950"
 
 # Packed float32 VALU ops are kept out of every code object.

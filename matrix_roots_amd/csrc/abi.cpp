@@ -17,6 +17,7 @@
 
 #include "cans.hpp"
 #include "launch.hpp"
+#include "peaks.hpp"
 #include "polar.hpp"
 #include "step.hpp"
 #include "schedule.hpp"
@@ -270,6 +271,49 @@ int32_t mr_newton_schedule(double m0, double* scales, int32_t capacity, int32_t*
     for (int i = 0; i < K && i < capacity; ++i) scales[i] = tmp[i];
   if (fp64_steps) *fp64_steps = j;
   return K;
+}
+
+mr_status mr_measure_peaks(mr_peak_info* out, void* hip_stream) {
+  if (!out) return fail(MR_ERR_NULL, "out is NULL");
+  memset(out, 0, sizeof *out);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipDeviceProp_t prop;
+  if ((e = hipGetDeviceProperties(&prop, dev)) != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  out->cu_count = prop.multiProcessorCount;
+  out->clock_khz = prop.clockRate;
+  for (int k = 0; k < kPeakKinds; ++k)
+    out->prop_tflops[k] = prop.multiProcessorCount * (prop.clockRate * 1e3) * kMfmaFlopsPerClockCU[k] / 1e12;
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  hipEvent_t a = nullptr, b = nullptr;
+  if ((e = hipEventCreate(&a)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+  if ((e = hipEventCreate(&b)) != hipSuccess) {
+    (void)hipEventDestroy(a);
+    return hip_fail(e, "hipEventCreate");
+  }
+  // eight workgroups (two waves per SIMD) per CU, about 5 ms per kind at the
+  // vendor peak; the first launch of each kind warms the clock up
+  const int blocks = 8 * std::max(1, prop.multiProcessorCount);
+  const int iters[kPeakKinds] = {3000, 1500, 6000};
+  mr_status st = MR_OK;
+  for (int k = 0; k < kPeakKinds && st == MR_OK; ++k) {
+    double flops = 0.0;
+    float ms = 0.f;
+    e = launch_peak_loop(k, blocks, iters[k], &flops, s);
+    if (e == hipSuccess) e = hipEventRecord(a, s);
+    if (e == hipSuccess) e = launch_peak_loop(k, blocks, iters[k], &flops, s);
+    if (e == hipSuccess) e = hipEventRecord(b, s);
+    if (e == hipSuccess) e = hipEventSynchronize(b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+    if (e != hipSuccess)
+      st = hip_fail(e, "peak loop");
+    else
+      out->measured_tflops[k] = ms > 0.f ? flops / (ms * 1e-3) / 1e12 : 0.0;
+  }
+  (void)hipEventDestroy(a);
+  (void)hipEventDestroy(b);
+  return st;
 }
 
 int32_t mr_newton_iterations(int32_t p, double m0, double tol) {

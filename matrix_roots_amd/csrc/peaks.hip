@@ -1,0 +1,103 @@
+// Matrix-core rate probes: each wave keeps its accumulators in registers
+// and issues independent MFMA chains back to back, with no memory traffic,
+// so the measured rate is what the MFMA pipes deliver at the clock the chip
+// sustains under that load.
+#include "mr_common.hpp"
+#include "peaks.hpp"
+
+namespace mr {
+
+namespace {
+
+// 8 chains of 16 registers for f32 32x32x2 and f16 32x32x16, 16 chains of 8
+// registers for f64 16x16x4: with two waves per SIMD that keeps enough
+// independent MFMAs in flight to cover each instruction's pipeline latency
+// (4 chains reach only 78% of the fp16 rate).
+template <int KIND>
+struct PeakCfg;
+template <>
+struct PeakCfg<kPeakF32> {
+  static constexpr int CHAINS = 8;
+  static constexpr double FLOPS = 2.0 * 32 * 32 * 2;
+};
+template <>
+struct PeakCfg<kPeakF16> {
+  static constexpr int CHAINS = 8;
+  static constexpr double FLOPS = 2.0 * 32 * 32 * 16;
+};
+template <>
+struct PeakCfg<kPeakF64> {
+  static constexpr int CHAINS = 16;
+  static constexpr double FLOPS = 2.0 * 16 * 16 * 4;
+};
+
+}  // namespace
+
+// `sink` is written only when iters < 0, which the host never passes: the
+// branch keeps the chains live without any memory access.
+template <int KIND>
+__global__ __launch_bounds__(256, 2) void peak_kernel(int iters, float* sink) {
+  constexpr int C = PeakCfg<KIND>::CHAINS;
+  const float x = (float)(threadIdx.x & 63) * (1.0f / 64.0f);
+  float total = 0.0f;
+  if constexpr (KIND == kPeakF64) {
+    v4d acc[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) acc[c] = v4d{0.0, 0.0, 0.0, 0.0};
+    const double a = x, b = 1.0 - x;
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int c = 0; c < C; ++c) acc[c] = mfma_f64_16x16x4(a, b, acc[c]);
+#pragma unroll
+    for (int c = 0; c < C; ++c) total += (float)(acc[c][0] + acc[c][3]);
+  } else {
+    v16f acc[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[c][v] = 0.0f;
+    if constexpr (KIND == kPeakF32) {
+      const float a = x, b = 1.0f - x;
+      for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc[c] = mfma_f32_32x32x2(a, b, acc[c]);
+    } else {
+      v8h a, b;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        a[e] = (_Float16)(x * 0.125f * (float)e);
+        b[e] = (_Float16)(0.5f - x * 0.0625f * (float)e);
+      }
+      for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc[c] = mfma_f16_32x32x16(a, b, acc[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) total += acc[c][0] + acc[c][15];
+  }
+  if (iters < 0) sink[threadIdx.x] = total;
+}
+
+hipError_t launch_peak_loop(int kind, int blocks, int iters, double* flops, hipStream_t s) {
+  if (blocks <= 0 || iters <= 0) return hipErrorInvalidValue;
+  const double waves = (double)blocks * 4.0 * (double)iters;
+  switch (kind) {
+    case kPeakF32:
+      hipLaunchKernelGGL(peak_kernel<kPeakF32>, dim3(blocks), dim3(256), 0, s, iters, (float*)nullptr);
+      *flops = waves * PeakCfg<kPeakF32>::CHAINS * PeakCfg<kPeakF32>::FLOPS;
+      break;
+    case kPeakF64:
+      hipLaunchKernelGGL(peak_kernel<kPeakF64>, dim3(blocks), dim3(256), 0, s, iters, (float*)nullptr);
+      *flops = waves * PeakCfg<kPeakF64>::CHAINS * PeakCfg<kPeakF64>::FLOPS;
+      break;
+    case kPeakF16:
+      hipLaunchKernelGGL(peak_kernel<kPeakF16>, dim3(blocks), dim3(256), 0, s, iters, (float*)nullptr);
+      *flops = waves * PeakCfg<kPeakF16>::CHAINS * PeakCfg<kPeakF16>::FLOPS;
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mr

@@ -302,3 +302,9 @@ def test_momentum_and_hyperball_validation(lib):
                                    B.HyperballProblem(3, 5, P3, 5, P4, 5))
     need = lib.hyperball_update_batched_workspace(ctypes.addressof(arr), 2)
     assert need >= 3 * 8 * 512 * 2  # 512 workgroups of 8 rows for the 4096 x 1024 matrix
+
+
+def test_measure_peaks_rejects_null(lib):
+    """mr_measure_peaks validates its output pointer before any HIP call."""
+    assert lib.mr_measure_peaks(None, None) == 1  # MR_ERR_NULL
+    assert "NULL" in lib.mr_last_error_message().decode()
