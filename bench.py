@@ -50,19 +50,21 @@ def newton_flops(d: int, K: int, j: int, x_low: bool = True):
     kernel class that runs them: iterations t < K-1 take 4 symmetric products
     (M^2, T2^2, T4 M, X M), the last one only X M; t < j run M's products in
     float64, and the X product too unless x_low (then it runs on the
-    split-fp16 kernel, like every product of the float32 steps)."""
+    split-fp16 kernel, like every product of the float32 steps).  With x_low
+    the first X product (X0 = I) is no product: the init writes X1."""
     f64 = low = 0.0
     g = sym_gemm_flops(d)
     for t in range(K):
         m_products = 3 * g if t < K - 1 else 0.0
+        x_product = 0.0 if (x_low and t == 0) else g
         if t < j:
             f64 += m_products
             if x_low:
-                low += g
+                low += x_product
             else:
-                f64 += g
+                f64 += x_product
         else:
-            low += m_products + g
+            low += m_products + x_product
     return f64, low
 
 

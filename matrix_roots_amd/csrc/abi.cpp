@@ -627,6 +627,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
       b.partial = partial;
       b.partial_stride = P.partial_stride;
       b.x_low = x_low ? 1 : 0;
+      b.sched = sched;
       for (const auto& c : P.classes) {
         for (int k = 0; k < c.count; ++k) {
           const int slot = c.first_slot + k;
@@ -767,7 +768,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
             if ((st = traced(kTrNewton64, true, s, [&] { return launch_newton_stage(L64, kStageF64, g.vec64, s); },
                              "newton f64 stage")) != MR_OK)
               return st;
-            if (split) {
+            if (split && t > 0) {  // the first X update is part of the init
               const NewtonLaunch LX = make_launch(g, 0, stage, t, 1);
               if ((st = traced(kTrNewtonX3, true, s, [&] { return launch_newton_stage(LX, kStageX3B64, g.vecx3, s); },
                                "newton x3 X update")) != MR_OK)

@@ -112,6 +112,7 @@ struct RootBatch {
   int64_t partial_stride;  // doubles per matrix slot in `partial`
   int32_t x_low;           // X kept in float32 from the first step
   int32_t a_packed;        // A stored packed (MR_PACKED)
+  const double* sched;     // per-slot step scales (kMaxNewtonIters each)
 };
 
 // ------------------------------------------------ Newton: per size class

@@ -285,8 +285,11 @@ __global__ __launch_bounds__(64) void root_bound_kernel(RootState* state, const 
   st.flags = flags;
 }
 
-// M0 = ((A + A^T)/2 / s + eps I) / c into S0 and X0 = I into S1 (float64),
-// 32 x 32 tiles through LDS so both A reads are coalesced.
+// M0 = ((A + A^T)/2 / s + eps I) / c into S0 (float64), 32 x 32 tiles
+// through LDS so both A reads are coalesced.  X: with split storage the
+// first X update needs no product (X0 = I, so X1 = s0^(-1/4) (5 I - M0/s0) / 4)
+// and is written here, in the buffer iteration 1 reads; otherwise X0 = I
+// into S1 (float64) for the first step's product.
 template <typename TA>
 __global__ __launch_bounds__(256) void root_init_kernel(const RootBatch B) {
   __shared__ double ta[32][33];
@@ -305,7 +308,10 @@ __global__ __launch_bounds__(256) void root_init_kernel(const RootBatch B) {
   double* M = reinterpret_cast<double*>(J.region);
   double* X = reinterpret_cast<double*>(J.region + (int64_t)d * d * 8);
   const RolesS rs = roless(J.region, d, 0);
+  const SplitBuf x1 = roless(J.region, d, 1).X;
   const float xs = B.x_low ? x_store_scale(st) : 1.0f;
+  const double s0 = B.x_low ? B.sched[(int64_t)J.slot * kMaxNewtonIters] : 1.0;
+  const double q0 = (double)xs * pow(s0, -0.25), inv_s0 = 1.0 / s0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int r = ty + 8 * e;
@@ -317,7 +323,7 @@ __global__ __launch_bounds__(256) void root_init_kernel(const RootBatch B) {
       M[e] = v;
       if (B.x_low) {
         split_put(rs.Mx, e, (float)v);
-        split_put(rs.X, e, gi == gj ? xs : 0.f);
+        split_put(x1, e, (float)(q0 * ((gi == gj ? 1.25 : 0.0) - 0.25 * v * inv_s0)));
       } else {
         X[e] = (gi == gj) ? 1.0 : 0.0;
       }
@@ -346,7 +352,8 @@ struct StageJob {
 //   kStageF64  : t < j (float64 steps); with x_low not the X update
 //   kStageX3B64: t < j, X update only (x_low: float32 X, float64 M)
 //   kStageF32 / kStageX3: t >= j (float32 steps)
-// and the last iteration (t = K-1) only updates X (stage 0, job 1).
+// and the last iteration (t = K-1) only updates X (stage 0, job 1); with
+// x_low the first X update (t = 0) was written by root_init_kernel.
 __device__ __forceinline__ StageJob stage_job(const NewtonLaunch& L, int kind) {
   StageJob s;
   const int64_t b = blockIdx.x;
@@ -374,6 +381,7 @@ __device__ __forceinline__ StageJob stage_job(const NewtonLaunch& L, int kind) {
   else
     act = t >= j && t < K;
   if (t == K - 1 && !xupdate) act = false;
+  if (t == 0 && xupdate && L.x_low) act = false;
   s.active = act;
   s.s = act ? L.sched[(int64_t)slot * kMaxNewtonIters + t] : 1.0;
   s.m0 = st.eps / st.c;
