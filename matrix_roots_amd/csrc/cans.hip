@@ -19,6 +19,7 @@
 #include <type_traits>
 
 #include "cans.hpp"
+#include "epilogue.hpp"
 #include "gemm_core.hpp"
 #include "gemm_h16.hpp"
 
@@ -243,36 +244,12 @@ __global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1
 
   const bool whole = m0 + S::BM <= d && n0 + S::BN <= d;
   if (VEC == 8 && whole && (full || ti < tj)) {
-    // A lane holds 4 consecutive rows of one column per MFMA value group:
-    // 4 consecutive columns of the transposed row, one 8-byte store per array.
+    // whole tile (P, or above the diagonal): wide stores of the tile and of
+    // its transpose (P^T, or the mirror) through per-wave LDS slabs
+    static_assert(S::CB == 2, "slab epilogue takes two 32-column blocks per wave");
     const Split T = full ? cans_buf(region, d, kBufPt) : Out;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / S::WN, wn = wave % S::WN;
-#pragma unroll
-    for (int rb = 0; rb < S::RB; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < S::CB; ++cb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int gc = n0 + wn * (S::BN / S::WN) + cb * 32 + (lane & 31);
-          const int gr0 = m0 + wm * (S::BM / S::WM) + rb * 32 + 8 * g + 4 * (lane >> 5);
-          v4h hh, ll;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int64_t i = (int64_t)(gr0 + e) * d + gc;
-            E v = alpha * (E)acc[rb][cb][4 * g + e];
-            if (!full) v += beta * (E)get(Cin, i);
-            _Float16 h, l;
-            split_f32((float)v, h, l);
-            Out.hi[i] = h;
-            Out.lo[i] = l;
-            hh[e] = h;
-            ll[e] = l;
-          }
-          const int64_t t = (int64_t)gc * d + gr0;
-          *reinterpret_cast<v4h*>(T.hi + t) = hh;
-          *reinterpret_cast<v4h*>(T.lo + t) = ll;
-        }
+    wide_store_tile<S::RB, S::WN, E>(acc, reinterpret_cast<float*>(smem), m0, n0, Out.hi, Out.lo, d, T.hi, T.lo, d,
+                                     full ? nullptr : Cin.hi, full ? nullptr : Cin.lo, alpha, beta);
     return;
   }
   const Split Pt = cans_buf(region, d, kBufPt);

@@ -13,6 +13,7 @@
 
 #include <type_traits>
 
+#include "epilogue.hpp"
 #include "gemm_core.hpp"
 #include "gemm_h16.hpp"
 #include "polar.hpp"
@@ -235,37 +236,13 @@ __global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1 : 2) void polar_g
 
   const bool whole = m0 + S::BM <= rows && n0 + S::BN <= cols;
   if (VEC == 8 && whole && (FULL || ti < tj)) {
-    // A lane holds 4 consecutive rows of one column per MFMA value group:
-    // 4 consecutive columns of the transposed row, one 8-byte store per array.
+    // whole tile (update, or Gram above the diagonal): wide stores of the
+    // tile and of its transpose (T^T, or the mirror) through per-wave LDS slabs
+    static_assert(S::CB == 2, "slab epilogue takes two 32-column blocks per wave");
     const Split T = FULL ? Tt : Out;
     const int64_t ldt = FULL ? M : N;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / S::WN, wn = wave % S::WN;
-#pragma unroll
-    for (int rb = 0; rb < S::RB; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < S::CB; ++cb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int gc = n0 + wn * (S::BN / S::WN) + cb * 32 + (lane & 31);
-          const int gr0 = m0 + wm * (S::BM / S::WM) + rb * 32 + 8 * g + 4 * (lane >> 5);
-          v4h hh, ll;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int64_t i = (int64_t)(gr0 + e) * cols + gc;
-            E v = alpha * (E)acc[rb][cb][4 * g + e];
-            if (FULL) v += beta * (E)get(Aop, i);
-            _Float16 h, l;
-            split_f32((float)v, h, l);
-            Out.hi[i] = h;
-            Out.lo[i] = l;
-            hh[e] = h;
-            ll[e] = l;
-          }
-          const int64_t t = (int64_t)gc * ldt + gr0;
-          *reinterpret_cast<v4h*>(T.hi + t) = hh;
-          *reinterpret_cast<v4h*>(T.lo + t) = ll;
-        }
+    wide_store_tile<S::RB, S::WN, E>(acc, reinterpret_cast<float*>(smem), m0, n0, Out.hi, Out.lo, cols, T.hi, T.lo,
+                                     ldt, FULL ? Aop.hi : nullptr, FULL ? Aop.lo : nullptr, alpha, beta);
     return;
   }
   h16g_for_each<S>(acc, [&](int rr, int cc, float a) {

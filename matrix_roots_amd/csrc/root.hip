@@ -34,6 +34,7 @@
 // half-slots that the float64 M and X of that parity do not use.
 #include <math.h>
 
+#include "epilogue.hpp"
 #include "gemm_core.hpp"
 #include "launch.hpp"
 #include "schedule.hpp"
@@ -512,7 +513,7 @@ __device__ __forceinline__ SplitOps split_ops(const RolesS& r, int stage, int jo
 
 template <int VEC>
 __global__ __launch_bounds__(256, 2) void newton_x3_kernel(const NewtonLaunch L, int kind) {
-  __shared__ _Float16 smem[X3Tile::LDS_HALVES];
+  __shared__ __attribute__((aligned(16))) _Float16 smem[X3Tile::LDS_HALVES];
   const StageJob s = stage_job(L, kind);
   if (!s.active) return;
   const RolesS r = roless(s.region, s.d, L.t);
@@ -522,36 +523,11 @@ __global__ __launch_bounds__(256, 2) void newton_x3_kernel(const NewtonLaunch L,
   x3_nt_tile<VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, smem, acc);
   const int d = s.d;
   if (VEC == 8 && s.ti < s.tj && m0 + X3Tile::BM <= d && n0 + X3Tile::BN <= d) {
-    // Full off-diagonal tile: every element is above the diagonal.  A lane
-    // holds 4 consecutive rows of one column per MFMA value group, i.e. 4
-    // consecutive columns of the mirrored row: one 8-byte store per array.
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int gc = n0 + wn * 64 + cb * 32 + (lane & 31);
-          const int gr0 = m0 + wm * 64 + rb * 32 + 8 * g + 4 * (lane >> 5);
-          v4h hh, ll;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int64_t idx = (int64_t)(gr0 + e) * d + gc;
-            double val = o.alpha * (double)acc[rb][cb][4 * g + e];
-            if (o.has_cin) val += o.beta * (double)join_f32(o.Cin.hi[idx], o.Cin.lo[idx]);
-            _Float16 h, l;
-            split_f32((float)val, h, l);
-            o.C.hi[idx] = h;
-            o.C.lo[idx] = l;
-            hh[e] = h;
-            ll[e] = l;
-          }
-          const int64_t midx = (int64_t)gc * d + gr0;
-          *reinterpret_cast<v4h*>(o.C.hi + midx) = hh;
-          *reinterpret_cast<v4h*>(o.C.lo + midx) = ll;
-        }
+    // Off-diagonal tile, every element above the diagonal: the tile and its
+    // mirror with wide stores through per-wave LDS slabs (the main loop ended
+    // with a block barrier, so the operand stages are free).
+    wide_store_tile<2, 2, double>(acc, reinterpret_cast<float*>(smem), m0, n0, o.C.hi, o.C.lo, d, o.C.hi, o.C.lo, d,
+                                  o.has_cin ? o.Cin.hi : nullptr, o.has_cin ? o.Cin.lo : nullptr, o.alpha, o.beta);
     return;
   }
   f32_for_each(acc, [&](int rr, int cc, float v) {
