@@ -191,7 +191,7 @@ __global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1
                                          : PREC == 3      ? 2
                                          : FULL           ? MR_CANS_OCC_FULL
                                                           : MR_CANS_OCC_SYM) void cans_gemm_kernel(const CansLaunch L) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[PREC == 3 ? 2 * X3Tile::LDS_HALVES : h16_lds_bytes<S>()];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[PREC == 3 ? 2 * X3Tile::LDS_HALVES : h16_kernel_lds_bytes<S>(4 * kSlabFloats)];
   const int64_t b = blockIdx.x;
   int ci = 0;
   while (ci + 1 < L.ncls && b >= L.cls[ci + 1].block_begin) ++ci;
@@ -247,6 +247,7 @@ __global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1
     // whole tile (P, or above the diagonal): wide stores of the tile and of
     // its transpose (P^T, or the mirror) through per-wave LDS slabs
     static_assert(S::CB == 2, "slab epilogue takes two 32-column blocks per wave");
+    static_assert((S::THREADS / 64) * kSlabFloats * 4 <= (int)sizeof(smem), "one slab per wave fits in the LDS");
     const Split T = full ? cans_buf(region, d, kBufPt) : Out;
     wide_store_tile<S::RB, S::WN, E>(acc, reinterpret_cast<float*>(smem), m0, n0, Out.hi, Out.lo, d, T.hi, T.lo, d,
                                      full ? nullptr : Cin.hi, full ? nullptr : Cin.lo, alpha, beta);

@@ -3,19 +3,21 @@
 // A lane of a 32 x 32 block holds one column and 16 rows, so storing straight
 // from the accumulators issues 2-byte stores (split fp16 outputs) that cover
 // 64 bytes per row: the store and a_k-term load instructions then dominate
-// kernels whose contraction is short.  Instead, each wave moves one 32-row
-// slab of its sub-tile (two 32 x 32 blocks side by side) into a private,
-// padded LDS slab and reads it back twice:
+// kernels whose contraction is short.  Instead, each wave moves a 64-row
+// slab of its sub-tile (2 x 2 blocks of 32 x 32) into a private, padded LDS
+// slab and reads it back twice:
 //   * by rows, 8 consecutive columns per lane: 16-byte loads of the a_k term
 //     and 16-byte stores of the output row chunk (the final value is written
 //     back into the slab);
 //   * by columns, 8 consecutive rows per lane: 16-byte stores of the
 //     transposed (or mirrored) output.
-// Padding of 4 floats per 64-float row keeps the slab writes (32 lanes per
-// row) and the row-chunk reads (16 lanes over two rows) free of bank
-// conflicts; column reads see at most two-way conflicts.  The slab lives in
-// the LDS the operand stages used, after the block barrier that ends the
-// main loop.
+// Eight lanes cover the 64 rows of one output column, so a transposed store
+// instruction writes 128-byte row segments.  Padding of 4 floats per
+// 64-float row keeps the slab writes (32 lanes per row) and the row-chunk
+// reads (16 lanes over two rows) free of bank conflicts; the column reads
+// (4-byte, eight rows apart) see four-way conflicts, which cost far less than
+// the global stores they feed.  The slab lives in the LDS the operand stages
+// used, after the block barrier that ends the main loop.
 #pragma once
 
 #include "gemm_core.hpp"
@@ -23,8 +25,9 @@
 
 namespace mr {
 
-constexpr int kSlabLd = 64 + 4;          // floats per slab row
-constexpr int kSlabFloats = 32 * kSlabLd;  // one wave's slab: 8.5 KB
+constexpr int kSlabLd = 64 + 4;            // floats per slab row
+constexpr int kSlabRows = 64;
+constexpr int kSlabFloats = kSlabRows * kSlabLd;  // one wave's slab: 17 KB
 
 // LDS writes by some lanes of a wave are read by other lanes of the same
 // wave: wait for them, and keep the compiler from moving accesses across.
@@ -36,23 +39,24 @@ __device__ __forceinline__ void slab_fence() {
   asm volatile("" ::: "memory");
 }
 
-// Rows 0..31 of the slab = the 32 rows of blocks (a0 | a1), columns 0..63.
-__device__ __forceinline__ void slab_put(float* slab, const v16f& a0, const v16f& a1, int lane) {
+// Rows 32 h .. 32 h + 31 of the slab = the 32 rows of blocks (a0 | a1),
+// columns 0..63.
+__device__ __forceinline__ void slab_put(float* slab, int h, const v16f& a0, const v16f& a1, int lane) {
   const int c = lane & 31;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    const int r = f32_row(lane, v);
+    const int r = 32 * h + f32_row(lane, v);
     slab[r * kSlabLd + c] = a0[v];
     slab[r * kSlabLd + 32 + c] = a1[v];
   }
 }
 
-// f(r, c, v[8]) for the 256 row chunks (row r, columns c .. c+7), four per
+// f(r, c, v[8]) for the 512 row chunks (row r, columns c .. c+7), eight per
 // lane; when f returns true, v is written back into the slab.
 template <typename F>
 __device__ __forceinline__ void slab_rows(float* slab, int lane, F&& f) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const int q = lane + 64 * i;
     const int r = q >> 3, c = (q & 7) * 8;
     float* p = slab + r * kSlabLd + c;
@@ -66,14 +70,14 @@ __device__ __forceinline__ void slab_rows(float* slab, int lane, F&& f) {
   }
 }
 
-// f(c, r, v[8]) for the 256 column chunks (column c, rows r .. r+7), four
-// per lane; four consecutive lanes cover the 32 rows of one column.
+// f(c, r, v[8]) for the 512 column chunks (column c, rows r .. r+7), eight
+// per lane; eight consecutive lanes cover the 64 rows of one column.
 template <typename F>
 __device__ __forceinline__ void slab_cols(const float* slab, int lane, F&& f) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const int q = lane + 64 * i;
-    const int c = q >> 2, r = (q & 3) * 8;
+    const int c = q >> 3, r = (q & 7) * 8;
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = slab[(r + e) * kSlabLd + c];
@@ -93,7 +97,7 @@ __device__ __forceinline__ void split8(const float (&v)[8], v8h& hi, v8h& lo) {
 }
 
 // A whole tile of a GEMM whose waves form a grid WN wide, each wave owning
-// RB x 2 blocks of 32 x 32 (rows wm * 32 RB .., columns wn * 64 ..):
+// RB x 2 blocks of 32 x 32 (rows wm * 32 RB .., columns wn * 64 ..; RB even):
 //   out[r][c] = alpha acc + beta cin[r][c]   (cin optional: cin_hi == NULL)
 // stored in split form at out (row stride ldo) and, transposed, at t (row
 // stride ldt: t[c][r] = out[r][c]); cin has out's layout.  E is the type the
@@ -107,10 +111,12 @@ __device__ __forceinline__ void wide_store_tile(const v16f (&acc)[RB][2], float*
                                                 const _Float16* cin_lo, E alpha, E beta) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
+  static_assert(RB % 2 == 0, "64-row slabs");
   float* slab = lds + wave * kSlabFloats;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    slab_put(slab, acc[rb][0], acc[rb][1], lane);
+  for (int rb = 0; rb < RB; rb += 2) {
+    slab_put(slab, 0, acc[rb][0], acc[rb][1], lane);
+    slab_put(slab, 1, acc[rb + 1][0], acc[rb + 1][1], lane);
     slab_fence();
     const int r0 = m0 + wm * 32 * RB + rb * 32, c0 = n0 + wn * 64;
     slab_rows(slab, lane, [&](int r, int c, float (&v)[8]) {

@@ -388,6 +388,12 @@ template <class S>
 constexpr int h16_lds_bytes() {
   return (MR_H16_DL && H16DLOf<S>::LDS_BYTES > 2 * S::LDS_HALVES) ? H16DLOf<S>::LDS_BYTES : 2 * S::LDS_HALVES;
 }
+// ... or the wide-store epilogue's slabs (17 KB per wave), whichever is larger
+template <class S>
+constexpr int h16_kernel_lds_bytes(int slab_bytes_per_wave) {
+  return h16_lds_bytes<S>() > slab_bytes_per_wave * (S::THREADS / 64) ? h16_lds_bytes<S>()
+                                                                       : slab_bytes_per_wave * (S::THREADS / 64);
+}
 
 // Direct-to-LDS core where its preconditions hold (VEC 8 implies 16-byte
 // aligned operands with leading dimensions multiple of 8), else the

@@ -188,7 +188,7 @@ using PolarF16Shape = H16Shape<MR_POLAR_TILE, MR_POLAR_TILE, 2, MR_POLAR_TILE / 
 
 template <int VEC, int PREC, bool FULL, class S>
 __global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1 : 2) void polar_gemm_kernel(const PolarLaunch L) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[PREC == 3 ? 2 * X3Tile::LDS_HALVES : h16_lds_bytes<S>()];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[PREC == 3 ? 2 * X3Tile::LDS_HALVES : h16_kernel_lds_bytes<S>(4 * kSlabFloats)];
   const int64_t b = blockIdx.x;
   int ci = 0;
   while (ci + 1 < L.ncls && b >= L.cls[ci + 1].block_begin) ++ci;
@@ -239,6 +239,7 @@ __global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1 : 2) void polar_g
     // whole tile (update, or Gram above the diagonal): wide stores of the
     // tile and of its transpose (T^T, or the mirror) through per-wave LDS slabs
     static_assert(S::CB == 2, "slab epilogue takes two 32-column blocks per wave");
+    static_assert((S::THREADS / 64) * kSlabFloats * 4 <= (int)sizeof(smem), "one slab per wave fits in the LDS");
     const Split T = FULL ? Tt : Out;
     const int64_t ldt = FULL ? M : N;
     wide_store_tile<S::RB, S::WN, E>(acc, reinterpret_cast<float*>(smem), m0, n0, Out.hi, Out.lo, cols, T.hi, T.lo,

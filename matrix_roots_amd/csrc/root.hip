@@ -526,6 +526,7 @@ __global__ __launch_bounds__(256, 2) void newton_x3_kernel(const NewtonLaunch L,
     // Off-diagonal tile, every element above the diagonal: the tile and its
     // mirror with wide stores through per-wave LDS slabs (the main loop ended
     // with a block barrier, so the operand stages are free).
+    static_assert(4 * kSlabFloats * 4 <= (int)sizeof(smem), "four slabs fit in the operand stages");
     wide_store_tile<2, 2, double>(acc, reinterpret_cast<float*>(smem), m0, n0, o.C.hi, o.C.lo, d, o.C.hi, o.C.lo, d,
                                   o.has_cin ? o.Cin.hi : nullptr, o.has_cin ? o.Cin.lo : nullptr, o.alpha, o.beta);
     return;
