@@ -243,14 +243,15 @@ __global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1
     h16_nt_tile_auto<S, VEC>(A.hi, d, Bm.hi, d, d, d, d, m0, n0, smem, acc);
 
   const bool whole = m0 + S::BM <= d && n0 + S::BN <= d;
-  if (VEC == 8 && whole && (full || ti < tj)) {
-    // whole tile (P, or above the diagonal): wide stores of the tile and of
-    // its transpose (P^T, or the mirror) through per-wave LDS slabs
+  if (VEC == 8 && whole && (full || ti <= tj)) {
+    // whole tile (P, or on or above the diagonal): wide stores of the tile
+    // and of its transpose (P^T, or the mirror) through per-wave LDS slabs
     static_assert(S::CB == 2, "slab epilogue takes two 32-column blocks per wave");
     static_assert((S::THREADS / 64) * kSlabFloats * 4 <= (int)sizeof(smem), "one slab per wave fits in the LDS");
     const Split T = full ? cans_buf(region, d, kBufPt) : Out;
     wide_store_tile<S::RB, S::WN, E>(acc, reinterpret_cast<float*>(smem), m0, n0, Out.hi, Out.lo, d, T.hi, T.lo, d,
-                                     full ? nullptr : Cin.hi, full ? nullptr : Cin.lo, alpha, beta);
+                                     full ? nullptr : Cin.hi, full ? nullptr : Cin.lo, alpha, beta, E(0),
+                                     !full && ti == tj);
     return;
   }
   const Split Pt = cans_buf(region, d, kBufPt);

@@ -98,17 +98,22 @@ __device__ __forceinline__ void split8(const float (&v)[8], v8h& hi, v8h& lo) {
 
 // A whole tile of a GEMM whose waves form a grid WN wide, each wave owning
 // RB x 2 blocks of 32 x 32 (rows wm * 32 RB .., columns wn * 64 ..; RB even):
-//   out[r][c] = alpha acc + beta cin[r][c]   (cin optional: cin_hi == NULL)
-// stored in split form at out (row stride ldo) and, transposed, at t (row
-// stride ldt: t[c][r] = out[r][c]); cin has out's layout.  E is the type the
-// combination is formed in before the float32 rounding.  The caller has
-// passed a block barrier since the LDS was last used for operands; `lds`
-// holds kSlabFloats floats per wave.
+//   out[r][c] = alpha acc + beta cin[r][c] (+ gamma on the diagonal)
+// (cin optional: cin_hi == NULL) stored in split form at out (row stride
+// ldo) and, transposed, at t (row stride ldt: t[c][r] = out[r][c]); cin has
+// out's layout.  E is the type the combination is formed in before the
+// float32 rounding.  diag: a symmetric output's diagonal tile (m0 == n0,
+// t == out): only elements with r <= c are stored, and the mirror stores
+// only those with r < c, so the tile's lower triangle is the mirror of its
+// upper one (16-byte stores away from the diagonal, 2-byte stores on the
+// chunks it crosses).  The caller has passed a block barrier since the LDS
+// was last used for operands; `lds` holds kSlabFloats floats per wave.
 template <int RB, int WN, typename E>
 __device__ __forceinline__ void wide_store_tile(const v16f (&acc)[RB][2], float* lds, int m0, int n0,
                                                 _Float16* out_hi, _Float16* out_lo, int64_t ldo, _Float16* t_hi,
                                                 _Float16* t_lo, int64_t ldt, const _Float16* cin_hi,
-                                                const _Float16* cin_lo, E alpha, E beta) {
+                                                const _Float16* cin_lo, E alpha, E beta, E gamma = E(0),
+                                                bool diag = false) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
   static_assert(RB % 2 == 0, "64-row slabs");
@@ -120,7 +125,9 @@ __device__ __forceinline__ void wide_store_tile(const v16f (&acc)[RB][2], float*
     slab_fence();
     const int r0 = m0 + wm * 32 * RB + rb * 32, c0 = n0 + wn * 64;
     slab_rows(slab, lane, [&](int r, int c, float (&v)[8]) {
-      const int64_t idx = (int64_t)(r0 + r) * ldo + c0 + c;
+      const int gr = r0 + r, gc = c0 + c;
+      if (diag && gr > gc + 7) return false;  // wholly below the diagonal
+      const int64_t idx = (int64_t)gr * ldo + gc;
       v8h ch = {}, cl = {};
       if (cin_hi) {
         ch = *reinterpret_cast<const v8h*>(cin_hi + idx);
@@ -130,21 +137,42 @@ __device__ __forceinline__ void wide_store_tile(const v16f (&acc)[RB][2], float*
       for (int e = 0; e < 8; ++e) {
         E val = alpha * (E)v[e];
         if (cin_hi) val += beta * (E)join_f32(ch[e], cl[e]);
+        if (diag && gr == gc + e) val += gamma;
         v[e] = (float)val;
       }
       v8h hh, ll;
       split8(v, hh, ll);
-      *reinterpret_cast<v8h*>(out_hi + idx) = hh;
-      *reinterpret_cast<v8h*>(out_lo + idx) = ll;
+      if (!diag || gr <= gc) {
+        *reinterpret_cast<v8h*>(out_hi + idx) = hh;
+        *reinterpret_cast<v8h*>(out_lo + idx) = ll;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (gc + e >= gr) {
+            out_hi[idx + e] = hh[e];
+            out_lo[idx + e] = ll[e];
+          }
+      }
       return true;
     });
     slab_fence();
     slab_cols(slab, lane, [&](int c, int r, const float (&v)[8]) {
-      const int64_t tidx = (int64_t)(c0 + c) * ldt + r0 + r;
+      const int gc = c0 + c, gr = r0 + r;  // source rows gr .. gr+7 of column gc
+      if (diag && gr >= gc) return;        // no source element above the diagonal
+      const int64_t tidx = (int64_t)gc * ldt + gr;
       v8h hh, ll;
       split8(v, hh, ll);
-      *reinterpret_cast<v8h*>(t_hi + tidx) = hh;
-      *reinterpret_cast<v8h*>(t_lo + tidx) = ll;
+      if (!diag || gr + 7 < gc) {
+        *reinterpret_cast<v8h*>(t_hi + tidx) = hh;
+        *reinterpret_cast<v8h*>(t_lo + tidx) = ll;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (gr + e < gc) {
+            t_hi[tidx + e] = hh[e];
+            t_lo[tidx + e] = ll[e];
+          }
+      }
     });
     slab_fence();
   }

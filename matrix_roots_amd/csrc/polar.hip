@@ -235,15 +235,17 @@ __global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1 : 2) void polar_g
   const Split Tt = polar_buf(region, M, N, 2);
 
   const bool whole = m0 + S::BM <= rows && n0 + S::BN <= cols;
-  if (VEC == 8 && whole && (FULL || ti < tj)) {
-    // whole tile (update, or Gram above the diagonal): wide stores of the
-    // tile and of its transpose (T^T, or the mirror) through per-wave LDS slabs
+  if (VEC == 8 && whole && (FULL || ti <= tj)) {
+    // whole tile (update, or Gram on or above the diagonal): wide stores of
+    // the tile and of its transpose (T^T, or the mirror) through per-wave LDS
+    // slabs
     static_assert(S::CB == 2, "slab epilogue takes two 32-column blocks per wave");
     static_assert((S::THREADS / 64) * kSlabFloats * 4 <= (int)sizeof(smem), "one slab per wave fits in the LDS");
     const Split T = FULL ? Tt : Out;
     const int64_t ldt = FULL ? M : N;
     wide_store_tile<S::RB, S::WN, E>(acc, reinterpret_cast<float*>(smem), m0, n0, Out.hi, Out.lo, cols, T.hi, T.lo,
-                                     ldt, FULL ? Aop.hi : nullptr, FULL ? Aop.lo : nullptr, alpha, beta);
+                                     ldt, FULL ? Aop.hi : nullptr, FULL ? Aop.lo : nullptr, alpha, beta, E(0),
+                                     !FULL && ti == tj);
     return;
   }
   h16g_for_each<S>(acc, [&](int rr, int cc, float a) {

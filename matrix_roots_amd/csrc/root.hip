@@ -522,13 +522,14 @@ __global__ __launch_bounds__(256, 2) void newton_x3_kernel(const NewtonLaunch L,
   v16f acc[2][2];
   x3_nt_tile<VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, smem, acc);
   const int d = s.d;
-  if (VEC == 8 && s.ti < s.tj && m0 + X3Tile::BM <= d && n0 + X3Tile::BN <= d) {
-    // Off-diagonal tile, every element above the diagonal: the tile and its
+  if (VEC == 8 && s.ti <= s.tj && m0 + X3Tile::BM <= d && n0 + X3Tile::BN <= d) {
+    // Whole tile on or above the diagonal: the upper elements and their
     // mirror with wide stores through per-wave LDS slabs (the main loop ended
     // with a block barrier, so the operand stages are free).
     static_assert(4 * kSlabFloats * 4 <= (int)sizeof(smem), "four slabs fit in the operand stages");
     wide_store_tile<2, 2, double>(acc, reinterpret_cast<float*>(smem), m0, n0, o.C.hi, o.C.lo, d, o.C.hi, o.C.lo, d,
-                                  o.has_cin ? o.Cin.hi : nullptr, o.has_cin ? o.Cin.lo : nullptr, o.alpha, o.beta);
+                                  o.has_cin ? o.Cin.hi : nullptr, o.has_cin ? o.Cin.lo : nullptr, o.alpha, o.beta,
+                                  o.gamma, s.ti == s.tj);
     return;
   }
   f32_for_each(acc, [&](int rr, int cc, float v) {
