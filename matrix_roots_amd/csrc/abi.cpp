@@ -24,6 +24,10 @@
 
 using namespace mr;
 
+#ifndef MR_NEWTON_BIG_FIRST
+#define MR_NEWTON_BIG_FIRST 1
+#endif
+
 namespace {
 
 thread_local std::string g_err;
@@ -732,7 +736,10 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
       L.sched = sched;
       L.x_low = x_low ? 1 : 0;
       L.job_only = job_only;
-      for (int ci : g.cls) {
+      // Largest Grams first: their long tiles start early and the short
+      // tiles of the small classes fill the launch's tail.
+      for (size_t q = 0; q < g.cls.size(); ++q) {
+        const int ci = MR_NEWTON_BIG_FIRST ? g.cls[g.cls.size() - 1 - q] : g.cls[q];
         const auto& c = P.classes[ci];
         NewtonClass& C = L.cls[L.ncls++];
         C.region = base + c.region_off;
