@@ -249,7 +249,12 @@ __global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1
     static_assert(S::CB == 2, "slab epilogue takes two 32-column blocks per wave");
     static_assert((S::THREADS / 64) * kSlabFloats * 4 <= (int)sizeof(smem), "one slab per wave fits in the LDS");
     const Split T = full ? cans_buf(region, d, kBufPt) : Out;
-    wide_store_tile<S::RB, S::WN, E>(acc, reinterpret_cast<float*>(smem), m0, n0, Out.hi, Out.lo, d, T.hi, T.lo, d,
+    // fp16 products read P and P^T as operands only (hi halves): P's lo half
+    // is kept for the last step's residual, P^T's never
+    const bool p_lo = PREC == 3 || k == kCansSteps - 1;
+    _Float16* out_lo = full && !p_lo ? nullptr : Out.lo;
+    _Float16* t_lo = full && PREC != 3 ? nullptr : T.lo;
+    wide_store_tile<S::RB, S::WN, E>(acc, reinterpret_cast<float*>(smem), m0, n0, Out.hi, out_lo, d, T.hi, t_lo, d,
                                      full ? nullptr : Cin.hi, full ? nullptr : Cin.lo, alpha, beta, E(0),
                                      !full && ti == tj);
     return;

@@ -101,7 +101,8 @@ __device__ __forceinline__ void split8(const float (&v)[8], v8h& hi, v8h& lo) {
 //   out[r][c] = alpha acc + beta cin[r][c] (+ gamma on the diagonal)
 // (cin optional: cin_hi == NULL) stored in split form at out (row stride
 // ldo) and, transposed, at t (row stride ldt: t[c][r] = out[r][c]); cin has
-// out's layout.  E is the type the combination is formed in before the
+// out's layout.  out_lo or t_lo NULL: that lo half is not stored (outputs
+// only ever read as fp16 operands).  E is the type the combination is formed in before the
 // float32 rounding.  diag: a symmetric output's diagonal tile (m0 == n0,
 // t == out): only elements with r <= c are stored, and the mirror stores
 // only those with r < c, so the tile's lower triangle is the mirror of its
@@ -144,13 +145,13 @@ __device__ __forceinline__ void wide_store_tile(const v16f (&acc)[RB][2], float*
       split8(v, hh, ll);
       if (!diag || gr <= gc) {
         *reinterpret_cast<v8h*>(out_hi + idx) = hh;
-        *reinterpret_cast<v8h*>(out_lo + idx) = ll;
+        if (out_lo) *reinterpret_cast<v8h*>(out_lo + idx) = ll;
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (gc + e >= gr) {
             out_hi[idx + e] = hh[e];
-            out_lo[idx + e] = ll[e];
+            if (out_lo) out_lo[idx + e] = ll[e];
           }
       }
       return true;
@@ -164,13 +165,13 @@ __device__ __forceinline__ void wide_store_tile(const v16f (&acc)[RB][2], float*
       split8(v, hh, ll);
       if (!diag || gr + 7 < gc) {
         *reinterpret_cast<v8h*>(t_hi + tidx) = hh;
-        *reinterpret_cast<v8h*>(t_lo + tidx) = ll;
+        if (t_lo) *reinterpret_cast<v8h*>(t_lo + tidx) = ll;
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (gr + e < gc) {
             t_hi[tidx + e] = hh[e];
-            t_lo[tidx + e] = ll[e];
+            if (t_lo) t_lo[tidx + e] = ll[e];
           }
       }
     });

@@ -243,7 +243,12 @@ __global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1 : 2) void polar_g
     static_assert((S::THREADS / 64) * kSlabFloats * 4 <= (int)sizeof(smem), "one slab per wave fits in the LDS");
     const Split T = FULL ? Tt : Out;
     const int64_t ldt = FULL ? M : N;
-    wide_store_tile<S::RB, S::WN, E>(acc, reinterpret_cast<float*>(smem), m0, n0, Out.hi, Out.lo, cols, T.hi, T.lo,
+    // fp16 products read X^T and A as operands only (hi halves); their lo
+    // halves are kept for the last step (finalize and residual)
+    const bool keep_lo = PREC == 3 || k == kCansSteps - 1;
+    _Float16* out_lo = !FULL && !keep_lo ? nullptr : Out.lo;
+    _Float16* t_lo = keep_lo ? T.lo : nullptr;
+    wide_store_tile<S::RB, S::WN, E>(acc, reinterpret_cast<float*>(smem), m0, n0, Out.hi, out_lo, cols, T.hi, t_lo,
                                      ldt, FULL ? Aop.hi : nullptr, FULL ? Aop.lo : nullptr, alpha, beta, E(0),
                                      !FULL && ti == tj);
     return;
