@@ -1,7 +1,7 @@
 """Summarise rocprofv3 output for one kernel of this library.
 
     python -m matrix_roots_amd.profile_summary \
-        --fetch gpurun_out/pmc_fetch --write gpurun_out/pmc_write \
+        --fetch prof/fetch --write prof/write \
         --kernel newton_f64_kernel --copy-mib 1024 [--out profiles/x.md]
 
 Reads the `*counter_collection.csv` files of two `rocprofv3 --pmc` runs
