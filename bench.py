@@ -531,19 +531,26 @@ def main(argv=None) -> int:
             if name == "newton_x3":  # three fp16 MFMA products per float32-accurate product
                 ent["mfma_tflops"] = round(3 * tf, 2)
         kernels[name] = ent
-    dom = max(kernels.items(), key=lambda kv: kv[1]["ms_total"])
-    dname, dk = dom
-    roofline = {"bound": "mfma", "kernel": dname, "achieved": dk.get("tflops"), "peak": dk.get("peak"),
-                "unit": "TFLOP/s", "frac": dk.get("frac"), "traffic": recorded_traffic(dname, args.workload),
-                "achieved_per_launch": "algorithmic flops of the class over the timed steps / sum of its "
-                                       "event-measured launch durations"}
-    if dname == "newton_x3":
-        # float32-accurate products, each three fp16 MFMA products (hi*hi, hi*lo, lo*hi)
-        roofline.update({"mfma_achieved": dk.get("mfma_tflops"),
-                         "mfma_frac": round(dk["mfma_tflops"] / PEAK_TFLOPS["f16"], 4),
-                         "frac_of_f32_peak": round(dk["tflops"] / PEAK_TFLOPS["f32"], 4),
-                         "note": "achieved/frac count the float32-accurate products against the fp16 MFMA peak "
-                                 "the kernel runs on; mfma_* count the three fp16 products each takes"})
+    def roofline_for(name):
+        k = kernels[name]
+        r = {"bound": "mfma", "kernel": name, "achieved": k.get("tflops"), "peak": k.get("peak"),
+             "unit": "TFLOP/s", "frac": k.get("frac"), "traffic": recorded_traffic(name, args.workload),
+             "achieved_per_launch": "algorithmic flops of the class over the timed steps / sum of its "
+                                    "event-measured launch durations"}
+        if name == "newton_x3":
+            # float32-accurate products, each three fp16 MFMA products (hi*hi, hi*lo, lo*hi)
+            r.update({"mfma_achieved": k.get("mfma_tflops"),
+                      "mfma_frac": round(k["mfma_tflops"] / PEAK_TFLOPS["f16"], 4),
+                      "frac_of_f32_peak": round(k["tflops"] / PEAK_TFLOPS["f32"], 4),
+                      "note": "achieved/frac count the float32-accurate products against the fp16 MFMA peak "
+                              "the kernel runs on; mfma_* count the three fp16 products each takes"})
+        return r
+
+    dname = max(kernels.items(), key=lambda kv: kv[1]["ms_total"])[0]
+    roofline = roofline_for(dname)
+    # newton_f64 and newton_x3 take about the same share of the step, so
+    # which one leads changes from run to run: every MFMA class's roofline
+    rooflines = {n: roofline_for(n) for n in kernels if "tflops" in kernels[n]}
 
     size_classes = None
     if args.per_size_class:
@@ -581,6 +588,7 @@ def main(argv=None) -> int:
         "pct_fp32_mfma_peak": round(100 * step_flops / (ms_per_step / 1e3) / 1e12 / PEAK_TFLOPS["f32"], 2),
         "newton_iters": {"min": kmin, "max": kmax},
         "roofline": roofline,
+        "rooflines": rooflines,
         "kernels": kernels,
         "cpu_baseline": cpu,
         "peaks": peaks,

@@ -28,12 +28,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # Sources whose kernels a counter record covers, per kernel family.
 KERNEL_SOURCES = {
     "quarter": ("csrc/gemm_core.hpp", "csrc/mr_common.hpp", "csrc/launch.hpp", "csrc/schedule.hpp",
-                "csrc/root.hip", "csrc/gram.hip", "csrc/apply.hip"),
+                "csrc/epilogue.hpp", "csrc/root.hip", "csrc/gram.hip", "csrc/apply.hip"),
     "cans": ("csrc/gemm_core.hpp", "csrc/gemm_h16.hpp", "csrc/mr_common.hpp", "csrc/launch.hpp", "csrc/cans.hpp",
-             "csrc/cans.hip"),
+             "csrc/epilogue.hpp", "csrc/cans.hip"),
     "step": ("csrc/mr_common.hpp", "csrc/launch.hpp", "csrc/step.hpp", "csrc/step.hip"),
     "polar": ("csrc/gemm_core.hpp", "csrc/gemm_h16.hpp", "csrc/mr_common.hpp", "csrc/launch.hpp", "csrc/cans.hpp",
-              "csrc/polar.hpp", "csrc/polar.hip"),
+              "csrc/epilogue.hpp", "csrc/polar.hpp", "csrc/polar.hip"),
 }
 
 
