@@ -405,8 +405,17 @@ struct F64Loader {
   static constexpr int ELEMS = F64Tile::BM * BK;
   static constexpr int PER = ELEMS / (F64Tile::THREADS * VEC);
   static constexpr int VPR_K = BK / VEC;            // vectors per row when !TRANS
-  static constexpr int VPR_I = F64Tile::BM / VEC;   // vectors per k-row when TRANS
   double reg[PER * VEC];
+
+  // TRANS (VEC consecutive i of one k per load): consecutive lanes take
+  // consecutive k, so the transposed LDS stores of a wave land on
+  // consecutive doubles of a row (16 lanes per row) instead of rows VEC
+  // apart, which put eight lanes on one bank pair; the global loads then
+  // cover 4 VEC floats of 16 rows per wave instruction.
+  __device__ __forceinline__ static void trans_slot(int idx, int& i, int& k) {
+    k = idx % BK;
+    i = (idx / BK) * VEC;
+  }
 
   __device__ __forceinline__ void load(const TIn* __restrict__ P, int64_t ld, int rows, int K, int r0,
                                        int k0, int tid) {
@@ -421,9 +430,11 @@ struct F64Loader {
       } else if constexpr (!TRANS) {
         i = idx / VPR_K;
         k = (idx % VPR_K) * VEC;
+      } else if constexpr (VEC == 1) {  // the element path's own order (store())
+        k = idx / F64Tile::BM;
+        i = idx % F64Tile::BM;
       } else {
-        k = idx / VPR_I;
-        i = (idx % VPR_I) * VEC;
+        trans_slot(idx, i, k);
       }
       const int gi = r0 + i, gk = k0 + k;
       if constexpr (VEC == 1) {
@@ -478,8 +489,8 @@ struct F64Loader {
           *reinterpret_cast<v2d*>(s + i * F64Tile::LDW + k + e) = v;
         }
       } else {
-        const int k = idx / VPR_I;
-        const int i = (idx % VPR_I) * VEC;
+        int i, k;
+        trans_slot(idx, i, k);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) s[(i + e) * F64Tile::LDW + k] = reg[p * VEC + e];
       }
