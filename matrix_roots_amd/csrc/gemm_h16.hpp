@@ -2,135 +2,27 @@
 // operands stored as fp16 arrays (the hi half of the split storage): one
 // v_mfma_f32_32x32x16_f16 per 32 x 32 x 16 block.
 //
-// Work split as in the other cores: 256 threads = 4 waves in a 2 x 2 grid,
-// each wave owns a 64 x 64 quarter of the 128 x 128 block tile (2 x 2 MFMA
-// blocks); K advances in chunks of BK through double-buffered LDS with one
-// barrier per chunk.  A and B rows are K-contiguous ("NT"), so both operand
-// panels are read along rows and staged the same way.
+// Two cores over one block-shape description (H16Shape: BM x BN block tile,
+// WM x WN waves, each wave (BM / WM) x (BN / WN) in 32 x 32 MFMA blocks).
+// A and B rows are K-contiguous ("NT"), so both operand panels are read
+// along rows and staged the same way:
+//   * h16g_nt_tile: register-staged, K in chunks of BK through two padded LDS
+//     stages with one barrier per chunk (any size and alignment);
+//   * h16dl_nt_tile: direct global -> LDS copies, unpadded XOR-swizzled rows,
+//     K-chunks of 64 (contraction a multiple of 64, 16-byte rows).
 #pragma once
 
 #include "mr_common.hpp"
 
-#ifndef MR_H16_BK
-#define MR_H16_BK 64
-#endif
-
 namespace mr {
 
-struct H16Tile {
-  static constexpr int BM = 128, BN = 128, BK = MR_H16_BK, PAD = 8, LDW = BK + PAD;  // halves per LDS row
-  static constexpr int THREADS = 256;
-  static constexpr int ARR = BM * LDW;  // halves per operand array
-  static constexpr int STAGE = 2 * ARR;
-  static constexpr int LDS_HALVES = 2 * STAGE;
-};
-
-// A BM x BK chunk of a K-contiguous fp16 operand.  VEC = 8 (16-byte loads:
-// ld and K multiples of 8, 16-byte aligned array) or 1.
-template <int VEC>
-struct H16Loader {
-  static constexpr int BK = H16Tile::BK;
-  static constexpr int GPR = BK / 8;  // groups of 8 halves per row
-  static constexpr int PER = (H16Tile::BM * BK) / (H16Tile::THREADS * 8);
-  v8h r[PER];
-
-  __device__ __forceinline__ void load(const _Float16* __restrict__ P, int64_t ld, int rows, int K, int r0, int k0,
-                                       int tid) {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      int row, grp;
-      tile_slot<GPR>(tid + p * H16Tile::THREADS, row, grp);
-      const int gr = r0 + row, gk = k0 + grp * 8;
-      const int64_t off = (int64_t)gr * ld + gk;
-      if constexpr (VEC == 8) {
-        v8h h = {};
-        if (gr < rows && gk < K) h = *reinterpret_cast<const v8h*>(P + off);
-        r[p] = h;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r[p][e] = (gr < rows && gk + e < K) ? P[off + e] : (_Float16)0.0f;
-      }
-    }
-  }
-  __device__ __forceinline__ void store(_Float16* __restrict__ dst, int tid) const {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      int row, grp;
-      tile_slot<GPR>(tid + p * H16Tile::THREADS, row, grp);
-      *reinterpret_cast<v8h*>(dst + row * H16Tile::LDW + grp * 8) = r[p];
-    }
-  }
-};
-
-__device__ __forceinline__ void h16_chunk(const _Float16* __restrict__ st, v16f (&acc)[2][2], int lane, int wm,
-                                          int wn) {
-  const _Float16* As = st;
-  const _Float16* Bs = st + H16Tile::ARR;
-  const int koff = (lane >> 5) * 8;
-#pragma unroll
-  for (int ks = 0; ks < H16Tile::BK / 16; ++ks) {
-    v8h a[2], b[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-      a[rb] = *reinterpret_cast<const v8h*>(As + (wm * 64 + rb * 32 + (lane & 31)) * H16Tile::LDW + ks * 16 + koff);
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-      b[cb] = *reinterpret_cast<const v8h*>(Bs + (wn * 64 + cb * 32 + (lane & 31)) * H16Tile::LDW + ks * 16 + koff);
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma_f16_32x32x16(a[rb], b[cb], acc[rb][cb]);
-  }
-}
-
-// acc (2 x 2 blocks of 32 x 32 per wave, layout of f32_for_each) =
-// A[m0:m0+128, :K] * B[n0:n0+128, :K]^T; rows beyond M / N and columns
-// beyond K read as zero.
-template <int VEC>
-__device__ __forceinline__ void h16_nt_tile(const _Float16* __restrict__ A, int64_t lda,
-                                            const _Float16* __restrict__ B, int64_t ldb, int M, int N, int K,
-                                            int m0, int n0, _Float16* __restrict__ lds, v16f (&acc)[2][2]) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  constexpr int BK = H16Tile::BK;
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.f;
-  H16Loader<VEC> la, lb;
-  la.load(A, lda, M, K, m0, 0, tid);
-  lb.load(B, ldb, N, K, n0, 0, tid);
-  la.store(lds, tid);
-  lb.store(lds + H16Tile::ARR, tid);
-  __syncthreads();
-  int stage = 0;
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    const bool more = k0 + BK < K;
-    if (more) {
-      la.load(A, lda, M, K, m0, k0 + BK, tid);
-      lb.load(B, ldb, N, K, n0, k0 + BK, tid);
-    }
-    h16_chunk(lds + stage * H16Tile::STAGE, acc, lane, wm, wn);
-    if (more) {
-      _Float16* nxt = lds + (stage ^ 1) * H16Tile::STAGE;
-      la.store(nxt, tid);
-      lb.store(nxt + H16Tile::ARR, tid);
-    }
-    __syncthreads();
-    stage ^= 1;
-  }
-}
-
-// ------------------------------------------------- block shapes (generic)
+// ------------------------------------------------------------ block shapes
 // BM x BN block tile, WM x WN waves, each wave (BM / WM) x (BN / WN) in 32 x 32
 // MFMA blocks (RB x CB of them), K in chunks of BK through two LDS stages.
-// H16Shape<128, 128, 2, 2> is the core above; H16Shape<256, 256, 2, 4> (512
-// threads, 128 accumulator registers per lane, 144 KB of LDS: one block and
-// two waves per SIMD) reads each operand panel half as often.
+// H16Shape<128, 128, 2, 2> (256 threads, two blocks per CU) and
+// H16Shape<256, 256, 2, 4> (512 threads, 128 accumulator registers per lane,
+// one block and two waves per SIMD: each operand panel read half as often)
+// are the shapes in use.
 template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64>
 struct H16Shape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
