@@ -42,6 +42,12 @@ __device__ __forceinline__ double jac_ld(const void* A, int64_t idx) {
   return (double)reinterpret_cast<const TA*>(A)[idx];
 }
 
+constexpr int kWBatch = 8;  // eigenvector element pairs per thread per memory round trip
+// Upper pairs (kr <= kc) of the rotations of one round, per thread: the
+// assignment is fixed for the whole kernel, so it is computed once and not
+// by integer divisions in every round.
+constexpr int kPairsPerThread = ((kJN / 2) * (kJN / 2 + 1) / 2 + 255) / 256;
+
 template <typename TA>
 __global__ __launch_bounds__(256) void jacobi_kernel(const JacobiBatch B) {
   __shared__ double sM[kJN * kJLD];
@@ -98,6 +104,29 @@ __global__ __launch_bounds__(256) void jacobi_kernel(const JacobiBatch B) {
     for (int idx = tid; idx < d * d; idx += 256) W[idx] = ((idx / d) == (idx % d)) ? 1.0 : 0.0;
     f2 = jac_sum(f2, red);  // also orders the W and sM writes before the sweeps
     const double tau = fmax(1e-15 * sqrt(f2), 1e-300);
+    // this thread's upper pairs u = tid + 256 m of the np x np rotation grid
+    int pkr[kPairsPerThread], pkc[kPairsPerThread];
+    {
+      const int npairs = np * (np + 1) / 2;
+#pragma unroll
+      for (int m = 0; m < kPairsPerThread; ++m) {
+        int u = tid + 256 * m, kr = 0;
+        if (u >= npairs) {
+          pkr[m] = -1;
+          pkc[m] = 0;
+          continue;
+        }
+        while (u >= np - kr) {  // row kr holds np - kr upper pairs
+          u -= np - kr;
+          ++kr;
+        }
+        pkr[m] = kr;
+        pkc[m] = kr + u;
+      }
+    }
+    // the first of this thread's (k, i) eigenvector pairs idx = tid + 256 m
+    // and the step between consecutive ones, without divisions in the rounds
+    const int wk0 = tid / d, wi0 = tid % d, wdk = 256 / d, wdi = 256 % d;
 
     bool rotated_last = true;
     for (int sweep = 0; sweep < B.max_sweeps && rotated_last; ++sweep) {
@@ -146,9 +175,10 @@ __global__ __launch_bounds__(256) void jacobi_kernel(const JacobiBatch B) {
         if (!__syncthreads_or(rot)) continue;
         any = 1;
         // A <- J^T A J, as independent 2x2 blocks (upper blocks + mirror).
-        for (int idx = tid; idx < np * np; idx += 256) {
-          const int kr = idx / np, kc = idx % np;
-          if (kr > kc) continue;
+#pragma unroll
+        for (int m = 0; m < kPairsPerThread; ++m) {
+          const int kr = pkr[m], kc = pkc[m];
+          if (kr < 0) continue;
           const int rot1 = rrot[kr], rot2 = rrot[kc];
           if (!rot1 && !rot2) continue;
           const int p1 = rp[kr], q1 = rq[kr];
@@ -176,15 +206,40 @@ __global__ __launch_bounds__(256) void jacobi_kernel(const JacobiBatch B) {
           sM[p2 * kJLD + q1] = z10;
           sM[q2 * kJLD + q1] = z11;
         }
-        // W <- J^T W (rows p, q of W = columns p, q of V).
-        for (int idx = tid; idx < np * d; idx += 256) {
-          const int k = idx / d, i = idx % d;
-          if (!rrot[k]) continue;
-          const int p = rp[k], q = rq[k];
-          const double c = rc[k], sn = rs[k];
-          const double wp = W[(int64_t)p * d + i], wq = W[(int64_t)q * d + i];
-          W[(int64_t)p * d + i] = c * wp - sn * wq;
-          W[(int64_t)q * d + i] = sn * wp + c * wq;
+        // W <- J^T W (rows p, q of W = columns p, q of V).  W lives in global
+        // memory: each thread first loads kWBatch element pairs, then
+        // rotates and stores them, so one memory latency covers the batch
+        // instead of one per pair.
+        int wk = wk0, wi = wi0;
+        for (int base = tid; base < np * d; base += 256 * kWBatch) {
+          double wp[kWBatch], wq[kWBatch];
+          int64_t op[kWBatch], oq[kWBatch];
+          int kk[kWBatch];
+#pragma unroll
+          for (int u = 0; u < kWBatch; ++u) {
+            const int k = wk, i = wi;  // (k, i) of idx = base + 256 u
+            wk += wdk;
+            wi += wdi;
+            if (wi >= d) {
+              wi -= d;
+              ++wk;
+            }
+            kk[u] = -1;
+            if (k < np && rrot[k]) {
+              kk[u] = k;
+              op[u] = (int64_t)rp[k] * d + i;
+              oq[u] = (int64_t)rq[k] * d + i;
+              wp[u] = W[op[u]];
+              wq[u] = W[oq[u]];
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < kWBatch; ++u) {
+            if (kk[u] < 0) continue;
+            const double c = rc[kk[u]], sn = rs[kk[u]];
+            W[op[u]] = c * wp[u] - sn * wq[u];
+            W[oq[u]] = sn * wp[u] + c * wq[u];
+          }
         }
         __syncthreads();
       }
