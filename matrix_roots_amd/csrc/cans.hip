@@ -238,7 +238,7 @@ __global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1
   const int m0 = ti * S::BM, n0 = tj * S::BN;
   v16f acc[S::RB][S::CB];
   if constexpr (PREC == 3)
-    x3_nt_tile<VEC>(A.ref(), d, Bm.ref(), d, d, d, d, m0, n0, reinterpret_cast<_Float16*>(smem), acc);
+    x3_nt_tile_auto<VEC>(A.ref(), d, Bm.ref(), d, d, d, d, m0, n0, smem, acc);
   else
     h16_nt_tile_auto<S, VEC>(A.hi, d, Bm.hi, d, d, d, d, m0, n0, smem, acc);
 

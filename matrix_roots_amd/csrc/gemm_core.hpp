@@ -360,6 +360,133 @@ __device__ __forceinline__ void x3_nt_tile(SplitRef A, int64_t lda, SplitRef B, 
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = acc[rb][cb][v] + acc2[rb][cb][v] * (1.0f / 2048.0f);
 }
 
+// The same product and accumulator layout with the operand chunks copied
+// straight from global memory into LDS (direct-to-LDS copies, no staging
+// registers and no LDS store instructions), chunks of 32 along k in two
+// stages: a wave waits for its own copies of the next chunk and a bare
+// s_barrier publishes them, so the copies of the chunk after stay in flight
+// during the MFMAs.  Stage layout: A_hi, A_lo, B_hi, B_lo, each 128 rows of
+// four 16-byte units in the dl_slot order.  Preconditions (checked by the
+// caller): K a multiple of 32, lda and ldb multiples of 8, 16-byte aligned
+// arrays.  Rows beyond M or N are read from row M - 1 or N - 1: they only feed
+// outputs that are never stored.
+struct X3DL {
+  static constexpr int BK = 32, UPR = BK / 8;
+  static constexpr int AU = X3Tile::BM * UPR;  // 16-byte units per array and stage
+  static constexpr int STAGE_BYTES = 4 * AU * 16;
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int CPA = AU / X3Tile::THREADS;  // copies per lane and array
+  static_assert(CPA * X3Tile::THREADS == AU, "copies cover the chunk");
+};
+
+__device__ __forceinline__ void x3dl_issue(SplitRef A, int64_t lda, SplitRef B, int64_t ldb, int M, int N, int m0,
+                                           int n0, int k0, unsigned char* stage, int wave, int lane) {
+#pragma unroll
+  for (int arr = 0; arr < 4; ++arr) {
+    const bool isA = arr < 2;
+    const _Float16* P = arr == 0 ? A.hi : arr == 1 ? A.lo : arr == 2 ? B.hi : B.lo;
+    const int64_t ld = isA ? lda : ldb;
+    const int r0 = isA ? m0 : n0, rmax = (isA ? M : N) - 1;
+#pragma unroll
+    for (int j = 0; j < X3DL::CPA; ++j) {
+      const int base_u = (j * (X3Tile::THREADS / 64) + wave) * 64;
+      const int u = base_u + lane;
+      const int row = u / X3DL::UPR;
+      const int kg = dl_slot(row, u % X3DL::UPR, X3DL::UPR);  // the map is its own inverse
+      const _Float16* src = P + (int64_t)min(r0 + row, rmax) * ld + k0 + kg * 8;
+      __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)(stage + (arr * X3DL::AU + base_u) * 16),
+                                       16, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ void x3dl_chunk(const unsigned char* __restrict__ st, v16f (&acc)[2][2],
+                                           v16f (&acc2)[2][2], int lane, int wm, int wn) {
+  constexpr int AB = X3DL::AU * 16;  // bytes per array
+#pragma unroll
+  for (int ks = 0; ks < X3DL::BK / 16; ++ks) {
+    const int kg = ks * 2 + (lane >> 5);
+    v8h ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int r = wm * 64 + rb * 32 + (lane & 31);
+      const int o = (r * X3DL::UPR + dl_slot(r, kg, X3DL::UPR)) * 16;
+      ah[rb] = *reinterpret_cast<const v8h*>(st + o);
+      al[rb] = *reinterpret_cast<const v8h*>(st + AB + o);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int r = wn * 64 + cb * 32 + (lane & 31);
+      const int o = (r * X3DL::UPR + dl_slot(r, kg, X3DL::UPR)) * 16;
+      bh[cb] = *reinterpret_cast<const v8h*>(st + 2 * AB + o);
+      bl[cb] = *reinterpret_cast<const v8h*>(st + 3 * AB + o);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        acc[rb][cb] = mfma_f16_32x32x16(ah[rb], bh[cb], acc[rb][cb]);
+        acc2[rb][cb] = mfma_f16_32x32x16(ah[rb], bl[cb], acc2[rb][cb]);
+        acc2[rb][cb] = mfma_f16_32x32x16(al[rb], bh[cb], acc2[rb][cb]);
+      }
+  }
+}
+
+__device__ __forceinline__ void x3dl_nt_tile(SplitRef A, int64_t lda, SplitRef B, int64_t ldb, int M, int N, int K,
+                                             int m0, int n0, unsigned char* __restrict__ lds, v16f (&acc)[2][2]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  v16f acc2[2][2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        acc[rb][cb][v] = 0.f;
+        acc2[rb][cb][v] = 0.f;
+      }
+  const int nch = K / X3DL::BK;
+  if (nch > 0) x3dl_issue(A, lda, B, ldb, M, N, m0, n0, 0, lds, wave, lane);
+  for (int c = 0; c < nch; c += 2) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (c + s < nch) {
+        wait_vmcnt<0>();  // this wave's copies of chunk c + s have landed
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // ... and every wave's; stage s ^ 1 is free
+        asm volatile("" ::: "memory");
+        if (c + s + 1 < nch)
+          x3dl_issue(A, lda, B, ldb, M, N, m0, n0, (c + s + 1) * X3DL::BK, lds + (s ^ 1) * X3DL::STAGE_BYTES, wave,
+                     lane);
+        x3dl_chunk(lds + s * X3DL::STAGE_BYTES, acc, acc2, lane, wm, wn);
+      }
+    }
+  }
+  __syncthreads();  // no wave leaves (or reuses the LDS) while another may still read the last stage
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = acc[rb][cb][v] + acc2[rb][cb][v] * (1.0f / 2048.0f);
+}
+
+// Direct-to-LDS core where its preconditions hold (VEC 8: 16-byte aligned
+// operands, leading dimensions multiples of 8), else the register-staged one.
+#ifndef MR_X3_DL
+#define MR_X3_DL 1
+#endif
+template <int VEC>
+__device__ __forceinline__ void x3_nt_tile_auto(SplitRef A, int64_t lda, SplitRef B, int64_t ldb, int M, int N, int K,
+                                                int m0, int n0, unsigned char* __restrict__ lds, v16f (&acc)[2][2]) {
+  static_assert(X3DL::LDS_BYTES <= 2 * X3Tile::LDS_HALVES, "both cores fit the same LDS");
+  if (MR_X3_DL && VEC == 8 && K % X3DL::BK == 0)
+    x3dl_nt_tile(A, lda, B, ldb, M, N, K, m0, n0, lds, acc);
+  else
+    x3_nt_tile<VEC>(A, lda, B, ldb, M, N, K, m0, n0, reinterpret_cast<_Float16*>(lds), acc);
+}
+
 // Visit every accumulator element of the f32 core as (row, col) local to the
 // block tile.
 template <typename F>

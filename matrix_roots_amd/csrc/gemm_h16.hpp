@@ -165,9 +165,6 @@ __device__ __forceinline__ void h16g_for_each(const v16f (&acc)[S::RB][S::CB], F
 // Preconditions (checked by the caller): K a multiple of BK, lda and ldb
 // multiples of 8, A and B 16-byte aligned.  Rows beyond M or N are read from
 // row M - 1 or N - 1: they only feed outputs that are never stored.
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-typedef __attribute__((address_space(1))) void* global_void_ptr;
-
 template <int BM_, int BN_, int WM_, int WN_, int BK_>
 struct H16DLShape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_;
@@ -181,15 +178,6 @@ struct H16DLShape {
   static_assert(NA * 64 * NW == AU && NB * 64 * NW == BU, "copies cover the chunk");
   static_assert(UPR == 4 || UPR == 8, "swizzle period");
 };
-
-__device__ __forceinline__ int dl_slot(int row, int kg, int upr) { return kg ^ ((row / (16 / upr)) % upr); }
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  // s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 
 template <class S>
 __device__ __forceinline__ void h16dl_issue(const _Float16* __restrict__ A, int64_t lda, const _Float16* __restrict__ B,

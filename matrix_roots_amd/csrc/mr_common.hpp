@@ -142,6 +142,25 @@ __device__ __forceinline__ double sym_tile_value(bool packed, int bi, int bj, in
   return 0.5 * (ta[r][c] + tb[c][r]);
 }
 
+// Direct global -> LDS copies (global_load_lds_dwordx4: 16 bytes per lane
+// into 1 KB of consecutive LDS per instruction).  Operand chunks of UPR
+// 16-byte units per row sit unpadded, the unit of k-group kg of row r in slot
+// dl_slot(r, kg, UPR) (an involution in kg), so the 16 lanes of one 128-bit
+// LDS read cycle (16 consecutive rows, one k-group) hit 16 distinct bank
+// groups.
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
+
+__device__ __forceinline__ int dl_slot(int row, int kg, int upr) { return kg ^ ((row / (16 / upr)) % upr); }
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // L2-friendly tile orders.  A launch keeps ~64 output tiles per XCD in
 // flight (32 CUs x 2 workgroups), and tiles advance through K at the same
 // pace, so what decides the operand traffic is how many distinct operand

@@ -226,7 +226,7 @@ __global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1 : 2) void polar_g
   const int m0 = ti * S::BM, n0 = tj * S::BN;
   v16f acc[S::RB][S::CB];
   if constexpr (PREC == 3)
-    x3_nt_tile<VEC>(Aop.ref(), lda, Bop.ref(), ldb, rows, cols, K, m0, n0, reinterpret_cast<_Float16*>(smem), acc);
+    x3_nt_tile_auto<VEC>(Aop.ref(), lda, Bop.ref(), ldb, rows, cols, K, m0, n0, smem, acc);
   else
     h16_nt_tile_auto<S, VEC>(Aop.hi, lda, Bop.hi, ldb, rows, cols, K, m0, n0, smem, acc);
   // epilogue arithmetic: float64 for split products, float32 for fp16 ones

@@ -520,7 +520,7 @@ __global__ __launch_bounds__(256, 2) void newton_x3_kernel(const NewtonLaunch L,
   const SplitOps o = split_ops(r, L.stage, s.job, s.s, kind == kStageX3B64);
   const int m0 = s.ti * X3Tile::BM, n0 = s.tj * X3Tile::BN;
   v16f acc[2][2];
-  x3_nt_tile<VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, smem, acc);
+  x3_nt_tile_auto<VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, reinterpret_cast<unsigned char*>(smem), acc);
   const int d = s.d;
   if (VEC == 8 && s.ti <= s.tj && m0 + X3Tile::BM <= d && n0 + X3Tile::BN <= d) {
     // Whole tile on or above the diagonal: the upper elements and their
