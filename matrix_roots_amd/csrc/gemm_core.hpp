@@ -712,6 +712,114 @@ __device__ __forceinline__ void f64_tile(const TA* __restrict__ A, int64_t lda, 
   }
 }
 
+// The same product (float64 operands along contiguous rows, NT) with the
+// operand chunks copied straight from global memory into LDS: rows of BK = 16
+// doubles as eight 16-byte units in the dl_slot order, two stages (64 KB).
+// A lane reads the unit holding k = 4 (lane / 16) + 2h + {0, 1} of its row,
+// the k order of f64_chunk, so both cores sum in the same order and agree
+// bitwise.  Preconditions (checked by the caller): K a multiple of 16, lda
+// and ldb even, 16-byte aligned arrays.  Rows beyond M or N are read from row
+// M - 1 or N - 1: they only feed outputs that are never stored.
+struct F64DL {
+  static constexpr int BK = F64Tile::BK, UPR = BK / 2;
+  static constexpr int AU = F64Tile::BM * UPR;  // 16-byte units per operand and stage
+  static constexpr int STAGE_BYTES = 2 * AU * 16;
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int CPO = AU / F64Tile::THREADS;  // copies per lane and operand
+  static_assert(BK == 16 && CPO * F64Tile::THREADS == AU, "eight units per row, copies cover the chunk");
+};
+
+__device__ __forceinline__ void f64dl_issue(const double* __restrict__ A, int64_t lda, const double* __restrict__ B,
+                                            int64_t ldb, int M, int N, int m0, int n0, int k0, unsigned char* stage,
+                                            int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < 2 * F64DL::CPO; ++j) {
+    const bool isA = j < F64DL::CPO;
+    const int base_u = ((isA ? j : j - F64DL::CPO) * (F64Tile::THREADS / 64) + wave) * 64;
+    const int u = base_u + lane;
+    const int row = u / F64DL::UPR;
+    const int kg = dl_slot(row, u % F64DL::UPR, F64DL::UPR);  // the map is its own inverse
+    const double* src = isA ? A + (int64_t)min(m0 + row, M - 1) * lda + k0 + kg * 2
+                            : B + (int64_t)min(n0 + row, N - 1) * ldb + k0 + kg * 2;
+    __builtin_amdgcn_global_load_lds((global_void_ptr)src,
+                                     (lds_void_ptr)(stage + ((isA ? 0 : F64DL::AU) + base_u) * 16), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void f64dl_chunk(const unsigned char* __restrict__ st, v4d (&acc)[4][4], int lane, int wm,
+                                            int wn) {
+  const unsigned char* As = st;
+  const unsigned char* Bs = st + F64DL::AU * 16;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int kg = (lane >> 4) * 2 + h;
+    v2d a[4], b[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int r = wm * 64 + rb * 16 + (lane & 15);
+      a[rb] = *reinterpret_cast<const v2d*>(As + (r * F64DL::UPR + dl_slot(r, kg, F64DL::UPR)) * 16);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int r = wn * 64 + cb * 16 + (lane & 15);
+      b[cb] = *reinterpret_cast<const v2d*>(Bs + (r * F64DL::UPR + dl_slot(r, kg, F64DL::UPR)) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma_f64_16x16x4(a[rb][i], b[cb][i], acc[rb][cb]);
+  }
+}
+
+__device__ __forceinline__ void f64dl_nt_tile(const double* __restrict__ A, int64_t lda, const double* __restrict__ B,
+                                              int64_t ldb, int M, int N, int K, int m0, int n0,
+                                              unsigned char* __restrict__ lds, v4d (&acc)[4][4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[rb][cb][v] = 0.0;
+  const int nch = K / F64DL::BK;
+  if (nch > 0) f64dl_issue(A, lda, B, ldb, M, N, m0, n0, 0, lds, wave, lane);
+  for (int c = 0; c < nch; c += 2) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (c + s < nch) {
+        wait_vmcnt<0>();  // this wave's copies of chunk c + s have landed
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // ... and every wave's; stage s ^ 1 is free
+        asm volatile("" ::: "memory");
+        if (c + s + 1 < nch)
+          f64dl_issue(A, lda, B, ldb, M, N, m0, n0, (c + s + 1) * F64DL::BK, lds + (s ^ 1) * F64DL::STAGE_BYTES, wave,
+                      lane);
+        f64dl_chunk(lds + s * F64DL::STAGE_BYTES, acc, lane, wm, wn);
+      }
+    }
+  }
+  __syncthreads();  // no wave leaves (or reuses the LDS) while another may still read the last stage
+}
+
+// Direct-to-LDS core for float64 operands where its preconditions hold
+// (VEC 2: 16-byte aligned rows), else the register-staged one.
+#ifndef MR_F64_DL
+#define MR_F64_DL 1
+#endif
+template <int VEC>
+__device__ __forceinline__ void f64_nt_tile_auto(const double* __restrict__ A, int64_t lda,
+                                                 const double* __restrict__ B, int64_t ldb, int M, int N, int K,
+                                                 int m0, int n0, double* __restrict__ lds, v4d (&acc)[4][4]) {
+  static_assert(F64DL::LDS_BYTES <= (int)sizeof(double) * F64Tile::LDS_DOUBLES, "both cores fit the same LDS");
+  if (MR_F64_DL && VEC == 2 && K % F64DL::BK == 0)
+    f64dl_nt_tile(A, lda, B, ldb, M, N, K, m0, n0, reinterpret_cast<unsigned char*>(lds), acc);
+  else
+    f64_tile<double, false, VEC, double, false, VEC>(A, lda, B, ldb, M, N, K, m0, n0, lds, acc);
+}
+
 template <typename F>
 __device__ __forceinline__ void f64_for_each(const v4d (&acc)[4][4], F&& f) {
   const int lane = threadIdx.x & 63;

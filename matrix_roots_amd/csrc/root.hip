@@ -435,14 +435,14 @@ __device__ __forceinline__ void sym_store(const StageOps<T>& o, int d, int gr, i
 template <int VEC>
 __global__ __launch_bounds__(256, VEC == 2 ? MR_F64_OCC : 1) void newton_f64_kernel(const NewtonLaunch L) {
   // (with x_low, stage 2 also writes the split copy Mx of the new M)
-  __shared__ double smem[F64Tile::LDS_DOUBLES];
+  __shared__ __attribute__((aligned(16))) double smem[F64Tile::LDS_DOUBLES];
   const StageJob s = stage_job(L, kStageF64);
   if (!s.active) return;
   const Roles64 r = roles64(s.region, s.d, L.t);
   const StageOps<double> o = stage_ops<double>(r, L.stage, s.job, s.s);
   const int m0 = s.ti * F64Tile::BM, n0 = s.tj * F64Tile::BN;
   v4d acc[4][4];
-  f64_tile<double, false, VEC, double, false, VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, smem, acc);
+  f64_nt_tile_auto<VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, smem, acc);
   const int d = s.d;
   if (L.x_low && L.stage == 2) {
     const SplitBuf mx = roless(s.region, d, L.t).Mx;
