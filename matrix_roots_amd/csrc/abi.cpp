@@ -27,6 +27,10 @@ using namespace mr;
 #ifndef MR_NEWTON_BIG_FIRST
 #define MR_NEWTON_BIG_FIRST 1
 #endif
+// Split-fp16 Newton stages on 256 x 256 tiles for classes with d % 32 == 0.
+#ifndef MR_NEWTON_WIDE
+#define MR_NEWTON_WIDE 1
+#endif
 
 namespace {
 
@@ -705,19 +709,22 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
     // Class groups: at most kMaxClasses per launch, split by vector width.
     // vec64: float64 loads of 2 (d even); vec32: float32 loads of 4 (d % 4 == 0);
     // vecx3: fp16 loads of 8 (d % 8 == 0).
+    // wide: d % 32 == 0, the split-fp16 stages run on 256 x 256 tiles.
     struct Group {
       std::vector<int> cls;
       int vec64, vec32, vecx3;
+      bool wide;
     };
     std::vector<Group> groups;
-    for (const int align : {8, 4, 2, 1}) {
+    for (const int align : {32, 8, 4, 2, 1}) {
       Group g;
       g.vec64 = align >= 2 ? 2 : 1;
       g.vec32 = align >= 4 ? 4 : 1;
       g.vecx3 = align >= 8 ? 8 : 1;
+      g.wide = align == 32 && MR_NEWTON_WIDE;
       for (int ci = 0; ci < (int)P.classes.size(); ++ci) {
         const int64_t d = P.classes[ci].d;
-        const int a = d % 8 == 0 ? 8 : d % 4 == 0 ? 4 : d % 2 == 0 ? 2 : 1;
+        const int a = d % 32 == 0 ? 32 : d % 8 == 0 ? 8 : d % 4 == 0 ? 4 : d % 2 == 0 ? 2 : 1;
         if (a != align) continue;
         g.cls.push_back(ci);
         if ((int)g.cls.size() == kMaxClasses) {
@@ -727,7 +734,8 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
       }
       if (!g.cls.empty()) groups.push_back(g);
     }
-    auto make_launch = [&](const Group& g, int kind, int stage, int t, int job_only) {
+    // tile: 256 for the wide split-fp16 kernel, else 128
+    auto make_launch = [&](const Group& g, int kind, int stage, int t, int job_only, int tile = 128) {
       NewtonLaunch L;
       memset(&L, 0, sizeof L);
       L.stage = stage;
@@ -736,6 +744,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
       L.sched = sched;
       L.x_low = x_low ? 1 : 0;
       L.job_only = job_only;
+      L.wide = tile == 256 ? 1 : 0;
       // Largest Grams first: their long tiles start early and the short
       // tiles of the small classes fill the launch's tail.
       for (size_t q = 0; q < g.cls.size(); ++q) {
@@ -746,7 +755,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
         C.matrix_bytes = (int64_t)c.matrix_bytes;
         C.d = (int32_t)c.d;
         C.count = c.count;
-        C.T = tiles(c.d, 128);
+        C.T = tiles(c.d, tile);
         C.U = C.T * (C.T + 1) / 2;
         C.slot_begin = c.first_slot;
         C.block_begin = L.total_blocks;
@@ -776,14 +785,14 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
                              "newton f64 stage")) != MR_OK)
               return st;
             if (split && t > 0) {  // the first X update is part of the init
-              const NewtonLaunch LX = make_launch(g, 0, stage, t, 1);
+              const NewtonLaunch LX = make_launch(g, 0, stage, t, 1, g.wide ? 256 : 128);
               if ((st = traced(kTrNewtonX3, true, s, [&] { return launch_newton_stage(LX, kStageX3B64, g.vecx3, s); },
                                "newton x3 X update")) != MR_OK)
                 return st;
             }
           }
           if (!all_f64) {
-            const NewtonLaunch L = make_launch(g, 0, stage, t, -1);
+            const NewtonLaunch L = make_launch(g, 0, stage, t, -1, g.wide && !f32_mfma ? 256 : 128);
             const int kind = f32_mfma ? kStageF32 : kStageX3;
             if ((st = traced(f32_mfma ? kTrNewton32 : kTrNewtonX3, true, s,
                              [&] { return launch_newton_stage(L, kind, f32_mfma ? g.vec32 : g.vecx3, s); },

@@ -487,6 +487,139 @@ __device__ __forceinline__ void x3_nt_tile_auto(SplitRef A, int64_t lda, SplitRe
     x3_nt_tile<VEC>(A, lda, B, ldb, M, N, K, m0, n0, reinterpret_cast<_Float16*>(lds), acc);
 }
 
+// Wide split-fp16 tile for operands whose B side is bounded: 256 x 256 block
+// tile, eight waves in a 2 x 4 grid (128 x 64 each: 4 x 2 blocks of 32 x 32),
+// direct-to-LDS copies in 32-deep chunks, two stages (128 KB).  One float32
+// accumulator takes all three products: with B's hi half multiplied by 2^11
+// in registers (exact: a power of two, and |B| < 32 keeps 2^11 hi_b inside
+// fp16's range),
+//   2^11 hi_a hi_b + hi_a lo_b + lo_a hi_b = 2^11 (hi_a hi_b + 2^-11 (hi_a lo_b + lo_a hi_b)),
+// whose float32 sum rounds like the larger of the two separate sums of
+// x3_nt_tile (the hi_a hi_b sum sets the rounding in both), so both forms
+// carry the same accuracy; the single accumulator halves the accumulator
+// registers, which is what lets one wave hold a 128 x 64 tile.
+// Preconditions (checked by the caller): K a multiple of 32, lda and ldb
+// multiples of 8, 16-byte aligned arrays, every |B| < 32.  Rows beyond M or N
+// are read from row M - 1 or N - 1: they only feed outputs never stored.
+struct X3W {
+  static constexpr int BM = 256, BN = 256, WM = 2, WN = 4, THREADS = 64 * WM * WN;
+  static constexpr int RB = BM / WM / 32, CB = BN / WN / 32;
+  static constexpr int BK = 32, UPR = BK / 8;
+  static constexpr int AU = BM * UPR;  // 16-byte units per array and stage (BM == BN)
+  static constexpr int STAGE_BYTES = 4 * AU * 16;
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int CPA = AU / THREADS;  // copies per lane and array
+  static_assert(BM == BN && CB == 2 && CPA * THREADS == AU, "square tile, two column blocks per wave");
+};
+
+__device__ __forceinline__ void x3w_issue(SplitRef A, int64_t lda, SplitRef B, int64_t ldb, int M, int N, int m0,
+                                          int n0, int k0, unsigned char* stage, int wave, int lane) {
+#pragma unroll
+  for (int arr = 0; arr < 4; ++arr) {
+    const bool isA = arr < 2;
+    const _Float16* P = arr == 0 ? A.hi : arr == 1 ? A.lo : arr == 2 ? B.hi : B.lo;
+    const int64_t ld = isA ? lda : ldb;
+    const int r0 = isA ? m0 : n0, rmax = (isA ? M : N) - 1;
+#pragma unroll
+    for (int j = 0; j < X3W::CPA; ++j) {
+      const int base_u = (j * (X3W::THREADS / 64) + wave) * 64;
+      const int u = base_u + lane;
+      const int row = u / X3W::UPR;
+      const int kg = dl_slot(row, u % X3W::UPR, X3W::UPR);  // the map is its own inverse
+      const _Float16* src = P + (int64_t)min(r0 + row, rmax) * ld + k0 + kg * 8;
+      __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)(stage + (arr * X3W::AU + base_u) * 16),
+                                       16, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ void x3w_chunk(const unsigned char* __restrict__ st, v16f (&acc)[X3W::RB][X3W::CB],
+                                          int lane, int wm, int wn) {
+  constexpr int AB = X3W::AU * 16;  // bytes per array
+#pragma unroll
+  for (int ks = 0; ks < X3W::BK / 16; ++ks) {
+    const int kg = ks * 2 + (lane >> 5);
+    v8h ah[X3W::RB], al[X3W::RB], bh[X3W::CB], bl[X3W::CB];
+#pragma unroll
+    for (int rb = 0; rb < X3W::RB; ++rb) {
+      const int r = wm * (X3W::BM / X3W::WM) + rb * 32 + (lane & 31);
+      const int o = (r * X3W::UPR + dl_slot(r, kg, X3W::UPR)) * 16;
+      ah[rb] = *reinterpret_cast<const v8h*>(st + o);
+      al[rb] = *reinterpret_cast<const v8h*>(st + AB + o);
+    }
+#pragma unroll
+    for (int cb = 0; cb < X3W::CB; ++cb) {
+      const int r = wn * (X3W::BN / X3W::WN) + cb * 32 + (lane & 31);
+      const int o = (r * X3W::UPR + dl_slot(r, kg, X3W::UPR)) * 16;
+      bh[cb] = *reinterpret_cast<const v8h*>(st + 2 * AB + o);
+      bl[cb] = *reinterpret_cast<const v8h*>(st + 3 * AB + o);
+    }
+#pragma unroll
+    for (int cb = 0; cb < X3W::CB; ++cb) {
+#pragma unroll
+      for (int rb = 0; rb < X3W::RB; ++rb) acc[rb][cb] = mfma_f16_32x32x16(al[rb], bh[cb], acc[rb][cb]);
+      const v8h bs = bh[cb] * (_Float16)2048.0f;
+#pragma unroll
+      for (int rb = 0; rb < X3W::RB; ++rb) {
+        acc[rb][cb] = mfma_f16_32x32x16(ah[rb], bl[cb], acc[rb][cb]);
+        acc[rb][cb] = mfma_f16_32x32x16(ah[rb], bs, acc[rb][cb]);
+      }
+    }
+  }
+}
+
+// Result in acc: float32 sums of the wave's 4 x 2 blocks (layout of x3w_for_each).
+__device__ __forceinline__ void x3w_nt_tile(SplitRef A, int64_t lda, SplitRef B, int64_t ldb, int M, int N, int K,
+                                            int m0, int n0, unsigned char* __restrict__ lds,
+                                            v16f (&acc)[X3W::RB][X3W::CB]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / X3W::WN, wn = wave % X3W::WN;
+#pragma unroll
+  for (int rb = 0; rb < X3W::RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < X3W::CB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.f;
+  const int nch = K / X3W::BK;
+  if (nch > 0) x3w_issue(A, lda, B, ldb, M, N, m0, n0, 0, lds, wave, lane);
+  for (int c = 0; c < nch; c += 2) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (c + s < nch) {
+        wait_vmcnt<0>();  // this wave's copies of chunk c + s have landed
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // ... and every wave's; stage s ^ 1 is free
+        asm volatile("" ::: "memory");
+        if (c + s + 1 < nch)
+          x3w_issue(A, lda, B, ldb, M, N, m0, n0, (c + s + 1) * X3W::BK, lds + (s ^ 1) * X3W::STAGE_BYTES, wave,
+                    lane);
+        x3w_chunk(lds + s * X3W::STAGE_BYTES, acc, lane, wm, wn);
+      }
+    }
+  }
+  __syncthreads();  // no wave leaves (or reuses the LDS) while another may still read the last stage
+#pragma unroll
+  for (int rb = 0; rb < X3W::RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < X3W::CB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = acc[rb][cb][v] * (1.0f / 2048.0f);
+}
+
+template <typename F>
+__device__ __forceinline__ void x3w_for_each(const v16f (&acc)[X3W::RB][X3W::CB], F&& f) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / X3W::WN, wn = wave % X3W::WN;
+#pragma unroll
+  for (int rb = 0; rb < X3W::RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < X3W::CB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        f(wm * (X3W::BM / X3W::WM) + rb * 32 + f32_row(lane, v), wn * (X3W::BN / X3W::WN) + cb * 32 + (lane & 31),
+          acc[rb][cb][v]);
+}
+
 // Visit every accumulator element of the f32 core as (row, col) local to the
 // block tile.
 template <typename F>

@@ -135,6 +135,7 @@ struct NewtonLaunch {
   const double* sched;  // per slot: kMaxNewtonIters step scales
   int32_t x_low;        // X kept in float32 from the first step
   int32_t job_only;     // -1: every job of the stage; else only that job
+  int32_t wide;         // split-fp16 stages on 256 x 256 tiles (every class's d a multiple of 32)
 };
 
 // ------------------------------------------------------------ Jacobi

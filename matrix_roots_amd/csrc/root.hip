@@ -545,6 +545,43 @@ __global__ __launch_bounds__(256, 2) void newton_x3_kernel(const NewtonLaunch L,
   });
 }
 
+// The same stages on 256 x 256 tiles with the single-accumulator split core
+// (x3w_nt_tile).  Its B operands are M, the split copy Mx of a float64 M, or
+// T2, whose spectra lie in [0, 1] and [1/4, 25/16] (u/s <= 3 in these steps,
+// the float64 steps' M <= 1), so every |B| < 2 and the 2^11 scaling of B's
+// hi half stays far inside fp16's range.  The host picks this kernel for
+// classes with d a multiple of 32 (whole 32-deep chunks).
+__global__ __launch_bounds__(X3W::THREADS, 1) void newton_x3w_kernel(const NewtonLaunch L, int kind) {
+  constexpr int kSmem = X3W::LDS_BYTES > 8 * kSlabFloats * 4 ? X3W::LDS_BYTES : 8 * kSlabFloats * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
+  const StageJob s = stage_job(L, kind);
+  if (!s.active) return;
+  const RolesS r = roless(s.region, s.d, L.t);
+  const SplitOps o = split_ops(r, L.stage, s.job, s.s, kind == kStageX3B64);
+  const int m0 = s.ti * X3W::BM, n0 = s.tj * X3W::BN;
+  const int d = s.d;
+  v16f acc[X3W::RB][X3W::CB];
+  x3w_nt_tile(o.A, d, o.B, d, d, d, d, m0, n0, smem, acc);
+  if (s.ti <= s.tj && m0 + X3W::BM <= d && n0 + X3W::BN <= d) {
+    // whole tile on or above the diagonal: wide stores through per-wave slabs
+    wide_store_tile<X3W::RB, X3W::WN, double>(acc, reinterpret_cast<float*>(smem), m0, n0, o.C.hi, o.C.lo, d, o.C.hi,
+                                              o.C.lo, d, o.has_cin ? o.Cin.hi : nullptr,
+                                              o.has_cin ? o.Cin.lo : nullptr, o.alpha, o.beta, o.gamma, s.ti == s.tj);
+    return;
+  }
+  x3w_for_each(acc, [&](int rr, int cc, float v) {
+    const int gr = m0 + rr, gc = n0 + cc;
+    if (gr < d && gc < d && gr <= gc) {
+      const int64_t e = (int64_t)gr * d + gc;
+      double val = o.alpha * (double)v;
+      if (o.has_cin) val += o.beta * (double)join_f32(o.Cin.hi[e], o.Cin.lo[e]);
+      if (gr == gc) val += o.gamma;
+      split_put(o.C, e, (float)val);
+      if (gr != gc) split_put(o.C, (int64_t)gc * d + gr, (float)val);
+    }
+  });
+}
+
 // float64 M, X of iteration t -> float32 M, X of iteration t, for the
 // matrices whose switch iteration is t.
 __global__ __launch_bounds__(256) void newton_convert_kernel(const NewtonLaunch L) {
@@ -685,7 +722,9 @@ hipError_t launch_root_init(const RootBatch& b, hipStream_t s) {
 hipError_t launch_newton_stage(const NewtonLaunch& L, int kind, int vec, hipStream_t s) {
   if (L.total_blocks <= 0) return hipSuccess;
   if (kind == kStageX3 || kind == kStageX3B64) {
-    if (vec >= 8)
+    if (L.wide)
+      hipLaunchKernelGGL(newton_x3w_kernel, dim3(L.total_blocks), dim3(X3W::THREADS), 0, s, L, kind);
+    else if (vec >= 8)
       hipLaunchKernelGGL(newton_x3_kernel<8>, dim3(L.total_blocks), dim3(256), 0, s, L, kind);
     else
       hipLaunchKernelGGL(newton_x3_kernel<1>, dim3(L.total_blocks), dim3(256), 0, s, L, kind);
