@@ -406,7 +406,16 @@ mr_status gram_ema_update(const mr_gram_problem* p, int32_t count, mr_dtype dt, 
         b.total_blocks = 0;
         return r;
       };
-      for (int i = 0; i < count; ++i) {
+      // Largest Grams first in each launch: their long tiles start early and
+      // the short tiles of the small Grams fill the launch's tail.
+      std::vector<int> order(count);
+      for (int i = 0; i < count; ++i) order[i] = i;
+      std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
+        const int64_t dx = right ? p[x].n : p[x].m, dy = right ? p[y].n : p[y].m;
+        const int64_t kx = right ? p[x].m : p[x].n, ky = right ? p[y].m : p[y].n;
+        return dx * dx * kx > dy * dy * ky;
+      });
+      for (const int i : order) {
         const mr_gram_problem& q = p[i];
         const int64_t d = right ? q.n : q.m;
         const int64_t K = right ? q.m : q.n;
@@ -424,7 +433,7 @@ mr_status gram_ema_update(const mr_gram_problem* p, int32_t count, mr_dtype dt, 
         J.block_begin = b.total_blocks;
         b.total_blocks += round8(J.T * (J.T + 1) / 2);
         ++b.njobs;
-        if (b.njobs == kMaxJobs && (st = flush()) != MR_OK) return st;
+        if (b.njobs == kMaxSyrkJobs && (st = flush()) != MR_OK) return st;
       }
       if ((st = flush()) != MR_OK) return st;
     }
@@ -479,6 +488,12 @@ mr_status precondition_apply(const mr_apply_problem* p, int32_t count, float alp
     off += align256((size_t)p[i].m * (size_t)p[i].n * 4);
   }
   auto v4ok = [](const float* ptr, int64_t ld, int64_t K) { return aligned(ptr, 16) && ld % 4 == 0 && K % 4 == 0; };
+  // largest weights first in each launch (their tiles start early, small ones fill the tail)
+  std::vector<int> order(count);
+  for (int i = 0; i < count; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
+    return p[x].m * p[x].n * (p[x].m + p[x].n) > p[y].m * p[y].n * (p[y].m + p[y].n);
+  });
   for (int stage = 0; stage < 2; ++stage) {
     for (int vecpass = 0; vecpass < 2; ++vecpass) {
       const int vec = vecpass == 0 ? 4 : 1;
@@ -492,7 +507,7 @@ mr_status precondition_apply(const mr_apply_problem* p, int32_t count, float alp
         b.total_blocks = 0;
         return r;
       };
-      for (int i = 0; i < count; ++i) {
+      for (const int i : order) {
         const mr_apply_problem& q = p[i];
         F32Job J;
         if (stage == 0) {  // W^T = XR * G^T : (n x m)
@@ -517,7 +532,7 @@ mr_status precondition_apply(const mr_apply_problem* p, int32_t count, float alp
         J.block_begin = b.total_blocks;
         b.job[b.njobs++] = J;
         b.total_blocks += round8(J.nblocks);
-        if (b.njobs == kMaxJobs && (st = flush()) != MR_OK) return st;
+        if (b.njobs == kMaxApplyJobs && (st = flush()) != MR_OK) return st;
       }
       if ((st = flush()) != MR_OK) return st;
     }

@@ -937,6 +937,137 @@ __device__ __forceinline__ void f64dl_nt_tile(const double* __restrict__ A, int6
   __syncthreads();  // no wave leaves (or reuses the LDS) while another may still read the last stage
 }
 
+// Gram products of float32 data on the float64 matrix cores, operands copied
+// straight into LDS as float32 (half the bytes of the widened copy, so NST
+// stages of 16 KB fit) and widened to float64 after the fragment read.
+//   RIGHT = false (G G^T): element (i, k) at G[i * ld + k]; chunk rows of 16
+//     floats (four 16-byte units, dl_slot order); a lane reads the unit
+//     holding k = 4 (lane / 16) + q, q = 0..3, with one 128-bit read.
+//   RIGHT = true (G^T G): element (i, k) at G[k * ld + i]; the chunk is 16
+//     rows k of 128 floats (32 units of four consecutive i), unit u of row k
+//     in slot u ^ (4 ((k / 4) % 4)), so the four rows k = 4g + q that one
+//     32-bit read touches (g = lane / 16) fall on distinct banks.
+// MFMA q of a chunk takes k = 4 (lane / 16) + q, the order of f64_tile, so
+// both cores agree bitwise.  Preconditions (checked by the caller): K a
+// multiple of 16, ld a multiple of 4 and G 16-byte aligned, and for RIGHT d
+// a multiple of 4.  Rows (or columns) beyond d are read from the last ones:
+// they only feed outputs that are never stored.
+template <bool RIGHT, int NST>
+struct F64G {
+  static constexpr int BK = 16;
+  static constexpr int OPB = 128 * BK * 4;  // bytes per operand and stage
+  static constexpr int STAGE_BYTES = 2 * OPB;
+  static constexpr int LDS_BYTES = NST * STAGE_BYTES;
+  static constexpr int CPO = OPB / 16 / F64Tile::THREADS;  // copies per lane and operand
+  static constexpr int PER = 2 * CPO;                      // copies per lane and chunk
+  static_assert(NST >= 2 && NST <= 4 && CPO * 16 * F64Tile::THREADS == OPB, "stages, copies cover the chunk");
+};
+
+__device__ __forceinline__ int f64g_tslot(int k, int u) { return u ^ (((k >> 2) & 3) << 2); }
+
+template <bool RIGHT, int NST>
+__device__ __forceinline__ void f64g_issue(const float* __restrict__ G, int64_t ld, int d, int m0, int n0, int k0,
+                                           unsigned char* stage, int wave, int lane) {
+  using C = F64G<RIGHT, NST>;
+#pragma unroll
+  for (int j = 0; j < 2 * C::CPO; ++j) {
+    const bool isA = j < C::CPO;
+    const int base_u = ((isA ? j : j - C::CPO) * (F64Tile::THREADS / 64) + wave) * 64;
+    const int p = base_u + lane;  // unit position inside the operand's chunk
+    const int r0 = isA ? m0 : n0;
+    const float* src;
+    if constexpr (!RIGHT) {
+      const int row = p / 4;
+      const int kg = dl_slot(row, p % 4, 4);  // the map is its own inverse
+      src = G + (int64_t)min(r0 + row, d - 1) * ld + k0 + kg * 4;
+    } else {
+      const int k = p / 32;
+      const int u = f64g_tslot(k, p % 32);  // an involution in the unit index too
+      src = G + (int64_t)(k0 + k) * ld + min(r0 + 4 * u, d - 4);
+    }
+    __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)(stage + (isA ? 0 : C::OPB) + base_u * 16),
+                                     16, 0, 0);
+  }
+}
+
+template <bool RIGHT, int NST>
+__device__ __forceinline__ void f64g_chunk(const unsigned char* __restrict__ st, v4d (&acc)[4][4], int lane, int wm,
+                                           int wn) {
+  using C = F64G<RIGHT, NST>;
+  const unsigned char* As = st;
+  const unsigned char* Bs = st + C::OPB;
+  const int g = lane >> 4;
+  v4f a[4], b[4];
+#pragma unroll
+  for (int blk = 0; blk < 8; ++blk) {
+    const bool isA = blk < 4;
+    const int i = (isA ? wm : wn) * 64 + (blk & 3) * 16 + (lane & 15);
+    const unsigned char* base = isA ? As : Bs;
+    v4f v;
+    if constexpr (!RIGHT) {
+      v = *reinterpret_cast<const v4f*>(base + (i * 4 + dl_slot(i, g, 4)) * 16);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k = 4 * g + q;
+        v[q] = *reinterpret_cast<const float*>(base + (k * 32 + f64g_tslot(k, i >> 2)) * 16 + (i & 3) * 4);
+      }
+    }
+    if (isA)
+      a[blk & 3] = v;
+    else
+      b[blk & 3] = v;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma_f64_16x16x4((double)a[rb][q], (double)b[cb][q], acc[rb][cb]);
+}
+
+template <bool RIGHT, int NST>
+__device__ __forceinline__ void f64g_tile(const float* __restrict__ G, int64_t ld, int d, int K, int m0, int n0,
+                                          unsigned char* __restrict__ lds, v4d (&acc)[4][4]) {
+  using C = F64G<RIGHT, NST>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[rb][cb][v] = 0.0;
+  const int nch = K / C::BK;
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nch) f64g_issue<RIGHT, NST>(G, ld, d, m0, n0, s * C::BK, lds + s * C::STAGE_BYTES, wave, lane);
+  for (int c0 = 0; c0 < nch; c0 += NST) {
+#pragma unroll
+    for (int s = 0; s < NST; ++s) {
+      const int c = c0 + s;
+      if (c < nch) {
+        // chunks issued after c and still allowed in flight
+        const int after = min(NST - 2, nch - 1 - c);
+        if (after >= 2)  // this wave's copies of chunk c have landed
+          wait_vmcnt<2 * C::PER>();
+        else if (after == 1)
+          wait_vmcnt<C::PER>();
+        else
+          wait_vmcnt<0>();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // ... and every wave's; the stage of chunk c - 1 is free
+        asm volatile("" ::: "memory");
+        if (c + NST - 1 < nch)
+          f64g_issue<RIGHT, NST>(G, ld, d, m0, n0, (c + NST - 1) * C::BK,
+                                 lds + ((s + NST - 1) % NST) * C::STAGE_BYTES, wave, lane);
+        f64g_chunk<RIGHT, NST>(lds + s * C::STAGE_BYTES, acc, lane, wm, wn);
+      }
+    }
+  }
+  __syncthreads();  // no wave leaves (or reuses the LDS) while another may still read the last stage
+}
+
 // Direct-to-LDS core for float64 operands where its preconditions hold
 // (VEC 2: 16-byte aligned rows), else the register-staged one.
 #ifndef MR_F64_DL

@@ -2,7 +2,8 @@
 // launcher functions each kernel file exports to the host runtime.
 //
 // Every per-problem table travels by value in the kernel arguments (at most
-// kMaxJobs records per launch, well under the 4 KiB argument limit), so an
+// kMaxJobs or kMaxSyrkJobs records per launch, under the 4 KiB argument
+// limit), so an
 // entry point never copies descriptors to the device.
 #pragma once
 
@@ -15,6 +16,8 @@
 namespace mr {
 
 constexpr int kMaxJobs = 16;
+constexpr int kMaxSyrkJobs = 48;   // Gram EMA: one launch per side for up to 48 weights (2.3 KiB)
+constexpr int kMaxApplyJobs = 48;  // apply: one launch per stage for up to 48 weights (3.8 KiB)
 constexpr int kMaxClasses = 8;
 constexpr int kJacobiMaxD = 128;
 constexpr int kStatsRows = 32;       // rows of A per statistics workgroup (one 32-row tile stripe)
@@ -57,8 +60,9 @@ struct SyrkJob {
   int32_t T;            // tiles per side
   int32_t block_begin;  // first workgroup of this job (multiple of 8; range round8(T(T+1)/2))
 };
+static_assert(sizeof(SyrkJob) * kMaxSyrkJobs + 64 < 4096, "Gram EMA table fits the kernel arguments");
 struct SyrkBatch {
-  SyrkJob job[kMaxJobs];
+  SyrkJob job[kMaxSyrkJobs];
   int32_t njobs;
   int32_t total_blocks;
   double alpha;  // 1 - beta
@@ -80,8 +84,9 @@ struct F32Job {
   float alpha;
   int32_t pad;
 };
+static_assert(sizeof(F32Job) * kMaxApplyJobs + 64 < 4096, "apply table fits the kernel arguments");
 struct F32Batch {
-  F32Job job[kMaxJobs];
+  F32Job job[kMaxApplyJobs];
   int32_t njobs;
   int32_t total_blocks;
 };

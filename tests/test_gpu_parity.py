@@ -43,7 +43,10 @@ def spd(d, rng, lo=-6.0, hi=0.0):
 @pytest.mark.parametrize("state", ["f64", "f32"])
 def test_gram_ema_matches_oracle(torch_dev, state):
     torch, dev = torch_dev
-    shapes = [(64, 128), (200, 328), (130, 7), (1, 5), (257, 129), (128, 256), (33, 97)]
+    # (64, 128), (128, 256), (176, 336) and (96, 400) take the direct-to-LDS
+    # core on both sides (contractions multiples of 16; 176, 336 and 400 leave
+    # ragged last tiles), the others the register-staged one on one or both
+    shapes = [(64, 128), (200, 328), (130, 7), (1, 5), (257, 129), (128, 256), (33, 97), (176, 336), (96, 400)]
     sdt = torch.float64 if state == "f64" else torch.float32
     beta = 0.95
     rng = np.random.default_rng(5)
@@ -114,6 +117,18 @@ def test_newton_root_matches_oracle(torch_dev, method, a_dtype):
     tol = 1e-6 if method == "newton_f64" else ROOT_TOL
     for normalize in ("trace", "none"):
         _check_roots(torch, dev, mats, 1e-6, normalize, method, dt, tol)
+
+
+def test_newton_wide_tiles_ragged(torch_dev):
+    """Sizes that are multiples of 32 take the split-fp16 stages on 256 x 256
+    tiles: one partial tile (160), a whole diagonal tile plus a 32-row strip
+    (288), two and three tile rows with ragged last rows (544, 800); 264 and
+    200 (multiples of 8, not of 32) share the call and take 128 x 128 tiles."""
+    torch, dev = torch_dev
+    rng = W.rng_for(90, 5)
+    mats = [spd(d, rng) for d in (160, 288, 264, 544, 200, 800)]
+    for normalize in ("trace", "none"):
+        _check_roots(torch, dev, mats, 1e-6, normalize, "newton", torch.float32, ROOT_TOL)
 
 
 def test_newton_small_d_matches_jacobi(torch_dev):
