@@ -673,7 +673,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
             J.nblocks = tiles(q.d, kFinalRows);
           b.total_blocks += J.nblocks;
           ++b.njobs;
-          if (b.njobs == kMaxJobs || slot == P.n_newton - 1) {
+          if (b.njobs == kMaxRootJobs || slot == P.n_newton - 1) {
             const int cls = kind == 0 ? kTrStats : kind == 1 ? kTrInit : kTrFinalize;
             mr_status r = traced(cls, b.total_blocks > 0, s, [&] {
               return kind == 0 ? launch_root_stats(b, s) : kind == 1 ? launch_root_init(b, s) : launch_root_finalize(b, s);
@@ -951,7 +951,7 @@ mr_status inv_sqrt_root_batched(const mr_root_problem* p, int32_t count, mr_dtyp
                                                                    : tiles(q.d, kFinalRows);
         b.total_blocks += J.nblocks;
         ++b.njobs;
-        if (b.njobs == kMaxJobs || slot == count - 1) {
+        if (b.njobs == kMaxRootJobs || slot == count - 1) {
           const int cls = kind == 0 ? kTrStats : kind == 1 ? kTrCansInit : kTrCansFinal;
           mr_status r = traced(cls, b.total_blocks > 0, s, [&] {
             if (kind == 0) return launch_root_stats(b, s);
@@ -1171,7 +1171,7 @@ mr_status polar_cans_batched(const mr_polar_problem* p, int32_t count, int32_t p
         J.nblocks = kind == 1 ? tiles(q.m, 32) * tiles(q.n, 32) : tiles(q.m, kFinalRows);
         b.total_blocks += J.nblocks;
         ++b.njobs;
-        if (b.njobs == kMaxJobs || slot == count - 1) {
+        if (b.njobs == kMaxRootJobs || slot == count - 1) {
           const int cls = kind == 0 ? kTrPolarStats : kind == 1 ? kTrPolarInit : kTrPolarFinal;
           mr_status r = traced(cls, b.total_blocks > 0, s, [&] {
             if (kind == 0) return launch_polar_stats(b, s);

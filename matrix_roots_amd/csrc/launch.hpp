@@ -18,6 +18,7 @@ namespace mr {
 constexpr int kMaxJobs = 16;
 constexpr int kMaxSyrkJobs = 48;   // Gram EMA: one launch per side for up to 48 weights (2.3 KiB)
 constexpr int kMaxApplyJobs = 48;  // apply: one launch per stage for up to 48 weights (3.8 KiB)
+constexpr int kMaxRootJobs = 48;   // root statistics, init and finalize launches (3.1 KiB)
 constexpr int kMaxClasses = 8;
 constexpr int kJacobiMaxD = 128;
 constexpr int kStatsRows = 32;       // rows of A per statistics workgroup (one 32-row tile stripe)
@@ -105,8 +106,9 @@ struct RootJob {
   int32_t nblocks;
   int32_t pad;
 };
+static_assert(sizeof(RootJob) * kMaxRootJobs + 128 < 4096, "root table fits the kernel arguments");
 struct RootBatch {
-  RootJob job[kMaxJobs];
+  RootJob job[kMaxRootJobs];
   int32_t njobs;
   int32_t total_blocks;
   int32_t a_f64;      // A is float64

@@ -51,8 +51,9 @@ struct PolarJob {
   int32_t slot, problem;
   int32_t block_begin, nblocks;
 };
+static_assert(sizeof(PolarJob) * kMaxRootJobs + 64 < 4096, "polar table fits the kernel arguments");
 struct PolarBatch {
-  PolarJob job[kMaxJobs];
+  PolarJob job[kMaxRootJobs];
   RootState* state;
   double* partial;
   int64_t partial_stride;
