@@ -852,7 +852,9 @@ __device__ __forceinline__ void f64_tile(const TA* __restrict__ A, int64_t lda, 
 // the k order of f64_chunk, so both cores sum in the same order and agree
 // bitwise.  Preconditions (checked by the caller): K a multiple of 16, lda
 // and ldb even, 16-byte aligned arrays.  Rows beyond M or N are read from row
-// M - 1 or N - 1: they only feed outputs that are never stored.
+// M - 1 or N - 1: they only feed outputs that are never stored.  Symmetric
+// outputs only: in a diagonal tile (m0 == n0) the blocks wholly below the
+// diagonal are left at zero (f64_block_mode).
 struct F64DL {
   static constexpr int BK = F64Tile::BK, UPR = BK / 2;
   static constexpr int AU = F64Tile::BM * UPR;  // 16-byte units per operand and stage
@@ -879,8 +881,32 @@ __device__ __forceinline__ void f64dl_issue(const double* __restrict__ A, int64_
   }
 }
 
+// Which 16 x 16 MFMA blocks a wave of a 128 x 128 float64 tile computes.  In
+// a diagonal tile (m0 == n0, the symmetric products keep only its upper
+// triangle) the wave at (1, 0) lies wholly below the diagonal and the waves
+// at (0, 0) and (1, 1) hold 6 blocks below it (rb > cb): their results are
+// never stored, so the waves skip those MFMAs and the wave of the other
+// workgroup on the same SIMD gets the cycles.
+enum F64Blocks { kF64All = 0, kF64Upper = 1, kF64None = 2 };
+__device__ __forceinline__ int f64_block_mode(bool diag_tile, int wm, int wn) {
+  const int m = !diag_tile || wm < wn ? kF64All : wm == wn ? kF64Upper : kF64None;
+  return __builtin_amdgcn_readfirstlane(m);  // wave-uniform
+}
+// The MFMAs of one 2-deep k step; blocks below the diagonal (rb > cb) only
+// when `full` (wave-uniform: a branch per block, not a second copy of the
+// sequence, which would double the live registers).
+__device__ __forceinline__ void f64_mfma_blocks(const v2d (&a)[4], const v2d (&b)[4], v4d (&acc)[4][4], bool full) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+        if (rb <= cb || full) acc[rb][cb] = mfma_f64_16x16x4(a[rb][i], b[cb][i], acc[rb][cb]);
+}
+
 __device__ __forceinline__ void f64dl_chunk(const unsigned char* __restrict__ st, v4d (&acc)[4][4], int lane, int wm,
-                                            int wn) {
+                                            int wn, int mode) {
   const unsigned char* As = st;
   const unsigned char* Bs = st + F64DL::AU * 16;
 #pragma unroll
@@ -897,12 +923,7 @@ __device__ __forceinline__ void f64dl_chunk(const unsigned char* __restrict__ st
       const int r = wn * 64 + cb * 16 + (lane & 15);
       b[cb] = *reinterpret_cast<const v2d*>(Bs + (r * F64DL::UPR + dl_slot(r, kg, F64DL::UPR)) * 16);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma_f64_16x16x4(a[rb][i], b[cb][i], acc[rb][cb]);
+    f64_mfma_blocks(a, b, acc, mode == kF64All);
   }
 }
 
@@ -918,6 +939,7 @@ __device__ __forceinline__ void f64dl_nt_tile(const double* __restrict__ A, int6
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[rb][cb][v] = 0.0;
   const int nch = K / F64DL::BK;
+  const int mode = f64_block_mode(m0 == n0, wm, wn);
   if (nch > 0) f64dl_issue(A, lda, B, ldb, M, N, m0, n0, 0, lds, wave, lane);
   for (int c = 0; c < nch; c += 2) {
 #pragma unroll
@@ -930,7 +952,7 @@ __device__ __forceinline__ void f64dl_nt_tile(const double* __restrict__ A, int6
         if (c + s + 1 < nch)
           f64dl_issue(A, lda, B, ldb, M, N, m0, n0, (c + s + 1) * F64DL::BK, lds + (s ^ 1) * F64DL::STAGE_BYTES, wave,
                       lane);
-        f64dl_chunk(lds + s * F64DL::STAGE_BYTES, acc, lane, wm, wn);
+        if (mode != kF64None) f64dl_chunk(lds + s * F64DL::STAGE_BYTES, acc, lane, wm, wn, mode);
       }
     }
   }
@@ -951,7 +973,8 @@ __device__ __forceinline__ void f64dl_nt_tile(const double* __restrict__ A, int6
 // both cores agree bitwise.  Preconditions (checked by the caller): K a
 // multiple of 16, ld a multiple of 4 and G 16-byte aligned, and for RIGHT d
 // a multiple of 4.  Rows (or columns) beyond d are read from the last ones:
-// they only feed outputs that are never stored.
+// they only feed outputs that are never stored.  As in f64dl_nt_tile, blocks
+// of a diagonal tile wholly below the diagonal are left at zero.
 template <bool RIGHT, int NST>
 struct F64G {
   static constexpr int BK = 16;
@@ -992,7 +1015,7 @@ __device__ __forceinline__ void f64g_issue(const float* __restrict__ G, int64_t 
 
 template <bool RIGHT, int NST>
 __device__ __forceinline__ void f64g_chunk(const unsigned char* __restrict__ st, v4d (&acc)[4][4], int lane, int wm,
-                                           int wn) {
+                                           int wn, int mode) {
   using C = F64G<RIGHT, NST>;
   const unsigned char* As = st;
   const unsigned char* Bs = st + C::OPB;
@@ -1018,12 +1041,14 @@ __device__ __forceinline__ void f64g_chunk(const unsigned char* __restrict__ st,
     else
       b[blk & 3] = v;
   }
+  const bool full = mode == kF64All;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma_f64_16x16x4((double)a[rb][q], (double)b[cb][q], acc[rb][cb]);
+      for (int cb = 0; cb < 4; ++cb)
+        if (rb <= cb || full) acc[rb][cb] = mfma_f64_16x16x4((double)a[rb][q], (double)b[cb][q], acc[rb][cb]);
 }
 
 template <bool RIGHT, int NST>
@@ -1039,6 +1064,7 @@ __device__ __forceinline__ void f64g_tile(const float* __restrict__ G, int64_t l
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[rb][cb][v] = 0.0;
   const int nch = K / C::BK;
+  const int mode = f64_block_mode(m0 == n0, wm, wn);
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
     if (s < nch) f64g_issue<RIGHT, NST>(G, ld, d, m0, n0, s * C::BK, lds + s * C::STAGE_BYTES, wave, lane);
@@ -1061,7 +1087,7 @@ __device__ __forceinline__ void f64g_tile(const float* __restrict__ G, int64_t l
         if (c + NST - 1 < nch)
           f64g_issue<RIGHT, NST>(G, ld, d, m0, n0, (c + NST - 1) * C::BK,
                                  lds + ((s + NST - 1) % NST) * C::STAGE_BYTES, wave, lane);
-        f64g_chunk<RIGHT, NST>(lds + s * C::STAGE_BYTES, acc, lane, wm, wn);
+        if (mode != kF64None) f64g_chunk<RIGHT, NST>(lds + s * C::STAGE_BYTES, acc, lane, wm, wn, mode);
       }
     }
   }
