@@ -45,17 +45,20 @@ def sym_gemm_flops(d: int) -> float:
     return float(d) * d * (d + 1)
 
 
-def newton_flops(d: int, K: int, j: int, x_low: bool = True):
+def newton_flops(d: int, K: int, j: int, x_low: bool = True, final_degree: int = 1):
     """Algorithmic (upper-triangle) flops of one Newton root, split by the
     kernel class that runs them: iterations t < K-1 take 4 symmetric products
-    (M^2, T2^2, T4 M, X M), the last one only X M; t < j run M's products in
-    float64, and the X product too unless x_low (then it runs on the
-    split-fp16 kernel, like every product of the float32 steps).  With x_low
-    the first X product (X0 = I) is no product: the init writes X1."""
+    (M^2, T2^2, T4 M, X M), the last one only X q(M): one product for the
+    step's own degree-1 polynomial, two for the degree-2 Taylor finish (q(M)
+    from M^2, then X q) and three for the degree-4 one (M^2, E^2 R, X q);
+    t < j run M's products in float64, and the X product too unless x_low
+    (then it runs on the split-fp16 kernel, like every product of the float32
+    steps).  With x_low the first X product (X0 = I) is no product: the init
+    writes X1."""
     f64 = low = 0.0
     g = sym_gemm_flops(d)
     for t in range(K):
-        m_products = 3 * g if t < K - 1 else 0.0
+        m_products = 3 * g if t < K - 1 else {1: 0.0, 2: g, 4: 2 * g}[max(final_degree, 1)]
         x_product = 0.0 if (x_low and t == 0) else g
         if t < j:
             f64 += m_products
@@ -119,7 +122,7 @@ def per_size_class(B, torch, grams, wl):
         ws = B.RootWorkspace()
         B.inv_quarter_root_batched(As, wl.eps, normalize=wl.normalize, Xs=Xs, workspace=ws, return_info=False)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        raw = torch.empty(32 * len(As), dtype=torch.uint8, device=As[0].device)
+        raw = torch.empty(B.ROOT_INFO_BYTES * len(As), dtype=torch.uint8, device=As[0].device)
         e0.record()
         B.inv_quarter_root_batched(As, wl.eps, normalize=wl.normalize, Xs=Xs, workspace=ws, return_info=False,
                                    info_out=raw)
@@ -127,7 +130,8 @@ def per_size_class(B, torch, grams, wl):
         torch.cuda.synchronize()
         info = B.decode_info(raw, len(As))
         ms = e0.elapsed_time(e1)
-        flops = sum(sum(newton_flops(d, int(r["iters"]), int(r["fp64_iters"]))) for r in info)
+        flops = sum(sum(newton_flops(d, int(r["iters"]), int(r["fp64_iters"]), final_degree=int(r["final_degree"])))
+                    for r in info)
         tf = flops / (ms / 1e3) / 1e12
         out[str(d)] = {"count": len(As), "ms": round(ms, 3), "tflops": round(tf, 2),
                        "pct_fp32_mfma_peak": round(100 * tf / PEAK_TFLOPS["f32"], 2),
@@ -157,7 +161,7 @@ def bench_cans(args, torch, B, peaks):
     del G
     Ws = [torch.empty(d, d, dtype=torch.float32, device=dev) for _ in As]
     ws = B.RootWorkspace()
-    infos = torch.empty(32 * batch, dtype=torch.uint8, device=dev)
+    infos = torch.empty(B.ROOT_INFO_BYTES * batch, dtype=torch.uint8, device=dev)
 
     def step():
         B.inv_sqrt_root_batched(As, eps, normalize="none", precision=args.precision, Xs=Ws, workspace=ws,
@@ -258,7 +262,7 @@ def bench_polar(args, torch, B, peaks):
     Gs = [torch.from_numpy(W.gradient("moe", w, 1)).to(dev) for w in range(len(wl.shapes))]
     Os = [torch.empty_like(G) for G in Gs]
     ws = B.RootWorkspace()
-    infos = torch.empty(32 * len(Gs), dtype=torch.uint8, device=dev)
+    infos = torch.empty(B.ROOT_INFO_BYTES * len(Gs), dtype=torch.uint8, device=dev)
 
     def step():
         B.polar_cans_batched(Gs, precision=args.precision, Os=Os, workspace=ws, return_info=False, info_out=infos)
@@ -460,7 +464,7 @@ def main(argv=None) -> int:
     Us = [torch.empty(m, n, dtype=torch.float32, device=dev) for m, n in shapes]
     ws = B.RootWorkspace()
     total = args.warmup + args.steps
-    infos = [torch.empty(32 * 2 * nw, dtype=torch.uint8, device=dev) for _ in range(total)]
+    infos = [torch.empty(B.ROOT_INFO_BYTES * 2 * nw, dtype=torch.uint8, device=dev) for _ in range(total)]
 
     if args.optimizer_step:
         Ms = [torch.zeros(m, n, dtype=torch.float32, device=dev) for m, n in shapes]
@@ -506,7 +510,7 @@ def main(argv=None) -> int:
             d = shapes[k % nw][0] if k < nw else shapes[k % nw][1]
             if d <= 128:
                 continue
-            a, b = newton_flops(d, int(rec["iters"]), int(rec["fp64_iters"]))
+            a, b = newton_flops(d, int(rec["iters"]), int(rec["fp64_iters"]), final_degree=int(rec["final_degree"]))
             f64 += a
             f32 += b
             iters.append((int(rec["iters"]), int(rec["fp64_iters"])))

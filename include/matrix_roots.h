@@ -85,7 +85,9 @@ typedef int32_t mr_dtype;
 #define MR_INFO_NOT_PD 4        /* Jacobi: an eigenvalue + eps <= 0; Newton: no usable bound;
                                    X is all NaN                                              */
 #define MR_INFO_NOT_CONVERGED 8 /* Jacobi: still rotating after 30 sweeps; Newton: residual
-                                   above 2e-3 * sqrt(d) (e.g. A + eps I not positive definite) */
+                                   above r * sqrt(d), r = 2e-3 after a plain last step, 0.0243
+                                   (0.135) after a degree-2 (degree-4) finish (e.g. A + eps I
+                                   not positive definite)                                    */
 
 /* One weight for gram_ema_update.  G: m x n float32 (ldg >= n).
  * L: m x m, R: n x n, both of the call's state dtype (ldl >= m, ldr >= n),
@@ -114,7 +116,7 @@ typedef struct {
 } mr_root_problem;
 
 /* Per-matrix outcome of inv_quarter_root_batched (device memory, written by
- * the call).  32 bytes. */
+ * the call).  40 bytes. */
 typedef struct {
   double scale;       /* s: trace(A) (MR_NORM_TRACE) or 1                        */
   double bound;       /* c >= lambda_max(A/s + eps I) (Newton); 0 for Jacobi      */
@@ -124,6 +126,9 @@ typedef struct {
                          used; Jacobi: off-diagonal Frobenius norm of the
                          rotated A/s at exit                                      */
   uint32_t flags;     /* MR_INFO_* bits                                           */
+  int32_t final_degree; /* Newton: degree in M of the last X update (1, 2 or 4,
+                           see MR_NEWTON); 0 for Jacobi and the other calls      */
+  int32_t reserved;   /* 0                                                        */
 } mr_root_info;
 
 /* One weight for precondition_apply.  XL: m x m, G: m x n, XR: n x n, U: m x n,
@@ -181,7 +186,11 @@ size_t gram_ema_update_workspace(const mr_gram_problem* problems, int32_t count,
  *    for the -1/2 root), taken to the 4th root.  c = 1.01 times the
  *    Wolkowicz-Styan upper bound on lambda_max(A/s + eps I) (the OKLS page,
  *    appendix D, normalises by an O(d^2) upper bound in the same way); the
- *    iteration count follows from eps/c.  The last iteration updates X only.
+ *    iteration count follows from eps/c.  The last iteration updates X only:
+ *    with the step's polynomial, or, once the spectrum of M lies within
+ *    0.0162 (0.0898) of 1, with the degree-2 (degree-4) Taylor polynomial of
+ *    M^(-1/4) about I, which ends the iteration a step or two earlier with a
+ *    truncation error below 5e-7.
  *  - MR_NEWTON_F32: as MR_NEWTON with the float32 steps on the float32
  *    matrix cores.
  *  - MR_NEWTON_F64: the Newton iteration with every step in float64 (twice
@@ -377,11 +386,14 @@ typedef struct {
 int32_t mr_trace_enable(int32_t on); /* returns the previous setting */
 int32_t mr_trace_collect(mr_trace_record* out, int32_t capacity);
 
-/* The step scales the library uses for a Newton root whose spectrum bound is
- * [m0, 1/1.01] (m0 = eps/c): writes min(K, capacity) scales s_t, stores the
- * count of float64 steps in *fp64_steps (may be NULL) and returns K, the
- * number of steps (-1 on bad arguments).  Host-only. */
-int32_t mr_newton_schedule(double m0, double* scales, int32_t capacity, int32_t* fp64_steps);
+/* The step scales the library uses for a Newton root (MR_NEWTON) whose
+ * spectrum bound is [m0, 1/1.01] (m0 = eps/c): writes min(K, capacity) scales
+ * s_t, stores the count of float64 steps in *fp64_steps and the degree in M of
+ * the last step's X update in *final_degree (1: the step's own (5 - M/s)/4;
+ * 2 or 4: the Taylor polynomial of M^(-1/4) about I; either pointer may be
+ * NULL) and returns K, the number of steps (-1 on bad arguments).  Host-only. */
+int32_t mr_newton_schedule(double m0, double* scales, int32_t capacity, int32_t* fp64_steps,
+                           int32_t* final_degree);
 
 /*
  * Matrix-core peaks of the current device, for reporting rooflines (the

@@ -88,8 +88,9 @@ class ApplyProblem(ctypes.Structure):
 
 
 ROOT_INFO_DTYPE = np.dtype([("scale", "<f8"), ("bound", "<f8"), ("iters", "<i4"), ("fp64_iters", "<i4"),
-                            ("residual", "<f4"), ("flags", "<u4")])
-assert ROOT_INFO_DTYPE.itemsize == 32
+                            ("residual", "<f4"), ("flags", "<u4"), ("final_degree", "<i4"), ("reserved", "<i4")])
+ROOT_INFO_BYTES = ROOT_INFO_DTYPE.itemsize
+assert ROOT_INFO_BYTES == 40
 
 
 class TraceRecord(ctypes.Structure):
@@ -147,7 +148,7 @@ def library() -> ctypes.CDLL:
     lib.precondition_apply_workspace.restype = sz
     lib.mr_newton_iterations.argtypes = [i32, f64, f64]
     lib.mr_newton_iterations.restype = i32
-    lib.mr_newton_schedule.argtypes = [f64, vp, i32, vp]
+    lib.mr_newton_schedule.argtypes = [f64, vp, i32, vp, vp]
     lib.mr_newton_schedule.restype = i32
     lib.mr_trace_enable.argtypes = [i32]
     lib.mr_trace_enable.restype = i32
@@ -287,8 +288,8 @@ class RootWorkspace:
 
         if self.buf is None or self.buf.numel() < nbytes or self.buf.device != torch.device(device):
             self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
-        if self.info is None or self.info.numel() < 32 * count or self.info.device != torch.device(device):
-            self.info = torch.empty(32 * max(count, 1), dtype=torch.uint8, device=device)
+        if self.info is None or self.info.numel() < ROOT_INFO_BYTES * count or self.info.device != torch.device(device):
+            self.info = torch.empty(ROOT_INFO_BYTES * max(count, 1), dtype=torch.uint8, device=device)
         return self.buf, self.info
 
 
@@ -300,7 +301,7 @@ def inv_quarter_root_batched(As: Sequence, eps: float, normalize: str = "trace",
 
     Returns (Xs, info) where info is a numpy structured array (fields of
     mr_root_info) read after synchronising the stream, or (Xs, None).
-    info_out: optional device uint8 tensor of 32*len(As) bytes that receives
+    info_out: optional device uint8 tensor of ROOT_INFO_BYTES*len(As) bytes that receives
     the info records instead of the workspace's buffer (no synchronisation
     when return_info is False); decode it later with decode_info().
     """
@@ -336,7 +337,7 @@ def _root_call(entry, size_entry, code, As, eps, normalize, Xs, workspace, strea
     ws = workspace or RootWorkspace()
     buf, info = ws.get(need, count, dev)
     if info_out is not None:
-        if info_out.numel() < 32 * count:
+        if info_out.numel() < ROOT_INFO_BYTES * count:
             raise ValueError("info_out too small")
         info = info_out
     _check(entry(ctypes.addressof(probs), count, dt, float(eps), _NORMS[normalize], code, _ptr(info), _ptr(buf),
@@ -383,7 +384,7 @@ def polar_cans_batched(Gs: Sequence, precision: str = "f16", Os: Optional[Sequen
     ws = workspace or RootWorkspace()
     buf, info = ws.get(need, count, dev)
     if info_out is not None:
-        if info_out.numel() < 32 * count:
+        if info_out.numel() < ROOT_INFO_BYTES * count:
             raise ValueError("info_out too small")
         info = info_out
     _check(lib.polar_cans_batched(ctypes.addressof(probs), count, code, _ptr(info), _ptr(buf), buf.numel(),
@@ -444,7 +445,7 @@ def cans_ceilings():
 
 def decode_info(info, count: int):
     """Device or host uint8 buffer of mr_root_info records -> numpy records."""
-    host = info[: 32 * count].cpu().numpy()
+    host = info[: ROOT_INFO_BYTES * count].cpu().numpy()
     return host.view(ROOT_INFO_DTYPE).copy()
 
 
@@ -473,14 +474,17 @@ def precondition_apply(XLs: Sequence, Gs: Sequence, XRs: Sequence, alpha: float 
     return Us
 
 
-def newton_schedule(m0: float):
-    """(scales, fp64_steps) of the library's Newton schedule for floor m0."""
+def newton_schedule(m0: float, final_degree: bool = False):
+    """(scales, fp64_steps) of the library's Newton schedule for floor m0, and
+    the degree of the last X update when final_degree is set."""
     buf = (ctypes.c_double * 128)()
     j = ctypes.c_int32(0)
-    K = library().mr_newton_schedule(float(m0), ctypes.addressof(buf), 128, ctypes.addressof(j))
+    deg = ctypes.c_int32(0)
+    K = library().mr_newton_schedule(float(m0), ctypes.addressof(buf), 128, ctypes.addressof(j), ctypes.addressof(deg))
     if K < 0:
         raise ValueError("bad m0")
-    return [buf[i] for i in range(K)], int(j.value)
+    out = ([buf[i] for i in range(K)], int(j.value))
+    return out + (int(deg.value),) if final_degree else out
 
 
 class PeakInfo(ctypes.Structure):

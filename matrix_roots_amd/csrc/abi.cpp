@@ -270,14 +270,16 @@ int32_t mr_trace_collect(mr_trace_record* out, int32_t capacity) {
   return std::min(k, capacity);
 }
 
-int32_t mr_newton_schedule(double m0, double* scales, int32_t capacity, int32_t* fp64_steps) {
+int32_t mr_newton_schedule(double m0, double* scales, int32_t capacity, int32_t* fp64_steps,
+                           int32_t* final_degree) {
   if (!(m0 > 0.0 && m0 <= 1.0 / kBoundSafety) || capacity < 0) return -1;
   double tmp[kMaxNewtonIters];
-  int K = 0, j = 0;
-  newton_scaled_schedule(m0, 1.0 / kBoundSafety, kNewtonTol, kSwitchM, kMaxNewtonIters, tmp, &K, &j);
+  int K = 0, j = 0, fin = 1;
+  newton_scaled_schedule(m0, 1.0 / kBoundSafety, kNewtonTol, kSwitchM, kMaxNewtonIters, tmp, &K, &j, true, &fin);
   if (scales)
     for (int i = 0; i < K && i < capacity; ++i) scales[i] = tmp[i];
   if (fp64_steps) *fp64_steps = j;
+  if (final_degree) *final_degree = fin;
   return K;
 }
 
@@ -695,14 +697,14 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
     int k_cap, j_cap;
     if (normalize == MR_NORM_TRACE) {
       newton_scaled_schedule(eps / (1.02 * (1.0 + eps)), 1.0 / kBoundSafety, kNewtonTol, kSwitchM, kMaxNewtonIters,
-                             nullptr, &k_cap, &j_cap);
+                             nullptr, &k_cap, &j_cap, x_low);
     } else {
       k_cap = kMaxNewtonIters;
       j_cap = kMaxNewtonIters;
     }
     if ((st = traced(kTrBound, true, s, [&] {
            return launch_root_bound(state, partial, P.partial_stride, sched, 0, P.n_newton, normalize, eps, k_cap,
-                                    all_f64 ? 1 : 0, s);
+                                    all_f64 ? 1 : 0, x_low ? 1 : 0, s);
          }, "root bound launch")) != MR_OK)
       return st;
     int k_max = k_cap, j_max = all_f64 ? k_cap : j_cap;

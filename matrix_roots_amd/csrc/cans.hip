@@ -335,6 +335,8 @@ __global__ __launch_bounds__(64) void cans_info_kernel(RootState* state, const d
     o.fp64_iters = 0;
     o.residual = st.residual;
     o.flags = st.flags;
+    o.final_degree = 0;
+    o.reserved = 0;
     info[st.problem] = o;
   }
 }

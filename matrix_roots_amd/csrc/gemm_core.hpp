@@ -1,20 +1,24 @@
 // MFMA tile cores for gfx950.
 //
-// Both cores compute one 128 x 128 block tile of C = A * B^T where row i of A
-// and row j of B are indexed along the contraction k.  With symmetric operands
-// (every product of the coupled Newton iteration, the Gram of G's rows) this
-// "NT" form reads both operands along contiguous rows.  The float64 core can
-// also read an operand "transposed" (element (i, k) at ptr[k * ld + i]), which
-// the right Gram G^T G needs, and can take float32 inputs that it widens to
-// float64 on the way into LDS (float32 products are exact in float64).
+// Every core computes a block tile of C = A * B^T where row i of A and row j
+// of B are indexed along the contraction k.  With symmetric operands (every
+// product of the coupled Newton iteration, the Gram of G's rows) this "NT"
+// form reads both operands along contiguous rows; the Gram cores can also read
+// an operand "transposed" (element (i, k) at ptr[k * ld + i]), which the right
+// Gram G^T G needs, and take float32 inputs widened to float64 (float32
+// products are exact in float64).
 //
-// Work split: 256 threads = 4 waves in a 2 x 2 grid, each wave owns a 64 x 64
-// sub-tile.  A and B tiles are staged through LDS (one buffer, loads for the
-// next k-chunk prefetched into registers while the current chunk is consumed).
-// Within a k-chunk each lane reads a run of consecutive k for its row with
-// 128-bit LDS reads; consecutive MFMAs consume that run element by element.
-// The k order inside a chunk is therefore permuted, identically for A and B,
-// which leaves the sum unchanged.
+// Cores (float32, float64 and split-fp16 arithmetic):
+//   f32_nt_tile, f64_tile, x3_nt_tile   128 x 128, register-staged loads
+//   f64dl_nt_tile, f64g_tile, x3dl_nt_tile   128 x 128, direct-to-LDS copies
+//   x3w_nt_tile   256 x 256, direct-to-LDS copies, one accumulator
+// The 128 x 128 cores run 256 threads = 4 waves in a 2 x 2 grid, each wave
+// owning a 64 x 64 sub-tile; x3w_nt_tile runs 8 waves in a 2 x 4 grid of
+// 128 x 64.  A and B chunks are staged through LDS stages.  Within a k-chunk
+// each lane reads a run of consecutive k for its row with 128-bit LDS reads;
+// consecutive MFMAs consume that run element by element.  The k order inside
+// a chunk is therefore permuted, identically for A and B, which leaves the
+// sum unchanged.
 #pragma once
 
 #include "mr_common.hpp"

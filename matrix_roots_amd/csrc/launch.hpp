@@ -47,8 +47,10 @@ struct RootState {
   int32_t method;  // MR_JACOBI or MR_NEWTON
   int32_t sweeps;
   int32_t problem;  // index of the problem in the caller's array
+  int32_t fin;      // degree in M of the last Newton step's X update (1, 2 or 4)
+  int32_t pad;
 };
-static_assert(sizeof(RootState) == 64, "RootState layout");
+static_assert(sizeof(RootState) == 72, "RootState layout");
 
 // ---------------------------------------------------------------- Gram EMA
 struct SyrkJob {
@@ -177,7 +179,7 @@ hipError_t launch_f32_nt(const F32Batch& b, int vec, hipStream_t s);
 hipError_t launch_root_stats(const RootBatch& b, hipStream_t s);
 hipError_t launch_root_bound(RootState* state, const double* partial, int64_t partial_stride, double* sched,
                              int32_t slot_begin, int32_t nslots, int32_t normalize, double eps,
-                             int32_t k_cap, int32_t all_f64, hipStream_t s);
+                             int32_t k_cap, int32_t all_f64, int32_t finish, hipStream_t s);
 hipError_t launch_root_init(const RootBatch& b, hipStream_t s);
 enum StageKind { kStageF64 = 0, kStageF32 = 1, kStageX3 = 2, kStageX3B64 = 3 };
 hipError_t launch_newton_stage(const NewtonLaunch& L, int kind, int vec, hipStream_t s);

@@ -92,7 +92,7 @@ __device__ __forceinline__ SplitBuf split_at(char* region, int d, int h) {
   return SplitBuf{hi, hi + (int64_t)d * d};
 }
 struct RolesS {
-  SplitBuf M, T2, X, Xn, T4, Mx;
+  SplitBuf M, T2, X, Xn, T4, Mx, Q;
 };
 __device__ __forceinline__ RolesS roless(char* region, int d, int t) {
   const bool even = (t & 1) == 0;
@@ -103,6 +103,7 @@ __device__ __forceinline__ RolesS roless(char* region, int d, int t) {
   r.Xn = split_at(region, d, even ? 2 : 4);
   r.T4 = split_at(region, d, 9);
   r.Mx = split_at(region, d, 5);
+  r.Q = split_at(region, d, 6);  // the degree-4 finish's q(M) (a float64 slot, dead in split steps)
   return r;
 }
 // X is stored times 2^-e so that |X| <= (eps/c)^(-1/4) stays below 2^13 in
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(256) void root_stats_kernel(const RootBatch B) {
 __global__ __launch_bounds__(64) void root_bound_kernel(RootState* state, const double* partial,
                                                         int64_t stride, double* sched, int32_t slot_begin,
                                                         int32_t normalize, double eps, int32_t k_cap,
-                                                        int32_t all_f64) {
+                                                        int32_t all_f64, int32_t finish) {
   __shared__ double red[64];
   const int slot = slot_begin + blockIdx.x;
   RootState& st = state[slot];
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(64) void root_bound_kernel(RootState* state, const 
   if (threadIdx.x != 0) return;
   uint32_t flags = 0;
   double s = 1.0, c = 1.0;
-  int K = 0, j = 0;
+  int K = 0, j = 0, fin = 1;
   if (nf > 0.0 || !isfinite(tr) || !isfinite(f2)) {
     flags |= MR_INFO_NONFINITE;
   } else {
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(64) void root_bound_kernel(RootState* state, const 
         c = 1.0;
       } else {
         newton_scaled_schedule(fmin(eps / c, 1.0 / kBoundSafety), 1.0 / kBoundSafety, kNewtonTol, kSwitchM,
-                               k_cap, sched + (int64_t)slot * kMaxNewtonIters, &K, &j);
+                               k_cap, sched + (int64_t)slot * kMaxNewtonIters, &K, &j, finish != 0, &fin);
         if (all_f64) j = K;
       }
     }
@@ -283,6 +284,7 @@ __global__ __launch_bounds__(64) void root_bound_kernel(RootState* state, const 
   st.out_scale = pow(c, -0.25);
   st.K = K;
   st.j = j;
+  st.fin = fin;
   st.flags = flags;
 }
 
@@ -342,6 +344,7 @@ __device__ __forceinline__ int find_class(const NewtonLaunch& L, int64_t b) {
 struct StageJob {
   bool active;
   int job;
+  int fin;  // this iteration's finish degree (1: a plain step)
   int ti, tj;
   int d;
   char* region;
@@ -381,8 +384,16 @@ __device__ __forceinline__ StageJob stage_job(const NewtonLaunch& L, int kind) {
     act = t < K && t < j && L.x_low && xupdate;
   else
     act = t >= j && t < K;
-  if (t == K - 1 && !xupdate) act = false;
+  if (t == K - 1) {
+    if (st.fin <= 1) {
+      if (!xupdate) act = false;
+    } else {
+      // Taylor finish (split steps): job 0 of stages 0..1 (degree 2) or 0..2 (degree 4)
+      act = act && s.job == 0 && L.stage <= (st.fin == 2 ? 1 : 2);
+    }
+  }
   if (t == 0 && xupdate && L.x_low) act = false;
+  s.fin = t == K - 1 ? st.fin : 1;
   s.active = act;
   s.s = act ? L.sched[(int64_t)slot * kMaxNewtonIters + t] : 1.0;
   s.m0 = st.eps / st.c;
@@ -483,18 +494,46 @@ __global__ __launch_bounds__(256, MR_F32_OCC) void newton_f32_kernel(const Newto
 // as a perturbation of 5, so its float32 rounding is harmless there.
 struct SplitOps {
   SplitRef A, B, Cin;
-  SplitBuf C;
-  bool has_cin;
+  SplitBuf C, C2;  // C2: a second output of the same product (degree-4 finish)
+  bool has_cin, has_c2;
   double alpha, beta, gamma;
+  double alpha2, beta2, gamma2;
 };
 
-__device__ __forceinline__ SplitOps split_ops(const RolesS& r, int stage, int job, double s, bool xm) {
+// Coefficients of the Taylor series of (1 - x)^(-1/4): c_k = c_{k-1} (k - 3/4) / k.
+constexpr double kTay0 = 1.0, kTay1 = 0.25, kTay2 = 5.0 / 32.0, kTay3 = 15.0 / 128.0, kTay4 = 195.0 / 2048.0;
+
+__device__ __forceinline__ SplitOps split_ops(const RolesS& r, int stage, int job, double s, bool xm, int fin = 1) {
   SplitOps o;
   o.has_cin = false;
+  o.has_c2 = false;
   o.alpha = 1.0;
   o.beta = 0.0;
   o.gamma = 0.0;
   const double is = 1.0 / s;
+  if (fin == 2) {  // last step, degree-2 Taylor finish in E = I - M
+    if (stage == 0) {  // Q = c0 + c1 E + c2 E^2 = c2 M^2 - (c1 + 2 c2) M + (c0 + c1 + c2) I
+      o.A = r.M.ref(); o.B = r.M.ref(); o.C = r.T2; o.Cin = r.M.ref(); o.has_cin = true;
+      o.alpha = kTay2; o.beta = -(kTay1 + 2.0 * kTay2); o.gamma = kTay0 + kTay1 + kTay2;
+    } else {  // X' = X Q
+      o.A = r.X.ref(); o.B = r.T2.ref(); o.C = r.Xn;
+    }
+    return o;
+  }
+  if (fin == 4) {  // last step, degree-4 Taylor finish: q = c0 + c1 E + E^2 (c2 + c3 E + c4 E^2)
+    if (stage == 0) {  // E^2 = M^2 - 2M + I, and R = c2 + c3 E + c4 E^2 from the same M^2
+      o.A = r.M.ref(); o.B = r.M.ref(); o.C = r.T2; o.Cin = r.M.ref(); o.has_cin = true;
+      o.alpha = 1.0; o.beta = -2.0; o.gamma = 1.0;
+      o.C2 = r.T4; o.has_c2 = true;
+      o.alpha2 = kTay4; o.beta2 = -(2.0 * kTay4 + kTay3); o.gamma2 = kTay2 + kTay3 + kTay4;
+    } else if (stage == 1) {  // Q = E^2 R + c1 E + c0 I = E^2 R - c1 M + (c0 + c1) I
+      o.A = r.T2.ref(); o.B = r.T4.ref(); o.C = r.Q; o.Cin = r.M.ref(); o.has_cin = true;
+      o.alpha = 1.0; o.beta = -kTay1; o.gamma = kTay0 + kTay1;
+    } else {  // X' = X Q
+      o.A = r.X.ref(); o.B = r.Q.ref(); o.C = r.Xn;
+    }
+    return o;
+  }
   if (stage == 0 && job == 0) {  // T2 = ((M/s)^2 - 10 M/s + 25 I) / 16
     o.A = r.M.ref(); o.B = r.M.ref(); o.C = r.T2; o.Cin = r.M.ref(); o.has_cin = true;
     o.alpha = is * is / 16.0; o.beta = -10.0 * is / 16.0; o.gamma = 25.0 / 16.0;
@@ -517,39 +556,49 @@ __global__ __launch_bounds__(256, 2) void newton_x3_kernel(const NewtonLaunch L,
   const StageJob s = stage_job(L, kind);
   if (!s.active) return;
   const RolesS r = roless(s.region, s.d, L.t);
-  const SplitOps o = split_ops(r, L.stage, s.job, s.s, kind == kStageX3B64);
+  const SplitOps o = split_ops(r, L.stage, s.job, s.s, kind == kStageX3B64, s.fin);
   const int m0 = s.ti * X3Tile::BM, n0 = s.tj * X3Tile::BN;
   v16f acc[2][2];
   x3_nt_tile_auto<VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, reinterpret_cast<unsigned char*>(smem), acc);
   const int d = s.d;
-  if (VEC == 8 && s.ti <= s.tj && m0 + X3Tile::BM <= d && n0 + X3Tile::BN <= d) {
-    // Whole tile on or above the diagonal: the upper elements and their
-    // mirror with wide stores through per-wave LDS slabs (the main loop ended
-    // with a block barrier, so the operand stages are free).
-    static_assert(4 * kSlabFloats * 4 <= (int)sizeof(smem), "four slabs fit in the operand stages");
-    wide_store_tile<2, 2, double>(acc, reinterpret_cast<float*>(smem), m0, n0, o.C.hi, o.C.lo, d, o.C.hi, o.C.lo, d,
-                                  o.has_cin ? o.Cin.hi : nullptr, o.has_cin ? o.Cin.lo : nullptr, o.alpha, o.beta,
-                                  o.gamma, s.ti == s.tj);
-    return;
-  }
-  f32_for_each(acc, [&](int rr, int cc, float v) {
-    const int gr = m0 + rr, gc = n0 + cc;
-    if (gr < d && gc < d && gr <= gc) {
-      const int64_t e = (int64_t)gr * d + gc;
-      double val = o.alpha * (double)v;
-      if (o.has_cin) val += o.beta * (double)join_f32(o.Cin.hi[e], o.Cin.lo[e]);
-      if (gr == gc) val += o.gamma;
-      split_put(o.C, e, (float)val);
-      if (gr != gc) split_put(o.C, (int64_t)gc * d + gr, (float)val);
+  const bool whole = VEC == 8 && s.ti <= s.tj && m0 + X3Tile::BM <= d && n0 + X3Tile::BN <= d;
+  static_assert(4 * kSlabFloats * 4 <= (int)sizeof(smem), "four slabs fit in the operand stages");
+  // Whole tile on or above the diagonal: the upper elements and their mirror
+  // with wide stores through per-wave LDS slabs (the main loop ended with a
+  // block barrier, so the operand stages are free); else element stores.
+  auto store = [&](const SplitBuf& C, double al, double be, double ga) __attribute__((always_inline)) {
+    if (whole) {
+      wide_store_tile<2, 2, double>(acc, reinterpret_cast<float*>(smem), m0, n0, C.hi, C.lo, d, C.hi, C.lo, d,
+                                    o.has_cin ? o.Cin.hi : nullptr, o.has_cin ? o.Cin.lo : nullptr, al, be, ga,
+                                    s.ti == s.tj);
+      return;
     }
-  });
+    f32_for_each(acc, [&](int rr, int cc, float v) {
+      const int gr = m0 + rr, gc = n0 + cc;
+      if (gr < d && gc < d && gr <= gc) {
+        const int64_t e = (int64_t)gr * d + gc;
+        double val = al * (double)v;
+        if (o.has_cin) val += be * (double)join_f32(o.Cin.hi[e], o.Cin.lo[e]);
+        if (gr == gc) val += ga;
+        split_put(C, e, (float)val);
+        if (gr != gc) split_put(C, (int64_t)gc * d + gr, (float)val);
+      }
+    });
+  };
+  if (!o.has_c2) {
+    store(o.C, o.alpha, o.beta, o.gamma);
+  } else {  // two outputs of one product (degree-4 finish)
+    store(o.C, o.alpha, o.beta, o.gamma);
+    store(o.C2, o.alpha2, o.beta2, o.gamma2);
+  }
 }
 
 // The same stages on 256 x 256 tiles with the single-accumulator split core
 // (x3w_nt_tile).  Its B operands are M, the split copy Mx of a float64 M, or
 // T2, whose spectra lie in [0, 1] and [1/4, 25/16] (u/s <= 3 in these steps,
-// the float64 steps' M <= 1), so every |B| < 2 and the 2^11 scaling of B's
-// hi half stays far inside fp16's range.  The host picks this kernel for
+// the float64 steps' M <= 1), or in a finishing step R (in [0.15, 0.17]) or
+// q(M) (in [1, 1.03]), so every |B| < 2 and the 2^11 scaling of B's hi half
+// stays far inside fp16's range.  The host picks this kernel for
 // classes with d a multiple of 32 (whole 32-deep chunks).
 __global__ __launch_bounds__(X3W::THREADS, 1) void newton_x3w_kernel(const NewtonLaunch L, int kind) {
   constexpr int kSmem = X3W::LDS_BYTES > 8 * kSlabFloats * 4 ? X3W::LDS_BYTES : 8 * kSlabFloats * 4;
@@ -557,29 +606,39 @@ __global__ __launch_bounds__(X3W::THREADS, 1) void newton_x3w_kernel(const Newto
   const StageJob s = stage_job(L, kind);
   if (!s.active) return;
   const RolesS r = roless(s.region, s.d, L.t);
-  const SplitOps o = split_ops(r, L.stage, s.job, s.s, kind == kStageX3B64);
+  const SplitOps o = split_ops(r, L.stage, s.job, s.s, kind == kStageX3B64, s.fin);
   const int m0 = s.ti * X3W::BM, n0 = s.tj * X3W::BN;
   const int d = s.d;
   v16f acc[X3W::RB][X3W::CB];
   x3w_nt_tile(o.A, d, o.B, d, d, d, d, m0, n0, smem, acc);
-  if (s.ti <= s.tj && m0 + X3W::BM <= d && n0 + X3W::BN <= d) {
-    // whole tile on or above the diagonal: wide stores through per-wave slabs
-    wide_store_tile<X3W::RB, X3W::WN, double>(acc, reinterpret_cast<float*>(smem), m0, n0, o.C.hi, o.C.lo, d, o.C.hi,
-                                              o.C.lo, d, o.has_cin ? o.Cin.hi : nullptr,
-                                              o.has_cin ? o.Cin.lo : nullptr, o.alpha, o.beta, o.gamma, s.ti == s.tj);
-    return;
-  }
-  x3w_for_each(acc, [&](int rr, int cc, float v) {
-    const int gr = m0 + rr, gc = n0 + cc;
-    if (gr < d && gc < d && gr <= gc) {
-      const int64_t e = (int64_t)gr * d + gc;
-      double val = o.alpha * (double)v;
-      if (o.has_cin) val += o.beta * (double)join_f32(o.Cin.hi[e], o.Cin.lo[e]);
-      if (gr == gc) val += o.gamma;
-      split_put(o.C, e, (float)val);
-      if (gr != gc) split_put(o.C, (int64_t)gc * d + gr, (float)val);
+  const bool whole = s.ti <= s.tj && m0 + X3W::BM <= d && n0 + X3W::BN <= d;
+  // whole tile on or above the diagonal: wide stores through per-wave slabs;
+  // else element stores
+  auto store = [&](const SplitBuf& C, double al, double be, double ga) __attribute__((always_inline)) {
+    if (whole) {
+      wide_store_tile<X3W::RB, X3W::WN, double>(acc, reinterpret_cast<float*>(smem), m0, n0, C.hi, C.lo, d, C.hi, C.lo,
+                                                d, o.has_cin ? o.Cin.hi : nullptr, o.has_cin ? o.Cin.lo : nullptr, al,
+                                                be, ga, s.ti == s.tj);
+      return;
     }
-  });
+    x3w_for_each(acc, [&](int rr, int cc, float v) {
+      const int gr = m0 + rr, gc = n0 + cc;
+      if (gr < d && gc < d && gr <= gc) {
+        const int64_t e = (int64_t)gr * d + gc;
+        double val = al * (double)v;
+        if (o.has_cin) val += be * (double)join_f32(o.Cin.hi[e], o.Cin.lo[e]);
+        if (gr == gc) val += ga;
+        split_put(C, e, (float)val);
+        if (gr != gc) split_put(C, (int64_t)gc * d + gr, (float)val);
+      }
+    });
+  };
+  if (!o.has_c2) {
+    store(o.C, o.alpha, o.beta, o.gamma);
+  } else {  // two outputs of one product (degree-4 finish)
+    store(o.C, o.alpha, o.beta, o.gamma);
+    store(o.C2, o.alpha2, o.beta2, o.gamma2);
+  }
 }
 
 // float64 M, X of iteration t -> float32 M, X of iteration t, for the
@@ -677,7 +736,10 @@ __global__ __launch_bounds__(64) void root_info_kernel(RootState* state, const d
   if (newton && st.K > 0) {
     const double r = sqrt(res);
     st.residual = (float)r;
-    if (!(r <= 2e-3 * sqrt((double)st.d))) st.flags |= MR_INFO_NOT_CONVERGED;
+    // rms deviation the last X update may start from: that of the plain step,
+    // or 1.5 times the spectrum radius a Taylor finish accepts
+    const double rms = st.fin == 2 ? 1.5 * kFinishQuad : st.fin == 4 ? 1.5 * kFinishQuartic : 2e-3;
+    if (!(r <= rms * sqrt((double)st.d))) st.flags |= MR_INFO_NOT_CONVERGED;
   }
   if (info) {
     mr_root_info o;
@@ -687,6 +749,8 @@ __global__ __launch_bounds__(64) void root_info_kernel(RootState* state, const d
     o.fp64_iters = newton ? min(st.j, st.K) : 0;
     o.residual = st.residual;
     o.flags = st.flags;
+    o.final_degree = newton ? st.fin : 0;
+    o.reserved = 0;
     info[st.problem] = o;
   }
 }
@@ -703,10 +767,10 @@ hipError_t launch_root_stats(const RootBatch& b, hipStream_t s) {
 
 hipError_t launch_root_bound(RootState* state, const double* partial, int64_t partial_stride, double* sched,
                              int32_t slot_begin, int32_t nslots, int32_t normalize, double eps, int32_t k_cap,
-                             int32_t all_f64, hipStream_t s) {
+                             int32_t all_f64, int32_t finish, hipStream_t s) {
   if (nslots <= 0) return hipSuccess;
   hipLaunchKernelGGL(root_bound_kernel, dim3(nslots), dim3(64), 0, s, state, partial, partial_stride, sched,
-                     slot_begin, normalize, eps, k_cap, all_f64);
+                     slot_begin, normalize, eps, k_cap, all_f64, finish);
   return hipGetLastError();
 }
 

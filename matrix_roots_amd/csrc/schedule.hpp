@@ -31,6 +31,17 @@ constexpr double kScaleCap64 = 4.8;  // cap on u/s while steps run in float64 (t
 constexpr double kScaleCap32 = 3.0;  // ... and in float32 (errors in the top
                                      // eigenvalues grow ~|1 - 4x/(5-x)| per step)
 
+// Finishing step.  Once the spectrum of M lies in [1 - delta, 1], the root is
+// X M^(-1/4) = X q(E) with E = I - M and q the Taylor polynomial of
+// (1 - x)^(-1/4) (coefficients 1, 1/4, 5/32, 15/128, 195/2048); the relative
+// error of X is max |(1 - x)^(1/4) q(x) - 1| over [0, delta].  Degree 2 costs
+// one product for q(M) and one for X q; degree 4 costs three, E^2 and
+// R = c2 + c3 E + c4 E^2 from one M M, then E^2 R and X q.  The limits keep
+// that error below 5e-7 (the plain step stops at 1 - l <= 1e-6, whose X error
+// is about 2.5e-7); past them the scaled step continues.
+constexpr double kFinishQuad = 0.0162;
+constexpr double kFinishQuartic = 0.0898;
+
 __host__ __device__ inline double newton_scalar_step(int p, double m) {
   const double t = ((double)(p + 1) - m) / (double)p;
   double tp = t;
@@ -46,12 +57,18 @@ __host__ __device__ inline double g4(double x) {
 
 // Scaled schedule for p = 4 from the spectrum bound [l, u] of M0, 0 < l <= u.
 // Writes the step scales to s_out[0..K) (s_out may be null), returns K >= 1
-// (steps until 1 - l <= tol, at most cap) and j <= K, the first step whose
-// input floor l >= switch_m (steps t < j run in float64).
+// (steps until 1 - l <= tol, at most cap), j <= K, the first step whose
+// input floor l >= switch_m (steps t < j run in float64), and fin, the
+// degree in M of the last step's X update: 1 (the plain step, X only), or,
+// with finish set, 2 or 4 (the Taylor finish above, taken at the first step
+// t >= max(j, 1) whose floor allows it and whose plain step would not already
+// end the iteration).
 __host__ __device__ inline void newton_scaled_schedule(double l, double u, double tol, double switch_m, int cap,
-                                                       double* s_out, int* K, int* j) {
+                                                       double* s_out, int* K, int* j, bool finish = false,
+                                                       int* fin = nullptr) {
   int k = 0;
   int jj = -1;
+  int deg = 1;
   while (true) {
     if (jj < 0 && l >= switch_m) jj = k;
     if ((k > 0 && 1.0 - l <= tol) || k >= cap) break;
@@ -76,13 +93,23 @@ __host__ __device__ inline void newton_scaled_schedule(double l, double u, doubl
     if (s_out) s_out[k] = s;
     const double a = g4(l / s), b = g4(u / s);
     const bool peak_inside = l / s <= 1.0 && u / s >= 1.0;
-    l = fmin(a, b);
+    const double l_next = fmin(a, b);
+    if (finish && jj >= 0 && k > 0 && 1.0 - l_next > tol) {
+      if (1.0 - l <= kFinishQuad) deg = 2;
+      else if (1.0 - l <= kFinishQuartic) deg = 4;
+      if (deg > 1) {
+        ++k;
+        break;
+      }
+    }
+    l = l_next;
     u = peak_inside ? 1.0 : fmax(a, b);
     ++k;
   }
   if (k == 0) k = 1;
   *K = k;
   *j = (jj < 0 || jj > k) ? k : jj;
+  if (fin) *fin = deg;
 }
 
 }  // namespace mr

@@ -151,26 +151,41 @@ def test_apply_validation(lib):
 
 def test_newton_schedule_converges_every_eigenvalue(lib):
     """For the library's step scales, every eigenvalue m0 <= m <= 1/1.01 of
-    M0 ends with x_K^4 m = m_K within 1e-6 of 1, i.e. x_K = m^(-1/4) to 2.5e-7:
-    each step maps m -> g(m/s), x -> x s^(-1/4) (5 - m/s)/4, g(y) = y((5-y)/4)^4.
-    Written here from the iteration's definition, independent of the library."""
+    M0 ends with x_K = m^(-1/4) to 1e-6: each step maps m -> g(m/s),
+    x -> x s^(-1/4) (5 - m/s)/4, g(y) = y((5-y)/4)^4; with the plain last step
+    x_K^4 m = m_K is within 1e-6 of 1, and a Taylor finish of degree n takes
+    x -> x sum_{k<=n} c_k (1-m)^k with c_k the binomial coefficients of
+    (1-e)^(-1/4), c_k = c_{k-1} (k - 3/4)/k.  Written here from the
+    iteration's definition, independent of the library."""
     import numpy as np
 
-    for m0 in (0.9, 0.5, 1e-2, 1e-4, 1e-6, 3e-7, 1e-8, 1e-10, 1e-14):
-        scales, j = B.newton_schedule(m0)
+    degrees = set()
+    for m0 in (0.9, 0.5, 1e-2, 1e-3, 1e-4, 1e-5, 1e-6, 3e-7, 1e-8, 1e-10, 1e-14):
+        scales, j, fin = B.newton_schedule(m0, final_degree=True)
         K = len(scales)
-        assert 1 <= K <= 40 and 0 <= j <= K
+        assert 1 <= K <= 40 and 0 <= j <= K and fin in (1, 2, 4)
+        degrees.add(fin)
         m = np.concatenate([np.geomspace(m0, 1 / 1.01, 4000), [m0, 1 / 1.01]])
         m_init = m.copy()
         x = np.ones_like(m)
         for t, s in enumerate(scales):
+            if t == K - 1 and fin > 1:
+                assert t >= max(j, 1)  # finishes run in the split steps
+                c = [1.0]
+                for k in range(1, fin + 1):
+                    c.append(c[-1] * (k - 0.75) / k)
+                e = 1.0 - m
+                x = x * sum(ck * e ** k for k, ck in enumerate(c))
+                break
             y = m / s
             x = x * s ** -0.25 * (5.0 - y) / 4.0
             m = y * ((5.0 - y) / 4.0) ** 4
             if t + 1 == j:
                 assert m.min() >= 5e-4 * (1 - 1e-12)  # float32 steps start at a floor >= 5e-4
-        assert np.max(np.abs(1.0 - m)) <= 1.01e-6, (m0, np.max(np.abs(1 - m)))
-        assert np.max(np.abs(x * m_init ** 0.25 - 1.0)) <= 1e-6
+        if fin == 1:
+            assert np.max(np.abs(1.0 - m)) <= 1.01e-6, (m0, np.max(np.abs(1 - m)))
+        assert np.max(np.abs(x * m_init ** 0.25 - 1.0)) <= 1e-6, (m0, fin)
+    assert degrees >= {2, 4}, degrees  # both finishes occur over these floors
 
 
 def test_newton_schedule_monotone_in_floor(lib):
@@ -178,7 +193,7 @@ def test_newton_schedule_monotone_in_floor(lib):
     launch count with the schedule of the smallest floor it can see."""
     prev = None
     for m0 in np.geomspace(1e-14, 0.99, 400):
-        K = len(B.newton_schedule(float(m0))[0])
+        K = len(B.newton_schedule(float(m0))[0])  # with the finishing rule
         if prev is not None:
             assert K <= prev, m0
         prev = K

@@ -162,6 +162,22 @@ def test_root_flags(torch_dev):
         assert np.isnan(Xs[1].cpu().numpy()).all()
 
 
+def test_newton_flags_indefinite_input(torch_dev):
+    """A + eps I with an eigenvalue well below zero has no inverse quarter
+    root: the Newton iterate never nears I, whichever last update the schedule
+    picks, and the residual check flags it."""
+    torch, dev = torch_dev
+    rng = W.rng_for(90, 6)
+    for d in (160, 288):
+        q, _ = np.linalg.qr(rng.standard_normal((d, d)))
+        lam = np.geomspace(1e-3, 1.0, d)
+        lam[d // 2] = -0.3
+        A = ((q * lam) @ q.T).astype(np.float32)
+        for normalize in ("none", "trace"):
+            _, info = B.inv_quarter_root_batched([to_dev(torch, dev, A)], 1e-6, normalize=normalize, method="newton")
+            assert info["flags"][0] & B.MR_INFO_NOT_CONVERGED, (d, normalize, info[0])
+
+
 # --------------------------------------------------------------------- apply
 def test_apply_matches_oracle(torch_dev):
     torch, dev = torch_dev
