@@ -32,7 +32,9 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6, "f16": 2500.0}  # MI355X dense MFMA (vendor figures)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E (vendor figure)
 # kernel class -> arithmetic whose peak bounds it
-CLASS_PREC = {"newton_f64": "f64", "syrk_ema": "f64", "newton_f32": "f32", "apply_f32": "f32", "newton_x3": "f16"}
+CLASS_PREC = {"newton_f64": "f64", "syrk_ema": "f64", "newton_f32": "f32", "apply_f32": "f32", "newton_x3": "f16",
+              "apply_x3": "f16"}
+SPLIT_CLASSES = ("newton_x3", "apply_x3")  # three fp16 MFMA products per float32-accurate product
 METRIC = "preconditioned matrix updates/sec + TFLOP/s as % fp32 MFMA peak, d=1024–4096"
 
 
@@ -519,11 +521,13 @@ def main(argv=None) -> int:
     step_flops = (f64 + f32 + syrk + apply_f) / args.steps
 
     elems = sum(m * n for m, n in shapes) * args.steps
-    stream_bytes = {"momentum": 12 * elems, "hyperball_reduce": 8 * elems, "hyperball_update": 12 * elems}
+    stream_bytes = {"momentum": 12 * elems, "hyperball_reduce": 8 * elems, "hyperball_update": 12 * elems,
+                    # maxima and split copies of XR, G, XL and W^T: 8 bytes read and 4 written per element
+                    "apply_split": 12 * sum(m * m + 2 * m * n + n * n for m, n in shapes) * args.steps}
     kernels = {}
     for name, (launches, ms) in sorted(trace.items()):
         flops = {"newton_f64": f64, "newton_f32": f32, "newton_x3": f32, "syrk_ema": syrk,
-                 "apply_f32": apply_f}.get(name)
+                 "apply_f32": apply_f, "apply_x3": apply_f}.get(name)
         ent = {"launches": launches, "ms_total": round(ms, 3), "ms_avg": round(ms / launches, 4)}
         if name in stream_bytes:
             gbs = stream_bytes[name] / (ms / 1e3) / 1e9
@@ -532,7 +536,7 @@ def main(argv=None) -> int:
             prec = CLASS_PREC[name]
             tf = flops / (ms / 1e3) / 1e12
             ent.update({"tflops": round(tf, 2), "peak": PEAK_TFLOPS[prec], "frac": round(tf / PEAK_TFLOPS[prec], 4)})
-            if name == "newton_x3":  # three fp16 MFMA products per float32-accurate product
+            if name in SPLIT_CLASSES:
                 ent["mfma_tflops"] = round(3 * tf, 2)
         kernels[name] = ent
     def roofline_for(name):
@@ -541,7 +545,7 @@ def main(argv=None) -> int:
              "unit": "TFLOP/s", "frac": k.get("frac"), "traffic": recorded_traffic(name, args.workload),
              "achieved_per_launch": "algorithmic flops of the class over the timed steps / sum of its "
                                     "event-measured launch durations"}
-        if name == "newton_x3":
+        if name in SPLIT_CLASSES:
             # float32-accurate products, each three fp16 MFMA products (hi*hi, hi*lo, lo*hi)
             r.update({"mfma_achieved": k.get("mfma_tflops"),
                       "mfma_frac": round(k["mfma_tflops"] / PEAK_TFLOPS["f16"], 4),

@@ -356,8 +356,15 @@ int32_t mr_cans_ceilings(double* y, double* z, double* p, int32_t capacity);
 /*
  * precondition_apply -- for every problem:  U = alpha * XL * G * XR
  * The two-sided application of the quarter powers (EMA-Gram page, section
- * "Background"; Shampoo form of the OKLS page, section 1).  float32 matrix
- * cores; the intermediate (G * XR)^T lives in the workspace.
+ * "Background"; Shampoo form of the OKLS page, section 1).  The two products
+ * (W^T = XR G^T, then U = alpha XL W) run on the fp16 matrix cores with
+ * float32-accurate split operands (x = hi + 2^-11 lo, three fp16 products per
+ * product, float32 accumulation), each operand scaled by the power of two
+ * that puts its largest magnitude in [2^14, 2^15) (exact, and undone after
+ * the product): the workspace holds split copies of XR, G, XL and W^T, rows
+ * padded with zeros to a multiple of 32 columns, W^T in float32 and the
+ * operands' maxima, each array 256-byte aligned.  Results scale exactly with
+ * power-of-two scalings of G, XL or XR.
  * Workspace: at least precondition_apply_workspace(...) bytes, 256-byte aligned.
  */
 mr_status precondition_apply(const mr_apply_problem* problems, int32_t count, float alpha,

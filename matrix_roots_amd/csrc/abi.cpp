@@ -31,6 +31,11 @@ using namespace mr;
 #ifndef MR_NEWTON_WIDE
 #define MR_NEWTON_WIDE 1
 #endif
+// precondition_apply on the fp16 matrix cores with split operands (else the
+// float32 matrix cores).
+#ifndef MR_APPLY_X3
+#define MR_APPLY_X3 1
+#endif
 
 namespace {
 
@@ -98,7 +103,7 @@ enum TraceClass {
   kTrSyrk, kTrApply, kTrJacobi, kTrStats, kTrBound, kTrInit, kTrNewton64, kTrNewton32, kTrConvert,
   kTrFinalize, kTrInfo, kTrNewtonX3, kTrCansBound, kTrCansInit, kTrCansP, kTrCansYZ, kTrCansFinal, kTrCansInfo,
   kTrPolarStats, kTrPolarBound, kTrPolarInit, kTrPolarA, kTrPolarX, kTrPolarFinal, kTrPolarInfo,
-  kTrMomentum, kTrHyperReduce, kTrHyperUpdate, kTrCount
+  kTrMomentum, kTrHyperReduce, kTrHyperUpdate, kTrApplyX3, kTrApplySplit, kTrCount
 };
 const char* const kTraceNames[kTrCount] = {"syrk_ema", "apply_f32", "jacobi", "root_stats", "root_bound",
                                            "root_init", "newton_f64", "newton_f32", "newton_convert",
@@ -106,7 +111,7 @@ const char* const kTraceNames[kTrCount] = {"syrk_ema", "apply_f32", "jacobi", "r
                                            "cans_init", "cans_p", "cans_yz", "cans_finalize", "cans_info",
                                            "polar_stats", "polar_bound", "polar_init", "polar_gram",
                                            "polar_update", "polar_finalize", "polar_info", "momentum",
-                                           "hyperball_reduce", "hyperball_update"};
+                                           "hyperball_reduce", "hyperball_update", "apply_x3", "apply_split"};
 struct TraceEntry {
   int cls;
   hipEvent_t a, b;
@@ -466,12 +471,174 @@ static mr_status validate_apply(const mr_apply_problem* p, int32_t count, float 
   return MR_OK;
 }
 
+// Split apply workspace of one problem: split copies (4 bytes per element)
+// of XR (n x n32), G (m x n32), XL (m x m32) and W^T (n x m32), and W^T in
+// float32 (n x m); each 256-aligned.  After all problems: the largest
+// magnitudes of every problem's XR, G, XL and W^T (4 words each).
+struct ApplySplitLayout {
+  size_t xr, g, xl, wt, wt32, end;
+  int64_t n32, m32;
+};
+static ApplySplitLayout apply_split_layout(const mr_apply_problem& q, size_t off) {
+  ApplySplitLayout L;
+  L.n32 = (q.n + 31) / 32 * 32;
+  L.m32 = (q.m + 31) / 32 * 32;
+  L.xr = off;
+  L.g = L.xr + align256((size_t)q.n * L.n32 * 4);
+  L.xl = L.g + align256((size_t)q.m * L.n32 * 4);
+  L.wt = L.xl + align256((size_t)q.m * L.m32 * 4);
+  L.wt32 = L.wt + align256((size_t)q.n * L.m32 * 4);
+  L.end = L.wt32 + align256((size_t)q.n * q.m * 4);
+  return L;
+}
+
 size_t precondition_apply_workspace(const mr_apply_problem* p, int32_t count) {
   if (!p || count <= 0) return 0;
   size_t tot = 0;
-  for (int i = 0; i < count; ++i)
-    if (p[i].m > 0 && p[i].n > 0) tot += align256((size_t)p[i].m * (size_t)p[i].n * 4);
+  for (int i = 0; i < count; ++i) {
+    if (p[i].m <= 0 || p[i].n <= 0) continue;
+    if (MR_APPLY_X3)
+      tot = apply_split_layout(p[i], tot).end;
+    else
+      tot += align256((size_t)p[i].m * (size_t)p[i].n * 4);
+  }
+  if (MR_APPLY_X3) tot += align256((size_t)count * 4 * sizeof(uint32_t));
   return tot;
+}
+
+// U = alpha XL G XR with split operands: maxima and split copies of XR, G and
+// XL; W^T = XR G^T (float32); its maxima and split copy; U = alpha XL W.
+static mr_status apply_split(const mr_apply_problem* p, int32_t count, float alpha, void* ws,
+                             const std::vector<int>& order, hipStream_t s) {
+  std::vector<ApplySplitLayout> lay(count);
+  size_t off = 0;
+  for (int i = 0; i < count; ++i) {
+    lay[i] = apply_split_layout(p[i], off);
+    off = lay[i].end;
+  }
+  char* base = static_cast<char*>(ws);
+  auto half = [&](size_t o) { return reinterpret_cast<_Float16*>(base + o); };
+  uint32_t* amax_all = reinterpret_cast<uint32_t*>(base + off);
+  auto amax = [&](int i, int which) { return amax_all + 4 * i + which; };
+  struct Src {
+    const float* ptr;
+    int64_t ld, rows, cols;
+    _Float16* dst;
+    int64_t ldd;
+    uint32_t* amax;
+  };
+  // the float32 sources of one split pass (phase 0: XR, G, XL; phase 1: W^T)
+  auto sources = [&](int i, int phase, std::vector<Src>& out) {
+    const mr_apply_problem& q = p[i];
+    const ApplySplitLayout& L = lay[i];
+    if (phase == 0) {
+      out.push_back({q.XR, q.ldxr, q.n, q.n, half(L.xr), L.n32, amax(i, 0)});
+      out.push_back({q.G, q.ldg, q.m, q.n, half(L.g), L.n32, amax(i, 1)});
+      out.push_back({q.XL, q.ldxl, q.m, q.m, half(L.xl), L.m32, amax(i, 2)});
+    } else {
+      out.push_back({reinterpret_cast<float*>(base + L.wt32), q.m, q.n, q.m, half(L.wt), L.m32, amax(i, 3)});
+    }
+  };
+  mr_status st = MR_OK;
+  auto split_pass = [&](int phase) -> mr_status {
+    std::vector<Src> srcs;
+    for (const int i : order) sources(i, phase, srcs);
+    for (size_t k0 = 0; k0 < srcs.size(); k0 += kMaxAbsMaxJobs) {
+      AbsMaxBatch b;
+      memset(&b, 0, sizeof b);
+      for (size_t k = k0; k < srcs.size() && b.njobs < kMaxAbsMaxJobs; ++k) {
+        const Src& x = srcs[k];
+        AbsMaxJob& J = b.job[b.njobs++];
+        J.src = x.ptr;
+        J.amax = x.amax;
+        J.lds = x.ld;
+        J.rows = (int32_t)x.rows;
+        J.cols = (int32_t)x.cols;
+        J.block_begin = b.total_blocks;
+        J.vec4 = aligned(x.ptr, 16) && x.ld % 4 == 0 && x.cols % 4 == 0 ? 1 : 0;
+        b.total_blocks += (int32_t)((x.rows + kAbsMaxRows - 1) / kAbsMaxRows);
+      }
+      mr_status r = traced(kTrApplySplit, b.total_blocks > 0, s, [&] { return launch_absmax(b, s); },
+                           "apply maxima launch");
+      if (r != MR_OK) return r;
+    }
+    for (size_t k0 = 0; k0 < srcs.size(); k0 += kMaxSplitPadJobs) {
+      SplitPadBatch b;
+      memset(&b, 0, sizeof b);
+      for (size_t k = k0; k < srcs.size() && b.njobs < kMaxSplitPadJobs; ++k) {
+        const Src& x = srcs[k];
+        SplitPadJob& J = b.job[b.njobs++];
+        J.src = x.ptr;
+        J.dst = x.dst;
+        J.amax = x.amax;
+        J.lds = x.ld;
+        J.ldd = x.ldd;
+        J.rows = (int32_t)x.rows;
+        J.cols = (int32_t)x.cols;
+        J.block_begin = b.total_blocks;
+        J.vec4 = aligned(x.ptr, 16) && x.ld % 4 == 0 ? 1 : 0;
+        b.total_blocks += (int32_t)((x.rows * x.ldd + 2047) / 2048);
+      }
+      mr_status r = traced(kTrApplySplit, b.total_blocks > 0, s, [&] { return launch_split_pad(b, s); },
+                           "apply split launch");
+      if (r != MR_OK) return r;
+    }
+    return MR_OK;
+  };
+  auto product = [&](int stage) -> mr_status {
+    X3ApplyBatch b;
+    memset(&b, 0, sizeof b);
+    auto flush = [&]() -> mr_status {
+      if (b.njobs == 0) return MR_OK;
+      mr_status r = traced(kTrApplyX3, b.total_blocks > 0, s, [&] { return launch_x3_apply(b, s); },
+                           "precondition_apply launch");
+      b.njobs = 0;
+      b.total_blocks = 0;
+      return r;
+    };
+    for (const int i : order) {
+      const mr_apply_problem& q = p[i];
+      const ApplySplitLayout& L = lay[i];
+      X3ApplyJob& J = b.job[b.njobs];
+      if (stage == 0) {  // W^T = XR G^T : n x m, contraction n
+        J.a = half(L.xr);
+        J.b = half(L.g);
+        J.c = reinterpret_cast<float*>(base + L.wt32);
+        J.a_max = amax(i, 0);
+        J.b_max = amax(i, 1);
+        J.ld = L.n32;
+        J.ldc = q.m;
+        J.M = (int32_t)q.n;
+        J.N = (int32_t)q.m;
+        J.alpha = 1.f;
+      } else {  // U = alpha XL W : m x n, contraction m
+        J.a = half(L.xl);
+        J.b = half(L.wt);
+        J.c = q.U;
+        J.a_max = amax(i, 2);
+        J.b_max = amax(i, 3);
+        J.ld = L.m32;
+        J.ldc = q.ldu;
+        J.M = (int32_t)q.m;
+        J.N = (int32_t)q.n;
+        J.alpha = alpha;
+      }
+      J.tiles_n = tiles(J.N, 128);
+      J.nblocks = tiles(J.M, 128) * J.tiles_n;
+      J.block_begin = b.total_blocks;
+      b.total_blocks += round8(J.nblocks);
+      ++b.njobs;
+      if (b.njobs == kMaxX3ApplyJobs && (st = flush()) != MR_OK) return st;
+    }
+    return flush();
+  };
+  if ((st = traced(kTrApplySplit, true, s, [&] { return launch_fill_zero(amax_all, 4 * count, s); },
+                   "apply maxima clear")) != MR_OK)
+    return st;
+  if ((st = split_pass(0)) != MR_OK) return st;
+  if ((st = product(0)) != MR_OK) return st;
+  if ((st = split_pass(1)) != MR_OK) return st;
+  return product(1);
 }
 
 mr_status precondition_apply(const mr_apply_problem* p, int32_t count, float alpha, void* ws, size_t ws_bytes,
@@ -496,6 +663,7 @@ mr_status precondition_apply(const mr_apply_problem* p, int32_t count, float alp
   std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
     return p[x].m * p[x].n * (p[x].m + p[x].n) > p[y].m * p[y].n * (p[y].m + p[y].n);
   });
+  if (MR_APPLY_X3) return apply_split(p, count, alpha, ws, order, s);
   for (int stage = 0; stage < 2; ++stage) {
     for (int vecpass = 0; vecpass < 2; ++vecpass) {
       const int vec = vecpass == 0 ? 4 : 1;

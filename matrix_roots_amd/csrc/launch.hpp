@@ -88,6 +88,73 @@ struct F32Job {
   int32_t pad;
 };
 static_assert(sizeof(F32Job) * kMaxApplyJobs + 64 < 4096, "apply table fits the kernel arguments");
+
+// Split-fp16 apply: operands are split copies of 2^s times a float32 matrix,
+// s per matrix such that the largest magnitude lands in [2^14, 2^15) (so
+// neither half overflows fp16 or loses precision to its subnormals, whatever
+// the matrix's scale), rows padded to a multiple of 32 and zero-filled,
+// written by split_pad_kernel; a split matrix of r rows and row stride ld is
+// its hi half (r * ld fp16) followed by its lo half.  The largest magnitude
+// of each matrix comes from absmax_kernel, as the bits of a float32 (for
+// non-negative floats their order is that of the unsigned bit patterns, and a
+// NaN sorts above infinity), combined with atomicMax over workgroups.
+struct X3ApplyJob {
+  const _Float16* a;     // split, M rows, row stride ld
+  const _Float16* b;     // split, N rows, row stride ld
+  float* c;              // float32 output, row stride ldc
+  const uint32_t* a_max; // largest magnitude of A's float32 source (sets its scale)
+  const uint32_t* b_max;
+  int64_t ld;            // the padded contraction length K (a multiple of 32)
+  int64_t ldc;
+  int32_t M, N;
+  int32_t tiles_n;
+  int32_t block_begin;   // multiple of 8
+  int32_t nblocks;
+  float alpha;           // C = alpha * A * B^T of the unscaled matrices
+};
+constexpr int kMaxX3ApplyJobs = 48;
+static_assert(sizeof(X3ApplyJob) * kMaxX3ApplyJobs + 64 < 4096, "split apply table fits the kernel arguments");
+struct X3ApplyBatch {
+  X3ApplyJob job[kMaxX3ApplyJobs];
+  int32_t njobs;
+  int32_t total_blocks;
+};
+// One float32 matrix (rows x cols, row stride lds) times 2^s into split form
+// at dst (row stride ldd >= cols, a multiple of 8; columns cols .. ldd - 1
+// zero); s from the matrix's largest magnitude *amax.
+struct SplitPadJob {
+  const float* src;
+  _Float16* dst;
+  const uint32_t* amax;
+  int64_t lds, ldd;
+  int32_t rows, cols;
+  int32_t block_begin;  // first workgroup of this job (2048 elements each)
+  int32_t vec4;         // src rows 16-byte aligned (float4 loads)
+};
+// Largest magnitude of a float32 matrix into *amax (zeroed beforehand), a
+// workgroup per kAbsMaxRows-row band.
+constexpr int kAbsMaxRows = 16;
+struct AbsMaxJob {
+  const float* src;
+  uint32_t* amax;
+  int64_t lds;
+  int32_t rows, cols;
+  int32_t block_begin;
+  int32_t vec4;  // rows 16-byte aligned, cols a multiple of 4
+};
+constexpr int kMaxAbsMaxJobs = 64;
+struct AbsMaxBatch {
+  AbsMaxJob job[kMaxAbsMaxJobs];
+  int32_t njobs;
+  int32_t total_blocks;
+};
+constexpr int kMaxSplitPadJobs = 64;
+static_assert(sizeof(SplitPadJob) * kMaxSplitPadJobs + 64 < 4096, "split table fits the kernel arguments");
+struct SplitPadBatch {
+  SplitPadJob job[kMaxSplitPadJobs];
+  int32_t njobs;
+  int32_t total_blocks;
+};
 struct F32Batch {
   F32Job job[kMaxApplyJobs];
   int32_t njobs;
@@ -175,6 +242,10 @@ struct JacobiBatch {
 // Each returns the HIP error of its launch (hipSuccess when launched).
 hipError_t launch_syrk_ema(const SyrkBatch& b, bool right, bool f64_state, int vec, hipStream_t s);
 hipError_t launch_f32_nt(const F32Batch& b, int vec, hipStream_t s);
+hipError_t launch_split_pad(const SplitPadBatch& b, hipStream_t s);
+hipError_t launch_absmax(const AbsMaxBatch& b, hipStream_t s);
+hipError_t launch_fill_zero(uint32_t* p, int32_t n, hipStream_t s);
+hipError_t launch_x3_apply(const X3ApplyBatch& b, hipStream_t s);
 
 hipError_t launch_root_stats(const RootBatch& b, hipStream_t s);
 hipError_t launch_root_bound(RootState* state, const double* partial, int64_t partial_stride, double* sched,

@@ -145,7 +145,10 @@ def test_apply_validation(lib):
     assert call([apply_p(4, 8, U=P2 + 4)]) == 8
     arr = (B.ApplyProblem * 1)(apply_p(4, 8))
     need = lib.precondition_apply_workspace(ctypes.addressof(arr), 1)
-    assert need == 256
+    # split copies (4 bytes per element) of XR (8 x 32), G (4 x 32), XL (4 x 32)
+    # and W^T (8 x 32), rows padded to 32 columns; W^T in float32 (8 x 4) and
+    # the 4 operands' largest magnitudes: arrays 256-byte aligned
+    assert need == 4 * (8 * 32 + 4 * 32 + 4 * 32 + 8 * 32) + 256 + 256
     assert call([apply_p(4, 8)], ws=None, ws_bytes=0) == 5
 
 

@@ -201,6 +201,26 @@ def test_apply_matches_oracle(torch_dev):
         assert err <= 1e-5, (sh, err)
 
 
+def test_apply_any_input_scale(torch_dev):
+    """Gradients from 1e-30 to 1e30 and roots from 1e-6 to 1e6 (far outside
+    fp16's range either way) keep float32-level accuracy: every operand is
+    scaled by a power of two before its fp16 split."""
+    torch, dev = torch_dev
+    rng = np.random.default_rng(9)
+    m, n = 160, 96
+    XL0 = rng.standard_normal((m, m)).astype(np.float32)
+    XL0 = (XL0 + XL0.T) / 2  # the roots are symmetric
+    XR0 = rng.standard_normal((n, n)).astype(np.float32)
+    XR0 = (XR0 + XR0.T) / 2
+    G0 = rng.standard_normal((m, n)).astype(np.float32)
+    for gs, xs in ((1e-30, 1.0), (1e30, 1e-6), (1e-8, 1e6), (3e-3, 7e2)):
+        XL, XR, G = (XL0 * np.float32(xs)), (XR0 / np.float32(xs)), G0 * np.float32(gs)
+        ref = oracle.precondition_apply(XL.astype(np.float64), G.astype(np.float64), XR.astype(np.float64), 1.0)
+        (U,) = B.precondition_apply([to_dev(torch, dev, XL)], [to_dev(torch, dev, G)], [to_dev(torch, dev, XR)])
+        err = oracle.relative_frobenius(U.cpu().numpy().astype(np.float64), ref)
+        assert np.isfinite(U.cpu().numpy()).all() and err <= 1e-5, (gs, xs, err)
+
+
 # ----------------------------------------------------------- end to end: toy
 def run_pipeline(torch, dev, grads_per_step, beta, eps, method="auto", state_dtype=None):
     """Drive the three entry points over steps; yield per-step device results."""
