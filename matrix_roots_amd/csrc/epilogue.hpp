@@ -97,7 +97,8 @@ __device__ __forceinline__ void split8(const float (&v)[8], v8h& hi, v8h& lo) {
 }
 
 // A whole tile of a GEMM whose waves form a grid WN wide, each wave owning
-// RB x 2 blocks of 32 x 32 (rows wm * 32 RB .., columns wn * 64 ..; RB even):
+// RB x CB blocks of 32 x 32 (rows wm * 32 RB .., columns wn * 32 CB ..; RB
+// and CB even), stored by 64 x 64 slabs:
 //   out[r][c] = alpha acc + beta cin[r][c] (+ gamma on the diagonal)
 // (cin optional: cin_hi == NULL) stored in split form at out (row stride
 // ldo) and, transposed, at t (row stride ldt: t[c][r] = out[r][c]); cin has
@@ -109,22 +110,25 @@ __device__ __forceinline__ void split8(const float (&v)[8], v8h& hi, v8h& lo) {
 // upper one (16-byte stores away from the diagonal, 2-byte stores on the
 // chunks it crosses).  The caller has passed a block barrier since the LDS
 // was last used for operands; `lds` holds kSlabFloats floats per wave.
-template <int RB, int WN, typename E>
-__device__ __forceinline__ void wide_store_tile(const v16f (&acc)[RB][2], float* lds, int m0, int n0,
+template <int RB, int WN, typename E, int CB = 2>
+__device__ __forceinline__ void wide_store_tile(const v16f (&acc)[RB][CB], float* lds, int m0, int n0,
                                                 _Float16* out_hi, _Float16* out_lo, int64_t ldo, _Float16* t_hi,
                                                 _Float16* t_lo, int64_t ldt, const _Float16* cin_hi,
                                                 const _Float16* cin_lo, E alpha, E beta, E gamma = E(0),
                                                 bool diag = false) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  static_assert(RB % 2 == 0, "64-row slabs");
+  static_assert(RB % 2 == 0 && CB % 2 == 0, "64 x 64 slabs");
   float* slab = lds + wave * kSlabFloats;
-#pragma unroll
-  for (int rb = 0; rb < RB; rb += 2) {
-    slab_put(slab, 0, acc[rb][0], acc[rb][1], lane);
-    slab_put(slab, 1, acc[rb + 1][0], acc[rb + 1][1], lane);
+  // one 64 x 64 slab per call, block indices known at compile time (a
+  // runtime index into acc would put the accumulators in scratch memory)
+  auto one_slab = [&](auto sl_c) __attribute__((always_inline)) {
+    constexpr int sl = decltype(sl_c)::value;
+    constexpr int rb = 2 * (sl / (CB / 2)), cb = 2 * (sl % (CB / 2));
+    slab_put(slab, 0, acc[rb][cb], acc[rb][cb + 1], lane);
+    slab_put(slab, 1, acc[rb + 1][cb], acc[rb + 1][cb + 1], lane);
     slab_fence();
-    const int r0 = m0 + wm * 32 * RB + rb * 32, c0 = n0 + wn * 64;
+    const int r0 = m0 + wm * 32 * RB + rb * 32, c0 = n0 + wn * 32 * CB + cb * 32;
     slab_rows(slab, lane, [&](int r, int c, float (&v)[8]) {
       const int gr = r0 + r, gc = c0 + c;
       if (diag && gr > gc + 7) return false;  // wholly below the diagonal
@@ -176,7 +180,8 @@ __device__ __forceinline__ void wide_store_tile(const v16f (&acc)[RB][2], float*
       }
     });
     slab_fence();
-  }
+  };
+  static_for<RB * CB / 4>(one_slab);
 }
 
 }  // namespace mr

@@ -505,34 +505,60 @@ __device__ __forceinline__ void x3_nt_tile_auto(SplitRef A, int64_t lda, SplitRe
 // Preconditions (checked by the caller): K a multiple of 32, lda and ldb
 // multiples of 8, 16-byte aligned arrays, every |B| < 32.  Rows beyond M or N
 // are read from row M - 1 or N - 1: they only feed outputs never stored.
-struct X3W {
-  static constexpr int BM = 256, BN = 256, WM = 2, WN = 4, THREADS = 64 * WM * WN;
+template <int BK_, int NST_, int WN_>
+struct X3WCfg {
+  static constexpr int BM = 256, BN = 256, WM = 2, WN = WN_, THREADS = 64 * WM * WN;
   static constexpr int RB = BM / WM / 32, CB = BN / WN / 32;
-  static constexpr int BK = 32, UPR = BK / 8;
+  static constexpr int BK = BK_, NST = NST_, UPR = BK / 8;
   static constexpr int AU = BM * UPR;  // 16-byte units per array and stage (BM == BN)
   static constexpr int STAGE_BYTES = 4 * AU * 16;
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int LDS_BYTES = NST * STAGE_BYTES;
   static constexpr int CPA = AU / THREADS;  // copies per lane and array
-  static_assert(BM == BN && CB == 2 && CPA * THREADS == AU, "square tile, two column blocks per wave");
+  static constexpr int LPC = 4 * CPA;       // copies per lane and chunk
+  static_assert(BM == BN && CB % 2 == 0 && RB % 2 == 0 && CPA * THREADS == AU, "square tile, 64 x 64 wave slabs");
+  static_assert(BK % 16 == 0 && 32 % BK == 0 && NST >= 2 && LDS_BYTES <= 160 * 1024, "chunk depth and stages");
 };
+#ifndef MR_X3W_BK
+#define MR_X3W_BK 32
+#endif
+#ifndef MR_X3W_NST
+#define MR_X3W_NST 2
+#endif
+#ifndef MR_X3W_WN
+#define MR_X3W_WN 4
+#endif
+using X3W = X3WCfg<MR_X3W_BK, MR_X3W_NST, MR_X3W_WN>;
 
 __device__ __forceinline__ void x3w_issue(SplitRef A, int64_t lda, SplitRef B, int64_t ldb, int M, int N, int m0,
                                           int n0, int k0, unsigned char* stage, int wave, int lane) {
+  // Copy j of a lane covers row lrow + j * THREADS / UPR of the tile, in the
+  // same k-group for every j (the slot map repeats every 16 rows).  Element
+  // offsets are 32-bit (a split array of a Gram holds d^2 < 2^31 elements);
+  // rows past the last are clamped to it through the offset.
+  static_assert((X3W::THREADS / 16) % X3W::UPR == 0, "one k-group per lane");
+  const int lu = wave * 64 + lane;
+  const int lrow = lu / X3W::UPR;
+  const int kg = dl_slot(lrow, lu % X3W::UPR, X3W::UPR);  // the map is its own inverse
 #pragma unroll
-  for (int arr = 0; arr < 4; ++arr) {
-    const bool isA = arr < 2;
-    const _Float16* P = arr == 0 ? A.hi : arr == 1 ? A.lo : arr == 2 ? B.hi : B.lo;
-    const int64_t ld = isA ? lda : ldb;
-    const int r0 = isA ? m0 : n0, rmax = (isA ? M : N) - 1;
+  for (int side = 0; side < 2; ++side) {
+    const uint32_t ld = (uint32_t)(side == 0 ? lda : ldb);
+    const int r0 = side == 0 ? m0 : n0, rmax = (side == 0 ? M : N) - 1;
+    uint32_t off0 = (uint32_t)(r0 + lrow) * ld + (uint32_t)(kg * 8);
+    uint32_t offmax = (uint32_t)rmax * ld + (uint32_t)(kg * 8);
+    // opaque per call: keeps the compiler from hoisting one 64-bit address
+    // per copy out of the main loop (registers it does not have to spare)
+    asm volatile("" : "+v"(off0), "+v"(offmax));
 #pragma unroll
-    for (int j = 0; j < X3W::CPA; ++j) {
-      const int base_u = (j * (X3W::THREADS / 64) + wave) * 64;
-      const int u = base_u + lane;
-      const int row = u / X3W::UPR;
-      const int kg = dl_slot(row, u % X3W::UPR, X3W::UPR);  // the map is its own inverse
-      const _Float16* src = P + (int64_t)min(r0 + row, rmax) * ld + k0 + kg * 8;
-      __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)(stage + (arr * X3W::AU + base_u) * 16),
-                                       16, 0, 0);
+    for (int half = 0; half < 2; ++half) {
+      const int arr = side * 2 + half;
+      const _Float16* P = (arr == 0 ? A.hi : arr == 1 ? A.lo : arr == 2 ? B.hi : B.lo) + k0;
+#pragma unroll
+      for (int j = 0; j < X3W::CPA; ++j) {
+        const int base_u = (j * (X3W::THREADS / 64) + wave) * 64;
+        const uint32_t off = min(off0 + (uint32_t)(j * (X3W::THREADS / X3W::UPR)) * ld, offmax);
+        __builtin_amdgcn_global_load_lds((global_void_ptr)(P + off),
+                                         (lds_void_ptr)(stage + (arr * X3W::AU + base_u) * 16), 16, 0, 0);
+      }
     }
   }
 }
@@ -576,7 +602,8 @@ __device__ __forceinline__ void x3w_chunk(const unsigned char* __restrict__ st, 
 __device__ __forceinline__ void x3w_nt_tile(SplitRef A, int64_t lda, SplitRef B, int64_t ldb, int M, int N, int K,
                                             int m0, int n0, unsigned char* __restrict__ lds,
                                             v16f (&acc)[X3W::RB][X3W::CB]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar LDS offsets
   const int wm = wave / X3W::WN, wn = wave % X3W::WN;
 #pragma unroll
   for (int rb = 0; rb < X3W::RB; ++rb)
@@ -585,18 +612,26 @@ __device__ __forceinline__ void x3w_nt_tile(SplitRef A, int64_t lda, SplitRef B,
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.f;
   const int nch = K / X3W::BK;
-  if (nch > 0) x3w_issue(A, lda, B, ldb, M, N, m0, n0, 0, lds, wave, lane);
-  for (int c = 0; c < nch; c += 2) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (c + s < nch) {
-        wait_vmcnt<0>();  // this wave's copies of chunk c + s have landed
+  for (int p = 0; p < X3W::NST - 1; ++p)
+    if (p < nch) x3w_issue(A, lda, B, ldb, M, N, m0, n0, p * X3W::BK, lds + p * X3W::STAGE_BYTES, wave, lane);
+  for (int c = 0; c < nch; c += X3W::NST) {
+#pragma unroll
+    for (int s = 0; s < X3W::NST; ++s) {
+      const int cc = c + s;
+      if (cc < nch) {
+        // this wave's copies of chunk cc have landed (NST - 2 later chunks may
+        // still be in flight; the counter retires loads in issue order)
+        if (cc + X3W::NST - 2 < nch)
+          wait_vmcnt<(X3W::NST - 2) * X3W::LPC>();
+        else
+          wait_vmcnt<0>();
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();  // ... and every wave's; stage s ^ 1 is free
+        __builtin_amdgcn_s_barrier();  // ... and every wave's; the stage of chunk cc - 1 is free
         asm volatile("" ::: "memory");
-        if (c + s + 1 < nch)
-          x3w_issue(A, lda, B, ldb, M, N, m0, n0, (c + s + 1) * X3W::BK, lds + (s ^ 1) * X3W::STAGE_BYTES, wave,
-                    lane);
+        if (cc + X3W::NST - 1 < nch)
+          x3w_issue(A, lda, B, ldb, M, N, m0, n0, (cc + X3W::NST - 1) * X3W::BK,
+                    lds + ((s + X3W::NST - 1) % X3W::NST) * X3W::STAGE_BYTES, wave, lane);
         x3w_chunk(lds + s * X3W::STAGE_BYTES, acc, lane, wm, wn);
       }
     }
@@ -614,14 +649,13 @@ template <typename F>
 __device__ __forceinline__ void x3w_for_each(const v16f (&acc)[X3W::RB][X3W::CB], F&& f) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / X3W::WN, wn = wave % X3W::WN;
+  static_for<X3W::RB * X3W::CB>([&](auto i_c) __attribute__((always_inline)) {
+    constexpr int rb = decltype(i_c)::value / X3W::CB, cb = decltype(i_c)::value % X3W::CB;
 #pragma unroll
-  for (int rb = 0; rb < X3W::RB; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < X3W::CB; ++cb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        f(wm * (X3W::BM / X3W::WM) + rb * 32 + f32_row(lane, v), wn * (X3W::BN / X3W::WN) + cb * 32 + (lane & 31),
-          acc[rb][cb][v]);
+    for (int v = 0; v < 16; ++v)
+      f(wm * (X3W::BM / X3W::WM) + rb * 32 + f32_row(lane, v), wn * (X3W::BN / X3W::WN) + cb * 32 + (lane & 31),
+        acc[rb][cb][v]);
+  });
 }
 
 // Visit every accumulator element of the f32 core as (row, col) local to the

@@ -616,9 +616,9 @@ __global__ __launch_bounds__(X3W::THREADS, 1) void newton_x3w_kernel(const Newto
   // else element stores
   auto store = [&](const SplitBuf& C, double al, double be, double ga) __attribute__((always_inline)) {
     if (whole) {
-      wide_store_tile<X3W::RB, X3W::WN, double>(acc, reinterpret_cast<float*>(smem), m0, n0, C.hi, C.lo, d, C.hi, C.lo,
-                                                d, o.has_cin ? o.Cin.hi : nullptr, o.has_cin ? o.Cin.lo : nullptr, al,
-                                                be, ga, s.ti == s.tj);
+      wide_store_tile<X3W::RB, X3W::WN, double, X3W::CB>(
+          acc, reinterpret_cast<float*>(smem), m0, n0, C.hi, C.lo, d, C.hi, C.lo, d,
+          o.has_cin ? o.Cin.hi : nullptr, o.has_cin ? o.Cin.lo : nullptr, al, be, ga, s.ti == s.tj);
       return;
     }
     x3w_for_each(acc, [&](int rr, int cc, float v) {
