@@ -73,10 +73,12 @@ def newton_flops(d: int, K: int, j: int, x_low: bool = True, final_degree: int =
     return f64, low
 
 
-def cpu_baseline(workload: str):
+def cpu_baseline(workload: str, min_seconds: float = 10.0, max_seconds: float = 30.0):
     """The fp64 oracle (as it stands): one step from zero state (Gram EMA, two
-    eigendecomposition roots, apply) on one weight of each distinct shape
-    class of layer 0; the per-layer time is the shape-count-weighted sum."""
+    eigendecomposition roots, apply) per (step, weight) pair, step 1's weights
+    in order first (layer 0 first), until at least `min_seconds` of oracle
+    time; a weight whose shape already took longer than what is left of
+    `max_seconds` is skipped.  value = pairs timed / seconds."""
     import oracle
     from matrix_roots_amd import workloads as W
 
@@ -87,27 +89,30 @@ def cpu_baseline(workload: str):
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
     wl = W.WORKLOADS[workload]
-    layer = [i for i, (name, _, _) in enumerate(wl.shapes) if name.startswith("L0.")] or [0, 1]
-    classes = {}
-    for i in layer:
-        _, m, n = wl.shapes[i]
-        key = (min(m, n), max(m, n))  # m x n and n x m cost the same
-        classes.setdefault(key, []).append(i)
-    per_layer = 0.0
+    total = 0.0
+    cost = {}  # seconds per shape class (m x n and n x m cost the same)
     timed = []
-    for key, members in classes.items():
-        i = members[0]
-        _, m, n = wl.shapes[i]
-        G = W.gradient(workload, i, 1)
+    pairs = [(t, i) for t in range(1, wl.steps + 1) for i in range(len(wl.shapes))]
+    for q in range(100000):  # cycles over (step, weight) only for workloads of tiny weights
+        if total >= min_seconds:
+            break
+        t, i = pairs[q % len(pairs)]
+        name, m, n = wl.shapes[i]
+        key = (min(m, n), max(m, n))
+        if key in cost and total + cost[key] > max_seconds:
+            continue
+        G = W.gradient(workload, i, t)
         t0 = time.perf_counter()
         oracle.preconditioner_step(np.zeros((m, m)), np.zeros((n, n)), G, wl.beta, wl.eps)
         dt = time.perf_counter() - t0
-        per_layer += dt * len(members)
-        timed.append(f"{wl.shapes[i][0]} {m}x{n}: {dt:.2f}s x{len(members)}")
-    sample = ("one step from zero state of one weight per shape class of layer 0 (" + "; ".join(timed)
-              + f"), scaled to the layer's {len(layer)} weights; fp64 numpy/LAPACK")
-    return {"value": len(layer) / per_layer, "unit": "matrix updates/s", "cores": cores, "kind": "oracle",
-            "sample": sample, "seconds": sum(float(x.split(": ")[1].split("s")[0]) for x in timed)}
+        cost[key] = max(cost.get(key, 0.0), dt)
+        total += dt
+        timed.append(f"{name} {m}x{n} {dt:.2f}s")
+    shown = "; ".join(timed[:12]) + ("; ..." if len(timed) > 12 else "")
+    sample = (f"one step from zero state for each of the first {len(timed)} (step, weight) pairs, step 1's "
+              f"weights first ({shown}); fp64 numpy/LAPACK")
+    return {"value": len(timed) / total, "unit": "matrix updates/s", "cores": cores, "kind": "oracle",
+            "sample": sample, "seconds": round(total, 2)}
 
 
 def per_size_class(B, torch, grams, wl):
