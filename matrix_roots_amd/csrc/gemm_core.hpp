@@ -527,6 +527,9 @@ struct X3WCfg {
 #ifndef MR_X3W_WN
 #define MR_X3W_WN 4
 #endif
+#ifndef MR_X3W_PREFETCH  // 2: fragment reads one k-step ahead across chunks; 1: within a chunk; 0: none
+#define MR_X3W_PREFETCH 2
+#endif
 using X3W = X3WCfg<MR_X3W_BK, MR_X3W_NST, MR_X3W_WN>;
 
 __device__ __forceinline__ void x3w_issue(SplitRef A, int64_t lda, SplitRef B, int64_t ldb, int M, int N, int m0,
@@ -566,8 +569,61 @@ __device__ __forceinline__ void x3w_issue(SplitRef A, int64_t lda, SplitRef B, i
 __device__ __forceinline__ void x3w_chunk(const unsigned char* __restrict__ st, v16f (&acc)[X3W::RB][X3W::CB],
                                           int lane, int wm, int wn) {
   constexpr int AB = X3W::AU * 16;  // bytes per array
+  constexpr int KS = X3W::BK / 16;
+#if MR_X3W_PREFETCH
+  // every k-step's fragments are read before the first product, so the
+  // reads of later k-steps land while the earlier k-steps' products run
+  // (LDS returns in order: the first products wait for their own reads only)
+  v8h ah[KS][X3W::RB], al[KS][X3W::RB], bh[KS][X3W::CB], bl[KS][X3W::CB];
 #pragma unroll
-  for (int ks = 0; ks < X3W::BK / 16; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
+    const int kg = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int rb = 0; rb < X3W::RB; ++rb) {
+      const int r = wm * (X3W::BM / X3W::WM) + rb * 32 + (lane & 31);
+      const int o = (r * X3W::UPR + dl_slot(r, kg, X3W::UPR)) * 16;
+      ah[ks][rb] = *reinterpret_cast<const v8h*>(st + o);
+      al[ks][rb] = *reinterpret_cast<const v8h*>(st + AB + o);
+    }
+#pragma unroll
+    for (int cb = 0; cb < X3W::CB; ++cb) {
+      const int r = wn * (X3W::BN / X3W::WN) + cb * 32 + (lane & 31);
+      const int o = (r * X3W::UPR + dl_slot(r, kg, X3W::UPR)) * 16;
+      bh[ks][cb] = *reinterpret_cast<const v8h*>(st + 2 * AB + o);
+      bl[ks][cb] = *reinterpret_cast<const v8h*>(st + 3 * AB + o);
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int cb = 0; cb < X3W::CB; ++cb) {
+#pragma unroll
+      for (int rb = 0; rb < X3W::RB; ++rb) acc[rb][cb] = mfma_f16_32x32x16(al[ks][rb], bh[ks][cb], acc[rb][cb]);
+      const v8h bs = bh[ks][cb] * (_Float16)2048.0f;
+#pragma unroll
+      for (int rb = 0; rb < X3W::RB; ++rb) {
+        acc[rb][cb] = mfma_f16_32x32x16(ah[ks][rb], bl[ks][cb], acc[rb][cb]);
+        acc[rb][cb] = mfma_f16_32x32x16(ah[ks][rb], bs, acc[rb][cb]);
+      }
+    }
+  }
+  // instruction order: the first k-step's reads, then each later k-step's
+  // reads spread over the previous k-step's products
+  constexpr int NR = 2 * (X3W::RB + X3W::CB), NM = 3 * X3W::RB * X3W::CB;
+  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+  for (int ks = 1; ks < KS; ++ks) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NM / NR, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - (NM / NR) * NR, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+#else
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
     const int kg = ks * 2 + (lane >> 5);
     v8h ah[X3W::RB], al[X3W::RB], bh[X3W::CB], bl[X3W::CB];
 #pragma unroll
@@ -596,6 +652,59 @@ __device__ __forceinline__ void x3w_chunk(const unsigned char* __restrict__ st, 
       }
     }
   }
+#endif
+}
+
+// One k-step's operand fragments of a wave (hi and lo halves of its A rows
+// and B columns), the reads that fill them and the products that use them.
+struct X3WFrag {
+  v8h ah[X3W::RB], al[X3W::RB], bh[X3W::CB], bl[X3W::CB];
+};
+
+__device__ __forceinline__ void x3w_read(const unsigned char* __restrict__ st, int ks, X3WFrag& f, int lane, int wm,
+                                         int wn) {
+  constexpr int AB = X3W::AU * 16;  // bytes per array
+  const int kg = ks * 2 + (lane >> 5);
+#pragma unroll
+  for (int rb = 0; rb < X3W::RB; ++rb) {
+    const int r = wm * (X3W::BM / X3W::WM) + rb * 32 + (lane & 31);
+    const int o = (r * X3W::UPR + dl_slot(r, kg, X3W::UPR)) * 16;
+    f.ah[rb] = *reinterpret_cast<const v8h*>(st + o);
+    f.al[rb] = *reinterpret_cast<const v8h*>(st + AB + o);
+  }
+#pragma unroll
+  for (int cb = 0; cb < X3W::CB; ++cb) {
+    const int r = wn * (X3W::BN / X3W::WN) + cb * 32 + (lane & 31);
+    const int o = (r * X3W::UPR + dl_slot(r, kg, X3W::UPR)) * 16;
+    f.bh[cb] = *reinterpret_cast<const v8h*>(st + 2 * AB + o);
+    f.bl[cb] = *reinterpret_cast<const v8h*>(st + 3 * AB + o);
+  }
+}
+
+__device__ __forceinline__ void x3w_mfma(const X3WFrag& f, v16f (&acc)[X3W::RB][X3W::CB]) {
+#pragma unroll
+  for (int cb = 0; cb < X3W::CB; ++cb) {
+#pragma unroll
+    for (int rb = 0; rb < X3W::RB; ++rb) acc[rb][cb] = mfma_f16_32x32x16(f.al[rb], f.bh[cb], acc[rb][cb]);
+    const v8h bs = f.bh[cb] * (_Float16)2048.0f;
+#pragma unroll
+    for (int rb = 0; rb < X3W::RB; ++rb) {
+      acc[rb][cb] = mfma_f16_32x32x16(f.ah[rb], f.bl[cb], acc[rb][cb]);
+      acc[rb][cb] = mfma_f16_32x32x16(f.ah[rb], bs, acc[rb][cb]);
+    }
+  }
+}
+
+// Instruction order for a region holding one k-step's products and the next
+// k-step's fragment reads: the reads spread evenly over the products.
+__device__ __forceinline__ void x3w_sched_overlap() {
+  constexpr int NR = 2 * (X3W::RB + X3W::CB), NM = 3 * X3W::RB * X3W::CB;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, NM / NR, 0);  // products
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // one LDS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NM - (NM / NR) * NR, 0);
 }
 
 // Result in acc: float32 sums of the wave's 4 x 2 blocks (layout of x3w_for_each).
@@ -612,6 +721,47 @@ __device__ __forceinline__ void x3w_nt_tile(SplitRef A, int64_t lda, SplitRef B,
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.f;
   const int nch = K / X3W::BK;
+#if MR_X3W_PREFETCH == 2
+  // Fragment reads one k-step ahead, across chunk boundaries too: a k-step's
+  // products run while the next k-step's fragments are read, from the same
+  // stage or, after the barrier, from the next one.  The barrier sits
+  // between the two halves of a chunk's products: each wave has finished
+  // reading the stage before it (LDS count 0) and holds the next chunk's
+  // copies (vector-memory count 0).
+  static_assert(X3W::NST == 2 && X3W::BK == 32, "two stages of two k-steps");
+  X3WFrag f0, f1;
+  if (nch > 0) {
+    x3w_issue(A, lda, B, ldb, M, N, m0, n0, 0, lds, wave, lane);
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (nch > 1) x3w_issue(A, lda, B, ldb, M, N, m0, n0, X3W::BK, lds + X3W::STAGE_BYTES, wave, lane);
+    x3w_read(lds, 0, f0, lane, wm, wn);
+  }
+  for (int c = 0; c < nch; c += 2) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int cc = c + s;
+      if (cc < nch) {
+        unsigned char* st = lds + s * X3W::STAGE_BYTES;
+        x3w_read(st, 1, f1, lane, wm, wn);
+        x3w_mfma(f0, acc);
+        x3w_sched_overlap();
+        wait_lgkmcnt0();
+        wait_vmcnt<0>();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // stage s is free, chunk cc + 1 is in stage s ^ 1
+        asm volatile("" ::: "memory");
+        if (cc + 2 < nch) x3w_issue(A, lda, B, ldb, M, N, m0, n0, (cc + 2) * X3W::BK, st, wave, lane);
+        // (after the last chunk this reads a stale stage; those fragments are never used)
+        x3w_read(lds + (s ^ 1) * X3W::STAGE_BYTES, 0, f0, lane, wm, wn);
+        x3w_mfma(f1, acc);
+        x3w_sched_overlap();
+      }
+    }
+  }
+#else
 #pragma unroll
   for (int p = 0; p < X3W::NST - 1; ++p)
     if (p < nch) x3w_issue(A, lda, B, ldb, M, N, m0, n0, p * X3W::BK, lds + p * X3W::STAGE_BYTES, wave, lane);
@@ -636,6 +786,7 @@ __device__ __forceinline__ void x3w_nt_tile(SplitRef A, int64_t lda, SplitRef B,
       }
     }
   }
+#endif
   __syncthreads();  // no wave leaves (or reuses the LDS) while another may still read the last stage
 #pragma unroll
   for (int rb = 0; rb < X3W::RB; ++rb)

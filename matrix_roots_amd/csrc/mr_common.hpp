@@ -173,6 +173,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Wait until every LDS (and scalar memory) operation of this wave is done.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  // vmcnt [3:0] and [15:14] and expcnt [6:4] at their maxima, lgkmcnt [11:8] = 0
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+}
+
 // L2-friendly tile orders.  A launch keeps ~64 output tiles per XCD in
 // flight (32 CUs x 2 workgroups), and tiles advance through K at the same
 // pace, so what decides the operand traffic is how many distinct operand
