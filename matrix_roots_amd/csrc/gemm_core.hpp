@@ -1044,6 +1044,9 @@ __device__ __forceinline__ void f64_tile(const TA* __restrict__ A, int64_t lda, 
 // M - 1 or N - 1: they only feed outputs that are never stored.  Symmetric
 // outputs only: in a diagonal tile (m0 == n0) the blocks wholly below the
 // diagonal are left at zero (f64_block_mode).
+#ifndef MR_F64_PREFETCH  // 1: fragment reads one half-chunk ahead, across chunks
+#define MR_F64_PREFETCH 1
+#endif
 struct F64DL {
   static constexpr int BK = F64Tile::BK, UPR = BK / 2;
   static constexpr int AU = F64Tile::BM * UPR;  // 16-byte units per operand and stage
@@ -1056,17 +1059,30 @@ struct F64DL {
 __device__ __forceinline__ void f64dl_issue(const double* __restrict__ A, int64_t lda, const double* __restrict__ B,
                                             int64_t ldb, int M, int N, int m0, int n0, int k0, unsigned char* stage,
                                             int wave, int lane) {
+  // Copy j of a lane covers row lrow + j * THREADS / UPR of the tile, in the
+  // same k-group for every j; 32-bit element offsets from a scalar base (a
+  // Gram slot holds d^2 < 2^31 elements), rows past the last clamped to it,
+  // recomputed per call rather than held in registers across the main loop.
+  static_assert((F64Tile::THREADS / 16) % F64DL::UPR == 0, "one k-group per lane");
+  const int lu = wave * 64 + lane;
+  const int lrow = lu / F64DL::UPR;
+  const int kg = dl_slot(lrow, lu % F64DL::UPR, F64DL::UPR);  // the map is its own inverse
 #pragma unroll
-  for (int j = 0; j < 2 * F64DL::CPO; ++j) {
-    const bool isA = j < F64DL::CPO;
-    const int base_u = ((isA ? j : j - F64DL::CPO) * (F64Tile::THREADS / 64) + wave) * 64;
-    const int u = base_u + lane;
-    const int row = u / F64DL::UPR;
-    const int kg = dl_slot(row, u % F64DL::UPR, F64DL::UPR);  // the map is its own inverse
-    const double* src = isA ? A + (int64_t)min(m0 + row, M - 1) * lda + k0 + kg * 2
-                            : B + (int64_t)min(n0 + row, N - 1) * ldb + k0 + kg * 2;
-    __builtin_amdgcn_global_load_lds((global_void_ptr)src,
-                                     (lds_void_ptr)(stage + ((isA ? 0 : F64DL::AU) + base_u) * 16), 16, 0, 0);
+  for (int side = 0; side < 2; ++side) {
+    const uint32_t ld = (uint32_t)(side == 0 ? lda : ldb);
+    const int r0 = side == 0 ? m0 : n0, rmax = (side == 0 ? M : N) - 1;
+    uint32_t off0 = (uint32_t)(r0 + lrow) * ld + (uint32_t)(kg * 2);
+    uint32_t offmax = (uint32_t)rmax * ld + (uint32_t)(kg * 2);
+    asm volatile("" : "+v"(off0), "+v"(offmax));
+    const double* P = (side == 0 ? A : B) + k0;
+#pragma unroll
+    for (int j = 0; j < F64DL::CPO; ++j) {
+      const int base_u = (j * (F64Tile::THREADS / 64) + wave) * 64;
+      const uint32_t off = min(off0 + (uint32_t)(j * (F64Tile::THREADS / F64DL::UPR)) * ld, offmax);
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(P + off),
+                                       (lds_void_ptr)(stage + ((side == 0 ? 0 : F64DL::AU) + base_u) * 16), 16, 0,
+                                       0);
+    }
   }
 }
 
@@ -1094,6 +1110,27 @@ __device__ __forceinline__ void f64_mfma_blocks(const v2d (&a)[4], const v2d (&b
         if (rb <= cb || full) acc[rb][cb] = mfma_f64_16x16x4(a[rb][i], b[cb][i], acc[rb][cb]);
 }
 
+struct F64Frag {
+  v2d a[4], b[4];
+};
+
+__device__ __forceinline__ void f64dl_read(const unsigned char* __restrict__ st, int h, F64Frag& f, int lane, int wm,
+                                           int wn) {
+  const unsigned char* As = st;
+  const unsigned char* Bs = st + F64DL::AU * 16;
+  const int kg = (lane >> 4) * 2 + h;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int r = wm * 64 + rb * 16 + (lane & 15);
+    f.a[rb] = *reinterpret_cast<const v2d*>(As + (r * F64DL::UPR + dl_slot(r, kg, F64DL::UPR)) * 16);
+  }
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int r = wn * 64 + cb * 16 + (lane & 15);
+    f.b[cb] = *reinterpret_cast<const v2d*>(Bs + (r * F64DL::UPR + dl_slot(r, kg, F64DL::UPR)) * 16);
+  }
+}
+
 __device__ __forceinline__ void f64dl_chunk(const unsigned char* __restrict__ st, v4d (&acc)[4][4], int lane, int wm,
                                             int wn, int mode) {
   const unsigned char* As = st;
@@ -1119,7 +1156,8 @@ __device__ __forceinline__ void f64dl_chunk(const unsigned char* __restrict__ st
 __device__ __forceinline__ void f64dl_nt_tile(const double* __restrict__ A, int64_t lda, const double* __restrict__ B,
                                               int64_t ldb, int M, int N, int K, int m0, int n0,
                                               unsigned char* __restrict__ lds, v4d (&acc)[4][4]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar LDS offsets
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
@@ -1129,6 +1167,43 @@ __device__ __forceinline__ void f64dl_nt_tile(const double* __restrict__ A, int6
       for (int v = 0; v < 4; ++v) acc[rb][cb][v] = 0.0;
   const int nch = K / F64DL::BK;
   const int mode = f64_block_mode(m0 == n0, wm, wn);
+#if MR_F64_PREFETCH
+  // Fragment reads one half-chunk ahead, across chunk boundaries too: the
+  // reads of the next half are issued before this half's products (the same
+  // scheme as the wide split-fp16 core).
+  F64Frag f0, f1;
+  if (nch > 0) {
+    f64dl_issue(A, lda, B, ldb, M, N, m0, n0, 0, lds, wave, lane);
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (nch > 1) f64dl_issue(A, lda, B, ldb, M, N, m0, n0, F64DL::BK, lds + F64DL::STAGE_BYTES, wave, lane);
+    f64dl_read(lds, 0, f0, lane, wm, wn);
+  }
+  for (int c = 0; c < nch; c += 2) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int cc = c + s;
+      if (cc < nch) {
+        unsigned char* st = lds + s * F64DL::STAGE_BYTES;
+        f64dl_read(st, 1, f1, lane, wm, wn);
+        if (mode != kF64None) f64_mfma_blocks(f0.a, f0.b, acc, mode == kF64All);
+        wait_lgkmcnt0();
+        wait_vmcnt<0>();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // stage s is free, chunk cc + 1 is in stage s ^ 1
+        asm volatile("" ::: "memory");
+        if (cc + 2 < nch) f64dl_issue(A, lda, B, ldb, M, N, m0, n0, (cc + 2) * F64DL::BK, st, wave, lane);
+        // (after the last chunk this reads a stale stage; those fragments are never used)
+        f64dl_read(lds + (s ^ 1) * F64DL::STAGE_BYTES, 0, f0, lane, wm, wn);
+        if (mode != kF64None) f64_mfma_blocks(f1.a, f1.b, acc, mode == kF64All);
+      }
+    }
+  }
+  __syncthreads();  // no wave leaves (or reuses the LDS) while another may still read the last stage
+  return;
+#endif
   if (nch > 0) f64dl_issue(A, lda, B, ldb, M, N, m0, n0, 0, lds, wave, lane);
   for (int c = 0; c < nch; c += 2) {
 #pragma unroll
