@@ -179,6 +179,10 @@ struct H16DLShape {
   static_assert(UPR == 4 || UPR == 8, "swizzle period");
 };
 
+#ifndef MR_H16_PREFETCH  // 1: fragment reads one k-step ahead, across chunks
+#define MR_H16_PREFETCH 1
+#endif
+
 template <class S>
 __device__ __forceinline__ void h16dl_issue(const _Float16* __restrict__ A, int64_t lda, const _Float16* __restrict__ B,
                                             int64_t ldb, int M, int N, int m0, int n0, int k0, unsigned char* stage,
@@ -223,13 +227,60 @@ __device__ __forceinline__ void h16dl_chunk(const unsigned char* __restrict__ st
   }
 }
 
+// One k-step's fragments of a wave, the reads that fill them, the products
+// that use them, and the instruction order for a region that holds one
+// k-step's products and the next k-step's reads (reads spread evenly).
+template <class S>
+struct H16Frag {
+  v8h a[S::RB], b[S::CB];
+};
+
+template <class S>
+__device__ __forceinline__ void h16dl_read(const unsigned char* __restrict__ st, int ks, H16Frag<S>& f, int wm,
+                                           int wn, int lane) {
+  const unsigned char* As = st;
+  const unsigned char* Bs = st + S::AU * 16;
+  const int kg = ks * 2 + (lane >> 5);
+#pragma unroll
+  for (int rb = 0; rb < S::RB; ++rb) {
+    const int r = wm * (S::BM / S::WM) + rb * 32 + (lane & 31);
+    f.a[rb] = *reinterpret_cast<const v8h*>(As + (r * S::UPR + dl_slot(r, kg, S::UPR)) * 16);
+  }
+#pragma unroll
+  for (int cb = 0; cb < S::CB; ++cb) {
+    const int r = wn * (S::BN / S::WN) + cb * 32 + (lane & 31);
+    f.b[cb] = *reinterpret_cast<const v8h*>(Bs + (r * S::UPR + dl_slot(r, kg, S::UPR)) * 16);
+  }
+}
+
+template <class S>
+__device__ __forceinline__ void h16dl_mfma(const H16Frag<S>& f, v16f (&acc)[S::RB][S::CB]) {
+#pragma unroll
+  for (int rb = 0; rb < S::RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < S::CB; ++cb) acc[rb][cb] = mfma_f16_32x32x16(f.a[rb], f.b[cb], acc[rb][cb]);
+}
+
+template <class S>
+__device__ __forceinline__ void h16dl_sched_overlap() {
+  constexpr int NR = S::RB + S::CB, NM = S::RB * S::CB;
+  constexpr int PER = NM / NR > 0 ? NM / NR : 1;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // products
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one LDS read
+  }
+  if (NM > PER * NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - PER * NR, 0);
+}
+
 // acc = A[m0:m0+BM, :K] * B[n0:n0+BN, :K]^T in the accumulator layout of
 // h16g_for_each for the H16Shape of the same BM, BN, WM, WN.
 template <class S>
 __device__ __forceinline__ void h16dl_nt_tile(const _Float16* __restrict__ A, int64_t lda,
                                               const _Float16* __restrict__ B, int64_t ldb, int M, int N, int K, int m0,
                                               int n0, unsigned char* __restrict__ lds, v16f (&acc)[S::RB][S::CB]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar LDS offsets
   const int wm = wave / S::WN, wn = wave % S::WN;
 #pragma unroll
   for (int rb = 0; rb < S::RB; ++rb)
@@ -238,6 +289,51 @@ __device__ __forceinline__ void h16dl_nt_tile(const _Float16* __restrict__ A, in
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.f;
   const int nch = K / S::BK;
+#if MR_H16_PREFETCH
+  // Fragment reads one k-step ahead, across chunk boundaries too (the scheme
+  // of the wide split-fp16 Newton core): the barrier sits before the last
+  // k-step's products, once every wave has finished reading the stage (LDS
+  // count 0) and holds the next chunk's copies (vector-memory count 0).
+  constexpr int KS = S::BK / 16;
+  static_assert(KS % 2 == 0, "an even number of k-steps per chunk");
+  H16Frag<S> f[2];
+  if (nch > 0) {
+    h16dl_issue<S>(A, lda, B, ldb, M, N, m0, n0, 0, lds, wave, lane);
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (nch > 1) h16dl_issue<S>(A, lda, B, ldb, M, N, m0, n0, S::BK, lds + S::STAGE_BYTES, wave, lane);
+    h16dl_read<S>(lds, 0, f[0], wm, wn, lane);
+  }
+  for (int c = 0; c < nch; c += 2) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int cc = c + s;
+      if (cc < nch) {
+        unsigned char* st = lds + s * S::STAGE_BYTES;
+#pragma unroll
+        for (int ks = 0; ks + 1 < KS; ++ks) {
+          h16dl_read<S>(st, ks + 1, f[(ks + 1) & 1], wm, wn, lane);
+          h16dl_mfma<S>(f[ks & 1], acc);
+          h16dl_sched_overlap<S>();
+        }
+        wait_lgkmcnt0();
+        wait_vmcnt<0>();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // stage s is free, chunk cc + 1 is in stage s ^ 1
+        asm volatile("" ::: "memory");
+        if (cc + 2 < nch) h16dl_issue<S>(A, lda, B, ldb, M, N, m0, n0, (cc + 2) * S::BK, st, wave, lane);
+        // (after the last chunk this reads a stale stage; those fragments are never used)
+        h16dl_read<S>(lds + (s ^ 1) * S::STAGE_BYTES, 0, f[0], wm, wn, lane);
+        h16dl_mfma<S>(f[(KS - 1) & 1], acc);
+        h16dl_sched_overlap<S>();
+      }
+    }
+  }
+  __syncthreads();  // no wave leaves while another may still read the last stage
+  return;
+#endif
   if (nch > 0) h16dl_issue<S>(A, lda, B, ldb, M, N, m0, n0, 0, lds, wave, lane);
   for (int c = 0; c < nch; c += 2) {
 #pragma unroll
