@@ -697,14 +697,18 @@ __device__ __forceinline__ void x3w_mfma(const X3WFrag& f, v16f (&acc)[X3W::RB][
 
 // Instruction order for a region holding one k-step's products and the next
 // k-step's fragment reads: the reads spread evenly over the products.
+#ifndef MR_X3W_SCHED  // products per LDS read in the interleave (0: spread evenly; 1 or more: that many, rest after)
+#define MR_X3W_SCHED 0
+#endif
 __device__ __forceinline__ void x3w_sched_overlap() {
   constexpr int NR = 2 * (X3W::RB + X3W::CB), NM = 3 * X3W::RB * X3W::CB;
+  constexpr int PER = MR_X3W_SCHED > 0 ? MR_X3W_SCHED : NM / NR;
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, NM / NR, 0);  // products
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // one LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // products
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one LDS read
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, NM - (NM / NR) * NR, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, NM - PER * NR, 0);
 }
 
 // Result in acc: float32 sums of the wave's 4 x 2 blocks (layout of x3w_for_each).
