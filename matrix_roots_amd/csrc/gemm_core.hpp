@@ -436,9 +436,59 @@ __device__ __forceinline__ void x3dl_chunk(const unsigned char* __restrict__ st,
   }
 }
 
+struct X3DLFrag {
+  v8h ah[2], al[2], bh[2], bl[2];
+};
+
+__device__ __forceinline__ void x3dl_read(const unsigned char* __restrict__ st, int ks, X3DLFrag& f, int lane, int wm,
+                                          int wn) {
+  constexpr int AB = X3DL::AU * 16;  // bytes per array
+  const int kg = ks * 2 + (lane >> 5);
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int r = wm * 64 + rb * 32 + (lane & 31);
+    const int o = (r * X3DL::UPR + dl_slot(r, kg, X3DL::UPR)) * 16;
+    f.ah[rb] = *reinterpret_cast<const v8h*>(st + o);
+    f.al[rb] = *reinterpret_cast<const v8h*>(st + AB + o);
+  }
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int r = wn * 64 + cb * 32 + (lane & 31);
+    const int o = (r * X3DL::UPR + dl_slot(r, kg, X3DL::UPR)) * 16;
+    f.bh[cb] = *reinterpret_cast<const v8h*>(st + 2 * AB + o);
+    f.bl[cb] = *reinterpret_cast<const v8h*>(st + 3 * AB + o);
+  }
+}
+
+__device__ __forceinline__ void x3dl_mfma(const X3DLFrag& f, v16f (&acc)[2][2], v16f (&acc2)[2][2]) {
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      acc[rb][cb] = mfma_f16_32x32x16(f.ah[rb], f.bh[cb], acc[rb][cb]);
+      acc2[rb][cb] = mfma_f16_32x32x16(f.ah[rb], f.bl[cb], acc2[rb][cb]);
+      acc2[rb][cb] = mfma_f16_32x32x16(f.al[rb], f.bh[cb], acc2[rb][cb]);
+    }
+}
+
+// 8 reads spread over 12 products (the scheme of x3w_sched_overlap)
+__device__ __forceinline__ void x3dl_sched_overlap() {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
+
+#ifndef MR_X3DL_PREFETCH  // 1: fragment reads one k-step ahead, across chunks
+#define MR_X3DL_PREFETCH 1
+#endif
+
 __device__ __forceinline__ void x3dl_nt_tile(SplitRef A, int64_t lda, SplitRef B, int64_t ldb, int M, int N, int K,
                                              int m0, int n0, unsigned char* __restrict__ lds, v16f (&acc)[2][2]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar LDS offsets
   const int wm = wave >> 1, wn = wave & 1;
   v16f acc2[2][2];
 #pragma unroll
@@ -451,6 +501,43 @@ __device__ __forceinline__ void x3dl_nt_tile(SplitRef A, int64_t lda, SplitRef B
         acc2[rb][cb][v] = 0.f;
       }
   const int nch = K / X3DL::BK;
+#if MR_X3DL_PREFETCH
+  // fragment reads one k-step ahead, across chunk boundaries too (the scheme
+  // of x3w_nt_tile)
+  static_assert(X3DL::BK == 32, "two k-steps per chunk");
+  X3DLFrag f0, f1;
+  if (nch > 0) {
+    x3dl_issue(A, lda, B, ldb, M, N, m0, n0, 0, lds, wave, lane);
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (nch > 1) x3dl_issue(A, lda, B, ldb, M, N, m0, n0, X3DL::BK, lds + X3DL::STAGE_BYTES, wave, lane);
+    x3dl_read(lds, 0, f0, lane, wm, wn);
+  }
+  for (int c = 0; c < nch; c += 2) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int cc = c + s;
+      if (cc < nch) {
+        unsigned char* st = lds + s * X3DL::STAGE_BYTES;
+        x3dl_read(st, 1, f1, lane, wm, wn);
+        x3dl_mfma(f0, acc, acc2);
+        x3dl_sched_overlap();
+        wait_lgkmcnt0();
+        wait_vmcnt<0>();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // stage s is free, chunk cc + 1 is in stage s ^ 1
+        asm volatile("" ::: "memory");
+        if (cc + 2 < nch) x3dl_issue(A, lda, B, ldb, M, N, m0, n0, (cc + 2) * X3DL::BK, st, wave, lane);
+        // (after the last chunk this reads a stale stage; those fragments are never used)
+        x3dl_read(lds + (s ^ 1) * X3DL::STAGE_BYTES, 0, f0, lane, wm, wn);
+        x3dl_mfma(f1, acc, acc2);
+        x3dl_sched_overlap();
+      }
+    }
+  }
+#else
   if (nch > 0) x3dl_issue(A, lda, B, ldb, M, N, m0, n0, 0, lds, wave, lane);
   for (int c = 0; c < nch; c += 2) {
 #pragma unroll
@@ -467,6 +554,7 @@ __device__ __forceinline__ void x3dl_nt_tile(SplitRef A, int64_t lda, SplitRef B
       }
     }
   }
+#endif
   __syncthreads();  // no wave leaves (or reuses the LDS) while another may still read the last stage
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
