@@ -131,6 +131,18 @@ def test_newton_wide_tiles_ragged(torch_dev):
         _check_roots(torch, dev, mats, 1e-6, normalize, "newton", torch.float32, ROOT_TOL)
 
 
+def test_newton_read_ahead_chunk_counts(torch_dev):
+    """Chunk counts at the edges of the main loops that read fragments one
+    k-step ahead: one chunk (d = 16 in the float64 core, d = 32 in the
+    256 x 256 split-fp16 core), two (d = 32 in float64) and an odd count
+    (d = 48: three float64 chunks)."""
+    torch, dev = torch_dev
+    rng = W.rng_for(90, 7)
+    mats = [spd(d, rng) for d in (16, 32, 48)]
+    for method in ("newton", "newton_f64"):
+        _check_roots(torch, dev, mats, 1e-6, "trace", method, torch.float32, ROOT_TOL)
+
+
 def test_newton_small_d_matches_jacobi(torch_dev):
     """Forced Newton on Jacobi-sized inputs agrees with the oracle too."""
     torch, dev = torch_dev
