@@ -85,14 +85,49 @@ def summarise(fetch_dir, write_dir, kernel, copy_mib):
     return res
 
 
+def mfma_busy(run_dir: str, kernels):
+    """Matrix-core busy fraction per kernel: SQ_VALU_MFMA_BUSY_CYCLES per
+    GRBM_GUI_ACTIVE cycle, summed over the kernel's dispatches, divided by the
+    same ratio of the register-only MFMA loop of the matching precision
+    (peak_kernel<0> float32, <1> float64, <2> fp16), which keeps every matrix
+    core busy: the counters' own scale (per SIMD or per CU) cancels."""
+    busy = read_counter(run_dir, "SQ_VALU_MFMA_BUSY_CYCLES")
+    active = read_counter(run_dir, "GRBM_GUI_ACTIVE")
+
+    def ratio(needle):
+        names, b = pick(busy, needle)
+        _, a = pick(active, needle)
+        return sum(b) / sum(a), len(b)
+
+    out = {}
+    for name, ref in kernels:
+        r, n = ratio(name)
+        p, _ = ratio(ref)
+        out[name] = {"dispatches": n, "busy_per_active": r, "peak_busy_per_active": p, "fraction": r / p}
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
-    ap.add_argument("--kernel", required=True)
-    ap.add_argument("--copy-mib", type=float, required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--kernel")
+    ap.add_argument("--copy-mib", type=float)
     ap.add_argument("--family", default="quarter", choices=sorted(KERNEL_SOURCES))
+    ap.add_argument("--mfma", help="run dir of a SQ_VALU_MFMA_BUSY_CYCLES + GRBM_GUI_ACTIVE pass")
+    ap.add_argument("--pair", action="append", default=[],
+                    help="KERNEL=PEAK_KERNEL for --mfma (e.g. newton_f64_kernel=peak_kernel<1>)")
     args = ap.parse_args(argv)
+    if args.mfma:
+        res = mfma_busy(args.mfma, [tuple(x.split("=", 1)) for x in args.pair])
+        for name, r in res.items():
+            print(f"{name}: dispatches {r['dispatches']}; MFMA busy per active cycle {r['busy_per_active']:.2f} "
+                  f"(register-only loop {r['peak_busy_per_active']:.2f}) -> {100 * r['fraction']:.1f}% busy")
+        print(f"source_family: {args.family}")
+        print(f"source_sha256: {sources_sha256(args.family)}")
+        return 0
+    if not (args.fetch and args.write and args.kernel and args.copy_mib):
+        ap.error("--fetch, --write, --kernel and --copy-mib are required without --mfma")
     res = summarise(args.fetch, args.write, args.kernel, args.copy_mib)
     f, w = res["FETCH_SIZE"], res["WRITE_SIZE"]
     print(f"kernel: {', '.join(f['kernels'])}")
