@@ -197,9 +197,13 @@ size_t gram_ema_update_workspace(const mr_gram_problem* problems, int32_t count,
  *    the cost of the float32 phase; for inputs near the float32 limit).
  *  - MR_AUTO: Jacobi for d <= 128, Newton otherwise.
  * a_dtype: MR_F32 or MR_F64.  eps > 0 and finite.  info_dev: device array of
- * `count` records (may be NULL).  MR_NORM_NONE with any Newton problem
- * synchronises hip_stream once (the iteration count depends on the bounds
- * computed on the device); MR_NORM_TRACE never synchronises.
+ * `count` records (may be NULL).  Never synchronises: the host launches a
+ * fixed number of Newton steps and each matrix runs its own schedule under
+ * it.  With MR_NORM_TRACE that number covers every matrix (c <= 1.01 (1 +
+ * eps)); with MR_NORM_NONE it covers floors eps/c down to 1e-16, and a
+ * matrix whose floor lies lower stops at that count with
+ * MR_INFO_NOT_CONVERGED set (float64 rounding of M0 is already of the
+ * floor's size there).
  * Workspace: at least inv_quarter_root_batched_workspace(...) bytes, 256-byte
  * aligned; its contents on entry are ignored.
  */

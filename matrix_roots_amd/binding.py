@@ -233,6 +233,17 @@ def _stream(stream) -> int:
     return int(stream.cuda_stream)
 
 
+def _in_use_on(stream, *tensors):
+    """Tell torch's caching allocator that these tensors are used by work on
+    `stream` (when it is not the current stream), so that their memory is not
+    handed out again before that work ends."""
+    if stream is None:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def _workspace(nbytes: int, device):
     import torch
 
@@ -328,7 +339,8 @@ def _root_call(entry, size_entry, code, As, eps, normalize, Xs, workspace, strea
     if layouts.pop():
         dt |= MR_PACKED
     dev = As[0].device
-    if Xs is None:
+    own_x = Xs is None
+    if own_x:
         Xs = [torch.empty(d, d, dtype=torch.float32, device=dev) for d, _, _ in syms]
     probs = (RootProblem * count)()
     for i, (A, X) in enumerate(zip(As, Xs)):
@@ -340,6 +352,7 @@ def _root_call(entry, size_entry, code, As, eps, normalize, Xs, workspace, strea
         if info_out.numel() < ROOT_INFO_BYTES * count:
             raise ValueError("info_out too small")
         info = info_out
+    _in_use_on(stream, buf, info, *(Xs if own_x else ()))
     _check(entry(ctypes.addressof(probs), count, dt, float(eps), _NORMS[normalize], code, _ptr(info), _ptr(buf),
                  buf.numel(), _stream(stream)))
     if not return_info:
@@ -374,7 +387,8 @@ def polar_cans_batched(Gs: Sequence, precision: str = "f16", Os: Optional[Sequen
     if count == 0:
         return [], None
     dev = Gs[0].device
-    if Os is None:
+    own_o = Os is None
+    if own_o:
         Os = [torch.empty_like(G) for G in Gs]
     probs = (PolarProblem * count)()
     for i, (G, O) in enumerate(zip(Gs, Os)):
@@ -387,6 +401,7 @@ def polar_cans_batched(Gs: Sequence, precision: str = "f16", Os: Optional[Sequen
         if info_out.numel() < ROOT_INFO_BYTES * count:
             raise ValueError("info_out too small")
         info = info_out
+    _in_use_on(stream, buf, info, *(Os if own_o else ()))
     _check(lib.polar_cans_batched(ctypes.addressof(probs), count, code, _ptr(info), _ptr(buf), buf.numel(),
                                   _stream(stream)))
     if not return_info:
@@ -428,9 +443,8 @@ def hyperball_update_batched(Ws: Sequence, Us: Sequence, lr: float, return_norms
         probs[i] = HyperballProblem(W.shape[0], W.shape[1], _ptr(W), _ld(W), _ptr(U), _ld(U))
     need = lib.hyperball_update_batched_workspace(ctypes.addressof(probs), count)
     ws = _workspace(need, dev)
-    if ws is not None and stream is not None:
-        ws.record_stream(stream)
     norms = torch.empty(count, 3, dtype=torch.float64, device=dev) if return_norms else None
+    _in_use_on(stream, ws, norms)
     _check(lib.hyperball_update_batched(ctypes.addressof(probs), count, float(lr), _ptr(norms), _ptr(ws), need,
                                         _stream(stream)))
     return norms
@@ -459,7 +473,8 @@ def precondition_apply(XLs: Sequence, Gs: Sequence, XRs: Sequence, alpha: float 
     if count == 0:
         return []
     dev = Gs[0].device
-    if Us is None:
+    own_u = Us is None
+    if own_u:
         Us = [torch.empty_like(G) for G in Gs]
     probs = (ApplyProblem * count)()
     for i in range(count):
@@ -468,8 +483,7 @@ def precondition_apply(XLs: Sequence, Gs: Sequence, XRs: Sequence, alpha: float 
                                 _ptr(U), _ld(U))
     need = lib.precondition_apply_workspace(ctypes.addressof(probs), count)
     ws = _workspace(need, dev)
-    if ws is not None and stream is not None:
-        ws.record_stream(stream)
+    _in_use_on(stream, ws, *(Us if own_u else ()))
     _check(lib.precondition_apply(ctypes.addressof(probs), count, float(alpha), _ptr(ws), need, _stream(stream)))
     return Us
 

@@ -31,11 +31,6 @@ using namespace mr;
 #ifndef MR_NEWTON_WIDE
 #define MR_NEWTON_WIDE 1
 #endif
-// precondition_apply on the fp16 matrix cores with split operands (else the
-// float32 matrix cores).
-#ifndef MR_APPLY_X3
-#define MR_APPLY_X3 1
-#endif
 
 namespace {
 
@@ -100,12 +95,12 @@ int tiles(int64_t d, int t) { return (int)((d + t - 1) / t); }
 
 // ------------------------------------------------------------ tracing
 enum TraceClass {
-  kTrSyrk, kTrApply, kTrJacobi, kTrStats, kTrBound, kTrInit, kTrNewton64, kTrNewton32, kTrConvert,
+  kTrSyrk, kTrJacobi, kTrStats, kTrBound, kTrInit, kTrNewton64, kTrNewton32, kTrConvert,
   kTrFinalize, kTrInfo, kTrNewtonX3, kTrCansBound, kTrCansInit, kTrCansP, kTrCansYZ, kTrCansFinal, kTrCansInfo,
   kTrPolarStats, kTrPolarBound, kTrPolarInit, kTrPolarA, kTrPolarX, kTrPolarFinal, kTrPolarInfo,
   kTrMomentum, kTrHyperReduce, kTrHyperUpdate, kTrApplyX3, kTrApplySplit, kTrCount
 };
-const char* const kTraceNames[kTrCount] = {"syrk_ema", "apply_f32", "jacobi", "root_stats", "root_bound",
+const char* const kTraceNames[kTrCount] = {"syrk_ema", "jacobi", "root_stats", "root_bound",
                                            "root_init", "newton_f64", "newton_f32", "newton_convert",
                                            "root_finalize", "root_info", "newton_x3", "cans_bound",
                                            "cans_init", "cans_p", "cans_yz", "cans_finalize", "cans_info",
@@ -497,17 +492,15 @@ size_t precondition_apply_workspace(const mr_apply_problem* p, int32_t count) {
   size_t tot = 0;
   for (int i = 0; i < count; ++i) {
     if (p[i].m <= 0 || p[i].n <= 0) continue;
-    if (MR_APPLY_X3)
-      tot = apply_split_layout(p[i], tot).end;
-    else
-      tot += align256((size_t)p[i].m * (size_t)p[i].n * 4);
+    tot = apply_split_layout(p[i], tot).end;
   }
-  if (MR_APPLY_X3) tot += align256((size_t)count * 4 * sizeof(uint32_t));
+  tot += align256((size_t)count * 4 * sizeof(uint32_t));
   return tot;
 }
 
-// U = alpha XL G XR with split operands: maxima and split copies of XR, G and
-// XL; W^T = XR G^T (float32); its maxima and split copy; U = alpha XL W.
+// U = alpha XL G XR with split operands: maxima and split copies of XR^T, G
+// and XL; W^T = XR^T G^T = (G XR)^T (float32); its maxima and split copy;
+// U = alpha XL W.
 static mr_status apply_split(const mr_apply_problem* p, int32_t count, float alpha, void* ws,
                              const std::vector<int>& order, hipStream_t s) {
   std::vector<ApplySplitLayout> lay(count);
@@ -522,21 +515,23 @@ static mr_status apply_split(const mr_apply_problem* p, int32_t count, float alp
   auto amax = [&](int i, int which) { return amax_all + 4 * i + which; };
   struct Src {
     const float* ptr;
-    int64_t ld, rows, cols;
+    int64_t ld, rows, cols;  // of the source (transposed copies: dst rows = source columns)
     _Float16* dst;
     int64_t ldd;
     uint32_t* amax;
+    int trans;
   };
-  // the float32 sources of one split pass (phase 0: XR, G, XL; phase 1: W^T)
+  // the float32 sources of one split pass (phase 0: XR (copied transposed),
+  // G, XL; phase 1: W^T)
   auto sources = [&](int i, int phase, std::vector<Src>& out) {
     const mr_apply_problem& q = p[i];
     const ApplySplitLayout& L = lay[i];
     if (phase == 0) {
-      out.push_back({q.XR, q.ldxr, q.n, q.n, half(L.xr), L.n32, amax(i, 0)});
-      out.push_back({q.G, q.ldg, q.m, q.n, half(L.g), L.n32, amax(i, 1)});
-      out.push_back({q.XL, q.ldxl, q.m, q.m, half(L.xl), L.m32, amax(i, 2)});
+      out.push_back({q.XR, q.ldxr, q.n, q.n, half(L.xr), L.n32, amax(i, 0), 1});
+      out.push_back({q.G, q.ldg, q.m, q.n, half(L.g), L.n32, amax(i, 1), 0});
+      out.push_back({q.XL, q.ldxl, q.m, q.m, half(L.xl), L.m32, amax(i, 2), 0});
     } else {
-      out.push_back({reinterpret_cast<float*>(base + L.wt32), q.m, q.n, q.m, half(L.wt), L.m32, amax(i, 3)});
+      out.push_back({reinterpret_cast<float*>(base + L.wt32), q.m, q.n, q.m, half(L.wt), L.m32, amax(i, 3), 0});
     }
   };
   mr_status st = MR_OK;
@@ -562,26 +557,40 @@ static mr_status apply_split(const mr_apply_problem* p, int32_t count, float alp
                            "apply maxima launch");
       if (r != MR_OK) return r;
     }
-    for (size_t k0 = 0; k0 < srcs.size(); k0 += kMaxSplitPadJobs) {
-      SplitPadBatch b;
-      memset(&b, 0, sizeof b);
-      for (size_t k = k0; k < srcs.size() && b.njobs < kMaxSplitPadJobs; ++k) {
-        const Src& x = srcs[k];
-        SplitPadJob& J = b.job[b.njobs++];
-        J.src = x.ptr;
-        J.dst = x.dst;
-        J.amax = x.amax;
-        J.lds = x.ld;
-        J.ldd = x.ldd;
-        J.rows = (int32_t)x.rows;
-        J.cols = (int32_t)x.cols;
-        J.block_begin = b.total_blocks;
-        J.vec4 = aligned(x.ptr, 16) && x.ld % 4 == 0 ? 1 : 0;
-        b.total_blocks += (int32_t)((x.rows * x.ldd + 2047) / 2048);
+    for (int trans = 0; trans < 2; ++trans) {
+      std::vector<const Src*> mine;
+      for (const Src& x : srcs)
+        if (x.trans == trans) mine.push_back(&x);
+      for (size_t k0 = 0; k0 < mine.size(); k0 += kMaxSplitPadJobs) {
+        SplitPadBatch b;
+        memset(&b, 0, sizeof b);
+        for (size_t k = k0; k < mine.size() && b.njobs < kMaxSplitPadJobs; ++k) {
+          const Src& x = *mine[k];
+          SplitPadJob& J = b.job[b.njobs++];
+          J.src = x.ptr;
+          J.dst = x.dst;
+          J.amax = x.amax;
+          J.lds = x.ld;
+          J.ldd = x.ldd;
+          J.trans = trans;
+          J.block_begin = b.total_blocks;
+          if (trans) {  // dst rows = source columns, valid dst columns = source rows
+            J.rows = (int32_t)x.cols;
+            J.cols = (int32_t)x.rows;
+            J.vec4 = 0;
+            b.total_blocks += tiles(x.cols, 64) * tiles(x.ldd, 64);
+          } else {
+            J.rows = (int32_t)x.rows;
+            J.cols = (int32_t)x.cols;
+            J.vec4 = aligned(x.ptr, 16) && x.ld % 4 == 0 ? 1 : 0;
+            b.total_blocks += (int32_t)((x.rows * x.ldd + 2047) / 2048);
+          }
+        }
+        mr_status r = traced(kTrApplySplit, b.total_blocks > 0, s,
+                             [&] { return trans ? launch_split_pad_t(b, s) : launch_split_pad(b, s); },
+                             "apply split launch");
+        if (r != MR_OK) return r;
       }
-      mr_status r = traced(kTrApplySplit, b.total_blocks > 0, s, [&] { return launch_split_pad(b, s); },
-                           "apply split launch");
-      if (r != MR_OK) return r;
     }
     return MR_OK;
   };
@@ -600,7 +609,7 @@ static mr_status apply_split(const mr_apply_problem* p, int32_t count, float alp
       const mr_apply_problem& q = p[i];
       const ApplySplitLayout& L = lay[i];
       X3ApplyJob& J = b.job[b.njobs];
-      if (stage == 0) {  // W^T = XR G^T : n x m, contraction n
+      if (stage == 0) {  // W^T = XR^T G^T : n x m, contraction n
         J.a = half(L.xr);
         J.b = half(L.g);
         J.c = reinterpret_cast<float*>(base + L.wt32);
@@ -650,64 +659,13 @@ mr_status precondition_apply(const mr_apply_problem* p, int32_t count, float alp
   if (!ws || ws_bytes < need || !aligned(ws, 256))
     return fail(MR_ERR_WORKSPACE, "workspace %p of %zu bytes; need %zu bytes, 256-byte aligned", ws, ws_bytes, need);
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  std::vector<float*> wt(count);
-  size_t off = 0;
-  for (int i = 0; i < count; ++i) {
-    wt[i] = reinterpret_cast<float*>(static_cast<char*>(ws) + off);
-    off += align256((size_t)p[i].m * (size_t)p[i].n * 4);
-  }
-  auto v4ok = [](const float* ptr, int64_t ld, int64_t K) { return aligned(ptr, 16) && ld % 4 == 0 && K % 4 == 0; };
   // largest weights first in each launch (their tiles start early, small ones fill the tail)
   std::vector<int> order(count);
   for (int i = 0; i < count; ++i) order[i] = i;
   std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
     return p[x].m * p[x].n * (p[x].m + p[x].n) > p[y].m * p[y].n * (p[y].m + p[y].n);
   });
-  if (MR_APPLY_X3) return apply_split(p, count, alpha, ws, order, s);
-  for (int stage = 0; stage < 2; ++stage) {
-    for (int vecpass = 0; vecpass < 2; ++vecpass) {
-      const int vec = vecpass == 0 ? 4 : 1;
-      F32Batch b;
-      memset(&b, 0, sizeof b);
-      auto flush = [&]() -> mr_status {
-        if (b.njobs == 0) return MR_OK;
-        mr_status r = traced(kTrApply, b.total_blocks > 0, s, [&] { return launch_f32_nt(b, vec, s); },
-                             "precondition_apply launch");
-        b.njobs = 0;
-        b.total_blocks = 0;
-        return r;
-      };
-      for (const int i : order) {
-        const mr_apply_problem& q = p[i];
-        F32Job J;
-        if (stage == 0) {  // W^T = XR * G^T : (n x m)
-          J.A = q.XR; J.lda = q.ldxr;
-          J.B = q.G; J.ldb = q.ldg;
-          J.C = wt[i]; J.ldc = q.m;
-          J.M = (int32_t)q.n; J.N = (int32_t)q.m; J.K = (int32_t)q.n;
-          J.alpha = 1.f;
-        } else {  // U = alpha * XL * W
-          J.A = q.XL; J.lda = q.ldxl;
-          J.B = wt[i]; J.ldb = q.m;
-          J.C = q.U; J.ldc = q.ldu;
-          J.M = (int32_t)q.m; J.N = (int32_t)q.n; J.K = (int32_t)q.m;
-          J.alpha = alpha;
-        }
-        const bool v4 = v4ok(J.A, J.lda, J.K) && v4ok(J.B, J.ldb, J.K);
-        if ((vec == 4) != v4) continue;
-        const int tm = tiles(J.M, 128), tn = tiles(J.N, 128);
-        J.tiles_n = tn;
-        J.nblocks = tm * tn;
-        J.pad = 0;
-        J.block_begin = b.total_blocks;
-        b.job[b.njobs++] = J;
-        b.total_blocks += round8(J.nblocks);
-        if (b.njobs == kMaxApplyJobs && (st = flush()) != MR_OK) return st;
-      }
-      if ((st = flush()) != MR_OK) return st;
-    }
-  }
-  return MR_OK;
+  return apply_split(p, count, alpha, ws, order, s);
 }
 
 // ================================================ inv_quarter_root_batched
@@ -859,36 +817,23 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
 
     if ((st = run_root_batches(0)) != MR_OK) return st;
 
-    // Iteration cap known on the host.  Trace mode: c <= 1.01 (1 + eps) up to
-    // rounding, so no matrix needs more steps than the schedule from the
-    // floor eps / (1.02 (1 + eps)).
+    // Iteration cap known on the host, so the call never waits for the
+    // device.  Trace mode: c <= 1.01 (1 + eps) up to rounding, so no matrix
+    // needs more steps than the schedule from the floor eps / (1.02 (1 + eps)).
+    // No rescale: the bound c is only known on the device; the cap is the
+    // schedule from the floor kNoneFloorCap, every matrix runs its own
+    // schedule under it (the launches past its last step exit at once), and
+    // one whose floor eps / c lies lower is flagged MR_INFO_NOT_CONVERGED.
     int k_cap, j_cap;
-    if (normalize == MR_NORM_TRACE) {
-      newton_scaled_schedule(eps / (1.02 * (1.0 + eps)), 1.0 / kBoundSafety, kNewtonTol, kSwitchM, kMaxNewtonIters,
-                             nullptr, &k_cap, &j_cap, x_low);
-    } else {
-      k_cap = kMaxNewtonIters;
-      j_cap = kMaxNewtonIters;
-    }
+    const double floor_cap = normalize == MR_NORM_TRACE ? eps / (1.02 * (1.0 + eps)) : kNoneFloorCap;
+    newton_scaled_schedule(floor_cap, 1.0 / kBoundSafety, kNewtonTol, kSwitchM, kMaxNewtonIters, nullptr, &k_cap,
+                           &j_cap, x_low);
     if ((st = traced(kTrBound, true, s, [&] {
            return launch_root_bound(state, partial, P.partial_stride, sched, 0, P.n_newton, normalize, eps, k_cap,
                                     all_f64 ? 1 : 0, x_low ? 1 : 0, s);
          }, "root bound launch")) != MR_OK)
       return st;
-    int k_max = k_cap, j_max = all_f64 ? k_cap : j_cap;
-    if (normalize != MR_NORM_TRACE) {
-      // The scale is unknown to the host: read the per-matrix schedules back.
-      std::vector<RootState> hs(P.n_newton);
-      hipError_t e = hipMemcpyAsync(hs.data(), state, sizeof(RootState) * P.n_newton, hipMemcpyDeviceToHost, s);
-      if (e == hipSuccess) e = hipStreamSynchronize(s);
-      if (e != hipSuccess) return hip_fail(e, "reading Newton schedules");
-      k_max = 0;
-      j_max = 0;
-      for (const auto& r : hs) {
-        k_max = std::max(k_max, r.K);
-        j_max = std::max(j_max, std::min(r.j, r.K));
-      }
-    }
+    const int k_max = k_cap, j_max = all_f64 ? k_cap : j_cap;
     if ((st = run_root_batches(1)) != MR_OK) return st;
 
     // Class groups: at most kMaxClasses per launch, split by vector width.

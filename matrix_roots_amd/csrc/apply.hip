@@ -1,47 +1,21 @@
-// Two-sided application of the quarter powers on the float32 matrix cores.
+// Two-sided application of the quarter powers on the fp16 matrix cores.
 //
 //   U = alpha * XL * G * XR
 //
 // (marin.community, "Sharding EMA-Gram eigensolves", section "Background":
 // the inverse quarter powers shape the update direction; the two-sided form
 // is Shampoo's, tilderesearch "Online KL Shampoo", section 1.)
-// Both products run as C = A * B^T on row-contiguous operands:
-//   W^T = XR * G^T   (n x m; A = XR rows, B = G rows, contraction n)
-//   U   = XL * W     (m x n; A = XL rows, B = W^T rows, contraction m)
-// using the symmetry of XR and XL.  This file holds the generic float32
-// job-batched kernel; the host runtime issues the two launches.
+// Both products run as C = A * B^T on row-contiguous split operands:
+//   W^T = XR^T * G^T  (n x m; A = rows of XR^T, B = G rows, contraction n)
+//   U   = XL * W      (m x n; A = XL rows, B = W^T rows, contraction m)
+// XR's split copy is written transposed, so no symmetry of XR is assumed
+// (the roots this library produces are symmetric to the last bit, and for
+// them the transposed copy is bitwise the plain one).  The host runtime
+// issues the launches.
 #include "gemm_core.hpp"
 #include "launch.hpp"
 
 namespace mr {
-
-template <int VEC>
-__global__ __launch_bounds__(256, 2) void f32_nt_kernel(const F32Batch batch) {
-  __shared__ float smem[F32Tile::LDS_FLOATS];
-
-  const int64_t b = blockIdx.x;
-  int jx = 0;
-  while (jx + 1 < batch.njobs && b >= batch.job[jx + 1].block_begin) ++jx;
-  const F32Job& J = batch.job[jx];
-  const int tile = (int)xcd_remap(b - J.block_begin, round8(J.nblocks));
-  if (tile >= J.nblocks) return;
-  int ti, tj;
-  full_tile_grouped(tile, (J.M + F32Tile::BM - 1) / F32Tile::BM, J.tiles_n, ti, tj);
-  const int m0 = ti * F32Tile::BM;
-  const int n0 = tj * F32Tile::BN;
-
-  v16f acc[2][2];
-  f32_nt_tile<VEC>(J.A, J.lda, J.B, J.ldb, J.M, J.N, J.K, m0, n0, smem, acc);
-
-  const float alpha = J.alpha;
-  float* C = J.C;
-  const int64_t ldc = J.ldc;
-  const int M = J.M, N = J.N;
-  f32_for_each(acc, [&](int r, int c, float v) {
-    const int gr = m0 + r, gc = n0 + c;
-    if (gr < M && gc < N) C[(int64_t)gr * ldc + gc] = alpha * v;
-  });
-}
 
 // ---------------------------------------------------------- split-fp16 apply
 // The same two products on the fp16 matrix cores with split operands
@@ -137,6 +111,50 @@ __global__ __launch_bounds__(256) void split_pad_kernel(const SplitPadBatch batc
   *reinterpret_cast<v8h*>(J.dst + total + e) = l;
 }
 
+// Transposed split copy: dst (rows x ldd) row r = src column r, for 64 x 64
+// dst tiles; the tile's src rows are read coalesced into LDS, then each lane
+// writes 8 consecutive dst elements of one row (16-byte hi and lo stores).
+// dst columns at or past cols (src rows that do not exist) are zero.
+__global__ __launch_bounds__(256) void split_pad_t_kernel(const SplitPadBatch batch) {
+  __shared__ float t[64][65];
+  const int64_t b = blockIdx.x;
+  int jx = 0;
+  while (jx + 1 < batch.njobs && b >= batch.job[jx + 1].block_begin) ++jx;
+  const SplitPadJob& J = batch.job[jx];
+  const int tiles_c = (int)((J.ldd + 63) / 64);
+  const int blk = (int)(b - J.block_begin);
+  const int r0 = (blk / tiles_c) * 64;  // dst rows = src columns
+  const int c0 = (blk % tiles_c) * 64;  // dst columns = src rows
+  const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int i = grp + 4 * e;  // src row c0 + i, src column r0 + lane
+    const int sr = c0 + i, sc = r0 + lane;
+    t[i][lane] = (sr < J.cols && sc < J.rows) ? J.src[(int64_t)sr * J.lds + sc] : 0.0f;
+  }
+  __syncthreads();
+  const float scale = ldexpf(1.0f, split_scale_exp(J.amax));
+  const int64_t total = (int64_t)J.rows * J.ldd;
+  const int b0 = (threadIdx.x & 7) * 8;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int a = (threadIdx.x >> 3) + 32 * h;
+    const int dr = r0 + a, dc = c0 + b0;
+    if (dr >= J.rows || dc >= J.ldd) continue;
+    v8h hi, lo;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      _Float16 x, y;
+      split_f32(t[b0 + k][a] * scale, x, y);
+      hi[k] = x;
+      lo[k] = y;
+    }
+    const int64_t e = (int64_t)dr * J.ldd + dc;
+    *reinterpret_cast<v8h*>(J.dst + e) = hi;
+    *reinterpret_cast<v8h*>(J.dst + total + e) = lo;
+  }
+}
+
 __global__ __launch_bounds__(256, 2) void x3_apply_kernel(const X3ApplyBatch batch) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[X3DL::LDS_BYTES];
   const int64_t b = blockIdx.x;
@@ -178,18 +196,15 @@ hipError_t launch_split_pad(const SplitPadBatch& b, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_x3_apply(const X3ApplyBatch& b, hipStream_t s) {
+hipError_t launch_split_pad_t(const SplitPadBatch& b, hipStream_t s) {
   if (b.total_blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(x3_apply_kernel, dim3(b.total_blocks), dim3(256), 0, s, b);
+  hipLaunchKernelGGL(split_pad_t_kernel, dim3(b.total_blocks), dim3(256), 0, s, b);
   return hipGetLastError();
 }
 
-hipError_t launch_f32_nt(const F32Batch& b, int vec, hipStream_t s) {
+hipError_t launch_x3_apply(const X3ApplyBatch& b, hipStream_t s) {
   if (b.total_blocks <= 0) return hipSuccess;
-  if (vec == 4)
-    hipLaunchKernelGGL(f32_nt_kernel<4>, dim3(b.total_blocks), dim3(256), 0, s, b);
-  else
-    hipLaunchKernelGGL(f32_nt_kernel<1>, dim3(b.total_blocks), dim3(256), 0, s, b);
+  hipLaunchKernelGGL(x3_apply_kernel, dim3(b.total_blocks), dim3(256), 0, s, b);
   return hipGetLastError();
 }
 

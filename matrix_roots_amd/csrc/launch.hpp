@@ -17,7 +17,6 @@ namespace mr {
 
 constexpr int kMaxJobs = 16;
 constexpr int kMaxSyrkJobs = 48;   // Gram EMA: one launch per side for up to 48 weights (2.3 KiB)
-constexpr int kMaxApplyJobs = 48;  // apply: one launch per stage for up to 48 weights (3.8 KiB)
 constexpr int kMaxRootJobs = 48;   // root statistics, init and finalize launches (3.1 KiB)
 constexpr int kMaxClasses = 8;
 constexpr int kJacobiMaxD = 128;
@@ -26,6 +25,9 @@ constexpr int kFinalRows = 8;        // rows of X per finalize workgroup
 constexpr double kSwitchM = 5e-4;    // float64 -> float32 once the eigenvalue floor reaches this
 constexpr double kNewtonTol = 1e-6;  // stop once 1 - m_K <= this (scalar recurrence)
 constexpr double kBoundSafety = 1.01;
+// Lowest eigenvalue floor eps / c the Newton launches cover without a rescale
+// (below it float64 rounding of M0 already reaches the floor's size).
+constexpr double kNoneFloorCap = 1e-16;
 
 // Workgroup ranges of jobs and size classes start on multiples of 8 (one per
 // XCD) and are padded to a multiple of 8.
@@ -74,21 +76,6 @@ struct SyrkBatch {
   int32_t pad;
 };
 
-// ------------------------------------------------- float32 NT GEMM (apply)
-struct F32Job {
-  const float* A;
-  const float* B;
-  float* C;
-  int64_t lda, ldb, ldc;
-  int32_t M, N, K;
-  int32_t tiles_n;
-  int32_t block_begin;  // multiple of 8
-  int32_t nblocks;      // tiles of this job (its range is round8(nblocks) long)
-  float alpha;
-  int32_t pad;
-};
-static_assert(sizeof(F32Job) * kMaxApplyJobs + 64 < 4096, "apply table fits the kernel arguments");
-
 // Split-fp16 apply: operands are split copies of 2^s times a float32 matrix,
 // s per matrix such that the largest magnitude lands in [2^14, 2^15) (so
 // neither half overflows fp16 or loses precision to its subnormals, whatever
@@ -119,17 +106,20 @@ struct X3ApplyBatch {
   int32_t njobs;
   int32_t total_blocks;
 };
-// One float32 matrix (rows x cols, row stride lds) times 2^s into split form
-// at dst (row stride ldd >= cols, a multiple of 8; columns cols .. ldd - 1
-// zero); s from the matrix's largest magnitude *amax.
+// One float32 matrix times 2^s into split form at dst (rows x ldd, ldd >= cols
+// a multiple of 8; columns cols .. ldd - 1 zero); s from the matrix's largest
+// magnitude *amax.  trans = 0: dst row r is src row r (src rows x cols, row
+// stride lds; 2048 elements per workgroup).  trans = 1: dst row r is src
+// column r (src cols x rows; 64 x 64 dst tiles per workgroup, through LDS).
 struct SplitPadJob {
   const float* src;
   _Float16* dst;
   const uint32_t* amax;
   int64_t lds, ldd;
   int32_t rows, cols;
-  int32_t block_begin;  // first workgroup of this job (2048 elements each)
-  int32_t vec4;         // src rows 16-byte aligned (float4 loads)
+  int32_t block_begin;  // first workgroup of this job
+  int16_t vec4;         // src rows 16-byte aligned (float4 loads; trans = 0)
+  int16_t trans;
 };
 // Largest magnitude of a float32 matrix into *amax (zeroed beforehand), a
 // workgroup per kAbsMaxRows-row band.
@@ -152,11 +142,6 @@ constexpr int kMaxSplitPadJobs = 64;
 static_assert(sizeof(SplitPadJob) * kMaxSplitPadJobs + 64 < 4096, "split table fits the kernel arguments");
 struct SplitPadBatch {
   SplitPadJob job[kMaxSplitPadJobs];
-  int32_t njobs;
-  int32_t total_blocks;
-};
-struct F32Batch {
-  F32Job job[kMaxApplyJobs];
   int32_t njobs;
   int32_t total_blocks;
 };
@@ -241,8 +226,8 @@ struct JacobiBatch {
 // ------------------------------------------------------------ launchers
 // Each returns the HIP error of its launch (hipSuccess when launched).
 hipError_t launch_syrk_ema(const SyrkBatch& b, bool right, bool f64_state, int vec, hipStream_t s);
-hipError_t launch_f32_nt(const F32Batch& b, int vec, hipStream_t s);
 hipError_t launch_split_pad(const SplitPadBatch& b, hipStream_t s);
+hipError_t launch_split_pad_t(const SplitPadBatch& b, hipStream_t s);
 hipError_t launch_absmax(const AbsMaxBatch& b, hipStream_t s);
 hipError_t launch_fill_zero(uint32_t* p, int32_t n, hipStream_t s);
 hipError_t launch_x3_apply(const X3ApplyBatch& b, hipStream_t s);

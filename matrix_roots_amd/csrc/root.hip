@@ -273,8 +273,17 @@ __global__ __launch_bounds__(64) void root_bound_kernel(RootState* state, const 
         flags |= MR_INFO_NOT_PD;
         c = 1.0;
       } else {
-        newton_scaled_schedule(fmin(eps / c, 1.0 / kBoundSafety), 1.0 / kBoundSafety, kNewtonTol, kSwitchM,
-                               k_cap, sched + (int64_t)slot * kMaxNewtonIters, &K, &j, finish != 0, &fin);
+        const double floor = fmin(eps / c, 1.0 / kBoundSafety);
+        newton_scaled_schedule(floor, 1.0 / kBoundSafety, kNewtonTol, kSwitchM, k_cap,
+                               sched + (int64_t)slot * kMaxNewtonIters, &K, &j, finish != 0, &fin);
+        if (K == k_cap) {
+          // The host launches k_cap steps at most: a matrix whose own schedule
+          // needs more is not iterated to convergence, and says so.
+          int K2 = 0, j2 = 0, fin2 = 1;
+          newton_scaled_schedule(floor, 1.0 / kBoundSafety, kNewtonTol, kSwitchM, k_cap + 1, nullptr, &K2, &j2,
+                                 finish != 0, &fin2);
+          if (K2 > k_cap) flags |= MR_INFO_NOT_CONVERGED;
+        }
         if (all_f64) j = K;
       }
     }

@@ -50,11 +50,13 @@ def sym_residual_rms(torch, A, X, eps, normalize="trace"):
     return float(torch.linalg.norm(R) / d ** 0.5)
 
 
-def run_and_check(torch, dev, workload, weights, steps, samples):
+def run_and_check(torch, dev, workload, weights, steps, samples, last_step_samples=()):
     """Run `steps` steps of `workload` restricted to `weights` (indices into the
     workload's weight list), all of them batched per call; compare the
-    `samples` (subset of weights) against the oracle at every step, and every
-    root through the properties above at the last step."""
+    `samples` (subset of weights) against the oracle at every step, the
+    `last_step_samples` at the last step only (the oracle runs their Gram EMA
+    alone before that step, then the whole step), and every root through the
+    properties above at the last step."""
     wl = W.WORKLOADS[workload]
     shapes = [wl.shapes[w][1:] for w in weights]
     nw = len(weights)
@@ -63,7 +65,8 @@ def run_and_check(torch, dev, workload, weights, steps, samples):
     Us = [torch.empty(m, n, dtype=torch.float32, device=dev) for m, n in shapes]
     ws = B.RootWorkspace()
     got = {w: [] for w in samples}
-    grads_host = {w: [] for w in samples}
+    grads_host = {w: [] for w in list(samples) + list(last_step_samples)}
+    last = {}
     worst = [0.0, 0.0, 0.0]
     for t in range(1, steps + 1):
         Gh = [W.gradient(workload, w, t) for w in weights]
@@ -77,7 +80,12 @@ def run_and_check(torch, dev, workload, weights, steps, samples):
             k = weights.index(w)
             got[w].append((Xs[k].cpu().numpy(), Xs[nw + k].cpu().numpy(), Us[k].cpu().numpy(),
                            Ls[k].cpu().numpy(), Rs[k].cpu().numpy()))
-            grads_host[w].append(Gh[k])
+        for w in grads_host:
+            grads_host[w].append(Gh[weights.index(w)])
+        if t == steps:
+            for w in last_step_samples:
+                k = weights.index(w)
+                last[w] = (Xs[k].cpu().numpy(), Xs[nw + k].cpu().numpy(), Us[k].cpu().numpy())
         if t == steps:
             for k, (A, X) in enumerate(zip(Ls + Rs, Xs)):
                 assert torch.equal(X, X.T) and bool(torch.isfinite(X).all()), k
@@ -96,6 +104,22 @@ def run_and_check(torch, dev, workload, weights, steps, samples):
             worst[0] = max(worst[0], e_root)
             worst[1] = max(worst[1], e_u)
             assert e_root <= ROOT_TOL and e_u <= UPDATE_TOL, (workload, w, t + 1, e_root, e_u)
+    for w in last_step_samples:
+        G = grads_host[w]
+        m, n = G[0].shape
+        rL, rR = np.zeros((m, m)), np.zeros((n, n))
+        for g in G[:-1]:
+            rL, rR = oracle.gram_ema_update(rL, rR, g, wl.beta)
+        _, _, rXL, rXR, rU, flags = oracle.preconditioner_step(rL, rR, G[-1], wl.beta, wl.eps, wl.normalize)
+        assert flags == 0
+        XL, XR, U = last[w]
+        e_root = max(oracle.relative_frobenius(XL, rXL), oracle.relative_frobenius(XR, rXR))
+        e_u = oracle.relative_frobenius(U, rU)
+        print(f"{workload} weight {w} ({m}x{n}) step {steps}: root err {e_root:.2e}, update err {e_u:.2e}",
+              flush=True)
+        worst[0] = max(worst[0], e_root)
+        worst[1] = max(worst[1], e_u)
+        assert e_root <= ROOT_TOL and e_u <= UPDATE_TOL, (workload, w, steps, e_root, e_u)
     print(f"{workload}: worst root err {worst[0]:.2e}, update err {worst[1]:.2e}, "
           f"residual rms {worst[2]:.2e}")
 
@@ -121,12 +145,15 @@ def test_moe_full(torch_dev):
 
 def test_w2048_layers_0_and_23(torch_dev):
     """Layers 0 and 23 of the width-2048 set (2048x2048, 2048x8192,
-    8192x2048), 3 steps; oracle on L0.q at every step."""
+    8192x2048), 3 steps; oracle on L0.q at every step, and on L0.up (its
+    8192 x 8192 right root, of rank-6144 Gram plus eps, and its 2048 x 8192
+    update direction) at step 3."""
     torch, dev = torch_dev
     wl = W.WORKLOADS["w2048"]
     names = [s[0] for s in wl.shapes]
     weights = [i for i, n in enumerate(names) if n.startswith("L0.") or n.startswith("L23.")]
-    run_and_check(torch, dev, "w2048", weights, wl.steps, [names.index("L0.q")])
+    run_and_check(torch, dev, "w2048", weights, wl.steps, [names.index("L0.q")],
+                  last_step_samples=[names.index("L0.up")])
 
 
 def test_w2048_one_8192_root_against_oracle(torch_dev):

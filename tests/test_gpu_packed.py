@@ -4,11 +4,15 @@ upper triangle the full path writes, and every root computed from a packed
 input equals the one computed from the full copy of the same matrix (the
 statistics sum the same values in the same order; the symmetric part of a
 packed matrix is its stored value, as (v + v)/2 is for the full one).  The
-full path itself is held to the oracle by the other GPU tests."""
+packed whole step is also held to the fp64 oracle directly (tilderesearch,
+"Online KL Shampoo", appendix F, counts a symmetric Kronecker factor as
+d(d+1)/2 stored elements)."""
 
 import numpy as np
 import pytest
 
+import oracle
+import parity
 from matrix_roots_amd import binding as B
 from matrix_roots_amd import workloads as W
 
@@ -75,9 +79,13 @@ def test_sqrt_root_from_packed_bitwise(torch_dev, precision):
 
 def test_packed_step_end_to_end(torch_dev):
     """Three steps of the whole preconditioner step on a small transformer-like
-    set with packed float64 state give bitwise the updates of full state."""
+    set with packed float64 state give bitwise the updates of full state, and
+    the packed run's states, roots and updates match the fp64 oracle run on
+    the same gradients (1e-12 on states, 1e-4 on roots, 1e-3 on updates)."""
     torch, dev = torch_dev
     shapes = [(256, 256), (256, 1024), (1024, 256), (200, 136)]
+    grads = [[W.gradient("w1024", k, t, shape=s) for k, s in enumerate(shapes)] for t in range(1, 4)]
+    refs = [list(oracle.run_sequence([grads[t][k] for t in range(3)], 0.95, 1e-6)) for k in range(len(shapes))]
     outs = []
     for packed in (False, True):
         if packed:
@@ -87,13 +95,23 @@ def test_packed_step_end_to_end(torch_dev):
             Ls = [torch.zeros(m, m, dtype=torch.float64, device=dev) for m, n in shapes]
             Rs = [torch.zeros(n, n, dtype=torch.float64, device=dev) for m, n in shapes]
         Us = []
+        nw = len(shapes)
         for t in range(1, 4):
-            Gs = [torch.from_numpy(W.gradient("w1024", k, t, shape=s)).to(dev) for k, s in enumerate(shapes)]
+            Gs = [torch.from_numpy(grads[t - 1][k]).to(dev) for k in range(nw)]
             B.gram_ema_update(Gs, Ls, Rs, 0.95)
             Xs, info = B.inv_quarter_root_batched(Ls + Rs, 1e-6)
             assert (info["flags"] == 0).all()
-            Us.append(B.precondition_apply(Xs[: len(shapes)], Gs, Xs[len(shapes):]))
-        torch.cuda.synchronize()
+            Us.append(B.precondition_apply(Xs[:nw], Gs, Xs[nw:]))
+            torch.cuda.synchronize()
+            if packed:
+                for k in range(nw):
+                    _, rL, rR, rXL, rXR, rU, flags = refs[k][t - 1]
+                    ctx = f"packed step {t} weight {shapes[k]}"
+                    parity.assert_state(B.unpack_upper(Ls[k]), rL, 1e-12, ctx + " L")
+                    parity.assert_state(B.unpack_upper(Rs[k]), rR, 1e-12, ctx + " R")
+                    parity.assert_root(Xs[k], rXL, ctx + " XL")
+                    parity.assert_root(Xs[nw + k], rXR, ctx + " XR")
+                    parity.assert_update(Us[-1][k], rU, ctx + " U")
         outs.append(Us)
     for Uf, Up in zip(*outs):
         for a, b in zip(Uf, Up):

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
+import parity
 from matrix_roots_amd import binding as B
 from matrix_roots_amd import workloads as W
 
@@ -211,6 +212,28 @@ def test_apply_matches_oracle(torch_dev):
     for U, ref, sh in zip(Us, refs, shapes):
         err = oracle.relative_frobenius(U.cpu().numpy(), ref)
         assert err <= 1e-5, (sh, err)
+
+
+def test_apply_asymmetric_operands(torch_dev):
+    """precondition_apply computes alpha XL G XR for any square XL and XR,
+    symmetric or not (the right product reads XR through a transposed split
+    copy): ragged shapes, several tiles, one 1 x 1 case."""
+    torch, dev = torch_dev
+    rng = np.random.default_rng(10)
+    shapes = [(64, 128), (200, 328), (130, 7), (1, 1), (257, 129), (96, 300)]
+    XLs, Gs, XRs, refs = [], [], [], []
+    for m, n in shapes:
+        XL = rng.standard_normal((m, m)).astype(np.float32)
+        XR = rng.standard_normal((n, n)).astype(np.float32)
+        G = rng.standard_normal((m, n)).astype(np.float32)
+        XLs.append(to_dev(torch, dev, XL))
+        XRs.append(to_dev(torch, dev, XR))
+        Gs.append(to_dev(torch, dev, G))
+        refs.append(oracle.precondition_apply(XL, G, XR, -0.75))
+    Us = B.precondition_apply(XLs, Gs, XRs, alpha=-0.75)
+    torch.cuda.synchronize()
+    for U, ref, sh in zip(Us, refs, shapes):
+        parity.assert_close(U, ref, 1e-5, f"asymmetric apply {sh}")
 
 
 def test_apply_any_input_scale(torch_dev):
