@@ -214,6 +214,28 @@ mr_status inv_quarter_root_batched(const mr_root_problem* problems, int32_t coun
 size_t inv_quarter_root_batched_workspace(const mr_root_problem* problems, int32_t count,
                                           mr_dtype a_dtype, int32_t method);
 
+/*
+ * inv_quarter_root_batched_noalloc -- inv_quarter_root_batched without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same problems, arguments, results and info records; the
+ * workspace is a file-scope device array of MR_NOALLOC_SCRATCH_BYTES bytes
+ * that each GPU the library runs on holds until the process ends.  The call
+ * allocates nothing.  Its device address is looked up on the first call on
+ * each device (the current device; hip_stream must belong to it).  A batch
+ * whose workspace (inv_quarter_root_batched_workspace) exceeds that size is
+ * rejected with MR_ERR_WORKSPACE before anything is enqueued: 32 MiB holds
+ * for instance 16 Newton roots of 224 x 224, 256 MR_JACOBI roots of
+ * 64 x 64, or one Newton root of 896 x 896.  The array's contents on entry
+ * are ignored (nothing in it must start at zero), but every call on one GPU
+ * uses the same array: calls that overlap on one GPU (other streams, other
+ * host threads) race and give wrong results; order them on one stream.
+ */
+#define MR_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+mr_status inv_quarter_root_batched_noalloc(const mr_root_problem* problems, int32_t count,
+                                           mr_dtype a_dtype, double eps, int32_t normalize,
+                                           int32_t method, mr_root_info* info_dev, void* hip_stream);
+
 /* inv_sqrt_root_batched: precision of the products */
 #define MR_CANS_F16 0   /* fp16 products with float32 accumulation (the OKLS page's) */
 #define MR_CANS_SPLIT 1 /* split-fp16 products: float32-accurate, three times the

@@ -35,6 +35,7 @@ EXPORTED = (
     "gram_ema_update_workspace",
     "inv_quarter_root_batched",
     "inv_quarter_root_batched_workspace",
+    "inv_quarter_root_batched_noalloc",
     "inv_sqrt_root_batched",
     "inv_sqrt_root_batched_workspace",
     "mr_cans_ceilings",
@@ -124,6 +125,8 @@ def library() -> ctypes.CDLL:
     lib.inv_quarter_root_batched.restype = i32
     lib.inv_quarter_root_batched_workspace.argtypes = [vp, i32, i32, i32]
     lib.inv_quarter_root_batched_workspace.restype = sz
+    lib.inv_quarter_root_batched_noalloc.argtypes = [vp, i32, i32, f64, i32, i32, vp, vp]
+    lib.inv_quarter_root_batched_noalloc.restype = i32
     lib.inv_sqrt_root_batched.argtypes = [vp, i32, i32, f64, i32, i32, vp, vp, sz, vp]
     lib.inv_sqrt_root_batched.restype = i32
     lib.inv_sqrt_root_batched_workspace.argtypes = [vp, i32, i32, i32]
@@ -359,6 +362,43 @@ def _root_call(entry, size_entry, code, As, eps, normalize, Xs, workspace, strea
         return Xs, None
     torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
     return Xs, decode_info(info, count)
+
+
+NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
+
+
+def inv_quarter_root_batched_noalloc(As: Sequence, eps: float, Xs: Sequence, info_out, normalize: str = "trace",
+                                     method: str = "auto", stream=None):
+    """inv_quarter_root_batched with the library's own scratch array as the
+    workspace: the caller passes the outputs Xs (float32 (d, d) device
+    tensors) and info_out (device uint8 tensor of ROOT_INFO_BYTES*len(As)
+    bytes, or None), and neither the library nor this wrapper allocates
+    device memory.  Nothing is synchronised; decode info_out with
+    decode_info() after the stream."""
+    lib = library()
+    count = len(As)
+    if count == 0:
+        return Xs
+    dts = {str(a.dtype) for a in As}
+    if len(dts) != 1:
+        raise ValueError("all A must share one dtype")
+    dt = MR_F64 if dts.pop() == "torch.float64" else MR_F32
+    syms = [_sym(a) for a in As]
+    layouts = {p for _, _, p in syms}
+    if len(layouts) != 1:
+        raise ValueError("A must be all full (2-D) or all packed (1-D)")
+    if layouts.pop():
+        dt |= MR_PACKED
+    if len(Xs) != count:
+        raise ValueError("one output per input")
+    if info_out is not None and info_out.numel() < ROOT_INFO_BYTES * count:
+        raise ValueError("info_out too small")
+    probs = (RootProblem * count)()
+    for i, (A, X) in enumerate(zip(As, Xs)):
+        probs[i] = RootProblem(syms[i][0], _ptr(A), syms[i][1], _ptr(X), _ld(X))
+    _check(lib.inv_quarter_root_batched_noalloc(ctypes.addressof(probs), count, dt, float(eps), _NORMS[normalize],
+                                                _METHODS[method], _ptr(info_out), _stream(stream)))
+    return Xs
 
 
 def inv_sqrt_root_batched(As: Sequence, eps: float = 0.0, normalize: str = "none", precision: str = "f16",

@@ -941,6 +941,60 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
 
 }  // extern "C"
 
+// ================================== inv_quarter_root_batched_noalloc
+// The same call with the workspace in a file-scope device array instead of a
+// caller buffer, for callers that cannot allocate device memory.  In host
+// code `scratch` names a host-side stand-in, so its device address is looked
+// up once per device (hipGetSymbolAddress, with that device current) and only
+// that address is ever passed on.
+static __device__ __align__(256) unsigned char scratch[MR_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_addr;  // device ordinal -> address of its copy of `scratch`
+
+mr_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch_addr.find(dev);
+  if (it != g_scratch_addr.end()) {
+    *out = it->second;
+    return MR_OK;
+  }
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  if (!ptr || !aligned(ptr, 256)) return fail(MR_ERR_HIP, "scratch array at %p is not 256-byte aligned", ptr);
+  g_scratch_addr.emplace(dev, ptr);
+  *out = ptr;
+  return MR_OK;
+}
+}  // namespace
+
+extern "C" {
+
+mr_status inv_quarter_root_batched_noalloc(const mr_root_problem* p, int32_t count, mr_dtype dt, double eps,
+                                           int32_t normalize, int32_t method, mr_root_info* info_dev,
+                                           void* hip_stream) {
+  mr_status st = validate_root(p, count, dt, eps, normalize, method);
+  if (st != MR_OK) return st;
+  if (count == 0) return MR_OK;
+  const size_t need = plan_root(p, count, method).total;
+  if (need > (size_t)MR_NOALLOC_SCRATCH_BYTES)
+    return fail(MR_ERR_WORKSPACE,
+                "inv_quarter_root_batched_noalloc: this batch needs %zu bytes of workspace, more than the %zu-byte "
+                "scratch array; call inv_quarter_root_batched with a workspace instead",
+                need, (size_t)MR_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != MR_OK) return st;
+  return inv_quarter_root_batched(p, count, dt, eps, normalize, method, info_dev, ws, MR_NOALLOC_SCRATCH_BYTES,
+                                  hip_stream);
+}
+
+}  // extern "C"
+
 // ================================================ inv_sqrt_root_batched
 namespace {
 

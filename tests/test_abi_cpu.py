@@ -129,6 +129,24 @@ def test_root_validation(lib):
     assert call_root(lib, [root(64), root(300, A=P3, X=P4)], ws=P5 + 8, ws_bytes=need) == 5
 
 
+def test_noalloc_root_validation(lib):
+    """The allocation-free root rejects invalid arguments like the workspace
+    call, and a batch whose workspace exceeds its scratch array with
+    MR_ERR_WORKSPACE, before it touches any device."""
+    def call(ps, eps=1e-6):
+        probs = (B.RootProblem * len(ps))(*ps)
+        return lib.inv_quarter_root_batched_noalloc(ctypes.addressof(probs), len(ps), B.MR_F32, eps,
+                                                    B.MR_NORM_TRACE, B.MR_AUTO, None, None)
+    assert call([root(8)], eps=0.0) == 4
+    assert call([root(0)]) == 2
+    assert call([root(8, X=P1 + 64)]) == 8
+    assert call([root(1024)]) == 5
+    assert b"scratch" in lib.mr_last_error_message()
+    probs = (B.RootProblem * 1)(root(920))
+    assert lib.inv_quarter_root_batched_workspace(ctypes.addressof(probs), 1, B.MR_F32, 0) > B.NOALLOC_SCRATCH_BYTES
+    assert call([root(920)]) == 5
+
+
 def apply_p(m, n, XL=P1, G=P2, XR=P3, U=P4, ldu=None):
     return B.ApplyProblem(m, n, XL, m, G, n, XR, n, U, ldu if ldu is not None else n)
 
