@@ -172,8 +172,9 @@ size_t gram_ema_update_workspace(const mr_gram_problem* problems, int32_t count,
  * raise them to -1/4, rebuild).  X is symmetric to the last bit.
  * Methods:
  *  - MR_JACOBI (d <= 128): cyclic Jacobi eigendecomposition of A/s in float64,
- *    one workgroup per matrix with A held in LDS; f = (lambda + eps)^(-1/4);
- *    X = V f V^T.
+ *    one workgroup per matrix with A held in LDS (and V too for d <= 96),
+ *    one launch per size class for any number of matrices;
+ *    f = (lambda + eps)^(-1/4); X = V f V^T.
  *  - MR_NEWTON: coupled Newton iteration for the inverse 4th root,
  *        M0 = (A/s + eps I)/c, X0 = I, T = (5 I - M)/4, X <- X T, M <- T^4 M,
  *    X = c^(-1/4) X_K, with M scaled by 1/s_t before each step (per-step
@@ -195,7 +196,8 @@ size_t gram_ema_update_workspace(const mr_gram_problem* problems, int32_t count,
  *    matrix cores.
  *  - MR_NEWTON_F64: the Newton iteration with every step in float64 (twice
  *    the cost of the float32 phase; for inputs near the float32 limit).
- *  - MR_AUTO: Jacobi for d <= 128, Newton otherwise.
+ *  - MR_AUTO: Jacobi for d <= 32, Newton otherwise (the faster route on
+ *    MI355X: Jacobi's sweeps are a chain of d - 1 dependent rounds each).
  * a_dtype: MR_F32 or MR_F64.  eps > 0 and finite.  info_dev: device array of
  * `count` records (may be NULL).  Never synchronises: the host launches a
  * fixed number of Newton steps and each matrix runs its own schedule under
@@ -337,8 +339,9 @@ typedef struct {
  *     M <- mu * M + (1 - mu) * G      (computed in float64, stored float32)
  * The momentum of each weight's gradient, whose preconditioned direction the
  * optimizer applies (EMA-Gram page, section "Results", compares update
- * directions at equal Grams and momentum; the MuonH notes of marin.community,
- * "A sphere for every matrix", take the momentum first).  0 <= mu < 1.  One
+ * directions at equal Grams and momentum; the MuonH notes of ai.thesatyajit.com,
+ * "Marin 535B-A23B", section "A sphere for every matrix", take the momentum
+ * first).  0 <= mu < 1.  One
  * HBM-bound pass (12 bytes per element; up to 48 matrices per launch).  No
  * workspace, no synchronisation.
  */
@@ -357,7 +360,8 @@ typedef struct {
 
 /*
  * hyperball_update_batched -- for every problem, in place, the MuonH
- * norm-preserving step (marin.community, "A sphere for every matrix"):
+ * norm-preserving step (ai.thesatyajit.com, "Marin 535B-A23B", section "A
+ * sphere for every matrix"):
  *     c = lr ||W|| / max(||U||, 1e-10),  W' = W - c U,
  *     W <- W' ||W|| / max(||W'||, 1e-10)
  * (Frobenius norms of the whole matrix), so every W keeps its norm.  Two
@@ -447,6 +451,14 @@ typedef struct {
   double measured_tflops[3]; /* register-only MFMA loops              */
 } mr_peak_info;
 mr_status mr_measure_peaks(mr_peak_info* out, void* hip_stream);
+
+/* Process-wide cap on the sweeps of the Jacobi route (default 30; the
+ * eigendecomposition converges in about 10 for float64 inputs).  A matrix
+ * still rotating after the last allowed sweep is reconstructed from where it
+ * stands and flagged MR_INFO_NOT_CONVERGED.  Takes effect for calls made
+ * after it returns; returns the previous cap, or -1 (and changes nothing)
+ * for a cap outside [1, 100].  Host-only. */
+int32_t mr_set_jacobi_max_sweeps(int32_t sweeps);
 
 const char* mr_status_string(mr_status status);
 const char* mr_last_error_message(void);

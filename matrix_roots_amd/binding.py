@@ -51,6 +51,7 @@ EXPORTED = (
     "mr_measure_peaks",
     "mr_trace_enable",
     "mr_trace_collect",
+    "mr_set_jacobi_max_sweeps",
     "mr_status_string",
     "mr_last_error_message",
     "mr_abi_version",
@@ -157,6 +158,8 @@ def library() -> ctypes.CDLL:
     lib.mr_trace_enable.restype = i32
     lib.mr_trace_collect.argtypes = [vp, i32]
     lib.mr_trace_collect.restype = i32
+    lib.mr_set_jacobi_max_sweeps.argtypes = [i32]
+    lib.mr_set_jacobi_max_sweeps.restype = i32
     lib.mr_status_string.argtypes = [i32]
     lib.mr_status_string.restype = ctypes.c_char_p
     lib.mr_last_error_message.argtypes = []
@@ -561,6 +564,14 @@ def measure_peaks(stream=None) -> dict:
 
 def newton_iterations(p: int, m0: float, tol: float) -> int:
     return int(library().mr_newton_iterations(p, m0, tol))
+
+
+def set_jacobi_max_sweeps(sweeps: int) -> int:
+    """Cap the Jacobi route's sweeps (process-wide); returns the previous cap."""
+    prev = int(library().mr_set_jacobi_max_sweeps(int(sweeps)))
+    if prev < 0:
+        raise ValueError(f"sweep cap {sweeps} outside [1, 100]")
+    return prev
 
 
 def trace_enable(on: bool = True) -> bool:

@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <string>
@@ -23,14 +24,6 @@
 #include "schedule.hpp"
 
 using namespace mr;
-
-#ifndef MR_NEWTON_BIG_FIRST
-#define MR_NEWTON_BIG_FIRST 1
-#endif
-// Split-fp16 Newton stages on 256 x 256 tiles for classes with d % 32 == 0.
-#ifndef MR_NEWTON_WIDE
-#define MR_NEWTON_WIDE 1
-#endif
 
 namespace {
 
@@ -154,14 +147,18 @@ struct RootPlan {
     size_t region_off, matrix_bytes;
   };
   std::vector<Cls> classes;
-  size_t state_off = 0, partial_off = 0, sched_off = 0, jac_off = 0;
+  size_t state_off = 0, partial_off = 0, sched_off = 0, jac_desc_off = 0;
   int64_t partial_stride = 0;
-  std::vector<size_t> jac_w_off;  // per Jacobi slot (index slot - n_newton)
+  std::vector<size_t> jac_w_off;  // per Jacobi slot (index slot - n_newton); 0 when W stays in LDS
+  int jac_first[kJacobiClasses] = {0, 0, 0, 0}, jac_count[kJacobiClasses] = {0, 0, 0, 0};  // slot ranges
   size_t total = 0;
 };
 
+// Sweep cap of the Jacobi route (mr_set_jacobi_max_sweeps).
+std::atomic<int32_t> g_jacobi_max_sweeps{kJacobiDefaultSweeps};
+
 bool use_jacobi(int64_t d, int32_t method) {
-  return method == MR_JACOBI || (method == MR_AUTO && d <= kJacobiMaxD);
+  return method == MR_JACOBI || (method == MR_AUTO && d <= kJacobiAutoMaxD);
 }
 
 RootPlan plan_root(const mr_root_problem* p, int32_t count, int32_t method) {
@@ -186,7 +183,14 @@ RootPlan plan_root(const mr_root_problem* p, int32_t count, int32_t method) {
     dmax_newton = std::max(dmax_newton, c.d);
   }
   P.n_newton = (int)P.slot_problem.size();
-  for (int i : jac) P.slot_problem.push_back(i);
+  // Jacobi slots grouped by size class (each class is one launch)
+  std::stable_sort(jac.begin(), jac.end(), [&](int x, int y) { return jacobi_class_of(p[x].d) < jacobi_class_of(p[y].d); });
+  for (size_t k = 0; k < jac.size(); ++k) {
+    const int c = jacobi_class_of(p[jac[k]].d);
+    if (P.jac_count[c] == 0) P.jac_first[c] = P.n_newton + (int)k;
+    ++P.jac_count[c];
+    P.slot_problem.push_back(jac[k]);
+  }
 
   size_t off = 0;
   P.state_off = off;
@@ -198,10 +202,15 @@ RootPlan plan_root(const mr_root_problem* p, int32_t count, int32_t method) {
   off = align256(off + sizeof(double) * (size_t)P.partial_stride * (size_t)std::max(P.n_newton, 1));
   P.sched_off = off;
   off = align256(off + sizeof(double) * kMaxNewtonIters * (size_t)std::max(P.n_newton, 1));
-  P.jac_off = off;
+  P.jac_desc_off = off;
+  off = align256(off + sizeof(JacobiDesc) * jac.size());
   for (size_t k = 0; k < jac.size(); ++k) {
-    P.jac_w_off.push_back(off);
     const int64_t d = p[jac[k]].d;
+    if (d + (d & 1) <= kJacobiLdsW) {
+      P.jac_w_off.push_back(0);
+      continue;
+    }
+    P.jac_w_off.push_back(off);
     off = align256(off + sizeof(double) * (size_t)d * (size_t)d);
   }
   for (auto& c : P.classes) {
@@ -217,6 +226,11 @@ RootPlan plan_root(const mr_root_problem* p, int32_t count, int32_t method) {
 extern "C" {
 
 int32_t mr_abi_version(void) { return MR_ABI_VERSION; }
+
+int32_t mr_set_jacobi_max_sweeps(int32_t sweeps) {
+  if (sweeps < 1 || sweeps > kJacobiMaxSweeps) return -1;
+  return g_jacobi_max_sweeps.exchange(sweeps);
+}
 
 const char* mr_last_error_message(void) { return g_err.c_str(); }
 
@@ -736,32 +750,47 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
   // the first step; only M and its powers run in float64 while the floor is low.
   const bool x_low = !all_f64 && !f32_mfma;
 
-  // ---------------- Jacobi matrices: one launch per 16
-  {
-    JacobiBatch jb;
-    memset(&jb, 0, sizeof jb);
-    jb.a_f64 = a_f64;
-    jb.a_packed = a_packed;
-    jb.normalize = normalize;
-    jb.max_sweeps = 30;
-    jb.eps = eps;
-    jb.state = state;
+  // ---------------- Jacobi matrices: descriptors into the workspace, then one
+  // launch per size class (one workgroup per matrix)
+  if (P.n_newton < count) {
+    JacobiDesc* table = reinterpret_cast<JacobiDesc*>(base + P.jac_desc_off);
+    JacobiDescBatch db;
+    memset(&db, 0, sizeof db);
+    db.dst = table;
     for (int slot = P.n_newton; slot < count; ++slot) {
       const mr_root_problem& q = p[P.slot_problem[slot]];
-      JacobiJob& J = jb.job[jb.njobs++];
-      J.A = q.A;
-      J.lda = q.lda;
-      J.X = q.X;
-      J.ldx = q.ldx;
-      J.W = reinterpret_cast<double*>(base + P.jac_w_off[slot - P.n_newton]);
-      J.d = (int32_t)q.d;
-      J.slot = slot;
-      J.problem = P.slot_problem[slot];
-      if (jb.njobs == kMaxJobs || slot == count - 1) {
-        if ((st = traced(kTrJacobi, jb.njobs > 0, s, [&] { return launch_jacobi(jb, s); }, "jacobi launch")) != MR_OK)
+      JacobiDesc& D = db.desc[db.count++];
+      D.A = q.A;
+      D.lda = q.lda;
+      D.X = q.X;
+      D.ldx = q.ldx;
+      const size_t woff = P.jac_w_off[slot - P.n_newton];
+      D.W = woff ? reinterpret_cast<double*>(base + woff) : nullptr;
+      D.d = (int32_t)q.d;
+      D.slot = slot;
+      D.problem = P.slot_problem[slot];
+      if (db.count == kMaxJacobiDesc || slot == count - 1) {
+        if ((st = traced(kTrJacobi, true, s, [&] { return launch_jacobi_desc(db, s); }, "jacobi table")) != MR_OK)
           return st;
-        jb.njobs = 0;
+        db.first += db.count;
+        db.count = 0;
       }
+    }
+    for (int c = 0; c < kJacobiClasses; ++c) {
+      if (P.jac_count[c] == 0) continue;
+      JacobiLaunch L;
+      memset(&L, 0, sizeof L);
+      L.desc = table;
+      L.state = state;
+      L.eps = eps;
+      L.first = P.jac_first[c] - P.n_newton;
+      L.count = P.jac_count[c];
+      L.normalize = normalize;
+      L.max_sweeps = g_jacobi_max_sweeps.load();
+      L.a_packed = a_packed;
+      if ((st = traced(kTrJacobi, true, s, [&] { return launch_jacobi(L, kJacobiClass[c], a_f64 != 0, s); },
+                       "jacobi launch")) != MR_OK)
+        return st;
     }
   }
 
@@ -851,7 +880,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
       g.vec64 = align >= 2 ? 2 : 1;
       g.vec32 = align >= 4 ? 4 : 1;
       g.vecx3 = align >= 8 ? 8 : 1;
-      g.wide = align == 32 && MR_NEWTON_WIDE;
+      g.wide = align == 32;  // split-fp16 stages on 256 x 256 tiles
       for (int ci = 0; ci < (int)P.classes.size(); ++ci) {
         const int64_t d = P.classes[ci].d;
         const int a = d % 32 == 0 ? 32 : d % 8 == 0 ? 8 : d % 4 == 0 ? 4 : d % 2 == 0 ? 2 : 1;
@@ -878,7 +907,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
       // Largest Grams first: their long tiles start early and the short
       // tiles of the small classes fill the launch's tail.
       for (size_t q = 0; q < g.cls.size(); ++q) {
-        const int ci = MR_NEWTON_BIG_FIRST ? g.cls[g.cls.size() - 1 - q] : g.cls[q];
+        const int ci = g.cls[g.cls.size() - 1 - q];
         const auto& c = P.classes[ci];
         NewtonClass& C = L.cls[L.ncls++];
         C.region = base + c.region_off;

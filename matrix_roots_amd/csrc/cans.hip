@@ -165,32 +165,24 @@ __global__ __launch_bounds__(256) void cans_init_kernel(const RootBatch B, doubl
 }
 
 // Block shapes: split products use the 128 x 128 split core; fp16 products
-// use MR_CANS_TILE x MR_CANS_TILE tiles (256: 8 waves of 128 x 64, each
+// use kCansTile x kCansTile tiles (256: 8 waves of 128 x 64, each
 // operand panel read half as often as with 128).
-#ifndef MR_CANS_TILE
-#define MR_CANS_TILE 256
-#endif
-#ifndef MR_CANS_BK
-#define MR_CANS_BK (MR_CANS_TILE == 256 ? 32 : 64)
-#endif
+constexpr int kCansTile = 256;
+constexpr int kCansBK = 32;
 using CansSplitShape = H16Shape<128, 128, 2, 2>;
-using CansF16Shape = H16Shape<MR_CANS_TILE, MR_CANS_TILE, 2, MR_CANS_TILE / 64, MR_CANS_BK>;
+using CansF16Shape = H16Shape<kCansTile, kCansTile, 2, kCansTile / 64, kCansBK>;
 
 // One launch stage of the iteration for every matrix of up to kMaxClasses
 // size classes; workgroup -> (class, matrix, job, tile) through the per-class
 // XCD remap.  PREC 1: fp16 products; PREC 3: split products.  FULL: the P
 // stage (every tile, stored with its transpose); else the symmetric stages.
-#ifndef MR_CANS_OCC_FULL
-#define MR_CANS_OCC_FULL 2
-#endif
-#ifndef MR_CANS_OCC_SYM
-#define MR_CANS_OCC_SYM 2
-#endif
+constexpr int kCansOccFull = 2;
+constexpr int kCansOccSym = 2;
 template <int VEC, int PREC, bool FULL, class S>
 __global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1
                                          : PREC == 3      ? 2
-                                         : FULL           ? MR_CANS_OCC_FULL
-                                                          : MR_CANS_OCC_SYM) void cans_gemm_kernel(const CansLaunch L) {
+                                         : FULL           ? kCansOccFull
+                                                          : kCansOccSym) void cans_gemm_kernel(const CansLaunch L) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[PREC == 3 ? 2 * X3Tile::LDS_HALVES : h16_kernel_lds_bytes<S>(4 * kSlabFloats)];
   const int64_t b = blockIdx.x;
   int ci = 0;

@@ -26,19 +26,12 @@
 namespace mr {
 
 // ------------------------------------------------------------------ float32
-#ifndef MR_F32_BK
-#define MR_F32_BK 32
-#endif
-#ifndef MR_F32_DBUF
-#define MR_F32_DBUF 1
-#endif
 
 struct F32Tile {
-  static constexpr int BM = 128, BN = 128, BK = MR_F32_BK, PAD = 4, LDW = BK + PAD;
+  static constexpr int BM = 128, BN = 128, BK = 32, PAD = 4, LDW = BK + PAD;
   static constexpr int THREADS = 256;
-  static constexpr bool DBUF = MR_F32_DBUF != 0;
   static constexpr int STAGE = (BM + BN) * LDW;         // floats per LDS stage (A then B)
-  static constexpr int LDS_FLOATS = STAGE * (DBUF ? 2 : 1);
+  static constexpr int LDS_FLOATS = 2 * STAGE;  // two stages
 };
 
 // Load a BM x BK chunk (rows r0.., k0..) of a K-contiguous float32 operand
@@ -146,40 +139,27 @@ __device__ __forceinline__ void f32_nt_tile(const float* __restrict__ A, int64_t
   F32Loader<VEC> la, lb;
   la.load(A, lda, M, K, m0, 0, tid);
   lb.load(B, ldb, N, K, n0, 0, tid);
-  if constexpr (F32Tile::DBUF) {
-    la.store(lds + AOFF, tid);
-    lb.store(lds + BOFF, tid);
+  la.store(lds + AOFF, tid);
+  lb.store(lds + BOFF, tid);
+  __syncthreads();
+  int stage = 0;
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    const bool more = k0 + BK < K;
+    if (more) {
+      la.load(A, lda, M, K, m0, k0 + BK, tid);
+      lb.load(B, ldb, N, K, n0, k0 + BK, tid);
+    }
+    const float* cur = lds + stage * F32Tile::STAGE;
+    f32_chunk(cur + AOFF, cur + BOFF, acc, lane, wm, wn);
+    if (more) {
+      float* nxt = lds + (stage ^ 1) * F32Tile::STAGE;
+      la.store(nxt + AOFF, tid);
+      lb.store(nxt + BOFF, tid);
+    }
     __syncthreads();
-    int stage = 0;
-    for (int k0 = 0; k0 < K; k0 += BK) {
-      const bool more = k0 + BK < K;
-      if (more) {
-        la.load(A, lda, M, K, m0, k0 + BK, tid);
-        lb.load(B, ldb, N, K, n0, k0 + BK, tid);
-      }
-      const float* cur = lds + stage * F32Tile::STAGE;
-      f32_chunk(cur + AOFF, cur + BOFF, acc, lane, wm, wn);
-      if (more) {
-        float* nxt = lds + (stage ^ 1) * F32Tile::STAGE;
-        la.store(nxt + AOFF, tid);
-        lb.store(nxt + BOFF, tid);
-      }
-      __syncthreads();
-      stage ^= 1;
-    }
-  } else {
-    for (int k0 = 0; k0 < K; k0 += BK) {
-      la.store(lds + AOFF, tid);
-      lb.store(lds + BOFF, tid);
-      __syncthreads();
-      if (k0 + BK < K) {
-        la.load(A, lda, M, K, m0, k0 + BK, tid);
-        lb.load(B, ldb, N, K, n0, k0 + BK, tid);
-      }
-      f32_chunk(lds + AOFF, lds + BOFF, acc, lane, wm, wn);
-      __syncthreads();
-    }
+    stage ^= 1;
   }
+  
 }
 
 // ------------------------------------------------------------- split fp16
@@ -193,22 +173,12 @@ __device__ __forceinline__ void f32_nt_tile(const float* __restrict__ A, int64_t
 // significands are exact in float32; the dropped lo*lo term and the rounding
 // of lo leave about 2^-22 relative error per product (float32: 2^-24), and
 // the float32 accumulation is the same as on the float32 matrix cores.
-#ifndef MR_X3_BK
-#define MR_X3_BK 32
-#endif
-#ifndef MR_X3_DBUF
-#define MR_X3_DBUF 1
-#endif
-#ifndef MR_X3_PAD
-#define MR_X3_PAD 8
-#endif
 struct X3Tile {
-  static constexpr int BM = 128, BN = 128, BK = MR_X3_BK, PAD = MR_X3_PAD, LDW = BK + PAD;  // halves per LDS row
+  static constexpr int BM = 128, BN = 128, BK = 32, PAD = 8, LDW = BK + PAD;  // halves per LDS row
   static constexpr int THREADS = 256;
-  static constexpr bool DBUF = MR_X3_DBUF != 0;
   static constexpr int ARR = BM * LDW;  // halves per array (A_hi, A_lo, B_hi, B_lo)
   static constexpr int STAGE = 4 * ARR;
-  static constexpr int LDS_HALVES = (DBUF ? 2 : 1) * STAGE;
+  static constexpr int LDS_HALVES = 2 * STAGE;  // two stages
 };
 
 struct SplitRef {
@@ -323,39 +293,26 @@ __device__ __forceinline__ void x3_nt_tile(SplitRef A, int64_t lda, SplitRef B, 
   SplitLoader<VEC> la, lb;
   la.load(A, lda, M, K, m0, 0, tid);
   lb.load(B, ldb, N, K, n0, 0, tid);
-  if constexpr (X3Tile::DBUF) {
-    la.store(lds, lds + X3Tile::ARR, tid);
-    lb.store(lds + 2 * X3Tile::ARR, lds + 3 * X3Tile::ARR, tid);
+  la.store(lds, lds + X3Tile::ARR, tid);
+  lb.store(lds + 2 * X3Tile::ARR, lds + 3 * X3Tile::ARR, tid);
+  __syncthreads();
+  int stage = 0;
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    const bool more = k0 + BK < K;
+    if (more) {
+      la.load(A, lda, M, K, m0, k0 + BK, tid);
+      lb.load(B, ldb, N, K, n0, k0 + BK, tid);
+    }
+    x3_chunk(lds + stage * X3Tile::STAGE, acc, acc2, lane, wm, wn);
+    if (more) {
+      _Float16* nxt = lds + (stage ^ 1) * X3Tile::STAGE;
+      la.store(nxt, nxt + X3Tile::ARR, tid);
+      lb.store(nxt + 2 * X3Tile::ARR, nxt + 3 * X3Tile::ARR, tid);
+    }
     __syncthreads();
-    int stage = 0;
-    for (int k0 = 0; k0 < K; k0 += BK) {
-      const bool more = k0 + BK < K;
-      if (more) {
-        la.load(A, lda, M, K, m0, k0 + BK, tid);
-        lb.load(B, ldb, N, K, n0, k0 + BK, tid);
-      }
-      x3_chunk(lds + stage * X3Tile::STAGE, acc, acc2, lane, wm, wn);
-      if (more) {
-        _Float16* nxt = lds + (stage ^ 1) * X3Tile::STAGE;
-        la.store(nxt, nxt + X3Tile::ARR, tid);
-        lb.store(nxt + 2 * X3Tile::ARR, nxt + 3 * X3Tile::ARR, tid);
-      }
-      __syncthreads();
-      stage ^= 1;
-    }
-  } else {
-    for (int k0 = 0; k0 < K; k0 += BK) {
-      la.store(lds, lds + X3Tile::ARR, tid);
-      lb.store(lds + 2 * X3Tile::ARR, lds + 3 * X3Tile::ARR, tid);
-      __syncthreads();
-      if (k0 + BK < K) {
-        la.load(A, lda, M, K, m0, k0 + BK, tid);
-        lb.load(B, ldb, N, K, n0, k0 + BK, tid);
-      }
-      x3_chunk(lds, acc, acc2, lane, wm, wn);
-      __syncthreads();
-    }
+    stage ^= 1;
   }
+  
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -481,9 +438,6 @@ __device__ __forceinline__ void x3dl_sched_overlap() {
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
-#ifndef MR_X3DL_PREFETCH  // 1: fragment reads one k-step ahead, across chunks
-#define MR_X3DL_PREFETCH 1
-#endif
 
 __device__ __forceinline__ void x3dl_nt_tile(SplitRef A, int64_t lda, SplitRef B, int64_t ldb, int M, int N, int K,
                                              int m0, int n0, unsigned char* __restrict__ lds, v16f (&acc)[2][2]) {
@@ -501,7 +455,6 @@ __device__ __forceinline__ void x3dl_nt_tile(SplitRef A, int64_t lda, SplitRef B
         acc2[rb][cb][v] = 0.f;
       }
   const int nch = K / X3DL::BK;
-#if MR_X3DL_PREFETCH
   // fragment reads one k-step ahead, across chunk boundaries too (the scheme
   // of x3w_nt_tile)
   static_assert(X3DL::BK == 32, "two k-steps per chunk");
@@ -537,24 +490,6 @@ __device__ __forceinline__ void x3dl_nt_tile(SplitRef A, int64_t lda, SplitRef B
       }
     }
   }
-#else
-  if (nch > 0) x3dl_issue(A, lda, B, ldb, M, N, m0, n0, 0, lds, wave, lane);
-  for (int c = 0; c < nch; c += 2) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (c + s < nch) {
-        wait_vmcnt<0>();  // this wave's copies of chunk c + s have landed
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();  // ... and every wave's; stage s ^ 1 is free
-        asm volatile("" ::: "memory");
-        if (c + s + 1 < nch)
-          x3dl_issue(A, lda, B, ldb, M, N, m0, n0, (c + s + 1) * X3DL::BK, lds + (s ^ 1) * X3DL::STAGE_BYTES, wave,
-                     lane);
-        x3dl_chunk(lds + s * X3DL::STAGE_BYTES, acc, acc2, lane, wm, wn);
-      }
-    }
-  }
-#endif
   __syncthreads();  // no wave leaves (or reuses the LDS) while another may still read the last stage
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
@@ -566,14 +501,11 @@ __device__ __forceinline__ void x3dl_nt_tile(SplitRef A, int64_t lda, SplitRef B
 
 // Direct-to-LDS core where its preconditions hold (VEC 8: 16-byte aligned
 // operands, leading dimensions multiples of 8), else the register-staged one.
-#ifndef MR_X3_DL
-#define MR_X3_DL 1
-#endif
 template <int VEC>
 __device__ __forceinline__ void x3_nt_tile_auto(SplitRef A, int64_t lda, SplitRef B, int64_t ldb, int M, int N, int K,
                                                 int m0, int n0, unsigned char* __restrict__ lds, v16f (&acc)[2][2]) {
   static_assert(X3DL::LDS_BYTES <= 2 * X3Tile::LDS_HALVES, "both cores fit the same LDS");
-  if (MR_X3_DL && VEC == 8 && K % X3DL::BK == 0)
+  if (VEC == 8 && K % X3DL::BK == 0)
     x3dl_nt_tile(A, lda, B, ldb, M, N, K, m0, n0, lds, acc);
   else
     x3_nt_tile<VEC>(A, lda, B, ldb, M, N, K, m0, n0, reinterpret_cast<_Float16*>(lds), acc);
@@ -606,19 +538,7 @@ struct X3WCfg {
   static_assert(BM == BN && CB % 2 == 0 && RB % 2 == 0 && CPA * THREADS == AU, "square tile, 64 x 64 wave slabs");
   static_assert(BK % 16 == 0 && 32 % BK == 0 && NST >= 2 && LDS_BYTES <= 160 * 1024, "chunk depth and stages");
 };
-#ifndef MR_X3W_BK
-#define MR_X3W_BK 32
-#endif
-#ifndef MR_X3W_NST
-#define MR_X3W_NST 2
-#endif
-#ifndef MR_X3W_WN
-#define MR_X3W_WN 4
-#endif
-#ifndef MR_X3W_PREFETCH  // 2: fragment reads one k-step ahead across chunks; 1: within a chunk; 0: none
-#define MR_X3W_PREFETCH 2
-#endif
-using X3W = X3WCfg<MR_X3W_BK, MR_X3W_NST, MR_X3W_WN>;
+using X3W = X3WCfg<32, 2, 4>;  // 32-deep chunks, two stages, 2 x 4 waves
 
 __device__ __forceinline__ void x3w_issue(SplitRef A, int64_t lda, SplitRef B, int64_t ldb, int M, int N, int m0,
                                           int n0, int k0, unsigned char* stage, int wave, int lane) {
@@ -652,95 +572,6 @@ __device__ __forceinline__ void x3w_issue(SplitRef A, int64_t lda, SplitRef B, i
       }
     }
   }
-}
-
-__device__ __forceinline__ void x3w_chunk(const unsigned char* __restrict__ st, v16f (&acc)[X3W::RB][X3W::CB],
-                                          int lane, int wm, int wn) {
-  constexpr int AB = X3W::AU * 16;  // bytes per array
-  constexpr int KS = X3W::BK / 16;
-#if MR_X3W_PREFETCH
-  // every k-step's fragments are read before the first product, so the
-  // reads of later k-steps land while the earlier k-steps' products run
-  // (LDS returns in order: the first products wait for their own reads only)
-  v8h ah[KS][X3W::RB], al[KS][X3W::RB], bh[KS][X3W::CB], bl[KS][X3W::CB];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int kg = ks * 2 + (lane >> 5);
-#pragma unroll
-    for (int rb = 0; rb < X3W::RB; ++rb) {
-      const int r = wm * (X3W::BM / X3W::WM) + rb * 32 + (lane & 31);
-      const int o = (r * X3W::UPR + dl_slot(r, kg, X3W::UPR)) * 16;
-      ah[ks][rb] = *reinterpret_cast<const v8h*>(st + o);
-      al[ks][rb] = *reinterpret_cast<const v8h*>(st + AB + o);
-    }
-#pragma unroll
-    for (int cb = 0; cb < X3W::CB; ++cb) {
-      const int r = wn * (X3W::BN / X3W::WN) + cb * 32 + (lane & 31);
-      const int o = (r * X3W::UPR + dl_slot(r, kg, X3W::UPR)) * 16;
-      bh[ks][cb] = *reinterpret_cast<const v8h*>(st + 2 * AB + o);
-      bl[ks][cb] = *reinterpret_cast<const v8h*>(st + 3 * AB + o);
-    }
-  }
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-    for (int cb = 0; cb < X3W::CB; ++cb) {
-#pragma unroll
-      for (int rb = 0; rb < X3W::RB; ++rb) acc[rb][cb] = mfma_f16_32x32x16(al[ks][rb], bh[ks][cb], acc[rb][cb]);
-      const v8h bs = bh[ks][cb] * (_Float16)2048.0f;
-#pragma unroll
-      for (int rb = 0; rb < X3W::RB; ++rb) {
-        acc[rb][cb] = mfma_f16_32x32x16(ah[ks][rb], bl[ks][cb], acc[rb][cb]);
-        acc[rb][cb] = mfma_f16_32x32x16(ah[ks][rb], bs, acc[rb][cb]);
-      }
-    }
-  }
-  // instruction order: the first k-step's reads, then each later k-step's
-  // reads spread over the previous k-step's products
-  constexpr int NR = 2 * (X3W::RB + X3W::CB), NM = 3 * X3W::RB * X3W::CB;
-  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-#pragma unroll
-  for (int ks = 1; ks < KS; ++ks) {
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, NM / NR, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, NM - (NM / NR) * NR, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-#else
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int kg = ks * 2 + (lane >> 5);
-    v8h ah[X3W::RB], al[X3W::RB], bh[X3W::CB], bl[X3W::CB];
-#pragma unroll
-    for (int rb = 0; rb < X3W::RB; ++rb) {
-      const int r = wm * (X3W::BM / X3W::WM) + rb * 32 + (lane & 31);
-      const int o = (r * X3W::UPR + dl_slot(r, kg, X3W::UPR)) * 16;
-      ah[rb] = *reinterpret_cast<const v8h*>(st + o);
-      al[rb] = *reinterpret_cast<const v8h*>(st + AB + o);
-    }
-#pragma unroll
-    for (int cb = 0; cb < X3W::CB; ++cb) {
-      const int r = wn * (X3W::BN / X3W::WN) + cb * 32 + (lane & 31);
-      const int o = (r * X3W::UPR + dl_slot(r, kg, X3W::UPR)) * 16;
-      bh[cb] = *reinterpret_cast<const v8h*>(st + 2 * AB + o);
-      bl[cb] = *reinterpret_cast<const v8h*>(st + 3 * AB + o);
-    }
-#pragma unroll
-    for (int cb = 0; cb < X3W::CB; ++cb) {
-#pragma unroll
-      for (int rb = 0; rb < X3W::RB; ++rb) acc[rb][cb] = mfma_f16_32x32x16(al[rb], bh[cb], acc[rb][cb]);
-      const v8h bs = bh[cb] * (_Float16)2048.0f;
-#pragma unroll
-      for (int rb = 0; rb < X3W::RB; ++rb) {
-        acc[rb][cb] = mfma_f16_32x32x16(ah[rb], bl[cb], acc[rb][cb]);
-        acc[rb][cb] = mfma_f16_32x32x16(ah[rb], bs, acc[rb][cb]);
-      }
-    }
-  }
-#endif
 }
 
 // One k-step's operand fragments of a wave (hi and lo halves of its A rows
@@ -785,12 +616,9 @@ __device__ __forceinline__ void x3w_mfma(const X3WFrag& f, v16f (&acc)[X3W::RB][
 
 // Instruction order for a region holding one k-step's products and the next
 // k-step's fragment reads: the reads spread evenly over the products.
-#ifndef MR_X3W_SCHED  // products per LDS read in the interleave (0: spread evenly; 1 or more: that many, rest after)
-#define MR_X3W_SCHED 0
-#endif
 __device__ __forceinline__ void x3w_sched_overlap() {
   constexpr int NR = 2 * (X3W::RB + X3W::CB), NM = 3 * X3W::RB * X3W::CB;
-  constexpr int PER = MR_X3W_SCHED > 0 ? MR_X3W_SCHED : NM / NR;
+  constexpr int PER = NM / NR;
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // products
@@ -813,7 +641,6 @@ __device__ __forceinline__ void x3w_nt_tile(SplitRef A, int64_t lda, SplitRef B,
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.f;
   const int nch = K / X3W::BK;
-#if MR_X3W_PREFETCH == 2
   // Fragment reads one k-step ahead, across chunk boundaries too: a k-step's
   // products run while the next k-step's fragments are read, from the same
   // stage or, after the barrier, from the next one.  The barrier sits
@@ -853,32 +680,6 @@ __device__ __forceinline__ void x3w_nt_tile(SplitRef A, int64_t lda, SplitRef B,
       }
     }
   }
-#else
-#pragma unroll
-  for (int p = 0; p < X3W::NST - 1; ++p)
-    if (p < nch) x3w_issue(A, lda, B, ldb, M, N, m0, n0, p * X3W::BK, lds + p * X3W::STAGE_BYTES, wave, lane);
-  for (int c = 0; c < nch; c += X3W::NST) {
-#pragma unroll
-    for (int s = 0; s < X3W::NST; ++s) {
-      const int cc = c + s;
-      if (cc < nch) {
-        // this wave's copies of chunk cc have landed (NST - 2 later chunks may
-        // still be in flight; the counter retires loads in issue order)
-        if (cc + X3W::NST - 2 < nch)
-          wait_vmcnt<(X3W::NST - 2) * X3W::LPC>();
-        else
-          wait_vmcnt<0>();
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();  // ... and every wave's; the stage of chunk cc - 1 is free
-        asm volatile("" ::: "memory");
-        if (cc + X3W::NST - 1 < nch)
-          x3w_issue(A, lda, B, ldb, M, N, m0, n0, (cc + X3W::NST - 1) * X3W::BK,
-                    lds + ((s + X3W::NST - 1) % X3W::NST) * X3W::STAGE_BYTES, wave, lane);
-        x3w_chunk(lds + s * X3W::STAGE_BYTES, acc, lane, wm, wn);
-      }
-    }
-  }
-#endif
   __syncthreads();  // no wave leaves (or reuses the LDS) while another may still read the last stage
 #pragma unroll
   for (int rb = 0; rb < X3W::RB; ++rb)
@@ -918,22 +719,12 @@ __device__ __forceinline__ void f32_for_each(const v16f (&acc)[2][2], F&& f) {
 }
 
 // ------------------------------------------------------------------ float64
-#ifndef MR_F64_BK
-#define MR_F64_BK 16
-#endif
-#ifndef MR_F64_DBUF
-#define MR_F64_DBUF 1
-#endif
 
-#ifndef MR_F64_PAD
-#define MR_F64_PAD 2
-#endif
 struct F64Tile {
-  static constexpr int BM = 128, BN = 128, BK = MR_F64_BK, PAD = MR_F64_PAD, LDW = BK + PAD;
+  static constexpr int BM = 128, BN = 128, BK = 16, PAD = 2, LDW = BK + PAD;
   static constexpr int THREADS = 256;
-  static constexpr bool DBUF = MR_F64_DBUF != 0;
   static constexpr int STAGE = (BM + BN) * LDW;  // doubles per LDS stage (A then B)
-  static constexpr int LDS_DOUBLES = STAGE * (DBUF ? 2 : 1);
+  static constexpr int LDS_DOUBLES = 2 * STAGE;  // two stages
 };
 
 // Loader of a BM x BK chunk of operand element (i, k), i in [r0, r0+BM),
@@ -1090,40 +881,27 @@ __device__ __forceinline__ void f64_tile(const TA* __restrict__ A, int64_t lda, 
   F64Loader<TB, TRANSB, VECB> lb;
   la.load(A, lda, M, K, m0, 0, tid);
   lb.load(B, ldb, N, K, n0, 0, tid);
-  if constexpr (F64Tile::DBUF) {
-    la.store(lds + AOFF, tid);
-    lb.store(lds + BOFF, tid);
+  la.store(lds + AOFF, tid);
+  lb.store(lds + BOFF, tid);
+  __syncthreads();
+  int stage = 0;
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    const bool more = k0 + BK < K;
+    if (more) {
+      la.load(A, lda, M, K, m0, k0 + BK, tid);
+      lb.load(B, ldb, N, K, n0, k0 + BK, tid);
+    }
+    const double* cur = lds + stage * F64Tile::STAGE;
+    f64_chunk(cur + AOFF, cur + BOFF, acc, lane, wm, wn);
+    if (more) {
+      double* nxt = lds + (stage ^ 1) * F64Tile::STAGE;
+      la.store(nxt + AOFF, tid);
+      lb.store(nxt + BOFF, tid);
+    }
     __syncthreads();
-    int stage = 0;
-    for (int k0 = 0; k0 < K; k0 += BK) {
-      const bool more = k0 + BK < K;
-      if (more) {
-        la.load(A, lda, M, K, m0, k0 + BK, tid);
-        lb.load(B, ldb, N, K, n0, k0 + BK, tid);
-      }
-      const double* cur = lds + stage * F64Tile::STAGE;
-      f64_chunk(cur + AOFF, cur + BOFF, acc, lane, wm, wn);
-      if (more) {
-        double* nxt = lds + (stage ^ 1) * F64Tile::STAGE;
-        la.store(nxt + AOFF, tid);
-        lb.store(nxt + BOFF, tid);
-      }
-      __syncthreads();
-      stage ^= 1;
-    }
-  } else {
-    for (int k0 = 0; k0 < K; k0 += BK) {
-      la.store(lds + AOFF, tid);
-      lb.store(lds + BOFF, tid);
-      __syncthreads();
-      if (k0 + BK < K) {
-        la.load(A, lda, M, K, m0, k0 + BK, tid);
-        lb.load(B, ldb, N, K, n0, k0 + BK, tid);
-      }
-      f64_chunk(lds + AOFF, lds + BOFF, acc, lane, wm, wn);
-      __syncthreads();
-    }
+    stage ^= 1;
   }
+  
 }
 
 // The same product (float64 operands along contiguous rows, NT) with the
@@ -1136,9 +914,6 @@ __device__ __forceinline__ void f64_tile(const TA* __restrict__ A, int64_t lda, 
 // M - 1 or N - 1: they only feed outputs that are never stored.  Symmetric
 // outputs only: in a diagonal tile (m0 == n0) the blocks wholly below the
 // diagonal are left at zero (f64_block_mode).
-#ifndef MR_F64_PREFETCH  // 1: fragment reads one half-chunk ahead, across chunks
-#define MR_F64_PREFETCH 1
-#endif
 struct F64DL {
   static constexpr int BK = F64Tile::BK, UPR = BK / 2;
   static constexpr int AU = F64Tile::BM * UPR;  // 16-byte units per operand and stage
@@ -1259,7 +1034,6 @@ __device__ __forceinline__ void f64dl_nt_tile(const double* __restrict__ A, int6
       for (int v = 0; v < 4; ++v) acc[rb][cb][v] = 0.0;
   const int nch = K / F64DL::BK;
   const int mode = f64_block_mode(m0 == n0, wm, wn);
-#if MR_F64_PREFETCH
   // Fragment reads one half-chunk ahead, across chunk boundaries too: the
   // reads of the next half are issued before this half's products (the same
   // scheme as the wide split-fp16 core).
@@ -1295,7 +1069,6 @@ __device__ __forceinline__ void f64dl_nt_tile(const double* __restrict__ A, int6
   }
   __syncthreads();  // no wave leaves (or reuses the LDS) while another may still read the last stage
   return;
-#endif
   if (nch > 0) f64dl_issue(A, lda, B, ldb, M, N, m0, n0, 0, lds, wave, lane);
   for (int c = 0; c < nch; c += 2) {
 #pragma unroll
@@ -1452,15 +1225,12 @@ __device__ __forceinline__ void f64g_tile(const float* __restrict__ G, int64_t l
 
 // Direct-to-LDS core for float64 operands where its preconditions hold
 // (VEC 2: 16-byte aligned rows), else the register-staged one.
-#ifndef MR_F64_DL
-#define MR_F64_DL 1
-#endif
 template <int VEC>
 __device__ __forceinline__ void f64_nt_tile_auto(const double* __restrict__ A, int64_t lda,
                                                  const double* __restrict__ B, int64_t ldb, int M, int N, int K,
                                                  int m0, int n0, double* __restrict__ lds, v4d (&acc)[4][4]) {
   static_assert(F64DL::LDS_BYTES <= (int)sizeof(double) * F64Tile::LDS_DOUBLES, "both cores fit the same LDS");
-  if (MR_F64_DL && VEC == 2 && K % F64DL::BK == 0)
+  if (VEC == 2 && K % F64DL::BK == 0)
     f64dl_nt_tile(A, lda, B, ldb, M, N, K, m0, n0, reinterpret_cast<unsigned char*>(lds), acc);
   else
     f64_tile<double, false, VEC, double, false, VEC>(A, lda, B, ldb, M, N, K, m0, n0, lds, acc);

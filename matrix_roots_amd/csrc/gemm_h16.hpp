@@ -179,9 +179,6 @@ struct H16DLShape {
   static_assert(UPR == 4 || UPR == 8, "swizzle period");
 };
 
-#ifndef MR_H16_PREFETCH  // 1: fragment reads one k-step ahead, across chunks
-#define MR_H16_PREFETCH 1
-#endif
 
 template <class S>
 __device__ __forceinline__ void h16dl_issue(const _Float16* __restrict__ A, int64_t lda, const _Float16* __restrict__ B,
@@ -289,7 +286,6 @@ __device__ __forceinline__ void h16dl_nt_tile(const _Float16* __restrict__ A, in
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.f;
   const int nch = K / S::BK;
-#if MR_H16_PREFETCH
   // Fragment reads one k-step ahead, across chunk boundaries too (the scheme
   // of the wide split-fp16 Newton core): the barrier sits before the last
   // k-step's products, once every wave has finished reading the stage (LDS
@@ -333,7 +329,6 @@ __device__ __forceinline__ void h16dl_nt_tile(const _Float16* __restrict__ A, in
   }
   __syncthreads();  // no wave leaves while another may still read the last stage
   return;
-#endif
   if (nch > 0) h16dl_issue<S>(A, lda, B, ldb, M, N, m0, n0, 0, lds, wave, lane);
   for (int c = 0; c < nch; c += 2) {
 #pragma unroll
@@ -355,14 +350,11 @@ __device__ __forceinline__ void h16dl_nt_tile(const _Float16* __restrict__ A, in
 
 // The direct-to-LDS tile of an H16Shape (K-chunks of 64) and the LDS bytes a
 // kernel needs for either core.
-#ifndef MR_H16_DL
-#define MR_H16_DL 1
-#endif
 template <class S>
 using H16DLOf = H16DLShape<S::BM, S::BN, S::WM, S::WN, 64>;
 template <class S>
 constexpr int h16_lds_bytes() {
-  return (MR_H16_DL && H16DLOf<S>::LDS_BYTES > 2 * S::LDS_HALVES) ? H16DLOf<S>::LDS_BYTES : 2 * S::LDS_HALVES;
+  return (H16DLOf<S>::LDS_BYTES > 2 * S::LDS_HALVES) ? H16DLOf<S>::LDS_BYTES : 2 * S::LDS_HALVES;
 }
 // ... or the wide-store epilogue's slabs (17 KB per wave), whichever is larger
 template <class S>
@@ -379,7 +371,7 @@ __device__ __forceinline__ void h16_nt_tile_auto(const _Float16* __restrict__ A,
                                                  const _Float16* __restrict__ B, int64_t ldb, int M, int N, int K,
                                                  int m0, int n0, unsigned char* __restrict__ lds,
                                                  v16f (&acc)[S::RB][S::CB]) {
-  if (MR_H16_DL && VEC == 8 && K % 64 == 0)
+  if (VEC == 8 && K % 64 == 0)
     h16dl_nt_tile<H16DLOf<S>>(A, lda, B, ldb, M, N, K, m0, n0, lds, acc);
   else
     h16g_nt_tile<S, VEC>(A, lda, B, ldb, M, N, K, m0, n0, reinterpret_cast<_Float16*>(lds), acc);

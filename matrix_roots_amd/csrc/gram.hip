@@ -16,13 +16,8 @@
 #include "launch.hpp"
 
 // Direct-to-LDS float32 operands (f64g_tile) where K is a multiple of 16 and
-// rows are 16-byte aligned; MR_SYRK_NST stages.
-#ifndef MR_SYRK_DL
-#define MR_SYRK_DL 1
-#endif
-#ifndef MR_SYRK_NST
-#define MR_SYRK_NST 3
-#endif
+// rows are 16-byte aligned; kSyrkStages stages.
+constexpr int kSyrkStages = 3;
 
 namespace mr {
 
@@ -42,9 +37,9 @@ __global__ __launch_bounds__(256, 2) void syrk_ema_kernel(const SyrkBatch batch)
   const int m0 = ti * F64Tile::BM, n0 = tj * F64Tile::BN;
 
   v4d acc[4][4];
-  if (MR_SYRK_DL && VEC == 4 && J.K % 16 == 0) {
-    static_assert(F64G<RIGHT, MR_SYRK_NST>::LDS_BYTES <= (int)sizeof(smem), "stages fit");
-    f64g_tile<RIGHT, MR_SYRK_NST>(J.G, J.ldg, J.d, J.K, m0, n0, reinterpret_cast<unsigned char*>(smem), acc);
+  if (VEC == 4 && J.K % 16 == 0) {
+    static_assert(F64G<RIGHT, kSyrkStages>::LDS_BYTES <= (int)sizeof(smem), "stages fit");
+    f64g_tile<RIGHT, kSyrkStages>(J.G, J.ldg, J.d, J.K, m0, n0, reinterpret_cast<unsigned char*>(smem), acc);
   } else {
     f64_tile<float, RIGHT, VEC, float, RIGHT, VEC>(J.G, J.ldg, J.G, J.ldg, J.d, J.d, J.K, m0, n0, smem, acc);
   }

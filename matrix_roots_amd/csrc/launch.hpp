@@ -1,10 +1,10 @@
 // Kernel-argument records shared by the host runtime and the kernels, and the
 // launcher functions each kernel file exports to the host runtime.
 //
-// Every per-problem table travels by value in the kernel arguments (at most
-// kMaxJobs or kMaxSyrkJobs records per launch, under the 4 KiB argument
-// limit), so an
-// entry point never copies descriptors to the device.
+// Per-problem tables travel by value in the kernel arguments (a bounded
+// number of records per launch, under the 4 KiB argument limit); the Jacobi
+// route copies its records into the caller's workspace with a kernel, so no
+// entry point ever copies descriptors with the host.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -15,11 +15,17 @@
 
 namespace mr {
 
-constexpr int kMaxJobs = 16;
 constexpr int kMaxSyrkJobs = 48;   // Gram EMA: one launch per side for up to 48 weights (2.3 KiB)
 constexpr int kMaxRootJobs = 48;   // root statistics, init and finalize launches (3.1 KiB)
 constexpr int kMaxClasses = 8;
 constexpr int kJacobiMaxD = 128;
+// MR_AUTO takes the eigendecomposition route up to this size: measured on
+// MI355X, Jacobi is faster than the Newton route's launch sequence for
+// d <= 32 (4 to 256 matrices per call) and slower above (d = 48: 0.92 against
+// 0.53 ms for 4 matrices; d = 128: 9.3 against 1.1 ms).
+constexpr int kJacobiAutoMaxD = 32;
+constexpr int kJacobiDefaultSweeps = 30;
+constexpr int kJacobiMaxSweeps = 100;
 constexpr int kStatsRows = 32;       // rows of A per statistics workgroup (one 32-row tile stripe)
 constexpr int kFinalRows = 8;        // rows of X per finalize workgroup
 constexpr double kSwitchM = 5e-4;    // float64 -> float32 once the eigenvalue floor reaches this
@@ -200,27 +206,46 @@ struct NewtonLaunch {
 };
 
 // ------------------------------------------------------------ Jacobi
-struct JacobiJob {
+// One matrix of a Jacobi launch; the host writes the batch's records into the
+// workspace (jacobi_desc_kernel) and each launch reads its size class's range.
+struct JacobiDesc {
   const void* A;
   int64_t lda;
   float* X;
   int64_t ldx;
-  double* W;  // d*d float64 eigenvector scratch in the workspace
+  double* W;  // d*d float64 eigenvector scratch in the workspace (d > 96 only)
   int32_t d;
   int32_t slot;
   int32_t problem;
   int32_t pad;
 };
-struct JacobiBatch {
-  JacobiJob job[kMaxJobs];
-  int32_t njobs;
-  int32_t a_f64;
+static_assert(sizeof(JacobiDesc) == 56, "JacobiDesc layout");
+constexpr int kMaxJacobiDesc = 64;
+struct JacobiDescBatch {
+  JacobiDesc desc[kMaxJacobiDesc];
+  JacobiDesc* dst;  // the workspace table
+  int32_t first, count;
+};
+static_assert(sizeof(JacobiDescBatch) + 64 < 4096, "Jacobi descriptor batch fits the kernel arguments");
+// Jacobi size classes: padded size n = d + (d odd) <= kJacobiClass[k]; W in
+// LDS for classes up to kJacobiLdsW.
+constexpr int kJacobiClasses = 4;
+constexpr int kJacobiClass[kJacobiClasses] = {32, 64, 96, 128};
+constexpr int kJacobiLdsW = 96;
+__host__ __device__ inline int jacobi_class_of(int64_t d) {
+  const int64_t n = d + (d & 1);
+  return n <= 32 ? 0 : n <= 64 ? 1 : n <= 96 ? 2 : 3;
+}
+struct JacobiLaunch {
+  const JacobiDesc* desc;
+  RootState* state;
+  double eps;
+  int32_t first;  // first record of this launch; one workgroup per record
+  int32_t count;
   int32_t normalize;
   int32_t max_sweeps;
   int32_t a_packed;  // A stored packed (MR_PACKED)
   int32_t pad;
-  double eps;
-  RootState* state;
 };
 
 // ------------------------------------------------------------ launchers
@@ -243,6 +268,7 @@ hipError_t launch_newton_convert(const NewtonLaunch& L, hipStream_t s);
 hipError_t launch_root_finalize(const RootBatch& b, hipStream_t s);
 hipError_t launch_root_info(RootState* state, const double* partial, int64_t partial_stride,
                             int32_t count, mr_root_info* info, hipStream_t s);
-hipError_t launch_jacobi(const JacobiBatch& b, hipStream_t s);
+hipError_t launch_jacobi(const JacobiLaunch& L, int nmax, bool a_f64, hipStream_t s);
+hipError_t launch_jacobi_desc(const JacobiDescBatch& b, hipStream_t s);
 
 }  // namespace mr

@@ -21,9 +21,6 @@ constexpr int kWave = 64;
 
 // Conflict-free LDS store order of the fp16 tile loaders (gemm_core.hpp,
 // gemm_h16.hpp); 0 keeps the row-major order.
-#ifndef MR_LDS_SWZ
-#define MR_LDS_SWZ 1
-#endif
 
 // Which (row, 16-byte group) of a loader chunk the thread slot idx moves,
 // for GPR groups per row and rows padded by one group (row stride
@@ -36,7 +33,6 @@ constexpr int kWave = 64;
 // Each row's GPR groups still come from consecutive lanes.
 template <int GPR>
 __device__ __forceinline__ void tile_slot(int idx, int& row, int& grp) {
-#if MR_LDS_SWZ
   if constexpr (GPR == 4) {
     const int g = idx >> 4, q = idx & 15;
     row = 16 * (g >> 2) + (g & 3) + 4 * (q >> 2);
@@ -48,7 +44,6 @@ __device__ __forceinline__ void tile_slot(int idx, int& row, int& grp) {
     grp = q & 7;
     return;
   }
-#endif
   row = idx / GPR;
   grp = idx % GPR;
 }
@@ -187,14 +182,12 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
 // (each column panel chunk used about twice before it leaves L2); bands of
 // G tile rows walked column by column touch ~G + G panels per G*G tiles.
 // G = 1 is the row-major order.
-#ifndef MR_TILE_GROUP
-#define MR_TILE_GROUP 8
-#endif
+constexpr int kTileGroup = 8;
 
 // Tile u of the upper triangle (ti <= tj) of a T x T grid, in bands of
-// MR_TILE_GROUP tile rows, each band column by column.
+// kTileGroup tile rows, each band column by column.
 __device__ __forceinline__ void upper_tile_grouped(int u, int T, int& ti, int& tj) {
-  constexpr int G = MR_TILE_GROUP;
+  constexpr int G = kTileGroup;
   int b0 = 0;
   while (true) {
     const int h = T - b0 < G ? T - b0 : G;
@@ -218,10 +211,10 @@ __device__ __forceinline__ void upper_tile_grouped(int u, int T, int& ti, int& t
   }
 }
 
-// Tile u of a full TM x TN grid, in bands of MR_TILE_GROUP tile rows, each
+// Tile u of a full TM x TN grid, in bands of kTileGroup tile rows, each
 // band column by column.
 __device__ __forceinline__ void full_tile_grouped(int u, int TM, int TN, int& ti, int& tj) {
-  constexpr int G = MR_TILE_GROUP;
+  constexpr int G = kTileGroup;
   const int b0 = (u / (G * TN)) * G;
   const int h = TM - b0 < G ? TM - b0 : G;
   const int v = u - b0 * TN;

@@ -176,15 +176,11 @@ __global__ __launch_bounds__(256) void polar_init_kernel(const PolarBatch B, dou
 // stored into T(k+1) and, transposed, into T^T.
 // Block shapes: 128 x 128 for split products and for the fp16 Gram (whose
 // few output tiles would leave the chip half idle with larger ones),
-// MR_POLAR_TILE-square tiles for the fp16 update.
-#ifndef MR_POLAR_TILE
-#define MR_POLAR_TILE 256
-#endif
-#ifndef MR_POLAR_BK
-#define MR_POLAR_BK (MR_POLAR_TILE == 256 ? 32 : 64)
-#endif
+// kPolarTile-square tiles for the fp16 update.
+constexpr int kPolarTile = 256;
+constexpr int kPolarBK = 32;
 using PolarSplitShape = H16Shape<128, 128, 2, 2>;
-using PolarF16Shape = H16Shape<MR_POLAR_TILE, MR_POLAR_TILE, 2, MR_POLAR_TILE / 64, MR_POLAR_BK>;
+using PolarF16Shape = H16Shape<kPolarTile, kPolarTile, 2, kPolarTile / 64, kPolarBK>;
 
 template <int VEC, int PREC, bool FULL, class S>
 __global__ __launch_bounds__(S::THREADS, S::THREADS >= 512 ? 1 : 2) void polar_gemm_kernel(const PolarLaunch L) {

@@ -39,12 +39,8 @@
 #include "launch.hpp"
 #include "schedule.hpp"
 
-#ifndef MR_F64_OCC
-#define MR_F64_OCC 2
-#endif
-#ifndef MR_F32_OCC
-#define MR_F32_OCC 2
-#endif
+constexpr int kF64Occupancy = 2;  // workgroups per CU of the float64 Newton kernel
+constexpr int kF32Occupancy = 2;  // ... and of the float32 one
 
 namespace mr {
 
@@ -453,7 +449,7 @@ __device__ __forceinline__ void sym_store(const StageOps<T>& o, int d, int gr, i
 }
 
 template <int VEC>
-__global__ __launch_bounds__(256, VEC == 2 ? MR_F64_OCC : 1) void newton_f64_kernel(const NewtonLaunch L) {
+__global__ __launch_bounds__(256, VEC == 2 ? kF64Occupancy : 1) void newton_f64_kernel(const NewtonLaunch L) {
   // (with x_low, stage 2 also writes the split copy Mx of the new M)
   __shared__ __attribute__((aligned(16))) double smem[F64Tile::LDS_DOUBLES];
   const StageJob s = stage_job(L, kStageF64);
@@ -484,7 +480,7 @@ __global__ __launch_bounds__(256, VEC == 2 ? MR_F64_OCC : 1) void newton_f64_ker
 }
 
 template <int VEC>
-__global__ __launch_bounds__(256, MR_F32_OCC) void newton_f32_kernel(const NewtonLaunch L) {
+__global__ __launch_bounds__(256, kF32Occupancy) void newton_f32_kernel(const NewtonLaunch L) {
   __shared__ float smem[F32Tile::LDS_FLOATS];
   const StageJob s = stage_job(L, kStageF32);
   if (!s.active) return;

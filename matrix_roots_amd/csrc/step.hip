@@ -3,8 +3,9 @@
 //
 //  * momentum EMA, M <- mu M + (1 - mu) G, the momentum whose preconditioned
 //    direction the optimizer applies (EMA-Gram page, section "Results");
-//  * the MuonH hyperball update (marin.community, "A sphere for every
-//    matrix"): c = lr ||W|| / max(||U||, 1e-10), W' = W - c U,
+//  * the MuonH hyperball update (ai.thesatyajit.com, "Marin 535B-A23B",
+//    section "A sphere for every matrix"): c = lr ||W|| / max(||U||, 1e-10),
+//    W' = W - c U,
 //    W <- W' ||W|| / max(||W'||, 1e-10), norms over the whole matrix.
 //
 // The hyperball update makes two passes instead of three: the first reduces

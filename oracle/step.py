@@ -23,7 +23,8 @@ What it computes, and where the pages define it:
   (sections 2.2-2.4, appendix D), as the same eigenvalue map with power -1/2.
 * The step around the preconditioner: a momentum EMA of the gradient and
   the MuonH norm-preserving (hyperball) update of the weight
-  (marin.community, "A sphere for every matrix").
+  (ai.thesatyajit.com, "Marin 535B-A23B", section "A sphere for
+  every matrix").
 * The polar orthogonalisation its CANS coefficients were designed for
   (section 2.3), as the odd polynomial those ten steps apply to the
   singular values (numpy.linalg.svd, LAPACK gesdd).
@@ -224,15 +225,15 @@ def polar_cans(G):
 def momentum_ema(M, G, mu: float) -> np.ndarray:
     """M <- mu M + (1 - mu) G: the momentum the preconditioned direction is
     taken of (EMA-Gram page, "Results", compares update directions at equal
-    Grams and momentum; marin.community's MuonH notes take the momentum of
+    Grams and momentum; the MuonH notes of the Marin 535B-A23B article take the momentum of
     each matrix's gradient first).  The EMA form is a reading: its scale
     cancels in the norm-preserving update below."""
     return float(mu) * _f64(M) + (1.0 - float(mu)) * _f64(G)
 
 
 def hyperball_update(W, U, lr: float):
-    """The MuonH hyperball step (marin.community, "A sphere for every
-    matrix"): move W against U by lr times W's own norm, then rescale back to
+    """The MuonH hyperball step (ai.thesatyajit.com, "Marin 535B-A23B",
+    section "A sphere for every matrix"): move W against U by lr times W's own norm, then rescale back to
     W's original norm, with the page's 1e-10 floors on both divisors:
 
         c = lr ||W|| / max(||U||, 1e-10),  W' = W - c U,

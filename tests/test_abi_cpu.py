@@ -124,7 +124,10 @@ def test_root_validation(lib):
     assert call_root(lib, [root(200)]) == 5
     probs = (B.RootProblem * 2)(root(64), root(300, A=P3, X=P4))
     need = lib.inv_quarter_root_batched_workspace(ctypes.addressof(probs), 2, B.MR_F32, 0)
-    assert need >= 40 * 300 * 300 + 8 * 64 * 64
+    assert need >= 40 * 300 * 300  # the d = 64 Jacobi root keeps its eigenvectors in LDS
+    probs128 = (B.RootProblem * 1)(root(128))
+    need128 = lib.inv_quarter_root_batched_workspace(ctypes.addressof(probs128), 1, B.MR_F32, B.MR_JACOBI)
+    assert need128 >= 8 * 128 * 128  # ... a d = 128 one in the workspace
     assert call_root(lib, [root(64), root(300, A=P3, X=P4)], ws=P5, ws_bytes=need - 1) == 5
     assert call_root(lib, [root(64), root(300, A=P3, X=P4)], ws=P5 + 8, ws_bytes=need) == 5
 

@@ -274,14 +274,17 @@ def run_pipeline(torch, dev, grads_per_step, beta, eps, method="auto", state_dty
         yield Xs[:k], Xs[k:], Us, info
 
 
-def test_toy_end_to_end(torch_dev):
+@pytest.mark.parametrize("method", ["auto", "jacobi"])
+def test_toy_end_to_end(torch_dev, method):
+    """The toy workload's 10 steps, by the default route (Newton for its 64^2
+    and 128^2 Grams) and by the eigendecomposition route."""
     torch, dev = torch_dev
     wl = W.WORKLOADS["toy"]
     steps = [[W.gradient("toy", w, t) for w in range(len(wl.shapes))] for t in range(1, wl.steps + 1)]
     refs = [list(oracle.run_sequence([steps[t][w] for t in range(wl.steps)], wl.beta, wl.eps))
             for w in range(len(wl.shapes))]
     worst = [0.0, 0.0]
-    for t, (XL, XR, U, info) in enumerate(run_pipeline(torch, dev, steps, wl.beta, wl.eps)):
+    for t, (XL, XR, U, info) in enumerate(run_pipeline(torch, dev, steps, wl.beta, wl.eps, method=method)):
         assert (info["flags"] == 0).all(), info
         for w in range(len(wl.shapes)):
             _, _, _, rXL, rXR, rU, _ = refs[w][t]
@@ -290,7 +293,7 @@ def test_toy_end_to_end(torch_dev):
             e_u = oracle.relative_frobenius(U[w].cpu().numpy(), rU)
             worst = [max(worst[0], e_root), max(worst[1], e_u)]
             assert e_root <= ROOT_TOL and e_u <= UPDATE_TOL, (t, w, e_root, e_u)
-    print(f"toy worst root err {worst[0]:.3e} update err {worst[1]:.3e}")
+    print(f"toy ({method}) worst root err {worst[0]:.3e} update err {worst[1]:.3e}")
 
 
 @pytest.mark.parametrize("method", ["auto", "newton", "newton_f32"])

@@ -1,5 +1,5 @@
 """Pins of the oracle's momentum EMA and MuonH hyperball update
-(marin.community, "A sphere for every matrix") by closed forms and
+(ai.thesatyajit.com, "Marin 535B-A23B", section "A sphere for every matrix") by closed forms and
 invariants, none of which retype the oracle's formulas."""
 
 import numpy as np
