@@ -174,22 +174,27 @@ def cpu_baseline_illcond(mats, eps_list, max_seconds: float = 20.0):
 
 # ----------------------------------------------------------- roofline helpers
 def recorded_traffic(kernel: str, workload: str, family: str = "quarter"):
-    """HBM bytes per launch of `kernel` from the committed counter summary,
-    if the kernel sources are unchanged since the counters were taken."""
+    """HBM bytes per working launch of `kernel` (FETCH_SIZE + WRITE_SIZE,
+    calibrated) from the committed counter summary, if the kernel sources are
+    unchanged since the counters were taken; None for a summary covering
+    several kernels."""
     from matrix_roots_amd import profile_summary
 
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
     if not os.path.exists(path):
         return None
     rec = {}
+    keys = ("traffic_bytes_per_working_launch", "traffic_bytes_per_launch", "source_sha256")
     for line in open(path):
-        if ":" in line and line.split(":", 1)[0].strip() in ("traffic_bytes_per_launch", "source_sha256"):
+        if ":" in line and line.split(":", 1)[0].strip() in keys:
             k, v = line.split(":", 1)
+            if k.strip() in rec and k.strip() != "source_sha256":
+                return None
             rec[k.strip()] = v.strip().strip("`")
     if rec.get("source_sha256") != profile_summary.sources_sha256(family):
         return None
     try:
-        return float(rec["traffic_bytes_per_launch"])
+        return float(rec.get("traffic_bytes_per_working_launch", rec["traffic_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
 
@@ -246,11 +251,13 @@ def roofline_for(kernels, name, workload):
         r = {"bound": "mfma", "kernel": name, "engine": k["engine"],
              "achieved": k["mfma_tflops"] if split else k["tflops"], "peak": k["peak"], "unit": "TFLOP/s",
              "frac": k["frac"], "traffic": recorded_traffic(name, workload),
+             "traffic_per": "working launch (calibrated FETCH_SIZE + WRITE_SIZE, profiles/)",
              "achieved_per_launch": "algorithmic flops of the class over the timed steps (x3 fp16 products for "
                                     "split classes) / sum of its event-measured launch durations"}
     else:
         r = {"bound": "hbm", "kernel": name, "achieved": k["gb_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
              "frac": k["hbm_frac"], "traffic": recorded_traffic(name, workload),
+             "traffic_per": "working launch (calibrated FETCH_SIZE + WRITE_SIZE, profiles/)",
              "achieved_per_launch": "algorithmic bytes of the class over the timed steps / sum of its "
                                     "event-measured launch durations"}
     if "launches_working" in k:

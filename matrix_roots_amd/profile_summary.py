@@ -2,7 +2,8 @@
 
     python -m matrix_roots_amd.profile_summary \
         --fetch prof/fetch --write prof/write \
-        --kernel newton_f64_kernel --copy-mib 1024 [--out profiles/x.md]
+        --kernel newton_f64_kernel --copy-mib 1024
+    python -m matrix_roots_amd.profile_summary --trace prof/kt
 
 Reads the `*counter_collection.csv` files of two `rocprofv3 --pmc` runs
 (FETCH_SIZE, then WRITE_SIZE; both in KiB per dispatch) of the same program.
@@ -80,9 +81,45 @@ def summarise(fetch_dir, write_dir, kernel, copy_mib):
         scale = copy_bytes / (copy_kib * 1024.0)
         names, kvals = pick(vals, kernel)
         mean_kib = sum(kvals) / len(kvals)
+        # working dispatches: the ones that moved data (a launch whose
+        # matrices have all finished exits at once and reads almost nothing)
+        top = max(kvals)
+        work = [v for v in kvals if v >= 0.05 * top] if top > 0 else kvals
+        wmean = sum(work) / len(work)
         res[name] = {"kernels": names, "dispatches": len(kvals), "mean_kib": mean_kib, "copy_kib": copy_kib,
-                     "scale": scale, "bytes_per_dispatch": mean_kib * 1024.0 * scale}
+                     "scale": scale, "bytes_per_dispatch": mean_kib * 1024.0 * scale,
+                     "working": len(work), "bytes_per_working_dispatch": wmean * 1024.0 * scale}
     return res
+
+
+def trace_table(run_dir: str, working_frac: float = 0.05):
+    """Markdown table of a `--kernel-trace` run: per kernel, dispatches,
+    working dispatches (those lasting at least `working_frac` of the kernel's
+    longest: the library launches a fixed number of Newton steps and a
+    launch whose matrices have all finished exits at once), total time,
+    average per dispatch and per working dispatch, and share of the total."""
+    files = glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no kernel_trace.csv under {run_dir}")
+    durs = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                ns = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+                durs.setdefault(r["Kernel_Name"], []).append(ns / 1e6)
+    total = sum(sum(v) for v in durs.values())
+    rows = []
+    for name, v in durs.items():
+        top = max(v)
+        work = [x for x in v if x >= working_frac * top]
+        rows.append((sum(v), name, len(v), len(work), sum(v) / len(v), sum(work) / len(work)))
+    rows.sort(reverse=True)
+    out = ["| kernel | dispatches | working | total (ms) | avg per dispatch (ms) | avg per working dispatch (ms) | % |",
+           "|:--|--:|--:|--:|--:|--:|--:|"]
+    for tot, name, n, nw, avg, avgw in rows:
+        short = name if len(name) <= 90 else name[:87] + "..."
+        out.append(f"| `{short}` | {n} | {nw} | {tot:.3f} | {avg:.4f} | {avgw:.4f} | {100 * tot / total:.2f} |")
+    return "\n".join(out)
 
 
 def mfma_busy(run_dir: str, kernels):
@@ -117,7 +154,11 @@ def main(argv=None) -> int:
     ap.add_argument("--mfma", help="run dir of a SQ_VALU_MFMA_BUSY_CYCLES + GRBM_GUI_ACTIVE pass")
     ap.add_argument("--pair", action="append", default=[],
                     help="KERNEL=PEAK_KERNEL for --mfma (e.g. newton_f64_kernel=peak_kernel<1>)")
+    ap.add_argument("--trace", help="run dir of a --kernel-trace run: print the per-kernel table")
     args = ap.parse_args(argv)
+    if args.trace:
+        print(trace_table(args.trace))
+        return 0
     if args.mfma:
         res = mfma_busy(args.mfma, [tuple(x.split("=", 1)) for x in args.pair])
         for name, r in res.items():
@@ -134,8 +175,11 @@ def main(argv=None) -> int:
     print(f"dispatches: {f['dispatches']}")
     for name, r in res.items():
         print(f"{name}: mean {r['mean_kib']:.1f} KiB/dispatch; calibration copy of {args.copy_mib:g} MiB "
-              f"read {r['copy_kib']:.1f} KiB -> scale {r['scale']:.4f}; {r['bytes_per_dispatch']:.4e} B/dispatch")
+              f"read {r['copy_kib']:.1f} KiB -> scale {r['scale']:.4f}; {r['bytes_per_dispatch']:.4e} B/dispatch; "
+              f"{r['working']} working dispatches: {r['bytes_per_working_dispatch']:.4e} B each")
     print(f"traffic_bytes_per_launch: {f['bytes_per_dispatch'] + w['bytes_per_dispatch']:.6e}")
+    print(f"traffic_bytes_per_working_launch: "
+          f"{f['bytes_per_working_dispatch'] + w['bytes_per_working_dispatch']:.6e}")
     print(f"source_family: {args.family}")
     print(f"source_sha256: {sources_sha256(args.family)}")
     return 0
