@@ -461,6 +461,11 @@ def bench_steps(args, torch, B, W, peaks):
 
     size_classes = None
     if args.size_classes:
+        # the per-class calls take their own workspaces: free the step's first
+        # (the width-2048 set needs most of the 288 GB otherwise)
+        del Xs, Us, grads
+        ws.buf = ws.info = None
+        torch.cuda.empty_cache()
         size_classes = per_size_class(B, torch, Ls + Rs, wl)
 
     cpu = None

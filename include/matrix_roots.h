@@ -28,6 +28,11 @@
  *    mr_root_info records in device memory that the caller reads after its
  *    own synchronisation.
  *  - Calls that share a workspace must be ordered on one stream.
+ *  - Within one call, no matrix the call writes may overlap another matrix it
+ *    writes or one it reads, in the same problem or in another problem of the
+ *    batch (matrices it only reads may share memory); each matrix counts as
+ *    the bytes from its first element to its last.  Violations return
+ *    MR_ERR_ALIAS before anything is enqueued.
  */
 #ifndef MATRIX_ROOTS_H
 #define MATRIX_ROOTS_H
@@ -50,7 +55,7 @@ typedef int32_t mr_status;
 #define MR_ERR_WORKSPACE 5   /* workspace NULL, too small or misaligned         */
 #define MR_ERR_HIP 6         /* the HIP runtime reported an error               */
 #define MR_ERR_UNSUPPORTED 7 /* valid request the library does not implement    */
-#define MR_ERR_ALIAS 8       /* an output overlaps an input it must not alias   */
+#define MR_ERR_ALIAS 8       /* an output overlaps another output or an input   */
 
 typedef int32_t mr_dtype;
 #define MR_F32 0

@@ -61,6 +61,37 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 Range sym_range_of(const void* p, int64_t d, int64_t ld, size_t es, bool packed) {
   return packed ? range_of(p, 1, d * (d + 1) / 2, 0, es) : range_of(p, d, d, ld, es);
 }
+// All-or-nothing alias check over a whole batch: no byte range a call writes
+// may overlap another one it writes or one it reads, within a problem or
+// across problems (inputs may share memory with each other).
+struct AliasSet {
+  struct Tagged {
+    Range r;
+    int problem;
+    const char* name;
+  };
+  std::vector<Tagged> outs, ins;
+  void out(Range r, int i, const char* name) { outs.push_back({r, i, name}); }
+  void in(Range r, int i, const char* name) { ins.push_back({r, i, name}); }
+  mr_status check() {
+    std::sort(outs.begin(), outs.end(), [](const Tagged& a, const Tagged& b) { return a.r.lo < b.r.lo; });
+    for (size_t k = 1; k < outs.size(); ++k)
+      if (outs[k].r.lo < outs[k - 1].r.hi)
+        return fail(MR_ERR_ALIAS, "problem %d: %s overlaps problem %d's %s", outs[k].problem, outs[k].name,
+                    outs[k - 1].problem, outs[k - 1].name);
+    // the outputs are now disjoint and sorted, so the last one starting before
+    // an input ends is the only one that can overlap it
+    for (const Tagged& x : ins) {
+      auto it = std::lower_bound(outs.begin(), outs.end(), x.r.hi,
+                                 [](const Tagged& a, uintptr_t v) { return a.r.lo < v; });
+      if (it != outs.begin() && std::prev(it)->r.hi > x.r.lo)
+        return fail(MR_ERR_ALIAS, "problem %d: %s overlaps problem %d's %s", std::prev(it)->problem,
+                    std::prev(it)->name, x.problem, x.name);
+    }
+    return MR_OK;
+  }
+};
+
 // Base dtype and storage flag of an mr_dtype argument.
 mr_dtype base_dtype(mr_dtype dt) { return dt & ~MR_PACKED; }
 bool is_packed(mr_dtype dt) { return (dt & MR_PACKED) != 0; }
@@ -362,6 +393,7 @@ static mr_status validate_gram(const mr_gram_problem* p, int32_t count, mr_dtype
   if (sides == 0 || (sides & ~(uint32_t)(MR_LEFT | MR_RIGHT)))
     return fail(MR_ERR_PARAM, "sides 0x%x must be a non-empty subset of MR_LEFT|MR_RIGHT", sides);
   const size_t es = base_dtype(dt) == MR_F64 ? 8 : 4;
+  AliasSet al;
   for (int i = 0; i < count; ++i) {
     const mr_gram_problem& q = p[i];
     if (q.m < 1 || q.n < 1 || q.m > kMaxDim || q.n > kMaxDim)
@@ -390,8 +422,11 @@ static mr_status validate_gram(const mr_gram_problem* p, int32_t count, mr_dtype
     }
     if ((sides & MR_LEFT) && (sides & MR_RIGHT) && overlap(rl, rr))
       return fail(MR_ERR_ALIAS, "problem %d: L overlaps R", i);
+    al.in(rg, i, "G");
+    if (sides & MR_LEFT) al.out(rl, i, "L");
+    if (sides & MR_RIGHT) al.out(rr, i, "R");
   }
-  return MR_OK;
+  return al.check();
 }
 
 size_t gram_ema_update_workspace(const mr_gram_problem*, int32_t, mr_dtype, uint32_t) { return 0; }
@@ -462,6 +497,7 @@ static mr_status validate_apply(const mr_apply_problem* p, int32_t count, float 
   if (count < 0) return fail(MR_ERR_PARAM, "count %d < 0", count);
   if (count > 0 && !p) return fail(MR_ERR_NULL, "problems is NULL");
   if (!std::isfinite(alpha)) return fail(MR_ERR_PARAM, "alpha is not finite");
+  AliasSet al;
   for (int i = 0; i < count; ++i) {
     const mr_apply_problem& q = p[i];
     if (q.m < 1 || q.n < 1 || q.m > kMaxDim || q.n > kMaxDim)
@@ -476,8 +512,12 @@ static mr_status validate_apply(const mr_apply_problem* p, int32_t count, float 
     if (overlap(ru, range_of(q.XL, q.m, q.m, q.ldxl, 4)) || overlap(ru, range_of(q.G, q.m, q.n, q.ldg, 4)) ||
         overlap(ru, range_of(q.XR, q.n, q.n, q.ldxr, 4)))
       return fail(MR_ERR_ALIAS, "problem %d: U overlaps XL, G or XR", i);
+    al.out(ru, i, "U");
+    al.in(range_of(q.XL, q.m, q.m, q.ldxl, 4), i, "XL");
+    al.in(range_of(q.G, q.m, q.n, q.ldg, 4), i, "G");
+    al.in(range_of(q.XR, q.n, q.n, q.ldxr, 4), i, "XR");
   }
-  return MR_OK;
+  return al.check();
 }
 
 // Split apply workspace of one problem: split copies (4 bytes per element)
@@ -686,6 +726,7 @@ mr_status precondition_apply(const mr_apply_problem* p, int32_t count, float alp
 static mr_status validate_root_problems(const mr_root_problem* p, int32_t count, mr_dtype dt) {
   const size_t es = base_dtype(dt) == MR_F64 ? 8 : 4;
   const bool packed = is_packed(dt);
+  AliasSet al;
   for (int i = 0; i < count; ++i) {
     const mr_root_problem& q = p[i];
     if (q.d < 1 || q.d > kMaxDim)
@@ -695,8 +736,10 @@ static mr_status validate_root_problems(const mr_root_problem* p, int32_t count,
     if (!aligned(q.A, es) || !aligned(q.X, 4)) return fail(MR_ERR_PARAM, "problem %d: A or X misaligned", i);
     if (overlap(sym_range_of(q.A, q.d, q.lda, es, packed), range_of(q.X, q.d, q.d, q.ldx, 4)))
       return fail(MR_ERR_ALIAS, "problem %d: X overlaps A", i);
+    al.in(sym_range_of(q.A, q.d, q.lda, es, packed), i, "A");
+    al.out(range_of(q.X, q.d, q.d, q.ldx, 4), i, "X");
   }
-  return MR_OK;
+  return al.check();
 }
 
 static mr_status validate_root(const mr_root_problem* p, int32_t count, mr_dtype dt, double eps, int32_t normalize,
@@ -1192,7 +1235,8 @@ mr_status inv_sqrt_root_batched(const mr_root_problem* p, int32_t count, mr_dtyp
     }
     if (!g.cls.empty()) groups.push_back(g);
   }
-  auto launch_stage = [&](int stage, int k, double a0, double b0, double a1, double b1) -> mr_status {
+  // sprec: the products' precision for this stage (3 split, 1 fp16)
+  auto launch_stage = [&](int stage, int k, double a0, double b0, double a1, double b1, int sprec) -> mr_status {
     for (const auto& g : groups) {
       CansLaunch L;
       memset(&L, 0, sizeof L);
@@ -1210,7 +1254,7 @@ mr_status inv_sqrt_root_batched(const mr_root_problem* p, int32_t count, mr_dtyp
         C.matrix_bytes = (int64_t)c.matrix_bytes;
         C.d = (int32_t)c.d;
         C.count = c.count;
-        C.T = tiles(c.d, cans_tile(prec));
+        C.T = tiles(c.d, cans_tile(sprec));
         C.U = C.T * (C.T + 1) / 2;
         C.slot_begin = c.first_slot;
         C.block_begin = L.total_blocks;
@@ -1219,24 +1263,27 @@ mr_status inv_sqrt_root_batched(const mr_root_problem* p, int32_t count, mr_dtyp
         L.total_blocks += round8(C.nblocks);
       }
       const int cls = stage == kCansP ? kTrCansP : kTrCansYZ;
-      mr_status r = traced(cls, true, s, [&] { return launch_cans_gemm(L, g.vec, prec, s); }, "cans gemm launch");
+      mr_status r = traced(cls, true, s, [&] { return launch_cans_gemm(L, g.vec, sprec, s); }, "cans gemm launch");
       if (r != MR_OK) return r;
     }
     return MR_OK;
   };
-  // k = 0: P_0 = Y_0, so Z_1 = Q_0 (written by the init) and Y_1 = a0 Y0 + b0 Y0^2
+  // k = 0: P_0 = Y_0, so Z_1 = Q_0 (written by the init) and Y_1 = a0 Y0 + b0 Y0^2.
+  // Always a split product: near the top of the spectrum a0 y + b0 y^2 is
+  // about y / 18, so an fp16 rounding of Y0 would enter 18-fold; in split
+  // form Y1 is float32-accurate and the later fp16 steps see no cancellation.
   {
     const double a = kCansCoeff[0][0], b = kCansCoeff[0][1];
-    if ((st = launch_stage(kCansY1, 0, b * sc.sy[1] / (sc.sy[0] * sc.sy[0]), a * sc.sy[1] / sc.sy[0], 0.0, 0.0)) !=
-        MR_OK)
+    if ((st = launch_stage(kCansY1, 0, b * sc.sy[1] / (sc.sy[0] * sc.sy[0]), a * sc.sy[1] / sc.sy[0], 0.0, 0.0,
+                           3)) != MR_OK)
       return st;
   }
   for (int k = 1; k < kCansSteps; ++k) {
     const double a = kCansCoeff[k][0], b = kCansCoeff[k][1];
-    if ((st = launch_stage(kCansP, k, sc.sp[k] / (sc.sz[k] * sc.sy[k]), 0.0, 0.0, 0.0)) != MR_OK) return st;
+    if ((st = launch_stage(kCansP, k, sc.sp[k] / (sc.sz[k] * sc.sy[k]), 0.0, 0.0, 0.0, prec)) != MR_OK) return st;
     const double ay = b * sc.sy[k + 1] / (sc.sy[k] * sc.sp[k]), by = a * sc.sy[k + 1] / sc.sy[k];
     const double az = b * sc.sz[k + 1] / (sc.sz[k] * sc.sp[k]), bz = a * sc.sz[k + 1] / sc.sz[k];
-    if ((st = launch_stage(k + 1 < kCansSteps ? kCansYZ : kCansZ, k, ay, by, az, bz)) != MR_OK) return st;
+    if ((st = launch_stage(k + 1 < kCansSteps ? kCansYZ : kCansZ, k, ay, by, az, bz, prec)) != MR_OK) return st;
   }
   if ((st = run_batches(2)) != MR_OK) return st;
   return traced(kTrCansInfo, true, s, [&] {
@@ -1302,6 +1349,7 @@ static mr_status validate_polar(const mr_polar_problem* p, int32_t count, int32_
   if (count > 0 && !p) return fail(MR_ERR_NULL, "problems is NULL");
   if (precision != MR_CANS_F16 && precision != MR_CANS_SPLIT)
     return fail(MR_ERR_PARAM, "precision %d is not MR_CANS_F16 or MR_CANS_SPLIT", precision);
+  AliasSet al;
   for (int i = 0; i < count; ++i) {
     const mr_polar_problem& q = p[i];
     if (q.m < 1 || q.n < 1 || q.m > kMaxDim || q.n > kMaxDim)
@@ -1312,8 +1360,10 @@ static mr_status validate_polar(const mr_polar_problem* p, int32_t count, int32_
     if (!aligned(q.G, 4) || !aligned(q.O, 4)) return fail(MR_ERR_PARAM, "problem %d: G or O misaligned", i);
     if (overlap(range_of(q.G, q.m, q.n, q.ldg, 4), range_of(q.O, q.m, q.n, q.ldo, 4)))
       return fail(MR_ERR_ALIAS, "problem %d: O overlaps G", i);
+    al.in(range_of(q.G, q.m, q.n, q.ldg, 4), i, "G");
+    al.out(range_of(q.O, q.m, q.n, q.ldo, 4), i, "O");
   }
-  return MR_OK;
+  return al.check();
 }
 
 size_t polar_cans_batched_workspace(const mr_polar_problem* p, int32_t count, int32_t) {
@@ -1528,10 +1578,14 @@ mr_status momentum_ema_batched(const mr_momentum_problem* p, int32_t count, doub
   if (count < 0) return fail(MR_ERR_PARAM, "count %d < 0", count);
   if (count > 0 && !p) return fail(MR_ERR_NULL, "problems is NULL");
   if (!(mu >= 0.0 && mu < 1.0)) return fail(MR_ERR_PARAM, "mu %g not in [0, 1)", mu);
+  AliasSet al;
   for (int i = 0; i < count; ++i) {
     mr_status st = validate_stream(i, p[i].m, p[i].n, p[i].G, p[i].ldg, p[i].M, p[i].ldm, "G", "M");
     if (st != MR_OK) return st;
+    al.in(range_of(p[i].G, p[i].m, p[i].n, p[i].ldg, 4), i, "G");
+    al.out(range_of(p[i].M, p[i].m, p[i].n, p[i].ldm, 4), i, "M");
   }
+  if (mr_status st = al.check(); st != MR_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
   return run_stream(
       count,
@@ -1566,10 +1620,14 @@ mr_status hyperball_update_batched(const mr_hyperball_problem* p, int32_t count,
   if (count < 0) return fail(MR_ERR_PARAM, "count %d < 0", count);
   if (count > 0 && !p) return fail(MR_ERR_NULL, "problems is NULL");
   if (!(lr >= 0.0) || !std::isfinite(lr)) return fail(MR_ERR_PARAM, "lr %g must be >= 0 and finite", lr);
+  AliasSet al;
   for (int i = 0; i < count; ++i) {
     mr_status st = validate_stream(i, p[i].m, p[i].n, p[i].U, p[i].ldu, p[i].W, p[i].ldw, "U", "W");
     if (st != MR_OK) return st;
+    al.in(range_of(p[i].U, p[i].m, p[i].n, p[i].ldu, 4), i, "U");
+    al.out(range_of(p[i].W, p[i].m, p[i].n, p[i].ldw, 4), i, "W");
   }
+  if (mr_status st = al.check(); st != MR_OK) return st;
   if (count == 0) return MR_OK;
   const size_t need = hyperball_update_batched_workspace(p, count);
   if (!ws || ws_bytes < need || !aligned(ws, 256))

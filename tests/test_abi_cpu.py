@@ -347,3 +347,34 @@ def test_measure_peaks_rejects_null(lib):
     """mr_measure_peaks validates its output pointer before any HIP call."""
     assert lib.mr_measure_peaks(None, None) == 1  # MR_ERR_NULL
     assert "NULL" in lib.mr_last_error_message().decode()
+
+
+def test_aliasing_across_problems_is_rejected(lib):
+    """Validation covers the whole batch: an output of one problem may not
+    overlap an output or input of another (inputs may be shared).  Every case
+    is rejected with MR_ERR_ALIAS before anything is enqueued."""
+    Q = 0x1000  # 4 KiB apart: an 8 x 8 float64 or a 16 x 16 float32 matrix fits in between
+    # Gram EMA: two problems updating one state; a state inside another problem's gradient
+    assert call_gram(lib, [gram(8, 8, G=P1, L=P2, R=P3), gram(8, 8, G=P1 + Q, L=P2, R=P3 + Q)]) == 8
+    assert b"overlaps" in lib.mr_last_error_message()
+    assert call_gram(lib, [gram(8, 8, G=P1, L=P2, R=P3), gram(8, 8, G=P2, L=P4, R=P5)]) == 8
+    # roots: X_1 over A_0, X_0 over X_1; a shared input is fine (then: no workspace)
+    assert call_root(lib, [root(8, A=P1, X=P2), root(8, A=P3, X=P1 + 64)]) == 8
+    assert call_root(lib, [root(8, A=P1, X=P2), root(8, A=P3, X=P2 + 128)]) == 8
+    assert call_root(lib, [root(8, A=P1, X=P2), root(8, A=P1, X=P3)]) == 5
+    assert call_sqrt(lib, [root(8, A=P1, X=P2), root(8, A=P3, X=P1)]) == 8
+    # apply: U_1 over XR_0; U_0 over U_1; shared roots are fine
+    assert lib.precondition_apply(ctypes.addressof((B.ApplyProblem * 2)(
+        apply_p(8, 8, XL=P1, G=P2, XR=P3, U=P4), apply_p(8, 8, XL=P1 + Q, G=P2 + Q, XR=P3 + Q, U=P3))),
+        2, 1.0, None, 0, None) == 8
+    assert lib.precondition_apply(ctypes.addressof((B.ApplyProblem * 2)(
+        apply_p(8, 8, U=P4), apply_p(8, 8, U=P4 + 32))), 2, 1.0, None, 0, None) == 8
+    assert lib.precondition_apply(ctypes.addressof((B.ApplyProblem * 2)(
+        apply_p(8, 8, U=P4), apply_p(8, 8, U=P5))), 2, 1.0, None, 0, None) == 5
+    # polar, momentum, hyperball
+    arr = (B.PolarProblem * 2)(B.PolarProblem(8, 4, P1, 4, P2, 4), B.PolarProblem(8, 4, P3, 4, P1, 4))
+    assert lib.polar_cans_batched(ctypes.addressof(arr), 2, 0, None, None, 0, None) == 8
+    arr = (B.MomentumProblem * 2)(B.MomentumProblem(4, 8, P1, 8, P2, 8), B.MomentumProblem(4, 8, P3, 8, P2, 8))
+    assert lib.momentum_ema_batched(ctypes.addressof(arr), 2, 0.9, None) == 8
+    arr = (B.HyperballProblem * 2)(B.HyperballProblem(4, 8, P1, 8, P2, 8), B.HyperballProblem(4, 8, P2, 8, P3, 8))
+    assert lib.hyperball_update_batched(ctypes.addressof(arr), 2, 0.1, None, None, 0, None) == 8

@@ -7,16 +7,19 @@ arithmetic: fp16 rounding of S alone (unit roundoff 2^-11) moves an
 eigenvalue lambda by up to about 2^-11 ||S|| / sqrt(3), a relative change of
 W's eigenvalue of half that over lambda / ||S||; over the matrices used here
 (condition number <= 1e3) a CPU emulation of the fp16 iteration gives at most
-2.6e-3 (7.3e-3 on a rank-deficient Gram with eps = 1e-3).  Eigenvalues near
-the bound L lose more: the first step's a0 y + b0 y^2 cancels to about 1/18
-of its terms there, so the fp16 rounding of y enters 18-fold (1.3e-2 for
-d = 1, where that eigenvalue is all of W).  MR_CANS_F16 is held to 2e-2.  Split products round at 2^-22; the
-ten-step CANS map itself stops at 3e-5 of the exact root for lambda/L >= 1e-6;
-the emulation gives at most 4.7e-5 up to condition number 1e4, so
-MR_CANS_SPLIT is held to 1e-4.  Every output is checked to be exactly
-symmetric, finite and unflagged, with the inverse-root residual
-||W S W - I||_F / sqrt(d) computed in float64 by torch below 5e-2 (f16) or
-1e-3 (split).
+2.6e-3 (7.3e-3 on a rank-deficient Gram with eps = 1e-3), and the GPU at
+most 4.9e-3 for d >= 7.  The first step's a0 y + b0 y^2 cancels to about
+1/18 of its terms near the top of the spectrum; it runs on split products in
+both precisions, so no fp16 rounding is amplified there (d = 1: 8.9e-5).
+MR_CANS_F16 is held to 1e-2, and to 2e-2 for d <= 3, where the smallest
+eigenvalue of a condition-1e3 spectrum carries most of ||W|| and the fp16
+resolution of S alone moves it by several times 1e-3 (1.3e-2 measured at
+d = 3).  Split products round at 2^-22; the ten-step CANS map itself stops
+at 3e-5 of the exact root for lambda/L >= 1e-6; the emulation gives at most
+4.7e-5 up to condition number 1e4, so MR_CANS_SPLIT is held to 1e-4.  Every
+output is checked to be exactly symmetric, finite and unflagged, with the
+inverse-root residual ||W S W - I||_F / sqrt(d) computed in float64 by
+torch below 5e-2 (f16) or 1e-3 (split).
 """
 
 import numpy as np
@@ -28,7 +31,8 @@ from matrix_roots_amd import workloads as W
 
 pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
 
-TOL = {"f16": 2e-2, "split": 1e-4}
+TOL = {"f16": 1e-2, "split": 1e-4}
+TOL_F16_TINY = 2e-2  # d <= 3
 RES = {"f16": 5e-2, "split": 1e-3}
 
 
@@ -58,7 +62,8 @@ def check(torch, dev, As, eps, normalize, precision, dtype=np.float32, tol=None)
         assert np.array_equal(Wg, Wg.T) and np.isfinite(Wg).all()
         err = oracle.relative_frobenius(Wg, ref)
         worst = max(worst, err)
-        assert err <= (tol or TOL[precision]), (i, A.shape, precision, err)
+        bound = tol or (TOL_F16_TINY if precision == "f16" and A.shape[0] <= 3 else TOL[precision])
+        assert err <= bound, (i, A.shape, precision, err)
         S = Ad[i].double()
         S = 0.5 * (S + S.T) / (torch.trace(S) if normalize == "trace" else 1.0)
         S = S + eps * torch.eye(S.shape[0], dtype=torch.float64, device=dev)
