@@ -208,9 +208,10 @@ size_t gram_ema_update_workspace(const mr_gram_problem* problems, int32_t count,
  * fixed number of Newton steps and each matrix runs its own schedule under
  * it.  With MR_NORM_TRACE that number covers every matrix (c <= 1.01 (1 +
  * eps)); with MR_NORM_NONE it covers floors eps/c down to 1e-16, and a
- * matrix whose floor lies lower stops at that count with
- * MR_INFO_NOT_CONVERGED set (float64 rounding of M0 is already of the
- * floor's size there).
+ * matrix whose floor lies lower runs the schedule of the floor 1e-16 and is
+ * flagged MR_INFO_NOT_CONVERGED (float64 rounding of M0 is already of the
+ * floor's size there; eigenvalues of A/c + eps/c above 1e-16 still
+ * converge).
  * Workspace: at least inv_quarter_root_batched_workspace(...) bytes, 256-byte
  * aligned; its contents on entry are ignored.
  */

@@ -895,14 +895,16 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
     // No rescale: the bound c is only known on the device; the cap is the
     // schedule from the floor kNoneFloorCap, every matrix runs its own
     // schedule under it (the launches past its last step exit at once), and
-    // one whose floor eps / c lies lower is flagged MR_INFO_NOT_CONVERGED.
+    // one whose floor eps / c lies lower runs the cap's schedule itself,
+    // flagged MR_INFO_NOT_CONVERGED.  Both rely on the step count and the
+    // float64 step count never rising with the floor.
     int k_cap, j_cap;
     const double floor_cap = normalize == MR_NORM_TRACE ? eps / (1.02 * (1.0 + eps)) : kNoneFloorCap;
     newton_scaled_schedule(floor_cap, 1.0 / kBoundSafety, kNewtonTol, kSwitchM, kMaxNewtonIters, nullptr, &k_cap,
                            &j_cap, x_low);
     if ((st = traced(kTrBound, true, s, [&] {
            return launch_root_bound(state, partial, P.partial_stride, sched, 0, P.n_newton, normalize, eps, k_cap,
-                                    all_f64 ? 1 : 0, x_low ? 1 : 0, s);
+                                    floor_cap, all_f64 ? 1 : 0, x_low ? 1 : 0, s);
          }, "root bound launch")) != MR_OK)
       return st;
     const int k_max = k_cap, j_max = all_f64 ? k_cap : j_cap;

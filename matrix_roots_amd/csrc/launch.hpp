@@ -260,7 +260,7 @@ hipError_t launch_x3_apply(const X3ApplyBatch& b, hipStream_t s);
 hipError_t launch_root_stats(const RootBatch& b, hipStream_t s);
 hipError_t launch_root_bound(RootState* state, const double* partial, int64_t partial_stride, double* sched,
                              int32_t slot_begin, int32_t nslots, int32_t normalize, double eps,
-                             int32_t k_cap, int32_t all_f64, int32_t finish, hipStream_t s);
+                             int32_t k_cap, double floor_cap, int32_t all_f64, int32_t finish, hipStream_t s);
 hipError_t launch_root_init(const RootBatch& b, hipStream_t s);
 enum StageKind { kStageF64 = 0, kStageF32 = 1, kStageX3 = 2, kStageX3B64 = 3 };
 hipError_t launch_newton_stage(const NewtonLaunch& L, int kind, int vec, hipStream_t s);

@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256) void root_stats_kernel(const RootBatch B) {
 __global__ __launch_bounds__(64) void root_bound_kernel(RootState* state, const double* partial,
                                                         int64_t stride, double* sched, int32_t slot_begin,
                                                         int32_t normalize, double eps, int32_t k_cap,
-                                                        int32_t all_f64, int32_t finish) {
+                                                        double floor_cap, int32_t all_f64, int32_t finish) {
   __shared__ double red[64];
   const int slot = slot_begin + blockIdx.x;
   RootState& st = state[slot];
@@ -269,17 +269,17 @@ __global__ __launch_bounds__(64) void root_bound_kernel(RootState* state, const 
         flags |= MR_INFO_NOT_PD;
         c = 1.0;
       } else {
-        const double floor = fmin(eps / c, 1.0 / kBoundSafety);
+        // The host launches the schedule of floor_cap: a matrix whose floor
+        // lies lower runs exactly that schedule (its steps and its float64
+        // steps are then those the host launches; both counts only fall as
+        // the floor rises) and is not iterated to convergence, and says so.
+        double floor = fmin(eps / c, 1.0 / kBoundSafety);
+        if (floor < floor_cap) {
+          floor = floor_cap;
+          flags |= MR_INFO_NOT_CONVERGED;
+        }
         newton_scaled_schedule(floor, 1.0 / kBoundSafety, kNewtonTol, kSwitchM, k_cap,
                                sched + (int64_t)slot * kMaxNewtonIters, &K, &j, finish != 0, &fin);
-        if (K == k_cap) {
-          // The host launches k_cap steps at most: a matrix whose own schedule
-          // needs more is not iterated to convergence, and says so.
-          int K2 = 0, j2 = 0, fin2 = 1;
-          newton_scaled_schedule(floor, 1.0 / kBoundSafety, kNewtonTol, kSwitchM, k_cap + 1, nullptr, &K2, &j2,
-                                 finish != 0, &fin2);
-          if (K2 > k_cap) flags |= MR_INFO_NOT_CONVERGED;
-        }
         if (all_f64) j = K;
       }
     }
@@ -772,10 +772,10 @@ hipError_t launch_root_stats(const RootBatch& b, hipStream_t s) {
 
 hipError_t launch_root_bound(RootState* state, const double* partial, int64_t partial_stride, double* sched,
                              int32_t slot_begin, int32_t nslots, int32_t normalize, double eps, int32_t k_cap,
-                             int32_t all_f64, int32_t finish, hipStream_t s) {
+                             double floor_cap, int32_t all_f64, int32_t finish, hipStream_t s) {
   if (nslots <= 0) return hipSuccess;
   hipLaunchKernelGGL(root_bound_kernel, dim3(nslots), dim3(64), 0, s, state, partial, partial_stride, sched,
-                     slot_begin, normalize, eps, k_cap, all_f64, finish);
+                     slot_begin, normalize, eps, k_cap, floor_cap, all_f64, finish);
   return hipGetLastError();
 }
 

@@ -213,14 +213,17 @@ def test_newton_schedule_converges_every_eigenvalue(lib):
 
 
 def test_newton_schedule_monotone_in_floor(lib):
-    """A larger eigenvalue floor never needs more steps: the host caps the
-    launch count with the schedule of the smallest floor it can see."""
+    """A larger eigenvalue floor never needs more steps, nor more float64
+    steps: the host launches the schedule of the smallest floor it covers
+    (and a matrix below it runs that schedule), so every matrix's steps and
+    float64 steps must fit under it."""
     prev = None
-    for m0 in np.geomspace(1e-14, 0.99, 400):
-        K = len(B.newton_schedule(float(m0))[0])  # with the finishing rule
+    for m0 in np.geomspace(1e-30, 0.99, 2000):
+        s, j = B.newton_schedule(float(m0))  # with the finishing rule
+        K = len(s)
         if prev is not None:
-            assert K <= prev, m0
-        prev = K
+            assert K <= prev[0] and j <= prev[1], (m0, K, j, prev)
+        prev = (K, j)
     # the scaled schedule beats the classical count (same tolerance)
     assert len(B.newton_schedule(1e-6)[0]) < lib.mr_newton_iterations(4, 1e-6, 1e-6)
 

@@ -323,3 +323,30 @@ def test_input_symmetric_part():
     X1, _ = oracle.inv_quarter_root(S, 1e-4)
     X2, _ = oracle.inv_quarter_root(S + 0.1 * K, 1e-4)
     np.testing.assert_allclose(X1, X2, rtol=1e-13, atol=1e-13)
+
+
+def test_coupled_iteration_fixed_point_is_stable():
+    """The coupled p = 4 step (X, M) -> (X T, T^4 M), T = (5I - M)/4, has
+    derivative zero in M at its fixed point M = I (the OKLS page, section
+    2.2, states this for the p = 2 member): from a converged pair with M
+    perturbed by delta E, M returns to I quadratically (delta^2 after one
+    step, far below after two) and X moves by O(delta) without growing."""
+    rng = np.random.default_rng(44)
+    d = 24
+    A = workloads.spd_loguniform(d, rng, -3.0, 0.0).astype(np.float64)
+    Xs, _ = oracle.inv_quarter_root(A, 0.0, "none")  # X* with X*^4 A = I
+    I = np.eye(d)
+    for delta in (1e-3, 1e-5):
+        E = rng.standard_normal((d, d))
+        E = (E + E.T) / (2 * np.linalg.norm(E + E.T) / 2)
+        M, X = I + delta * E, Xs.copy()
+        devs = []
+        for _ in range(3):
+            T = (5.0 * I - M) / 4.0
+            X = X @ T
+            T2 = T @ T
+            M = T2 @ T2 @ M
+            devs.append(np.linalg.norm(M - I))
+        assert devs[0] <= 4.0 * delta ** 2, (delta, devs)
+        assert devs[1] <= max(1e2 * delta ** 4, 1e-13), (delta, devs)
+        assert np.linalg.norm(X - Xs) <= 0.5 * delta * np.linalg.norm(Xs), delta
