@@ -244,19 +244,25 @@ def engine_table(kernels):
     return out
 
 
+# classes whose counters come from the optimizer-step run (their own source family)
+STEP_CLASSES = ("momentum", "hyperball_reduce", "hyperball_update")
+
+
 def roofline_for(kernels, name, workload):
     k = kernels[name]
+    traffic = (recorded_traffic(name, f"{workload}_step", "step") if name in STEP_CLASSES
+               else recorded_traffic(name, workload))
     if "tflops" in k:
         split = name in SPLIT_CLASSES
         r = {"bound": "mfma", "kernel": name, "engine": k["engine"],
              "achieved": k["mfma_tflops"] if split else k["tflops"], "peak": k["peak"], "unit": "TFLOP/s",
-             "frac": k["frac"], "traffic": recorded_traffic(name, workload),
+             "frac": k["frac"], "traffic": traffic,
              "traffic_per": "working launch (calibrated FETCH_SIZE + WRITE_SIZE, profiles/)",
              "achieved_per_launch": "algorithmic flops of the class over the timed steps (x3 fp16 products for "
                                     "split classes) / sum of its event-measured launch durations"}
     else:
         r = {"bound": "hbm", "kernel": name, "achieved": k["gb_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-             "frac": k["hbm_frac"], "traffic": recorded_traffic(name, workload),
+             "frac": k["hbm_frac"], "traffic": traffic,
              "traffic_per": "working launch (calibrated FETCH_SIZE + WRITE_SIZE, profiles/)",
              "achieved_per_launch": "algorithmic bytes of the class over the timed steps / sum of its "
                                     "event-measured launch durations"}
