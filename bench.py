@@ -431,6 +431,12 @@ def bench_steps(args, torch, B, W, peaks):
                     else n * n) for m, n in shapes)
         kernels["syrk_ema"]["hbm_bytes_per_step"] = 2 * es * st_el + 2 * 4 * sum(m * n for m, n in shapes)
     engines = engine_table(kernels)
+    vend = peaks.get("vendor_gemm_tflops")
+    if vend:
+        for eng, e in engines.items():
+            if eng in vend:
+                e["vendor_gemm_tflops"] = vend[eng]
+                e["frac_of_vendor_gemm"] = round(e["mfma_tflops"] / vend[eng], 4)
     dname = max((kv for kv in kernels.items() if "tflops" in kv[1]), key=lambda kv: kv[1]["ms_total"])[0]
     roofline = roofline_for(kernels, dname, args.workload)
     rooflines = {n: roofline_for(kernels, n, args.workload) for n in kernels
@@ -828,6 +834,34 @@ def calibration_copies(torch, dev, mib):
     log(f"calibration copies of {mib} MiB done")
 
 
+def vendor_gemm(torch, dev):
+    """torch.matmul (hipBLASLt / rocBLAS) on the shape of the width-1024 set's
+    4096 x 4096 Grams, full products, contiguous operands: what the vendor
+    library sustains on this device with real data, as context for the
+    hand-written kernels' rates (which count symmetric products as d^2 (d+1))."""
+    out = {"shape": "batch 16 (fp16) / 4 (fp64) of 4096 x 4096 x 4096, C = A B, flops 2 m n k"}
+    for name, dt, b, reps in (("f16", torch.float16, 16, 10), ("f64", torch.float64, 4, 4)):
+        g = torch.Generator(device=dev)
+        g.manual_seed(0)
+        A = torch.randn(b, 4096, 4096, device=dev, dtype=dt, generator=g)
+        Bm = torch.randn(b, 4096, 4096, device=dev, dtype=dt, generator=g)
+        C = torch.empty_like(A)
+        for _ in range(2):
+            torch.matmul(A, Bm, out=C)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(A, Bm, out=C)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = round(2.0 * b * 4096 ** 3 / (ms / 1e3) / 1e12, 1)
+        del A, Bm, C
+    torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -854,6 +888,8 @@ def main(argv=None) -> int:
                          "(default 3; 1 for w2048)")
     ap.add_argument("--no-size-classes", dest="size_classes", action="store_false",
                     help="skip the per-size-class root calls on the final state")
+    ap.add_argument("--no-vendor-gemm", dest="vendor_gemm", action="store_false",
+                    help="skip timing torch.matmul (the vendor GEMM) on the 4096^3 shape as context")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run a plain device copy of this many MiB 3 times first (counter calibration)")
     args = ap.parse_args(argv)
@@ -879,6 +915,8 @@ def main(argv=None) -> int:
     # roofline fractions use)
     peaks = B.measure_peaks()
     peaks["published_tflops"] = dict(PEAK_TFLOPS)
+    if args.vendor_gemm:
+        peaks["vendor_gemm_tflops"] = vendor_gemm(torch, dev)
     log(f"peaks: {peaks}")
     if args.calibration_copy_mib > 0:
         calibration_copies(torch, dev, args.calibration_copy_mib)
