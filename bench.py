@@ -369,8 +369,8 @@ def bench_steps(args, torch, B, W, peaks):
         if args.optimizer_step:
             B.momentum_ema_batched(G, Ms, 0.9)
         B.gram_ema_update(G, Ls, Rs, wl.beta)
-        B.inv_quarter_root_batched(Ls + Rs, wl.eps, normalize=wl.normalize, Xs=Xs, workspace=ws,
-                                   return_info=False, info_out=info_buf)
+        B.inv_quarter_root_batched(Ls + Rs, wl.eps, normalize=wl.normalize, method=args.method, Xs=Xs,
+                                   workspace=ws, return_info=False, info_out=info_buf)
         B.precondition_apply(Xs[:nw], Ms if args.optimizer_step else G, Xs[nw:], Us=Us)
         if args.optimizer_step:
             B.hyperball_update_batched(Wts, Us, 0.02)
@@ -506,7 +506,7 @@ def bench_steps(args, torch, B, W, peaks):
                    "shapes": sorted({f"{m}x{n}" for m, n in shapes}), "beta": wl.beta, "eps": wl.eps,
                    "normalize": wl.normalize, "state_dtype": args.state_dtype, "gradients": gen,
                    "state_layout": "packed" if args.packed_state else "full", "state_gb": round(state_bytes / 1e9, 3),
-                   "optimizer_step": bool(args.optimizer_step)},
+                   "optimizer_step": bool(args.optimizer_step), "method": args.method},
         "tflops": round(tf_step, 2),
         "pct_fp32_mfma_peak": round(100 * tf_step / PEAK_TFLOPS["f32"], 2),
         "pct_fp32_mfma_peak_note": "the metric's headline: float32-accurate algorithmic TFLOP/s of the whole step "
@@ -888,6 +888,8 @@ def main(argv=None) -> int:
                          "(default 3; 1 for w2048)")
     ap.add_argument("--no-size-classes", dest="size_classes", action="store_false",
                     help="skip the per-size-class root calls on the final state")
+    ap.add_argument("--method", default="auto", choices=["auto", "jacobi", "newton"],
+                    help="root method of the step's root call (auto: Jacobi for d <= 32, else Newton)")
     ap.add_argument("--no-vendor-gemm", dest="vendor_gemm", action="store_false",
                     help="skip timing torch.matmul (the vendor GEMM) on the 4096^3 shape as context")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,

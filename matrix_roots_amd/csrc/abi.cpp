@@ -116,6 +116,11 @@ mr_status check_launch(hipError_t e, hipStream_t s, const char* what) {
 }
 
 int tiles(int64_t d, int t) { return (int)((d + t - 1) / t); }
+// workgroups of the upper tile pairs (upper_pair) of a d x d matrix
+int upper_tiles(int64_t d, int t) {
+  const int T = tiles(d, t);
+  return T * (T + 1) / 2;
+}
 
 // ------------------------------------------------------------ tracing
 enum TraceClass {
@@ -868,7 +873,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
           if (kind == 0)
             J.nblocks = tiles(q.d, kStatsRows);
           else if (kind == 1)
-            J.nblocks = tiles(q.d, 32) * tiles(q.d, 32);
+            J.nblocks = upper_tiles(q.d, 32);
           else
             J.nblocks = tiles(q.d, kFinalRows);
           b.total_blocks += J.nblocks;
@@ -1190,8 +1195,7 @@ mr_status inv_sqrt_root_batched(const mr_root_problem* p, int32_t count, mr_dtyp
         J.slot = slot;
         J.problem = P.slot_problem[slot];
         J.block_begin = b.total_blocks;
-        J.nblocks = kind == 0 ? tiles(q.d, kStatsRows) : kind == 1 ? tiles(q.d, 32) * tiles(q.d, 32)
-                                                                   : tiles(q.d, kFinalRows);
+        J.nblocks = kind == 0 ? tiles(q.d, kStatsRows) : kind == 1 ? upper_tiles(q.d, 32) : tiles(q.d, kFinalRows);
         b.total_blocks += J.nblocks;
         ++b.njobs;
         if (b.njobs == kMaxRootJobs || slot == count - 1) {

@@ -144,23 +144,27 @@ __global__ __launch_bounds__(256) void cans_init_kernel(const RootBatch B, doubl
   if (st.K == 0) return;
   const int d = J.d;
   const int Tt = (d + 31) / 32;
-  const int tile = (int)(b - J.block_begin);
-  const int bi = tile / Tt, bj = tile % Tt;
+  int bi, bj;
+  upper_pair((int)(b - J.block_begin), Tt, bi, bj);
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  load_sym_tile<TA>(J.A, J.lda, d, B.a_packed != 0, bi, bj, ta, tb);
+  const bool packed = B.a_packed != 0;
+  load_sym_tile<TA>(J.A, J.lda, d, packed, bi, bj, ta, tb);
   const double inv_s = 1.0 / st.s, inv_L = 1.0 / st.c, eps = B.eps;
   const Split Y = cans_buf(J.region, d, buf_y(0));
   const Split Z = cans_buf(J.region, d, buf_z(1));
+  auto put_yz = [&](int gi, int gj, double sym) __attribute__((always_inline)) {
+    const double y0 = (sym * inv_s + (gi == gj ? eps : 0.0)) * inv_L;
+    const int64_t i = (int64_t)gi * d + gj;
+    put(Y, i, (float)(sy0 * y0));
+    put(Z, i, (float)(zb * y0 + (gi == gj ? za : 0.0)));
+  };
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int r = ty + 8 * e;
-    const int gi = bi * 32 + r, gj = bj * 32 + tx;
-    if (gi < d && gj < d) {
-      const double y0 = (sym_tile_value(B.a_packed != 0, bi, bj, r, tx, ta, tb) * inv_s + (gi == gj ? eps : 0.0)) * inv_L;
-      const int64_t i = (int64_t)gi * d + gj;
-      put(Y, i, (float)(sy0 * y0));
-      put(Z, i, (float)(zb * y0 + (gi == gj ? za : 0.0)));
-    }
+    // tile (bi, bj), then its mirror (bj, bi) from the same LDS tiles
+    if (bi * 32 + r < d && bj * 32 + tx < d) put_yz(bi * 32 + r, bj * 32 + tx, sym_tile_value(packed, bi, bj, r, tx, ta, tb));
+    if (bi != bj && bj * 32 + r < d && bi * 32 + tx < d)
+      put_yz(bj * 32 + r, bi * 32 + tx, sym_tile_value(packed, bi, bj, tx, r, ta, tb));
   }
 }
 

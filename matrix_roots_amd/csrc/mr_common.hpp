@@ -132,6 +132,21 @@ __device__ __forceinline__ void load_sym_tile(const void* A, int64_t lda, int d,
   }
   __syncthreads();
 }
+// Tile pair u of the upper triangle of a T x T grid of tiles, row by row:
+// (bi, bj) with bi <= bj, row i holding T - i pairs (the first at
+// i T - i (i - 1) / 2).  A workgroup that owns the pair reads tiles (bi, bj)
+// and (bj, bi) once and writes both.
+__host__ __device__ __forceinline__ void upper_pair(int u, int T, int& bi, int& bj) {
+  auto first = [T](int k) { return k * T - k * (k - 1) / 2; };
+  const double b = 2.0 * T + 1.0;
+  int i = (int)(0.5 * (b - sqrt(b * b - 8.0 * u)));
+  if (i < 0) i = 0;
+  while (i > 0 && first(i) > u) --i;
+  while (first(i + 1) <= u) ++i;
+  bi = i;
+  bj = i + (u - first(i));
+}
+
 // Element (r, c) of the tile loaded by load_sym_tile.
 __device__ __forceinline__ double sym_tile_value(bool packed, int bi, int bj, int r, int c, const double (*ta)[33],
                                                  const double (*tb)[33]) {
@@ -186,7 +201,7 @@ constexpr int kTileGroup = 8;
 
 // Tile u of the upper triangle (ti <= tj) of a T x T grid, in bands of
 // kTileGroup tile rows, each band column by column.
-__device__ __forceinline__ void upper_tile_grouped(int u, int T, int& ti, int& tj) {
+__host__ __device__ __forceinline__ void upper_tile_grouped(int u, int T, int& ti, int& tj) {
   constexpr int G = kTileGroup;
   int b0 = 0;
   while (true) {

@@ -308,10 +308,11 @@ __global__ __launch_bounds__(256) void root_init_kernel(const RootBatch B) {
   if (st.K == 0) return;
   const int d = J.d;
   const int Tt = (d + 31) / 32;
-  const int tile = (int)(b - J.block_begin);
-  const int bi = tile / Tt, bj = tile % Tt;
+  int bi, bj;
+  upper_pair((int)(b - J.block_begin), Tt, bi, bj);
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  load_sym_tile<TA>(J.A, J.lda, d, B.a_packed != 0, bi, bj, ta, tb);
+  const bool packed = B.a_packed != 0;
+  load_sym_tile<TA>(J.A, J.lda, d, packed, bi, bj, ta, tb);
   const double inv_s = 1.0 / st.s, inv_c = 1.0 / st.c, eps = B.eps;
   double* M = reinterpret_cast<double*>(J.region);
   double* X = reinterpret_cast<double*>(J.region + (int64_t)d * d * 8);
@@ -320,22 +321,24 @@ __global__ __launch_bounds__(256) void root_init_kernel(const RootBatch B) {
   const float xs = B.x_low ? x_store_scale(st) : 1.0f;
   const double s0 = B.x_low ? B.sched[(int64_t)J.slot * kMaxNewtonIters] : 1.0;
   const double q0 = (double)xs * pow(s0, -0.25), inv_s0 = 1.0 / s0;
+  auto put = [&](int gi, int gj, double sym) __attribute__((always_inline)) {
+    const double v = (sym * inv_s + (gi == gj ? eps : 0.0)) * inv_c;
+    const int64_t e = (int64_t)gi * d + gj;
+    M[e] = v;
+    if (B.x_low) {
+      split_put(rs.Mx, e, (float)v);
+      split_put(x1, e, (float)(q0 * ((gi == gj ? 1.25 : 0.0) - 0.25 * v * inv_s0)));
+    } else {
+      X[e] = (gi == gj) ? 1.0 : 0.0;
+    }
+  };
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int r = ty + 8 * e;
-    const int gi = bi * 32 + r, gj = bj * 32 + tx;
-    if (gi < d && gj < d) {
-      const double sym = sym_tile_value(B.a_packed != 0, bi, bj, r, tx, ta, tb);
-      const double v = (sym * inv_s + (gi == gj ? eps : 0.0)) * inv_c;
-      const int64_t e = (int64_t)gi * d + gj;
-      M[e] = v;
-      if (B.x_low) {
-        split_put(rs.Mx, e, (float)v);
-        split_put(x1, e, (float)(q0 * ((gi == gj ? 1.25 : 0.0) - 0.25 * v * inv_s0)));
-      } else {
-        X[e] = (gi == gj) ? 1.0 : 0.0;
-      }
-    }
+    // tile (bi, bj), then its mirror (bj, bi) from the same LDS tiles
+    if (bi * 32 + r < d && bj * 32 + tx < d) put(bi * 32 + r, bj * 32 + tx, sym_tile_value(packed, bi, bj, r, tx, ta, tb));
+    if (bi != bj && bj * 32 + r < d && bi * 32 + tx < d)
+      put(bj * 32 + r, bi * 32 + tx, sym_tile_value(packed, bi, bj, tx, r, ta, tb));
   }
 }
 
