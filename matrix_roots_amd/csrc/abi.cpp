@@ -918,7 +918,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
     // Class groups: at most kMaxClasses per launch, split by vector width.
     // vec64: float64 loads of 2 (d even); vec32: float32 loads of 4 (d % 4 == 0);
     // vecx3: fp16 loads of 8 (d % 8 == 0).
-    // wide: d % 32 == 0, the split-fp16 stages run on 256 x 256 tiles.
+    // wide: d % 32 == 0 and d >= kWideMinD, the split-fp16 stages run on 256 x 256 tiles.
     struct Group {
       std::vector<int> cls;
       int vec64, vec32, vecx3;
@@ -933,7 +933,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
       g.wide = align == 32;  // split-fp16 stages on 256 x 256 tiles
       for (int ci = 0; ci < (int)P.classes.size(); ++ci) {
         const int64_t d = P.classes[ci].d;
-        const int a = d % 32 == 0 ? 32 : d % 8 == 0 ? 8 : d % 4 == 0 ? 4 : d % 2 == 0 ? 2 : 1;
+        const int a = d % 32 == 0 && d >= kWideMinD ? 32 : d % 8 == 0 ? 8 : d % 4 == 0 ? 4 : d % 2 == 0 ? 2 : 1;
         if (a != align) continue;
         g.cls.push_back(ci);
         if ((int)g.cls.size() == kMaxClasses) {

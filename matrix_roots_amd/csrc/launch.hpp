@@ -24,6 +24,16 @@ constexpr int kJacobiMaxD = 128;
 // d <= 32 (4 to 256 matrices per call) and slower above (d = 48: 0.92 against
 // 0.53 ms for 4 matrices; d = 128: 9.3 against 1.1 ms).
 constexpr int kJacobiAutoMaxD = 32;
+// Smallest Gram size whose split-fp16 Newton stages take the 256 x 256 tile
+// (d a multiple of 32).  Smaller Grams take the 128 x 128 direct-to-LDS tile
+// (two workgroups per CU): a d = 128 Gram fills it instead of a quarter of
+// the wide one, and the more numerous tiles balance better.  Measured on
+// MI355X, one root call: 4 x 128^2 1.41 -> 1.03 ms, 64 x 256^2 1.97 -> 1.52
+// ms, 256 x 512^2 12.6 -> 12.2 ms.  In whole weight sets the wide tile's
+// fewer operand re-reads win from d = 1536 (128 x 1536^2 + 128 x 3072^2:
+// 716 against 759 ms with narrow tiles; 80 x 1024^2 + 16 x 4096^2: 199
+// against 208), and the 1024^2 class takes either at the same speed.
+constexpr int kWideMinD = 1024;
 constexpr int kJacobiDefaultSweeps = 30;
 constexpr int kJacobiMaxSweeps = 100;
 constexpr int kStatsRows = 32;       // rows of A per statistics workgroup (one 32-row tile stripe)
