@@ -379,20 +379,43 @@ def bench_steps(args, torch, B, W, peaks):
         step(i, infos[i])
         torch.cuda.synchronize()
         log(f"warmup step {i + 1}/{args.warmup} done")
-    B.trace_collect()
-    B.trace_enable(True)
+
+    graphs = None
+    if args.graph:
+        # one HIP graph per gradient of the cycle (each bakes in its buffers);
+        # the entry points only enqueue kernels, so they capture as they run
+        graphs = []
+        for k in range(wl.steps):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                step(k, infos[args.warmup + k] if args.warmup + k < total else infos[-1])
+            graphs.append(gr)
+        torch.cuda.synchronize()
+        log(f"captured {len(graphs)} step graphs")
+
+    # the timed region: exactly --steps steps, no per-launch events
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.warmup, total):
-        step(i, infos[i])
+        if graphs is not None:
+            graphs[i % wl.steps].replay()
+        else:
+            step(i, infos[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    B.trace_enable(False)
-    trace = B.trace_collect()
-    log(f"timed {args.steps} steps in {t1 - t0:.3f}s")
-
+    log(f"timed {args.steps} steps in {t1 - t0:.3f}s{' (graph replays)' if graphs is not None else ''}")
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = nw / (ms_per_step / 1e3)
+
+    # the same number of steps again, each launch bracketed by events on its
+    # stream: per-class durations for the rooflines (the state keeps evolving)
+    B.trace_collect()
+    B.trace_enable(True)
+    for i in range(args.warmup, total):
+        step(i, infos[i])
+    torch.cuda.synchronize()
+    B.trace_enable(False)
+    trace = B.trace_collect()
 
     # algorithmic work and bytes over the timed steps
     es = 8 if args.state_dtype == "f64" else 4
@@ -506,7 +529,8 @@ def bench_steps(args, torch, B, W, peaks):
                    "shapes": sorted({f"{m}x{n}" for m, n in shapes}), "beta": wl.beta, "eps": wl.eps,
                    "normalize": wl.normalize, "state_dtype": args.state_dtype, "gradients": gen,
                    "state_layout": "packed" if args.packed_state else "full", "state_gb": round(state_bytes / 1e9, 3),
-                   "optimizer_step": bool(args.optimizer_step), "method": args.method},
+                   "optimizer_step": bool(args.optimizer_step), "method": args.method,
+                   "timing": "HIP graph replays" if args.graph else "eager launches"},
         "tflops": round(tf_step, 2),
         "pct_fp32_mfma_peak": round(100 * tf_step / PEAK_TFLOPS["f32"], 2),
         "pct_fp32_mfma_peak_note": "the metric's headline: float32-accurate algorithmic TFLOP/s of the whole step "
@@ -888,6 +912,8 @@ def main(argv=None) -> int:
                          "(default 3; 1 for w2048)")
     ap.add_argument("--no-size-classes", dest="size_classes", action="store_false",
                     help="skip the per-size-class root calls on the final state")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as HIP graph replays (one captured graph per gradient of the cycle)")
     ap.add_argument("--method", default="auto", choices=["auto", "jacobi", "newton"],
                     help="root method of the step's root call (auto: Jacobi for d <= 32, else Newton)")
     ap.add_argument("--no-vendor-gemm", dest="vendor_gemm", action="store_false",
