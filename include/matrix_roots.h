@@ -20,7 +20,10 @@
  *    library keeps no pointer after returning and allocates nothing on the
  *    device.  All work is enqueued on `hip_stream` (a hipStream_t passed as
  *    void*; NULL = the null stream); nothing is waited for, except where an
- *    entry point says so.
+ *    entry point says so.  The enqueued work is kernel launches only (no
+ *    copies or memsets; events only while mr_trace_enable is on), so a
+ *    sequence of calls can be captured in a HIP graph and replayed on the
+ *    same buffers.
  *  - Validation is all-or-nothing and happens before anything is enqueued:
  *    on an error status nothing was enqueued and mr_last_error_message()
  *    (thread-local) says what was wrong.
