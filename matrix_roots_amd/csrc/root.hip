@@ -451,10 +451,95 @@ __device__ __forceinline__ void sym_store(const StageOps<T>& o, int d, int gr, i
   }
 }
 
+// Float64 epilogue of a whole 128 x 128 tile (d even).  A lane of a 16 x 16
+// float64 MFMA block holds one column and four rows, so the upper elements go
+// straight from the accumulators (16 lanes write 128 consecutive bytes of a
+// row), while their mirror would be 8-byte stores d * 8 bytes apart.  Each
+// wave therefore also puts its values, 32 rows at a time, into a private LDS
+// slab and writes columns of it as rows of the mirror, 8 values (64 bytes) per
+// lane.  plain: C = alpha acc (stage 2 of a float64 step, which also writes the
+// split copy mx of C); else C = alpha acc + beta Cin (+ gamma on the
+// diagonal), the values of sym_store.  diag: a tile on the diagonal (r <= c
+// stored, r < c mirrored).  The main loop ended with a block barrier, so the
+// operand stages are free.
+constexpr int kF64SlabLd = 64 + 2;  // doubles per slab row
+__device__ __forceinline__ void f64_store_tile(const v4d (&acc)[4][4], double* lds, int d, int m0, int n0,
+                                               const StageOps<double>& o, bool plain, const SplitBuf& mx, bool diag) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  double* slab = lds + wave * 32 * kF64SlabLd;
+  const bool mx_vec = d % 8 == 0;  // 16-byte split stores of 8 halves
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int rb2 = 0; rb2 < 2; ++rb2)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int lr = rb2 * 16 + f64_row(lane, v), lc = cb * 16 + (lane & 15);
+          const int gr = m0 + wm * 64 + h * 32 + lr, gc = n0 + wn * 64 + lc;
+          const int64_t e = (int64_t)gr * d + gc;
+          double val = o.alpha * acc[2 * h + rb2][cb][v];
+          if (!plain) {
+            if (o.Cin) val += o.beta * o.Cin[e];
+            if (gr == gc) val += o.gamma;
+          }
+          if (!diag || gr <= gc) {
+            o.C[e] = val;
+            if (plain) split_put(mx, e, (float)val);
+          }
+          slab[lr * kF64SlabLd + lc] = val;
+        }
+    slab_fence();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = lane + 64 * i;
+      const int c = q >> 2, rg = q & 3;  // slab column, group of 8 rows
+      const int gc = n0 + wn * 64 + c, gr0 = m0 + wm * 64 + h * 32 + rg * 8;
+      if (diag && gr0 >= gc) continue;  // no element of the group above the diagonal
+      double v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = slab[(rg * 8 + e) * kF64SlabLd + c];
+      const int64_t t = (int64_t)gc * d + gr0;  // mirror: C[gc][gr0 + e] = value at (gr0 + e, gc)
+      if (!diag || gr0 + 7 < gc) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) *reinterpret_cast<v2d*>(o.C + t + e) = v2d{v[e], v[e + 1]};
+        if (plain) {
+          if (mx_vec) {
+            v8h hh, ll;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              _Float16 a, b;
+              split_f32((float)v[e], a, b);
+              hh[e] = a;
+              ll[e] = b;
+            }
+            *reinterpret_cast<v8h*>(mx.hi + t) = hh;
+            *reinterpret_cast<v8h*>(mx.lo + t) = ll;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) split_put(mx, t + e, (float)v[e]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (gr0 + e < gc) {
+            o.C[t + e] = v[e];
+            if (plain) split_put(mx, t + e, (float)v[e]);
+          }
+      }
+    }
+    slab_fence();
+  }
+}
+
 template <int VEC>
 __global__ __launch_bounds__(256, VEC == 2 ? kF64Occupancy : 1) void newton_f64_kernel(const NewtonLaunch L) {
   // (with x_low, stage 2 also writes the split copy Mx of the new M)
   __shared__ __attribute__((aligned(16))) double smem[F64Tile::LDS_DOUBLES];
+  static_assert(4 * 32 * kF64SlabLd <= F64Tile::LDS_DOUBLES, "four 32-row slabs fit in the operand stages");
   const StageJob s = stage_job(L, kStageF64);
   if (!s.active) return;
   const Roles64 r = roles64(s.region, s.d, L.t);
@@ -463,8 +548,13 @@ __global__ __launch_bounds__(256, VEC == 2 ? kF64Occupancy : 1) void newton_f64_
   v4d acc[4][4];
   f64_nt_tile_auto<VEC>(o.A, s.d, o.B, s.d, s.d, s.d, s.d, m0, n0, smem, acc);
   const int d = s.d;
-  if (L.x_low && L.stage == 2) {
-    const SplitBuf mx = roless(s.region, d, L.t).Mx;
+  const bool plain = L.x_low && L.stage == 2;
+  const SplitBuf mx = roless(s.region, d, L.t).Mx;
+  // (Grams below 256 keep the element stores: their tiles are latency-bound,
+  // and the slab passes cost more than the scattered mirror stores there)
+  if (VEC == 2 && d >= 256 && m0 + F64Tile::BM <= d && n0 + F64Tile::BN <= d) {
+    f64_store_tile(acc, smem, d, m0, n0, o, plain, mx, s.ti == s.tj);
+  } else if (plain) {
     f64_for_each(acc, [&](int rr, int cc, double v) {
       const int gr = m0 + rr, gc = n0 + cc;
       if (gr < d && gc < d && gr <= gc) {
