@@ -381,3 +381,20 @@ def test_aliasing_across_problems_is_rejected(lib):
     assert lib.momentum_ema_batched(ctypes.addressof(arr), 2, 0.9, None) == 8
     arr = (B.HyperballProblem * 2)(B.HyperballProblem(4, 8, P1, 8, P2, 8), B.HyperballProblem(4, 8, P2, 8, P3, 8))
     assert lib.hyperball_update_batched(ctypes.addressof(arr), 2, 0.1, None, None, 0, None) == 8
+
+
+def test_empty_batches_are_no_ops(lib):
+    """count = 0 returns MR_OK without touching the device (NULL arrays
+    allowed); a negative count is a parameter error."""
+    assert lib.inv_quarter_root_batched(None, 0, B.MR_F32, 1e-6, B.MR_NORM_TRACE, B.MR_AUTO, None, None, 0, None) == 0
+    assert lib.inv_quarter_root_batched_workspace(None, 0, B.MR_F32, B.MR_AUTO) == 0
+    assert lib.inv_quarter_root_batched_noalloc(None, 0, B.MR_F32, 1e-6, B.MR_NORM_TRACE, B.MR_AUTO, None,
+                                                None) == 0
+    assert lib.precondition_apply(None, 0, 1.0, None, 0, None) == 0
+    assert lib.precondition_apply_workspace(None, 0) == 0
+    assert lib.inv_sqrt_root_batched(None, 0, B.MR_F32, 1e-3, 0, 0, None, None, 0, None) == 0
+    assert lib.polar_cans_batched(None, 0, 0, None, None, 0, None) == 0
+    assert lib.momentum_ema_batched(None, 0, 0.9, None) == 0
+    assert lib.hyperball_update_batched(None, 0, 0.1, None, None, 0, None) == 0
+    assert lib.inv_quarter_root_batched(None, -1, B.MR_F32, 1e-6, B.MR_NORM_TRACE, B.MR_AUTO, None, None, 0,
+                                        None) == 4
