@@ -59,6 +59,19 @@ def host_cores():
     return cores, blas
 
 
+def blas_vendor() -> str:
+    """The BLAS/LAPACK library numpy's oracle runs on (name and version)."""
+    try:
+        import threadpoolctl
+
+        libs = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            return f"{libs[0].get('internal_api', '?')} {libs[0].get('version', '?')}"
+    except Exception:  # pragma: no cover
+        pass
+    return "unknown"
+
+
 def sym_gemm_flops(d: int) -> float:
     """One symmetric-output product of d x d matrices: d(d+1)/2 outputs x d MACs x 2."""
     return float(d) * d * (d + 1)
@@ -149,7 +162,7 @@ def cpu_baseline(workload: str, max_seconds: float = 30.0):
     sample = (f"one weight per shape class runs its own steps from zero state ({shown}); "
               f"per-step seconds weighted by the workload's {len(wl.shapes)} weights; fp64 numpy/LAPACK")
     return {"value": len(wl.shapes) / step_seconds, "unit": "matrix updates/s", "cores": blas,
-            "host_cores": cores, "kind": "oracle", "sample": sample, "seconds": round(total, 2),
+            "host_cores": cores, "kind": "oracle", "blas": blas_vendor(), "sample": sample, "seconds": round(total, 2),
             "seconds_per_optimizer_step": round(step_seconds, 3)}
 
 
@@ -167,7 +180,7 @@ def cpu_baseline_illcond(mats, eps_list, max_seconds: float = 20.0):
         oracle.inv_quarter_root(A, eps, "none")
         secs += time.perf_counter() - t0
         roots += 1
-    return {"value": roots / secs, "unit": "roots/s", "cores": blas, "host_cores": cores, "kind": "oracle",
+    return {"value": roots / secs, "unit": "roots/s", "cores": blas, "host_cores": cores, "kind": "oracle", "blas": blas_vendor(),
             "sample": f"the first {roots} 512x512 roots of the batch (eigh, fp64 numpy/LAPACK, eps 1e-8 first)",
             "seconds": round(secs, 2)}
 
@@ -723,7 +736,7 @@ def bench_cans(args, torch, B, peaks):
         c0 = time.perf_counter()
         oracle.inv_sqrt_root(A0, eps, "none")
         sec = time.perf_counter() - c0
-        cpu = {"value": round(1.0 / sec, 5), "unit": "roots/s", "cores": cores, "host_cores": host, "kind": "oracle",
+        cpu = {"value": round(1.0 / sec, 5), "unit": "roots/s", "cores": cores, "host_cores": host, "kind": "oracle", "blas": blas_vendor(),
                "sample": "one 8192 x 8192 root of the batch (eigh, fp64 numpy/LAPACK)", "seconds": round(sec, 2)}
         log(f"oracle: {sec:.1f}s per root on {cores} threads")
     out = {
@@ -820,7 +833,7 @@ def bench_polar(args, torch, B, peaks):
             for g in sample:
                 oracle.polar_cans(g)
         sec = (time.perf_counter() - c0) / 8
-        cpu = {"value": round(1.0 / sec, 4), "unit": "matrices/s", "cores": cores, "host_cores": host, "kind": "oracle",
+        cpu = {"value": round(1.0 / sec, 4), "unit": "matrices/s", "cores": cores, "host_cores": host, "kind": "oracle", "blas": blas_vendor(),
                "sample": "E0.in (3072x1536) and E63.out (1536x3072), 4 times each (thin SVD, fp64 numpy/LAPACK)",
                "seconds": round(8 * sec, 2)}
         log(f"oracle: {sec:.2f}s per matrix on {cores} threads")
