@@ -293,8 +293,9 @@ __global__ __launch_bounds__(64) void root_bound_kernel(RootState* state, const 
   st.flags = flags;
 }
 
-// M0 = ((A + A^T)/2 / s + eps I) / c into S0 (float64), 32 x 32 tiles
-// through LDS so both A reads are coalesced.  X: with split storage the
+// M0 = ((A + A^T)/2 / s + eps I) / c into S0 (float64), one workgroup per
+// pair of mirrored 32 x 32 tiles (upper_pair), both read once through LDS so
+// every A read and write is coalesced.  X: with split storage the
 // first X update needs no product (X0 = I, so X1 = s0^(-1/4) (5 I - M0/s0) / 4)
 // and is written here, in the buffer iteration 1 reads; otherwise X0 = I
 // into S1 (float64) for the first step's product.
@@ -697,7 +698,7 @@ __global__ __launch_bounds__(256, 2) void newton_x3_kernel(const NewtonLaunch L,
 // the float64 steps' M <= 1), or in a finishing step R (in [0.15, 0.17]) or
 // q(M) (in [1, 1.03]), so every |B| < 2 and the 2^11 scaling of B's hi half
 // stays far inside fp16's range.  The host picks this kernel for
-// classes with d a multiple of 32 (whole 32-deep chunks).
+// classes with d a multiple of 32 (whole 32-deep chunks) and d >= kWideMinD.
 __global__ __launch_bounds__(X3W::THREADS, 1) void newton_x3w_kernel(const NewtonLaunch L, int kind) {
   constexpr int kSmem = X3W::LDS_BYTES > 8 * kSlabFloats * 4 ? X3W::LDS_BYTES : 8 * kSlabFloats * 4;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
