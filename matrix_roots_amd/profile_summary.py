@@ -38,11 +38,38 @@ KERNEL_SOURCES = {
 }
 
 
+def code_only(text: str) -> str:
+    """C++ source without its comments, whitespace runs collapsed to one
+    space (string and character literals kept as written): what the compiler
+    sees, so that editing a comment does not change a source hash."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        ch = text[i]
+        if ch in "\"'":
+            j = i + 1
+            while j < n and text[j] != ch:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(ch)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def sources_sha256(family: str = "quarter") -> str:
+    """sha256 over the family's sources, comments and layout left out."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[family]:
-        with open(os.path.join(HERE, rel), "rb") as f:
-            h.update(rel.encode() + b"\0" + f.read())
+        with open(os.path.join(HERE, rel), encoding="utf-8") as f:
+            h.update(rel.encode() + b"\0" + code_only(f.read()).encode())
     return h.hexdigest()
 
 
