@@ -44,3 +44,8 @@ def test_root_stream_bytes():
     bp = bench.root_stream_bytes(d, 8, True, 2, 5)  # packed state, every step float64
     assert bp["root_stats"] == 8 * (d * (d + 1) // 2) and bp["newton_convert"] == 0
     assert bp["root_finalize"] == (4 + 8 + 4) * n
+
+
+def test_bench_refuses_more_than_one_gpu(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU only" in capsys.readouterr().err
