@@ -121,13 +121,15 @@ def test_newton_root_matches_oracle(torch_dev, method, a_dtype):
 
 
 def test_newton_wide_tiles_ragged(torch_dev):
-    """Sizes that are multiples of 32 take the split-fp16 stages on 256 x 256
-    tiles: one partial tile (160), a whole diagonal tile plus a 32-row strip
-    (288), two and three tile rows with ragged last rows (544, 800); 264 and
-    200 (multiples of 8, not of 32) share the call and take 128 x 128 tiles."""
+    """Multiples of 32 from d = 1024 take the split-fp16 stages on 256 x 256
+    tiles: four whole tile rows plus a 32-row strip (1056), plus 160 rows
+    (1184) and plus 224 (1248), so the last tile row and column are partial
+    and take the element stores; smaller multiples of 32 (160, 288, 544 on
+    128 x 128 direct-to-LDS tiles) and of 8 (264, 200: register-staged 128 x
+    128 tiles) share the call."""
     torch, dev = torch_dev
     rng = W.rng_for(90, 5)
-    mats = [spd(d, rng) for d in (160, 288, 264, 544, 200, 800)]
+    mats = [spd(d, rng) for d in (1056, 160, 288, 1184, 264, 544, 200, 1248)]
     for normalize in ("trace", "none"):
         _check_roots(torch, dev, mats, 1e-6, normalize, "newton", torch.float32, ROOT_TOL)
 
@@ -135,7 +137,7 @@ def test_newton_wide_tiles_ragged(torch_dev):
 def test_newton_read_ahead_chunk_counts(torch_dev):
     """Chunk counts at the edges of the main loops that read fragments one
     k-step ahead: one chunk (d = 16 in the float64 core, d = 32 in the
-    256 x 256 split-fp16 core), two (d = 32 in float64) and an odd count
+    direct-to-LDS split-fp16 core), two (d = 32 in float64) and an odd count
     (d = 48: three float64 chunks)."""
     torch, dev = torch_dev
     rng = W.rng_for(90, 7)
