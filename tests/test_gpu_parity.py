@@ -112,7 +112,9 @@ def test_jacobi_root_matches_oracle(torch_dev, a_dtype, normalize):
 def test_newton_root_matches_oracle(torch_dev, method, a_dtype):
     torch, dev = torch_dev
     rng = W.rng_for(90, 2)
-    sizes = [129, 200, 256, 301, 384]
+    # 270: even but not a multiple of 8, with whole float64 tiles (the mirror
+    # through LDS slabs with element stores of the split copy)
+    sizes = [129, 200, 256, 301, 384, 270]
     mats = [spd(d, rng) for d in sizes]
     dt = torch.float64 if a_dtype == "f64" else torch.float32
     tol = 1e-6 if method == "newton_f64" else ROOT_TOL
