@@ -81,7 +81,7 @@ typedef int32_t mr_dtype;
 #define MR_NORM_TRACE 1 /* s = trace(A): the rescaled Gram has trace 1 */
 
 /* inv_quarter_root_batched: method */
-#define MR_AUTO 0   /* Jacobi for d <= 128, coupled Newton above             */
+#define MR_AUTO 0   /* Jacobi for d <= 32, coupled Newton above              */
 #define MR_JACOBI 1 /* eigendecomposition in LDS (d <= 128 only)             */
 #define MR_NEWTON 2 /* GEMM-only coupled Newton inverse 4th root             */
 #define MR_NEWTON_F64 3 /* the same iteration with every step in float64       */
@@ -204,8 +204,10 @@ size_t gram_ema_update_workspace(const mr_gram_problem* problems, int32_t count,
  *    matrix cores.
  *  - MR_NEWTON_F64: the Newton iteration with every step in float64 (twice
  *    the cost of the float32 phase; for inputs near the float32 limit).
- *  - MR_AUTO: Jacobi for d <= 32, Newton otherwise (the faster route on
- *    MI355X: Jacobi's sweeps are a chain of d - 1 dependent rounds each).
+ *  - MR_AUTO: Jacobi for d <= 32, Newton otherwise (Jacobi's sweeps are a
+ *    chain of d - 1 dependent rounds each: on MI355X it is the faster route
+ *    up to d = 24 for a few matrices and up to d = 40 for hundreds, and its
+ *    roots are accurate to float64 rounding).
  * a_dtype: MR_F32 or MR_F64.  eps > 0 and finite.  info_dev: device array of
  * `count` records (may be NULL).  Never synchronises: the host launches a
  * fixed number of Newton steps and each matrix runs its own schedule under

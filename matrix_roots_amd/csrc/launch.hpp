@@ -19,10 +19,12 @@ constexpr int kMaxSyrkJobs = 48;   // Gram EMA: one launch per side for up to 48
 constexpr int kMaxRootJobs = 48;   // root statistics, init and finalize launches (3.1 KiB)
 constexpr int kMaxClasses = 8;
 constexpr int kJacobiMaxD = 128;
-// MR_AUTO takes the eigendecomposition route up to this size: measured on
-// MI355X, Jacobi is faster than the Newton route's launch sequence for
-// d <= 32 (4 to 256 matrices per call) and slower above (d = 48: 0.92 against
-// 0.53 ms for 4 matrices; d = 128: 9.3 against 1.1 ms).
+// MR_AUTO takes the eigendecomposition route up to this size.  Measured on
+// MI355X per root call, Jacobi against Newton: d = 24: 0.33 / 0.33 ms for 4
+// matrices, 0.50 / 0.69 for 256; d = 32: 0.49 / 0.36 and 0.57 / 0.73; d = 48:
+// 1.01 / 0.53 and 1.15 / 0.92; d = 128: 9.3 / 1.0.  Up to 32 the eigen route
+// costs at most a tenth of a millisecond more on small batches, wins on large
+// ones, and its roots are accurate to float64 rounding.
 constexpr int kJacobiAutoMaxD = 32;
 // Smallest Gram size whose split-fp16 Newton stages take the 256 x 256 tile
 // (d a multiple of 32).  Smaller Grams take the 128 x 128 direct-to-LDS tile
