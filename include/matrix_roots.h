@@ -92,10 +92,12 @@ typedef int32_t mr_dtype;
 #define MR_INFO_ZERO_TRACE 2    /* trace(A) == 0 under MR_NORM_TRACE; X = eps^(-1/4) * I    */
 #define MR_INFO_NOT_PD 4        /* Jacobi: an eigenvalue + eps <= 0; Newton: no usable bound;
                                    X is all NaN                                              */
-#define MR_INFO_NOT_CONVERGED 8 /* Jacobi: still rotating after 30 sweeps; Newton: residual
-                                   above r * sqrt(d), r = 2e-3 after a plain last step, 0.0243
+#define MR_INFO_NOT_CONVERGED 8 /* Jacobi: still rotating after the sweep cap (default 30,
+                                   mr_set_jacobi_max_sweeps); Newton: residual above
+                                   r * sqrt(d), r = 2e-3 after a plain last step, 0.0243
                                    (0.135) after a degree-2 (degree-4) finish (e.g. A + eps I
-                                   not positive definite)                                    */
+                                   not positive definite), or, under MR_NORM_NONE, a floor
+                                   eps/c below 1e-16                                         */
 
 /* One weight for gram_ema_update.  G: m x n float32 (ldg >= n).
  * L: m x m, R: n x n, both of the call's state dtype (ldl >= m, ldr >= n),
