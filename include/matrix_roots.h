@@ -274,10 +274,11 @@ mr_status inv_quarter_root_batched_noalloc(const mr_root_problem* problems, int3
  * launches for the whole batch; no host synchronisation.
  * Accuracy: the composed CANS map reaches (lambda/L)^(-1/2) to 3e-5 for
  * lambda/L in [1e-6, 1] and fails far below; with MR_CANS_F16 the fp16
- * rounding of S itself limits the relative error to a few 1e-3 for
- * condition numbers up to 1e3, and to about 1e-2 on eigenvalues near L,
- * where the first step cancels (fp16-grade, as on the page); MR_CANS_SPLIT
- * reaches about 1e-4 up to 1e4.  W is symmetric to the last bit.
+ * rounding of the operands limits the relative error to a few 1e-3 for
+ * condition numbers up to 1e3 (fp16-grade, as on the page); the first step,
+ * whose coefficients cancel to about y/18 for eigenvalues near L, runs on
+ * split operands in both precisions; MR_CANS_SPLIT reaches about 1e-4 up to
+ * 1e4.  W is symmetric to the last bit.
  * a_dtype: MR_F32 or MR_F64.  eps >= 0 and finite.  precision: MR_CANS_F16
  * or MR_CANS_SPLIT.  info_dev: device array of `count` records (may be
  * NULL): scale = s, bound = L, iters = 10, fp64_iters = 0, residual =
