@@ -401,7 +401,8 @@ int32_t mr_cans_ceilings(double* y, double* z, double* p, int32_t capacity);
  * precondition_apply -- for every problem:  U = alpha * XL * G * XR
  * The two-sided application of the quarter powers (EMA-Gram page, section
  * "Background"; Shampoo form of the OKLS page, section 1).  The two products
- * (W^T = XR G^T, then U = alpha XL W) run on the fp16 matrix cores with
+ * (W^T = XR^T G^T from a transposed split copy of XR, then U = alpha XL W;
+ * any square XR, symmetric or not) run on the fp16 matrix cores with
  * float32-accurate split operands (x = hi + 2^-11 lo, three fp16 products per
  * product, float32 accumulation), each operand scaled by the power of two
  * that puts its largest magnitude in [2^14, 2^15) (exact, and undone after
