@@ -22,16 +22,22 @@
 // X' = s^(-1/4) (5 X - X M/s)/4 in one launch, stage 1 T4 = T2 T2, stage 2
 // M' = T4 M / s.
 // All matrices are polynomials in M0: symmetric and mutually commuting, so
-// every product is an upper-tile symmetric GEMM.  The last iteration only
-// updates X.  Iterations run in float64 until the scalar map says the
-// smallest eigenvalue of M has reached 1e-2, then in float32.
+// every product is an upper-tile symmetric GEMM.  The last iteration updates
+// X only: the plain step, or a degree-2 or degree-4 Taylor finish in
+// E = I - M (schedule.hpp).  M and its powers run in float64 while the
+// schedule's floor of the spectrum of M is below kSwitchM, then on the
+// split-fp16 kernels (float32-accurate products); X lives in split storage
+// from the first step (the X update of a float64 step reads a split copy of
+// M), or in float64 / float32 for MR_NEWTON_F64 / MR_NEWTON_F32.
 //
-// Buffers per matrix (region of 5 float64 slots of d*d, S0..S4): in float64,
-// M alternates S0/S3, X alternates S1/S2, T4 is S4; in float32 (half-slots
-// h0..h9 of 4*d*d bytes) M alternates h8/h0, X h4/h2, T4 is h9.  Roles are a
-// function of the iteration's parity, so every workgroup finds its operands
-// without any table; the conversion at the switch writes float32 M and X into
-// half-slots that the float64 M and X of that parity do not use.
+// Buffers per matrix (region of 5 float64 slots of d*d, S0..S4, or 10
+// half-slots h0..h9 of 4*d*d bytes): float64 M alternates S0/S3 (T2 the
+// other), T4 is S4; a split matrix (hi[d*d] then lo[d*d]) fills a half-slot:
+// M alternates h8/h0 (T2 the other), X h4/h2, T4 h9, the split copy of a
+// float64 M h5, a degree-4 finish's q(M) h6.  Roles are a function of the
+// iteration's parity, so every workgroup finds its operands without any
+// table; the conversion at the switch writes the split M where the float64 M
+// of that parity is not.
 #include <math.h>
 
 #include "epilogue.hpp"
