@@ -26,7 +26,7 @@ namespace mr {
 // scale, and makes the result exactly equivariant under power-of-two
 // scalings of the inputs.  Rows are padded with zeros to a multiple of 32
 // (the zeros add nothing and make every contraction whole 32-deep chunks).
-// W^T = XR G^T goes through float32 and is split with its own scale before
+// W^T = XR^T G^T goes through float32 and is split with its own scale before
 // U = alpha XL W; each product multiplies by 2^-(s_A + s_B).
 
 // Scale exponent of a matrix from its largest magnitude (float32 bits):

@@ -40,7 +40,7 @@ constexpr int kJacobiDefaultSweeps = 30;
 constexpr int kJacobiMaxSweeps = 100;
 constexpr int kStatsRows = 32;       // rows of A per statistics workgroup (one 32-row tile stripe)
 constexpr int kFinalRows = 8;        // rows of X per finalize workgroup
-constexpr double kSwitchM = 5e-4;    // float64 -> float32 once the eigenvalue floor reaches this
+constexpr double kSwitchM = 5e-4;    // float64 -> split-fp16 products once the eigenvalue floor reaches this
 constexpr double kNewtonTol = 1e-6;  // stop once 1 - m_K <= this (scalar recurrence)
 constexpr double kBoundSafety = 1.01;
 // Lowest eigenvalue floor eps / c the Newton launches cover without a rescale
