@@ -34,11 +34,17 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6, "f16": 2500.0}  # MI355X dense MFMA (vendor figures)
+PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6, "f16": 2500.0, "i8": 5000.0}  # MI355X dense MFMA (vendor figures; i8 in TOP/s)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E (vendor figure)
 # kernel class -> matrix-core unit it runs on
-CLASS_ENGINE = {"newton_f64": "f64", "syrk_ema": "f64", "newton_f32": "f32", "newton_x3": "f16", "apply_x3": "f16"}
-SPLIT_CLASSES = ("newton_x3", "apply_x3")  # three fp16 MFMA products per float32-accurate product
+CLASS_ENGINE = {"newton_f64": "f64", "syrk_ema": "f64", "newton_f32": "f32", "newton_x3": "f16", "apply_x3": "f16",
+                "newton_i8": "i8"}
+# matrix-core products per algorithmic product: three fp16 products per
+# float32-accurate one (split classes), 21 int8 digit-plane products per
+# float64-accurate one (the default path's float64 steps)
+MFMA_PER_PRODUCT = {"newton_x3": 3, "apply_x3": 3, "newton_i8": 21}
+SPLIT_CLASSES = tuple(MFMA_PER_PRODUCT)
+DTYPE = "f64(int8 digit-plane products)+f32(split-f16 products)"
 METRIC = "preconditioned matrix updates/sec + TFLOP/s as % fp32 MFMA peak, d=1024–4096"
 ILLCOND_METRIC = "inverse quarter roots/s (256 ill-conditioned 512x512, one call per eps, no rescale)"
 
@@ -72,6 +78,12 @@ def blas_vendor() -> str:
     return "unknown"
 
 
+def f64_class(trace) -> str:
+    """Kernel class of the float64 steps' products: newton_i8 (int8 digit
+    planes, the default path) unless only the float64 kernel ran."""
+    return "newton_f64" if "newton_f64" in trace and "newton_i8" not in trace else "newton_i8"
+
+
 def sym_gemm_flops(d: int) -> float:
     """One symmetric-output product of d x d matrices: d(d+1)/2 outputs x d MACs x 2."""
     return float(d) * d * (d + 1)
@@ -83,7 +95,8 @@ def newton_flops(d: int, K: int, j: int, x_low: bool = True, final_degree: int =
     (M^2, T2^2, T4 M, X M), the last one only X q(M): one product for the
     step's own degree-1 polynomial, two for the degree-2 Taylor finish (q(M)
     from M^2, then X q) and three for the degree-4 one (M^2, E^2 R, X q);
-    t < j run M's products in float64, and the X product too unless x_low
+    t < j run M's products float64-accurate (on int8 digit planes with x_low,
+    in float64 otherwise), and the X product too unless x_low
     (then it runs on the split-fp16 kernel, like every product of the float32
     steps).  With x_low the first X product (X0 = I) is no product: the init
     writes X1."""
@@ -111,14 +124,20 @@ def root_stream_bytes(d: int, state_bytes: int, packed: bool, K: int, j: int):
                     M0 and X1 (4 bytes each) per element;
       newton_convert  at the float64 -> split switch: reads M (8), writes its
                     split copy (4) per element;
+      newton_slice  each float64 step with products (t < min(j, K - 1)):
+                    reads M (8 per element), writes its six digit planes (6
+                    per element of the matrix padded to dp, a multiple of 128)
+                    and dp row exponents (4 each);
       root_finalize reads X (split, 4) and M_{K-1} (8 in float64, 4 split),
                     writes X (float32, 4) per element."""
     n = d * d
+    dp = (d + 127) // 128 * 128
     stored = d * (d + 1) // 2 if packed else n
     m_last = 8 if (K - 1) < j else 4
     return {"root_stats": state_bytes * stored,
             "root_init": state_bytes * stored + 16 * n,
             "newton_convert": 12 * n if j < K else 0,
+            "newton_slice": (8 * n + 6 * dp * dp + 4 * dp) * max(min(j, K - 1), 0),
             "root_finalize": (4 + m_last + 4) * n}
 
 
@@ -215,8 +234,10 @@ def recorded_traffic(kernel: str, workload: str, family: str = "quarter"):
 def kernel_table(trace, flops, bytes_, launches_working=None):
     """Per kernel class: launches, time, and its rate against the roofline of
     the unit it runs on: matrix-core classes in algorithmic TFLOP/s (split
-    classes also in fp16 MFMA work, three products each) against their own
-    unit's peak; streaming classes in algorithmic GB/s against HBM."""
+    classes also in the matrix-core work they issue: three fp16 products per
+    float32-accurate product, 21 int8 products per float64-accurate one)
+    against their own unit's peak; streaming classes in algorithmic GB/s
+    against HBM."""
     out = {}
     for name, (launches, ms) in sorted(trace.items()):
         ent = {"launches": launches, "ms_total": round(ms, 3), "ms_avg": round(ms / launches, 4)}
@@ -228,9 +249,13 @@ def kernel_table(trace, flops, bytes_, launches_working=None):
             tf = f / (ms / 1e3) / 1e12
             ent.update({"engine": eng, "tflops": round(tf, 2)})
             if name in SPLIT_CLASSES:
-                ent.update({"mfma_tflops": round(3 * tf, 2), "peak": PEAK_TFLOPS[eng],
-                            "frac": round(3 * tf / PEAK_TFLOPS[eng], 4),
+                x = MFMA_PER_PRODUCT[name]
+                ent.update({"mfma_tflops": round(x * tf, 2), "peak": PEAK_TFLOPS[eng],
+                            "frac": round(x * tf / PEAK_TFLOPS[eng], 4),
                             "frac_algorithmic": round(tf / PEAK_TFLOPS[eng], 4)})
+                if eng == "i8":
+                    ent["note"] = ("tflops: float64-accurate algorithmic TFLOP/s; mfma_tflops: int8 TOP/s "
+                                   "(21 digit-plane products each)")
             else:
                 ent.update({"peak": PEAK_TFLOPS[eng], "frac": round(tf / PEAK_TFLOPS[eng], 4)})
         b = bytes_.get(name)
@@ -245,7 +270,7 @@ def kernel_table(trace, flops, bytes_, launches_working=None):
 def engine_table(kernels):
     """Time and work per matrix-core unit over its kernel classes."""
     out = {}
-    for eng in ("f64", "f16", "f32"):
+    for eng in ("f64", "i8", "f16", "f32"):
         names = [n for n, k in kernels.items() if k.get("engine") == eng]
         if not names:
             continue
@@ -268,11 +293,13 @@ def roofline_for(kernels, name, workload):
     if "tflops" in k:
         split = name in SPLIT_CLASSES
         r = {"bound": "mfma", "kernel": name, "engine": k["engine"],
-             "achieved": k["mfma_tflops"] if split else k["tflops"], "peak": k["peak"], "unit": "TFLOP/s",
+             "achieved": k["mfma_tflops"] if split else k["tflops"], "peak": k["peak"],
+             "unit": "TOP/s" if k["engine"] == "i8" else "TFLOP/s",
              "frac": k["frac"], "traffic": traffic,
              "traffic_per": "working launch (calibrated FETCH_SIZE + WRITE_SIZE, profiles/)",
-             "achieved_per_launch": "algorithmic flops of the class over the timed steps (x3 fp16 products for "
-                                    "split classes) / sum of its event-measured launch durations"}
+             "achieved_per_launch": "algorithmic flops of the class over the timed steps (x3 fp16 products "
+                                    "for split-fp16 classes, x21 int8 products for newton_i8) / sum of its "
+                                    "event-measured launch durations"}
     else:
         r = {"bound": "hbm", "kernel": name, "achieved": k["gb_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
              "frac": k["hbm_frac"], "traffic": traffic,
@@ -329,6 +356,11 @@ def per_size_class(B, torch, grams, wl, min_d=129):
             t64 = f64 / (tr["newton_f64"][1] / 1e3) / 1e12
             ent["newton_f64"] = {"ms": round(tr["newton_f64"][1], 3), "tflops": round(t64, 2),
                                  "frac_of_f64_peak": round(t64 / PEAK_TFLOPS["f64"], 4)}
+        if "newton_i8" in tr and f64 > 0:
+            t8 = f64 / (tr["newton_i8"][1] / 1e3) / 1e12
+            ent["newton_i8"] = {"ms": round(tr["newton_i8"][1], 3), "f64_equivalent_tflops": round(t8, 2),
+                                "int8_tops": round(21 * t8, 1),
+                                "frac_of_i8_peak": round(21 * t8 / PEAK_TFLOPS["i8"], 4)}
         if "newton_x3" in tr and low > 0:
             tx = low / (tr["newton_x3"][1] / 1e3) / 1e12
             ent["newton_x3"] = {"ms": round(tr["newton_x3"][1], 3), "tflops": round(tx, 2),
@@ -433,7 +465,7 @@ def bench_steps(args, torch, B, W, peaks):
     # algorithmic work and bytes over the timed steps
     es = 8 if args.state_dtype == "f64" else 4
     f64 = low = 0.0
-    sbytes = {"root_stats": 0, "root_init": 0, "newton_convert": 0, "root_finalize": 0}
+    sbytes = {"root_stats": 0, "root_init": 0, "newton_convert": 0, "newton_slice": 0, "root_finalize": 0}
     iters = []
     n_newton = 0
     for i in range(args.warmup, total):
@@ -459,7 +491,7 @@ def bench_steps(args, torch, B, W, peaks):
     sbytes.update({"momentum": 12 * elems, "hyperball_reduce": 8 * elems, "hyperball_update": 12 * elems,
                    # maxima and split copies of XR, G, XL and W^T: 8 bytes read and 4 written per element
                    "apply_split": 12 * sum(m * m + 2 * m * n + n * n for m, n in shapes) * args.steps})
-    flops = {"newton_f64": f64, "newton_x3": low, "syrk_ema": syrk, "apply_x3": apply_f}
+    flops = {f64_class(trace): f64, "newton_x3": low, "syrk_ema": syrk, "apply_x3": apply_f}
     kernels = kernel_table(trace, flops, sbytes)
     # the syrk's HBM bytes (state read + write, gradient read) as context: it is matrix-core bound
     if "syrk_ema" in kernels:
@@ -536,7 +568,7 @@ def bench_steps(args, torch, B, W, peaks):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f64+f32(split-f16 products)",
+        "dtype": DTYPE,
         "data": "synthetic",
         "config": {"workload": args.workload, "weights": nw, "grams_per_step": 2 * nw,
                    "shapes": sorted({f"{m}x{n}" for m, n in shapes}), "beta": wl.beta, "eps": wl.eps,
@@ -547,9 +579,9 @@ def bench_steps(args, torch, B, W, peaks):
         "tflops": round(tf_step, 2),
         "pct_fp32_mfma_peak": round(100 * tf_step / PEAK_TFLOPS["f32"], 2),
         "pct_fp32_mfma_peak_note": "the metric's headline: float32-accurate algorithmic TFLOP/s of the whole step "
-                                   "over the fp32 MFMA peak; the work runs on the fp64 and fp16 matrix cores, not "
-                                   "the fp32 ones, so this is not a fraction of any unit's roofline (those are in "
-                                   "engines, kernels and rooflines)",
+                                   "over the fp32 MFMA peak; the work runs on the int8, fp16 and fp64 matrix "
+                                   "cores, not the fp32 ones, so this is not a fraction of any unit's roofline "
+                                   "(those are in engines, kernels and rooflines)",
         "newton_iters": {"min": kmin, "max": kmax},
         "engines": engines,
         "roofline": roofline,
@@ -603,7 +635,7 @@ def bench_illcond(args, torch, B, W, peaks):
     # per-eps call time (events around single calls, after the timed region)
     per_eps = {}
     f64 = low = 0.0
-    sbytes = {"root_stats": 0, "root_init": 0, "newton_convert": 0, "root_finalize": 0}
+    sbytes = {"root_stats": 0, "root_init": 0, "newton_convert": 0, "newton_slice": 0, "root_finalize": 0}
     for eps in wl.eps_list:
         info = B.decode_info(infos[eps], count)
         assert (info["flags"] == 0).all(), info[info["flags"] != 0]
@@ -629,7 +661,7 @@ def bench_illcond(args, torch, B, W, peaks):
                                "fp64_iters": [int(info["fp64_iters"].min()), int(info["fp64_iters"].max())],
                                "tflops": round((ef64 + elow) / (cms / 1e3) / 1e12, 2)}
         log(f"eps {eps:g}: {per_eps[f'{eps:g}']}")
-    kernels = kernel_table(trace, {"newton_f64": f64, "newton_x3": low}, sbytes)
+    kernels = kernel_table(trace, {f64_class(trace): f64, "newton_x3": low}, sbytes)
     dname = max((kv for kv in kernels.items() if "tflops" in kv[1]), key=lambda kv: kv[1]["ms_total"])[0]
     cpu = None
     if not args.no_cpu_baseline:
@@ -647,7 +679,7 @@ def bench_illcond(args, torch, B, W, peaks):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f64+f32(split-f16 products)",
+        "dtype": DTYPE,
         "data": "synthetic",
         "config": {"workload": "illcond", "matrices": count, "d": 512, "eps": list(wl.eps_list),
                    "normalize": "none", "calls_per_step": len(wl.eps_list)},

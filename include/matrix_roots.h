@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MR_ABI_VERSION 1
+#define MR_ABI_VERSION 2
 
 typedef int32_t mr_status;
 #define MR_OK 0
@@ -451,19 +451,21 @@ int32_t mr_newton_schedule(double m0, double* scales, int32_t capacity, int32_t*
  * Matrix-core peaks of the current device, for reporting rooflines (the
  * measurement the hot path's roofline figures are set against).
  * prop_tflops: multiProcessorCount x clockRate x dense MFMA flops per clock
- * per compute unit (gfx950: 256 float32, 128 float64, 4096 fp16).
+ * per compute unit (gfx950: 256 float32, 128 float64, 4096 fp16, 8192 int8
+ * operations).
  * measured_tflops: register-only MFMA loops (v_mfma_f32_32x32x2_f32,
- * v_mfma_f64_16x16x4_f64, v_mfma_f32_32x32x16_f16), eight workgroups per
- * CU, about 5 ms each, timed with events on `hip_stream` after one warm-up
- * launch.  Index 0 float32, 1 float64, 2 fp16.  Synchronises the stream and
+ * v_mfma_f64_16x16x4_f64, v_mfma_f32_32x32x16_f16,
+ * v_mfma_i32_32x32x32_i8), eight workgroups per CU, a few ms each, timed
+ * with events on `hip_stream` after one warm-up launch.  Index 0 float32,
+ * 1 float64, 2 fp16, 3 int8 (TOP/s).  Synchronises the stream and
  * touches no device memory; MR_ERR_NULL for a NULL `out`, MR_ERR_HIP on a
  * runtime error (then `out` holds what was measured before it).
  */
 typedef struct {
   int32_t cu_count;          /* hipDeviceProp_t::multiProcessorCount   */
   int32_t clock_khz;         /* hipDeviceProp_t::clockRate (peak, kHz) */
-  double prop_tflops[3];     /* derived from CU count and clock        */
-  double measured_tflops[3]; /* register-only MFMA loops              */
+  double prop_tflops[4];     /* derived from CU count and clock        */
+  double measured_tflops[4]; /* register-only MFMA loops              */
 } mr_peak_info;
 mr_status mr_measure_peaks(mr_peak_info* out, void* hip_stream);
 

@@ -166,7 +166,7 @@ def library() -> ctypes.CDLL:
     lib.mr_last_error_message.restype = ctypes.c_char_p
     lib.mr_abi_version.argtypes = []
     lib.mr_abi_version.restype = i32
-    if lib.mr_abi_version() != 1:
+    if lib.mr_abi_version() != 2:
         raise RuntimeError("libmatrix_roots.so ABI version mismatch")
     _lib = lib
     return lib
@@ -546,10 +546,10 @@ def newton_schedule(m0: float, final_degree: bool = False):
 
 class PeakInfo(ctypes.Structure):
     _fields_ = [("cu_count", ctypes.c_int32), ("clock_khz", ctypes.c_int32),
-                ("prop_tflops", ctypes.c_double * 3), ("measured_tflops", ctypes.c_double * 3)]
+                ("prop_tflops", ctypes.c_double * 4), ("measured_tflops", ctypes.c_double * 4)]
 
 
-PEAK_KINDS = ("f32", "f64", "f16")
+PEAK_KINDS = ("f32", "f64", "f16", "i8")
 
 
 def measure_peaks(stream=None) -> dict:

@@ -127,7 +127,7 @@ enum TraceClass {
   kTrSyrk, kTrJacobi, kTrStats, kTrBound, kTrInit, kTrNewton64, kTrNewton32, kTrConvert,
   kTrFinalize, kTrInfo, kTrNewtonX3, kTrCansBound, kTrCansInit, kTrCansP, kTrCansYZ, kTrCansFinal, kTrCansInfo,
   kTrPolarStats, kTrPolarBound, kTrPolarInit, kTrPolarA, kTrPolarX, kTrPolarFinal, kTrPolarInfo,
-  kTrMomentum, kTrHyperReduce, kTrHyperUpdate, kTrApplyX3, kTrApplySplit, kTrCount
+  kTrMomentum, kTrHyperReduce, kTrHyperUpdate, kTrApplyX3, kTrApplySplit, kTrSlice, kTrNewtonI8, kTrCount
 };
 const char* const kTraceNames[kTrCount] = {"syrk_ema", "jacobi", "root_stats", "root_bound",
                                            "root_init", "newton_f64", "newton_f32", "newton_convert",
@@ -135,7 +135,8 @@ const char* const kTraceNames[kTrCount] = {"syrk_ema", "jacobi", "root_stats", "
                                            "cans_init", "cans_p", "cans_yz", "cans_finalize", "cans_info",
                                            "polar_stats", "polar_bound", "polar_init", "polar_gram",
                                            "polar_update", "polar_finalize", "polar_info", "momentum",
-                                           "hyperball_reduce", "hyperball_update", "apply_x3", "apply_split"};
+                                           "hyperball_reduce", "hyperball_update", "apply_x3", "apply_split",
+                                           "newton_slice", "newton_i8"};
 struct TraceEntry {
   int cls;
   hipEvent_t a, b;
@@ -193,6 +194,10 @@ struct RootPlan {
 // Sweep cap of the Jacobi route (mr_set_jacobi_max_sweeps).
 std::atomic<int32_t> g_jacobi_max_sweeps{kJacobiDefaultSweeps};
 
+// Default Newton path: X in split-fp16 storage from the first step, the
+// float64 steps' products on int8 digit planes.
+bool split_path(int32_t method) { return method != MR_NEWTON_F64 && method != MR_NEWTON_F32; }
+
 bool use_jacobi(int64_t d, int32_t method) {
   return method == MR_JACOBI || (method == MR_AUTO && d <= kJacobiAutoMaxD);
 }
@@ -213,7 +218,8 @@ RootPlan plan_root(const mr_root_problem* p, int32_t count, int32_t method) {
     c.d = kv.first;
     c.first_slot = (int)P.slot_problem.size();
     c.count = (int)kv.second.size();
-    c.matrix_bytes = align256((size_t)40 * (size_t)c.d * (size_t)c.d);
+    // five float64 slots; the split-storage path adds the digit planes of its float64 steps
+    c.matrix_bytes = (size_t)oz_f64_bytes(c.d) + (split_path(method) ? (size_t)oz_extra_bytes(c.d) : 0);
     for (int i : kv.second) P.slot_problem.push_back(i);
     P.classes.push_back(c);
     dmax_newton = std::max(dmax_newton, c.d);
@@ -355,7 +361,7 @@ mr_status mr_measure_peaks(mr_peak_info* out, void* hip_stream) {
   // eight workgroups (two waves per SIMD) per CU, about 5 ms per kind at the
   // vendor peak; the first launch of each kind warms the clock up
   const int blocks = 8 * std::max(1, prop.multiProcessorCount);
-  const int iters[kPeakKinds] = {3000, 1500, 6000};
+  const int iters[kPeakKinds] = {3000, 1500, 6000, 6000};
   mr_status st = MR_OK;
   for (int k = 0; k < kPeakKinds && st == MR_OK; ++k) {
     double flops = 0.0;
@@ -796,7 +802,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
   const bool f32_mfma = method == MR_NEWTON_F32;
   // Default Newton path: X in float32 storage with split-fp16 products from
   // the first step; only M and its powers run in float64 while the floor is low.
-  const bool x_low = !all_f64 && !f32_mfma;
+  const bool x_low = split_path(method);
 
   // ---------------- Jacobi matrices: descriptors into the workspace, then one
   // launch per size class (one workgroup per matrix)
@@ -970,6 +976,8 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
         C.block_begin = L.total_blocks;
         if (kind == 0)
           C.blocks_per_matrix = (stage == 0 && job_only < 0 ? 2 : 1) * C.U;
+        else if (kind == 2)
+          C.blocks_per_matrix = (int32_t)oz_pad(c.d);  // digit planes of M: a workgroup per padded row
         else
           C.blocks_per_matrix = (int32_t)((c.d * c.d + 2047) / 2048);
         C.nblocks = C.blocks_per_matrix * C.count;
@@ -984,13 +992,21 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
                            "newton convert")) != MR_OK)
             return st;
       }
+      if (t < j_max && x_low) {  // digit planes of M
+        for (const auto& g : groups)
+          if ((st = traced(kTrSlice, true, s, [&] { return launch_newton_slice(make_launch(g, 2, 0, t, -1), s); },
+                           "newton slice")) != MR_OK)
+            return st;
+      }
       for (int stage = 0; stage < 3; ++stage) {
         for (const auto& g : groups) {
           if (t < j_max) {
-            // float64 steps; with x_low the X update goes to the split-fp16 kernel
+            // float64 steps; with x_low the products run on digit planes and
+            // the X update goes to the split-fp16 kernel
             const bool split = x_low && stage == 0;
             const NewtonLaunch L64 = make_launch(g, 0, stage, t, split ? 0 : -1);
-            if ((st = traced(kTrNewton64, true, s, [&] { return launch_newton_stage(L64, kStageF64, g.vec64, s); },
+            if ((st = traced(x_low ? kTrNewtonI8 : kTrNewton64, true, s,
+                             [&] { return launch_newton_stage(L64, x_low ? kStageI8 : kStageF64, g.vec64, s); },
                              "newton f64 stage")) != MR_OK)
               return st;
             if (split && t > 0) {  // the first X update is part of the init

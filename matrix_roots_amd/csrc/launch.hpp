@@ -47,6 +47,19 @@ constexpr double kBoundSafety = 1.01;
 // (below it float64 rounding of M0 already reaches the floor's size).
 constexpr double kNoneFloorCap = 1e-16;
 
+// Float64 Newton steps of the default path run their products on int8 digit
+// planes (gemm_i8.hpp): kOzSlices planes per matrix, rows and columns padded
+// to dp = d rounded up to kOzTile.  Per matrix, after the five float64 slots
+// of d*d: the planes of M, of T2 and of T4, then M's row exponents (dp int32).
+constexpr int kOzSlices = 6;
+constexpr int kOzTile = 128;
+__host__ __device__ inline int64_t oz_pad(int64_t d) { return (d + kOzTile - 1) / kOzTile * kOzTile; }
+__host__ __device__ inline int64_t oz_f64_bytes(int64_t d) { return (40 * d * d + 255) & ~(int64_t)255; }
+__host__ __device__ inline int64_t oz_set_bytes(int64_t d) { return kOzSlices * oz_pad(d) * oz_pad(d); }
+__host__ __device__ inline int64_t oz_extra_bytes(int64_t d) {
+  return (3 * oz_set_bytes(d) + 4 * oz_pad(d) + 255) & ~(int64_t)255;
+}
+
 // Workgroup ranges of jobs and size classes start on multiples of 8 (one per
 // XCD) and are padded to a multiple of 8.
 __host__ __device__ inline int32_t round8(int32_t n) { return (n + 7) & ~7; }
@@ -170,7 +183,7 @@ struct RootJob {
   int64_t lda;
   float* X;
   int64_t ldx;
-  char* region;  // Newton buffers (5 float64 slots of d*d), NULL for Jacobi
+  char* region;  // Newton buffers (5 float64 slots of d*d, then the digit planes), NULL for Jacobi
   int32_t d;
   int32_t slot;     // index into the RootState array
   int32_t problem;  // index in the caller's problem array
@@ -274,8 +287,9 @@ hipError_t launch_root_bound(RootState* state, const double* partial, int64_t pa
                              int32_t slot_begin, int32_t nslots, int32_t normalize, double eps,
                              int32_t k_cap, double floor_cap, int32_t all_f64, int32_t finish, hipStream_t s);
 hipError_t launch_root_init(const RootBatch& b, hipStream_t s);
-enum StageKind { kStageF64 = 0, kStageF32 = 1, kStageX3 = 2, kStageX3B64 = 3 };
+enum StageKind { kStageF64 = 0, kStageF32 = 1, kStageX3 = 2, kStageX3B64 = 3, kStageI8 = 4 };
 hipError_t launch_newton_stage(const NewtonLaunch& L, int kind, int vec, hipStream_t s);
+hipError_t launch_newton_slice(const NewtonLaunch& L, hipStream_t s);
 hipError_t launch_newton_convert(const NewtonLaunch& L, hipStream_t s);
 hipError_t launch_root_finalize(const RootBatch& b, hipStream_t s);
 hipError_t launch_root_info(RootState* state, const double* partial, int64_t partial_stride,

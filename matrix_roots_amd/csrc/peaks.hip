@@ -9,7 +9,7 @@ namespace mr {
 
 namespace {
 
-// 8 chains of 16 registers for f32 32x32x2 and f16 32x32x16, 16 chains of 8
+// 8 chains of 16 registers for f32 32x32x2, f16 32x32x16 and i8 32x32x32, 16 chains of 8
 // registers for f64 16x16x4: with two waves per SIMD that keeps enough
 // independent MFMAs in flight to cover each instruction's pipeline latency
 // (4 chains reach only 78% of the fp16 rate).
@@ -24,6 +24,11 @@ template <>
 struct PeakCfg<kPeakF16> {
   static constexpr int CHAINS = 8;
   static constexpr double FLOPS = 2.0 * 32 * 32 * 16;
+};
+template <>
+struct PeakCfg<kPeakI8> {
+  static constexpr int CHAINS = 8;
+  static constexpr double FLOPS = 2.0 * 32 * 32 * 32;
 };
 template <>
 struct PeakCfg<kPeakF64> {
@@ -50,6 +55,25 @@ __global__ __launch_bounds__(256, 2) void peak_kernel(int iters, float* sink) {
       for (int c = 0; c < C; ++c) acc[c] = mfma_f64_16x16x4(a, b, acc[c]);
 #pragma unroll
     for (int c = 0; c < C; ++c) total += (float)(acc[c][0] + acc[c][3]);
+  } else if constexpr (KIND == kPeakI8) {
+    typedef int v4i_ __attribute__((ext_vector_type(4)));
+    typedef int v16i_ __attribute__((ext_vector_type(16)));
+    v16i_ acc[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[c][v] = 0;
+    v4i_ a, b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = (int)(threadIdx.x * 7u + (unsigned)e) & 0x3f3f3f3f;
+      b[e] = (int)(threadIdx.x * 3u + 5u * (unsigned)e) & 0x3f3f3f3f;
+    }
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int c = 0; c < C; ++c) acc[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[c], 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < C; ++c) total += (float)(acc[c][0] + acc[c][15]);
   } else {
     v16f acc[C];
 #pragma unroll
@@ -93,6 +117,10 @@ hipError_t launch_peak_loop(int kind, int blocks, int iters, double* flops, hipS
     case kPeakF16:
       hipLaunchKernelGGL(peak_kernel<kPeakF16>, dim3(blocks), dim3(256), 0, s, iters, (float*)nullptr);
       *flops = waves * PeakCfg<kPeakF16>::CHAINS * PeakCfg<kPeakF16>::FLOPS;
+      break;
+    case kPeakI8:
+      hipLaunchKernelGGL(peak_kernel<kPeakI8>, dim3(blocks), dim3(256), 0, s, iters, (float*)nullptr);
+      *flops = waves * PeakCfg<kPeakI8>::CHAINS * PeakCfg<kPeakI8>::FLOPS;
       break;
     default:
       return hipErrorInvalidValue;

@@ -7,11 +7,12 @@
 
 namespace mr {
 
-enum PeakKind { kPeakF32 = 0, kPeakF64 = 1, kPeakF16 = 2 };
-constexpr int kPeakKinds = 3;
+enum PeakKind { kPeakF32 = 0, kPeakF64 = 1, kPeakF16 = 2, kPeakI8 = 3 };
+constexpr int kPeakKinds = 4;
 
-// Dense MFMA flops per clock per compute unit on gfx950 (4 SIMDs).
-constexpr double kMfmaFlopsPerClockCU[kPeakKinds] = {256.0, 128.0, 4096.0};
+// Dense MFMA flops (int8: operations) per clock per compute unit on gfx950
+// (4 SIMDs).
+constexpr double kMfmaFlopsPerClockCU[kPeakKinds] = {256.0, 128.0, 4096.0, 8192.0};
 
 // Launch `blocks` workgroups of 256 threads, each wave running `iters`
 // rounds of independent MFMA chains of the kind; returns the flops one such

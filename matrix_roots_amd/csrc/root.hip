@@ -42,6 +42,7 @@
 
 #include "epilogue.hpp"
 #include "gemm_core.hpp"
+#include "gemm_i8.hpp"
 #include "launch.hpp"
 #include "schedule.hpp"
 
@@ -393,7 +394,7 @@ __device__ __forceinline__ StageJob stage_job(const NewtonLaunch& L, int kind) {
   const int t = L.t, K = st.K, j = st.j;
   const bool xupdate = L.stage == 0 && s.job == 1;
   bool act;
-  if (kind == kStageF64)
+  if (kind == kStageF64 || kind == kStageI8)
     act = t < K && t < j && !(L.x_low && xupdate);
   else if (kind == kStageX3B64)
     act = t < K && t < j && L.x_low && xupdate;
@@ -746,6 +747,215 @@ __global__ __launch_bounds__(X3W::THREADS, 1) void newton_x3w_kernel(const Newto
   }
 }
 
+// 16 values -> kOzSlices planes of 16 digits at dst (+ p * ps), one 16-byte
+// store per plane.
+__device__ __forceinline__ void oz_store16(const double (&w)[16], int e, int8_t* dst, int64_t ps) {
+  uint32_t pk[kOzSlices][4];
+#pragma unroll
+  for (int p = 0; p < kOzSlices; ++p)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pk[p][q] = 0u;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    int8_t dg[kOzSlices];
+    oz_digits(w[k], e, dg);
+#pragma unroll
+    for (int p = 0; p < kOzSlices; ++p) pk[p][k >> 2] |= (uint32_t)(uint8_t)dg[p] << (8 * (k & 3));
+  }
+#pragma unroll
+  for (int p = 0; p < kOzSlices; ++p)
+    *reinterpret_cast<v4i*>(dst + p * ps) = v4i{(int)pk[p][0], (int)pk[p][1], (int)pk[p][2], (int)pk[p][3]};
+}
+
+// ------------------------------------------------ int8 digit-plane steps
+// Float64 steps of the split-storage path: the products of M, T2 and T4 run
+// on int8 digit planes (gemm_i8.hpp).  M gets one exponent per row, cut from
+// the float64 M at the start of each step by a pass of its own: its entries
+// can sit far below its spectral bound (a log-uniform spectrum puts the
+// diagonal near the mean eigenvalue), and a fixed exponent there loses
+// enough digits to show in the root.  T2 and T4 take the fixed exponents 1
+// and 2 (spectra in [0, 25/16] and [0, 625/256]: T = (5 I - M/s)/4 with the
+// spectrum of M/s in [0, 4.8], so their diagonals, and with them their
+// largest entries, sit near the top of those ranges), and their planes come
+// straight from the product epilogues.  Stage 2 writes the float64 M' and its
+// split copy, as the float64 kernel does.
+struct OzRegion {
+  int8_t *M, *T2, *T4;
+  int32_t* eM;  // M's row exponents
+  int64_t dp;
+};
+__device__ __forceinline__ OzRegion oz_region(char* region, int d) {
+  OzRegion z;
+  const int64_t set = oz_set_bytes(d);
+  int8_t* base = reinterpret_cast<int8_t*>(region + oz_f64_bytes(d));
+  z.M = base;
+  z.T2 = base + set;
+  z.T4 = base + 2 * set;
+  z.eM = reinterpret_cast<int32_t*>(base + 3 * set);
+  z.dp = oz_pad(d);
+  return z;
+}
+constexpr int kOzExpT2 = 1, kOzExpT4 = 2;
+
+// Digit planes of M (iteration t) with per-row exponents: one workgroup per
+// padded row; each lane holds up to kOzSliceSeg segments of 16 consecutive
+// elements in registers (rows up to 8192 are read once), longer rows are read
+// again for the digits.  Rows and columns past d get zero digits (and rows
+// exponent 0).  Runs for the matrices whose step t is a float64 step with
+// products (t < j, t < K - 1).
+constexpr int kOzSliceSeg = 2;
+__global__ __launch_bounds__(256) void newton_slice_kernel(const NewtonLaunch L) {
+  __shared__ double red[4];
+  const int64_t b = blockIdx.x;
+  const NewtonClass& C = L.cls[find_class(L, b)];
+  const int local = (int)(b - C.block_begin);
+  if (local >= C.nblocks) return;
+  const int mat = local / C.blocks_per_matrix;
+  const int row = local % C.blocks_per_matrix;
+  const RootState& st = L.state[C.slot_begin + mat];
+  const int t = L.t;
+  if (!(t < st.j && t < st.K - 1)) return;
+  const int d = C.d;
+  char* region = C.region + (int64_t)mat * C.matrix_bytes;
+  const OzRegion z = oz_region(region, d);
+  const double* M = roles64(region, d, t).M + (int64_t)row * d;
+  const bool real = row < d;
+  const bool vec = (d & 1) == 0;  // 16-byte loads (rows 16-byte aligned)
+  auto load16 = [&](int c0, double (&w)[16]) __attribute__((always_inline)) {
+    if (real && vec && c0 + 16 <= d) {
+#pragma unroll
+      for (int k = 0; k < 16; k += 2) {
+        const v2d x = *reinterpret_cast<const v2d*>(M + c0 + k);
+        w[k] = x[0];
+        w[k + 1] = x[1];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) w[k] = real && c0 + k < d ? M[c0 + k] : 0.0;
+    }
+  };
+  double seg[kOzSliceSeg][16];
+  double mx = 0.0;
+  for (int c0 = threadIdx.x * 16, i = 0; c0 < z.dp; c0 += 256 * 16, ++i) {
+    double w[16];
+    load16(c0, w);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) mx = fmax(mx, fabs(w[k]));
+#pragma unroll
+    for (int q = 0; q < kOzSliceSeg; ++q)
+      if (q == i)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) seg[q][k] = w[k];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+  int e = 0;
+  if (mx > 0.0) frexp(mx, &e);  // mx < 2^e
+  if (threadIdx.x == 0) z.eM[row] = e;
+  const int64_t ps = z.dp * z.dp;
+  for (int c0 = threadIdx.x * 16, i = 0; c0 < z.dp; c0 += 256 * 16, ++i) {
+    double w[16];
+    if (i < kOzSliceSeg) {
+#pragma unroll
+      for (int q = 0; q < kOzSliceSeg; ++q)
+        if (q == i)
+#pragma unroll
+          for (int k = 0; k < 16; ++k) w[k] = seg[q][k];
+    } else {
+      load16(c0, w);
+    }
+    oz_store16(w, e, z.M + (int64_t)row * z.dp + c0, ps);
+  }
+}
+
+// One 128 x 128 upper tile of a float64 step's product on the digit planes:
+//   stage 0: T2 = ((M/s)^2 - 10 M/s + 25 I) / 16   -> T2 planes
+//   stage 1: T4 = T2 T2                            -> T4 planes
+//   stage 2: M' = T4 M / s                         -> float64 M' and its split copy
+// The tile's values go through LDS (128 x kOzOutLd doubles, in the operand
+// stages the main loop has released) and leave as 16-element row segments of
+// the tile and of its mirror; a lane takes a row, so the LDS reads of a wave
+// (one column segment of 64 rows, or one row segment transposed) are
+// conflict-free with the odd row pitch.  Outside the d x d matrix the planes
+// get zeros.
+constexpr int kOzOutLd = kOzTile + 1;
+__global__ __launch_bounds__(OzCfg::THREADS, 1) void newton_i8_kernel(const NewtonLaunch L) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[OzCfg::LDS_BYTES];
+  static_assert(kOzTile * kOzOutLd * 8 <= OzCfg::LDS_BYTES, "the output tile fits in the operand stages");
+  const StageJob s = stage_job(L, kStageI8);
+  if (!s.active) return;
+  const int d = s.d;
+  const int stage = L.stage;
+  const OzRegion z = oz_region(s.region, d);
+  const int64_t dp = z.dp, ps = dp * dp;
+  const int8_t* A = stage == 0 ? z.M : stage == 1 ? z.T2 : z.T4;
+  const int8_t* B = stage == 1 ? z.T2 : z.M;
+  const int m0 = s.ti * kOzTile, n0 = s.tj * kOzTile;
+  v16i acc[kOzSlices][2];
+  oz_nt_tile(A, B, dp, ps, (int)dp, m0, n0, smem, acc);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const Roles64 r64 = roles64(s.region, d, L.t);
+  const double is = 1.0 / s.s;
+  double* T = reinterpret_cast<double*>(smem);
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int li = wm * 32 + f32_row(lane, v), lj = wn * 64 + cb * 32 + (lane & 31);
+      const int gi = m0 + li, gj = n0 + lj;
+      const int ea = stage == 0 ? z.eM[gi] : stage == 1 ? kOzExpT2 : kOzExpT4;
+      const int eb = stage == 1 ? kOzExpT2 : z.eM[gj];
+      const double x = oz_value(acc, cb, v, ea + eb);
+      double val = 0.0;
+      if (gi < d && gj < d) {
+        if (stage == 0)
+          val = x * (is * is / 16.0) - (10.0 * is / 16.0) * r64.M[(int64_t)gi * d + gj] + (gi == gj ? 25.0 / 16.0 : 0.0);
+        else
+          val = stage == 1 ? x : x * is;
+      }
+      T[li * kOzOutLd + lj] = val;
+    }
+  __syncthreads();
+
+  const bool diag = s.ti == s.tj;
+  const SplitBuf mx = roless(s.region, d, L.t).Mx;
+  int8_t* const out = stage == 0 ? z.T2 : z.T4;
+  const int eo = stage == 0 ? kOzExpT2 : kOzExpT4;
+  // pass 0: the tile's own region (on the diagonal: upper values, mirrored
+  // below); pass 1: the mirror region (n0.., m0..)
+  for (int pass = 0; pass < (diag ? 1 : 2); ++pass) {
+    const int R0 = pass == 0 ? m0 : n0, C0 = pass == 0 ? n0 : m0;
+    for (int sg = threadIdx.x; sg < kOzTile * (kOzTile / 16); sg += OzCfg::THREADS) {
+      const int lr = sg & (kOzTile - 1), c0 = (sg / kOzTile) * 16;
+      double w[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int lc = c0 + k;
+        w[k] = (pass == 1 || (diag && lr > lc)) ? T[lc * kOzOutLd + lr] : T[lr * kOzOutLd + lc];
+      }
+      const int gi = R0 + lr, gj0 = C0 + c0;
+      if (stage < 2) {
+        oz_store16(w, eo, out + (int64_t)gi * dp + gj0, ps);
+      } else if (gi < d) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int gj = gj0 + k;
+          if (gj < d) {
+            const int64_t e = (int64_t)gi * d + gj;
+            r64.T2[e] = w[k];
+            split_put(mx, e, (float)w[k]);
+          }
+        }
+      }
+    }
+  }
+}
+
 // float64 M, X of iteration t -> float32 M, X of iteration t, for the
 // matrices whose switch iteration is t.
 __global__ __launch_bounds__(256) void newton_convert_kernel(const NewtonLaunch L) {
@@ -899,6 +1109,10 @@ hipError_t launch_newton_stage(const NewtonLaunch& L, int kind, int vec, hipStre
       hipLaunchKernelGGL(newton_x3_kernel<1>, dim3(L.total_blocks), dim3(256), 0, s, L, kind);
     return hipGetLastError();
   }
+  if (kind == kStageI8) {
+    hipLaunchKernelGGL(newton_i8_kernel, dim3(L.total_blocks), dim3(OzCfg::THREADS), 0, s, L);
+    return hipGetLastError();
+  }
   if (kind == kStageF64) {
     if (vec > 1)
       hipLaunchKernelGGL(newton_f64_kernel<2>, dim3(L.total_blocks), dim3(256), 0, s, L);
@@ -910,6 +1124,12 @@ hipError_t launch_newton_stage(const NewtonLaunch& L, int kind, int vec, hipStre
     else
       hipLaunchKernelGGL(newton_f32_kernel<1>, dim3(L.total_blocks), dim3(256), 0, s, L);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_newton_slice(const NewtonLaunch& L, hipStream_t s) {
+  if (L.total_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(newton_slice_kernel, dim3(L.total_blocks), dim3(256), 0, s, L);
   return hipGetLastError();
 }
 

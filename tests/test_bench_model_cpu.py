@@ -39,11 +39,17 @@ def test_newton_flops_finishes_and_float64_x():
 def test_root_stream_bytes():
     d, n = 1024, 1024 * 1024
     b = bench.root_stream_bytes(d, 8, False, 8, 2)
+    # two float64 steps with products: M read (8) and cut into six digit planes
+    # (6 per element, d = 1024 needs no padding) with d row exponents, each
     assert b == {"root_stats": 8 * n, "root_init": 8 * n + 16 * n, "newton_convert": 12 * n,
-                 "root_finalize": (4 + 4 + 4) * n}
+                 "newton_slice": 2 * (8 * n + 6 * n + 4 * d), "root_finalize": (4 + 4 + 4) * n}
     bp = bench.root_stream_bytes(d, 8, True, 2, 5)  # packed state, every step float64
     assert bp["root_stats"] == 8 * (d * (d + 1) // 2) and bp["newton_convert"] == 0
     assert bp["root_finalize"] == (4 + 8 + 4) * n
+    assert bp["newton_slice"] == 8 * n + 6 * n + 4 * d  # K = 2: the last step has no products
+    # a ragged size pads the planes to a multiple of 128
+    br = bench.root_stream_bytes(200, 8, False, 6, 1)
+    assert br["newton_slice"] == 8 * 200 * 200 + 6 * 256 * 256 + 4 * 256
 
 
 def test_bench_refuses_more_than_one_gpu(capsys):

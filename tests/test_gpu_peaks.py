@@ -1,7 +1,8 @@
 """Matrix-core peaks of the device: the rates derived from its CU count and
 clock (what the published MI355X figures are made of: 256 CUs at 2.4 GHz,
-256 / 128 / 4096 dense MFMA flops per clock per CU for float32 / float64 /
-fp16) and the rates register-only MFMA loops reach through the library."""
+256 / 128 / 4096 / 8192 dense MFMA flops (int8: operations) per clock per CU
+for float32 / float64 / fp16 / int8) and the rates register-only MFMA loops
+reach through the library."""
 
 import pytest
 
@@ -9,7 +10,7 @@ from matrix_roots_amd import binding as B
 
 pytestmark = pytest.mark.gpu
 
-VENDOR = {"f32": 157.3, "f64": 78.6, "f16": 2500.0}
+VENDOR = {"f32": 157.3, "f64": 78.6, "f16": 2500.0, "i8": 5000.0}
 
 
 def test_measure_peaks(gpu_available):
