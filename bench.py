@@ -908,7 +908,8 @@ def vendor_gemm(torch, dev):
     4096 x 4096 Grams, full products, contiguous operands: what the vendor
     library sustains on this device with real data, as context for the
     hand-written kernels' rates (which count symmetric products as d^2 (d+1))."""
-    out = {"shape": "batch 16 (fp16) / 4 (fp64) of 4096 x 4096 x 4096, C = A B, flops 2 m n k"}
+    out = {"shape": "batch 16 (fp16) / 4 (fp64) of 4096 x 4096 x 4096, C = A B, flops 2 m n k; int8: "
+                    "torch._int_mm of one 8192 x 8192 x 8192 product (int32 result), operations 2 m n k"}
     for name, dt, b, reps in (("f16", torch.float16, 16, 10), ("f64", torch.float64, 4, 4)):
         g = torch.Generator(device=dev)
         g.manual_seed(0)
@@ -927,6 +928,21 @@ def vendor_gemm(torch, dev):
         ms = e0.elapsed_time(e1) / reps
         out[name] = round(2.0 * b * 4096 ** 3 / (ms / 1e3) / 1e12, 1)
         del A, Bm, C
+    # int8 with int32 accumulation (the digit-plane products' arithmetic)
+    n = 8192
+    A = torch.randint(-64, 64, (n, n), device=dev, dtype=torch.int8)
+    Bm = torch.randint(-64, 64, (n, n), device=dev, dtype=torch.int8)
+    for _ in range(2):
+        torch._int_mm(A, Bm)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        torch._int_mm(A, Bm)
+    e1.record()
+    torch.cuda.synchronize()
+    out["i8"] = round(2.0 * n ** 3 / (e0.elapsed_time(e1) / 5 / 1e3) / 1e12, 1)
+    del A, Bm
     torch.cuda.empty_cache()
     return out
 

@@ -131,7 +131,8 @@ typedef struct {
   double scale;       /* s: trace(A) (MR_NORM_TRACE) or 1                        */
   double bound;       /* c >= lambda_max(A/s + eps I) (Newton); 0 for Jacobi      */
   int32_t iters;      /* Newton iterations run, or Jacobi sweeps                  */
-  int32_t fp64_iters; /* of those Newton iterations, the ones run in float64      */
+  int32_t fp64_iters; /* of those Newton iterations, the ones with float64-accurate
+                         products                                                */
   float residual;     /* Newton: ||M_{K-1} - I||_F, the iterate the last X update
                          used; Jacobi: off-diagonal Frobenius norm of the
                          rotated A/s at exit                                      */
@@ -188,11 +189,17 @@ size_t gram_ema_update_workspace(const mr_gram_problem* problems, int32_t count,
  *  - MR_NEWTON: coupled Newton iteration for the inverse 4th root,
  *        M0 = (A/s + eps I)/c, X0 = I, T = (5 I - M)/4, X <- X T, M <- T^4 M,
  *    X = c^(-1/4) X_K, with M scaled by 1/s_t before each step (per-step
- *    scales from the spectrum bounds, see mr_newton_schedule), run in float64
- *    while the smallest eigenvalue of M is below 5e-4, then with float32
- *    storage on the fp16 matrix cores with split operands (x = hi + 2^-11 lo,
- *    three products per product, float32 accumulation: about 2^-22 relative
- *    error per product).  The GEMM-only
+ *    scales from the spectrum bounds, see mr_newton_schedule), with
+ *    float64-accurate products of M and its powers while the smallest
+ *    eigenvalue of M is below 5e-4, then with float32 storage on the fp16
+ *    matrix cores with split operands (x = hi + 2^-11 lo, three products per
+ *    product, float32 accumulation: about 2^-22 relative error per product).
+ *    X is kept in that split storage from the first step.  The
+ *    float64-accurate products run on the int8 matrix cores: each operand as
+ *    six int8 digit planes (7 bits each, one power-of-two exponent per row of
+ *    M, fixed ones for M's powers), 21 exact plane products with int32
+ *    accumulation, summed in float64 (about 2^-40 relative to each row's
+ *    largest entry).  The GEMM-only
  *    route of tilderesearch, "Online KL Shampoo", sections 2.1-2.2 (there
  *    for the -1/2 root), taken to the 4th root.  c = 1.01 times the
  *    Wolkowicz-Styan upper bound on lambda_max(A/s + eps I) (the OKLS page,
@@ -203,9 +210,9 @@ size_t gram_ema_update_workspace(const mr_gram_problem* problems, int32_t count,
  *    M^(-1/4) about I, which ends the iteration a step or two earlier with a
  *    truncation error below 5e-7.
  *  - MR_NEWTON_F32: as MR_NEWTON with the float32 steps on the float32
- *    matrix cores.
- *  - MR_NEWTON_F64: the Newton iteration with every step in float64 (twice
- *    the cost of the float32 phase; for inputs near the float32 limit).
+ *    matrix cores, its float64 steps (X included) on the float64 ones.
+ *  - MR_NEWTON_F64: the Newton iteration with every step on the float64
+ *    matrix cores (for inputs near the float32 limit).
  *  - MR_AUTO: Jacobi for d <= 32, Newton otherwise (Jacobi's sweeps are a
  *    chain of d - 1 dependent rounds each: on MI355X it is the faster route
  *    up to d = 24 for a few matrices and up to d = 40 for hundreds, and its
@@ -220,7 +227,10 @@ size_t gram_ema_update_workspace(const mr_gram_problem* problems, int32_t count,
  * floor's size there; eigenvalues of A/c + eps/c above 1e-16 still
  * converge).
  * Workspace: at least inv_quarter_root_batched_workspace(...) bytes, 256-byte
- * aligned; its contents on entry are ignored.
+ * aligned; its contents on entry are ignored.  Per Newton matrix it holds
+ * 40 d^2 bytes (rounded up to 256), plus, for MR_NEWTON and MR_AUTO, the
+ * digit planes of M, T2 and T4 and M's row exponents, 18 dp^2 + 4 dp bytes
+ * (dp = d rounded up to 128).
  */
 mr_status inv_quarter_root_batched(const mr_root_problem* problems, int32_t count,
                                    mr_dtype a_dtype, double eps, int32_t normalize, int32_t method,

@@ -3,16 +3,16 @@
 // A float64 matrix X with one power-of-two exponent per row, e_i >= log2
 // max_j |X_ij|, is held as kOzSlices int8 digit planes D_0 .. D_5:
 //
-//   X_ij ~= 2^e_i * sum_p D_p[i][j] 2^-(6 + 7 p),   |D_p[i][j]| <= 64,
+//   X_ij ~= 2^e_i * sum_p D_p[i][j] 2^-(6 + 7 p),   |D_p[i][j]| <= 65,
 //
-// every digit the nearest integer to the remainder left by the previous
-// ones, so the planes hold X to 2^(e_i - 42).  The NT product C = A B^T of
+// the balanced base-128 digits of X_ij rounded to a multiple of 2^(e_i - 41),
+// so the planes hold X to 2^(e_i - 42).  The NT product C = A B^T of
 // two such matrices is
 //
 //   C_ij = 2^(eA_i + eB_j - 12) * sum_r 2^(-7 r) * (sum_{p + q = r} D^A_p D^B_q^T)_ij,
 //
 // with every plane product D^A_p D^B_q^T exact in int32 on
-// v_mfma_i32_32x32x32_i8 (|sum| <= 6 * K * 64^2 < 2^31 for K < 87000), one
+// v_mfma_i32_32x32x32_i8 (|sum| <= 6 * K * 65^2 < 2^31 for K < 84000), one
 // int32 accumulator per anti-diagonal r = p + q, and the pairs with
 // p + q > 5 left out: they weigh at most 2^-47 relative to the leading one,
 // below the representation error of the planes.  That is 21 int8 products
@@ -35,17 +35,33 @@ namespace mr {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-// Digit planes of value v with exponent e (|v| <= 2^e up to rounding): each
-// digit is clamped to the int8 range, which only an input outside that
-// bound (an indefinite matrix, a failed iteration) can reach.
-__device__ __forceinline__ void oz_digits(double v, int e, int8_t (&dg)[kOzSlices]) {
-  double r = ldexp(v, -e) * 64.0;
+// Digit planes of value v with exponent e (|v| <= 2^e up to rounding):
+// N = rint(v 2^(41 - e)) in two int32 halves (N = hi 2^21 + lo, both exact
+// conversions of float64), then balanced base-128 digits from the least
+// significant, each in [-64, 63] with the carry passed up; the leading digit
+// takes what is left (|digit| <= 65), clamped to the int8 range, which only
+// an input outside the bound (an indefinite matrix, a failed iteration) can
+// reach.  Digit p has weight 2^(e - 6 - 7 p).
+__host__ __device__ __forceinline__ void oz_digits(double v, int e, int8_t (&dg)[kOzSlices]) {
+  static_assert(kOzSlices == 6, "three digits per int32 half");
+  const double t = fmin(fmax(ldexp(v, 20 - e), -1073741824.0), 1073741824.0);
+  const double th = rint(t);
+  int hi = (int)th;
+  int x = (int)rint(ldexp(t - th, 21));  // |x| <= 2^20
 #pragma unroll
-  for (int p = 0; p < kOzSlices; ++p) {
-    const double q = fmin(fmax(rint(r), -127.0), 127.0);
-    dg[p] = (int8_t)(int)q;
-    r = (r - q) * 128.0;
+  for (int p = kOzSlices - 1; p >= 3; --p) {
+    const int dd = ((x + 64) & 127) - 64;
+    dg[p] = (int8_t)dd;
+    x = (x - dd) >> 7;
   }
+  hi += x;
+#pragma unroll
+  for (int p = 2; p >= 1; --p) {
+    const int dd = ((hi + 64) & 127) - 64;
+    dg[p] = (int8_t)dd;
+    hi = (hi - dd) >> 7;
+  }
+  dg[0] = (int8_t)min(max(hi, -127), 127);
 }
 
 // 128 x 128 output tile, 512 threads = 8 waves in a 4 x 2 grid of 32 x 64
@@ -151,7 +167,7 @@ __device__ __forceinline__ void oz_nt_tile(const int8_t* A, const int8_t* B, int
 }
 
 // float64 value of element v of block cb: sum_r 2^(-7 r) acc[r], times
-// 2^(e - 12) for the caller's e = eA_i + eB_j.
+// 2^(e - 12) for the caller's e = eA_i + eB_j (e = 12: the unscaled sum).
 __device__ __forceinline__ double oz_value(const v16i (&acc)[kOzSlices][2], int cb, int v, int e) {
   double x = (double)acc[kOzSlices - 1][cb][v];
 #pragma unroll

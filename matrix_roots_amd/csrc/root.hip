@@ -875,16 +875,32 @@ __global__ __launch_bounds__(256) void newton_slice_kernel(const NewtonLaunch L)
 //   stage 0: T2 = ((M/s)^2 - 10 M/s + 25 I) / 16   -> T2 planes
 //   stage 1: T4 = T2 T2                            -> T4 planes
 //   stage 2: M' = T4 M / s                         -> float64 M' and its split copy
-// The tile's values go through LDS (128 x kOzOutLd doubles, in the operand
-// stages the main loop has released) and leave as 16-element row segments of
-// the tile and of its mirror; a lane takes a row, so the LDS reads of a wave
-// (one column segment of 64 rows, or one row segment transposed) are
-// conflict-free with the odd row pitch.  Outside the d x d matrix the planes
-// get zeros.
-constexpr int kOzOutLd = kOzTile + 1;
+// The tile goes through LDS (in the operand stages the main loop has
+// released) as float64 values: row pitch kOzOutLd doubles (16 banks apart),
+// columns interleaved by 16-element segment with the segment index XORed
+// with r / 16, so that a row's eight segments and a column's eight 16-row
+// groups both read on distinct banks.  It leaves as rows: eight lanes write
+// one row of the tile, or of its mirror, 16 elements each, so every store
+// instruction fills whole 128-byte lines.  Stages 0 and 1 cut each value
+// into its digits once: a lane takes two row segments, stores their digits
+// as the tile's rows and keeps them in six 128 x 128 byte planes (byte
+// (r, c) in row r, segment (c / 16) XOR (r / 16 mod 8)), from which the
+// mirror's rows are gathered a byte at a time.  Outside the d x d matrix the
+// planes get zeros.
+constexpr int kOzOutLd = kOzTile + 8;
+constexpr int kOzPlaneBytes = kOzTile * kOzTile;
+__device__ __forceinline__ int oz_tpos(int r, int c) {
+  return r * kOzOutLd + ((c & 15) << 3) + ((c >> 4) ^ ((r >> 4) & 7));
+}
+__device__ __forceinline__ int oz_bpos(int r, int c) {
+  return r * kOzTile + ((((c >> 4) ^ (r >> 4)) & 7) << 4) + (c & 15);
+}
 __global__ __launch_bounds__(OzCfg::THREADS, 1) void newton_i8_kernel(const NewtonLaunch L) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[OzCfg::LDS_BYTES];
-  static_assert(kOzTile * kOzOutLd * 8 <= OzCfg::LDS_BYTES, "the output tile fits in the operand stages");
+  static_assert(kOzTile * kOzOutLd * 8 + 2 * kOzTile * 4 <= OzCfg::LDS_BYTES,
+                "the float64 tile and its exponents fit in the operand stages");
+  static_assert(kOzSlices * kOzPlaneBytes <= OzCfg::LDS_BYTES, "the byte planes fit in the operand stages");
+  static_assert(kOzTile == 128, "eight 16-element segments per row, eight 16-row groups per column");
   const StageJob s = stage_job(L, kStageI8);
   if (!s.active) return;
   const int d = s.d;
@@ -901,55 +917,116 @@ __global__ __launch_bounds__(OzCfg::THREADS, 1) void newton_i8_kernel(const Newt
   const int wm = wave >> 1, wn = wave & 1;
   const Roles64 r64 = roles64(s.region, d, L.t);
   const double is = 1.0 / s.s;
-  double* T = reinterpret_cast<double*>(smem);
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int li = wm * 32 + f32_row(lane, v), lj = wn * 64 + cb * 32 + (lane & 31);
-      const int gi = m0 + li, gj = n0 + lj;
-      const int ea = stage == 0 ? z.eM[gi] : stage == 1 ? kOzExpT2 : kOzExpT4;
-      const int eb = stage == 1 ? kOzExpT2 : z.eM[gj];
-      const double x = oz_value(acc, cb, v, ea + eb);
-      double val = 0.0;
-      if (gi < d && gj < d) {
-        if (stage == 0)
-          val = x * (is * is / 16.0) - (10.0 * is / 16.0) * r64.M[(int64_t)gi * d + gj] + (gi == gj ? 25.0 / 16.0 : 0.0);
-        else
-          val = stage == 1 ? x : x * is;
-      }
-      T[li * kOzOutLd + lj] = val;
-    }
-  __syncthreads();
-
   const bool diag = s.ti == s.tj;
-  const SplitBuf mx = roless(s.region, d, L.t).Mx;
-  int8_t* const out = stage == 0 ? z.T2 : z.T4;
-  const int eo = stage == 0 ? kOzExpT2 : kOzExpT4;
-  // pass 0: the tile's own region (on the diagonal: upper values, mirrored
-  // below); pass 1: the mirror region (n0.., m0..)
-  for (int pass = 0; pass < (diag ? 1 : 2); ++pass) {
-    const int R0 = pass == 0 ? m0 : n0, C0 = pass == 0 ? n0 : m0;
-    for (int sg = threadIdx.x; sg < kOzTile * (kOzTile / 16); sg += OzCfg::THREADS) {
-      const int lr = sg & (kOzTile - 1), c0 = (sg / kOzTile) * 16;
-      double w[16];
+  // the unscaled sums into LDS, the operands' exponents of the tile's rows
+  // (E[0..127]) and columns (E[128..255]) after them
+  double* T = reinterpret_cast<double*>(smem);
+  int* E = reinterpret_cast<int*>(smem + kOzTile * kOzOutLd * 8);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int li = wm * 32 + f32_row(lane, v);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) T[oz_tpos(li, wn * 64 + cb * 32 + (lane & 31))] = oz_value(acc, cb, v, 12);
+  }
+  if (threadIdx.x < 2 * kOzTile) {
+    const int i = threadIdx.x & (kOzTile - 1);
+    E[threadIdx.x] = threadIdx.x < kOzTile ? (stage == 0 ? z.eM[m0 + i] : stage == 1 ? kOzExpT2 : kOzExpT4)
+                                           : (stage == 1 ? kOzExpT2 : z.eM[n0 + i]);
+  }
+  __syncthreads();
+  // product element (m0 + a, n0 + b), as float64
+  auto prod = [&](int a, int b) __attribute__((always_inline)) {
+    return ldexp(T[oz_tpos(a, b)], E[a] + E[kOzTile + b] - 12);
+  };
+  if (stage < 2) {
+    // each lane takes two 16-element row segments of the tile: their values,
+    // then (the float64 tile released) their digits, stored as the tile's
+    // rows and kept in the byte planes for the mirror
+    constexpr int kSeg = kOzTile * (kOzTile / 16) / OzCfg::THREADS;
+    double w[kSeg][16];
+#pragma unroll
+    for (int it = 0; it < kSeg; ++it) {
+      const int q = threadIdx.x + it * OzCfg::THREADS;
+      const int lr = q >> 3, c0 = (q & 7) * 16;
+      const int gi = m0 + lr;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        const int lc = c0 + k;
-        w[k] = (pass == 1 || (diag && lr > lc)) ? T[lc * kOzOutLd + lr] : T[lr * kOzOutLd + lc];
+        const int gj = n0 + c0 + k;
+        const double x = prod(lr, c0 + k);
+        double val = 0.0;
+        if (gi < d && gj < d)
+          val = stage == 0 ? x * (is * is / 16.0) - (10.0 * is / 16.0) * r64.M[(int64_t)gi * d + gj] +
+                                 (gi == gj ? 25.0 / 16.0 : 0.0)
+                           : x;
+        w[it][k] = val;
       }
-      const int gi = R0 + lr, gj0 = C0 + c0;
-      if (stage < 2) {
-        oz_store16(w, eo, out + (int64_t)gi * dp + gj0, ps);
-      } else if (gi < d) {
+    }
+    __syncthreads();
+    unsigned char* Dg = smem;
+    int8_t* const out = stage == 0 ? z.T2 : z.T4;
+    const int eo = stage == 0 ? kOzExpT2 : kOzExpT4;
+#pragma unroll
+    for (int it = 0; it < kSeg; ++it) {
+      const int q = threadIdx.x + it * OzCfg::THREADS;
+      const int lr = q >> 3, c0 = (q & 7) * 16;
+      uint32_t pk[kOzSlices][4];
+#pragma unroll
+      for (int p = 0; p < kOzSlices; ++p)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) pk[p][u] = 0u;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        int8_t dg[kOzSlices];
+        oz_digits(w[it][k], eo, dg);
+#pragma unroll
+        for (int p = 0; p < kOzSlices; ++p) pk[p][k >> 2] |= (uint32_t)(uint8_t)dg[p] << (8 * (k & 3));
+      }
+      int8_t* dst = out + (int64_t)(m0 + lr) * dp + n0 + c0;
+#pragma unroll
+      for (int p = 0; p < kOzSlices; ++p) {
+        const v4i x = v4i{(int)pk[p][0], (int)pk[p][1], (int)pk[p][2], (int)pk[p][3]};
+        *reinterpret_cast<v4i*>(Dg + p * kOzPlaneBytes + oz_bpos(lr, c0)) = x;
+        if (!diag) *reinterpret_cast<v4i*>(dst + p * ps) = x;
+      }
+    }
+    __syncthreads();
+    // on the diagonal: the tile's region (upper bytes, mirrored below); else
+    // the mirror region (n0.., m0..)
+    const int R0 = diag ? m0 : n0, C0 = diag ? n0 : m0;
+    for (int q = threadIdx.x; q < kOzTile * (kOzTile / 16); q += OzCfg::THREADS) {
+      const int lr = q >> 3, c0 = (q & 7) * 16;
+      int8_t* dst = out + (int64_t)(R0 + lr) * dp + C0 + c0;
+#pragma unroll
+      for (int p = 0; p < kOzSlices; ++p) {
+        uint32_t wv[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-          const int gj = gj0 + k;
-          if (gj < d) {
-            const int64_t e = (int64_t)gi * d + gj;
-            r64.T2[e] = w[k];
-            split_put(mx, e, (float)w[k]);
-          }
+          const int lc = c0 + k;
+          const bool mir = !diag || lr > lc;
+          const uint32_t bt = Dg[p * kOzPlaneBytes + (mir ? oz_bpos(lc, lr) : oz_bpos(lr, lc))];
+          wv[k >> 2] |= bt << (8 * (k & 3));
+        }
+        *reinterpret_cast<v4i*>(dst + p * ps) = v4i{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
+      }
+    }
+    return;
+  }
+
+  const SplitBuf mx = roless(s.region, d, L.t).Mx;
+  for (int pass = 0; pass < (diag ? 1 : 2); ++pass) {
+    const int R0 = pass == 0 ? m0 : n0, C0 = pass == 0 ? n0 : m0;
+    for (int q = threadIdx.x; q < kOzTile * (kOzTile / 16); q += OzCfg::THREADS) {
+      const int lr = q >> 3, c0 = (q & 7) * 16;
+      const int gi = R0 + lr, gj0 = C0 + c0;
+      if (gi >= d) continue;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int lc = c0 + k, gj = gj0 + k;
+        if (gj < d) {
+          const double w = ((pass == 1 || (diag && lr > lc)) ? prod(lc, lr) : prod(lr, lc)) * is;
+          const int64_t e = (int64_t)gi * d + gj;
+          r64.T2[e] = w;
+          split_put(mx, e, (float)w);
         }
       }
     }
