@@ -28,8 +28,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 # Sources whose kernels a counter record covers, per kernel family.
 KERNEL_SOURCES = {
-    "quarter": ("csrc/gemm_core.hpp", "csrc/mr_common.hpp", "csrc/launch.hpp", "csrc/schedule.hpp",
-                "csrc/epilogue.hpp", "csrc/root.hip", "csrc/gram.hip", "csrc/apply.hip"),
+    "quarter": ("csrc/gemm_core.hpp", "csrc/gemm_i8.hpp", "csrc/mr_common.hpp", "csrc/launch.hpp",
+                "csrc/schedule.hpp", "csrc/epilogue.hpp", "csrc/root.hip", "csrc/gram.hip", "csrc/apply.hip"),
     "cans": ("csrc/gemm_core.hpp", "csrc/gemm_h16.hpp", "csrc/mr_common.hpp", "csrc/launch.hpp", "csrc/cans.hpp",
              "csrc/epilogue.hpp", "csrc/cans.hip"),
     "step": ("csrc/mr_common.hpp", "csrc/launch.hpp", "csrc/step.hpp", "csrc/step.hip"),
