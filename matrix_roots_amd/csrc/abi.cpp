@@ -219,7 +219,7 @@ RootPlan plan_root(const mr_root_problem* p, int32_t count, int32_t method) {
     c.first_slot = (int)P.slot_problem.size();
     c.count = (int)kv.second.size();
     // five float64 slots; the split-storage path adds the digit planes of its float64 steps
-    c.matrix_bytes = (size_t)oz_f64_bytes(c.d) + (split_path(method) ? (size_t)oz_extra_bytes(c.d) : 0);
+    c.matrix_bytes = (size_t)oz_f64_bytes(c.d) + (split_path(method) ? (size_t)oz_layout(c.d).extra : 0);
     for (int i : kv.second) P.slot_problem.push_back(i);
     P.classes.push_back(c);
     dmax_newton = std::max(dmax_newton, c.d);

@@ -24,7 +24,8 @@
 // accumulation per anti-diagonal are this file's.
 //
 // Planes are row-major with row stride dp = d rounded up to 128 (rows and
-// columns past d hold zero digits), plane p at base + p * dp * dp.
+// columns past d hold zero digits); each plane is contiguous, the six of a
+// matrix need not be (OzPlanes lists them).
 #pragma once
 
 #include "launch.hpp"
@@ -34,6 +35,10 @@ namespace mr {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+
+struct OzPlanes {
+  int8_t* p[kOzSlices];
+};
 
 // Digit planes of value v with exponent e (|v| <= 2^e up to rounding):
 // N = rint(v 2^(41 - e)) in two int32 halves (N = hi 2^21 + lo, both exact
@@ -84,13 +89,17 @@ static_assert(OzCfg::S * 2 * OzCfg::PLANE_UNITS == OzCfg::THREADS * OzCfg::S, "o
 // Copy chunk k0 .. k0+31 of rows m0.. (A) and n0.. (B), every plane, into
 // `stage`: 12 arrays of 256 units; wave w copies units 64 (w & 3) .. +63 of
 // the arrays of parity w >> 2.
-__device__ __forceinline__ void oz_issue(const int8_t* A, const int8_t* B, int64_t ld, int64_t ps, int m0, int n0,
-                                         int k0, unsigned char* stage, int wave, int lane) {
+__device__ __forceinline__ void oz_issue(const OzPlanes& A, const OzPlanes& B, int64_t ld, int m0, int n0, int k0,
+                                         unsigned char* stage, int wave, int lane) {
 #pragma unroll
   for (int j = 0; j < OzCfg::S; ++j) {
     const int a = 2 * j + (wave >> 2);
     const int op = a / OzCfg::S, p = a % OzCfg::S;
-    const int8_t* P = (op == 0 ? A : B) + p * ps;
+    // (p depends on the wave: select the pointer, never index the lists with it)
+    const int8_t* P = nullptr;
+#pragma unroll
+    for (int q = 0; q < OzCfg::S; ++q)
+      if (q == p) P = op == 0 ? A.p[q] : B.p[q];
     const int r0 = op == 0 ? m0 : n0;
     const int base_u = (wave & 3) * 64;
     const int u = base_u + lane;
@@ -133,8 +142,8 @@ __device__ __forceinline__ void oz_chunk(const unsigned char* __restrict__ st, v
 // Accumulators of the 128 x 128 tile at (m0, n0) of A B^T over K (a multiple
 // of 32; rows m0 .. m0+127 and n0 .. n0+127 exist in both plane sets).  Ends
 // with a block barrier: the LDS is free for the epilogue.
-__device__ __forceinline__ void oz_nt_tile(const int8_t* A, const int8_t* B, int64_t ld, int64_t ps, int K, int m0,
-                                           int n0, unsigned char* __restrict__ lds, v16i (&acc)[kOzSlices][2]) {
+__device__ __forceinline__ void oz_nt_tile(const OzPlanes& A, const OzPlanes& B, int64_t ld, int K, int m0, int n0,
+                                           unsigned char* __restrict__ lds, v16i (&acc)[kOzSlices][2]) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar LDS offsets
   const int wm = wave >> 1, wn = wave & 1;
@@ -145,8 +154,8 @@ __device__ __forceinline__ void oz_nt_tile(const int8_t* A, const int8_t* B, int
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[r][cb][v] = 0;
   const int nch = K / OzCfg::BK;
-  if (nch > 0) oz_issue(A, B, ld, ps, m0, n0, 0, lds, wave, lane);
-  if (nch > 1) oz_issue(A, B, ld, ps, m0, n0, OzCfg::BK, lds + OzCfg::STAGE_BYTES, wave, lane);
+  if (nch > 0) oz_issue(A, B, ld, m0, n0, 0, lds, wave, lane);
+  if (nch > 1) oz_issue(A, B, ld, m0, n0, OzCfg::BK, lds + OzCfg::STAGE_BYTES, wave, lane);
   for (int c = 0; c < nch; ++c) {
     const unsigned char* st = lds + (c % OzCfg::NST) * OzCfg::STAGE_BYTES;
     // chunk c is complete once at most the next chunk's copies are in flight
@@ -159,8 +168,7 @@ __device__ __forceinline__ void oz_nt_tile(const int8_t* A, const int8_t* B, int
     __builtin_amdgcn_s_barrier();  // chunk c visible to all waves; all are done with chunk c - 1
     asm volatile("" ::: "memory");
     if (c + 2 < nch)  // into the stage chunk c - 1 occupied
-      oz_issue(A, B, ld, ps, m0, n0, (c + 2) * OzCfg::BK, lds + ((c + 2) % OzCfg::NST) * OzCfg::STAGE_BYTES, wave,
-               lane);
+      oz_issue(A, B, ld, m0, n0, (c + 2) * OzCfg::BK, lds + ((c + 2) % OzCfg::NST) * OzCfg::STAGE_BYTES, wave, lane);
     oz_chunk(st, acc, lane, wm, wn);
   }
   __syncthreads();  // no wave reuses the LDS while another may still read the last stage

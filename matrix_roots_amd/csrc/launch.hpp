@@ -48,16 +48,39 @@ constexpr double kBoundSafety = 1.01;
 constexpr double kNoneFloorCap = 1e-16;
 
 // Float64 Newton steps of the default path run their products on int8 digit
-// planes (gemm_i8.hpp): kOzSlices planes per matrix, rows and columns padded
-// to dp = d rounded up to kOzTile.  Per matrix, after the five float64 slots
-// of d*d: the planes of M, of T2 and of T4, then M's row exponents (dp int32).
+// planes (gemm_i8.hpp): kOzSlices planes per matrix, each dp x dp bytes (dp =
+// d rounded up to kOzTile), for M, T2 and T4, plus M's row exponents (dp
+// int32).  They live in the parts of the five float64 slots of d*d that a
+// float64 step leaves idle, where those are 16-byte aligned (d a multiple of
+// 4): M's and T4's twelve planes fill the fifth slot (8 d^2 bytes) and the
+// second half of the second (4 d^2, a split half-slot no step uses) as far
+// as whole planes go; T2's six sit in the slot that will take M' (its float64
+// M of the step before is dead, and stage 2 writes M' only once T2 is read),
+// when they fit.  The rest, and the exponents, follow the slots.
 constexpr int kOzSlices = 6;
 constexpr int kOzTile = 128;
 __host__ __device__ inline int64_t oz_pad(int64_t d) { return (d + kOzTile - 1) / kOzTile * kOzTile; }
-__host__ __device__ inline int64_t oz_f64_bytes(int64_t d) { return (40 * d * d + 255) & ~(int64_t)255; }
-__host__ __device__ inline int64_t oz_set_bytes(int64_t d) { return kOzSlices * oz_pad(d) * oz_pad(d); }
-__host__ __device__ inline int64_t oz_extra_bytes(int64_t d) {
-  return (3 * oz_set_bytes(d) + 4 * oz_pad(d) + 255) & ~(int64_t)255;
+__host__ __device__ inline int64_t oz_align256(int64_t n) { return (n + 255) & ~(int64_t)255; }
+__host__ __device__ inline int64_t oz_f64_bytes(int64_t d) { return oz_align256(40 * d * d); }
+struct OzLayout {
+  int64_t plane;     // bytes per plane, dp * dp
+  int n_slot4;       // persistent planes (M's 0..5, then T4's) in the fifth slot
+  int n_half3;       // ... then in half-slot 3
+  int t2_in_slot;    // T2's planes in the slot that will take M'
+  int64_t extra;     // bytes past the float64 slots: exponents, then the other planes
+};
+__host__ __device__ inline OzLayout oz_layout(int64_t d) {
+  OzLayout L;
+  const int64_t dp = oz_pad(d), d2 = d * d;
+  L.plane = dp * dp;
+  const bool holes = d % 4 == 0;
+  const int64_t b = holes ? 8 * d2 / L.plane : 0, a = holes ? 4 * d2 / L.plane : 0;
+  L.n_slot4 = (int)(b < 2 * kOzSlices ? b : 2 * kOzSlices);
+  L.n_half3 = (int)(a < 2 * kOzSlices - L.n_slot4 ? a : 2 * kOzSlices - L.n_slot4);
+  L.t2_in_slot = holes && kOzSlices * L.plane <= 8 * d2 ? 1 : 0;
+  const int64_t over = 2 * kOzSlices - L.n_slot4 - L.n_half3 + (L.t2_in_slot ? 0 : kOzSlices);
+  L.extra = oz_align256(4 * dp) + over * L.plane;
+  return L;
 }
 
 // Workgroup ranges of jobs and size classes start on multiples of 8 (one per

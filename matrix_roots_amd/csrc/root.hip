@@ -58,7 +58,7 @@ struct Roles64 {
 struct Roles32 {
   float *M, *T2, *X, *Xn, *T4;
 };
-__device__ __forceinline__ Roles64 roles64(char* region, int d, int t) {
+__host__ __device__ __forceinline__ Roles64 roles64(char* region, int d, int t) {
   const int64_t S = (int64_t)d * d * 8;
   const bool even = (t & 1) == 0;
   Roles64 r;
@@ -90,14 +90,14 @@ struct SplitBuf {
   _Float16* lo;
   __device__ SplitRef ref() const { return SplitRef{hi, lo}; }
 };
-__device__ __forceinline__ SplitBuf split_at(char* region, int d, int h) {
+__host__ __device__ __forceinline__ SplitBuf split_at(char* region, int d, int h) {
   _Float16* hi = reinterpret_cast<_Float16*>(region + (int64_t)h * d * d * 4);
   return SplitBuf{hi, hi + (int64_t)d * d};
 }
 struct RolesS {
   SplitBuf M, T2, X, Xn, T4, Mx, Q;
 };
-__device__ __forceinline__ RolesS roless(char* region, int d, int t) {
+__host__ __device__ __forceinline__ RolesS roless(char* region, int d, int t) {
   const bool even = (t & 1) == 0;
   RolesS r;
   r.M = split_at(region, d, even ? 8 : 0);
@@ -747,9 +747,9 @@ __global__ __launch_bounds__(X3W::THREADS, 1) void newton_x3w_kernel(const Newto
   }
 }
 
-// 16 values -> kOzSlices planes of 16 digits at dst (+ p * ps), one 16-byte
+// 16 values -> their digits at byte offset `off` of each plane, one 16-byte
 // store per plane.
-__device__ __forceinline__ void oz_store16(const double (&w)[16], int e, int8_t* dst, int64_t ps) {
+__device__ __forceinline__ void oz_store16(const double (&w)[16], int e, const OzPlanes& P, int64_t off) {
   uint32_t pk[kOzSlices][4];
 #pragma unroll
   for (int p = 0; p < kOzSlices; ++p)
@@ -764,7 +764,7 @@ __device__ __forceinline__ void oz_store16(const double (&w)[16], int e, int8_t*
   }
 #pragma unroll
   for (int p = 0; p < kOzSlices; ++p)
-    *reinterpret_cast<v4i*>(dst + p * ps) = v4i{(int)pk[p][0], (int)pk[p][1], (int)pk[p][2], (int)pk[p][3]};
+    *reinterpret_cast<v4i*>(P.p[p] + off) = v4i{(int)pk[p][0], (int)pk[p][1], (int)pk[p][2], (int)pk[p][3]};
 }
 
 // ------------------------------------------------ int8 digit-plane steps
@@ -779,19 +779,34 @@ __device__ __forceinline__ void oz_store16(const double (&w)[16], int e, int8_t*
 // largest entries, sit near the top of those ranges), and their planes come
 // straight from the product epilogues.  Stage 2 writes the float64 M' and its
 // split copy, as the float64 kernel does.
+// Plane positions (oz_layout): M's planes are persistent planes 0..5, T4's
+// 6..11; T2's at iteration t are in the float64 slot M' of iteration t takes.
 struct OzRegion {
-  int8_t *M, *T2, *T4;
+  OzPlanes M, T2, T4;
   int32_t* eM;  // M's row exponents
   int64_t dp;
 };
-__device__ __forceinline__ OzRegion oz_region(char* region, int d) {
+__host__ __device__ __forceinline__ OzRegion oz_region(char* region, int d, int t) {
+  const OzLayout ly = oz_layout(d);
+  const int64_t d2 = (int64_t)d * d;
+  char* extra = region + oz_f64_bytes(d);
+  char* over = extra + oz_align256(4 * oz_pad(d));
+  auto persistent = [&](int i) -> int8_t* {
+    if (i < ly.n_slot4) return reinterpret_cast<int8_t*>(region + 32 * d2 + i * ly.plane);
+    if (i < ly.n_slot4 + ly.n_half3)
+      return reinterpret_cast<int8_t*>(region + 12 * d2 + (i - ly.n_slot4) * ly.plane);
+    return reinterpret_cast<int8_t*>(over + (i - ly.n_slot4 - ly.n_half3) * ly.plane);
+  };
   OzRegion z;
-  const int64_t set = oz_set_bytes(d);
-  int8_t* base = reinterpret_cast<int8_t*>(region + oz_f64_bytes(d));
-  z.M = base;
-  z.T2 = base + set;
-  z.T4 = base + 2 * set;
-  z.eM = reinterpret_cast<int32_t*>(base + 3 * set);
+#pragma unroll
+  for (int p = 0; p < kOzSlices; ++p) {
+    z.M.p[p] = persistent(p);
+    z.T4.p[p] = persistent(kOzSlices + p);
+    z.T2.p[p] = ly.t2_in_slot
+                    ? reinterpret_cast<int8_t*>(reinterpret_cast<char*>(roles64(region, d, t).T2) + p * ly.plane)
+                    : reinterpret_cast<int8_t*>(over + (2 * kOzSlices - ly.n_slot4 - ly.n_half3 + p) * ly.plane);
+  }
+  z.eM = reinterpret_cast<int32_t*>(extra);
   z.dp = oz_pad(d);
   return z;
 }
@@ -817,7 +832,7 @@ __global__ __launch_bounds__(256) void newton_slice_kernel(const NewtonLaunch L)
   if (!(t < st.j && t < st.K - 1)) return;
   const int d = C.d;
   char* region = C.region + (int64_t)mat * C.matrix_bytes;
-  const OzRegion z = oz_region(region, d);
+  const OzRegion z = oz_region(region, d, t);
   const double* M = roles64(region, d, t).M + (int64_t)row * d;
   const bool real = row < d;
   const bool vec = (d & 1) == 0;  // 16-byte loads (rows 16-byte aligned)
@@ -855,7 +870,6 @@ __global__ __launch_bounds__(256) void newton_slice_kernel(const NewtonLaunch L)
   int e = 0;
   if (mx > 0.0) frexp(mx, &e);  // mx < 2^e
   if (threadIdx.x == 0) z.eM[row] = e;
-  const int64_t ps = z.dp * z.dp;
   for (int c0 = threadIdx.x * 16, i = 0; c0 < z.dp; c0 += 256 * 16, ++i) {
     double w[16];
     if (i < kOzSliceSeg) {
@@ -867,7 +881,7 @@ __global__ __launch_bounds__(256) void newton_slice_kernel(const NewtonLaunch L)
     } else {
       load16(c0, w);
     }
-    oz_store16(w, e, z.M + (int64_t)row * z.dp + c0, ps);
+    oz_store16(w, e, z.M, (int64_t)row * z.dp + c0);
   }
 }
 
@@ -905,13 +919,17 @@ __global__ __launch_bounds__(OzCfg::THREADS, 1) void newton_i8_kernel(const Newt
   if (!s.active) return;
   const int d = s.d;
   const int stage = L.stage;
-  const OzRegion z = oz_region(s.region, d);
-  const int64_t dp = z.dp, ps = dp * dp;
-  const int8_t* A = stage == 0 ? z.M : stage == 1 ? z.T2 : z.T4;
-  const int8_t* B = stage == 1 ? z.T2 : z.M;
+  const OzRegion z = oz_region(s.region, d, L.t);
+  const int64_t dp = z.dp;
+  OzPlanes A, B;  // by value: a reference picked at run time would put z in scratch memory
+#pragma unroll
+  for (int p = 0; p < kOzSlices; ++p) {
+    A.p[p] = stage == 0 ? z.M.p[p] : stage == 1 ? z.T2.p[p] : z.T4.p[p];
+    B.p[p] = stage == 1 ? z.T2.p[p] : z.M.p[p];
+  }
   const int m0 = s.ti * kOzTile, n0 = s.tj * kOzTile;
   v16i acc[kOzSlices][2];
-  oz_nt_tile(A, B, dp, ps, (int)dp, m0, n0, smem, acc);
+  oz_nt_tile(A, B, dp, (int)dp, m0, n0, smem, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -963,7 +981,9 @@ __global__ __launch_bounds__(OzCfg::THREADS, 1) void newton_i8_kernel(const Newt
     }
     __syncthreads();
     unsigned char* Dg = smem;
-    int8_t* const out = stage == 0 ? z.T2 : z.T4;
+    OzPlanes out;
+#pragma unroll
+    for (int p = 0; p < kOzSlices; ++p) out.p[p] = stage == 0 ? z.T2.p[p] : z.T4.p[p];
     const int eo = stage == 0 ? kOzExpT2 : kOzExpT4;
 #pragma unroll
     for (int it = 0; it < kSeg; ++it) {
@@ -981,12 +1001,12 @@ __global__ __launch_bounds__(OzCfg::THREADS, 1) void newton_i8_kernel(const Newt
 #pragma unroll
         for (int p = 0; p < kOzSlices; ++p) pk[p][k >> 2] |= (uint32_t)(uint8_t)dg[p] << (8 * (k & 3));
       }
-      int8_t* dst = out + (int64_t)(m0 + lr) * dp + n0 + c0;
+      const int64_t off = (int64_t)(m0 + lr) * dp + n0 + c0;
 #pragma unroll
       for (int p = 0; p < kOzSlices; ++p) {
         const v4i x = v4i{(int)pk[p][0], (int)pk[p][1], (int)pk[p][2], (int)pk[p][3]};
         *reinterpret_cast<v4i*>(Dg + p * kOzPlaneBytes + oz_bpos(lr, c0)) = x;
-        if (!diag) *reinterpret_cast<v4i*>(dst + p * ps) = x;
+        if (!diag) *reinterpret_cast<v4i*>(out.p[p] + off) = x;
       }
     }
     __syncthreads();
@@ -995,7 +1015,7 @@ __global__ __launch_bounds__(OzCfg::THREADS, 1) void newton_i8_kernel(const Newt
     const int R0 = diag ? m0 : n0, C0 = diag ? n0 : m0;
     for (int q = threadIdx.x; q < kOzTile * (kOzTile / 16); q += OzCfg::THREADS) {
       const int lr = q >> 3, c0 = (q & 7) * 16;
-      int8_t* dst = out + (int64_t)(R0 + lr) * dp + C0 + c0;
+      const int64_t off = (int64_t)(R0 + lr) * dp + C0 + c0;
 #pragma unroll
       for (int p = 0; p < kOzSlices; ++p) {
         uint32_t wv[4] = {0u, 0u, 0u, 0u};
@@ -1006,7 +1026,7 @@ __global__ __launch_bounds__(OzCfg::THREADS, 1) void newton_i8_kernel(const Newt
           const uint32_t bt = Dg[p * kOzPlaneBytes + (mir ? oz_bpos(lc, lr) : oz_bpos(lr, lc))];
           wv[k >> 2] |= bt << (8 * (k & 3));
         }
-        *reinterpret_cast<v4i*>(dst + p * ps) = v4i{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
+        *reinterpret_cast<v4i*>(out.p[p] + off) = v4i{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
       }
     }
     return;

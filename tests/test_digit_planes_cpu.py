@@ -103,3 +103,80 @@ def test_anti_diagonal_product(tmp_path):
             assert abs(c - exact) <= bound, (i, j, float(c - exact), float(bound))
     # int32 headroom of one anti-diagonal at K = 8192: at most 6 pairs of 65 x 65
     assert 6 * 8192 * 65 * 65 < 2 ** 31
+
+
+LAYOUT = r"""
+#include "root.hip"
+#include <cstdio>
+#include <vector>
+struct Iv { long a, b; const char* what; };
+static bool overlap(const Iv& x, const Iv& y) { return x.a < y.b && y.a < x.b; }
+int main() {
+  int bad = 0;
+  std::vector<int> ds;
+  for (int d = 33; d <= 600; ++d) ds.push_back(d);
+  for (int d : {1024, 1056, 1184, 1248, 1536, 2048, 3072, 4096, 8192}) ds.push_back(d);
+  for (int d : ds) {
+    const mr::OzLayout ly = mr::oz_layout(d);
+    const long d2 = (long)d * d, dp = mr::oz_pad(d);
+    const long bytes = mr::oz_f64_bytes(d) + ly.extra;
+    if (bytes % 256 != 0) { std::printf("d=%d: region %ld not a multiple of 256\n", d, bytes); ++bad; }
+    for (int t = 0; t < 2; ++t) {
+      char* R = nullptr;
+      const mr::OzRegion z = mr::oz_region(R + 4096, d, t);  // offsets from a 4096-aligned base
+      const mr::Roles64 r64 = mr::roles64(R + 4096, d, t);
+      const mr::RolesS rs = mr::roless(R + 4096, d, t);
+      auto off = [&](const void* p) { return (long)((const char*)p - (R + 4096)); };
+      // live through a float64 step: M (float64), X, X', the split copy of M
+      std::vector<Iv> live = {{off(r64.M), off(r64.M) + 8 * d2, "M f64"},
+                              {off(rs.X.hi), off(rs.X.hi) + 4 * d2, "X"},
+                              {off(rs.Xn.hi), off(rs.Xn.hi) + 4 * d2, "X'"},
+                              {off(rs.Mx.hi), off(rs.Mx.hi) + 4 * d2, "Mx"}};
+      std::vector<Iv> mine;
+      for (int p = 0; p < mr::kOzSlices; ++p) {
+        mine.push_back({off(z.M.p[p]), off(z.M.p[p]) + ly.plane, "M plane"});
+        mine.push_back({off(z.T4.p[p]), off(z.T4.p[p]) + ly.plane, "T4 plane"});
+        mine.push_back({off(z.T2.p[p]), off(z.T2.p[p]) + ly.plane, "T2 plane"});
+      }
+      mine.push_back({off(z.eM), off(z.eM) + 4 * dp, "exponents"});
+      const Iv slot_next = {off(r64.T2), off(r64.T2) + 8 * d2, "M' slot"};
+      for (size_t i = 0; i < mine.size(); ++i) {
+        const Iv& x = mine[i];
+        if (x.a < 0 || x.b > bytes || (x.a % 16) != 0) {
+          std::printf("d=%d t=%d: %s [%ld,%ld) outside [0,%ld) or misaligned\n", d, t, x.what, x.a, x.b, bytes);
+          ++bad;
+        }
+        for (const Iv& y : live)
+          if (overlap(x, y)) { std::printf("d=%d t=%d: %s overlaps %s\n", d, t, x.what, y.what); ++bad; }
+        // only T2's planes may sit in the slot M' is written to (after stage 1)
+        if (x.what[0] != 'T' || x.what[1] != '2')
+          if (overlap(x, slot_next)) { std::printf("d=%d t=%d: %s overlaps the M' slot\n", d, t, x.what); ++bad; }
+        for (size_t j = i + 1; j < mine.size(); ++j)
+          if (overlap(x, mine[j])) { std::printf("d=%d t=%d: %s overlaps %s\n", d, t, x.what, mine[j].what); ++bad; }
+      }
+    }
+    if (bad > 20) break;
+  }
+  // the planes sit in the float64 slots where they fit (no growth for d % 128 == 0)
+  if (mr::oz_layout(4096).extra != 16384 || mr::oz_layout(1024).extra != 4096) { std::printf("extra grew\n"); ++bad; }
+  std::printf("%s\n", bad ? "FAIL" : "OK");
+  return bad != 0;
+}
+"""
+
+
+def test_plane_layout(tmp_path):
+    """The digit planes of M, T2 and T4 and M's exponents never overlap each
+    other or what a float64 step keeps live (M, X, X', the split copy of M),
+    stay inside the region, are 16-byte aligned, and only T2's share the slot
+    M' is written to; for d a multiple of 128 they add nothing but the
+    exponents to the region."""
+    src = tmp_path / "layout.hip"
+    src.write_text(LAYOUT)
+    exe = tmp_path / "layout"
+    cmd = [mb.hipcc(), "-O1", "-std=c++17", f"--offload-arch={mb.ARCH}", "-I", mb.CSRC, "-x", "hip", str(src),
+           "-o", str(exe)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0 and run.stdout.strip().endswith("OK"), run.stdout[-3000:]
