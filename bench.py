@@ -78,10 +78,13 @@ def blas_vendor() -> str:
     return "unknown"
 
 
-def f64_class(trace) -> str:
-    """Kernel class of the float64 steps' products: newton_i8 (int8 digit
-    planes, the default path) unless only the float64 kernel ran."""
-    return "newton_f64" if "newton_f64" in trace and "newton_i8" not in trace else "newton_i8"
+I8_MIN_D = 1024  # the library's kI8MinD: Grams from this size take the int8 digit-plane products
+
+
+def f64_class(d: int) -> str:
+    """Kernel class of the float64 steps' products of a d x d Gram on the
+    default path: int8 digit planes from I8_MIN_D, the float64 kernel below."""
+    return "newton_i8" if d >= I8_MIN_D else "newton_f64"
 
 
 def sym_gemm_flops(d: int) -> float:
@@ -124,10 +127,10 @@ def root_stream_bytes(d: int, state_bytes: int, packed: bool, K: int, j: int):
                     M0 and X1 (4 bytes each) per element;
       newton_convert  at the float64 -> split switch: reads M (8), writes its
                     split copy (4) per element;
-      newton_slice  each float64 step with products (t < min(j, K - 1)):
-                    reads M (8 per element), writes its six digit planes (6
-                    per element of the matrix padded to dp, a multiple of 128)
-                    and dp row exponents (4 each);
+      newton_slice  each float64 step with products (t < min(j, K - 1)) of a
+                    Gram of I8_MIN_D or more: reads M (8 per element), writes
+                    its six digit planes (6 per element of the matrix padded
+                    to dp, a multiple of 128) and dp row exponents (4 each);
       root_finalize reads X (split, 4) and M_{K-1} (8 in float64, 4 split),
                     writes X (float32, 4) per element."""
     n = d * d
@@ -137,7 +140,7 @@ def root_stream_bytes(d: int, state_bytes: int, packed: bool, K: int, j: int):
     return {"root_stats": state_bytes * stored,
             "root_init": state_bytes * stored + 16 * n,
             "newton_convert": 12 * n if j < K else 0,
-            "newton_slice": (8 * n + 6 * dp * dp + 4 * dp) * max(min(j, K - 1), 0),
+            "newton_slice": (8 * n + 6 * dp * dp + 4 * dp) * max(min(j, K - 1), 0) if d >= I8_MIN_D else 0,
             "root_finalize": (4 + m_last + 4) * n}
 
 
@@ -347,6 +350,7 @@ def per_size_class(B, torch, grams, wl, min_d=129):
             a, b = newton_flops(d, int(r["iters"]), int(r["fp64_iters"]), final_degree=int(r["final_degree"]))
             f64 += a
             low += b
+        # (one size per call: its float64 products ran on one kernel class, f64_class(d))
         tf = (f64 + low) / (ms / 1e3) / 1e12
         ent = {"count": len(As), "ms": round(ms, 3), "tflops": round(tf, 2),
                "fp32_equivalent_pct_of_fp32_peak": round(100 * tf / PEAK_TFLOPS["f32"], 2),
@@ -464,7 +468,8 @@ def bench_steps(args, torch, B, W, peaks):
 
     # algorithmic work and bytes over the timed steps
     es = 8 if args.state_dtype == "f64" else 4
-    f64 = low = 0.0
+    f64 = {"newton_i8": 0.0, "newton_f64": 0.0}
+    low = 0.0
     sbytes = {"root_stats": 0, "root_init": 0, "newton_convert": 0, "newton_slice": 0, "root_finalize": 0}
     iters = []
     n_newton = 0
@@ -478,20 +483,20 @@ def bench_steps(args, torch, B, W, peaks):
             n_newton += 1
             K, j = int(rec["iters"]), int(rec["fp64_iters"])
             a, b = newton_flops(d, K, j, final_degree=int(rec["final_degree"]))
-            f64 += a
+            f64[f64_class(d)] += a
             low += b
             for kk, v in root_stream_bytes(d, es, args.packed_state, K, j).items():
                 sbytes[kk] += v
             iters.append((K, j))
     syrk = sum(m * (m + 1) * n + n * (n + 1) * m for m, n in shapes) * args.steps
     apply_f = sum(2.0 * m * n * (m + n) for m, n in shapes) * args.steps
-    step_flops = (f64 + low + syrk + apply_f) / args.steps
+    step_flops = (sum(f64.values()) + low + syrk + apply_f) / args.steps
 
     elems = sum(m * n for m, n in shapes) * args.steps
     sbytes.update({"momentum": 12 * elems, "hyperball_reduce": 8 * elems, "hyperball_update": 12 * elems,
                    # maxima and split copies of XR, G, XL and W^T: 8 bytes read and 4 written per element
                    "apply_split": 12 * sum(m * m + 2 * m * n + n * n for m, n in shapes) * args.steps})
-    flops = {f64_class(trace): f64, "newton_x3": low, "syrk_ema": syrk, "apply_x3": apply_f}
+    flops = {**f64, "newton_x3": low, "syrk_ema": syrk, "apply_x3": apply_f}
     kernels = kernel_table(trace, flops, sbytes)
     # the syrk's HBM bytes (state read + write, gradient read) as context: it is matrix-core bound
     if "syrk_ema" in kernels:
@@ -661,7 +666,7 @@ def bench_illcond(args, torch, B, W, peaks):
                                "fp64_iters": [int(info["fp64_iters"].min()), int(info["fp64_iters"].max())],
                                "tflops": round((ef64 + elow) / (cms / 1e3) / 1e12, 2)}
         log(f"eps {eps:g}: {per_eps[f'{eps:g}']}")
-    kernels = kernel_table(trace, {f64_class(trace): f64, "newton_x3": low}, sbytes)
+    kernels = kernel_table(trace, {f64_class(512): f64, "newton_x3": low}, sbytes)
     dname = max((kv for kv in kernels.items() if "tflops" in kv[1]), key=lambda kv: kv[1]["ms_total"])[0]
     cpu = None
     if not args.no_cpu_baseline:

@@ -195,7 +195,7 @@ struct RootPlan {
 std::atomic<int32_t> g_jacobi_max_sweeps{kJacobiDefaultSweeps};
 
 // Default Newton path: X in split-fp16 storage from the first step, the
-// float64 steps' products on int8 digit planes.
+// float64 steps' products on int8 digit planes from kI8MinD.
 bool split_path(int32_t method) { return method != MR_NEWTON_F64 && method != MR_NEWTON_F32; }
 
 bool use_jacobi(int64_t d, int32_t method) {
@@ -218,8 +218,10 @@ RootPlan plan_root(const mr_root_problem* p, int32_t count, int32_t method) {
     c.d = kv.first;
     c.first_slot = (int)P.slot_problem.size();
     c.count = (int)kv.second.size();
-    // five float64 slots; the split-storage path adds the digit planes of its float64 steps
-    c.matrix_bytes = (size_t)oz_f64_bytes(c.d) + (split_path(method) ? (size_t)oz_layout(c.d).extra : 0);
+    // five float64 slots; the split-storage path adds what of the digit
+    // planes of its float64 steps does not fit in them (d >= kI8MinD)
+    c.matrix_bytes =
+        (size_t)oz_f64_bytes(c.d) + (split_path(method) && c.d >= kI8MinD ? (size_t)oz_layout(c.d).extra : 0);
     for (int i : kv.second) P.slot_problem.push_back(i);
     P.classes.push_back(c);
     dmax_newton = std::max(dmax_newton, c.d);
@@ -925,30 +927,33 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
     // vec64: float64 loads of 2 (d even); vec32: float32 loads of 4 (d % 4 == 0);
     // vecx3: fp16 loads of 8 (d % 8 == 0).
     // wide: d % 32 == 0 and d >= kWideMinD, the split-fp16 stages run on 256 x 256 tiles.
+    // i8: the float64 steps' products on int8 digit planes (split path, d >= kI8MinD).
     struct Group {
       std::vector<int> cls;
       int vec64, vec32, vecx3;
-      bool wide;
+      bool wide, i8;
     };
     std::vector<Group> groups;
-    for (const int align : {32, 8, 4, 2, 1}) {
-      Group g;
-      g.vec64 = align >= 2 ? 2 : 1;
-      g.vec32 = align >= 4 ? 4 : 1;
-      g.vecx3 = align >= 8 ? 8 : 1;
-      g.wide = align == 32;  // split-fp16 stages on 256 x 256 tiles
-      for (int ci = 0; ci < (int)P.classes.size(); ++ci) {
-        const int64_t d = P.classes[ci].d;
-        const int a = d % 32 == 0 && d >= kWideMinD ? 32 : d % 8 == 0 ? 8 : d % 4 == 0 ? 4 : d % 2 == 0 ? 2 : 1;
-        if (a != align) continue;
-        g.cls.push_back(ci);
-        if ((int)g.cls.size() == kMaxClasses) {
-          groups.push_back(g);
-          g.cls.clear();
+    for (const int align : {32, 8, 4, 2, 1})
+      for (const bool big : {true, false}) {
+        Group g;
+        g.vec64 = align >= 2 ? 2 : 1;
+        g.vec32 = align >= 4 ? 4 : 1;
+        g.vecx3 = align >= 8 ? 8 : 1;
+        g.wide = align == 32;  // split-fp16 stages on 256 x 256 tiles
+        g.i8 = x_low && big;
+        for (int ci = 0; ci < (int)P.classes.size(); ++ci) {
+          const int64_t d = P.classes[ci].d;
+          const int a = d % 32 == 0 && d >= kWideMinD ? 32 : d % 8 == 0 ? 8 : d % 4 == 0 ? 4 : d % 2 == 0 ? 2 : 1;
+          if (a != align || (d >= kI8MinD) != big) continue;
+          g.cls.push_back(ci);
+          if ((int)g.cls.size() == kMaxClasses) {
+            groups.push_back(g);
+            g.cls.clear();
+          }
         }
+        if (!g.cls.empty()) groups.push_back(g);
       }
-      if (!g.cls.empty()) groups.push_back(g);
-    }
     // tile: 256 for the wide split-fp16 kernel, else 128
     auto make_launch = [&](const Group& g, int kind, int stage, int t, int job_only, int tile = 128) {
       NewtonLaunch L;
@@ -977,7 +982,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
         if (kind == 0)
           C.blocks_per_matrix = (stage == 0 && job_only < 0 ? 2 : 1) * C.U;
         else if (kind == 2)
-          C.blocks_per_matrix = (int32_t)oz_pad(c.d);  // digit planes of M: a workgroup per padded row
+          C.blocks_per_matrix = (int32_t)(oz_pad(c.d) / kOzSliceRows);  // digit planes of M: a wave per padded row
         else
           C.blocks_per_matrix = (int32_t)((c.d * c.d + 2047) / 2048);
         C.nblocks = C.blocks_per_matrix * C.count;
@@ -992,21 +997,22 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
                            "newton convert")) != MR_OK)
             return st;
       }
-      if (t < j_max && x_low) {  // digit planes of M
+      if (t < j_max) {  // digit planes of M
         for (const auto& g : groups)
-          if ((st = traced(kTrSlice, true, s, [&] { return launch_newton_slice(make_launch(g, 2, 0, t, -1), s); },
-                           "newton slice")) != MR_OK)
+          if (g.i8 && (st = traced(kTrSlice, true, s,
+                                   [&] { return launch_newton_slice(make_launch(g, 2, 0, t, -1), s); },
+                                   "newton slice")) != MR_OK)
             return st;
       }
       for (int stage = 0; stage < 3; ++stage) {
         for (const auto& g : groups) {
           if (t < j_max) {
-            // float64 steps; with x_low the products run on digit planes and
-            // the X update goes to the split-fp16 kernel
+            // float64 steps; with x_low the X update goes to the split-fp16
+            // kernel, and from kI8MinD the products run on digit planes
             const bool split = x_low && stage == 0;
             const NewtonLaunch L64 = make_launch(g, 0, stage, t, split ? 0 : -1);
-            if ((st = traced(x_low ? kTrNewtonI8 : kTrNewton64, true, s,
-                             [&] { return launch_newton_stage(L64, x_low ? kStageI8 : kStageF64, g.vec64, s); },
+            if ((st = traced(g.i8 ? kTrNewtonI8 : kTrNewton64, true, s,
+                             [&] { return launch_newton_stage(L64, g.i8 ? kStageI8 : kStageF64, g.vec64, s); },
                              "newton f64 stage")) != MR_OK)
               return st;
             if (split && t > 0) {  // the first X update is part of the init

@@ -36,6 +36,13 @@ constexpr int kJacobiAutoMaxD = 32;
 // 716 against 759 ms with narrow tiles; 80 x 1024^2 + 16 x 4096^2: 199
 // against 208), and the 1024^2 class takes either at the same speed.
 constexpr int kWideMinD = 1024;
+// Smallest Gram size whose float64 Newton steps take the int8 digit-plane
+// products (smaller ones keep the float64 kernel).  Measured on MI355X per
+// size class, digit-plane stages (plus the pass that cuts M's planes) against
+// the float64 kernel: 512^2 x 256 (ill-conditioned batch) 26.3 + 6.5 against
+// 27.9 ms per step of three calls; 1024^2 x 80: 9.0 + 0.5 against 9.8 ms;
+// 1536^2 x 128: 17.7 against 23.8 ms; 4096^2 x 16: 77.8 against 98.8 ms.
+constexpr int kI8MinD = 1024;
 constexpr int kJacobiDefaultSweeps = 30;
 constexpr int kJacobiMaxSweeps = 100;
 constexpr int kStatsRows = 32;       // rows of A per statistics workgroup (one 32-row tile stripe)
@@ -59,6 +66,7 @@ constexpr double kNoneFloorCap = 1e-16;
 // when they fit.  The rest, and the exponents, follow the slots.
 constexpr int kOzSlices = 6;
 constexpr int kOzTile = 128;
+constexpr int kOzSliceRows = 16;  // rows per workgroup of the pass that cuts M's planes
 __host__ __device__ inline int64_t oz_pad(int64_t d) { return (d + kOzTile - 1) / kOzTile * kOzTile; }
 __host__ __device__ inline int64_t oz_align256(int64_t n) { return (n + 255) & ~(int64_t)255; }
 __host__ __device__ inline int64_t oz_f64_bytes(int64_t d) { return oz_align256(40 * d * d); }

@@ -812,76 +812,61 @@ __host__ __device__ __forceinline__ OzRegion oz_region(char* region, int d, int 
 }
 constexpr int kOzExpT2 = 1, kOzExpT4 = 2;
 
-// Digit planes of M (iteration t) with per-row exponents: one workgroup per
-// padded row; each lane holds up to kOzSliceSeg segments of 16 consecutive
-// elements in registers (rows up to 8192 are read once), longer rows are read
-// again for the digits.  Rows and columns past d get zero digits (and rows
-// exponent 0).  Runs for the matrices whose step t is a float64 step with
-// products (t < j, t < K - 1).
-constexpr int kOzSliceSeg = 2;
+// Digit planes of M (iteration t) with per-row exponents: a wave per padded
+// row, kOzSliceRows (16) rows per workgroup (a long schedule launches this
+// pass for every step it might need, and most workgroups exit at once); each
+// lane takes 16-element segments 1024 elements apart, reads them for the
+// row's largest magnitude and again (from cache) for the digits.  Rows and
+// columns past d get zero digits (and rows exponent 0).  Runs for the
+// matrices whose step t is a float64 step with products (t < j, t < K - 1).
 __global__ __launch_bounds__(256) void newton_slice_kernel(const NewtonLaunch L) {
-  __shared__ double red[4];
   const int64_t b = blockIdx.x;
   const NewtonClass& C = L.cls[find_class(L, b)];
   const int local = (int)(b - C.block_begin);
   if (local >= C.nblocks) return;
   const int mat = local / C.blocks_per_matrix;
-  const int row = local % C.blocks_per_matrix;
+  const int row0 = (local % C.blocks_per_matrix) * kOzSliceRows;
   const RootState& st = L.state[C.slot_begin + mat];
   const int t = L.t;
   if (!(t < st.j && t < st.K - 1)) return;
   const int d = C.d;
   char* region = C.region + (int64_t)mat * C.matrix_bytes;
   const OzRegion z = oz_region(region, d, t);
-  const double* M = roles64(region, d, t).M + (int64_t)row * d;
-  const bool real = row < d;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool vec = (d & 1) == 0;  // 16-byte loads (rows 16-byte aligned)
-  auto load16 = [&](int c0, double (&w)[16]) __attribute__((always_inline)) {
-    if (real && vec && c0 + 16 <= d) {
+  for (int row = row0 + wave; row < row0 + kOzSliceRows; row += 4) {
+    const double* M = roles64(region, d, t).M + (int64_t)row * d;
+    const bool real = row < d;
+    auto load16 = [&](int c0, double (&w)[16]) __attribute__((always_inline)) {
+      if (real && vec && c0 + 16 <= d) {
 #pragma unroll
-      for (int k = 0; k < 16; k += 2) {
-        const v2d x = *reinterpret_cast<const v2d*>(M + c0 + k);
-        w[k] = x[0];
-        w[k + 1] = x[1];
+        for (int k = 0; k < 16; k += 2) {
+          const v2d x = *reinterpret_cast<const v2d*>(M + c0 + k);
+          w[k] = x[0];
+          w[k + 1] = x[1];
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) w[k] = real && c0 + k < d ? M[c0 + k] : 0.0;
       }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) w[k] = real && c0 + k < d ? M[c0 + k] : 0.0;
-    }
-  };
-  double seg[kOzSliceSeg][16];
-  double mx = 0.0;
-  for (int c0 = threadIdx.x * 16, i = 0; c0 < z.dp; c0 += 256 * 16, ++i) {
-    double w[16];
-    load16(c0, w);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) mx = fmax(mx, fabs(w[k]));
-#pragma unroll
-    for (int q = 0; q < kOzSliceSeg; ++q)
-      if (q == i)
-#pragma unroll
-        for (int k = 0; k < 16; ++k) seg[q][k] = w[k];
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
-  __syncthreads();
-  mx = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
-  int e = 0;
-  if (mx > 0.0) frexp(mx, &e);  // mx < 2^e
-  if (threadIdx.x == 0) z.eM[row] = e;
-  for (int c0 = threadIdx.x * 16, i = 0; c0 < z.dp; c0 += 256 * 16, ++i) {
-    double w[16];
-    if (i < kOzSliceSeg) {
-#pragma unroll
-      for (int q = 0; q < kOzSliceSeg; ++q)
-        if (q == i)
-#pragma unroll
-          for (int k = 0; k < 16; ++k) w[k] = seg[q][k];
-    } else {
+    };
+    double mx = 0.0;
+    for (int c0 = lane * 16; c0 < z.dp; c0 += 64 * 16) {
+      double w[16];
       load16(c0, w);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) mx = fmax(mx, fabs(w[k]));
     }
-    oz_store16(w, e, z.M, (int64_t)row * z.dp + c0);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+    int e = 0;
+    if (mx > 0.0) frexp(mx, &e);  // mx < 2^e
+    if (lane == 0) z.eM[row] = e;
+    for (int c0 = lane * 16; c0 < z.dp; c0 += 64 * 16) {
+      double w[16];
+      load16(c0, w);
+      oz_store16(w, e, z.M, (int64_t)row * z.dp + c0);
+    }
   }
 }
 

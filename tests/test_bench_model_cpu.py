@@ -48,8 +48,11 @@ def test_root_stream_bytes():
     assert bp["root_finalize"] == (4 + 8 + 4) * n
     assert bp["newton_slice"] == 8 * n + 6 * n + 4 * d  # K = 2: the last step has no products
     # a ragged size pads the planes to a multiple of 128
-    br = bench.root_stream_bytes(200, 8, False, 6, 1)
-    assert br["newton_slice"] == 8 * 200 * 200 + 6 * 256 * 256 + 4 * 256
+    br = bench.root_stream_bytes(1100, 8, False, 6, 1)
+    assert br["newton_slice"] == 8 * 1100 * 1100 + 6 * 1152 * 1152 + 4 * 1152
+    # below 1024 the float64 steps keep the float64 kernel: no planes
+    assert bench.root_stream_bytes(512, 4, False, 9, 3)["newton_slice"] == 0
+    assert bench.f64_class(512) == "newton_f64" and bench.f64_class(1024) == "newton_i8"
 
 
 def test_bench_refuses_more_than_one_gpu(capsys):

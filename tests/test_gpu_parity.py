@@ -136,6 +136,21 @@ def test_newton_wide_tiles_ragged(torch_dev):
         _check_roots(torch, dev, mats, 1e-6, normalize, "newton", torch.float32, ROOT_TOL)
 
 
+def test_newton_digit_plane_placements(torch_dev):
+    """From d = 1024 the float64 steps' products run on int8 digit planes,
+    placed in the float64 slots a float64 step leaves idle where they fit:
+    1024 (every plane there), 1056 (padded to 1152: some planes past the
+    slots), 1030 (d % 4 != 0: every plane past the slots, ragged tiles) and
+    1027 (odd: unaligned rows of the float64 M read element by element),
+    next to a 1000 that keeps the float64 kernel, in one call; log-uniform
+    spectra down to 1e-8 keep several float64 steps."""
+    torch, dev = torch_dev
+    rng = W.rng_for(90, 11)
+    mats = [spd(d, rng, lo=-8.0) for d in (1024, 1056, 1030, 1027, 1000)]
+    for normalize in ("trace", "none"):
+        _check_roots(torch, dev, mats, 1e-6, normalize, "newton", torch.float32, ROOT_TOL)
+
+
 def test_newton_read_ahead_chunk_counts(torch_dev):
     """Chunk counts at the edges of the main loops that read fragments one
     k-step ahead: one chunk (d = 16 in the float64 core, d = 32 in the
