@@ -194,12 +194,13 @@ size_t gram_ema_update_workspace(const mr_gram_problem* problems, int32_t count,
  *    eigenvalue of M is below 5e-4, then with float32 storage on the fp16
  *    matrix cores with split operands (x = hi + 2^-11 lo, three products per
  *    product, float32 accumulation: about 2^-22 relative error per product).
- *    X is kept in that split storage from the first step.  The
+ *    X is kept in that split storage from the first step.  For d >= 1024 the
  *    float64-accurate products run on the int8 matrix cores: each operand as
  *    six int8 digit planes (7 bits each, one power-of-two exponent per row of
  *    M, fixed ones for M's powers), 21 exact plane products with int32
  *    accumulation, summed in float64 (about 2^-40 relative to each row's
- *    largest entry).  The GEMM-only
+ *    largest entry); smaller Grams run them on the float64 matrix cores.
+ *    The GEMM-only
  *    route of tilderesearch, "Online KL Shampoo", sections 2.1-2.2 (there
  *    for the -1/2 root), taken to the 4th root.  c = 1.01 times the
  *    Wolkowicz-Styan upper bound on lambda_max(A/s + eps I) (the OKLS page,
@@ -228,9 +229,11 @@ size_t gram_ema_update_workspace(const mr_gram_problem* problems, int32_t count,
  * converge).
  * Workspace: at least inv_quarter_root_batched_workspace(...) bytes, 256-byte
  * aligned; its contents on entry are ignored.  Per Newton matrix it holds
- * 40 d^2 bytes (rounded up to 256), plus, for MR_NEWTON and MR_AUTO, the
- * digit planes of M, T2 and T4 and M's row exponents, 18 dp^2 + 4 dp bytes
- * (dp = d rounded up to 128).
+ * 40 d^2 bytes (rounded up to 256), plus, for MR_NEWTON and MR_AUTO from
+ * d = 1024, M's row exponents (4 dp bytes, dp = d rounded up to 128) and
+ * whatever of the 18 dp x dp digit planes does not fit in the parts of the
+ * 40 d^2 bytes a float64 step leaves idle (none for d a multiple of 128,
+ * all of them for d not a multiple of 4).
  */
 mr_status inv_quarter_root_batched(const mr_root_problem* problems, int32_t count,
                                    mr_dtype a_dtype, double eps, int32_t normalize, int32_t method,
