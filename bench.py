@@ -285,6 +285,22 @@ def engine_table(kernels):
     return out
 
 
+def annotate_engines(engines, peaks):
+    """Each unit's rate beside what the vendor GEMM sustains on it in the same
+    run and what its register-only MFMA loop reaches on random operands (the
+    clock real data leave the chip); the roofline fractions stay against
+    the published peaks."""
+    vend = peaks.get("vendor_gemm_tflops") or {}
+    rnd = peaks.get("measured_random_tflops") or {}
+    for eng, e in engines.items():
+        if eng in vend:
+            e["vendor_gemm_tflops"] = vend[eng]
+            e["frac_of_vendor_gemm"] = round(e["mfma_tflops"] / vend[eng], 4)
+        if rnd.get(eng):
+            e["random_operand_loop_tflops"] = rnd[eng]
+            e["frac_of_random_operand_loop"] = round(e["mfma_tflops"] / rnd[eng], 4)
+
+
 # classes whose counters come from the optimizer-step run (their own source family)
 STEP_CLASSES = ("momentum", "hyperball_reduce", "hyperball_update")
 
@@ -504,12 +520,7 @@ def bench_steps(args, torch, B, W, peaks):
                     else n * n) for m, n in shapes)
         kernels["syrk_ema"]["hbm_bytes_per_step"] = 2 * es * st_el + 2 * 4 * sum(m * n for m, n in shapes)
     engines = engine_table(kernels)
-    vend = peaks.get("vendor_gemm_tflops")
-    if vend:
-        for eng, e in engines.items():
-            if eng in vend:
-                e["vendor_gemm_tflops"] = vend[eng]
-                e["frac_of_vendor_gemm"] = round(e["mfma_tflops"] / vend[eng], 4)
+    annotate_engines(engines, peaks)
     dname = max((kv for kv in kernels.items() if "tflops" in kv[1]), key=lambda kv: kv[1]["ms_total"])[0]
     roofline = roofline_for(kernels, dname, args.workload)
     rooflines = {n: roofline_for(kernels, n, args.workload) for n in kernels
@@ -667,6 +678,8 @@ def bench_illcond(args, torch, B, W, peaks):
                                "tflops": round((ef64 + elow) / (cms / 1e3) / 1e12, 2)}
         log(f"eps {eps:g}: {per_eps[f'{eps:g}']}")
     kernels = kernel_table(trace, {f64_class(512): f64, "newton_x3": low}, sbytes)
+    engines = engine_table(kernels)
+    annotate_engines(engines, peaks)
     dname = max((kv for kv in kernels.items() if "tflops" in kv[1]), key=lambda kv: kv[1]["ms_total"])[0]
     cpu = None
     if not args.no_cpu_baseline:
@@ -689,7 +702,7 @@ def bench_illcond(args, torch, B, W, peaks):
         "config": {"workload": "illcond", "matrices": count, "d": 512, "eps": list(wl.eps_list),
                    "normalize": "none", "calls_per_step": len(wl.eps_list)},
         "per_eps": per_eps,
-        "engines": engine_table(kernels),
+        "engines": engines,
         "roofline": roofline_for(kernels, dname, "illcond"),
         "rooflines": {n: roofline_for(kernels, n, "illcond") for n in kernels
                       if "tflops" in kernels[n] or "gb_per_s" in kernels[n]},

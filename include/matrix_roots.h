@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MR_ABI_VERSION 2
+#define MR_ABI_VERSION 3
 
 typedef int32_t mr_status;
 #define MR_OK 0
@@ -469,7 +469,10 @@ int32_t mr_newton_schedule(double m0, double* scales, int32_t capacity, int32_t*
  * measured_tflops: register-only MFMA loops (v_mfma_f32_32x32x2_f32,
  * v_mfma_f64_16x16x4_f64, v_mfma_f32_32x32x16_f16,
  * v_mfma_i32_32x32x32_i8), eight workgroups per CU, a few ms each, timed
- * with events on `hip_stream` after one warm-up launch.  Index 0 float32,
+ * with events on `hip_stream` after one warm-up launch, on fixed small
+ * operands; measured_random_tflops: the same loops with per-lane random
+ * operands (uniform in [-1, 1), int8 digits in [-64, 63]), which draw more
+ * power and hold a lower clock, as real data do.  Index 0 float32,
  * 1 float64, 2 fp16, 3 int8 (TOP/s).  Synchronises the stream and
  * touches no device memory; MR_ERR_NULL for a NULL `out`, MR_ERR_HIP on a
  * runtime error (then `out` holds what was measured before it).
@@ -477,8 +480,9 @@ int32_t mr_newton_schedule(double m0, double* scales, int32_t capacity, int32_t*
 typedef struct {
   int32_t cu_count;          /* hipDeviceProp_t::multiProcessorCount   */
   int32_t clock_khz;         /* hipDeviceProp_t::clockRate (peak, kHz) */
-  double prop_tflops[4];     /* derived from CU count and clock        */
-  double measured_tflops[4]; /* register-only MFMA loops              */
+  double prop_tflops[4];            /* derived from CU count and clock   */
+  double measured_tflops[4];        /* register-only MFMA loops         */
+  double measured_random_tflops[4]; /* ... on random operands           */
 } mr_peak_info;
 mr_status mr_measure_peaks(mr_peak_info* out, void* hip_stream);
 

@@ -166,7 +166,7 @@ def library() -> ctypes.CDLL:
     lib.mr_last_error_message.restype = ctypes.c_char_p
     lib.mr_abi_version.argtypes = []
     lib.mr_abi_version.restype = i32
-    if lib.mr_abi_version() != 2:
+    if lib.mr_abi_version() != 3:
         raise RuntimeError("libmatrix_roots.so ABI version mismatch")
     _lib = lib
     return lib
@@ -546,7 +546,8 @@ def newton_schedule(m0: float, final_degree: bool = False):
 
 class PeakInfo(ctypes.Structure):
     _fields_ = [("cu_count", ctypes.c_int32), ("clock_khz", ctypes.c_int32),
-                ("prop_tflops", ctypes.c_double * 4), ("measured_tflops", ctypes.c_double * 4)]
+                ("prop_tflops", ctypes.c_double * 4), ("measured_tflops", ctypes.c_double * 4),
+                ("measured_random_tflops", ctypes.c_double * 4)]
 
 
 PEAK_KINDS = ("f32", "f64", "f16", "i8")
@@ -559,7 +560,8 @@ def measure_peaks(stream=None) -> dict:
     _check(library().mr_measure_peaks(ctypes.addressof(out), _stream(stream)))
     return {"cu_count": int(out.cu_count), "clock_mhz": out.clock_khz / 1e3,
             "device_prop_tflops": {k: round(out.prop_tflops[i], 1) for i, k in enumerate(PEAK_KINDS)},
-            "measured_tflops": {k: round(out.measured_tflops[i], 1) for i, k in enumerate(PEAK_KINDS)}}
+            "measured_tflops": {k: round(out.measured_tflops[i], 1) for i, k in enumerate(PEAK_KINDS)},
+            "measured_random_tflops": {k: round(out.measured_random_tflops[i], 1) for i, k in enumerate(PEAK_KINDS)}}
 
 
 def newton_iterations(p: int, m0: float, tol: float) -> int:

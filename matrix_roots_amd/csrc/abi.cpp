@@ -365,20 +365,22 @@ mr_status mr_measure_peaks(mr_peak_info* out, void* hip_stream) {
   const int blocks = 8 * std::max(1, prop.multiProcessorCount);
   const int iters[kPeakKinds] = {3000, 1500, 6000, 6000};
   mr_status st = MR_OK;
-  for (int k = 0; k < kPeakKinds && st == MR_OK; ++k) {
-    double flops = 0.0;
-    float ms = 0.f;
-    e = launch_peak_loop(k, blocks, iters[k], &flops, s);
-    if (e == hipSuccess) e = hipEventRecord(a, s);
-    if (e == hipSuccess) e = launch_peak_loop(k, blocks, iters[k], &flops, s);
-    if (e == hipSuccess) e = hipEventRecord(b, s);
-    if (e == hipSuccess) e = hipEventSynchronize(b);
-    if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
-    if (e != hipSuccess)
-      st = hip_fail(e, "peak loop");
-    else
-      out->measured_tflops[k] = ms > 0.f ? flops / (ms * 1e-3) / 1e12 : 0.0;
-  }
+  for (int r = 0; r < 2; ++r)
+    for (int k = 0; k < kPeakKinds && st == MR_OK; ++k) {
+      double flops = 0.0;
+      float ms = 0.f;
+      e = launch_peak_loop(k, blocks, iters[k], r == 1, &flops, s);
+      if (e == hipSuccess) e = hipEventRecord(a, s);
+      if (e == hipSuccess) e = launch_peak_loop(k, blocks, iters[k], r == 1, &flops, s);
+      if (e == hipSuccess) e = hipEventRecord(b, s);
+      if (e == hipSuccess) e = hipEventSynchronize(b);
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+      if (e != hipSuccess)
+        st = hip_fail(e, "peak loop");
+      else
+        (r == 0 ? out->measured_tflops : out->measured_random_tflops)[k] =
+            ms > 0.f ? flops / (ms * 1e-3) / 1e12 : 0.0;
+    }
   (void)hipEventDestroy(a);
   (void)hipEventDestroy(b);
   return st;

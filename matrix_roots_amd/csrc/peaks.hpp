@@ -15,8 +15,9 @@ constexpr int kPeakKinds = 4;
 constexpr double kMfmaFlopsPerClockCU[kPeakKinds] = {256.0, 128.0, 4096.0, 8192.0};
 
 // Launch `blocks` workgroups of 256 threads, each wave running `iters`
-// rounds of independent MFMA chains of the kind; returns the flops one such
-// launch performs through *flops.
-hipError_t launch_peak_loop(int kind, int blocks, int iters, double* flops, hipStream_t s);
+// rounds of independent MFMA chains of the kind, on fixed small operands or
+// (random) on per-lane random ones; returns the flops one such launch
+// performs through *flops.
+hipError_t launch_peak_loop(int kind, int blocks, int iters, bool random, double* flops, hipStream_t s);
 
 }  // namespace mr

@@ -153,8 +153,9 @@ def mfma_busy(run_dir: str, kernels):
     """Matrix-core busy fraction per kernel: SQ_VALU_MFMA_BUSY_CYCLES per
     GRBM_GUI_ACTIVE cycle, summed over the kernel's dispatches, divided by the
     same ratio of the register-only MFMA loop of the matching precision
-    (peak_kernel<0> float32, <1> float64, <2> fp16), which keeps every matrix
-    core busy: the counters' own scale (per SIMD or per CU) cancels."""
+    (peak_kernel<K, 0> with K = 0 float32, 1 float64, 2 fp16, 3 int8), which
+    keeps every matrix core busy: the counters' own scale (per SIMD or per
+    CU) cancels."""
     busy = read_counter(run_dir, "SQ_VALU_MFMA_BUSY_CYCLES")
     active = read_counter(run_dir, "GRBM_GUI_ACTIVE")
 
@@ -180,7 +181,7 @@ def main(argv=None) -> int:
     ap.add_argument("--family", default="quarter", choices=sorted(KERNEL_SOURCES))
     ap.add_argument("--mfma", help="run dir of a SQ_VALU_MFMA_BUSY_CYCLES + GRBM_GUI_ACTIVE pass")
     ap.add_argument("--pair", action="append", default=[],
-                    help="KERNEL=PEAK_KERNEL for --mfma (e.g. newton_f64_kernel=peak_kernel<1>)")
+                    help="KERNEL=PEAK_KERNEL for --mfma (e.g. newton_i8_kernel=\"peak_kernel<3, 0>\")")
     ap.add_argument("--trace", help="run dir of a --kernel-trace run: print the per-kernel table")
     args = ap.parse_args(argv)
     if args.trace:

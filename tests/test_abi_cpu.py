@@ -44,7 +44,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.mr_abi_version() == 2
+    assert lib.mr_abi_version() == 3
     for s in range(9):
         assert lib.mr_status_string(s)
     assert b"unknown" in lib.mr_status_string(99)

@@ -24,3 +24,6 @@ def test_measure_peaks(gpu_available):
         assert 0.8 * v <= prop <= 1.2 * v, (k, prop)
         # a loop without memory traffic reaches most of it and cannot beat it
         assert 0.5 * prop <= meas <= 1.05 * prop, (k, meas, prop)
+        # random operands: a lower clock, never above the fixed-operand loop
+        rnd = p["measured_random_tflops"][k]
+        assert 0.3 * prop <= rnd <= 1.05 * meas, (k, rnd, meas)
