@@ -24,6 +24,7 @@ def test_measure_peaks(gpu_available):
         assert 0.8 * v <= prop <= 1.2 * v, (k, prop)
         # a loop without memory traffic reaches most of it and cannot beat it
         assert 0.5 * prop <= meas <= 1.05 * prop, (k, meas, prop)
-        # random operands: a lower clock, never above the fixed-operand loop
+        # random operands: the clock the chip holds with real data (lower for
+        # int8 and fp16; float32 and float64 draw about the same either way)
         rnd = p["measured_random_tflops"][k]
-        assert 0.3 * prop <= rnd <= 1.05 * meas, (k, rnd, meas)
+        assert 0.3 * prop <= rnd <= 1.05 * prop, (k, rnd, prop)
