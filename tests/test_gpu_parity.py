@@ -197,10 +197,11 @@ def test_root_flags(torch_dev):
 def test_newton_flags_indefinite_input(torch_dev):
     """A + eps I with an eigenvalue well below zero has no inverse quarter
     root: the Newton iterate never nears I, whichever last update the schedule
-    picks, and the residual check flags it."""
+    picks, and the residual check flags it (d = 1056: through the int8 digit
+    planes, whose digits clamp on such input)."""
     torch, dev = torch_dev
     rng = W.rng_for(90, 6)
-    for d in (160, 288):
+    for d in (160, 288, 1056):
         q, _ = np.linalg.qr(rng.standard_normal((d, d)))
         lam = np.geomspace(1e-3, 1.0, d)
         lam[d // 2] = -0.3
