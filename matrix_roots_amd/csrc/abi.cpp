@@ -804,8 +804,9 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
   const int a_packed = is_packed(dt) ? 1 : 0;
   const bool all_f64 = method == MR_NEWTON_F64;
   const bool f32_mfma = method == MR_NEWTON_F32;
-  // Default Newton path: X in float32 storage with split-fp16 products from
-  // the first step; only M and its powers run in float64 while the floor is low.
+  // Default Newton path: X in split-fp16 storage with split-fp16 products from
+  // the first step; only M and its powers take float64-accurate products while
+  // the floor is low (on int8 digit planes from kI8MinD).
   const bool x_low = split_path(method);
 
   // ---------------- Jacobi matrices: descriptors into the workspace, then one
