@@ -543,30 +543,31 @@ using X3W = X3WCfg<32, 2, 4>;  // 32-deep chunks, two stages, 2 x 4 waves
 __device__ __forceinline__ void x3w_issue(SplitRef A, int64_t lda, SplitRef B, int64_t ldb, int M, int N, int m0,
                                           int n0, int k0, unsigned char* stage, int wave, int lane) {
   // Copy j of a lane covers row lrow + j * THREADS / UPR of the tile, in the
-  // same k-group for every j (the slot map repeats every 16 rows).  Element
-  // offsets are 32-bit (a split array of a Gram holds d^2 < 2^31 elements);
-  // rows past the last are clamped to it through the offset.
+  // same k-group for every j (the slot map repeats every 16 rows); rows past
+  // the last are clamped to it.  Each copy is one instruction: a scalar base
+  // (the array at row r0, column k0) plus a 32-bit lane byte offset within
+  // the tile's rows (under 2 * 256 * ld bytes).
   static_assert((X3W::THREADS / 16) % X3W::UPR == 0, "one k-group per lane");
   const int lu = wave * 64 + lane;
   const int lrow = lu / X3W::UPR;
   const int kg = dl_slot(lrow, lu % X3W::UPR, X3W::UPR);  // the map is its own inverse
 #pragma unroll
   for (int side = 0; side < 2; ++side) {
-    const uint32_t ld = (uint32_t)(side == 0 ? lda : ldb);
-    const int r0 = side == 0 ? m0 : n0, rmax = (side == 0 ? M : N) - 1;
-    uint32_t off0 = (uint32_t)(r0 + lrow) * ld + (uint32_t)(kg * 8);
-    uint32_t offmax = (uint32_t)rmax * ld + (uint32_t)(kg * 8);
-    // opaque per call: keeps the compiler from hoisting one 64-bit address
-    // per copy out of the main loop (registers it does not have to spare)
-    asm volatile("" : "+v"(off0), "+v"(offmax));
+    const int64_t ld = side == 0 ? lda : ldb;
+    const int r0 = side == 0 ? m0 : n0, rlast = (side == 0 ? M : N) - 1 - r0;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int arr = side * 2 + half;
-      const _Float16* P = (arr == 0 ? A.hi : arr == 1 ? A.lo : arr == 2 ? B.hi : B.lo) + k0;
+      const char* P = reinterpret_cast<const char*>((arr == 0 ? A.hi : arr == 1 ? A.lo : arr == 2 ? B.hi : B.lo) +
+                                                    (int64_t)r0 * ld + k0);
 #pragma unroll
       for (int j = 0; j < X3W::CPA; ++j) {
         const int base_u = (j * (X3W::THREADS / 64) + wave) * 64;
-        const uint32_t off = min(off0 + (uint32_t)(j * (X3W::THREADS / X3W::UPR)) * ld, offmax);
+        const uint32_t row = (uint32_t)min(lrow + j * (X3W::THREADS / X3W::UPR), rlast);
+        uint32_t off = (row * (uint32_t)ld + (uint32_t)(kg * 8)) * 2u;
+        // opaque per copy: the base stays scalar and the offset 32-bit (else
+        // the compiler hoists a 64-bit lane address out of the main loop)
+        asm volatile("" : "+s"(P), "+v"(off));
         __builtin_amdgcn_global_load_lds((global_void_ptr)(P + off),
                                          (lds_void_ptr)(stage + (arr * X3W::AU + base_u) * 16), 16, 0, 0);
       }

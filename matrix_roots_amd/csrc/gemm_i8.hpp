@@ -73,7 +73,8 @@ __host__ __device__ __forceinline__ void oz_digits(double v, int e, int8_t (&dg)
 // (one 32 x 32 MFMA block per row of waves, two per column), six int32
 // accumulators of 32 x 64 per wave (192 registers: two waves per SIMD).
 // K-chunks of 32 digits per plane, copied straight to LDS (16-byte units,
-// swizzled by dl_slot) in three stages of 48 KiB; one barrier per chunk.
+// swizzled by dl_slot) in three stages of 48 KiB, the copies of chunk c + 2
+// spread over chunk c's products; one barrier per chunk.
 struct OzCfg {
   static constexpr int S = kOzSlices;
   static constexpr int BM = kOzTile, BN = kOzTile, BK = 32, UPR = BK / 16;
@@ -86,56 +87,91 @@ struct OzCfg {
 };
 static_assert(OzCfg::S * 2 * OzCfg::PLANE_UNITS == OzCfg::THREADS * OzCfg::S, "one unit per thread and plane pair");
 
-// Copy chunk k0 .. k0+31 of rows m0.. (A) and n0.. (B), every plane, into
-// `stage`: 12 arrays of 256 units; wave w copies units 64 (w & 3) .. +63 of
-// the arrays of parity w >> 2.
+// Copy j (0 .. 5) of chunk k0 .. k0+31 of rows m0.. (A) and n0.. (B) into
+// `stage`, which holds 12 arrays of 256 units (A planes 0 .. 5, then B
+// planes): wave w copies units 64 (w & 3) .. +63 of array 2 j + (w >> 2), an
+// A plane for j < 3, a B plane after.  The address is a wave-uniform base
+// (the plane at row m0 or n0, column k0) plus a 32-bit lane offset within the
+// tile's 128 rows, so each copy is one instruction on a scalar base.
+__device__ __forceinline__ void oz_copy(const OzPlanes& A, const OzPlanes& B, int64_t ld, int m0, int n0, int k0,
+                                        unsigned char* stage, int wave, int lane, int j) {
+  const int base_u = (wave & 3) * 64;
+  const int u = base_u + lane;
+  const int row = u / OzCfg::UPR;
+  const int kg = dl_slot(row, u % OzCfg::UPR, OzCfg::UPR);  // the map is its own inverse
+  const bool is_a = j < OzCfg::S / 2;
+  uint32_t off = (uint32_t)row * (uint32_t)ld + (uint32_t)(kg * 16);
+  const int a = 2 * j + (wave >> 2);
+  const int p = is_a ? a : a - OzCfg::S;
+  // (p depends on the wave: select the pointer, never index the lists with it)
+  const int8_t* P = nullptr;
+#pragma unroll
+  for (int q = 0; q < OzCfg::S; ++q)
+    if (q == p) P = is_a ? A.p[q] : B.p[q];
+  P += (int64_t)(is_a ? m0 : n0) * ld + k0;
+  // opaque per copy: the base stays scalar and the offset 32-bit (else the
+  // compiler hoists a 64-bit lane address out of the main loop)
+  asm volatile("" : "+s"(P), "+v"(off));
+  __builtin_amdgcn_global_load_lds((global_void_ptr)(P + off),
+                                   (lds_void_ptr)(stage + (a * OzCfg::PLANE_UNITS + base_u) * 16), 16, 0, 0);
+}
+
+// The whole chunk k0 .. k0+31 into `stage`.
 __device__ __forceinline__ void oz_issue(const OzPlanes& A, const OzPlanes& B, int64_t ld, int m0, int n0, int k0,
                                          unsigned char* stage, int wave, int lane) {
 #pragma unroll
-  for (int j = 0; j < OzCfg::S; ++j) {
-    const int a = 2 * j + (wave >> 2);
-    const int op = a / OzCfg::S, p = a % OzCfg::S;
-    // (p depends on the wave: select the pointer, never index the lists with it)
-    const int8_t* P = nullptr;
-#pragma unroll
-    for (int q = 0; q < OzCfg::S; ++q)
-      if (q == p) P = op == 0 ? A.p[q] : B.p[q];
-    const int r0 = op == 0 ? m0 : n0;
-    const int base_u = (wave & 3) * 64;
-    const int u = base_u + lane;
-    const int row = u / OzCfg::UPR;
-    const int kg = dl_slot(row, u % OzCfg::UPR, OzCfg::UPR);  // the map is its own inverse
-    const int8_t* src = P + (int64_t)(r0 + row) * ld + k0 + kg * 16;
-    __builtin_amdgcn_global_load_lds((global_void_ptr)src,
-                                     (lds_void_ptr)(stage + (a * OzCfg::PLANE_UNITS + base_u) * 16), 16, 0, 0);
-  }
+  for (int j = 0; j < OzCfg::S; ++j) oz_copy(A, B, ld, m0, n0, k0, stage, wave, lane, j);
 }
 
-// acc[r][cb] += sum_{p + q = r} D^A_p D^B_q^T over one chunk.
+// Fragment (row r, k-group kg) of array `plane` of a stage.
+__device__ __forceinline__ v4i oz_frag(const unsigned char* __restrict__ st, int plane, int r, int kg) {
+  return *reinterpret_cast<const v4i*>(st + (plane * OzCfg::PLANE_UNITS + r * OzCfg::UPR + dl_slot(r, kg, OzCfg::UPR)) *
+                                                16);
+}
+
+// The copies a chunk's products carry for a later chunk.
+struct OzNext {
+  bool on;
+  int k0;
+  unsigned char* stage;
+};
+
+// acc[r][cb] += sum_{p + q = r} D^A_p D^B_q^T over one chunk, B plane by B
+// plane (q = 0 .. 5 pairs with A planes 0 .. 5 - q).  The B fragments of
+// plane q + 1 are read while the products of plane q run (two register
+// sets), each wait falls on reads issued a group of products earlier, and
+// copy q of the next chunk goes out with group q; scheduling barriers keep
+// that order.
 __device__ __forceinline__ void oz_chunk(const unsigned char* __restrict__ st, v16i (&acc)[kOzSlices][2], int lane,
-                                         int wm, int wn) {
+                                         int wave, const OzPlanes& A, const OzPlanes& B, int64_t ld, int m0, int n0,
+                                         const OzNext& next) {
   const int kg = lane >> 5;
+  const int ra = (wave >> 1) * 32 + (lane & 31);
+  const int rb = (wave & 1) * 64 + (lane & 31);
   v4i af[OzCfg::S];
+  v4i bf[2][2];
+  af[0] = oz_frag(st, 0, ra, kg);
+  bf[0][0] = oz_frag(st, OzCfg::S, rb, kg);
+  bf[0][1] = oz_frag(st, OzCfg::S, rb + 32, kg);
 #pragma unroll
-  for (int p = 0; p < OzCfg::S; ++p) {
-    const int r = wm * 32 + (lane & 31);
-    af[p] = *reinterpret_cast<const v4i*>(
-        st + (p * OzCfg::PLANE_UNITS + r * OzCfg::UPR + dl_slot(r, kg, OzCfg::UPR)) * 16);
-  }
+  for (int p = 1; p < OzCfg::S; ++p) af[p] = oz_frag(st, p, ra, kg);
 #pragma unroll
   for (int q = 0; q < OzCfg::S; ++q) {
-    v4i bf[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int r = wn * 64 + cb * 32 + (lane & 31);
-      bf[cb] = *reinterpret_cast<const v4i*>(
-          st + ((OzCfg::S + q) * OzCfg::PLANE_UNITS + r * OzCfg::UPR + dl_slot(r, kg, OzCfg::UPR)) * 16);
+    // B plane q (before q = 0 also the A planes) is the only read in
+    // flight: wait for it before issuing plane q + 1's
+    wait_lgkmcnt0();
+    if (q + 1 < OzCfg::S) {
+      bf[(q + 1) & 1][0] = oz_frag(st, OzCfg::S + q + 1, rb, kg);
+      bf[(q + 1) & 1][1] = oz_frag(st, OzCfg::S + q + 1, rb + 32, kg);
     }
+    if (next.on) oz_copy(A, B, ld, m0, n0, next.k0, next.stage, wave, lane, q);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int p = 0; p + q < OzCfg::S; ++p)
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
-        acc[p + q][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[p], bf[cb], acc[p + q][cb], 0, 0, 0);
+        acc[p + q][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[p], bf[q & 1][cb], acc[p + q][cb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -146,7 +182,6 @@ __device__ __forceinline__ void oz_nt_tile(const OzPlanes& A, const OzPlanes& B,
                                            unsigned char* __restrict__ lds, v16i (&acc)[kOzSlices][2]) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar LDS offsets
-  const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
   for (int r = 0; r < OzCfg::S; ++r)
 #pragma unroll
@@ -167,9 +202,9 @@ __device__ __forceinline__ void oz_nt_tile(const OzPlanes& A, const OzPlanes& B,
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();  // chunk c visible to all waves; all are done with chunk c - 1
     asm volatile("" ::: "memory");
-    if (c + 2 < nch)  // into the stage chunk c - 1 occupied
-      oz_issue(A, B, ld, m0, n0, (c + 2) * OzCfg::BK, lds + ((c + 2) % OzCfg::NST) * OzCfg::STAGE_BYTES, wave, lane);
-    oz_chunk(st, acc, lane, wm, wn);
+    // chunk c + 2 goes into the stage chunk c - 1 occupied
+    const OzNext next{c + 2 < nch, (c + 2) * OzCfg::BK, lds + ((c + 2) % OzCfg::NST) * OzCfg::STAGE_BYTES};
+    oz_chunk(st, acc, lane, wave, A, B, ld, m0, n0, next);
   }
   __syncthreads();  // no wave reuses the LDS while another may still read the last stage
 }
