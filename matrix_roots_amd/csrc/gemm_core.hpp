@@ -345,18 +345,21 @@ __device__ __forceinline__ void x3dl_issue(SplitRef A, int64_t lda, SplitRef B, 
 #pragma unroll
   for (int arr = 0; arr < 4; ++arr) {
     const bool isA = arr < 2;
-    const _Float16* P = arr == 0 ? A.hi : arr == 1 ? A.lo : arr == 2 ? B.hi : B.lo;
     const int64_t ld = isA ? lda : ldb;
-    const int r0 = isA ? m0 : n0, rmax = (isA ? M : N) - 1;
+    const int r0 = isA ? m0 : n0, rlast = (isA ? M : N) - 1 - r0;
+    // scalar base (row r0, column k0) plus a 32-bit lane byte offset within
+    // the tile's rows: one copy instruction each
+    const char* P = wave_uniform((arr == 0 ? A.hi : arr == 1 ? A.lo : arr == 2 ? B.hi : B.lo) + (int64_t)r0 * ld + k0);
 #pragma unroll
     for (int j = 0; j < X3DL::CPA; ++j) {
       const int base_u = (j * (X3Tile::THREADS / 64) + wave) * 64;
       const int u = base_u + lane;
       const int row = u / X3DL::UPR;
       const int kg = dl_slot(row, u % X3DL::UPR, X3DL::UPR);  // the map is its own inverse
-      const _Float16* src = P + (int64_t)min(r0 + row, rmax) * ld + k0 + kg * 8;
-      __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)(stage + (arr * X3DL::AU + base_u) * 16),
-                                       16, 0, 0);
+      uint32_t off = ((uint32_t)min(row, rlast) * (uint32_t)ld + (uint32_t)(kg * 8)) * 2u;
+      asm volatile("" : "+v"(off));  // opaque per copy: the offset stays a 32-bit lane value
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(P + off),
+                                       (lds_void_ptr)(stage + (arr * X3DL::AU + base_u) * 16), 16, 0, 0);
     }
   }
 }
@@ -558,16 +561,14 @@ __device__ __forceinline__ void x3w_issue(SplitRef A, int64_t lda, SplitRef B, i
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int arr = side * 2 + half;
-      const char* P = reinterpret_cast<const char*>((arr == 0 ? A.hi : arr == 1 ? A.lo : arr == 2 ? B.hi : B.lo) +
-                                                    (int64_t)r0 * ld + k0);
+      const char* P =
+          wave_uniform((arr == 0 ? A.hi : arr == 1 ? A.lo : arr == 2 ? B.hi : B.lo) + (int64_t)r0 * ld + k0);
 #pragma unroll
       for (int j = 0; j < X3W::CPA; ++j) {
         const int base_u = (j * (X3W::THREADS / 64) + wave) * 64;
         const uint32_t row = (uint32_t)min(lrow + j * (X3W::THREADS / X3W::UPR), rlast);
         uint32_t off = (row * (uint32_t)ld + (uint32_t)(kg * 8)) * 2u;
-        // opaque per copy: the base stays scalar and the offset 32-bit (else
-        // the compiler hoists a 64-bit lane address out of the main loop)
-        asm volatile("" : "+s"(P), "+v"(off));
+        asm volatile("" : "+v"(off));  // opaque per copy: the offset stays a 32-bit lane value
         __builtin_amdgcn_global_load_lds((global_void_ptr)(P + off),
                                          (lds_void_ptr)(stage + (arr * X3W::AU + base_u) * 16), 16, 0, 0);
       }
@@ -928,25 +929,24 @@ __device__ __forceinline__ void f64dl_issue(const double* __restrict__ A, int64_
                                             int64_t ldb, int M, int N, int m0, int n0, int k0, unsigned char* stage,
                                             int wave, int lane) {
   // Copy j of a lane covers row lrow + j * THREADS / UPR of the tile, in the
-  // same k-group for every j; 32-bit element offsets from a scalar base (a
-  // Gram slot holds d^2 < 2^31 elements), rows past the last clamped to it,
-  // recomputed per call rather than held in registers across the main loop.
+  // same k-group for every j, rows past the last clamped to it.  Each copy is
+  // one instruction: a scalar base (row r0, column k0) plus a 32-bit lane byte
+  // offset within the tile's rows.
   static_assert((F64Tile::THREADS / 16) % F64DL::UPR == 0, "one k-group per lane");
   const int lu = wave * 64 + lane;
   const int lrow = lu / F64DL::UPR;
   const int kg = dl_slot(lrow, lu % F64DL::UPR, F64DL::UPR);  // the map is its own inverse
 #pragma unroll
   for (int side = 0; side < 2; ++side) {
-    const uint32_t ld = (uint32_t)(side == 0 ? lda : ldb);
-    const int r0 = side == 0 ? m0 : n0, rmax = (side == 0 ? M : N) - 1;
-    uint32_t off0 = (uint32_t)(r0 + lrow) * ld + (uint32_t)(kg * 2);
-    uint32_t offmax = (uint32_t)rmax * ld + (uint32_t)(kg * 2);
-    asm volatile("" : "+v"(off0), "+v"(offmax));
-    const double* P = (side == 0 ? A : B) + k0;
+    const int64_t ld = side == 0 ? lda : ldb;
+    const int r0 = side == 0 ? m0 : n0, rlast = (side == 0 ? M : N) - 1 - r0;
+    const char* P = wave_uniform((side == 0 ? A : B) + (int64_t)r0 * ld + k0);
 #pragma unroll
     for (int j = 0; j < F64DL::CPO; ++j) {
       const int base_u = (j * (F64Tile::THREADS / 64) + wave) * 64;
-      const uint32_t off = min(off0 + (uint32_t)(j * (F64Tile::THREADS / F64DL::UPR)) * ld, offmax);
+      const uint32_t row = (uint32_t)min(lrow + j * (F64Tile::THREADS / F64DL::UPR), rlast);
+      uint32_t off = (row * (uint32_t)ld + (uint32_t)(kg * 2)) * 8u;
+      asm volatile("" : "+v"(off));  // opaque per copy: the offset stays a 32-bit lane value
       __builtin_amdgcn_global_load_lds((global_void_ptr)(P + off),
                                        (lds_void_ptr)(stage + ((side == 0 ? 0 : F64DL::AU) + base_u) * 16), 16, 0,
                                        0);
@@ -1128,18 +1128,24 @@ __device__ __forceinline__ void f64g_issue(const float* __restrict__ G, int64_t 
     const int base_u = ((isA ? j : j - C::CPO) * (F64Tile::THREADS / 64) + wave) * 64;
     const int p = base_u + lane;  // unit position inside the operand's chunk
     const int r0 = isA ? m0 : n0;
-    const float* src;
+    // scalar base plus a 32-bit lane byte offset within the chunk: one copy
+    // instruction each
+    const char* P;
+    uint32_t off;
     if constexpr (!RIGHT) {
       const int row = p / 4;
       const int kg = dl_slot(row, p % 4, 4);  // the map is its own inverse
-      src = G + (int64_t)min(r0 + row, d - 1) * ld + k0 + kg * 4;
+      P = wave_uniform(G + (int64_t)r0 * ld + k0);
+      off = ((uint32_t)min(row, d - 1 - r0) * (uint32_t)ld + (uint32_t)(kg * 4)) * 4u;
     } else {
       const int k = p / 32;
       const int u = f64g_tslot(k, p % 32);  // an involution in the unit index too
-      src = G + (int64_t)(k0 + k) * ld + min(r0 + 4 * u, d - 4);
+      P = wave_uniform(G + (int64_t)k0 * ld);
+      off = ((uint32_t)k * (uint32_t)ld + (uint32_t)min(r0 + 4 * u, d - 4)) * 4u;
     }
-    __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)(stage + (isA ? 0 : C::OPB) + base_u * 16),
-                                     16, 0, 0);
+    asm volatile("" : "+v"(off));  // opaque per copy: the offset stays a 32-bit lane value
+    __builtin_amdgcn_global_load_lds((global_void_ptr)(P + off),
+                                     (lds_void_ptr)(stage + (isA ? 0 : C::OPB) + base_u * 16), 16, 0, 0);
   }
 }
 

@@ -191,9 +191,13 @@ __device__ __forceinline__ void h16dl_issue(const _Float16* __restrict__ A, int6
     const int u = base_u + lane;
     const int row = u / S::UPR;
     const int kg = dl_slot(row, u % S::UPR, S::UPR);  // the map is its own inverse
-    const _Float16* src = isA ? A + (int64_t)min(m0 + row, M - 1) * lda + k0 + kg * 8
-                              : B + (int64_t)min(n0 + row, N - 1) * ldb + k0 + kg * 8;
-    __builtin_amdgcn_global_load_lds((global_void_ptr)src,
+    // scalar base (row m0 or n0, column k0) plus a 32-bit lane byte offset
+    // within the tile's rows: one copy instruction each
+    const char* P = wave_uniform(isA ? A + (int64_t)m0 * lda + k0 : B + (int64_t)n0 * ldb + k0);
+    uint32_t off = ((uint32_t)min(row, isA ? M - 1 - m0 : N - 1 - n0) * (uint32_t)(isA ? lda : ldb) +
+                    (uint32_t)(kg * 8)) * 2u;
+    asm volatile("" : "+v"(off));  // opaque per copy: the offset stays a 32-bit lane value
+    __builtin_amdgcn_global_load_lds((global_void_ptr)(P + off),
                                      (lds_void_ptr)(stage + (isA ? 0 : S::AU * 16) + base_u * 16), 16, 0, 0);
   }
 }

@@ -108,11 +108,9 @@ __device__ __forceinline__ void oz_copy(const OzPlanes& A, const OzPlanes& B, in
 #pragma unroll
   for (int q = 0; q < OzCfg::S; ++q)
     if (q == p) P = is_a ? A.p[q] : B.p[q];
-  P += (int64_t)(is_a ? m0 : n0) * ld + k0;
-  // opaque per copy: the base stays scalar and the offset 32-bit (else the
-  // compiler hoists a 64-bit lane address out of the main loop)
-  asm volatile("" : "+s"(P), "+v"(off));
-  __builtin_amdgcn_global_load_lds((global_void_ptr)(P + off),
+  const char* base = wave_uniform(P + (int64_t)(is_a ? m0 : n0) * ld + k0);
+  asm volatile("" : "+v"(off));  // opaque per copy: the offset stays a 32-bit lane value
+  __builtin_amdgcn_global_load_lds((global_void_ptr)(base + off),
                                    (lds_void_ptr)(stage + (a * OzCfg::PLANE_UNITS + base_u) * 16), 16, 0, 0);
 }
 

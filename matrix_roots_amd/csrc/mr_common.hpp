@@ -165,6 +165,19 @@ typedef __attribute__((address_space(1))) void* global_void_ptr;
 
 __device__ __forceinline__ int dl_slot(int row, int kg, int upr) { return kg ^ ((row / (16 / upr)) % upr); }
 
+// A pointer every lane of the wave holds (a workgroup's operand base) as a
+// scalar value, opaque to the compiler: the direct-to-LDS copies then take it
+// as their scalar base with a 32-bit lane offset, instead of a 64-bit address
+// per lane that the compiler would hoist out of the main loop.
+__device__ __forceinline__ const char* wave_uniform(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  const char* u = reinterpret_cast<const char*>(lo | (hi << 32));
+  asm volatile("" : "+s"(u));
+  return u;
+}
+
 // f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
