@@ -53,3 +53,21 @@ def test_no_spills_or_scratch(device_asm):
                             f.get("private_segment_fixed_size")))
     assert seen >= 30, seen  # every kernel source parsed
     assert not bad, bad
+
+
+def test_direct_to_lds_copies_take_scalar_bases(device_asm):
+    """Every direct-to-LDS copy is one instruction on a scalar base with a
+    32-bit lane offset (`global_load_lds_dwordx4 vOFF, s[BASE:BASE+1]`), not
+    a per-lane 64-bit address (`..., off`): the 64-bit form costs three
+    64-bit adds per copy and registers held across the GEMM main loops."""
+    copies = 0
+    bad = []
+    for src, asm in device_asm.items():
+        for line in asm.splitlines():
+            s = line.strip()
+            if s.startswith("global_load_lds"):
+                copies += 1
+                if not re.match(r"global_load_lds_dword\w*\s+v\d+,\s+s\[\d+:\d+\]", s):
+                    bad.append((src, s))
+    assert copies >= 100, copies  # the GEMM cores of every source were parsed
+    assert not bad, bad[:5]
