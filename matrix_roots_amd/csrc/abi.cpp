@@ -127,7 +127,7 @@ enum TraceClass {
   kTrSyrk, kTrJacobi, kTrStats, kTrBound, kTrInit, kTrNewton64, kTrNewton32, kTrConvert,
   kTrFinalize, kTrInfo, kTrNewtonX3, kTrCansBound, kTrCansInit, kTrCansP, kTrCansYZ, kTrCansFinal, kTrCansInfo,
   kTrPolarStats, kTrPolarBound, kTrPolarInit, kTrPolarA, kTrPolarX, kTrPolarFinal, kTrPolarInfo,
-  kTrMomentum, kTrHyperReduce, kTrHyperUpdate, kTrApplyX3, kTrApplySplit, kTrSlice, kTrNewtonI8, kTrCount
+  kTrMomentum, kTrHyperReduce, kTrHyperUpdate, kTrApplyX3, kTrApplySplit, kTrSlice, kTrNewtonI8, kTrMoment, kTrCount
 };
 const char* const kTraceNames[kTrCount] = {"syrk_ema", "jacobi", "root_stats", "root_bound",
                                            "root_init", "newton_f64", "newton_f32", "newton_convert",
@@ -136,7 +136,7 @@ const char* const kTraceNames[kTrCount] = {"syrk_ema", "jacobi", "root_stats", "
                                            "polar_stats", "polar_bound", "polar_init", "polar_gram",
                                            "polar_update", "polar_finalize", "polar_info", "momentum",
                                            "hyperball_reduce", "hyperball_update", "apply_x3", "apply_split",
-                                           "newton_slice", "newton_i8"};
+                                           "newton_slice", "newton_i8", "root_moment"};
 struct TraceEntry {
   int cls;
   hipEvent_t a, b;
@@ -241,6 +241,9 @@ RootPlan plan_root(const mr_root_problem* p, int32_t count, int32_t method) {
   off = align256(off + sizeof(RootState) * (size_t)std::max(count, 1));
   P.partial_stride = std::max<int64_t>(3 * ((dmax_newton + kStatsRows - 1) / kStatsRows),
                                        (dmax_newton + kFinalRows - 1) / kFinalRows);
+  // the fourth-moment bound: |B/c|_F^2 and one sum per upper tile of H H
+  if (dmax_newton >= kMomentMinD)
+    P.partial_stride = std::max<int64_t>(P.partial_stride, 2 + (int64_t)moment_tiles((int)dmax_newton));
   P.partial_stride = std::max<int64_t>(P.partial_stride, 1);
   P.partial_off = off;
   off = align256(off + sizeof(double) * (size_t)P.partial_stride * (size_t)std::max(P.n_newton, 1));
@@ -881,18 +884,29 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
           J.slot = slot;
           J.problem = P.slot_problem[slot];
           J.block_begin = b.total_blocks;
+          const bool moment = q.d >= kMomentMinD;
           if (kind == 0)
             J.nblocks = tiles(q.d, kStatsRows);
           else if (kind == 1)
             J.nblocks = upper_tiles(q.d, 32);
+          else if (kind == 3)  // fp16 copy for the fourth-moment bound
+            J.nblocks = moment ? upper_tiles(moment_pad((int)q.d), 32) : 0;
+          else if (kind == 4)  // its square's tile sums
+            J.nblocks = moment ? moment_tiles((int)q.d) : 0;
           else
             J.nblocks = tiles(q.d, kFinalRows);
           b.total_blocks += J.nblocks;
           ++b.njobs;
           if (b.njobs == kMaxRootJobs || slot == P.n_newton - 1) {
-            const int cls = kind == 0 ? kTrStats : kind == 1 ? kTrInit : kTrFinalize;
+            const int cls = kind == 0 ? kTrStats : kind == 1 ? kTrInit : kind >= 3 ? kTrMoment : kTrFinalize;
             mr_status r = traced(cls, b.total_blocks > 0, s, [&] {
-              return kind == 0 ? launch_root_stats(b, s) : kind == 1 ? launch_root_init(b, s) : launch_root_finalize(b, s);
+              switch (kind) {
+                case 0: return launch_root_stats(b, s);
+                case 1: return launch_root_init(b, s);
+                case 3: return launch_root_moment_convert(b, s);
+                case 4: return launch_root_moment(b, s);
+                default: return launch_root_finalize(b, s);
+              }
             }, "root launch");
             if (r != MR_OK) return r;
             b.njobs = 0;
@@ -923,6 +937,19 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
                                     floor_cap, all_f64 ? 1 : 0, x_low ? 1 : 0, s);
          }, "root bound launch")) != MR_OK)
       return st;
+    // The fourth-moment bound where it is tighter: a higher floor, fewer steps
+    // (never more: the host's count above still covers every matrix).
+    int64_t dmax_newton_call = 0;
+    for (const auto& c : P.classes) dmax_newton_call = std::max<int64_t>(dmax_newton_call, c.d);
+    if (dmax_newton_call >= kMomentMinD) {
+      if ((st = run_root_batches(3)) != MR_OK) return st;
+      if ((st = run_root_batches(4)) != MR_OK) return st;
+      if ((st = traced(kTrMoment, true, s, [&] {
+             return launch_root_tighten(state, partial, P.partial_stride, sched, 0, P.n_newton, eps, k_cap, floor_cap,
+                                        all_f64 ? 1 : 0, x_low ? 1 : 0, s);
+           }, "root tighten launch")) != MR_OK)
+        return st;
+    }
     const int k_max = k_cap, j_max = all_f64 ? k_cap : j_cap;
     if ((st = run_root_batches(1)) != MR_OK) return st;
 

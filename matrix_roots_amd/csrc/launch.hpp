@@ -314,10 +314,26 @@ hipError_t launch_fill_zero(uint32_t* p, int32_t n, hipStream_t s);
 hipError_t launch_x3_apply(const X3ApplyBatch& b, hipStream_t s);
 
 hipError_t launch_root_stats(const RootBatch& b, hipStream_t s);
-hipError_t launch_root_bound(RootState* state, const double* partial, int64_t partial_stride, double* sched,
+hipError_t launch_root_bound(RootState* state, double* partial, int64_t partial_stride, double* sched,
                              int32_t slot_begin, int32_t nslots, int32_t normalize, double eps,
                              int32_t k_cap, double floor_cap, int32_t all_f64, int32_t finish, hipStream_t s);
 hipError_t launch_root_init(const RootBatch& b, hipStream_t s);
+// Fourth-moment bound on the largest eigenvalue (Newton matrices with d >=
+// kMomentMinD): fp16 copy of (A/s + eps I)/c zero-padded to moment_pad(d),
+// its square's tile sums of squares into the partials, then the tighter c and
+// its schedule.
+constexpr int kMomentMinD = 256;  // below, three more launches outweigh the steps a tighter bound saves
+constexpr int kMomentTile = 128;
+__host__ __device__ inline int moment_pad(int d) { return (d + 63) / 64 * 64; }
+__host__ __device__ inline int moment_tiles(int d) {
+  const int t = (moment_pad(d) + kMomentTile - 1) / kMomentTile;
+  return t * (t + 1) / 2;
+}
+hipError_t launch_root_moment_convert(const RootBatch& b, hipStream_t s);
+hipError_t launch_root_moment(const RootBatch& b, hipStream_t s);
+hipError_t launch_root_tighten(RootState* state, const double* partial, int64_t partial_stride, double* sched,
+                               int32_t slot_begin, int32_t nslots, double eps, int32_t k_cap, double floor_cap,
+                               int32_t all_f64, int32_t finish, hipStream_t s);
 enum StageKind { kStageF64 = 0, kStageF32 = 1, kStageX3 = 2, kStageX3B64 = 3, kStageI8 = 4 };
 hipError_t launch_newton_stage(const NewtonLaunch& L, int kind, int vec, hipStream_t s);
 hipError_t launch_newton_slice(const NewtonLaunch& L, hipStream_t s);

@@ -42,6 +42,7 @@
 
 #include "epilogue.hpp"
 #include "gemm_core.hpp"
+#include "gemm_h16.hpp"
 #include "gemm_i8.hpp"
 #include "launch.hpp"
 #include "schedule.hpp"
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(256) void root_stats_kernel(const RootBatch B) {
 // largest eigenvalue by the minimum of this and a second bound before its
 // iteration).  |A|_F is taken over A itself, which bounds that of (A + A^T)/2.
 // For a positive semidefinite A/s of unit trace WS <= 1 + eps.
-__global__ __launch_bounds__(64) void root_bound_kernel(RootState* state, const double* partial,
+__global__ __launch_bounds__(64) void root_bound_kernel(RootState* state, double* partial,
                                                         int64_t stride, double* sched, int32_t slot_begin,
                                                         int32_t normalize, double eps, int32_t k_cap,
                                                         double floor_cap, int32_t all_f64, int32_t finish) {
@@ -276,6 +277,8 @@ __global__ __launch_bounds__(64) void root_bound_kernel(RootState* state, const 
         flags |= MR_INFO_NOT_PD;
         c = 1.0;
       } else {
+        // |B/c|_F^2 for the fourth-moment bound (the stripe partials are read)
+        partial[(int64_t)slot * stride + 1] = f2B / (c * c);
         // The host launches the schedule of floor_cap: a matrix whose floor
         // lies lower runs exactly that schedule (its steps and its float64
         // steps are then those the host launches; both counts only fall as
@@ -299,6 +302,126 @@ __global__ __launch_bounds__(64) void root_bound_kernel(RootState* state, const 
   st.fin = fin;
   st.flags = flags;
 }
+
+// ------------------------------------------------------------ fourth-moment bound
+// A second upper bound on the largest eigenvalue beside Wolkowicz-Styan (the
+// OKLS page, appendix D, takes the smaller of two bounds in the same place):
+// for a symmetric H, |mu|_max(H)^4 <= tr(H^4) = |H^2|_F^2.  H is the fp16 copy
+// of B/c (B = A/s + eps I, c the Wolkowicz-Styan bound), its square comes from
+// fp16 products with float32 sums, and the tighten kernel adds the rounding of
+// both to the bound (Weyl's inequality for the copy, the float32 sum error
+// for the product), so the result stays an upper bound.  On Grams of gradients
+// it is 2-3 times tighter than Wolkowicz-Styan: a higher floor eps/c, fewer
+// Newton steps.
+
+// H = fp16((A/s + eps I)/c), zero-padded to dp = moment_pad(d), row stride dp,
+// at the start of the matrix's region (root_init writes M0 there afterwards):
+// the 32 x 32 tile pairs of root_init over the padded grid.
+template <typename TA>
+__global__ __launch_bounds__(256) void root_moment_convert_kernel(const RootBatch B) {
+  __shared__ double ta[32][33];
+  __shared__ double tb[32][33];
+  const int64_t b = blockIdx.x;
+  const RootJob& J = B.job[find_job(B, b)];
+  const RootState& st = B.state[J.slot];
+  const int d = J.d;
+  if (st.K == 0 || d < kMomentMinD) return;
+  const int dp = moment_pad(d);
+  int bi, bj;
+  upper_pair((int)(b - J.block_begin), dp / 32, bi, bj);
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const bool packed = B.a_packed != 0;
+  load_sym_tile<TA>(J.A, J.lda, d, packed, bi, bj, ta, tb);  // zero past d
+  const double inv_s = 1.0 / st.s, inv_c = 1.0 / st.c, eps = B.eps;
+  _Float16* H = reinterpret_cast<_Float16*>(J.region);
+  auto put = [&](int gi, int gj, double sym) __attribute__((always_inline)) {
+    const double v = gi < d && gj < d ? (sym * inv_s + (gi == gj ? eps : 0.0)) * inv_c : 0.0;
+    H[(int64_t)gi * dp + gj] = (_Float16)v;
+  };
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = ty + 8 * e;
+    put(bi * 32 + r, bj * 32 + tx, sym_tile_value(packed, bi, bj, r, tx, ta, tb));
+    if (bi != bj) put(bj * 32 + r, bi * 32 + tx, sym_tile_value(packed, bi, bj, tx, r, ta, tb));
+  }
+}
+
+// Sum of squares of the upper 128 x 128 tile u of H H (twice for tiles off the
+// diagonal), elements past d left out, into partial[2 + u] of the matrix.
+using MomentShape = H16Shape<kMomentTile, kMomentTile, 2, 2>;
+static_assert(MomentShape::THREADS == 256, "block_sum_256");
+__global__ __launch_bounds__(256) void root_moment_kernel(const RootBatch B) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[h16_lds_bytes<MomentShape>()];
+  __shared__ double red[256];
+  const int64_t b = blockIdx.x;
+  const RootJob& J = B.job[find_job(B, b)];
+  const RootState& st = B.state[J.slot];
+  const int d = J.d;
+  if (st.K == 0 || d < kMomentMinD) return;
+  const int dp = moment_pad(d);
+  const int T = (dp + kMomentTile - 1) / kMomentTile;
+  const int u = (int)(b - J.block_begin);
+  int ti, tj;
+  upper_pair(u, T, ti, tj);
+  const _Float16* H = reinterpret_cast<const _Float16*>(J.region);
+  v16f acc[MomentShape::RB][MomentShape::CB];
+  // dp is a multiple of 64: the direct-to-LDS core, whole 64-deep chunks
+  h16_nt_tile_auto<MomentShape, 8>(H, dp, H, dp, dp, dp, dp, ti * kMomentTile, tj * kMomentTile, smem, acc);
+  double sq = 0.0;
+  h16g_for_each<MomentShape>(acc, [&](int rr, int cc, float v) {
+    if (ti * kMomentTile + rr < d && tj * kMomentTile + cc < d) sq += (double)v * (double)v;
+  });
+  sq = block_sum_256(sq, red);
+  if (threadIdx.x == 0) B.partial[(int64_t)J.slot * B.partial_stride + 2 + u] = (ti == tj ? 1.0 : 2.0) * sq;
+}
+
+// One wave per matrix: the fourth-moment bound from the tile sums, and where
+// it is below the Wolkowicz-Styan c, that c and its schedule instead.
+//   |H^2|_F <= |P|_F + g |H|_F^2, g = d u / (1 - d u), u = 2^-24 (float32 sums
+//     of exact fp16 products, in any order),
+//   lambda_max(B/c) <= |mu|_max(H) + |B/c - H|_F, |B/c - H|_F <= 2^-11 |B/c|_F
+//     + d 2^-25 (fp16 rounding: half an ulp, or half the smallest subnormal),
+// |H|_F <= (1 + 2^-11) |B/c|_F + d 2^-25.
+__global__ __launch_bounds__(64) void root_tighten_kernel(RootState* state, const double* partial, int64_t stride,
+                                                          double* sched, int32_t slot_begin, double eps,
+                                                          int32_t k_cap, double floor_cap, int32_t all_f64,
+                                                          int32_t finish) {
+  __shared__ double red[64];
+  const int slot = slot_begin + blockIdx.x;
+  RootState& st = state[slot];
+  if (st.K == 0 || st.d < kMomentMinD) return;
+  const double* p = partial + (int64_t)slot * stride;
+  const int U = moment_tiles(st.d);
+  double m4 = 0.0;
+  for (int i = threadIdx.x; i < U; i += 64) m4 += p[2 + i];
+  m4 = block_sum_64(m4, red);
+  if (threadIdx.x != 0) return;
+  const double dd = (double)st.d;
+  const double fb = sqrt(p[1]);  // |B/c|_F
+  const double nh = (1.0 + 0x1p-11) * fb + dd * 0x1p-25;
+  const double g = dd * 0x1p-24 / (1.0 - dd * 0x1p-24);
+  const double mu = sqrt(sqrt(m4) + g * nh * nh);
+  const double beta = mu + 0x1p-11 * fb + dd * 0x1p-25;
+  const double c = kBoundSafety * st.c * beta;
+  if (!(c > 0.0) || !(c < st.c) || !isfinite(c)) return;
+  double floor = fmin(eps / c, 1.0 / kBoundSafety);
+  uint32_t flags = st.flags & ~(uint32_t)MR_INFO_NOT_CONVERGED;
+  if (floor < floor_cap) {
+    floor = floor_cap;
+    flags |= MR_INFO_NOT_CONVERGED;
+  }
+  int K = 0, j = 0, fin = 1;
+  newton_scaled_schedule(floor, 1.0 / kBoundSafety, kNewtonTol, kSwitchM, k_cap,
+                         sched + (int64_t)slot * kMaxNewtonIters, &K, &j, finish != 0, &fin);
+  if (all_f64) j = K;
+  st.c = c;
+  st.out_scale = pow(c, -0.25);
+  st.K = K;
+  st.j = j;
+  st.fin = fin;
+  st.flags = flags;
+}
+
 
 // M0 = ((A + A^T)/2 / s + eps I) / c into S0 (float64), one workgroup per
 // pair of mirrored 32 x 32 tiles (upper_pair), both read once through LDS so
@@ -1162,12 +1285,36 @@ hipError_t launch_root_stats(const RootBatch& b, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_root_bound(RootState* state, const double* partial, int64_t partial_stride, double* sched,
+hipError_t launch_root_bound(RootState* state, double* partial, int64_t partial_stride, double* sched,
                              int32_t slot_begin, int32_t nslots, int32_t normalize, double eps, int32_t k_cap,
                              double floor_cap, int32_t all_f64, int32_t finish, hipStream_t s) {
   if (nslots <= 0) return hipSuccess;
   hipLaunchKernelGGL(root_bound_kernel, dim3(nslots), dim3(64), 0, s, state, partial, partial_stride, sched,
                      slot_begin, normalize, eps, k_cap, floor_cap, all_f64, finish);
+  return hipGetLastError();
+}
+
+hipError_t launch_root_moment_convert(const RootBatch& b, hipStream_t s) {
+  if (b.total_blocks <= 0) return hipSuccess;
+  if (b.a_f64)
+    hipLaunchKernelGGL(root_moment_convert_kernel<double>, dim3(b.total_blocks), dim3(256), 0, s, b);
+  else
+    hipLaunchKernelGGL(root_moment_convert_kernel<float>, dim3(b.total_blocks), dim3(256), 0, s, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_root_moment(const RootBatch& b, hipStream_t s) {
+  if (b.total_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(root_moment_kernel, dim3(b.total_blocks), dim3(256), 0, s, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_root_tighten(RootState* state, const double* partial, int64_t partial_stride, double* sched,
+                               int32_t slot_begin, int32_t nslots, double eps, int32_t k_cap, double floor_cap,
+                               int32_t all_f64, int32_t finish, hipStream_t s) {
+  if (nslots <= 0) return hipSuccess;
+  hipLaunchKernelGGL(root_tighten_kernel, dim3(nslots), dim3(64), 0, s, state, partial, partial_stride, sched,
+                     slot_begin, eps, k_cap, floor_cap, all_f64, finish);
   return hipGetLastError();
 }
 
