@@ -202,10 +202,13 @@ size_t gram_ema_update_workspace(const mr_gram_problem* problems, int32_t count,
  *    largest entry); smaller Grams run them on the float64 matrix cores.
  *    The GEMM-only
  *    route of tilderesearch, "Online KL Shampoo", sections 2.1-2.2 (there
- *    for the -1/2 root), taken to the 4th root.  c = 1.01 times the
- *    Wolkowicz-Styan upper bound on lambda_max(A/s + eps I) (the OKLS page,
- *    appendix D, normalises by an O(d^2) upper bound in the same way); the
- *    iteration count follows from eps/c.  The last iteration updates X only:
+ *    for the -1/2 root), taken to the 4th root.  c = 1.01 times an upper
+ *    bound on lambda_max(A/s + eps I): the Wolkowicz-Styan bound (the OKLS
+ *    page, appendix D, normalises by an O(d^2) upper bound in the same way),
+ *    or for d >= 256, where it is smaller, the fourth-moment bound
+ *    |B^2|_F^(1/2) of B = A/s + eps I from one fp16 product (its fp16 and
+ *    float32 rounding added, so it stays an upper bound); the iteration
+ *    count follows from eps/c.  The last iteration updates X only:
  *    with the step's polynomial, or, once the spectrum of M lies within
  *    0.0162 (0.0898) of 1, with the degree-2 (degree-4) Taylor polynomial of
  *    M^(-1/4) about I, which ends the iteration a step or two earlier with a
