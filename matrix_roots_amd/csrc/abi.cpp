@@ -241,9 +241,9 @@ RootPlan plan_root(const mr_root_problem* p, int32_t count, int32_t method) {
   off = align256(off + sizeof(RootState) * (size_t)std::max(count, 1));
   P.partial_stride = std::max<int64_t>(3 * ((dmax_newton + kStatsRows - 1) / kStatsRows),
                                        (dmax_newton + kFinalRows - 1) / kFinalRows);
-  // the fourth-moment bound: |B/c|_F^2 and one sum per upper tile of H H
+  // the moment bounds: |B/c|_F^2 and one sum per upper tile of H H and of P16 P16
   if (dmax_newton >= kMomentMinD)
-    P.partial_stride = std::max<int64_t>(P.partial_stride, 2 + (int64_t)moment_tiles((int)dmax_newton));
+    P.partial_stride = std::max<int64_t>(P.partial_stride, 2 + 2 * (int64_t)moment_tiles((int)dmax_newton));
   P.partial_stride = std::max<int64_t>(P.partial_stride, 1);
   P.partial_off = off;
   off = align256(off + sizeof(double) * (size_t)P.partial_stride * (size_t)std::max(P.n_newton, 1));
@@ -891,7 +891,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
             J.nblocks = upper_tiles(q.d, 32);
           else if (kind == 3)  // fp16 copy for the fourth-moment bound
             J.nblocks = moment ? upper_tiles(moment_pad((int)q.d), 32) : 0;
-          else if (kind == 4)  // its square's tile sums
+          else if (kind == 4 || kind == 5)  // tile sums of its square (4) and fourth power (5)
             J.nblocks = moment ? moment_tiles((int)q.d) : 0;
           else
             J.nblocks = tiles(q.d, kFinalRows);
@@ -904,7 +904,8 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
                 case 0: return launch_root_stats(b, s);
                 case 1: return launch_root_init(b, s);
                 case 3: return launch_root_moment_convert(b, s);
-                case 4: return launch_root_moment(b, s);
+                case 4: return launch_root_moment(b, 0, s);
+                case 5: return launch_root_moment(b, 1, s);
                 default: return launch_root_finalize(b, s);
               }
             }, "root launch");
@@ -944,6 +945,7 @@ mr_status inv_quarter_root_batched(const mr_root_problem* p, int32_t count, mr_d
     if (dmax_newton_call >= kMomentMinD) {
       if ((st = run_root_batches(3)) != MR_OK) return st;
       if ((st = run_root_batches(4)) != MR_OK) return st;
+      if ((st = run_root_batches(5)) != MR_OK) return st;
       if ((st = traced(kTrMoment, true, s, [&] {
              return launch_root_tighten(state, partial, P.partial_stride, sched, 0, P.n_newton, eps, k_cap, floor_cap,
                                         all_f64 ? 1 : 0, x_low ? 1 : 0, s);

@@ -318,10 +318,11 @@ hipError_t launch_root_bound(RootState* state, double* partial, int64_t partial_
                              int32_t slot_begin, int32_t nslots, int32_t normalize, double eps,
                              int32_t k_cap, double floor_cap, int32_t all_f64, int32_t finish, hipStream_t s);
 hipError_t launch_root_init(const RootBatch& b, hipStream_t s);
-// Fourth-moment bound on the largest eigenvalue (Newton matrices with d >=
-// kMomentMinD): fp16 copy of (A/s + eps I)/c zero-padded to moment_pad(d),
-// its square's tile sums of squares into the partials, then the tighter c and
-// its schedule.
+// Moment bounds on the largest eigenvalue (Newton matrices with d >=
+// kMomentMinD): fp16 copy H of (A/s + eps I)/c zero-padded to moment_pad(d),
+// the tile sums of squares of H H (fourth moment) and of its fp16 copy
+// squared (eighth moment) into the partials, then the tighter c and its
+// schedule.
 constexpr int kMomentMinD = 256;  // below, three more launches outweigh the steps a tighter bound saves
 constexpr int kMomentTile = 128;
 __host__ __device__ inline int moment_pad(int d) { return (d + 63) / 64 * 64; }
@@ -330,7 +331,7 @@ __host__ __device__ inline int moment_tiles(int d) {
   return t * (t + 1) / 2;
 }
 hipError_t launch_root_moment_convert(const RootBatch& b, hipStream_t s);
-hipError_t launch_root_moment(const RootBatch& b, hipStream_t s);
+hipError_t launch_root_moment(const RootBatch& b, int pass, hipStream_t s);
 hipError_t launch_root_tighten(RootState* state, const double* partial, int64_t partial_stride, double* sched,
                                int32_t slot_begin, int32_t nslots, double eps, int32_t k_cap, double floor_cap,
                                int32_t all_f64, int32_t finish, hipStream_t s);

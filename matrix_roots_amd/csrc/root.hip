@@ -346,10 +346,13 @@ __global__ __launch_bounds__(256) void root_moment_convert_kernel(const RootBatc
   }
 }
 
-// Sum of squares of the upper 128 x 128 tile u of H H (twice for tiles off the
-// diagonal), elements past d left out, into partial[2 + u] of the matrix.
+// Pass 0: sum of squares of the upper 128 x 128 tile u of P = H H (twice for
+// tiles off the diagonal), elements past d left out, into partial[2 + u] of
+// the matrix, and the tile and its mirror as fp16 into P16 (dp x dp after
+// H in the region).  Pass 1: the same sums for P16 P16 into partial[2 + U + u].
 using MomentShape = H16Shape<kMomentTile, kMomentTile, 2, 2>;
 static_assert(MomentShape::THREADS == 256, "block_sum_256");
+template <int PASS>
 __global__ __launch_bounds__(256) void root_moment_kernel(const RootBatch B) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[h16_lds_bytes<MomentShape>()];
   __shared__ double red[256];
@@ -363,16 +366,24 @@ __global__ __launch_bounds__(256) void root_moment_kernel(const RootBatch B) {
   const int u = (int)(b - J.block_begin);
   int ti, tj;
   upper_pair(u, T, ti, tj);
-  const _Float16* H = reinterpret_cast<const _Float16*>(J.region);
+  _Float16* H = reinterpret_cast<_Float16*>(J.region);
+  _Float16* P16 = H + (int64_t)dp * dp;
+  const _Float16* In = PASS == 0 ? H : P16;
   v16f acc[MomentShape::RB][MomentShape::CB];
   // dp is a multiple of 64: the direct-to-LDS core, whole 64-deep chunks
-  h16_nt_tile_auto<MomentShape, 8>(H, dp, H, dp, dp, dp, dp, ti * kMomentTile, tj * kMomentTile, smem, acc);
+  h16_nt_tile_auto<MomentShape, 8>(In, dp, In, dp, dp, dp, dp, ti * kMomentTile, tj * kMomentTile, smem, acc);
   double sq = 0.0;
   h16g_for_each<MomentShape>(acc, [&](int rr, int cc, float v) {
-    if (ti * kMomentTile + rr < d && tj * kMomentTile + cc < d) sq += (double)v * (double)v;
+    const int gr = ti * kMomentTile + rr, gc = tj * kMomentTile + cc;
+    if (gr < d && gc < d) sq += (double)v * (double)v;
+    if (PASS == 0 && gr < dp && gc < dp && (ti != tj || rr <= cc)) {  // one writer per pair: P16 symmetric
+      P16[(int64_t)gr * dp + gc] = (_Float16)v;
+      P16[(int64_t)gc * dp + gr] = (_Float16)v;
+    }
   });
   sq = block_sum_256(sq, red);
-  if (threadIdx.x == 0) B.partial[(int64_t)J.slot * B.partial_stride + 2 + u] = (ti == tj ? 1.0 : 2.0) * sq;
+  if (threadIdx.x == 0)
+    B.partial[(int64_t)J.slot * B.partial_stride + 2 + PASS * moment_tiles(d) + u] = (ti == tj ? 1.0 : 2.0) * sq;
 }
 
 // One wave per matrix: the fourth-moment bound from the tile sums, and where
@@ -392,16 +403,29 @@ __global__ __launch_bounds__(64) void root_tighten_kernel(RootState* state, cons
   if (st.K == 0 || st.d < kMomentMinD) return;
   const double* p = partial + (int64_t)slot * stride;
   const int U = moment_tiles(st.d);
-  double m4 = 0.0;
-  for (int i = threadIdx.x; i < U; i += 64) m4 += p[2 + i];
+  double m4 = 0.0, m8 = 0.0;
+  for (int i = threadIdx.x; i < U; i += 64) {
+    m4 += p[2 + i];
+    m8 += p[2 + U + i];
+  }
   m4 = block_sum_64(m4, red);
+  m8 = block_sum_64(m8, red);
   if (threadIdx.x != 0) return;
-  const double dd = (double)st.d;
+  const double dd = (double)moment_pad(st.d);
   const double fb = sqrt(p[1]);  // |B/c|_F
   const double nh = (1.0 + 0x1p-11) * fb + dd * 0x1p-25;
   const double g = dd * 0x1p-24 / (1.0 - dd * 0x1p-24);
-  const double mu = sqrt(sqrt(m4) + g * nh * nh);
-  const double beta = mu + 0x1p-11 * fb + dd * 0x1p-25;
+  // fourth moment: |mu|_max(H)^2 <= |H^2|_F <= |P|_F + g |H|_F^2
+  const double e2 = g * nh * nh;  // |P - H^2|_F
+  const double mu4 = sqrt(sqrt(m4) + e2);
+  // eighth moment through P16 = fp16(P), symmetric: |mu|_max(H)^2 =
+  // |nu|_max(H^2) <= |nu|_max(P16) + |P16 - H^2|_F, |nu|_max(P16)^2 <=
+  // |P16^2|_F <= |Q|_F + g |P16|_F^2 (Q the float32 product of P16)
+  const double np = sqrt(m4);  // |P|_F
+  const double np16 = (1.0 + 0x1p-11) * np + dd * 0x1p-25;
+  const double nu = sqrt(sqrt(m8) + g * np16 * np16) + 0x1p-11 * np + dd * 0x1p-25 + e2;
+  const double mu8 = sqrt(nu);
+  const double beta = fmin(mu4, mu8) + 0x1p-11 * fb + dd * 0x1p-25;
   const double c = kBoundSafety * st.c * beta;
   if (!(c > 0.0) || !(c < st.c) || !isfinite(c)) return;
   double floor = fmin(eps / c, 1.0 / kBoundSafety);
@@ -1303,9 +1327,12 @@ hipError_t launch_root_moment_convert(const RootBatch& b, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_root_moment(const RootBatch& b, hipStream_t s) {
+hipError_t launch_root_moment(const RootBatch& b, int pass, hipStream_t s) {
   if (b.total_blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(root_moment_kernel, dim3(b.total_blocks), dim3(256), 0, s, b);
+  if (pass == 0)
+    hipLaunchKernelGGL(root_moment_kernel<0>, dim3(b.total_blocks), dim3(256), 0, s, b);
+  else
+    hipLaunchKernelGGL(root_moment_kernel<1>, dim3(b.total_blocks), dim3(256), 0, s, b);
   return hipGetLastError();
 }
 
