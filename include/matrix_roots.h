@@ -205,10 +205,10 @@ size_t gram_ema_update_workspace(const mr_gram_problem* problems, int32_t count,
  *    for the -1/2 root), taken to the 4th root.  c = 1.01 times an upper
  *    bound on lambda_max(A/s + eps I): the Wolkowicz-Styan bound (the OKLS
  *    page, appendix D, normalises by an O(d^2) upper bound in the same way),
- *    or for d >= 256, where it is smaller, the fourth-moment bound
- *    |B^2|_F^(1/2) of B = A/s + eps I from one fp16 product (its fp16 and
- *    float32 rounding added, so it stays an upper bound); the iteration
- *    count follows from eps/c.  The last iteration updates X only:
+ *    or for d >= 256, where smaller, the fourth- or eighth-moment bound
+ *    |B^2|_F^(1/2) or |B^4|_F^(1/4) of B = A/s + eps I from two fp16
+ *    products (their fp16 and float32 rounding added, so they stay upper
+ *    bounds); the iteration count follows from eps/c.  The last iteration updates X only:
  *    with the step's polynomial, or, once the spectrum of M lies within
  *    0.0162 (0.0898) of 1, with the degree-2 (degree-4) Taylor polynomial of
  *    M^(-1/4) about I, which ends the iteration a step or two earlier with a
