@@ -38,7 +38,15 @@ PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6, "f16": 2500.0, "i8": 5000.0}  # MI355X
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E (vendor figure)
 # kernel class -> matrix-core unit it runs on
 CLASS_ENGINE = {"newton_f64": "f64", "syrk_ema": "f64", "newton_f32": "f32", "newton_x3": "f16", "apply_x3": "f16",
-                "newton_i8": "i8"}
+                "newton_i8": "i8", "root_moment": "f16"}
+MOMENT_MIN_D = 256  # Newton roots from this size take the moment bounds
+
+
+def moment_flops(d: int) -> float:
+    """The moment bounds' two plain fp16 products of a Newton root (H H and
+    P16 P16, symmetric: d^2 (d + 1) algorithmic flops each); 0 below the
+    size that takes them."""
+    return 2.0 * d * d * (d + 1) if d >= MOMENT_MIN_D else 0.0
 # matrix-core products per algorithmic product: three fp16 products per
 # float32-accurate one (split classes), 21 int8 digit-plane products per
 # float64-accurate one (the default path's float64 steps)
@@ -512,7 +520,8 @@ def bench_steps(args, torch, B, W, peaks):
     sbytes.update({"momentum": 12 * elems, "hyperball_reduce": 8 * elems, "hyperball_update": 12 * elems,
                    # maxima and split copies of XR, G, XL and W^T: 8 bytes read and 4 written per element
                    "apply_split": 12 * sum(m * m + 2 * m * n + n * n for m, n in shapes) * args.steps})
-    flops = {**f64, "newton_x3": low, "syrk_ema": syrk, "apply_x3": apply_f}
+    moment = sum(moment_flops(m) + moment_flops(n) for m, n in shapes) * args.steps
+    flops = {**f64, "newton_x3": low, "syrk_ema": syrk, "apply_x3": apply_f, "root_moment": moment}
     kernels = kernel_table(trace, flops, sbytes)
     # the syrk's HBM bytes (state read + write, gradient read) as context: it is matrix-core bound
     if "syrk_ema" in kernels:
@@ -677,7 +686,8 @@ def bench_illcond(args, torch, B, W, peaks):
                                "fp64_iters": [int(info["fp64_iters"].min()), int(info["fp64_iters"].max())],
                                "tflops": round((ef64 + elow) / (cms / 1e3) / 1e12, 2)}
         log(f"eps {eps:g}: {per_eps[f'{eps:g}']}")
-    kernels = kernel_table(trace, {f64_class(512): f64, "newton_x3": low}, sbytes)
+    moment = moment_flops(512) * count * len(per_eps) * args.steps
+    kernels = kernel_table(trace, {f64_class(512): f64, "newton_x3": low, "root_moment": moment}, sbytes)
     engines = engine_table(kernels)
     annotate_engines(engines, peaks)
     dname = max((kv for kv in kernels.items() if "tflops" in kv[1]), key=lambda kv: kv[1]["ms_total"])[0]
